@@ -1,0 +1,356 @@
+"""CPU oracle for tile-based differentiable 3D Gaussian splatting (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  It never imports the HIP library or its binding, and the HIP library never
+imports it.  The per-Gaussian projection and the per-pixel compositing and backward are
+plain double-precision C (``gs_oracle.c``); binning is plain NumPy (a cumulative sum, an
+enumeration and a stable sort).
+
+What the method computes is never written out on the pages: ByteSplat (arXiv 2610.02851,
+English abstract) names forward and backward rasterization, their fusion and a per-tile
+pruning; Grendel (arXiv 2406.18533, English abstract) notes that each Gaussian touches a small
+subset of pixels and trains on batches of views; GS-Scale (arXiv 2509.15645, English abstract)
+adds per-view frustum culling.  The formulas are the plainest reading of EWA splatting with
+front-to-back alpha compositing; the constants are readings and arrive as parameters.
+Parity status per function is stated in each docstring.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gs_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the C part of the oracle (gcc, OpenMP, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-std=c11", "-Wall",
+                               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Camera(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("height", ctypes.c_int32),
+                ("fx", ctypes.c_double), ("fy", ctypes.c_double),
+                ("cx", ctypes.c_double), ("cy", ctypes.c_double),
+                ("R", ctypes.c_double * 9), ("t", ctypes.c_double * 3),
+                ("campos", ctypes.c_double * 3)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("znear", ctypes.c_double), ("eps2d", ctypes.c_double),
+                ("alpha_min", ctypes.c_double), ("alpha_max", ctypes.c_double),
+                ("t_min", ctypes.c_double), ("bg", ctypes.c_double * 3),
+                ("sh_degree", ctypes.c_int32), ("tile", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=False)
+        _lib = ctypes.CDLL(_LIB)
+        _lib.orc_sh_basis.restype = None
+        _lib.orc_project.restype = None
+        _lib.orc_raster_forward.restype = None
+        _lib.orc_raster_backward.restype = None
+        _lib.orc_raster_bruteforce.restype = None
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x) -> float:
+    """Constants reach both implementations as float32 values; the oracle widens them."""
+    return float(np.float32(x))
+
+
+def _cam(c) -> _Camera:
+    cam = _Camera()
+    cam.width, cam.height = int(c.width), int(c.height)
+    cam.fx, cam.fy, cam.cx, cam.cy = _f32(c.fx), _f32(c.fy), _f32(c.cx), _f32(c.cy)
+    R = np.asarray(c.R, np.float32).astype(np.float64).reshape(9)
+    t = np.asarray(c.t, np.float32).astype(np.float64).reshape(3)
+    cp = np.asarray(c.campos, np.float32).astype(np.float64).reshape(3)
+    for k in range(9):
+        cam.R[k] = R[k]
+    for k in range(3):
+        cam.t[k] = t[k]
+        cam.campos[k] = cp[k]
+    return cam
+
+
+def _params(s, tile: int = 16) -> _Params:
+    p = _Params()
+    p.znear, p.eps2d = _f32(s.znear), _f32(s.eps2d)
+    p.alpha_min, p.alpha_max, p.t_min = _f32(s.alpha_min), _f32(s.alpha_max), _f32(s.t_min)
+    for k in range(3):
+        p.bg[k] = _f32(s.bg[k])
+    p.sh_degree = int(s.sh_degree)
+    p.tile = tile
+    return p
+
+
+# ---------------------------------------------------------------------------------------
+# Spherical harmonics
+# ---------------------------------------------------------------------------------------
+def sh_basis(degree: int, dirs: np.ndarray) -> np.ndarray:
+    """Real orthonormal SH basis values Y[l*l+l+m] at unit directions dirs (n, 3).
+
+    Parity: pinned against scipy's complex spherical harmonics (converted to real form) and
+    by quadrature orthonormality."""
+    lib = _load()
+    dirs = np.ascontiguousarray(dirs, np.float64)
+    out = np.zeros((dirs.shape[0], 16), np.float64)
+    for i in range(dirs.shape[0]):
+        lib.orc_sh_basis(ctypes.c_int(degree), _p(dirs[i]), _p(out[i]))
+    return out[:, : (degree + 1) ** 2]
+
+
+# ---------------------------------------------------------------------------------------
+# Projection (per view)
+# ---------------------------------------------------------------------------------------
+def project(scene, cam, settings) -> dict:
+    """Project every Gaussian of ``scene`` into camera ``cam`` (no compaction).
+
+    Returns per-Gaussian arrays: visible, mean2d (n,2), cov2d (n,3), conic (n,3), opacity,
+    color (n,3), depth, rect (n,4) int32 (tx0, ty0, tx1, ty1), n_tiles, flag.
+    Parity: pinned by closed forms (on/off-axis isotropic Gaussians, quaternion axes,
+    camera-frame equivalence) and by a brute-force check of the opacity-aware box."""
+    lib = _load()
+    n = scene.means.shape[1]
+    out = dict(visible=np.zeros(n, np.int8), mean2d=np.zeros((n, 2)), cov2d=np.zeros((n, 3)),
+               conic=np.zeros((n, 3)), opacity=np.zeros(n), color=np.zeros((n, 3)), depth=np.zeros(n),
+               rect=np.zeros((n, 4), np.int32), n_tiles=np.zeros(n, np.int32), flag=np.zeros(n, np.int8))
+    arrs = [np.ascontiguousarray(a, np.float32) for a in
+            (scene.means, scene.log_scales, scene.quats, scene.opacity_logits, scene.sh)]
+    c, pp = _cam(cam), _params(settings)
+    lib.orc_project(ctypes.c_int64(n), *[_p(a) for a in arrs], ctypes.byref(c), ctypes.byref(pp),
+                    _p(out["visible"]), _p(out["mean2d"]), _p(out["cov2d"]), _p(out["conic"]),
+                    _p(out["opacity"]), _p(out["color"]), _p(out["depth"]), _p(out["rect"]),
+                    _p(out["n_tiles"]), _p(out["flag"]))
+    return out
+
+
+def compact(proj: dict) -> dict:
+    """Visible Gaussians in ascending original index become slots 0..n_vis-1."""
+    ids = np.nonzero(proj["visible"])[0].astype(np.int32)
+    rec = {k: v[ids] for k, v in proj.items() if k != "visible"}
+    rec["vis_ids"] = ids
+    rec["vis_count"] = int(ids.size)
+    return rec
+
+
+# ---------------------------------------------------------------------------------------
+# Binning (NumPy): scan, emission, stable sort by (tile, depth), ranges, cap
+# ---------------------------------------------------------------------------------------
+def depth_bits(depth) -> np.ndarray:
+    """The depth key is the raw float32 bit pattern of camera-space z (positive, monotone)."""
+    return np.asarray(depth, np.float32).view(np.uint32)
+
+
+def bin_tiles(rect: np.ndarray, n_tiles: np.ndarray, dbits: np.ndarray, tiles_x: int, tiles_y: int) -> dict:
+    """Instances of (tile, slot) for each slot's tile rectangle, sorted by (tile, depth, slot).
+
+    offsets = exclusive cumulative sum of n_tiles; slot s emits its tiles row-major at
+    offsets[s] + k with key (tile << 32) | depth_bits and value s; a stable sort by key keeps
+    equal keys in slot order; ranges[t] = [first, last + 1) of tile t, (0, 0) when empty.
+    Parity: pinned by brute-force enumeration and Python's sorted() on tuples."""
+    n = int(n_tiles.shape[0])
+    n_tiles = n_tiles.astype(np.int64)
+    offsets = np.zeros(n, np.int64)
+    if n:
+        offsets[1:] = np.cumsum(n_tiles)[:-1]
+    M = int(n_tiles.sum()) if n else 0
+    slot = np.repeat(np.arange(n, dtype=np.int64), n_tiles)
+    k = np.arange(M, dtype=np.int64) - np.repeat(offsets, n_tiles)
+    tx0, ty0, tx1, ty1 = (rect[:, i].astype(np.int64) for i in range(4))
+    w = np.repeat(tx1 - tx0 + 1, n_tiles)
+    tx = np.repeat(tx0, n_tiles) + k % np.maximum(w, 1)
+    ty = np.repeat(ty0, n_tiles) + k // np.maximum(w, 1)
+    tile = ty * tiles_x + tx
+    keys = (tile.astype(np.uint64) << np.uint64(32)) | dbits.astype(np.uint64)[slot]
+    order = np.argsort(keys, kind="stable")
+    keys_sorted = keys[order]
+    vals_sorted = slot[order].astype(np.int32)
+    T = tiles_x * tiles_y
+    ranges = np.zeros((T, 2), np.int32)
+    tiles_sorted = (keys_sorted >> np.uint64(32)).astype(np.int64)
+    if M:
+        starts = np.searchsorted(tiles_sorted, np.arange(T), side="left")
+        ends = np.searchsorted(tiles_sorted, np.arange(T), side="right")
+        nonempty = ends > starts
+        ranges[nonempty, 0] = starts[nonempty]
+        ranges[nonempty, 1] = ends[nonempty]
+    return dict(offsets=offsets, num_instances=M, keys_emitted=keys, keys=keys_sorted, vals=vals_sorted,
+                ranges=ranges)
+
+
+def cap_score(conic_f32: np.ndarray, opacity_f32: np.ndarray) -> np.ndarray:
+    """score = o / sqrt(A*C - B*B) = o * sqrt(det of the dilated 2D covariance), in float32
+    with one rounding per operation (no contraction), so that it is a decision both
+    implementations take identically from the same float32 records."""
+    A = conic_f32[:, 0].astype(np.float32)
+    B = conic_f32[:, 1].astype(np.float32)
+    C = conic_f32[:, 2].astype(np.float32)
+    det = np.subtract(np.multiply(A, C, dtype=np.float32), np.multiply(B, B, dtype=np.float32), dtype=np.float32)
+    return np.divide(opacity_f32.astype(np.float32), np.sqrt(det, dtype=np.float32), dtype=np.float32)
+
+
+def cap_tiles(ranges: np.ndarray, vals: np.ndarray, score: np.ndarray, dbits: np.ndarray, K: int) -> dict:
+    """Per-tile cap (ByteSplat, arXiv 2610.02851, English abstract: pruning under per-tile
+    on-chip memory limits): in a tile with more than K entries keep the K best by
+    (score desc, depth asc, slot asc) and leave them in their depth order.
+    Parity: pinned by K >= longest list (identity), K = 1 (per-tile argmax) and a Python sort."""
+    T = ranges.shape[0]
+    out_vals = []
+    out_ranges = np.zeros((T, 2), np.int32)
+    pos = 0
+    for t in range(T):
+        s, e = int(ranges[t, 0]), int(ranges[t, 1])
+        lst = vals[s:e]
+        if e - s > K:
+            sc = score[lst]
+            d = dbits[lst]
+            order = np.lexsort((lst, d, -sc))  # last key is primary
+            keep = np.sort(order[:K])
+            lst = lst[keep]
+        if lst.size:
+            out_ranges[t] = (pos, pos + lst.size)
+            out_vals.append(lst)
+            pos += lst.size
+    vals_k = np.concatenate(out_vals).astype(np.int32) if out_vals else np.zeros(0, np.int32)
+    return dict(vals=vals_k, ranges=out_ranges, num_instances=int(vals_k.size))
+
+
+# ---------------------------------------------------------------------------------------
+# Rasterization
+# ---------------------------------------------------------------------------------------
+def _rec(records: dict):
+    return [np.ascontiguousarray(records[k], np.float64) for k in ("mean2d", "conic", "opacity", "color")]
+
+
+def raster_forward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray, records: dict, settings) -> dict:
+    """Front-to-back compositing of every pixel over its tile's list.
+
+    Per pixel: alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop before a
+    blend that takes T below t_min; C += alpha T c; T *= 1 - alpha; finally C += T bg.
+    Returns image (3,H,W), T_final (H,W), n_contrib (H,W), flag (H,W), err_C (H,W),
+    evaluated and blended pair counts.
+    Parity: pinned by the single-Gaussian profile, telescoping identities, a two-Gaussian
+    closed form and brute-force all-Gaussians-per-pixel compositing."""
+    lib = _load()
+    image = np.zeros((3, height, width))
+    T = np.zeros((height, width))
+    nc = np.zeros((height, width), np.int32)
+    flag = np.zeros((height, width), np.int8)
+    err = np.zeros((height, width))
+    counters = np.zeros(3, np.int64)
+    ranges = np.ascontiguousarray(ranges, np.int32)
+    vals = np.ascontiguousarray(vals, np.int32)
+    pp = _params(settings)
+    m, c, o, col = _rec(records)
+    lib.orc_raster_forward(ctypes.c_int32(width), ctypes.c_int32(height), _p(ranges), _p(vals), _p(m), _p(c), _p(o),
+                           _p(col), ctypes.byref(pp), _p(image), _p(T), _p(nc), _p(flag), _p(err), _p(counters))
+    return dict(image=image, T_final=T, n_contrib=nc, flag=flag.astype(bool), err_C=err,
+                n_evaluated=int(counters[0]), n_blended=int(counters[1]), n_clamped=int(counters[2]))
+
+
+def loss_grad_l1(image: np.ndarray, target: np.ndarray, scale: float, err_C: Optional[np.ndarray] = None):
+    """dL/dC of L = scale * sum |C - target|: scale * sign(C - target), sign(0) = 0.
+    Also returns the pixels whose sign float32 evaluation could decide differently."""
+    diff = image - target.astype(np.float64)
+    g = np.sign(diff) * scale
+    unsure = None
+    if err_C is not None:
+        unsure = (np.abs(diff) <= 4.0 * err_C[None] + 1e-12).any(axis=0)
+    return g, unsure
+
+
+def raster_backward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray, records: dict, settings,
+                    dldc: np.ndarray, pixel_skip: Optional[np.ndarray] = None) -> dict:
+    """Gradients of L with respect to the per-slot 2D records (means2D in pixels, conic
+    (A, B, C), activated opacity, post-clamp colour), by reverse traversal of each pixel's
+    blended entries.  Returns d_mean2d (S,2), d_conic (S,3), d_opacity (S,), d_color (S,3),
+    mag (S,9) = summed absolute contributions, slot_flag (S,).
+    Parity: pinned by central finite differences of the loss and closed-form derivatives."""
+    lib = _load()
+    S = records["opacity"].shape[0]
+    out = dict(d_mean2d=np.zeros((S, 2)), d_conic=np.zeros((S, 3)), d_opacity=np.zeros(S), d_color=np.zeros((S, 3)),
+               mag=np.zeros((S, 9)), slot_flag=np.zeros(S, np.int8))
+    ranges = np.ascontiguousarray(ranges, np.int32)
+    vals = np.ascontiguousarray(vals, np.int32)
+    dldc = np.ascontiguousarray(dldc, np.float64)
+    skip = None if pixel_skip is None else np.ascontiguousarray(pixel_skip, np.int8)
+    pp = _params(settings)
+    m, c, o, col = _rec(records)
+    lib.orc_raster_backward(ctypes.c_int32(width), ctypes.c_int32(height), _p(ranges), _p(vals), _p(m), _p(c), _p(o),
+                            _p(col), ctypes.byref(pp), _p(dldc), None if skip is None else _p(skip),
+                            _p(out["d_mean2d"]), _p(out["d_conic"]), _p(out["d_opacity"]), _p(out["d_color"]),
+                            _p(out["mag"]), _p(out["slot_flag"]))
+    out["slot_flag"] = out["slot_flag"].astype(bool)
+    return out
+
+
+def raster_bruteforce(width: int, height: int, order: np.ndarray, records: dict, settings) -> dict:
+    """All slots composited at every pixel in the given global order (no tiles)."""
+    lib = _load()
+    image = np.zeros((3, height, width))
+    T = np.zeros((height, width))
+    nc = np.zeros((height, width), np.int32)
+    order = np.ascontiguousarray(order, np.int32)
+    pp = _params(settings)
+    m, c, o, col = _rec(records)
+    lib.orc_raster_bruteforce(ctypes.c_int32(width), ctypes.c_int32(height), _p(order), ctypes.c_int32(order.size),
+                              _p(m), _p(c), _p(o), _p(col), ctypes.byref(pp), _p(image), _p(T), _p(nc))
+    return dict(image=image, T_final=T, n_contrib=nc)
+
+
+# ---------------------------------------------------------------------------------------
+# One iteration over all views
+# ---------------------------------------------------------------------------------------
+def iteration(scene, settings, loss_scale: float = 1.0, views=None, backward: bool = True) -> list:
+    """project -> compact -> bin (-> cap) -> forward -> loss gradient -> backward, per view.
+
+    The views of a batch are independent renders (Grendel, arXiv 2406.18533, English
+    abstract: batched training over several views); per-view 2D gradients are not summed."""
+    out = []
+    views = range(len(scene.cameras)) if views is None else views
+    for v in views:
+        cam = scene.cameras[v]
+        proj = project(scene, cam, settings)
+        rec = compact(proj)
+        dbits = depth_bits(rec["depth"])
+        bins = bin_tiles(rec["rect"], rec["n_tiles"], dbits, cam.tiles_x, cam.tiles_y)
+        ranges, vals = bins["ranges"], bins["vals"]
+        if settings.tile_cap > 0:
+            score = cap_score(rec["conic"].astype(np.float32), rec["opacity"].astype(np.float32))
+            capped = cap_tiles(ranges, vals, score, dbits, settings.tile_cap)
+            ranges, vals = capped["ranges"], capped["vals"]
+            bins["capped"] = capped
+        fwd = raster_forward(cam.width, cam.height, ranges, vals, rec, settings)
+        res = dict(view=v, proj=proj, rec=rec, bins=bins, fwd=fwd)
+        if backward:
+            if scene.loss == "l1":
+                g, unsure = loss_grad_l1(fwd["image"], scene.target[v], loss_scale, fwd["err_C"])
+            else:
+                g, unsure = scene.dldc[v].astype(np.float64), None
+            res["dldc"] = g
+            res["bwd"] = raster_backward(cam.width, cam.height, ranges, vals, rec, settings, g,
+                                         pixel_skip=(fwd["flag"] | unsure) if unsure is not None else fwd["flag"])
+        out.append(res)
+    return out

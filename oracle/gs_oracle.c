@@ -1,0 +1,540 @@
+/*
+ * gs_oracle.c -- CPU oracle for one training iteration of tile-based differentiable
+ * 3D Gaussian splatting.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline load this library.  It shares no code, header, table or constant with the HIP
+ * library: it is a plain, slow, double-precision definition of what the HIP path computes,
+ * written so that it can be checked against the mathematics by eye.
+ *
+ * The pages (ByteSplat arXiv 2610.02851; Grendel arXiv 2406.18533; GS-Scale arXiv
+ * 2509.15645; Splaxel arXiv 2606.18588) describe the systems built around this
+ * computation, not its formulas: none of them spells out the projection, compositing or
+ * backward equations.  Every formula below is therefore the plainest reading of standard
+ * EWA splatting with front-to-back alpha compositing, and each open constant (near plane,
+ * low-pass dilation, alpha bounds, transmittance cut-off) arrives as a parameter.
+ *
+ * Parity status of each function:
+ *   orc_sh_basis        pinned: scipy complex spherical harmonics converted to real form;
+ *                       orthonormality by quadrature.
+ *   orc_project         pinned: closed forms for on-axis and off-axis isotropic Gaussians,
+ *                       quaternion axis test, camera-frame equivalence, box brute force.
+ *   orc_raster_forward  pinned: single-Gaussian profile, telescoping identities,
+ *                       two-Gaussian closed form, brute-force all-Gaussians-per-pixel.
+ *   orc_raster_backward pinned: central finite differences of the loss, two-Gaussian and
+ *                       single-Gaussian closed-form derivatives.
+ *   The constants themselves (0.2, 0.3, 1/255, 0.99, 1e-4, 60 degree FOV) are readings that
+ *   no page fixes: parity unpinned for their values.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC gs_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int32_t width, height;
+    double fx, fy, cx, cy;
+    double R[9];      /* world -> camera rotation, row-major */
+    double t[3];      /* world -> camera translation */
+    double campos[3]; /* camera centre, world coordinates */
+} orc_camera;
+
+typedef struct {
+    double znear;     /* Gaussians with camera z <= znear are dropped */
+    double eps2d;     /* low-pass dilation added to the 2D covariance diagonal, px^2 */
+    double alpha_min; /* pairs with alpha below this are skipped */
+    double alpha_max; /* alpha is clamped to this */
+    double t_min;     /* a pixel stops before the blend that would take T below this */
+    double bg[3];     /* background colour */
+    int32_t sh_degree;
+    int32_t tile;     /* tile side in pixels */
+} orc_params;
+
+/* Unit roundoff of IEEE binary32, used only by the decision-margin model. */
+#define EPS32 5.9604644775390625e-08
+
+/* ------------------------------------------------------------------------------------- */
+/* Real orthonormal spherical harmonics, degree 0..3, index l*l + l + m, at unit vector d. */
+/* Cartesian forms of the textbook real basis (no Condon-Shortley phase).                 */
+/* ------------------------------------------------------------------------------------- */
+void orc_sh_basis(int degree, const double d[3], double* Y)
+{
+    const double x = d[0], y = d[1], z = d[2];
+    const double pi = 3.14159265358979323846;
+    Y[0] = 0.5 * sqrt(1.0 / pi);
+    if (degree < 1) return;
+    Y[1] = sqrt(3.0 / (4.0 * pi)) * y;
+    Y[2] = sqrt(3.0 / (4.0 * pi)) * z;
+    Y[3] = sqrt(3.0 / (4.0 * pi)) * x;
+    if (degree < 2) return;
+    Y[4] = 0.5 * sqrt(15.0 / pi) * x * y;
+    Y[5] = 0.5 * sqrt(15.0 / pi) * y * z;
+    Y[6] = 0.25 * sqrt(5.0 / pi) * (3.0 * z * z - 1.0);
+    Y[7] = 0.5 * sqrt(15.0 / pi) * x * z;
+    Y[8] = 0.25 * sqrt(15.0 / pi) * (x * x - y * y);
+    if (degree < 3) return;
+    Y[9] = 0.25 * sqrt(35.0 / (2.0 * pi)) * y * (3.0 * x * x - y * y);
+    Y[10] = 0.5 * sqrt(105.0 / pi) * x * y * z;
+    Y[11] = 0.25 * sqrt(21.0 / (2.0 * pi)) * y * (5.0 * z * z - 1.0);
+    Y[12] = 0.25 * sqrt(7.0 / pi) * z * (5.0 * z * z - 3.0);
+    Y[13] = 0.25 * sqrt(21.0 / (2.0 * pi)) * x * (5.0 * z * z - 1.0);
+    Y[14] = 0.25 * sqrt(105.0 / pi) * z * (x * x - y * y);
+    Y[15] = 0.25 * sqrt(35.0 / (2.0 * pi)) * x * (x * x - 3.0 * y * y);
+}
+
+/* Rotation matrix (row-major) of the unit quaternion (w, x, y, z). */
+static void quat_to_matrix(const double q[4], double M[9])
+{
+    const double w = q[0], x = q[1], y = q[2], z = q[3];
+    M[0] = 1.0 - 2.0 * (y * y + z * z);
+    M[1] = 2.0 * (x * y - w * z);
+    M[2] = 2.0 * (x * z + w * y);
+    M[3] = 2.0 * (x * y + w * z);
+    M[4] = 1.0 - 2.0 * (x * x + z * z);
+    M[5] = 2.0 * (y * z - w * x);
+    M[6] = 2.0 * (x * z - w * y);
+    M[7] = 2.0 * (y * z + w * x);
+    M[8] = 1.0 - 2.0 * (x * x + y * y);
+}
+
+/* Distance from v to the nearest integer. */
+static double frac_dist(double v)
+{
+    return fabs(v - nearbyint(v));
+}
+
+/*
+ * Projection of every Gaussian into one view (no compaction; the caller compacts).
+ *
+ * Inputs are the float32 parameter arrays in structure-of-arrays layout:
+ *   means[3][n], log_scales[3][n], quats[4][n] (w,x,y,z), opacity_logits[n],
+ *   sh[3*(deg+1)^2][n] with row k*3 + channel.
+ * Outputs per Gaussian i (double unless stated):
+ *   visible[i] (0/1), mean2d[i][2] (pixels), cov2d[i][3] = dilated 2D covariance (xx, xy, yy),
+ *   conic[i][3] = (A, B, C) with q = A dx^2 + 2 B dx dy + C dy^2, opacity[i], color[i][3],
+ *   depth[i] = camera-space z, rect[i][4] = (tx0, ty0, tx1, ty1) inclusive tile rectangle
+ *   (int32), n_tiles[i] (int32), flag[i] = 1 when a visibility or box decision lies so close
+ *   to its threshold that float32 arithmetic may decide it the other way.
+ */
+void orc_project(int64_t n, const float* means, const float* log_scales, const float* quats,
+                 const float* opacity_logits, const float* sh, const orc_camera* cam,
+                 const orc_params* p, int8_t* visible, double* mean2d, double* cov2d,
+                 double* conic, double* opacity, double* color, double* depth, int32_t* rect,
+                 int32_t* n_tiles, int8_t* flag)
+{
+    const int deg = p->sh_degree;
+    const int nk = (deg + 1) * (deg + 1);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        visible[i] = 0;
+        flag[i] = 0;
+        n_tiles[i] = 0;
+        rect[4 * i + 0] = rect[4 * i + 1] = rect[4 * i + 2] = rect[4 * i + 3] = 0;
+        mean2d[2 * i] = mean2d[2 * i + 1] = 0.0;
+        cov2d[3 * i] = cov2d[3 * i + 1] = cov2d[3 * i + 2] = 0.0;
+        conic[3 * i] = conic[3 * i + 1] = conic[3 * i + 2] = 0.0;
+        opacity[i] = 0.0;
+        color[3 * i] = color[3 * i + 1] = color[3 * i + 2] = 0.0;
+        depth[i] = 0.0;
+
+        double mu[3], ls[3], q[4];
+        for (int k = 0; k < 3; k++) mu[k] = means[k * n + i];
+        for (int k = 0; k < 3; k++) ls[k] = log_scales[k * n + i];
+        for (int k = 0; k < 4; k++) q[k] = quats[k * n + i];
+        const double logit = opacity_logits[i];
+        int finite = isfinite(logit);
+        for (int k = 0; k < 3; k++) finite = finite && isfinite(mu[k]) && isfinite(ls[k]);
+        for (int k = 0; k < 4; k++) finite = finite && isfinite(q[k]);
+        if (!finite) continue;
+
+        /* 1. activations */
+        const double o = 1.0 / (1.0 + exp(-logit));
+        double s[3];
+        for (int k = 0; k < 3; k++) s[k] = exp(ls[k]);
+        const double qn = sqrt(q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3]);
+        if (!(qn > 0.0)) continue;
+        for (int k = 0; k < 4; k++) q[k] /= qn;
+
+        /* 2. world -> camera, near cull */
+        double tc[3];
+        for (int r = 0; r < 3; r++)
+            tc[r] = cam->R[3 * r + 0] * mu[0] + cam->R[3 * r + 1] * mu[1] + cam->R[3 * r + 2] * mu[2] + cam->t[r];
+        if (fabs(tc[2] - p->znear) <= 1e-5 * fmax(1.0, fabs(tc[2]))) flag[i] = 1;
+        if (!(tc[2] > p->znear)) continue;
+
+        /* 3. world covariance Sigma = Rq diag(s^2) Rq^T */
+        double Rq[9], Sig[9];
+        quat_to_matrix(q, Rq);
+        for (int a = 0; a < 3; a++)
+            for (int b = 0; b < 3; b++) {
+                double acc = 0.0;
+                for (int k = 0; k < 3; k++) acc += Rq[3 * a + k] * s[k] * s[k] * Rq[3 * b + k];
+                Sig[3 * a + b] = acc;
+            }
+
+        /* 4. EWA: Sigma2D = J W Sigma W^T J^T, plus the low-pass dilation */
+        const double tz = tc[2];
+        double J[6] = {cam->fx / tz, 0.0, -cam->fx * tc[0] / (tz * tz),
+                       0.0, cam->fy / tz, -cam->fy * tc[1] / (tz * tz)};
+        double T[6]; /* T = J W, 2x3 */
+        for (int r = 0; r < 2; r++)
+            for (int c = 0; c < 3; c++) {
+                double acc = 0.0;
+                for (int k = 0; k < 3; k++) acc += J[3 * r + k] * cam->R[3 * k + c];
+                T[3 * r + c] = acc;
+            }
+        double S2[4]; /* T Sigma T^T, 2x2 */
+        for (int r = 0; r < 2; r++)
+            for (int c = 0; c < 2; c++) {
+                double acc = 0.0;
+                for (int a = 0; a < 3; a++)
+                    for (int b = 0; b < 3; b++) acc += T[3 * r + a] * Sig[3 * a + b] * T[3 * c + b];
+                S2[2 * r + c] = acc;
+            }
+        const double a = S2[0] + p->eps2d;
+        const double b = S2[1];
+        const double c = S2[3] + p->eps2d;
+        const double det = a * c - b * b;
+        if (!(det > 0.0) || !isfinite(det)) continue;
+        const double A = c / det, B = -b / det, C = a / det;
+
+        /* 5. projected centre, pixel (u, v) has its centre at (u + 1/2, v + 1/2) */
+        const double mx = cam->fx * tc[0] / tz + cam->cx;
+        const double my = cam->fy * tc[1] / tz + cam->cy;
+
+        /* 7. opacity-aware box: all pixels with o * exp(-q/2) >= alpha_min */
+        if (fabs(255.0 * o - 1.0) <= 1e-5) flag[i] = 1;
+        if (!(o * (1.0 / p->alpha_min) > 1.0)) continue;
+        const double Q = 2.0 * log(o / p->alpha_min);
+        const double ex = 1.001 * sqrt(Q * a);
+        const double ey = 1.001 * sqrt(Q * c);
+        const double lo_x = mx - ex - 0.5, hi_x = mx + ex - 0.5;
+        const double lo_y = my - ey - 0.5, hi_y = my + ey - 0.5;
+        if (!(isfinite(lo_x) && isfinite(hi_x) && isfinite(lo_y) && isfinite(hi_y))) continue;
+        const double mx_margin = 1e-3 + 4e-6 * (fabs(mx) + ex);
+        const double my_margin = 1e-3 + 4e-6 * (fabs(my) + ey);
+        if (frac_dist(lo_x) < mx_margin || frac_dist(hi_x) < mx_margin ||
+            frac_dist(lo_y) < my_margin || frac_dist(hi_y) < my_margin)
+            flag[i] = 1;
+        const double u0 = fmax(0.0, ceil(lo_x));
+        const double u1 = fmin((double)(cam->width - 1), floor(hi_x));
+        const double v0 = fmax(0.0, ceil(lo_y));
+        const double v1 = fmin((double)(cam->height - 1), floor(hi_y));
+        if (!(u0 <= u1) || !(v0 <= v1)) continue;
+
+        /* 6. colour from spherical harmonics along the viewing direction; DC taken as the
+         *    base colour, lower clamp at zero */
+        double dir[3] = {mu[0] - cam->campos[0], mu[1] - cam->campos[1], mu[2] - cam->campos[2]};
+        const double dn = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+        if (!(dn > 0.0)) continue;
+        for (int k = 0; k < 3; k++) dir[k] /= dn;
+        double Y[16];
+        orc_sh_basis(deg, dir, Y);
+        double col[3];
+        int col_ok = 1;
+        for (int ch = 0; ch < 3; ch++) {
+            double v = sh[(0 * 3 + ch) * n + i];
+            for (int k = 1; k < nk; k++) v += sh[(k * 3 + ch) * n + i] * Y[k];
+            if (!isfinite(v)) col_ok = 0;
+            col[ch] = v > 0.0 ? v : 0.0;
+        }
+        if (!col_ok) continue;
+
+        /* 8. outputs */
+        const int tile = p->tile;
+        const int tx0 = (int)u0 / tile, tx1 = (int)u1 / tile;
+        const int ty0 = (int)v0 / tile, ty1 = (int)v1 / tile;
+        visible[i] = 1;
+        mean2d[2 * i] = mx;
+        mean2d[2 * i + 1] = my;
+        cov2d[3 * i] = a;
+        cov2d[3 * i + 1] = b;
+        cov2d[3 * i + 2] = c;
+        conic[3 * i] = A;
+        conic[3 * i + 1] = B;
+        conic[3 * i + 2] = C;
+        opacity[i] = o;
+        for (int ch = 0; ch < 3; ch++) color[3 * i + ch] = col[ch];
+        depth[i] = tz;
+        rect[4 * i + 0] = tx0;
+        rect[4 * i + 1] = ty0;
+        rect[4 * i + 2] = tx1;
+        rect[4 * i + 3] = ty1;
+        n_tiles[i] = (tx1 - tx0 + 1) * (ty1 - ty0 + 1);
+    }
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* Rasterization                                                                          */
+/* ------------------------------------------------------------------------------------- */
+
+/* The 2D records the rasterizer reads, indexed by visible slot (double precision). */
+typedef struct {
+    const double* mean2d;  /* [slots][2] */
+    const double* conic;   /* [slots][3] */
+    const double* opacity; /* [slots] */
+    const double* color;   /* [slots][3] */
+} orc_records;
+
+/* One blended entry of a pixel's walk, kept for the backward pass. */
+typedef struct {
+    int32_t j;        /* position in the tile list */
+    int32_t slot;
+    double alpha;     /* alpha used for blending */
+    double T;         /* transmittance in front of this entry */
+    double G;         /* exp(-q/2) */
+    double dx, dy;    /* pixel centre minus projected centre */
+    int clamped;      /* 1 if o*G exceeded alpha_max */
+} orc_blend;
+
+/*
+ * Front-to-back compositing of one pixel over its tile list.
+ * Writes C[3], returns n_contrib; *T_out = final transmittance.  When log != NULL, the
+ * blended entries are appended to log (capacity n).  *flag is set when a decision (alpha
+ * against alpha_min, the transmittance cut-off, alpha against alpha_max) lies within the
+ * error that float32 evaluation of the same formulas can make, so that float32 code may
+ * decide it differently.  Counters: evaluated pairs; n_blend[0] blended pairs and n_blend[1]
+ * blended pairs with a clamped alpha.  touch[j] (optional,
+ * per list position) marks the evaluated entries whose alpha reaches alpha_min within that
+ * error: the entries whose gradient at this pixel a flipped decision can change.
+ */
+static int composite_pixel(double px, double py, const int32_t* list, int n, const orc_records* r,
+                           const orc_params* p, double C[3], double* T_out, orc_blend* log,
+                           int* n_log, int* flag, int* flag_clamp, int64_t* n_eval, int64_t* n_blend,
+                           double* err_C, int8_t* touch)
+{
+    double T = 1.0;
+    double errT = 0.0;   /* relative error model of T in float32 */
+    double eC = 0.0;     /* absolute error model of C (any channel) in float32 */
+    int n_contrib = 0;
+    C[0] = C[1] = C[2] = 0.0;
+    if (n_log) *n_log = 0;
+    for (int j = 0; j < n; j++) {
+        const int s = list[j];
+        const double dx = px - r->mean2d[2 * s];
+        const double dy = py - r->mean2d[2 * s + 1];
+        const double A = r->conic[3 * s], B = r->conic[3 * s + 1], Cc = r->conic[3 * s + 2];
+        const double q = A * dx * dx + 2.0 * B * dx * dy + Cc * dy * dy;
+        const double G = exp(-0.5 * q);
+        const double o = r->opacity[s];
+        const double v = o * G;
+        const double alpha = v < p->alpha_max ? v : p->alpha_max;
+        if (n_eval) (*n_eval)++;
+        /* float32 error model: q carries ~8 ulp of its absolute-term sum, exp adds a few ulp */
+        const double qabs = fabs(A) * dx * dx + 2.0 * fabs(B * dx * dy) + fabs(Cc) * dy * dy;
+        const double rel_a = 0.5 * 8.0 * EPS32 * qabs + 4.0 * EPS32;
+        if (fabs(v - p->alpha_min) <= 4.0 * rel_a * p->alpha_min + 1e-12) *flag = 1;
+        if (fabs(v - p->alpha_max) <= 4.0 * rel_a * p->alpha_max + 1e-12) *flag_clamp = 1;
+        if (touch) touch[j] = (int8_t)(v >= p->alpha_min * (1.0 - 4.0 * rel_a) - 1e-12);
+        if (alpha < p->alpha_min) continue;
+        const double Tn = T * (1.0 - alpha);
+        const double rel_1ma = (alpha * rel_a + EPS32) / (1.0 - alpha);
+        const double errTn = errT + rel_1ma + EPS32;
+        if (fabs(Tn - p->t_min) <= 4.0 * errTn * p->t_min + 1e-15) *flag = 1;
+        if (Tn < p->t_min) break;
+        for (int ch = 0; ch < 3; ch++) C[ch] += alpha * T * r->color[3 * s + ch];
+        {
+            double cmax = fmax(fabs(r->color[3 * s]), fmax(fabs(r->color[3 * s + 1]), fabs(r->color[3 * s + 2])));
+            eC += alpha * T * cmax * (rel_a + errT + 3.0 * EPS32) + fabs(C[0] + C[1] + C[2]) * EPS32;
+        }
+        if (log) {
+            orc_blend* e = &log[*n_log];
+            e->j = j;
+            e->slot = s;
+            e->alpha = alpha;
+            e->T = T;
+            e->G = G;
+            e->dx = dx;
+            e->dy = dy;
+            e->clamped = !(v <= p->alpha_max);
+            (*n_log)++;
+        }
+        if (n_blend) {
+            (*n_blend)++;
+            if (!(v <= p->alpha_max)) n_blend[1]++;
+        }
+        T = Tn;
+        errT = errTn;
+        n_contrib = j + 1;
+    }
+    for (int ch = 0; ch < 3; ch++) C[ch] += T * p->bg[ch];
+    eC += T * fmax(fabs(p->bg[0]), fmax(fabs(p->bg[1]), fabs(p->bg[2]))) * (errT + EPS32);
+    if (err_C) *err_C = eC;
+    *T_out = T;
+    return n_contrib;
+}
+
+/*
+ * Forward rasterization of one view.
+ * ranges[tile][2] = [start, end) into vals; vals[] = slot of each list entry; tiles are
+ * row-major with tiles_x = ceil(W / tile).  Outputs: image[3][H][W], T_final[H][W],
+ * n_contrib[H][W], flag[H][W] (decision within float32 reach), err_C[H][W] (float32 error
+ * model of the colour), counters[3] = {evaluated pairs, blended pairs, blended pairs whose
+ * alpha was clamped}.
+ */
+void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals,
+                        const double* mean2d, const double* conic, const double* opacity,
+                        const double* color, const orc_params* p, double* image, double* T_final,
+                        int32_t* n_contrib, int8_t* flag, double* err_C, int64_t* counters)
+{
+    const int tile = p->tile;
+    const int tx_n = (W + tile - 1) / tile, ty_n = (H + tile - 1) / tile;
+    const orc_records r = {mean2d, conic, opacity, color};
+    int64_t tot_eval = 0, tot_blend = 0, tot_clamp = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : tot_eval, tot_blend, tot_clamp)
+    for (int t = 0; t < tx_n * ty_n; t++) {
+        const int tx = t % tx_n, ty = t / tx_n;
+        const int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+        for (int y = ty * tile; y < (ty + 1) * tile && y < H; y++)
+            for (int x = tx * tile; x < (tx + 1) * tile && x < W; x++) {
+                double C[3], T, eC;
+                int f = 0, fc = 0;
+                int64_t ne = 0, nb[2] = {0, 0};
+                const int nc = composite_pixel(x + 0.5, y + 0.5, vals + start, end - start, &r, p, C, &T,
+                                               NULL, NULL, &f, &fc, &ne, nb, &eC, NULL);
+                const int64_t px = (int64_t)y * W + x;
+                for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = C[ch];
+                T_final[px] = T;
+                n_contrib[px] = nc;
+                flag[px] = (int8_t)(f ? 1 : 0);
+                err_C[px] = eC;
+                tot_eval += ne;
+                tot_blend += nb[0];
+                tot_clamp += nb[1];
+            }
+    }
+    counters[0] = tot_eval;
+    counters[1] = tot_blend;
+    counters[2] = tot_clamp;
+}
+
+/*
+ * Backward rasterization of one view: gradients of L with respect to the per-slot 2D
+ * records, given dL/dC (dldc[3][H][W]).  The forward walk of each pixel is recomputed with
+ * its blend log, then the log is traversed from the last blended entry to the first:
+ *   dL/dc_j     += alpha_j T_j g
+ *   dL/dalpha_j  = sum_ch g_ch (T_j (c_j,ch - Bk_ch) - T_final bg_ch / (1 - alpha_j))
+ *   Bk          <- alpha_j c_j + (1 - alpha_j) Bk           (colour behind entry j)
+ * and, unless alpha was clamped (o G > alpha_max),
+ *   dL/do       += G dL/dalpha
+ *   dL/dmean2d  += o G dL/dalpha (A dx + B dy, B dx + C dy)   with d = pixel - mean2d
+ *   dL/dconic   += o G dL/dalpha (-dx^2/2, -dx dy, -dy^2/2).
+ * Outputs (double, accumulated over the view's pixels): d_mean2d[slots][2],
+ * d_conic[slots][3], d_opacity[slots], d_color[slots][3]; mag[slots][9] = sum of the
+ * absolute values of the same contributions; slot_flag[slots] = 1 when the slot was
+ * evaluated at a pixel whose decisions (including the clamp) lie within float32 reach.
+ * Output arrays must be zeroed by the caller.
+ */
+void orc_raster_backward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals,
+                         const double* mean2d, const double* conic, const double* opacity,
+                         const double* color, const orc_params* p, const double* dldc,
+                         const int8_t* pixel_skip, double* d_mean2d, double* d_conic,
+                         double* d_opacity, double* d_color, double* mag, int8_t* slot_flag)
+{
+    const int tile = p->tile;
+    const int tx_n = (W + tile - 1) / tile, ty_n = (H + tile - 1) / tile;
+    const orc_records r = {mean2d, conic, opacity, color};
+    int max_n = 0;
+    for (int t = 0; t < tx_n * ty_n; t++)
+        if (ranges[2 * t + 1] - ranges[2 * t] > max_n) max_n = ranges[2 * t + 1] - ranges[2 * t];
+#pragma omp parallel
+    {
+        orc_blend* log = (orc_blend*)malloc(sizeof(orc_blend) * (size_t)(max_n > 0 ? max_n : 1));
+        int8_t* touch = (int8_t*)calloc((size_t)(max_n > 0 ? max_n : 1), 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < tx_n * ty_n; t++) {
+            const int tx = t % tx_n, ty = t / tx_n;
+            const int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
+            const int32_t* list = vals + start;
+            for (int y = ty * tile; y < (ty + 1) * tile && y < H; y++)
+                for (int x = tx * tile; x < (tx + 1) * tile && x < W; x++) {
+                    const int64_t px = (int64_t)y * W + x;
+                    double C[3], T_fin;
+                    int f = 0, fc = 0, nl = 0;
+                    int64_t n_evaluated = 0;
+                    composite_pixel(x + 0.5, y + 0.5, list, end - start, &r, p, C, &T_fin, log, &nl, &f, &fc,
+                                    &n_evaluated, NULL, NULL, touch);
+                    if (f || fc || (pixel_skip && pixel_skip[px])) {
+                        /* the slots this pixel blends, or could blend under float32 decisions */
+                        for (int j = 0; j < (int)n_evaluated; j++)
+                            if (touch[j]) {
+#pragma omp atomic write
+                                slot_flag[list[j]] = 1;
+                            }
+                    }
+                    double g[3];
+                    for (int ch = 0; ch < 3; ch++) g[ch] = dldc[(int64_t)ch * W * H + px];
+                    double Bk[3] = {0.0, 0.0, 0.0};
+                    for (int e = nl - 1; e >= 0; e--) {
+                        const orc_blend* b = &log[e];
+                        const int s = b->slot;
+                        const double* c = &color[3 * s];
+                        double dL_dalpha = 0.0;
+                        for (int ch = 0; ch < 3; ch++) {
+                            const double dc = b->alpha * b->T * g[ch];
+#pragma omp atomic
+                            d_color[3 * s + ch] += dc;
+#pragma omp atomic
+                            mag[9 * s + 6 + ch] += fabs(dc);
+                            dL_dalpha += g[ch] * (b->T * (c[ch] - Bk[ch]) - T_fin * p->bg[ch] / (1.0 - b->alpha));
+                        }
+                        for (int ch = 0; ch < 3; ch++) Bk[ch] = b->alpha * c[ch] + (1.0 - b->alpha) * Bk[ch];
+                        if (b->clamped) continue;
+                        const double o = opacity[s];
+                        const double A = conic[3 * s], B = conic[3 * s + 1], Cc = conic[3 * s + 2];
+                        const double gh = o * b->G * dL_dalpha; /* dL/dalpha * dalpha/dG * G */
+                        const double v[6] = {
+                            gh * (A * b->dx + B * b->dy),       /* d mean2d x */
+                            gh * (B * b->dx + Cc * b->dy),      /* d mean2d y */
+                            -0.5 * gh * b->dx * b->dx,          /* d A */
+                            -gh * b->dx * b->dy,                /* d B */
+                            -0.5 * gh * b->dy * b->dy,          /* d C */
+                            b->G * dL_dalpha};                  /* d opacity */
+#pragma omp atomic
+                        d_mean2d[2 * s] += v[0];
+#pragma omp atomic
+                        d_mean2d[2 * s + 1] += v[1];
+#pragma omp atomic
+                        d_conic[3 * s] += v[2];
+#pragma omp atomic
+                        d_conic[3 * s + 1] += v[3];
+#pragma omp atomic
+                        d_conic[3 * s + 2] += v[4];
+#pragma omp atomic
+                        d_opacity[s] += v[5];
+                        for (int k = 0; k < 6; k++) {
+#pragma omp atomic
+                            mag[9 * s + k] += fabs(v[k]);
+                        }
+                    }
+                }
+        }
+        free(log);
+        free(touch);
+    }
+}
+
+/*
+ * Per-pixel brute force (no tiles): composite every slot in the given global order
+ * (the caller passes slots sorted by depth, then slot).  Used only to pin the tiled path.
+ */
+void orc_raster_bruteforce(int32_t W, int32_t H, const int32_t* order, int32_t n, const double* mean2d,
+                           const double* conic, const double* opacity, const double* color,
+                           const orc_params* p, double* image, double* T_final, int32_t* n_contrib)
+{
+    const orc_records r = {mean2d, conic, opacity, color};
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int y = 0; y < H; y++)
+        for (int x = 0; x < W; x++) {
+            double C[3], T;
+            int f = 0, fc = 0;
+            const int nc = composite_pixel(x + 0.5, y + 0.5, order, n, &r, p, C, &T, NULL, NULL, &f, &fc, NULL,
+                                           NULL, NULL, NULL);
+            const int64_t px = (int64_t)y * W + x;
+            for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = C[ch];
+            T_final[px] = T;
+            n_contrib[px] = nc; /* position in the global order, not in a tile list */
+        }
+}
