@@ -1,0 +1,431 @@
+// Host side of the C ABI in gsmi.h: argument validation (before anything is enqueued),
+// workspace carving, the single count read-back of gs_bin_tiles, and launch orchestration.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.h"
+
+using namespace gsmi;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gs_status fail(gs_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+gs_status hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return GS_OK;
+    return fail(GS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+    char* base;
+    size_t used = 0;
+    explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+        used += align256(sizeof(T) * count);
+        return p;
+    }
+};
+
+int tiles_along(int px) { return (px + kTile - 1) / kTile; }
+
+gs_status check_cams(const gs_camera* cams, int32_t V) {
+    if (!cams) return fail(GS_ERR_INVALID_ARGUMENT, "cams is null");
+    if (V < 1 || V > GS_MAX_VIEWS) return fail(GS_ERR_INVALID_ARGUMENT, "V=%d outside 1..%d", V, GS_MAX_VIEWS);
+    for (int v = 0; v < V; v++) {
+        const gs_camera& c = cams[v];
+        if (c.width <= 0 || c.height <= 0 || c.width > 65535 * kTile || c.height > 65535 * kTile)
+            return fail(GS_ERR_INVALID_ARGUMENT, "view %d: image size %dx%d", v, c.width, c.height);
+        if (c.width != cams[0].width || c.height != cams[0].height)
+            return fail(GS_ERR_INVALID_ARGUMENT, "view %d: image size differs from view 0", v);
+        if ((int64_t)tiles_along(c.width) * tiles_along(c.height) * V >= (int64_t(1) << 31))
+            return fail(GS_ERR_INVALID_ARGUMENT, "too many tiles");
+    }
+    return GS_OK;
+}
+
+gs_status check_params(const gs_render_params* p) {
+    if (!p) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+    if (p->sh_degree < 0 || p->sh_degree > 3) return fail(GS_ERR_INVALID_ARGUMENT, "sh_degree=%d", p->sh_degree);
+    if (p->tile_cap < 0) return fail(GS_ERR_INVALID_ARGUMENT, "tile_cap=%d", p->tile_cap);
+    if (!(p->alpha_min > 0.0f) || !(p->alpha_max <= 1.0f) || !(p->alpha_min < p->alpha_max) || !(p->alpha_max < 1.0f))
+        return fail(GS_ERR_INVALID_ARGUMENT, "alpha bounds must satisfy 0 < alpha_min < alpha_max < 1");
+    if (!(p->t_min >= 0.0f) || !(p->t_min < 1.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "t_min outside [0, 1)");
+    if (!(p->eps2d >= 0.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "eps2d < 0");
+    return GS_OK;
+}
+
+CamArray to_dev(const gs_camera* cams, int32_t V) {
+    CamArray a;
+    std::memset(&a, 0, sizeof(a));
+    for (int v = 0; v < V; v++) {
+        CamDev& d = a.c[v];
+        d.width = cams[v].width;
+        d.height = cams[v].height;
+        d.tiles_x = tiles_along(cams[v].width);
+        d.tiles_y = tiles_along(cams[v].height);
+        d.fx = cams[v].fx;
+        d.fy = cams[v].fy;
+        d.cx = cams[v].cx;
+        d.cy = cams[v].cy;
+        std::memcpy(d.R, cams[v].R, sizeof(d.R));
+        std::memcpy(d.t, cams[v].t, sizeof(d.t));
+        std::memcpy(d.campos, cams[v].campos, sizeof(d.campos));
+    }
+    return a;
+}
+
+ParamsDev to_dev(const gs_render_params* p) {
+    ParamsDev d;
+    d.znear = p->znear;
+    d.eps2d = p->eps2d;
+    d.alpha_min = p->alpha_min;
+    d.alpha_max = p->alpha_max;
+    d.t_min = p->t_min;
+    d.bg[0] = p->bg[0];
+    d.bg[1] = p->bg[1];
+    d.bg[2] = p->bg[2];
+    d.sh_degree = p->sh_degree;
+    d.tile_cap = p->tile_cap;
+    return d;
+}
+
+gs_status check_projected(const gs_projected* pr, bool records) {
+    if (!pr) return fail(GS_ERR_INVALID_ARGUMENT, "projected is null");
+    if (pr->capacity < 0) return fail(GS_ERR_INVALID_ARGUMENT, "projected capacity < 0");
+    if (!pr->vis_count || !pr->inst_count) return fail(GS_ERR_INVALID_ARGUMENT, "projected counts are null");
+    if (records && (!pr->mean2d || !pr->conic_opacity || !pr->color))
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected records are null");
+    return GS_OK;
+}
+
+// Workspace layout of gs_bin_tiles.
+struct BinWs {
+    uint32_t *dkey, *dval, *dkey_alt, *dval_alt;
+    int32_t *ntiles_sorted, *offsets;
+    uint32_t *tkey_alt, *tval_alt;
+    int32_t *hist, *partials;
+    int32_t *kept, *cap_offsets;
+};
+
+BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t inst_cap, size_t* bytes) {
+    Carver c(ws);
+    const int64_t nv = (int64_t)n * V;
+    const int32_t sort_n = (int32_t)(nv > inst_cap ? nv : inst_cap);
+    BinWs w;
+    w.dkey = c.take<uint32_t>(nv);
+    w.dval = c.take<uint32_t>(nv);
+    w.dkey_alt = c.take<uint32_t>(nv);
+    w.dval_alt = c.take<uint32_t>(nv);
+    w.ntiles_sorted = c.take<int32_t>(nv);
+    w.offsets = c.take<int32_t>(nv);
+    w.tkey_alt = c.take<uint32_t>(inst_cap);
+    w.tval_alt = c.take<uint32_t>(inst_cap);
+    w.hist = c.take<int32_t>(radix_hist_bytes(sort_n) / sizeof(int32_t));
+    size_t part = radix_partials_bytes(sort_n);
+    const size_t p2 = scan_partials_bytes((int32_t)(nv > 0 ? nv : 1), 1);
+    const size_t p3 = scan_partials_bytes(tiles_total, 1);
+    if (p2 > part) part = p2;
+    if (p3 > part) part = p3;
+    w.partials = c.take<int32_t>(part / sizeof(int32_t));
+    w.kept = c.take<int32_t>(tiles_total);
+    w.cap_offsets = c.take<int32_t>(tiles_total);
+    *bytes = c.used;
+    return w;
+}
+
+int bits_for(int64_t count) {
+    int b = 1;
+    while ((int64_t(1) << b) < count) b++;
+    return b;
+}
+
+gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs_bins* bins, int32_t V,
+                       const gs_render_params* p, int32_t use_capped, RasterArgs* ra) {
+    gs_status st = check_cams(cams, V);
+    if (st != GS_OK) return st;
+    if ((st = check_params(p)) != GS_OK) return st;
+    if ((st = check_projected(proj, true)) != GS_OK) return st;
+    if (!bins) return fail(GS_ERR_INVALID_ARGUMENT, "bins is null");
+    const int32_t* ranges = use_capped ? bins->ranges_capped : bins->ranges;
+    const int32_t* vals = use_capped ? bins->vals_capped : bins->vals;
+    if (!ranges || !vals) return fail(GS_ERR_INVALID_ARGUMENT, "bins ranges/vals are null");
+    ra->V = V;
+    ra->width = cams[0].width;
+    ra->height = cams[0].height;
+    ra->tiles_x = tiles_along(cams[0].width);
+    ra->tiles_y = tiles_along(cams[0].height);
+    ra->capacity = proj->capacity;
+    ra->p = to_dev(p);
+    ra->ranges = ranges;
+    ra->vals = vals;
+    ra->mean2d = reinterpret_cast<const float2*>(proj->mean2d);
+    ra->conic_opacity = reinterpret_cast<const float4*>(proj->conic_opacity);
+    ra->color = proj->color;
+    ra->vis_count = proj->vis_count;
+    ra->counters = nullptr;
+    return GS_OK;
+}
+
+gs_status check_grads(const gs_grads2d* g, Grads* out) {
+    if (!g || !g->d_mean2d || !g->d_conic || !g->d_opacity || !g->d_color)
+        return fail(GS_ERR_INVALID_ARGUMENT, "gradient outputs are null");
+    out->d_mean2d = reinterpret_cast<float2*>(g->d_mean2d);
+    out->d_conic = g->d_conic;
+    out->d_opacity = g->d_opacity;
+    out->d_color = g->d_color;
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gs_version(void) { return "gsmi 0.1 (gfx950)"; }
+
+const char* gs_status_string(gs_status s) {
+    switch (s) {
+        case GS_OK: return "ok";
+        case GS_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GS_ERR_CAPACITY: return "capacity exceeded";
+        case GS_ERR_UNSUPPORTED: return "unsupported";
+        case GS_ERR_HIP: return "HIP runtime error";
+        case GS_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+const char* gs_last_error(void) { return g_last_error.c_str(); }
+
+size_t gs_project_workspace_size(int32_t n, int32_t V) {
+    if (n < 0 || V < 1) return 0;
+    return project_ws_bytes(n, V);
+}
+
+gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
+                     gs_projected* out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!g) return fail(GS_ERR_INVALID_ARGUMENT, "gaussians is null");
+    gs_status st = check_cams(cams, V);
+    if (st != GS_OK) return st;
+    if ((st = check_params(p)) != GS_OK) return st;
+    if (g->n < 0 || g->n >= (1 << 28)) return fail(GS_ERR_INVALID_ARGUMENT, "n=%d outside [0, 2^28)", g->n);
+    if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
+        return fail(GS_ERR_INVALID_ARGUMENT, "a parameter array is null");
+    if ((st = check_projected(out, true)) != GS_OK) return st;
+    if (!out->vis_ids || !out->depth || !out->tile_rect || !out->n_tiles)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected outputs are null");
+    if (out->capacity < g->n) return fail(GS_ERR_INVALID_ARGUMENT, "capacity %d < n %d", out->capacity, g->n);
+    if ((int64_t)out->capacity * V >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARGUMENT, "capacity * V must stay below 2^31");
+    const size_t need = project_ws_bytes(g->n, V);
+    if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "project workspace %zu < %zu bytes", ws_bytes, need);
+    ProjectArgs a;
+    a.n = g->n;
+    a.V = V;
+    a.capacity = out->capacity;
+    a.means = g->means;
+    a.log_scales = g->log_scales;
+    a.quats = g->quats;
+    a.logits = g->opacity_logits;
+    a.sh = g->sh;
+    a.cams = to_dev(cams, V);
+    a.p = to_dev(p);
+    a.vis_count = out->vis_count;
+    a.inst_count = out->inst_count;
+    a.vis_ids = out->vis_ids;
+    a.mean2d = reinterpret_cast<float2*>(out->mean2d);
+    a.conic_opacity = reinterpret_cast<float4*>(out->conic_opacity);
+    a.color = out->color;
+    a.depth = out->depth;
+    a.tile_rect = reinterpret_cast<ushort4*>(out->tile_rect);
+    a.n_tiles = out->n_tiles;
+    const int32_t nb = (g->n + 255) / 256 > 0 ? (g->n + 255) / 256 : 1;
+    Carver c(ws);
+    a.block_counts = c.take<int32_t>((size_t)nb * V);
+    a.block_offsets = c.take<int32_t>((size_t)nb * V);
+    a.scan_partials = c.take<int32_t>(scan_partials_bytes(nb, V) / sizeof(int32_t));
+    return hip_check(launch_project(a, static_cast<hipStream_t>(stream)), "gs_project launch");
+}
+
+size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height, int64_t instance_capacity) {
+    if (n < 0 || V < 1 || width <= 0 || height <= 0 || instance_capacity < 0) return 0;
+    size_t bytes = 0;
+    carve_bin(nullptr, n, V, tiles_along(width) * tiles_along(height) * V, instance_capacity, &bytes);
+    return bytes;
+}
+
+gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t V, const gs_render_params* p,
+                       gs_bins* bins, gs_bin_info* info, int64_t* required, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    gs_status st = check_cams(cams, V);
+    if (st != GS_OK) return st;
+    if ((st = check_params(p)) != GS_OK) return st;
+    if ((st = check_projected(proj, true)) != GS_OK) return st;
+    if (!proj->depth || !proj->tile_rect || !proj->n_tiles)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected depth/rect/n_tiles are null");
+    if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges)
+        return fail(GS_ERR_INVALID_ARGUMENT, "bins outputs are null");
+    if (p->tile_cap > 0 && (!bins->vals_capped || !bins->ranges_capped || !bins->num_capped))
+        return fail(GS_ERR_INVALID_ARGUMENT, "capped outputs are null while tile_cap > 0");
+    if (!info) return fail(GS_ERR_INVALID_ARGUMENT, "info is null");
+    if (bins->capacity < 0 || bins->capacity >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARGUMENT, "bins capacity outside [0, 2^31)");
+    const int tiles_x = tiles_along(cams[0].width), tiles_y = tiles_along(cams[0].height);
+    const int32_t tpv = tiles_x * tiles_y;
+    const int32_t tiles_total = tpv * V;
+    size_t need = 0;
+    carve_bin(nullptr, proj->capacity, V, tiles_total, bins->capacity, &need);
+    if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "bin workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // the one read-back: visible and instance counts of every view
+    int32_t vis[GS_MAX_VIEWS];
+    int64_t inst[GS_MAX_VIEWS];
+    if ((st = hip_check(hipMemcpyAsync(vis, proj->vis_count, sizeof(int32_t) * V, hipMemcpyDeviceToHost, s),
+                        "count read")) != GS_OK)
+        return st;
+    if ((st = hip_check(hipMemcpyAsync(inst, proj->inst_count, sizeof(int64_t) * V, hipMemcpyDeviceToHost, s),
+                        "count read")) != GS_OK)
+        return st;
+    if ((st = hip_check(hipStreamSynchronize(s), "count read sync")) != GS_OK) return st;
+    std::memset(info, 0, sizeof(*info));
+    int64_t total_vis = 0, M = 0;
+    for (int v = 0; v < V; v++) {
+        if (vis[v] < 0 || vis[v] > proj->capacity || inst[v] < 0)
+            return fail(GS_ERR_INTERNAL, "view %d: implausible counts (%d, %lld)", v, vis[v], (long long)inst[v]);
+        info->vis_count[v] = vis[v];
+        info->view_offset[v] = M;
+        total_vis += vis[v];
+        M += inst[v];
+    }
+    info->view_offset[V] = M;
+    info->num_instances = M;
+    info->num_instances_capped = p->tile_cap > 0 ? -1 : M;
+    if (required) *required = M;
+    if (M >= (int64_t(1) << 31)) return fail(GS_ERR_CAPACITY, "%lld instances exceed 2^31 - 1", (long long)M);
+    if (M > bins->capacity)
+        return fail(GS_ERR_CAPACITY, "%lld instances exceed the bins capacity %lld", (long long)M,
+                    (long long)bins->capacity);
+
+    BinWs w = carve_bin(ws, proj->capacity, V, tiles_total, bins->capacity, &need);
+    hipError_t e = launch_fill_i32(bins->ranges, 0, 2 * (int64_t)tiles_total, s);
+    if (e == hipSuccess && M > 0) {
+        // depth digits, one entry per visible slot
+        int64_t first[GS_MAX_VIEWS + 1];
+        int64_t acc = 0;
+        for (int v = 0; v < V; v++) {
+            first[v] = acc;
+            acc += vis[v];
+        }
+        first[V] = acc;
+        const int32_t nvis = (int32_t)total_vis;
+        e = launch_depth_keys(proj->depth, proj->vis_count, first, V, proj->capacity, nvis, w.dkey, w.dval, s);
+        if (e == hipSuccess) e = launch_radix_sort(w.dkey, w.dval, w.dkey_alt, w.dval_alt, nvis, 32, w.hist, w.partials, s);
+        uint32_t* packed = (radix_passes(32) % 2 == 0) ? w.dval : w.dval_alt;
+        if (e == hipSuccess) e = launch_gather_ntiles(packed, proj->n_tiles, proj->capacity, nvis, w.ntiles_sorted, s);
+        if (e == hipSuccess) e = launch_scan_rows(w.ntiles_sorted, w.offsets, nullptr, nvis, 1, w.partials, s);
+        // emit so that the tile sort's final pass lands in the output buffers
+        const int tbits = bits_for(tiles_total);
+        const bool odd = radix_passes(tbits) % 2 == 1;
+        uint32_t* k0 = odd ? w.tkey_alt : bins->tile_keys;
+        uint32_t* v0 = odd ? w.tval_alt : reinterpret_cast<uint32_t*>(bins->vals);
+        uint32_t* k1 = odd ? bins->tile_keys : w.tkey_alt;
+        uint32_t* v1 = odd ? reinterpret_cast<uint32_t*>(bins->vals) : w.tval_alt;
+        if (e == hipSuccess)
+            e = launch_emit(packed, w.offsets, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity, nvis,
+                            tiles_x, tpv, (int32_t)M, k0, reinterpret_cast<int32_t*>(v0), s);
+        if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
+        if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);
+    }
+    if (e == hipSuccess && p->tile_cap > 0) {
+        e = launch_cap_count(bins->ranges, tiles_total, p->tile_cap, w.kept, s);
+        if (e == hipSuccess) e = launch_scan_rows(w.kept, w.cap_offsets, bins->num_capped, tiles_total, 1, w.partials, s);
+        if (e == hipSuccess)
+            e = launch_cap_select(bins->ranges, bins->vals, reinterpret_cast<const float4*>(proj->conic_opacity),
+                                  proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets, bins->vals_capped,
+                                  bins->ranges_capped, w.tkey_alt, s);
+    }
+    return hip_check(e, "gs_bin_tiles launch");
+}
+
+gs_status gs_raster_fwd(const gs_camera* cams, const gs_projected* proj, const gs_bins* bins, int32_t V,
+                        const gs_render_params* p, int32_t use_capped, float* image, float* t_final,
+                        int32_t* n_contrib, gs_counters* counters, void* stream) {
+    g_last_error.clear();
+    RasterArgs ra;
+    gs_status st = check_raster(cams, proj, bins, V, p, use_capped, &ra);
+    if (st != GS_OK) return st;
+    if (!image || !t_final || !n_contrib) return fail(GS_ERR_INVALID_ARGUMENT, "forward outputs are null");
+    ra.counters = counters;
+    return hip_check(launch_raster_fwd(ra, image, t_final, n_contrib, static_cast<hipStream_t>(stream)),
+                     "gs_raster_fwd launch");
+}
+
+gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float* image, const float* target,
+                          float scale, float* dl_dimage, float* loss_sum, void* stream) {
+    g_last_error.clear();
+    if (V < 1 || width <= 0 || height <= 0) return fail(GS_ERR_INVALID_ARGUMENT, "bad image size");
+    if (!image || !target || !dl_dimage) return fail(GS_ERR_INVALID_ARGUMENT, "loss buffers are null");
+    const int64_t n = (int64_t)V * 3 * width * height;
+    return hip_check(launch_loss_l1(n, image, target, scale, dl_dimage, loss_sum, static_cast<hipStream_t>(stream)),
+                     "gs_loss_l1_grad launch");
+}
+
+gs_status gs_raster_bwd(const gs_camera* cams, const gs_projected* proj, const gs_bins* bins, int32_t V,
+                        const gs_render_params* p, int32_t use_capped, const float* image, const float* t_final,
+                        const int32_t* n_contrib, const float* dl_dimage, gs_grads2d* grads, void* stream) {
+    g_last_error.clear();
+    RasterArgs ra;
+    gs_status st = check_raster(cams, proj, bins, V, p, use_capped, &ra);
+    if (st != GS_OK) return st;
+    if (!t_final || !n_contrib || !dl_dimage) return fail(GS_ERR_INVALID_ARGUMENT, "backward inputs are null");
+    Grads g;
+    if ((st = check_grads(grads, &g)) != GS_OK) return st;
+    return hip_check(launch_raster_bwd(ra, image, t_final, n_contrib, dl_dimage, g, static_cast<hipStream_t>(stream)),
+                     "gs_raster_bwd launch");
+}
+
+gs_status gs_raster_fused(const gs_camera* cams, const gs_projected* proj, const gs_bins* bins, int32_t V,
+                          const gs_render_params* p, int32_t use_capped, gs_loss_mode mode,
+                          const float* target_or_dldc, float loss_scale, float* image_opt, float* loss_sum_opt,
+                          gs_grads2d* grads, gs_counters* counters, void* stream) {
+    g_last_error.clear();
+    RasterArgs ra;
+    gs_status st = check_raster(cams, proj, bins, V, p, use_capped, &ra);
+    if (st != GS_OK) return st;
+    if (mode != GS_LOSS_L1 && mode != GS_LOSS_EXTERNAL) return fail(GS_ERR_INVALID_ARGUMENT, "loss mode %d", (int)mode);
+    if (!target_or_dldc) return fail(GS_ERR_INVALID_ARGUMENT, "target_or_dldc is null");
+    Grads g;
+    if ((st = check_grads(grads, &g)) != GS_OK) return st;
+    ra.counters = counters;
+    return hip_check(launch_raster_fused(ra, (int)mode, target_or_dldc, loss_scale, image_opt, loss_sum_opt, g,
+                                         static_cast<hipStream_t>(stream)),
+                     "gs_raster_fused launch");
+}
+
+gs_status gs_fused_max_cap(int32_t* k) {
+    if (!k) return fail(GS_ERR_INVALID_ARGUMENT, "k is null");
+    *k = fused_lds_entries();
+    return GS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,242 @@
+// A2-A6: tile binning of the visible slots of all views.
+//
+// The (view, tile, depth, slot) order is produced by an LSD radix sort whose depth digits run
+// first, over one entry per visible slot (key = float32 bits of camera-space z, value =
+// view << 28 | slot, input in (view, slot) order); each slot then emits its tile instances in
+// that depth order at offsets from a prefix sum of n_tiles, and a stable radix sort on the
+// global tile id (view * tiles_per_view + tile) finishes the sort.  Emission copies a slot's
+// depth to each of its instances, so this equals sorting every instance by (tile, depth) with
+// ties in slot order, while the depth passes move one entry per slot instead of one per
+// instance.
+#include "common.h"
+
+namespace gsmi {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr uint32_t kSlotBits = 28;
+constexpr uint32_t kSlotMask = (1u << kSlotBits) - 1u;
+
+struct ViewFirst {
+    int32_t first[GS_MAX_VIEWS + 1];
+};
+
+__global__ __launch_bounds__(kBlock) void depth_keys_kernel(const float* depth, ViewFirst vf, int32_t V,
+                                                            int32_t capacity, int32_t total, uint32_t* keys,
+                                                            uint32_t* vals) {
+    const int32_t e = blockIdx.x * kBlock + threadIdx.x;
+    if (e >= total) return;
+    int v = 0;
+    while (v + 1 < V && e >= vf.first[v + 1]) v++;
+    const int32_t slot = e - vf.first[v];
+    keys[e] = __float_as_uint(depth[(size_t)v * capacity + slot]);
+    vals[e] = ((uint32_t)v << kSlotBits) | (uint32_t)slot;
+}
+
+__global__ __launch_bounds__(kBlock) void gather_ntiles_kernel(const uint32_t* packed, const int32_t* n_tiles,
+                                                               int32_t capacity, int32_t total, int32_t* out) {
+    const int32_t r = blockIdx.x * kBlock + threadIdx.x;
+    if (r >= total) return;
+    const uint32_t p = packed[r];
+    out[r] = n_tiles[(size_t)(p >> kSlotBits) * capacity + (p & kSlotMask)];
+}
+
+__global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* offsets, const ushort4* rect,
+                                                      int32_t capacity, int32_t total, int32_t tiles_x,
+                                                      int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
+                                                      int32_t* vals) {
+    const int32_t r = blockIdx.x * kBlock + threadIdx.x;
+    if (r >= total) return;
+    const uint32_t p = packed[r];
+    const uint32_t v = p >> kSlotBits, slot = p & kSlotMask;
+    const ushort4 rc = rect[(size_t)v * capacity + slot];
+    int32_t o = offsets[r];
+    const uint32_t vbase = v * (uint32_t)tiles_per_view;
+    for (int ty = rc.y; ty <= rc.w; ty++)
+        for (int tx = rc.x; tx <= rc.z; tx++) {
+            if (o >= M) return;  // never past the instance count sized on the host
+            tile_keys[o] = vbase + (uint32_t)(ty * tiles_x + tx);
+            vals[o] = (int32_t)slot;
+            o++;
+        }
+}
+
+__global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) p[i] = value;
+}
+
+// ranges[t] = [first, last + 1) of tile t in the sorted keys (untouched tiles keep (0, 0)).
+__global__ __launch_bounds__(kBlock) void ranges_kernel(const uint32_t* keys, int32_t M, int32_t* ranges) {
+    const int32_t j = blockIdx.x * kBlock + threadIdx.x;
+    if (j >= M) return;
+    const uint32_t k = keys[j];
+    if (j == 0 || keys[j - 1] != k) ranges[2 * (size_t)k] = j;
+    if (j == M - 1 || keys[j + 1] != k) ranges[2 * (size_t)k + 1] = j + 1;
+}
+
+__global__ __launch_bounds__(kBlock) void cap_count_kernel(const int32_t* ranges, int32_t n_tiles_total, int32_t K,
+                                                           int32_t* kept) {
+    const int32_t t = blockIdx.x * kBlock + threadIdx.x;
+    if (t >= n_tiles_total) return;
+    const int32_t n = ranges[2 * t + 1] - ranges[2 * t];
+    kept[t] = n < K ? n : K;
+}
+
+// Cap score o / sqrt(A C - B^2), one IEEE rounding per operation, compared as its bit pattern.
+__device__ __forceinline__ uint32_t cap_score_bits(float4 co) {
+    const float det = __fsub_rn(__fmul_rn(co.x, co.z), __fmul_rn(co.y, co.y));
+    return __float_as_uint(__fdiv_rn(co.w, __fsqrt_rn(det)));
+}
+
+__device__ __forceinline__ int block_excl_scan(int x, int* s_wave, int* total) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int inc = x;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == kWave - 1) s_wave[w] = inc;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int k = 0; k < kBlock / kWave; k++) {
+        if (k < w) off += s_wave[k];
+        tot += s_wave[k];
+    }
+    __syncthreads();
+    *total = tot;
+    return off + inc - x;
+}
+
+// One block per global tile.  Tiles with at most K entries copy their list; longer lists keep
+// the K best by (score desc, depth asc, slot asc).  The list is in (depth, slot) order, so the
+// tie-break is list order: a radix select over the score bits (most significant digit first)
+// finds the K-th best bit pattern `thr`; entries above it are kept, and of those equal to it the
+// first `need` in list order.
+__global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* ranges, const int32_t* vals,
+                                                            const float4* conic_opacity, int32_t capacity,
+                                                            int32_t tiles_per_view, int32_t K,
+                                                            const int32_t* cap_offsets, int32_t* vals_capped,
+                                                            int32_t* ranges_capped, uint32_t* scratch_bits) {
+    __shared__ int s_hist[256];
+    __shared__ int s_wave[kBlock / kWave];
+    __shared__ uint32_t s_sel[2];
+    const int32_t g = blockIdx.x;
+    const int32_t start = ranges[2 * g], end = ranges[2 * g + 1];
+    const int32_t n = end - start;
+    const int32_t out0 = cap_offsets[g];
+    const int32_t kept = n < K ? n : K;
+    if (threadIdx.x == 0) {
+        ranges_capped[2 * g] = kept > 0 ? out0 : 0;
+        ranges_capped[2 * g + 1] = kept > 0 ? out0 + kept : 0;
+    }
+    if (n <= K) {
+        for (int32_t j = threadIdx.x; j < n; j += kBlock) vals_capped[out0 + j] = vals[start + j];
+        return;
+    }
+    const size_t vbase = (size_t)(g / tiles_per_view) * capacity;
+    for (int32_t j = threadIdx.x; j < n; j += kBlock)
+        scratch_bits[start + j] = cap_score_bits(conic_opacity[vbase + vals[start + j]]);
+    __syncthreads();
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        s_hist[threadIdx.x] = 0;
+        __syncthreads();
+        for (int32_t j = threadIdx.x; j < n; j += kBlock) {
+            const uint32_t b = scratch_bits[start + j];
+            if ((b & pmask) == prefix) atomicAdd(&s_hist[(b >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int cum = 0;
+            int d = 255;
+            for (; d > 0; d--) {
+                if (cum + s_hist[d] >= remaining) break;
+                cum += s_hist[d];
+            }
+            s_sel[0] = (uint32_t)d;
+            s_sel[1] = (uint32_t)(remaining - cum);
+        }
+        __syncthreads();
+        prefix |= s_sel[0] << shift;
+        pmask |= 255u << shift;
+        remaining = (int)s_sel[1];
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;
+    const int need = remaining;  // entries equal to thr to keep, in list order
+    int eq_seen = 0, out_seen = 0;
+    for (int32_t j0 = 0; j0 < n; j0 += kBlock) {
+        const int32_t j = j0 + threadIdx.x;
+        const uint32_t b = j < n ? scratch_bits[start + j] : 0u;
+        const int is_eq = (j < n && b == thr) ? 1 : 0;
+        int eq_tot;
+        const int eq_rank = eq_seen + block_excl_scan(is_eq, s_wave, &eq_tot);
+        const int keep = (j < n) && (b > thr || (is_eq && eq_rank < need)) ? 1 : 0;
+        int keep_tot;
+        const int pos = out_seen + block_excl_scan(keep, s_wave, &keep_tot);
+        if (keep) vals_capped[out0 + pos] = vals[start + j];
+        eq_seen += eq_tot;
+        out_seen += keep_tot;
+    }
+}
+
+}  // namespace
+
+static unsigned blocks_for(int64_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
+
+hipError_t launch_depth_keys(const float* depth, const int32_t* /*vis_count*/, const int64_t* view_first, int32_t V,
+                             int32_t capacity, int32_t total, uint32_t* keys, uint32_t* vals, hipStream_t s) {
+    if (total <= 0) return hipSuccess;
+    ViewFirst vf;
+    for (int v = 0; v <= GS_MAX_VIEWS; v++) vf.first[v] = v <= V ? (int32_t)view_first[v] : total;
+    hipLaunchKernelGGL(depth_keys_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, depth, vf, V, capacity, total,
+                       keys, vals);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity, int32_t total,
+                                int32_t* out, hipStream_t s) {
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_ntiles_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, packed, n_tiles, capacity,
+                       total, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
+                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
+                       int32_t* vals, hipStream_t s) {
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(emit_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, packed, offsets, rect, capacity,
+                       total, tiles_x, tiles_per_view, M, tile_keys, vals);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks_for(n)), dim3(kBlock), 0, s, p, value, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(ranges_kernel, dim3(blocks_for(M)), dim3(kBlock), 0, s, tile_keys, M, ranges);
+    return hipGetLastError();
+}
+
+hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s) {
+    hipLaunchKernelGGL(cap_count_kernel, dim3(blocks_for(n_tiles_total)), dim3(kBlock), 0, s, ranges, n_tiles_total,
+                       K, kept);
+    return hipGetLastError();
+}
+
+hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity, int32_t capacity,
+                             int32_t tiles_per_view, int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets,
+                             int32_t* vals_capped, int32_t* ranges_capped, uint32_t* scratch_bits, hipStream_t s) {
+    hipLaunchKernelGGL(cap_select_kernel, dim3(n_tiles_total), dim3(kBlock), 0, s, ranges, vals, conic_opacity, capacity,
+                       tiles_per_view, K, cap_offsets, vals_capped, ranges_capped, scratch_bits);
+    return hipGetLastError();
+}
+
+}  // namespace gsmi

@@ -1,0 +1,139 @@
+// Internal declarations of the gfx950 HIP implementation behind include/gsmi.h.
+//
+// Every kernel is compiled with -ffp-contract=off: multiply-adds are fused only where an
+// explicit fmaf() says so, so that a formula evaluated in two kernels (the forward and the
+// backward recompute of alpha) rounds identically in both.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gsmi.h"
+
+namespace gsmi {
+
+constexpr int kTile = GS_TILE;            // 16x16 pixels per tile
+constexpr int kTileThreads = kTile * kTile;  // one thread per pixel, 4 wavefronts of 64
+constexpr int kWave = 64;
+
+// Camera as the kernels read it (kernel-argument struct, by value).
+struct CamDev {
+    int32_t width, height, tiles_x, tiles_y;
+    float fx, fy, cx, cy;
+    float R[9];
+    float t[3];
+    float campos[3];
+};
+
+struct CamArray {
+    CamDev c[GS_MAX_VIEWS];
+};
+
+struct ParamsDev {
+    float znear, eps2d, alpha_min, alpha_max, t_min;
+    float bg[3];
+    int32_t sh_degree, tile_cap;
+};
+
+// ---------------------------------------------------------------------------------------
+// Pair evaluation shared by every rasterizer: the forward, the backward's recomputation and
+// the fused kernel call this one function, so they take bit-identical decisions.
+// q = A dx^2 + 2 B dx dy + C dy^2 with d = pixel centre - projected centre;
+// G = exp(-q/2); v = o G; alpha = min(alpha_max, v).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float pair_power(float dx, float dy, float A, float B, float C) {
+    const float cdy = C * dy;
+    const float bdx = B * dx;
+    const float q = fmaf(A * dx, dx, fmaf(2.0f * bdx, dy, cdy * dy));
+    return -0.5f * q;
+}
+
+__device__ __forceinline__ float pair_gauss(float power) { return __expf(power); }
+
+// ---------------------------------------------------------------------------------------
+// Launchers (defined next to their kernels).
+// ---------------------------------------------------------------------------------------
+struct ProjectArgs {
+    int32_t n, V, capacity;
+    const float *means, *log_scales, *quats, *logits, *sh;
+    CamArray cams;
+    ParamsDev p;
+    int32_t* vis_count;
+    int64_t* inst_count;
+    int32_t* vis_ids;
+    float2* mean2d;
+    float4* conic_opacity;
+    float* color;
+    float* depth;
+    ushort4* tile_rect;
+    int32_t* n_tiles;
+    // workspace
+    int32_t* block_counts;   // [V][nb]
+    int32_t* block_offsets;  // [V][nb]
+    int32_t* scan_partials;  // scan workspace
+    int64_t* inst_accum;     // [V]
+};
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
+size_t project_ws_bytes(int32_t n, int32_t V);
+
+// Exclusive scan of `rows` independent int32 rows of length n (row r at in + r*n):
+// out[r][i] = sum_{k<i} in[r][k]; totals[r] = sum of row r (totals may be null).
+hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, int32_t n, int32_t rows,
+                            int32_t* partials, hipStream_t s);
+size_t scan_partials_bytes(int32_t n, int32_t rows);
+
+// LSD radix sort of (uint32 key, uint32 value) pairs over bits [0, bits).  Sorts keys/vals in
+// place through the alternate buffers; the result lands in keys/vals when the number of
+// passes is even and in keys_alt/vals_alt when it is odd (radix_passes() tells which).
+int radix_passes(int bits);
+hipError_t launch_radix_sort(uint32_t* keys, uint32_t* vals, uint32_t* keys_alt, uint32_t* vals_alt, int32_t n,
+                             int bits, int32_t* hist, int32_t* partials, hipStream_t s);
+size_t radix_hist_bytes(int32_t n);
+size_t radix_partials_bytes(int32_t n);
+
+// Binning helpers.
+hipError_t launch_depth_keys(const float* depth, const int32_t* vis_count, const int64_t* view_first,
+                             int32_t V, int32_t capacity, int32_t total, uint32_t* keys, uint32_t* vals,
+                             hipStream_t s);
+hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity, int32_t total,
+                                int32_t* out, hipStream_t s);
+hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
+                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
+                       int32_t* vals, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s);
+hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s);
+hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
+                             int32_t capacity, int32_t tiles_per_view, int32_t n_tiles_total, int32_t K,
+                             const int32_t* cap_offsets, int32_t* vals_capped, int32_t* ranges_capped,
+                             uint32_t* scratch_bits, hipStream_t s);
+
+// Rasterizers.
+struct RasterArgs {
+    int32_t V, width, height, tiles_x, tiles_y, capacity;
+    ParamsDev p;
+    const int32_t* ranges;   // [V*T][2]
+    const int32_t* vals;
+    const float2* mean2d;
+    const float4* conic_opacity;
+    const float* color;
+    const int32_t* vis_count;
+    int64_t* counters;       // optional
+};
+hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s);
+hipError_t launch_loss_l1(int64_t n, const float* image, const float* target, float scale, float* dl, float* loss_sum,
+                          hipStream_t s);
+struct Grads {
+    float2* d_mean2d;
+    float* d_conic;
+    float* d_opacity;
+    float* d_color;
+};
+hipError_t launch_zero_grads(const int32_t* vis_count, int32_t V, int32_t capacity, Grads g, hipStream_t s);
+hipError_t launch_raster_bwd(const RasterArgs& a, const float* image, const float* t_final, const int32_t* n_contrib,
+                             const float* dl, Grads g, hipStream_t s);
+hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,
+                               float* loss_sum, Grads g, hipStream_t s);
+int32_t fused_lds_entries();
+
+}  // namespace gsmi

@@ -1,0 +1,104 @@
+// Device-wide exclusive prefix sums of int32 rows (reduce, scan the block sums, apply).
+// Each block owns kChunk = 2048 consecutive elements (8 per thread, thread-contiguous), so
+// every pass reads the input with 128-bit loads where the row length allows.
+#include "common.h"
+
+namespace gsmi {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kItems = 8;
+constexpr int kChunk = kBlock * kItems;
+
+// Exclusive scan of one value per thread across the block; returns the prefix, *total the sum.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* s_wave, int* total) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int inc = x;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == kWave - 1) s_wave[w] = inc;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int k = 0; k < kBlock / kWave; k++) {
+        if (k < w) off += s_wave[k];
+        tot += s_wave[k];
+    }
+    __syncthreads();
+    *total = tot;
+    return off + inc - x;
+}
+
+__global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const int32_t* in, int32_t n, int32_t nblocks,
+                                                             int32_t* partials) {
+    __shared__ int s_wave[kBlock / kWave];
+    const int row = blockIdx.y;
+    const int32_t* r = in + (size_t)row * n;
+    const int64_t base = (int64_t)blockIdx.x * kChunk + threadIdx.x * kItems;
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; k++)
+        if (base + k < n) sum += r[base + k];
+    int tot;
+    block_exclusive_scan(sum, s_wave, &tot);
+    if (threadIdx.x == 0) partials[(size_t)row * nblocks + blockIdx.x] = tot;
+}
+
+// One block per row scans that row's block sums in place (exclusive) and writes the total.
+__global__ __launch_bounds__(kBlock) void scan_partials_kernel(int32_t* partials, int32_t nblocks, int32_t* totals) {
+    __shared__ int s_wave[kBlock / kWave];
+    int32_t* r = partials + (size_t)blockIdx.x * nblocks;
+    int carry = 0;
+    for (int32_t b0 = 0; b0 < nblocks; b0 += kBlock) {
+        const int32_t j = b0 + threadIdx.x;
+        const int x = j < nblocks ? r[j] : 0;
+        int tot;
+        const int ex = block_exclusive_scan(x, s_wave, &tot);
+        if (j < nblocks) r[j] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0 && totals) totals[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(kBlock) void scan_apply_kernel(const int32_t* in, int32_t* out, int32_t n, int32_t nblocks,
+                                                            const int32_t* partials) {
+    __shared__ int s_wave[kBlock / kWave];
+    const int row = blockIdx.y;
+    const int32_t* r = in + (size_t)row * n;
+    int32_t* o = out + (size_t)row * n;
+    const int64_t base = (int64_t)blockIdx.x * kChunk + threadIdx.x * kItems;
+    int v[kItems];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; k++) {
+        v[k] = (base + k < n) ? r[base + k] : 0;
+        sum += v[k];
+    }
+    int tot;
+    int run = block_exclusive_scan(sum, s_wave, &tot) + partials[(size_t)row * nblocks + blockIdx.x];
+#pragma unroll
+    for (int k = 0; k < kItems; k++) {
+        if (base + k < n) o[base + k] = run;
+        run += v[k];
+    }
+}
+
+}  // namespace
+
+static int32_t scan_blocks(int32_t n) { return (n + kChunk - 1) / kChunk; }
+
+size_t scan_partials_bytes(int32_t n, int32_t rows) {
+    return sizeof(int32_t) * (size_t)(scan_blocks(n > 0 ? n : 1)) * (size_t)rows;
+}
+
+hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, int32_t n, int32_t rows,
+                            int32_t* partials, hipStream_t s) {
+    const int32_t nb = scan_blocks(n > 0 ? n : 1);
+    hipLaunchKernelGGL(scan_reduce_kernel, dim3(nb, rows), dim3(kBlock), 0, s, in, n, nb, partials);
+    hipLaunchKernelGGL(scan_partials_kernel, dim3(rows), dim3(kBlock), 0, s, partials, nb, totals);
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(nb, rows), dim3(kBlock), 0, s, in, out, n, nb, partials);
+    return hipGetLastError();
+}
+
+}  // namespace gsmi

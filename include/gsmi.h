@@ -1,0 +1,241 @@
+/*
+ * gsmi.h -- C ABI of a single-GPU (MI355X, gfx950) implementation of one training iteration of
+ * tile-based differentiable 3D Gaussian splatting: EWA projection, tile binning with a
+ * (tile, depth) radix sort, front-to-back alpha compositing, its reverse-order backward pass,
+ * a fused forward+backward rasterizer and an optional per-tile cap.
+ *
+ * Where the operations come from.  ByteSplat (arXiv 2610.02851, English abstract) names the
+ * forward and backward rasterization, their fusion into one kernel that keeps intermediates on
+ * chip, and pruning under per-tile on-chip memory limits.  Grendel (arXiv 2406.18533, English
+ * abstract) notes that each Gaussian touches a small, view-dependent subset of pixels, the
+ * sparsity tile binning exploits, and trains on batches of views.  GS-Scale (arXiv 2509.15645,
+ * English abstract) culls against each view's frustum.  No page writes out the formulas; the
+ * library computes standard EWA splatting, with every open constant in gs_render_params.
+ *
+ * Conventions for every entry point.
+ *  - Pointers inside the structs and the array arguments are DEVICE pointers unless a comment
+ *    says "host".  All device memory is owned by the caller; the library never allocates
+ *    device memory.  Scratch space comes from a caller-provided workspace whose size the
+ *    matching *_workspace_size query returns; it must be 256-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on it
+ *    and returns, except gs_bin_tiles, which performs one device-to-host read of the counts it
+ *    needs to size its launches (and therefore synchronizes `stream`).
+ *  - Arguments are validated on the host before anything is enqueued; a call that returns an
+ *    error has enqueued nothing, except GS_ERR_HIP, which reports a failed launch or copy
+ *    (asynchronous faults of earlier work surface as GS_ERR_HIP from a later call).
+ *  - gs_last_error() returns a thread-local message describing the last failure.
+ *  - Sizes: Gaussians per call n < 2^28; views per call 1 <= V <= GS_MAX_VIEWS; instances
+ *    ((Gaussian, tile) pairs) per call < 2^31.
+ *  - Images are float32 [V][3][H][W]; per-pixel maps [V][H][W]; all views of a call share
+ *    one width and height.
+ *  - The library keeps no state between calls other than the error message.
+ */
+#ifndef GSMI_H
+#define GSMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GS_MAX_VIEWS 16
+#define GS_TILE 16 /* tile side in pixels */
+
+typedef enum {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent cameras, ... */
+    GS_ERR_CAPACITY = 2,         /* an output buffer is too small; *required says how large */
+    GS_ERR_UNSUPPORTED = 3,      /* e.g. a tile cap above the fused kernel's on-chip limit */
+    GS_ERR_HIP = 4,              /* a HIP runtime call failed */
+    GS_ERR_INTERNAL = 5
+} gs_status;
+
+/* Pinhole camera, OpenCV axes (x right, y down, z forward).  Host struct.
+ * Pixel (u, v) covers [u, u+1) x [v, v+1); its centre is (u + 1/2, v + 1/2). */
+typedef struct {
+    int32_t width, height;
+    float fx, fy, cx, cy;   /* focal lengths and principal point, pixels */
+    float R[9];             /* world -> camera rotation, row-major */
+    float t[3];             /* world -> camera translation: x_cam = R x_world + t */
+    float campos[3];        /* camera centre in world coordinates (SH view direction origin) */
+} gs_camera;
+
+/* Constants the pages leave open.  Host struct.  Typical values in brackets. */
+typedef struct {
+    float znear;      /* [0.2]   Gaussians with camera-space z <= znear are culled */
+    float eps2d;      /* [0.3]   low-pass dilation added to the 2D covariance diagonal, px^2 */
+    float alpha_min;  /* [1/255] pairs with alpha below this are skipped */
+    float alpha_max;  /* [0.99]  alpha = min(alpha_max, o * exp(-q/2)) */
+    float t_min;      /* [1e-4]  a pixel stops before a blend that would take T below t_min */
+    float bg[3];      /* [0,0,0] background colour, added as T_final * bg */
+    int32_t sh_degree;/* 0..3 */
+    int32_t tile_cap; /* 0 = off; else keep at most this many entries per tile (gs_bin_tiles) */
+} gs_render_params;
+
+/* Gaussian parameters, structure of arrays, float32, device. */
+typedef struct {
+    int32_t n;
+    const float* means;          /* [3][n] world position */
+    const float* log_scales;     /* [3][n] per-axis log standard deviation */
+    const float* quats;          /* [4][n] rotation (w, x, y, z), need not be normalized */
+    const float* opacity_logits; /* [n]    opacity = sigmoid(logit) */
+    const float* sh;             /* [3*(d+1)^2][n], row k*3 + channel; row 0..2 = DC = base colour */
+} gs_gaussians;
+
+/* Per-view projected records, indexed by visible slot.  All arrays are [V][capacity][...]
+ * with capacity >= n; slot s of view v lives at index v*capacity + s.  Visible Gaussians of
+ * a view take slots 0..vis_count[v]-1 in ascending Gaussian index. */
+typedef struct {
+    int32_t capacity;
+    int32_t* vis_count;       /* [V]  number of visible Gaussians per view */
+    int64_t* inst_count;      /* [V]  sum of n_tiles per view ((Gaussian, tile) instances) */
+    int32_t* vis_ids;         /* [V][capacity]    Gaussian index of each slot */
+    float* mean2d;            /* [V][capacity][2] projected centre, pixels */
+    float* conic_opacity;     /* [V][capacity][4] (A, B, C, o): q = A dx^2 + 2B dx dy + C dy^2 */
+    float* color;             /* [V][capacity][3] RGB after the lower clamp at 0 */
+    float* depth;             /* [V][capacity]    camera-space z */
+    uint16_t* tile_rect;      /* [V][capacity][4] (tx0, ty0, tx1, ty1), inclusive */
+    int32_t* n_tiles;         /* [V][capacity]    tiles in the rectangle */
+} gs_projected;
+
+/* Tile bins of all views of one call.  Global tile id = v * tiles_per_view + ty * tiles_x + tx.
+ * ranges[g] = [start, end) into vals (positions over all views); empty tiles hold (0, 0). */
+typedef struct {
+    int64_t capacity;           /* instance capacity of tile_keys / vals / vals_capped */
+    uint32_t* tile_keys;        /* [capacity] global tile id of each sorted instance */
+    int32_t* vals;              /* [capacity] slot of each sorted instance */
+    int32_t* ranges;            /* [V * tiles_per_view][2] */
+    int32_t* vals_capped;       /* [capacity]  only written when tile_cap > 0 */
+    int32_t* ranges_capped;     /* [V * tiles_per_view][2]  only written when tile_cap > 0 */
+    int32_t* num_capped;        /* [1] instances kept by the cap, all views (tile_cap > 0) */
+} gs_bins;
+
+/* Host-side counts that gs_bin_tiles reports. */
+typedef struct {
+    int32_t vis_count[GS_MAX_VIEWS];
+    int64_t view_offset[GS_MAX_VIEWS + 1]; /* first instance position of each view */
+    int64_t num_instances;                 /* all views */
+    int64_t num_instances_capped;          /* = num_instances when the cap is off; -1 when it is
+                                              on (the count is then on the device, bins->num_capped) */
+} gs_bin_info;
+
+/* Per-slot 2D gradients, [V][capacity][k], float32, device.  Overwritten by the raster calls
+ * (zeroed for slots < vis_count, then accumulated with atomics). */
+typedef struct {
+    float* d_mean2d;  /* [V][capacity][2] dL/d mean2d (pixels) */
+    float* d_conic;   /* [V][capacity][3] dL/d (A, B, C) */
+    float* d_opacity; /* [V][capacity]    dL/d o (activated opacity) */
+    float* d_color;   /* [V][capacity][3] dL/d colour (post-clamp RGB) */
+} gs_grads2d;
+
+typedef enum { GS_LOSS_L1 = 0, GS_LOSS_EXTERNAL = 1 } gs_loss_mode;
+
+/* Optional per-call diagnostics (device int64 counters; pass NULL to skip; counting costs a
+ * little time).  [0] pairs evaluated, [1] pairs blended. */
+typedef int64_t gs_counters;
+
+const char* gs_version(void);
+const char* gs_status_string(gs_status s);
+const char* gs_last_error(void);
+
+/* Workspace bytes of gs_project for n Gaussians and V views. */
+size_t gs_project_workspace_size(int32_t n, int32_t V);
+
+/*
+ * A1: project every Gaussian into each of V views.  Per Gaussian and view: activations
+ * (sigmoid opacity, exp scales, normalized quaternion); camera transform and near cull; world
+ * covariance R diag(s^2) R^T; EWA 2D covariance J W Sigma W^T J^T + eps2d I, conic = its
+ * inverse; projected centre; colour from spherical harmonics along the view direction (DC is
+ * the base colour; lower clamp at 0); the exact bounding box of the region where
+ * o exp(-q/2) >= alpha_min (half extents 1.001 sqrt(2 ln(o/alpha_min) Sigma'_xx) etc.) clipped
+ * to the image, and its tile rectangle.  Gaussians with any non-finite input or derived value,
+ * det <= 0, o <= alpha_min or an empty box are culled (per-view frustum culling as in GS-Scale,
+ * arXiv 2509.15645, English abstract).  Visible Gaussians are compacted into slots in ascending
+ * index order.  Parameters are read once for all V views.
+ * Errors: GS_ERR_INVALID_ARGUMENT for null pointers, n < 0, V outside 1..GS_MAX_VIEWS,
+ * capacity < n, sh_degree outside 0..3, non-positive image sizes or differing image sizes
+ * between views; GS_ERR_CAPACITY if ws_bytes is too small.
+ */
+gs_status gs_project(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, int32_t V,
+                     const gs_render_params* p, gs_projected* out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes of gs_bin_tiles for n Gaussians, V views and an instance capacity. */
+size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height, int64_t instance_capacity);
+
+/*
+ * A2-A6: bin the visible slots of all V views into 16x16 tiles.  Instances (one per slot and
+ * tile of its rectangle) are ordered by (view, tile, depth, slot) with an LSD radix sort whose
+ * low (depth) digits are sorted once per slot before the instances are emitted (the emission
+ * keeps each slot's depth, so this is the same stable sort of the (tile, depth) key); the
+ * result is a total order, so tile ids, order and ranges are exact.  With tile_cap K > 0,
+ * every tile holding more than K entries keeps the K entries with the largest
+ * score = o / sqrt(A C - B^2) (opacity times the square root of the dilated covariance's
+ * determinant, evaluated in float32 with one rounding per operation), ties broken by
+ * depth then slot, kept in depth order (ByteSplat's pruning under per-tile on-chip limits).
+ * Reads the per-view counts back to the host once (info, host), then sizes its launches.
+ * Errors: GS_ERR_INVALID_ARGUMENT as for gs_project; GS_ERR_CAPACITY (with *required, host,
+ * set to the instances needed) when bins->capacity is too small, in which case the bins are
+ * left undefined; GS_ERR_CAPACITY if the workspace is too small.
+ */
+gs_status gs_bin_tiles(const gs_camera* cams /*host [V]*/, const gs_projected* proj, int32_t V,
+                       const gs_render_params* p, gs_bins* bins, gs_bin_info* info /*host*/,
+                       int64_t* required /*host*/, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A7: forward rasterization.  One 256-thread workgroup per 16x16 tile and view; records of the
+ * tile list are staged in LDS in batches.  Per pixel, front to back:
+ * alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop before a blend that would
+ * take T below t_min; C += alpha T c; T *= (1 - alpha); at the end C += T bg.
+ * n_contrib = 1 + list position of the last blended entry (0 if none).  `use_capped` selects
+ * the capped lists.  Outputs: image [V][3][H][W], t_final [V][H][W], n_contrib [V][H][W].
+ */
+gs_status gs_raster_fwd(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
+                        int32_t V, const gs_render_params* p, int32_t use_capped, float* image,
+                        float* t_final, int32_t* n_contrib, gs_counters* counters, void* stream);
+
+/* A8: dL/dC of L = scale * sum |C - target| (L1): scale * sign(C - target), sign(0) = 0.
+ * image, target, dl_dimage: [V][3][H][W].  loss_sum (optional, device float, accumulated). */
+gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float* image, const float* target,
+                          float scale, float* dl_dimage, float* loss_sum, void* stream);
+
+/*
+ * A9: backward rasterization.  Per pixel, back to front from n_contrib: T is recovered by
+ * division by (1 - alpha); with Bk the colour behind entry j,
+ *   dL/dc_j = alpha_j T_j g,  dL/dalpha_j = sum_ch g_ch (T_j (c_j - Bk) - T_final bg / (1 - alpha_j)),
+ * and unless alpha was clamped, dL/do = G dL/dalpha, dL/dmean2d = o G dL/dalpha (A dx + B dy,
+ * B dx + C dy) with d = pixel centre - mean2d, dL/d(A,B,C) = o G dL/dalpha (-dx^2/2, -dx dy,
+ * -dy^2/2).  Contributions are summed across each wavefront before one float atomic per
+ * (entry, wavefront, component).  grads are zeroed for the visible slots, then accumulated.
+ */
+gs_status gs_raster_bwd(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
+                        int32_t V, const gs_render_params* p, int32_t use_capped, const float* image,
+                        const float* t_final, const int32_t* n_contrib, const float* dl_dimage,
+                        gs_grads2d* grads, void* stream);
+
+/*
+ * A10: fused forward + loss gradient + backward in one kernel per tile (ByteSplat, arXiv
+ * 2610.02851, English abstract: forward and backward rasterization fused into one kernel that
+ * keeps intermediates on chip).  Per-pixel colour, transmittance and n_contrib stay in
+ * registers; the tile list's records stay in LDS between the two passes when they fit, else
+ * they are re-read in chunks.  mode GS_LOSS_L1: target_or_dldc is the target image and the
+ * gradient is loss_scale * sign(C - target); GS_LOSS_EXTERNAL: target_or_dldc is dL/dC.
+ * image_opt (optional) receives the rendered image; loss_sum_opt (optional, device float)
+ * accumulates scale * sum |C - target| (L1 mode only).  Same gradients as A7+A8+A9.
+ */
+gs_status gs_raster_fused(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
+                          int32_t V, const gs_render_params* p, int32_t use_capped, gs_loss_mode mode,
+                          const float* target_or_dldc, float loss_scale, float* image_opt,
+                          float* loss_sum_opt, gs_grads2d* grads, gs_counters* counters, void* stream);
+
+/* Largest per-tile list length the fused kernel keeps resident in LDS for one pass
+ * (longer lists are processed in chunks).  *k (host) receives it. */
+gs_status gs_fused_max_cap(int32_t* k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSMI_H */

@@ -1,0 +1,157 @@
+"""Comparison helpers for the GPU parity tests (HIP path vs the CPU oracle).
+
+Comparison contract (stage-isolated, so that every integer result is compared bit for bit):
+  * projection: visible sets equal up to Gaussians whose decision the oracle flags as within
+    float32 reach; records within the float tolerances below;
+  * binning and cap: the oracle's NumPy binning run on the GPU's own projected records must
+    reproduce tile keys, order, ranges and capped lists exactly;
+  * forward: the oracle composites the GPU's records over the GPU's lists in double
+    precision; image and T_final within 1e-5 relative + 1e-7 absolute, n_contrib exact, on
+    pixels whose decisions are not within float32 reach;
+  * backward: gradients within 1e-3 relative + 1e-6 absolute on slots that no flagged pixel
+    blends (dL/dC scaled to O(1): L1 summed, scale 1).
+"""
+import numpy as np
+
+EPS32 = 2.0 ** -24
+IMG_RTOL, IMG_ATOL = 1e-5, 1e-7
+GRAD_RTOL, GRAD_ATOL = 1e-3, 1e-6
+
+
+def close(a, b, rtol, atol):
+    return np.abs(a - b) <= rtol * np.abs(b) + atol
+
+
+def report(name, ok, extra=""):
+    bad = int((~ok).sum())
+    print(f"[parity] {name}: {ok.size - bad}/{ok.size} within tolerance {extra}", flush=True)
+    return bad
+
+
+def compare_projection(oracle, scene, cam, settings, gpu: dict):
+    """A1 end-to-end from the raw parameters."""
+    proj = oracle.project(scene, cam, settings)
+    vis_o = np.nonzero(proj["visible"])[0]
+    vis_g = gpu["vis_ids"]
+    assert np.all(np.diff(vis_g) > 0), "slots must follow ascending Gaussian index"
+    diff = np.setxor1d(vis_o, vis_g)
+    unexplained = diff[proj["flag"][diff] == 0]
+    assert unexplained.size == 0, f"visibility differs for unflagged Gaussians {unexplained[:10]}"
+    common, io, ig = np.intersect1d(vis_o, vis_g, return_indices=True)
+    keep = proj["flag"][common] == 0
+    o_idx = common[keep]
+    g_sel = ig[keep]
+    # float records
+    m_o = proj["mean2d"][o_idx]
+    m_g = gpu["mean2d"][g_sel].astype(np.float64)
+    assert close(m_g, m_o, 1e-6, 2e-4).all(), "mean2d"
+    cov = proj["cov2d"][o_idx]
+    kappa = (np.abs(cov[:, 0] * cov[:, 2]) + cov[:, 1] ** 2) / (cov[:, 0] * cov[:, 2] - cov[:, 1] ** 2)
+    conic_o = proj["conic"][o_idx]
+    conic_g = gpu["conic_opacity"][g_sel, :3].astype(np.float64)
+    scale = np.maximum(np.abs(conic_o[:, 0]), np.abs(conic_o[:, 2]))[:, None]
+    tol = (1e-5 + 64 * EPS32 * kappa)[:, None] * scale
+    bad_conic = ~(np.abs(conic_g - conic_o) <= tol)
+    assert not bad_conic.any(), f"conic: {int(bad_conic.any(1).sum())} Gaussians off"
+    assert close(gpu["conic_opacity"][g_sel, 3].astype(np.float64), proj["opacity"][o_idx], 1e-6, 1e-7).all(), "opacity"
+    assert close(gpu["color"][g_sel].astype(np.float64), proj["color"][o_idx], 1e-5, 1e-5).all(), "color"
+    assert close(gpu["depth"][g_sel].astype(np.float64), proj["depth"][o_idx], 1e-6, 0).all(), "depth"
+    assert np.array_equal(gpu["rect"][g_sel], proj["rect"][o_idx]), "tile rect"
+    assert np.array_equal(gpu["n_tiles"][g_sel], proj["n_tiles"][o_idx]), "n_tiles"
+    print(f"[parity] projection: {vis_g.size} visible, {diff.size} flagged differences, "
+          f"{int((proj['flag'][common] != 0).sum())} flagged in common", flush=True)
+    return proj
+
+
+def gpu_records(gpu: dict) -> dict:
+    """The GPU's float32 records, widened exactly to float64 for the oracle."""
+    co = gpu["conic_opacity"].astype(np.float64)
+    return dict(mean2d=gpu["mean2d"].astype(np.float64), conic=co[:, :3].copy(), opacity=co[:, 3].copy(),
+                color=gpu["color"].astype(np.float64))
+
+
+def compare_binning(oracle, cam, gpu: dict, bins_g: dict):
+    """A2-A5 stage-isolated: oracle binning of the GPU's own rect / n_tiles / depth."""
+    dbits = gpu["depth"].view(np.uint32)
+    b = oracle.bin_tiles(gpu["rect"], gpu["n_tiles"], dbits, cam.tiles_x, cam.tiles_y)
+    assert b["num_instances"] == gpu["inst_count"] == bins_g["vals"].size, "instance count"
+    assert np.array_equal(bins_g["vals"], b["vals"]), "sorted slots"
+    assert np.array_equal(bins_g["tile_keys"].astype(np.int64), (b["keys"] >> np.uint64(32)).astype(np.int64)), "keys"
+    assert np.array_equal(bins_g["ranges"], b["ranges"]), "ranges"
+    return b
+
+
+def compare_cap(oracle, gpu: dict, b: dict, capped_g: dict, K: int):
+    score = oracle.cap_score(gpu["conic_opacity"][:, :3], gpu["conic_opacity"][:, 3])
+    c = oracle.cap_tiles(b["ranges"], b["vals"], score, gpu["depth"].view(np.uint32), K)
+    assert np.array_equal(capped_g["vals"], c["vals"]), "capped slots"
+    assert np.array_equal(capped_g["ranges"], c["ranges"]), "capped ranges"
+    return c
+
+
+def region_ranges(ranges: np.ndarray, tiles_x: int, region):
+    """Keep only the tiles of region = (tx0, ty0, tx1, ty1) inclusive (others empty)."""
+    if region is None:
+        return ranges
+    r = np.zeros_like(ranges)
+    tx0, ty0, tx1, ty1 = region
+    for ty in range(ty0, ty1 + 1):
+        for tx in range(tx0, tx1 + 1):
+            r[ty * tiles_x + tx] = ranges[ty * tiles_x + tx]
+    return r
+
+
+def pixel_mask(cam, region):
+    m = np.zeros((cam.height, cam.width), bool)
+    if region is None:
+        m[:] = True
+        return m
+    tx0, ty0, tx1, ty1 = region
+    m[ty0 * 16:min(cam.height, (ty1 + 1) * 16), tx0 * 16:min(cam.width, (tx1 + 1) * 16)] = True
+    return m
+
+
+def compare_forward(oracle, cam, settings, rec, ranges, vals, img_g, T_g, nc_g, region=None):
+    r = region_ranges(ranges, cam.tiles_x, region)
+    f = oracle.raster_forward(cam.width, cam.height, r, vals, rec, settings)
+    sel = pixel_mask(cam, region) & ~f["flag"]
+    ok_img = close(img_g[:, sel].astype(np.float64), f["image"][:, sel], IMG_RTOL, IMG_ATOL)
+    ok_T = close(T_g[sel].astype(np.float64), f["T_final"][sel], IMG_RTOL, IMG_ATOL)
+    ok_nc = nc_g[sel] == f["n_contrib"][sel]
+    nflag = int((pixel_mask(cam, region) & f["flag"]).sum())
+    bad = report("image", ok_img, f"({nflag} flagged pixels skipped)") + report("T_final", ok_T) + \
+        report("n_contrib", ok_nc)
+    if bad:
+        err = np.abs(img_g[:, sel].astype(np.float64) - f["image"][:, sel]) / (np.abs(f["image"][:, sel]) + 1e-7)
+        print("[parity] worst image rel err", float(err.max()), flush=True)
+    assert bad == 0
+    return f
+
+
+def compare_backward(oracle, cam, settings, rec, ranges, vals, dldc, grads_g, fwd_o, region=None, extra_skip=None,
+                     slots_rect=None):
+    r = region_ranges(ranges, cam.tiles_x, region)
+    skip = fwd_o["flag"].copy()
+    if extra_skip is not None:
+        skip |= extra_skip
+    b = oracle.raster_backward(cam.width, cam.height, r, vals, rec, settings, dldc, pixel_skip=skip)
+    S = rec["opacity"].shape[0]
+    use = ~b["slot_flag"]
+    if region is not None:
+        # only slots whose whole tile rectangle lies inside the region have complete gradients
+        tx0, ty0, tx1, ty1 = region
+        rc = slots_rect
+        use &= (rc[:, 0] >= tx0) & (rc[:, 2] <= tx1) & (rc[:, 1] >= ty0) & (rc[:, 3] <= ty1)
+    total_bad = 0
+    for key, k in [("d_mean2d", 2), ("d_conic", 3), ("d_opacity", 1), ("d_color", 3)]:
+        go = b[key].reshape(S, k)[use]
+        gg = grads_g[key].reshape(S, k)[use].astype(np.float64)
+        ok = close(gg, go, GRAD_RTOL, GRAD_ATOL)
+        bad = report(key, ok, f"({int((~use).sum())} slots skipped)")
+        if bad:
+            i = np.argwhere(~ok)[:5]
+            for (s, c) in i:
+                print(f"    slot {s} comp {c}: gpu {gg[s, c]:.9g} oracle {go[s, c]:.9g}", flush=True)
+        total_bad += bad
+    assert total_bad == 0
+    return b

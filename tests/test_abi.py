@@ -1,0 +1,167 @@
+"""The C-ABI library loads, exports every entry point its header declares, and rejects bad
+arguments on the host before anything reaches the GPU (these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsmi.h")
+
+
+@pytest.fixture(scope="module")
+def gs():
+    from differentiable_raster_amd import gsmi
+    if not os.path.exists(gsmi.LIB_PATH):
+        from differentiable_raster_amd import build
+        build.build()
+    gsmi.load()
+    return gsmi
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gs_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ["gs_project", "gs_bin_tiles", "gs_raster_fwd", "gs_raster_bwd", "gs_raster_fused",
+                 "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
+                 "gs_version", "gs_status_string", "gs_last_error"]:
+        assert must in names, must
+
+
+def test_library_exports_every_declared_symbol(gs):
+    lib = ctypes.CDLL(gs.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(gs):
+    lib = gs.load()
+    assert b"gfx950" in lib.gs_version()
+    assert lib.gs_status_string(0) == b"ok"
+    assert lib.gs_status_string(2) == b"capacity exceeded"
+
+
+def test_fused_max_cap(gs):
+    assert gs.gs_fused_max_cap() >= 256
+    assert gs.load().gs_fused_max_cap(None) == 1
+
+
+def test_workspace_queries(gs):
+    assert gs.gs_project_workspace_size(1000, 4) > 0
+    assert gs.gs_project_workspace_size(-1, 4) == 0
+    assert gs.gs_bin_workspace_size(1000, 4, 128, 128, 5000) > gs.gs_bin_workspace_size(1000, 4, 128, 128, 10)
+    assert gs.gs_bin_workspace_size(10, 0, 128, 128, 10) == 0
+
+
+FAKE = 0x10000  # never dereferenced: validation fails before any device access
+
+
+def cams(gs, V=1, w=64, h=48):
+    from differentiable_raster_amd import scenes
+    return gs.make_cameras([scenes.identity_camera(w, h) for _ in range(V)])
+
+
+def params(gs, **kw):
+    from differentiable_raster_amd import scenes
+    s = scenes.RenderSettings(sh_degree=0)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return gs.make_params(s)
+
+
+def projected(gs, capacity=100, null=()):
+    fields = {f: FAKE for f, _ in gs.gs_projected._fields_ if f != "capacity"}
+    for f in null:
+        fields[f] = None
+    return gs.gs_projected(capacity, *[fields[f] for f, _ in gs.gs_projected._fields_ if f != "capacity"])
+
+
+def test_project_rejects_bad_arguments(gs):
+    lib = gs.load()
+    g = gs.gs_gaussians(100, FAKE, FAKE, FAKE, FAKE, FAKE)
+    c = cams(gs)
+    p = params(gs)
+    out = projected(gs)
+    ws_ok = gs.gs_project_workspace_size(100, 1)
+    call = lambda g_, c_, V, p_, o_, ws, nbytes: lib.gs_project(g_, c_, V, p_, o_, ws, nbytes, None)
+    assert call(None, c, 1, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+    assert call(ctypes.byref(g), None, 1, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+    assert call(ctypes.byref(g), c, 0, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+    assert call(ctypes.byref(g), c, 17, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+    bad = params(gs, sh_degree=4)
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(bad), ctypes.byref(out), FAKE, ws_ok) == 1
+    bad = params(gs, alpha_max=1.0)
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(bad), ctypes.byref(out), FAKE, ws_ok) == 1
+    small = projected(gs, capacity=50)
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(small), FAKE, ws_ok) == 1
+    assert b"capacity" in lib.gs_last_error()
+    nulls = projected(gs, null=("mean2d",))
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(nulls), FAKE, ws_ok) == 1
+    g_null = gs.gs_gaussians(100, FAKE, None, FAKE, FAKE, FAKE)
+    assert call(ctypes.byref(g_null), c, 1, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+    g_big = gs.gs_gaussians(1 << 28, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(ctypes.byref(g_big), c, 1, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+    # workspace too small -> capacity error, nothing launched
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok - 1) == 2
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(out), None, ws_ok) == 2
+    # views of different image sizes
+    from differentiable_raster_amd import scenes
+    mixed = gs.make_cameras([scenes.identity_camera(64, 48), scenes.identity_camera(32, 48)])
+    assert call(ctypes.byref(g), mixed, 2, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
+
+
+def test_bin_and_raster_reject_bad_arguments(gs):
+    lib = gs.load()
+    c = cams(gs)
+    p = params(gs)
+    proj = projected(gs)
+    bins = gs.gs_bins(1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    info = gs.gs_bin_info()
+    req = ctypes.c_int64()
+    ws = gs.gs_bin_workspace_size(100, 1, 64, 48, 1000)
+    assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(p), None, ctypes.byref(info), ctypes.byref(req),
+                            FAKE, ws, None) == 1
+    assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(p), ctypes.byref(bins), None, ctypes.byref(req),
+                            FAKE, ws, None) == 1
+    assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(p), ctypes.byref(bins), ctypes.byref(info),
+                            ctypes.byref(req), FAKE, ws - 1, None) == 2
+    capped = params(gs, tile_cap=64)
+    nocap = gs.gs_bins(1000, FAKE, FAKE, FAKE, None, None, None)
+    assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(capped), ctypes.byref(nocap), ctypes.byref(info),
+                            ctypes.byref(req), FAKE, ws, None) == 1
+    neg = params(gs, tile_cap=-1)
+    assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(neg), ctypes.byref(bins), ctypes.byref(info),
+                            ctypes.byref(req), FAKE, ws, None) == 1
+    grads = gs.gs_grads2d(FAKE, FAKE, FAKE, FAKE)
+    assert lib.gs_raster_fwd(c, ctypes.byref(proj), None, 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, None) == 1
+    assert lib.gs_raster_fwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, None, FAKE, FAKE, None,
+                             None) == 1
+    assert lib.gs_raster_bwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None,
+                             ctypes.byref(grads), None) == 1
+    bad_grads = gs.gs_grads2d(FAKE, None, FAKE, FAKE)
+    assert lib.gs_raster_bwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE,
+                             ctypes.byref(bad_grads), None) == 1
+    assert lib.gs_raster_fused(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, 7, FAKE,
+                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, None) == 1
+    assert lib.gs_raster_fused(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, 0, None,
+                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, None) == 1
+    assert lib.gs_loss_l1_grad(0, 64, 48, FAKE, FAKE, ctypes.c_float(1.0), FAKE, None, None) == 1
+    assert lib.gs_loss_l1_grad(1, 64, 48, None, FAKE, ctypes.c_float(1.0), FAKE, None, None) == 1
+
+
+def test_product_path_imports_no_oracle():
+    """The binding and the pipeline never import the oracle (it is test infrastructure)."""
+    pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle|from\s+\.\.?\s*import\s+oracle)|oracle[/.]|liboracle",
+                     re.M)
+    for f in ["gsmi.py", "pipeline.py", "scenes.py", "build.py", "__init__.py"]:
+        src = open(os.path.join(ROOT, "differentiable_raster_amd", f)).read()
+        assert not pat.search(src), f
+    for f in os.listdir(os.path.join(ROOT, "differentiable_raster_amd", "csrc")):
+        src = open(os.path.join(ROOT, "differentiable_raster_amd", "csrc", f)).read()
+        assert "oracle" not in src.lower(), f

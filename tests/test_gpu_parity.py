@@ -1,0 +1,216 @@
+"""HIP path vs the CPU oracle, through the C ABI, on seeded scenes (needs an MI355X)."""
+import numpy as np
+import pytest
+
+from differentiable_raster_amd import scenes
+from helpers import logit, pinhole, scene_from
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env(oracle_mod):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the gpu-marked tests")
+    from differentiable_raster_amd import gsmi, pipeline
+    gsmi.load()
+    return oracle_mod, pipeline, torch
+
+
+def run_view_checks(env, scene, settings, mode="separate", region=None, check_projection=True, views=None):
+    oracle, pipeline, torch = env
+    r = pipeline.Renderer(scene, settings)
+    r.project()
+    r.bin()
+    if mode == "separate":
+        r.forward()
+        dl = r.loss_grad(1.0)
+        r.backward(dl)
+    else:
+        r.fused(scale=1.0, image=True)
+    torch.cuda.synchronize()
+    img, T, nc = r.images_host()
+    dl_host = dl.view(r.V, 3, r.H, r.W).cpu().numpy() if mode == "separate" else None
+    capped = settings.tile_cap > 0
+    for v in (range(r.V) if views is None else views):
+        cam = scene.cameras[v]
+        print(f"[parity] {scene.name} view {v} mode {mode} cap {settings.tile_cap}", flush=True)
+        gpu = r.projected_host(v)
+        if check_projection:
+            parity.compare_projection(oracle, scene, cam, settings, gpu)
+        bins_g = r.bins_host(v)
+        b = parity.compare_binning(oracle, cam, gpu, bins_g)
+        ranges, vals = b["ranges"], b["vals"]
+        if capped:
+            cg = r.bins_host(v, capped=True)
+            c = parity.compare_cap(oracle, gpu, b, cg, settings.tile_cap)
+            ranges, vals = c["ranges"], c["vals"]
+        rec = parity.gpu_records(gpu)
+        f = parity.compare_forward(oracle, cam, settings, rec, ranges, vals, img[v], T[v], nc[v], region=region)
+        if mode == "separate":
+            dldc = dl_host[v].astype(np.float64)
+            extra = None
+        else:
+            if scene.loss == "l1":
+                dldc, extra = oracle.loss_grad_l1(f["image"], scene.target[v], 1.0, f["err_C"])
+            else:
+                dldc, extra = scene.dldc[v].astype(np.float64), None
+        parity.compare_backward(oracle, cam, settings, rec, ranges, vals, dldc, r.grads_host(v), f, region=region,
+                                extra_skip=extra, slots_rect=gpu["rect"])
+    return r
+
+
+def test_library_binds_to_torch_hip_runtime(env):
+    oracle, pipeline, torch = env
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+    assert any("libgsmi.so" in line for line in maps.splitlines())
+
+
+@pytest.mark.parametrize("mode", ["separate", "fused"])
+def test_tiny_scene(env, mode):
+    sc = scenes.make_scene(1)
+    run_view_checks(env, sc, sc.settings(), mode=mode)
+
+
+@pytest.mark.parametrize("seed,views,size", [(101, 2, (100, 75)), (102, 3, (130, 47)), (103, 1, (16, 16))])
+def test_random_multiview_ragged(env, seed, views, size):
+    sc = scenes.random_scene(3000, size[0], size[1], seed=seed, views=views, log_scale_mean=-3.2, sh_degree=2,
+                             opacity_std=1.5)
+    run_view_checks(env, sc, sc.settings(), mode="separate")
+    run_view_checks(env, sc, sc.settings(), mode="fused", check_projection=False)
+
+
+@pytest.mark.parametrize("K", [1, 7, 64])
+def test_tile_cap(env, K):
+    sc = scenes.random_scene(6000, 96, 64, seed=200 + K, views=2, log_scale_mean=-3.0, opacity_std=1.5)
+    run_view_checks(env, sc, sc.settings(tile_cap=K), mode="fused", check_projection=False)
+    run_view_checks(env, sc, sc.settings(tile_cap=K), mode="separate", check_projection=False)
+
+
+def test_background_and_external_gradient(env):
+    sc = scenes.random_scene(2500, 80, 64, seed=301, views=2, loss="external", sh_degree=1)
+    st = sc.settings(bg=(0.2, 0.5, 0.8))
+    run_view_checks(env, sc, st, mode="fused")
+    run_view_checks(env, sc, st, mode="separate", check_projection=False)
+
+
+def test_long_lists_take_the_chunked_fused_path(env):
+    """4000 Gaussians in one tile: longer than the fused kernel's LDS-resident budget."""
+    oracle, pipeline, torch = env
+    from differentiable_raster_amd import gsmi
+    assert gsmi.gs_fused_max_cap() < 4000
+    rng = np.random.default_rng(5)
+    n = 4000
+    cam = pinhole(32, 32, f=40.0, cx=16.0, cy=16.0)
+    means = np.stack([rng.uniform(-0.15, 0.15, n), rng.uniform(-0.15, 0.15, n), rng.uniform(2, 3, n)], 1)
+    sc = scene_from(means, np.full((n, 3), -4.0), rng.standard_normal((n, 4)), rng.normal(-3.0, 1.0, n),
+                    rng.uniform(0, 1, (n, 3)), [cam], target=rng.uniform(0, 1, (1, 3, 32, 32)))
+    r = run_view_checks(env, sc, sc.settings(), mode="fused")
+    assert r.info.num_instances > 4000
+    run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
+
+
+def test_fused_equals_separate(env):
+    oracle, pipeline, torch = env
+    sc = scenes.make_scene(1)
+    st = sc.settings()
+    a = pipeline.Renderer(sc, st)
+    a.project(); a.bin(); a.forward(); a.backward(a.loss_grad(1.0))
+    b = pipeline.Renderer(sc, st)
+    b.project(); b.bin(); b.fused(image=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.images_host()[0], b.images_host()[0]), "images differ between fused and separate"
+    ga, gb = a.grads_host(0), b.grads_host(0)
+    for k in ga:
+        assert parity.close(gb[k].astype(np.float64), ga[k].astype(np.float64), 1e-3, 1e-6).all(), k
+
+
+def test_counters_match_oracle(env):
+    oracle, pipeline, torch = env
+    sc = scenes.make_scene(1)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.project(); r.bin(); r.forward(counters=True)
+    torch.cuda.synchronize()
+    ev, bl = [int(x) for x in r.counters.cpu().numpy()]
+    ref = oracle.iteration(sc, st, backward=False)[0]["fwd"]
+    # the GPU walks every pixel of a tile until the whole tile stops; blends are exact up to
+    # flagged decisions
+    assert abs(bl - ref["n_blended"]) <= 50, (bl, ref["n_blended"])
+    assert ev >= ref["n_evaluated"] * 0.99
+
+
+def test_empty_and_fully_culled_scenes(env):
+    oracle, pipeline, torch = env
+    cam = pinhole(40, 24, f=30.0, cx=20.0, cy=12.0)
+    behind = scene_from([[0, 0, -2.0], [0.1, 0, -3.0]], [[-2] * 3] * 2, [[1, 0, 0, 0]] * 2, [2.0, 2.0],
+                        [[1, 1, 1]] * 2, [cam])
+    for sc in [behind]:
+        for bg in [(0.0, 0.0, 0.0), (0.3, 0.2, 0.1)]:
+            st = sc.settings(bg=bg)
+            for mode in ["separate", "fused"]:
+                r = pipeline.Renderer(sc, st)
+                r.iteration(mode=mode, image=True)
+                torch.cuda.synchronize()
+                img, T, nc = r.images_host()
+                assert r.info.num_instances == 0 and int(r.vis_count[0].item()) == 0
+                assert (T == 1).all() and (nc == 0).all()
+                for ch in range(3):
+                    assert (img[0, ch] == np.float32(bg[ch])).all()
+    # n = 0
+    empty = scene_from(np.zeros((0, 3)), np.zeros((0, 3)), np.zeros((0, 4)), np.zeros(0), np.zeros((0, 3)), [cam])
+    r = pipeline.Renderer(empty, empty.settings())
+    r.iteration(mode="fused", image=True)
+    torch.cuda.synchronize()
+    assert (r.images_host()[1] == 1).all()
+
+
+def test_gaussian_covering_every_tile_and_image_edges(env):
+    cam = pinhole(72, 40, f=50.0, cx=36.0, cy=20.0)
+    rows = [([0, 0, 2.0], [-0.3] * 3, 0.5),      # huge: covers every tile
+            ([0.72, 0.4, 1.0], [-3.0] * 3, 1.0),  # near the right/bottom edge
+            ([-0.72, -0.4, 1.0], [-3.0] * 3, 1.0),  # near the top-left corner
+            ([0.0, 0.0, 0.2001], [-3.0] * 3, 1.0)]  # just beyond the near plane
+    sc = scene_from([r[0] for r in rows], [r[1] for r in rows], [[1, 0, 0, 0]] * 4, [r[2] for r in rows],
+                    [[0.2, 0.4, 0.6]] * 4, [cam], target=np.full((1, 3, 40, 72), 0.5))
+    r = run_view_checks(env, sc, sc.settings(), mode="fused")
+    assert r.info.num_instances >= cam.tiles_x * cam.tiles_y
+    run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
+
+
+def test_capacity_error_then_retry(env):
+    oracle, pipeline, torch = env
+    from differentiable_raster_amd import gsmi
+    sc = scenes.make_scene(1)
+    r = pipeline.Renderer(sc, sc.settings(), instance_capacity=10)
+    r.project()
+    st, info, req = gsmi.gs_bin_tiles(r.cams, r.proj, r.V, r.params, r.bins, r.ws_bin)
+    assert st == 2 and req > 10
+    r.bin()
+    assert r.info.num_instances == req
+
+
+def test_integer_outputs_are_deterministic(env):
+    oracle, pipeline, torch = env
+    sc = scenes.random_scene(8000, 160, 120, seed=77, views=2, log_scale_mean=-3.0)
+    out = []
+    for _ in range(2):
+        r = pipeline.Renderer(sc, sc.settings(tile_cap=16))
+        r.iteration(mode="fused", image=True)
+        torch.cuda.synchronize()
+        out.append((r.vals[:r.info.num_instances].cpu().numpy(), r.ranges.cpu().numpy(),
+                    r.vals_capped[:int(r.num_capped.item())].cpu().numpy(), r.images_host()))
+    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
+    assert np.array_equal(out[0][2], out[1][2])
+    for a, b in zip(out[0][3], out[1][3]):
+        assert np.array_equal(a, b)
+
+
+def test_scene_100k_720p_external_gradient(env):
+    sc = scenes.make_scene(2)
+    run_view_checks(env, sc, sc.settings(), mode="fused")
+    run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
