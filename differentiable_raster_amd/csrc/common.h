@@ -50,6 +50,13 @@ __device__ __forceinline__ float pair_power(float dx, float dy, float A, float B
 
 __device__ __forceinline__ float pair_gauss(float power) { return __expf(power); }
 
+// 1 - alpha.  Unclamped (v = o G <= alpha_max) it is 1 - o G with a single rounding, which
+// keeps the relative error of a small 1 - alpha (alpha near alpha_max) from growing by the
+// rounding of alpha itself; clamped it is 1 - alpha_max.
+__device__ __forceinline__ float one_minus_alpha(float o, float G, float v, float amax) {
+    return v <= amax ? fmaf(-o, G, 1.0f) : 1.0f - amax;
+}
+
 // ---------------------------------------------------------------------------------------
 // Launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------------------

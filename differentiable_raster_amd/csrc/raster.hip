@@ -82,10 +82,11 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float4 co = s.co[k];
         const float dx = c.fpx - xy.x, dy = c.fpy - xy.y;
         const float G = pair_gauss(pair_power(dx, dy, co.x, co.y, co.z));
-        const float alpha = fminf(amax, co.w * G);
+        const float v = co.w * G;
+        const float alpha = fminf(amax, v);
         if (COUNT) n_eval++;
         if (alpha < amin) continue;
-        const float Tn = f.T * (1.0f - alpha);
+        const float Tn = f.T * one_minus_alpha(co.w, G, v, amax);
         if (Tn < tmin) {
             f.done = true;
             break;
@@ -132,7 +133,7 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
             const float alpha = fminf(amax, v);
             if (alpha >= amin) {
                 contrib = true;
-                const float oma = 1.0f - alpha;
+                const float oma = one_minus_alpha(co.w, G, v, amax);
                 const float Tj = b.T / oma;
                 const float4 rgb = s.rgb[k];
                 const float bgterm = b.Tfin / oma;

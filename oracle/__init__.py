@@ -259,14 +259,16 @@ def raster_forward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray
     nc = np.zeros((height, width), np.int32)
     flag = np.zeros((height, width), np.int8)
     err = np.zeros((height, width))
+    err_T = np.zeros((height, width))
     counters = np.zeros(3, np.int64)
     ranges = np.ascontiguousarray(ranges, np.int32)
     vals = np.ascontiguousarray(vals, np.int32)
     pp = _params(settings)
     m, c, o, col = _rec(records)
     lib.orc_raster_forward(ctypes.c_int32(width), ctypes.c_int32(height), _p(ranges), _p(vals), _p(m), _p(c), _p(o),
-                           _p(col), ctypes.byref(pp), _p(image), _p(T), _p(nc), _p(flag), _p(err), _p(counters))
-    return dict(image=image, T_final=T, n_contrib=nc, flag=flag.astype(bool), err_C=err,
+                           _p(col), ctypes.byref(pp), _p(image), _p(T), _p(nc), _p(flag), _p(err), _p(err_T),
+                           _p(counters))
+    return dict(image=image, T_final=T, n_contrib=nc, flag=flag.astype(bool), err_C=err, err_T=err_T,
                 n_evaluated=int(counters[0]), n_blended=int(counters[1]), n_clamped=int(counters[2]))
 
 

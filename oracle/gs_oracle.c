@@ -303,7 +303,7 @@ typedef struct {
 static int composite_pixel(double px, double py, const int32_t* list, int n, const orc_records* r,
                            const orc_params* p, double C[3], double* T_out, orc_blend* log,
                            int* n_log, int* flag, int* flag_clamp, int64_t* n_eval, int64_t* n_blend,
-                           double* err_C, int8_t* touch)
+                           double* err_C, int8_t* touch, double* err_T)
 {
     double T = 1.0;
     double errT = 0.0;   /* relative error model of T in float32 */
@@ -362,6 +362,7 @@ static int composite_pixel(double px, double py, const int32_t* list, int n, con
     for (int ch = 0; ch < 3; ch++) C[ch] += T * p->bg[ch];
     eC += T * fmax(fabs(p->bg[0]), fmax(fabs(p->bg[1]), fabs(p->bg[2]))) * (errT + EPS32);
     if (err_C) *err_C = eC;
+    if (err_T) *err_T = errT;
     *T_out = T;
     return n_contrib;
 }
@@ -371,13 +372,13 @@ static int composite_pixel(double px, double py, const int32_t* list, int n, con
  * ranges[tile][2] = [start, end) into vals; vals[] = slot of each list entry; tiles are
  * row-major with tiles_x = ceil(W / tile).  Outputs: image[3][H][W], T_final[H][W],
  * n_contrib[H][W], flag[H][W] (decision within float32 reach), err_C[H][W] (float32 error
- * model of the colour), counters[3] = {evaluated pairs, blended pairs, blended pairs whose
+ * model of the colour, absolute), err_T[H][W] (float32 error model of T_final, relative), counters[3] = {evaluated pairs, blended pairs, blended pairs whose
  * alpha was clamped}.
  */
 void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals,
                         const double* mean2d, const double* conic, const double* opacity,
                         const double* color, const orc_params* p, double* image, double* T_final,
-                        int32_t* n_contrib, int8_t* flag, double* err_C, int64_t* counters)
+                        int32_t* n_contrib, int8_t* flag, double* err_C, double* err_T, int64_t* counters)
 {
     const int tile = p->tile;
     const int tx_n = (W + tile - 1) / tile, ty_n = (H + tile - 1) / tile;
@@ -389,17 +390,18 @@ void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32
         const int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
         for (int y = ty * tile; y < (ty + 1) * tile && y < H; y++)
             for (int x = tx * tile; x < (tx + 1) * tile && x < W; x++) {
-                double C[3], T, eC;
+                double C[3], T, eC, eT;
                 int f = 0, fc = 0;
                 int64_t ne = 0, nb[2] = {0, 0};
                 const int nc = composite_pixel(x + 0.5, y + 0.5, vals + start, end - start, &r, p, C, &T,
-                                               NULL, NULL, &f, &fc, &ne, nb, &eC, NULL);
+                                               NULL, NULL, &f, &fc, &ne, nb, &eC, NULL, &eT);
                 const int64_t px = (int64_t)y * W + x;
                 for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = C[ch];
                 T_final[px] = T;
                 n_contrib[px] = nc;
                 flag[px] = (int8_t)(f ? 1 : 0);
                 err_C[px] = eC;
+                err_T[px] = eT;
                 tot_eval += ne;
                 tot_blend += nb[0];
                 tot_clamp += nb[1];
@@ -455,7 +457,7 @@ void orc_raster_backward(int32_t W, int32_t H, const int32_t* ranges, const int3
                     int f = 0, fc = 0, nl = 0;
                     int64_t n_evaluated = 0;
                     composite_pixel(x + 0.5, y + 0.5, list, end - start, &r, p, C, &T_fin, log, &nl, &f, &fc,
-                                    &n_evaluated, NULL, NULL, touch);
+                                    &n_evaluated, NULL, NULL, touch, NULL);
                     if (f || fc || (pixel_skip && pixel_skip[px])) {
                         /* the slots this pixel blends, or could blend under float32 decisions */
                         for (int j = 0; j < (int)n_evaluated; j++)
@@ -531,7 +533,7 @@ void orc_raster_bruteforce(int32_t W, int32_t H, const int32_t* order, int32_t n
             double C[3], T;
             int f = 0, fc = 0;
             const int nc = composite_pixel(x + 0.5, y + 0.5, order, n, &r, p, C, &T, NULL, NULL, &f, &fc, NULL,
-                                           NULL, NULL, NULL);
+                                           NULL, NULL, NULL, NULL);
             const int64_t px = (int64_t)y * W + x;
             for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = C[ch];
             T_final[px] = T;

@@ -7,15 +7,22 @@ Comparison contract (stage-isolated, so that every integer result is compared bi
     reproduce tile keys, order, ranges and capped lists exactly;
   * forward: the oracle composites the GPU's records over the GPU's lists in double
     precision; image and T_final within 1e-5 relative + 1e-7 absolute, n_contrib exact, on
-    pixels whose decisions are not within float32 reach;
+    pixels whose decisions are not within float32 reach; for the image, plus the oracle's
+    first-order float32 error bound of the pixel (large only behind near-opaque splats, where
+    1 / (1 - alpha) amplifies the rounding of alpha), with the count of components that pass
+    only through it reported;
   * backward: gradients within 1e-3 relative + 1e-6 absolute on slots that no flagged pixel
-    blends (dL/dC scaled to O(1): L1 summed, scale 1).
+    blends (dL/dC scaled to O(1): L1 summed, scale 1), plus 1e-5 times the summed magnitude of
+    the component's contributions, which bounds float32 error when the contributions cancel;
+    the report counts the comparisons that pass only through that term.
 """
 import numpy as np
 
 EPS32 = 2.0 ** -24
 IMG_RTOL, IMG_ATOL = 1e-5, 1e-7
+IMG_COND_FACTOR = 1.0  # times the oracle's float32 error bound of the pixel colour
 GRAD_RTOL, GRAD_ATOL = 1e-3, 1e-6
+GRAD_MAG_TOL = 1e-5  # times the summed |contributions| of a gradient component
 
 
 def close(a, b, rtol, atol):
@@ -112,18 +119,30 @@ def pixel_mask(cam, region):
 
 
 def compare_forward(oracle, cam, settings, rec, ranges, vals, img_g, T_g, nc_g, region=None):
+    """T_g / nc_g may be None (the fused kernel returns only the image)."""
     r = region_ranges(ranges, cam.tiles_x, region)
     f = oracle.raster_forward(cam.width, cam.height, r, vals, rec, settings)
     sel = pixel_mask(cam, region) & ~f["flag"]
-    ok_img = close(img_g[:, sel].astype(np.float64), f["image"][:, sel], IMG_RTOL, IMG_ATOL)
-    ok_T = close(T_g[sel].astype(np.float64), f["T_final"][sel], IMG_RTOL, IMG_ATOL)
-    ok_nc = nc_g[sel] == f["n_contrib"][sel]
+    go, oo = img_g[:, sel].astype(np.float64), f["image"][:, sel]
+    strict = close(go, oo, IMG_RTOL, IMG_ATOL)
+    # conditioning: behind a near-opaque splat the float32 rounding of alpha is amplified by
+    # 1 / (1 - alpha) in T; the oracle's first-order float32 error bound err_C covers it
+    cond = IMG_COND_FACTOR * f["err_C"][sel][None, :]
+    ok_img = np.abs(go - oo) <= IMG_RTOL * np.abs(oo) + IMG_ATOL + cond
     nflag = int((pixel_mask(cam, region) & f["flag"]).sum())
-    bad = report("image", ok_img, f"({nflag} flagged pixels skipped)") + report("T_final", ok_T) + \
-        report("n_contrib", ok_nc)
+    bad = report("image", ok_img, f"({nflag} flagged pixels skipped; {int((ok_img & ~strict).sum())} within "
+                                  f"tolerance only through the conditioning term)")
+    if T_g is not None:
+        To = f["T_final"][sel]
+        ok_T = np.abs(T_g[sel].astype(np.float64) - To) <= IMG_RTOL * To + IMG_ATOL + \
+            IMG_COND_FACTOR * f["err_T"][sel] * To
+        ok_nc = nc_g[sel] == f["n_contrib"][sel]
+        bad += report("T_final", ok_T) + report("n_contrib", ok_nc)
     if bad:
-        err = np.abs(img_g[:, sel].astype(np.float64) - f["image"][:, sel]) / (np.abs(f["image"][:, sel]) + 1e-7)
-        print("[parity] worst image rel err", float(err.max()), flush=True)
+        err = np.abs(go - oo)
+        worst = np.unravel_index(np.argmax(err / (IMG_RTOL * np.abs(oo) + IMG_ATOL + cond)), err.shape)
+        print(f"[parity] worst image component: gpu {go[worst]:.9g} oracle {oo[worst]:.9g} "
+              f"err {err[worst]:.3g} err_C {f['err_C'][sel][worst[1]]:.3g}", flush=True)
     assert bad == 0
     return f
 
@@ -143,11 +162,17 @@ def compare_backward(oracle, cam, settings, rec, ranges, vals, dldc, grads_g, fw
         rc = slots_rect
         use &= (rc[:, 0] >= tx0) & (rc[:, 2] <= tx1) & (rc[:, 1] >= ty0) & (rc[:, 3] <= ty1)
     total_bad = 0
+    mag_cols = {"d_mean2d": [0, 1], "d_conic": [2, 3, 4], "d_opacity": [5], "d_color": [6, 7, 8]}
     for key, k in [("d_mean2d", 2), ("d_conic", 3), ("d_opacity", 1), ("d_color", 3)]:
         go = b[key].reshape(S, k)[use]
         gg = grads_g[key].reshape(S, k)[use].astype(np.float64)
-        ok = close(gg, go, GRAD_RTOL, GRAD_ATOL)
-        bad = report(key, ok, f"({int((~use).sum())} slots skipped)")
+        mag = b["mag"][:, mag_cols[key]][use]
+        strict = close(gg, go, GRAD_RTOL, GRAD_ATOL)
+        # cancellation: the float32 sum of contributions whose magnitudes add up to `mag`
+        # carries an error proportional to mag, not to the (possibly much smaller) result
+        ok = np.abs(gg - go) <= GRAD_RTOL * np.abs(go) + GRAD_ATOL + GRAD_MAG_TOL * mag
+        bad = report(key, ok, f"({int((~use).sum())} slots skipped; {int((ok & ~strict).sum())} within "
+                              f"tolerance only through the cancellation term)")
         if bad:
             i = np.argwhere(~ok)[:5]
             for (s, c) in i:

@@ -48,7 +48,9 @@ def run_view_checks(env, scene, settings, mode="separate", region=None, check_pr
             c = parity.compare_cap(oracle, gpu, b, cg, settings.tile_cap)
             ranges, vals = c["ranges"], c["vals"]
         rec = parity.gpu_records(gpu)
-        f = parity.compare_forward(oracle, cam, settings, rec, ranges, vals, img[v], T[v], nc[v], region=region)
+        sep = mode == "separate"
+        f = parity.compare_forward(oracle, cam, settings, rec, ranges, vals, img[v], T[v] if sep else None,
+                                   nc[v] if sep else None, region=region)
         if mode == "separate":
             dldc = dl_host[v].astype(np.float64)
             extra = None
@@ -158,15 +160,17 @@ def test_empty_and_fully_culled_scenes(env):
                 torch.cuda.synchronize()
                 img, T, nc = r.images_host()
                 assert r.info.num_instances == 0 and int(r.vis_count[0].item()) == 0
-                assert (T == 1).all() and (nc == 0).all()
+                if mode == "separate":
+                    assert (T == 1).all() and (nc == 0).all()
                 for ch in range(3):
                     assert (img[0, ch] == np.float32(bg[ch])).all()
     # n = 0
     empty = scene_from(np.zeros((0, 3)), np.zeros((0, 3)), np.zeros((0, 4)), np.zeros(0), np.zeros((0, 3)), [cam])
-    r = pipeline.Renderer(empty, empty.settings())
-    r.iteration(mode="fused", image=True)
-    torch.cuda.synchronize()
-    assert (r.images_host()[1] == 1).all()
+    for mode in ["separate", "fused"]:
+        r = pipeline.Renderer(empty, empty.settings())
+        r.iteration(mode=mode, image=True)
+        torch.cuda.synchronize()
+        assert (r.images_host()[0] == 0).all()
 
 
 def test_gaussian_covering_every_tile_and_image_edges(env):
@@ -203,11 +207,10 @@ def test_integer_outputs_are_deterministic(env):
         r.iteration(mode="fused", image=True)
         torch.cuda.synchronize()
         out.append((r.vals[:r.info.num_instances].cpu().numpy(), r.ranges.cpu().numpy(),
-                    r.vals_capped[:int(r.num_capped.item())].cpu().numpy(), r.images_host()))
+                    r.vals_capped[:int(r.num_capped.item())].cpu().numpy(), r.images_host()[0]))
     assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
     assert np.array_equal(out[0][2], out[1][2])
-    for a, b in zip(out[0][3], out[1][3]):
-        assert np.array_equal(a, b)
+    assert np.array_equal(out[0][3], out[1][3])
 
 
 def test_scene_100k_720p_external_gradient(env):
