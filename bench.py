@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of one training iteration of tile-based differentiable 3D Gaussian splatting on one
+MI355X: project -> bin (radix sort) -> fused forward + L1 gradient + backward, for all views.
+
+Default workload: 1M Gaussians in 64 blobs, 1920x1080, a batch of 4 ring views, SH degree 3
+(the synthetic stand-in for the pages' large-scene captures).  Prints ONE JSON line with
+Gaussian-pixel blends per second (fwd+bwd), ms per iteration, the fused rasterizer's roofline
+figures and the CPU oracle's rate on the host as a baseline.  Everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gaussian-pixel blends/s (fwd+bwd) and ms/iter, 1M Gaussians @1080p, 1 GPU"
+# Algorithmic float32 operations (FMA = 2) of the fused rasterizer, per unit:
+FLOPS_PER_BOX_PAIR = 16   # evaluate one (pixel, Gaussian) pair inside the Gaussian's alpha box
+FLOPS_PER_BLEND = 81      # blend it in the forward (11) and back-propagate it (70)
+# Non-packed float32 vector peak of MI355X: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz.
+ALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_raster_fused_1m_1080p.md")
+RASTER_SRC = os.path.join(ROOT, "differentiable_raster_amd", "csrc", "raster.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per fused launch from the committed rocprofv3 counter summary, if it was taken
+    on the current rasterizer source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = hashlib.sha256(open(RASTER_SRC, "rb").read()).hexdigest()
+    if vals.get("raster.hip sha256") != src:
+        return None
+    try:
+        return float(vals["hbm bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(scene, settings, views):
+    import oracle
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    res = oracle.iteration(scene, settings, loss_scale=1.0, views=views, backward=True)
+    dt = time.perf_counter() - t0
+    blends = sum(r["fwd"]["n_blended"] for r in res)
+    return dict(value=blends / dt, unit="blends/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{len(views)} of {len(scene.cameras)} views of the same workload, full iteration "
+                       f"(project, bin, forward, L1 gradient, backward) in float64: {blends} blends in {dt:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload 1..5 (3 = 1M Gaussians @1080p)")
+    ap.add_argument("--cap", type=int, default=0, help="per-tile cap K (0 = off)")
+    ap.add_argument("--cpu-views", type=int, default=4, help="views of the workload the CPU oracle times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); this build "
+              f"has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from differentiable_raster_amd import gsmi, pipeline, scenes
+    gsmi.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t = time.perf_counter()
+    scene = scenes.make_scene(args.workload)
+    settings = scene.settings(tile_cap=args.cap)
+    log(f"[bench] workload {args.workload} ({scene.name}) generated in {time.perf_counter() - t:.1f} s")
+    r = pipeline.Renderer(scene, settings, device="cuda:0")
+
+    # sizing pass and algorithmic counts (outside the timed region)
+    r.project()
+    info = r.bin()
+    r.forward(counters=True)
+    torch.cuda.synchronize()
+    E_eval, B, E_box = [int(x) for x in r.counters.cpu().tolist()]
+    vis = [info.vis_count[v] for v in range(r.V)]
+    M = int(info.num_instances)
+    log(f"[bench] visible {vis}, instances {M}, evaluated pairs {E_eval}, box pairs {E_box}, blends {B}")
+
+    def stage_times(mode):
+        ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for k in ("project", "bin", "raster")}
+        ev["project"][0].record(); r.project(); ev["project"][1].record()
+        ev["bin"][0].record(); r.bin(); ev["bin"][1].record()
+        ev["raster"][0].record()
+        if mode == "fused":
+            r.fused(image=False)
+        else:
+            r.forward()
+            r.backward(r.loss_grad(1.0))
+        ev["raster"][1].record()
+        torch.cuda.synchronize()
+        return {k: a.elapsed_time(b) for k, (a, b) in ev.items()}
+
+    def run(mode, steps, warmup):
+        for _ in range(warmup):
+            r.iteration(mode=mode)
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            r.project()
+            r.bin()
+            starts[k].record()
+            if mode == "fused":
+                r.fused(image=False)
+            else:
+                r.forward()
+                r.backward(r.loss_grad(1.0))
+            ends[k].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        raster_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+        return (t1 - t0) * 1000.0 / steps, raster_ms
+
+    ms_fused, raster_fused_ms = run("fused", args.steps, args.warmup)
+    stages_fused = stage_times("fused")
+    ms_sep, raster_sep_ms = run("separate", max(3, args.steps // 4), 1)
+    stages_sep = stage_times("separate")
+    log(f"[bench] fused: {ms_fused:.3f} ms/iter (raster call {raster_fused_ms:.3f} ms); "
+        f"separate: {ms_sep:.3f} ms/iter (raster calls {raster_sep_ms:.3f} ms)")
+
+    flops = FLOPS_PER_BOX_PAIR * E_box + FLOPS_PER_BLEND * B
+    achieved = flops / (raster_fused_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": B / (ms_fused * 1e-3),
+        "unit": "blends/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_fused,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{scene.name}: {scene.n} Gaussians, {r.W}x{r.H}, {r.V} views, SH degree "
+                        f"{scene.sh_degree}, project + bin + fused fwd/L1/bwd"
+                        + (f", tile cap {args.cap}" if args.cap else ""),
+            "gaussians": scene.n, "width": r.W, "height": r.H, "views": r.V, "tile_cap": args.cap,
+        },
+        "roofline": {
+            "kernel": "raster_fused (gs_raster_fused call: gradient zeroing + fused kernel)",
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": ALU_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / ALU_PEAK_TFLOPS,
+            "traffic": traffic,
+            "algorithmic_flops": flops,
+            "launch_ms": raster_fused_ms,
+            "hbm_frac_algorithmic": None,
+        },
+        "counts": {"visible": vis, "instances": M, "evaluated_pairs": E_eval, "box_pairs": E_box, "blends": B},
+        "stages_ms": {"fused": stages_fused, "separate": stages_sep},
+        "separate_path": {"ms_per_step": ms_sep, "blends_per_s": B / (ms_sep * 1e-3), "raster_ms": raster_sep_ms},
+        "cpu_baseline": None,
+    }
+    # the fused kernel's algorithmic HBM bytes: records of every list entry it stages (40 B per
+    # entry incl. the slot id), the target image (12 B/px) and one float atomic per gradient
+    # component and entry (9 x 4 B read-modify-write).
+    alg_bytes = 40 * M + 12 * r.V * r.W * r.H + 72 * M
+    out["roofline"]["hbm_frac_algorithmic"] = alg_bytes / (raster_fused_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    if not args.no_cpu_baseline:
+        views = list(range(min(args.cpu_views, r.V)))
+        out["cpu_baseline"] = cpu_baseline(scene, settings, views)
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -72,9 +72,22 @@ struct Fwd {
 };
 
 // Front-to-back over records [k0, k1) of LDS, list positions j = jbase + k.
+// Diagnostic only: is the pixel inside the exact bounding box of {o exp(-q/2) >= alpha_min}?
+__device__ __forceinline__ bool in_alpha_box(float dx, float dy, float4 co, float amin) {
+    if (!(co.w > amin)) return false;
+    const float det = co.x * co.z - co.y * co.y;
+    const float Q = 2.0f * logf(co.w / amin);
+    const float ex = 1.001f * sqrtf(Q * co.z / det), ey = 1.001f * sqrtf(Q * co.x / det);
+    return fabsf(dx) <= ex && fabsf(dy) <= ey;
+}
+
+struct Counts {
+    int64_t eval, blend, box;
+};
+
 template <bool COUNT>
 __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, Lds s, int k0, int k1, int32_t jbase,
-                                         Fwd& f, int64_t& n_eval, int64_t& n_blend) {
+                                         Fwd& f, Counts& cnt) {
     if (f.done) return;
     const float amin = a.p.alpha_min, amax = a.p.alpha_max, tmin = a.p.t_min;
     for (int k = k0; k < k1; k++) {
@@ -84,7 +97,10 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float G = pair_gauss(pair_power(dx, dy, co.x, co.y, co.z));
         const float v = co.w * G;
         const float alpha = fminf(amax, v);
-        if (COUNT) n_eval++;
+        if (COUNT) {
+            cnt.eval++;
+            cnt.box += in_alpha_box(dx, dy, co, amin) ? 1 : 0;
+        }
         if (alpha < amin) continue;
         const float Tn = f.T * one_minus_alpha(co.w, G, v, amax);
         if (Tn < tmin) {
@@ -98,7 +114,7 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         f.C2 = fmaf(wgt, rgb.z, f.C2);
         f.T = Tn;
         f.last = jbase + k + 1;
-        if (COUNT) n_blend++;
+        if (COUNT) cnt.blend++;
     }
 }
 
@@ -188,15 +204,17 @@ __device__ __forceinline__ int block_max(int x, int* s_red) {
     return m;
 }
 
-__device__ __forceinline__ void add_counters(int64_t* counters, int64_t e, int64_t b) {
+__device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
     // wave sums then one atomic per wave
     for (int o = kWave / 2; o > 0; o >>= 1) {
-        e += __shfl_xor(e, o);
-        b += __shfl_xor(b, o);
+        c.eval += __shfl_xor(c.eval, o);
+        c.blend += __shfl_xor(c.blend, o);
+        c.box += __shfl_xor(c.box, o);
     }
     if ((threadIdx.x & (kWave - 1)) == 0) {
-        atomicAdd((unsigned long long*)&counters[0], (unsigned long long)e);
-        atomicAdd((unsigned long long*)&counters[1], (unsigned long long)b);
+        atomicAdd((unsigned long long*)&counters[0], (unsigned long long)c.eval);
+        atomicAdd((unsigned long long*)&counters[1], (unsigned long long)c.blend);
+        atomicAdd((unsigned long long*)&counters[2], (unsigned long long)c.box);
     }
 }
 
@@ -210,16 +228,16 @@ __global__ __launch_bounds__(kBlock) void raster_fwd_kernel(RasterArgs a, float*
     const Lds s{s_xy, s_co, s_rgb, s_slot};
     const TileCtx c = tile_ctx(a, a.ranges);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
-    int64_t ne = 0, nbl = 0;
+    Counts cnts{0, 0, 0};
     for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
         if (__syncthreads_count(f.done) == kBlock) break;
         const int32_t j = b0 + threadIdx.x;
         if (j < c.n) stage(a, c, s, threadIdx.x, j);
         __syncthreads();
         const int cnt = min(kBatch, c.n - b0);
-        fwd_walk<COUNT>(a, c, s, 0, cnt, b0, f, ne, nbl);
+        fwd_walk<COUNT>(a, c, s, 0, cnt, b0, f, cnts);
     }
-    if (COUNT) add_counters(a.counters, ne, nbl);
+    if (COUNT) add_counters(a.counters, cnts);
     if (!c.inside) return;
     const size_t plane = (size_t)a.width * a.height;
     const size_t p = (size_t)c.py * a.width + c.px;
@@ -311,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
     const bool resident = c.n <= kFusedEntries;
     // forward
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
-    int64_t ne = 0, nbl = 0;
+    Counts cnts{0, 0, 0};
     int32_t loaded = 0;  // resident entries staged so far
     for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
         if (__syncthreads_count(f.done) == kBlock) break;
@@ -320,10 +338,10 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
         if (j < c.n) stage(a, c, s, base + threadIdx.x, j);
         __syncthreads();
         const int cnt = min(kBatch, c.n - b0);
-        fwd_walk<COUNT>(a, c, s, base, base + cnt, b0 - base, f, ne, nbl);
+        fwd_walk<COUNT>(a, c, s, base, base + cnt, b0 - base, f, cnts);
         loaded = b0 + cnt;
     }
-    if (COUNT) add_counters(a.counters, ne, nbl);
+    if (COUNT) add_counters(a.counters, cnts);
     // loss gradient in registers
     const size_t plane = (size_t)a.width * a.height;
     const size_t p = (size_t)c.py * a.width + c.px;

@@ -67,7 +67,13 @@ def _load():
         _lib.orc_raster_forward.restype = None
         _lib.orc_raster_backward.restype = None
         _lib.orc_raster_bruteforce.restype = None
+        _lib.orc_num_threads.restype = ctypes.c_int
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 def _p(a: np.ndarray):

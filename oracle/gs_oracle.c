@@ -29,6 +29,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC gs_oracle.c -lm
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -539,4 +540,10 @@ void orc_raster_bruteforce(int32_t W, int32_t H, const int32_t* order, int32_t n
             T_final[px] = T;
             n_contrib[px] = nc; /* position in the global order, not in a tile list */
         }
+}
+
+/* Threads the parallel loops above use (for reporting the CPU baseline). */
+int orc_num_threads(void)
+{
+    return omp_get_max_threads();
 }

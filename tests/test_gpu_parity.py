@@ -138,7 +138,8 @@ def test_counters_match_oracle(env):
     r = pipeline.Renderer(sc, st)
     r.project(); r.bin(); r.forward(counters=True)
     torch.cuda.synchronize()
-    ev, bl = [int(x) for x in r.counters.cpu().numpy()]
+    ev, bl, box = [int(x) for x in r.counters.cpu().numpy()]
+    assert bl <= box <= ev
     ref = oracle.iteration(sc, st, backward=False)[0]["fwd"]
     # the GPU walks every pixel of a tile until the whole tile stops; blends are exact up to
     # flagged decisions
