@@ -1,17 +1,32 @@
 // A7-A10: forward, loss-gradient, backward and fused rasterizers.
 //
-// One 256-thread workgroup per (view, 16x16 tile): four wavefronts, each covering an 8x8
-// quarter of the tile (lane l of wave w -> pixel ((w & 1) * 8 + (l & 7), (w >> 1) * 8 + (l >> 3))).
-// The tile's list is staged through LDS in batches of 256 records (one gather per thread).
+// One 256-thread workgroup per (view, 16x16 tile).  Each wavefront owns an 8x8 quarter of the
+// tile and each of its four 16-lane DPP rows owns a 4x4 block of that quarter: lane l of wave w
+// shades pixel ((w & 1) * 8 + (r & 1) * 4 + (l & 3), (w >> 1) * 8 + (r >> 1) * 4 + ((l & 15) >> 2))
+// with r = l >> 4.  Splats in these scenes cover a few pixels, so giving every 4x4 block its own
+// list keeps the lanes of an instruction on pixels the splat can reach.
 //
-// The forward walks the list front to back; a workgroup stops loading batches once every
-// pixel has terminated.  The backward walks each pixel's blended entries back to front from
-// n_contrib, recovering T by division by (1 - alpha) and carrying the colour behind; it sums
-// each entry's nine gradient components over the wavefront (butterfly shuffles) and issues one
-// float atomic per component from one lane.  The fused kernel runs the forward, forms dL/dC
-// in registers (L1 against a target, or a supplied gradient) and runs the backward on the same
-// workgroup: per-pixel C, T and n_contrib never leave registers, and when the tile's list fits
-// the LDS budget its records are read from HBM once for both passes.
+// The tile's list is staged through LDS in batches of 256 entries, one gather per thread.  While
+// staging, each entry gets a conservative 16-bit mask of the 4x4 blocks its alpha_min box
+// touches, and every block gets its own compacted list of the batch entries that touch it
+// (ballot + popcount), so a row never evaluates a pair its pixels cannot blend.  The box is
+// widened beyond float32 reach and the mask is all ones for ill-conditioned conics: the culled
+// pairs are pairs with alpha < alpha_min, and forward and backward cull the same pairs (they run
+// this same code on the same records).
+//
+// Pair evaluation works in base-2 logarithm units: the staged conic is pre-scaled so that the
+// exponent p2 = -q/2 * log2(e) comes out of two FMAs, and the alpha_min test is p2 >= log2(
+// alpha_min / o), taken before the exponential, so skipped pairs never pay for exp2.
+//
+// The forward walks each block's list front to back; a workgroup stops staging once every pixel
+// has stopped.  The backward walks it back to front from n_contrib, recovering T by division by
+// (1 - alpha) and carrying the colour behind.  A row sums each entry's nine gradient components
+// over its 16 lanes with four DPP adds each and adds the sums into per-entry accumulators in LDS
+// (ds_add_f32); after each batch one thread per entry flushes its accumulators with one global
+// float atomic per component, so global atomics are one per (entry, tile, component).  The fused
+// kernel runs both passes on one workgroup: per-pixel C, T and n_contrib stay in registers, dL/dC
+// is formed in registers, and the last staged forward batch (which holds the last blended entry
+// of every pixel of the tile) is reused as the first backward batch.
 #include "common.h"
 
 namespace gsmi {
@@ -19,17 +34,28 @@ namespace {
 
 constexpr int kBlock = kTileThreads;
 constexpr int kBatch = 256;
-constexpr int kFusedEntries = 1024;  // records kept resident in LDS by the fused kernel
+constexpr int kWaves = kBlock / kWave;
+constexpr int kRowsPerWave = 4;
+constexpr int kBlocks4 = kWaves * kRowsPerWave;  // 4x4-pixel blocks per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct TileCtx {
-    int v, g, px, py, lane, w;
+    int v, g, px, py, lane, w, row, x0, y0;
+    int list_id;   // this lane's 4x4 block, as a list index: w * 4 + row
     bool inside;
     float fpx, fpy;
     int32_t start, n;
     size_t vbase;
 };
 
-__device__ __forceinline__ TileCtx tile_ctx(const RasterArgs& a, const int32_t* ranges) {
+// Bit of the 16-bit block mask for block (i, j) of the tile (i, j in 0..3, 4-pixel units).
+__device__ __forceinline__ int block_bit(int w, int r) {
+    const int i = (w & 1) * 2 + (r & 1), j = (w >> 1) * 2 + (r >> 1);
+    return j * 4 + i;
+}
+
+__device__ __forceinline__ TileCtx tile_ctx(const RasterArgs& a) {
     TileCtx c;
     c.g = blockIdx.x;
     const int tpv = a.tiles_x * a.tiles_y;
@@ -38,31 +64,122 @@ __device__ __forceinline__ TileCtx tile_ctx(const RasterArgs& a, const int32_t* 
     const int tx = t % a.tiles_x, ty = t / a.tiles_x;
     c.lane = threadIdx.x & (kWave - 1);
     c.w = threadIdx.x / kWave;
-    c.px = tx * kTile + (c.w & 1) * 8 + (c.lane & 7);
-    c.py = ty * kTile + (c.w >> 1) * 8 + (c.lane >> 3);
+    c.row = c.lane >> 4;
+    c.list_id = c.w * kRowsPerWave + c.row;
+    c.x0 = tx * kTile;
+    c.y0 = ty * kTile;
+    const int l16 = c.lane & 15;
+    c.px = c.x0 + (c.w & 1) * 8 + (c.row & 1) * 4 + (l16 & 3);
+    c.py = c.y0 + (c.w >> 1) * 8 + (c.row >> 1) * 4 + (l16 >> 2);
     c.inside = c.px < a.width && c.py < a.height;
     c.fpx = (float)c.px + 0.5f;
     c.fpy = (float)c.py + 0.5f;
-    c.start = ranges[2 * c.g];
-    c.n = ranges[2 * c.g + 1] - c.start;
+    c.start = a.ranges[2 * c.g];
+    c.n = a.ranges[2 * c.g + 1] - c.start;
     c.vbase = (size_t)c.v * a.capacity;
     return c;
 }
 
-struct Lds {
-    float2* xy;
-    float4* co;
-    float4* rgb;
-    int32_t* slot;
+// One staged batch: records in evaluation-ready form, each 4x4 block's compacted list, and the
+// per-entry gradient accumulators of the backward.
+struct Batch {
+    float2 xy[kBatch];      // projected centre
+    float4 q[kBatch];       // (a, b, c, thr): p2 = a dx^2 + b dx dy + c dy^2, blend iff p2 >= thr
+    float4 oc[kBatch];      // (o, r, g, b)
+    int32_t slot[kBatch];
+    uint16_t mask[kBatch];  // 4x4 blocks of the tile the entry's alpha_min box touches
+    uint8_t list[kBlocks4][kBatch];
+    float acc[9][kBatch];
 };
 
-__device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Lds s, int dst, int32_t j) {
+// Stage list position j of the tile into batch index k (one thread per entry).
+__device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Batch& b, int k, int32_t j) {
     const int32_t slot = a.vals[c.start + j];
     const size_t idx = c.vbase + slot;
-    s.xy[dst] = a.mean2d[idx];
-    s.co[dst] = a.conic_opacity[idx];
-    s.rgb[dst] = make_float4(a.color[3 * idx], a.color[3 * idx + 1], a.color[3 * idx + 2], 0.0f);
-    s.slot[dst] = slot;
+    const float2 xy = a.mean2d[idx];
+    const float4 co = a.conic_opacity[idx];
+    const float amin = a.p.alpha_min;
+    b.xy[k] = xy;
+    b.q[k] = make_float4(-0.5f * kLog2e * co.x, -kLog2e * co.y, -0.5f * kLog2e * co.z, __log2f(amin / co.w));
+    b.oc[k] = make_float4(co.w, a.color[3 * idx], a.color[3 * idx + 1], a.color[3 * idx + 2]);
+    b.slot[k] = slot;
+    // conservative block mask from the alpha_min box of the conic (Sigma' = conic^-1)
+    uint32_t m = 0xFFFFu;
+    const float det = co.x * co.z - co.y * co.y;
+    if (co.w <= amin) {
+        m = 0u;  // never reaches alpha_min (the projection culls these already)
+    } else if (det > 0.0f && co.x * co.z <= 1e4f * det && isfinite(det)) {
+        const float Q = 2.0f * __logf(co.w / amin);
+        const float ex = 1.01f * sqrtf(Q * co.z / det) + 0.05f;
+        const float ey = 1.01f * sqrtf(Q * co.x / det) + 0.05f;
+        if (isfinite(ex) && isfinite(ey)) {
+            const float lx = xy.x - ex, hx = xy.x + ex, ly = xy.y - ey, hy = xy.y + ey;
+            uint32_t mx = 0u, my = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float cx0 = (float)(c.x0 + 4 * i) + 0.5f, cx1 = cx0 + 3.0f;
+                const float cy0 = (float)(c.y0 + 4 * i) + 0.5f, cy1 = cy0 + 3.0f;
+                mx |= (lx <= cx1 && hx >= cx0) ? (1u << i) : 0u;
+                my |= (ly <= cy1 && hy >= cy0) ? (1u << i) : 0u;
+            }
+            m = 0u;
+#pragma unroll
+            for (int jy = 0; jy < 4; jy++)
+                if ((my >> jy) & 1u) m |= mx << (4 * jy);
+        }
+    }
+    b.mask[k] = (uint16_t)m;
+}
+
+struct Lists {
+    int len;      // this lane's block list length
+    int max_len;  // longest of the wavefront's four block lists (the loop bound)
+};
+
+// Each wavefront compacts batch entries [0, cnt) into the lists of its four 4x4 blocks, in list
+// order.  The lengths are wave-uniform (from the ballots).  Ends with a workgroup barrier so that
+// every lane reads the list entries its neighbours wrote.
+__device__ __forceinline__ Lists build_lists(const TileCtx& c, Batch& b, int cnt) {
+    int len[kRowsPerWave] = {0, 0, 0, 0};
+    const unsigned long long lt = (1ull << c.lane) - 1ull;
+    for (int base = 0; base < cnt; base += kWave) {
+        const int k = base + c.lane;
+        const uint32_t m = k < cnt ? (uint32_t)b.mask[k] : 0u;
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; r++) {
+            const bool hit = (m >> block_bit(c.w, r)) & 1u;
+            const unsigned long long bal = __ballot(hit);
+            if (hit) b.list[c.w * kRowsPerWave + r][len[r] + __popcll(bal & lt)] = (uint8_t)k;
+            len[r] += __popcll(bal);
+        }
+    }
+    __syncthreads();
+    Lists l;
+    l.len = c.row == 0 ? len[0] : c.row == 1 ? len[1] : c.row == 2 ? len[2] : len[3];
+    l.max_len = max(max(len[0], len[1]), max(len[2], len[3]));
+    return l;
+}
+
+struct Pair {
+    float dx, dy, p2, G, v, alpha, oma;
+};
+
+// The shared pair evaluation.  Returns false when alpha < alpha_min (exp2 not evaluated).
+__device__ __forceinline__ bool eval_pair(const TileCtx& c, const Batch& b, int k, float amax, Pair& e) {
+    const float2 xy = b.xy[k];
+    const float4 q = b.q[k];
+    e.dx = c.fpx - xy.x;
+    e.dy = c.fpy - xy.y;
+    const float bdx = q.y * e.dx;
+    const float cdy = q.z * e.dy;
+    e.p2 = fmaf(q.x * e.dx, e.dx, fmaf(bdx, e.dy, cdy * e.dy));
+    if (!(e.p2 >= q.w)) return false;
+    const float o = b.oc[k].x;
+    e.G = exp2f(e.p2);
+    e.v = o * e.G;
+    e.alpha = fminf(amax, e.v);
+    e.oma = e.v <= amax ? fmaf(-o, e.G, 1.0f) : 1.0f - amax;
+    return true;
 }
 
 struct Fwd {
@@ -71,7 +188,10 @@ struct Fwd {
     bool done;
 };
 
-// Front-to-back over records [k0, k1) of LDS, list positions j = jbase + k.
+struct Counts {
+    int64_t eval, blend, box;
+};
+
 // Diagnostic only: is the pixel inside the exact bounding box of {o exp(-q/2) >= alpha_min}?
 __device__ __forceinline__ bool in_alpha_box(float dx, float dy, float4 co, float amin) {
     if (!(co.w > amin)) return false;
@@ -81,37 +201,35 @@ __device__ __forceinline__ bool in_alpha_box(float dx, float dy, float4 co, floa
     return fabsf(dx) <= ex && fabsf(dy) <= ey;
 }
 
-struct Counts {
-    int64_t eval, blend, box;
-};
-
 template <bool COUNT>
-__device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, Lds s, int k0, int k1, int32_t jbase,
+__device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Lists l, int32_t jbase,
                                          Fwd& f, Counts& cnt) {
-    if (f.done) return;
-    const float amin = a.p.alpha_min, amax = a.p.alpha_max, tmin = a.p.t_min;
-    for (int k = k0; k < k1; k++) {
-        const float2 xy = s.xy[k];
-        const float4 co = s.co[k];
-        const float dx = c.fpx - xy.x, dy = c.fpy - xy.y;
-        const float G = pair_gauss(pair_power(dx, dy, co.x, co.y, co.z));
-        const float v = co.w * G;
-        const float alpha = fminf(amax, v);
+    const float amax = a.p.alpha_max, tmin = a.p.t_min;
+    const uint8_t* lst = b.list[c.list_id];
+    for (int i = 0; i < l.max_len; i++) {
+        const bool work = !f.done && i < l.len;
+        if (__ballot(work) == 0ull) break;
+        if (!work) continue;
+        const int k = lst[i];
+        Pair e;
+        const bool hit = eval_pair(c, b, k, amax, e);
         if (COUNT) {
             cnt.eval++;
-            cnt.box += in_alpha_box(dx, dy, co, amin) ? 1 : 0;
+            const float4 q = b.q[k];
+            const float4 co = make_float4(-2.0f * kLn2 * q.x, -kLn2 * q.y, -2.0f * kLn2 * q.z, b.oc[k].x);
+            cnt.box += in_alpha_box(e.dx, e.dy, co, a.p.alpha_min) ? 1 : 0;
         }
-        if (alpha < amin) continue;
-        const float Tn = f.T * one_minus_alpha(co.w, G, v, amax);
+        if (!hit) continue;
+        const float Tn = f.T * e.oma;
         if (Tn < tmin) {
             f.done = true;
-            break;
+            continue;
         }
-        const float wgt = alpha * f.T;
-        const float4 rgb = s.rgb[k];
-        f.C0 = fmaf(wgt, rgb.x, f.C0);
-        f.C1 = fmaf(wgt, rgb.y, f.C1);
-        f.C2 = fmaf(wgt, rgb.z, f.C2);
+        const float wgt = e.alpha * f.T;
+        const float4 oc = b.oc[k];
+        f.C0 = fmaf(wgt, oc.y, f.C0);
+        f.C1 = fmaf(wgt, oc.z, f.C1);
+        f.C2 = fmaf(wgt, oc.w, f.C2);
         f.T = Tn;
         f.last = jbase + k + 1;
         if (COUNT) cnt.blend++;
@@ -125,73 +243,113 @@ struct Bwd {
     int32_t nc;
 };
 
+// Sum over each 16-lane row with DPP adds; every lane of a row receives the row's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_src(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_total(float v) {
+    v += dpp_src<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_src<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_src<0x141>(v);  // row_half_mirror
+    v += dpp_src<0x140>(v);  // row_mirror
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
     for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
 }
 
-// Back-to-front over records [k0, k1) of LDS (k descending), list positions j = jbase + k.
-__device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, Lds s, int k0, int k1, int32_t jbase,
-                                         Bwd& b, Grads gr) {
-    const float amin = a.p.alpha_min, amax = a.p.alpha_max;
+// Back-to-front over this block's list of the staged batch (positions j = jbase + k).
+__device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, Batch& b, Lists l, int32_t jbase,
+                                         int row_nc, Bwd& s) {
+    const float amax = a.p.alpha_max;
     const float bg0 = a.p.bg[0], bg1 = a.p.bg[1], bg2 = a.p.bg[2];
-    for (int k = k1 - 1; k >= k0; k--) {
+    const uint8_t* lst = b.list[c.list_id];
+    for (int i = l.max_len - 1; i >= 0; i--) {
+        const int k = i < l.len ? (int)lst[i] : 0;
+        const bool active = i < l.len && jbase + k < row_nc;  // uniform over the row
+        if (__ballot(active) == 0ull) continue;
         float d[9];
 #pragma unroll
-        for (int q = 0; q < 9; q++) d[q] = 0.0f;
+        for (int t = 0; t < 9; t++) d[t] = 0.0f;
         bool contrib = false;
-        if (jbase + k < b.nc) {
-            const float2 xy = s.xy[k];
-            const float4 co = s.co[k];
-            const float dx = c.fpx - xy.x, dy = c.fpy - xy.y;
-            const float G = pair_gauss(pair_power(dx, dy, co.x, co.y, co.z));
-            const float v = co.w * G;
-            const float alpha = fminf(amax, v);
-            if (alpha >= amin) {
-                contrib = true;
-                const float oma = one_minus_alpha(co.w, G, v, amax);
-                const float Tj = b.T / oma;
-                const float4 rgb = s.rgb[k];
-                const float bgterm = b.Tfin / oma;
-                float dLda = b.g0 * (Tj * (rgb.x - b.B0) - bgterm * bg0);
-                dLda = fmaf(b.g1, Tj * (rgb.y - b.B1) - bgterm * bg1, dLda);
-                dLda = fmaf(b.g2, Tj * (rgb.z - b.B2) - bgterm * bg2, dLda);
-                const float wgt = alpha * Tj;
-                d[6] = wgt * b.g0;
-                d[7] = wgt * b.g1;
-                d[8] = wgt * b.g2;
-                b.B0 = fmaf(alpha, rgb.x, oma * b.B0);
-                b.B1 = fmaf(alpha, rgb.y, oma * b.B1);
-                b.B2 = fmaf(alpha, rgb.z, oma * b.B2);
-                if (v <= amax) {
-                    const float gh = co.w * G * dLda;
-                    d[0] = gh * fmaf(co.x, dx, co.y * dy);
-                    d[1] = gh * fmaf(co.y, dx, co.z * dy);
-                    d[2] = -0.5f * gh * dx * dx;
-                    d[3] = -gh * dx * dy;
-                    d[4] = -0.5f * gh * dy * dy;
-                    d[5] = G * dLda;
-                }
-                b.T = Tj;
+        Pair e;
+        if (active && jbase + k < s.nc && eval_pair(c, b, k, amax, e)) {
+            contrib = true;
+            const float4 oc = b.oc[k];
+            const float Tj = s.T / e.oma;
+            const float bgterm = s.Tfin / e.oma;
+            float dLda = s.g0 * (Tj * (oc.y - s.B0) - bgterm * bg0);
+            dLda = fmaf(s.g1, Tj * (oc.z - s.B1) - bgterm * bg1, dLda);
+            dLda = fmaf(s.g2, Tj * (oc.w - s.B2) - bgterm * bg2, dLda);
+            const float wgt = e.alpha * Tj;
+            d[6] = wgt * s.g0;
+            d[7] = wgt * s.g1;
+            d[8] = wgt * s.g2;
+            s.B0 = fmaf(e.alpha, oc.y, e.oma * s.B0);
+            s.B1 = fmaf(e.alpha, oc.z, e.oma * s.B1);
+            s.B2 = fmaf(e.alpha, oc.w, e.oma * s.B2);
+            if (e.v <= amax) {
+                // dalpha/dG = o; dG/dq = -G/2; conic (A, B, C) = (-2 a, -b, -2 c) ln 2
+                const float gh = e.v * dLda;
+                const float4 q = b.q[k];
+                const float ghl = -kLn2 * gh;
+                d[0] = ghl * fmaf(2.0f * q.x, e.dx, q.y * e.dy);  // gh (A dx + B dy)
+                d[1] = ghl * fmaf(q.y, e.dx, 2.0f * q.z * e.dy);  // gh (B dx + C dy)
+                d[2] = -0.5f * gh * e.dx * e.dx;
+                d[3] = -gh * e.dx * e.dy;
+                d[4] = -0.5f * gh * e.dy * e.dy;
+                d[5] = e.G * dLda;
             }
+            s.T = Tj;
         }
-        if (__ballot(contrib) != 0ull) {
+        const unsigned long long cm = __ballot(contrib);
+        if (cm != 0ull) {
 #pragma unroll
-            for (int q = 0; q < 9; q++) d[q] = wave_sum(d[q]);
-            if (c.lane == 0) {
-                const size_t idx = c.vbase + s.slot[k];
-                if (d[0] != 0.0f) atomicAdd(&gr.d_mean2d[idx].x, d[0]);
-                if (d[1] != 0.0f) atomicAdd(&gr.d_mean2d[idx].y, d[1]);
-                if (d[2] != 0.0f) atomicAdd(&gr.d_conic[3 * idx + 0], d[2]);
-                if (d[3] != 0.0f) atomicAdd(&gr.d_conic[3 * idx + 1], d[3]);
-                if (d[4] != 0.0f) atomicAdd(&gr.d_conic[3 * idx + 2], d[4]);
-                if (d[5] != 0.0f) atomicAdd(&gr.d_opacity[idx], d[5]);
-                if (d[6] != 0.0f) atomicAdd(&gr.d_color[3 * idx + 0], d[6]);
-                if (d[7] != 0.0f) atomicAdd(&gr.d_color[3 * idx + 1], d[7]);
-                if (d[8] != 0.0f) atomicAdd(&gr.d_color[3 * idx + 2], d[8]);
+            for (int t = 0; t < 9; t++) d[t] = row_total(d[t]);
+            if ((c.lane & 15) == 15 && ((cm >> (16 * c.row)) & 0xFFFFull) != 0ull) {
+#pragma unroll
+                for (int t = 0; t < 9; t++) atomicAdd(&b.acc[t][k], d[t]);
             }
         }
     }
+}
+
+// After a backward batch: one thread per entry adds its accumulated gradient to the outputs
+// (one float atomic per nonzero component) and clears the accumulators.
+__device__ __forceinline__ void flush_batch(const TileCtx& c, Batch& b, int cnt, Grads gr) {
+    __syncthreads();
+    const int k = threadIdx.x;
+    if (k < cnt) {
+        float d[9];
+        bool any = false;
+#pragma unroll
+        for (int t = 0; t < 9; t++) {
+            d[t] = b.acc[t][k];
+            any |= d[t] != 0.0f;
+            b.acc[t][k] = 0.0f;
+        }
+        if (any) {
+            const size_t idx = c.vbase + b.slot[k];
+            atomicAdd(&gr.d_mean2d[idx].x, d[0]);
+            atomicAdd(&gr.d_mean2d[idx].y, d[1]);
+            atomicAdd(&gr.d_conic[3 * idx + 0], d[2]);
+            atomicAdd(&gr.d_conic[3 * idx + 1], d[3]);
+            atomicAdd(&gr.d_conic[3 * idx + 2], d[4]);
+            atomicAdd(&gr.d_opacity[idx], d[5]);
+            atomicAdd(&gr.d_color[3 * idx + 0], d[6]);
+            atomicAdd(&gr.d_color[3 * idx + 1], d[7]);
+            atomicAdd(&gr.d_color[3 * idx + 2], d[8]);
+        }
+    }
+}
+
+__device__ __forceinline__ int row_max(int x) {
+    for (int o = 8; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+    return x;
 }
 
 __device__ __forceinline__ int block_max(int x, int* s_red) {
@@ -199,13 +357,12 @@ __device__ __forceinline__ int block_max(int x, int* s_red) {
     if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x / kWave] = x;
     __syncthreads();
     int m = s_red[0];
-    for (int k = 1; k < kBlock / kWave; k++) m = max(m, s_red[k]);
+    for (int k = 1; k < kWaves; k++) m = max(m, s_red[k]);
     __syncthreads();
     return m;
 }
 
 __device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
-    // wave sums then one atomic per wave
     for (int o = kWave / 2; o > 0; o >>= 1) {
         c.eval += __shfl_xor(c.eval, o);
         c.blend += __shfl_xor(c.blend, o);
@@ -218,26 +375,68 @@ __device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
     }
 }
 
+__device__ __forceinline__ void zero_acc(Batch& b) {
+#pragma unroll
+    for (int t = 0; t < 9; t++) b.acc[t][threadIdx.x] = 0.0f;
+}
+
+// Forward over the whole tile list.  On return *last_b0 is the list position of the last staged
+// batch (-1 if none), *last_cnt its entry count and *last_lists this lane's lists in it.
+template <bool COUNT>
+__device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Fwd& f, Counts& cnt,
+                                             int32_t* last_b0, int* last_cnt, Lists* last_lists) {
+    *last_b0 = -1;
+    *last_cnt = 0;
+    last_lists->len = last_lists->max_len = 0;
+    for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
+        if (__syncthreads_count(f.done) == kBlock) break;
+        const int cnt_b = min(kBatch, c.n - b0);
+        if ((int)threadIdx.x < cnt_b) stage(a, c, b, threadIdx.x, b0 + threadIdx.x);
+        __syncthreads();
+        const Lists l = build_lists(c, b, cnt_b);
+        fwd_walk<COUNT>(a, c, b, l, b0, f, cnt);
+        *last_b0 = b0;
+        *last_cnt = cnt_b;
+        *last_lists = l;
+    }
+}
+
+// Backward over list positions [0, maxnc); the batch starting at `resident_b0` (with
+// `resident_cnt` entries and this lane's lists `resident`) is already staged.  The gradient
+// accumulators must be zero on entry.
+__device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, int32_t maxnc,
+                                              int32_t resident_b0, int resident_cnt, Lists resident, Bwd& s,
+                                              Grads gr) {
+    const int row_nc = row_max(s.nc);
+    if (maxnc <= 0) return;
+    for (int32_t b0 = ((maxnc - 1) / kBatch) * kBatch; b0 >= 0; b0 -= kBatch) {
+        Lists l = resident;
+        int cnt_b = resident_cnt;
+        if (b0 != resident_b0) {
+            cnt_b = min(kBatch, maxnc - b0);
+            __syncthreads();
+            if ((int)threadIdx.x < cnt_b) stage(a, c, b, threadIdx.x, b0 + threadIdx.x);
+            __syncthreads();
+            l = build_lists(c, b, cnt_b);
+        }
+        bwd_walk(a, c, b, l, b0, row_nc, s);
+        flush_batch(c, b, cnt_b, gr);
+        resident_b0 = -1;
+    }
+}
+
 template <bool COUNT>
 __global__ __launch_bounds__(kBlock) void raster_fwd_kernel(RasterArgs a, float* image, float* t_final,
                                                             int32_t* n_contrib) {
-    __shared__ float2 s_xy[kBatch];
-    __shared__ float4 s_co[kBatch];
-    __shared__ float4 s_rgb[kBatch];
-    __shared__ int32_t s_slot[kBatch];
-    const Lds s{s_xy, s_co, s_rgb, s_slot};
-    const TileCtx c = tile_ctx(a, a.ranges);
+    __shared__ Batch b;
+    const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
-    Counts cnts{0, 0, 0};
-    for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
-        if (__syncthreads_count(f.done) == kBlock) break;
-        const int32_t j = b0 + threadIdx.x;
-        if (j < c.n) stage(a, c, s, threadIdx.x, j);
-        __syncthreads();
-        const int cnt = min(kBatch, c.n - b0);
-        fwd_walk<COUNT>(a, c, s, 0, cnt, b0, f, cnts);
-    }
-    if (COUNT) add_counters(a.counters, cnts);
+    Counts cnt{0, 0, 0};
+    int32_t last_b0;
+    int last_cnt;
+    Lists last_lists;
+    forward_tile<COUNT>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
+    if (COUNT) add_counters(a.counters, cnt);
     if (!c.inside) return;
     const size_t plane = (size_t)a.width * a.height;
     const size_t p = (size_t)c.py * a.width + c.px;
@@ -283,74 +482,53 @@ __global__ __launch_bounds__(256) void zero_grads_kernel(const int32_t* vis_coun
 
 __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const float* t_final, const int32_t* n_contrib,
                                                             const float* dl, Grads gr) {
-    __shared__ float2 s_xy[kBatch];
-    __shared__ float4 s_co[kBatch];
-    __shared__ float4 s_rgb[kBatch];
-    __shared__ int32_t s_slot[kBatch];
-    __shared__ int s_red[kBlock / kWave];
-    const Lds s{s_xy, s_co, s_rgb, s_slot};
-    const TileCtx c = tile_ctx(a, a.ranges);
+    __shared__ Batch b;
+    __shared__ int s_red[kWaves];
+    const TileCtx c = tile_ctx(a);
     const size_t plane = (size_t)a.width * a.height;
     const size_t p = (size_t)c.py * a.width + c.px;
-    Bwd b{};
+    Bwd s{};
     if (c.inside) {
-        b.T = t_final[(size_t)c.v * plane + p];
-        b.nc = n_contrib[(size_t)c.v * plane + p];
-        b.g0 = dl[(size_t)(3 * c.v + 0) * plane + p];
-        b.g1 = dl[(size_t)(3 * c.v + 1) * plane + p];
-        b.g2 = dl[(size_t)(3 * c.v + 2) * plane + p];
+        s.T = t_final[(size_t)c.v * plane + p];
+        s.nc = n_contrib[(size_t)c.v * plane + p];
+        s.g0 = dl[(size_t)(3 * c.v + 0) * plane + p];
+        s.g1 = dl[(size_t)(3 * c.v + 1) * plane + p];
+        s.g2 = dl[(size_t)(3 * c.v + 2) * plane + p];
     } else {
-        b.T = 1.0f;
-        b.nc = 0;
-        b.g0 = b.g1 = b.g2 = 0.0f;
+        s.T = 1.0f;
+        s.nc = 0;
+        s.g0 = s.g1 = s.g2 = 0.0f;
     }
-    b.Tfin = b.T;
-    b.B0 = b.B1 = b.B2 = 0.0f;
-    const int maxnc = block_max(b.nc, s_red);
-    for (int32_t bend = maxnc; bend > 0; bend -= kBatch) {
-        const int32_t b0 = bend > kBatch ? bend - kBatch : 0;
-        __syncthreads();
-        if (b0 + (int32_t)threadIdx.x < bend) stage(a, c, s, threadIdx.x, b0 + threadIdx.x);
-        __syncthreads();
-        bwd_walk(a, c, s, 0, bend - b0, b0, b, gr);
-    }
+    s.Tfin = s.T;
+    s.B0 = s.B1 = s.B2 = 0.0f;
+    zero_acc(b);
+    const int maxnc = block_max(s.nc, s_red);
+    backward_tile(a, c, b, maxnc, -1, 0, Lists{0, 0}, s, gr);
 }
 
 template <bool COUNT>
 __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int mode, const float* tgt, float scale,
                                                               float* image, float* loss_sum, Grads gr) {
-    __shared__ float2 s_xy[kFusedEntries];
-    __shared__ float4 s_co[kFusedEntries];
-    __shared__ float4 s_rgb[kFusedEntries];
-    __shared__ int32_t s_slot[kFusedEntries];
-    __shared__ int s_red[kBlock / kWave];
-    const Lds s{s_xy, s_co, s_rgb, s_slot};
-    const TileCtx c = tile_ctx(a, a.ranges);
-    const bool resident = c.n <= kFusedEntries;
-    // forward
+    __shared__ Batch b;
+    __shared__ int s_red[kWaves];
+    const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
-    Counts cnts{0, 0, 0};
-    int32_t loaded = 0;  // resident entries staged so far
-    for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
-        if (__syncthreads_count(f.done) == kBlock) break;
-        const int32_t j = b0 + threadIdx.x;
-        const int base = resident ? b0 : 0;
-        if (j < c.n) stage(a, c, s, base + threadIdx.x, j);
-        __syncthreads();
-        const int cnt = min(kBatch, c.n - b0);
-        fwd_walk<COUNT>(a, c, s, base, base + cnt, b0 - base, f, cnts);
-        loaded = b0 + cnt;
-    }
-    if (COUNT) add_counters(a.counters, cnts);
+    Counts cnt{0, 0, 0};
+    int32_t last_b0;
+    int last_cnt;
+    Lists last_lists;
+    zero_acc(b);
+    forward_tile<COUNT>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
+    if (COUNT) add_counters(a.counters, cnt);
     // loss gradient in registers
     const size_t plane = (size_t)a.width * a.height;
     const size_t p = (size_t)c.py * a.width + c.px;
-    Bwd b{};
-    b.T = f.T;
-    b.Tfin = f.T;
-    b.nc = c.inside ? f.last : 0;
-    b.B0 = b.B1 = b.B2 = 0.0f;
-    b.g0 = b.g1 = b.g2 = 0.0f;
+    Bwd s{};
+    s.T = f.T;
+    s.Tfin = f.T;
+    s.nc = c.inside ? f.last : 0;
+    s.B0 = s.B1 = s.B2 = 0.0f;
+    s.g0 = s.g1 = s.g2 = 0.0f;
     float lsum = 0.0f;
     if (c.inside) {
         const float C0 = fmaf(f.T, a.p.bg[0], f.C0);
@@ -366,40 +544,28 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
         const float t2 = tgt[(size_t)(3 * c.v + 2) * plane + p];
         if (mode == GS_LOSS_L1) {
             const float d0 = C0 - t0, d1 = C1 - t1, d2 = C2 - t2;
-            b.g0 = d0 > 0.0f ? scale : (d0 < 0.0f ? -scale : 0.0f);
-            b.g1 = d1 > 0.0f ? scale : (d1 < 0.0f ? -scale : 0.0f);
-            b.g2 = d2 > 0.0f ? scale : (d2 < 0.0f ? -scale : 0.0f);
+            s.g0 = d0 > 0.0f ? scale : (d0 < 0.0f ? -scale : 0.0f);
+            s.g1 = d1 > 0.0f ? scale : (d1 < 0.0f ? -scale : 0.0f);
+            s.g2 = d2 > 0.0f ? scale : (d2 < 0.0f ? -scale : 0.0f);
             lsum = scale * (fabsf(d0) + fabsf(d1) + fabsf(d2));
         } else {
-            b.g0 = t0;
-            b.g1 = t1;
-            b.g2 = t2;
+            s.g0 = t0;
+            s.g1 = t1;
+            s.g2 = t2;
         }
     }
     if (loss_sum && mode == GS_LOSS_L1) {
         lsum = wave_sum(lsum);
         if (c.lane == 0 && lsum != 0.0f) atomicAdd(loss_sum, lsum);
     }
-    // backward
-    const int maxnc = block_max(b.nc, s_red);
-    if (resident) {
-        // every entry below maxnc was staged by the forward (maxnc <= loaded)
-        (void)loaded;
-        bwd_walk(a, c, s, 0, maxnc, 0, b, gr);
-    } else {
-        for (int32_t bend = maxnc; bend > 0; bend -= kBatch) {
-            const int32_t b0 = bend > kBatch ? bend - kBatch : 0;
-            __syncthreads();
-            if (b0 + (int32_t)threadIdx.x < bend) stage(a, c, s, threadIdx.x, b0 + threadIdx.x);
-            __syncthreads();
-            bwd_walk(a, c, s, 0, bend - b0, b0, b, gr);
-        }
-    }
+    const int maxnc = block_max(s.nc, s_red);
+    // every pixel's last blended entry lies in the last staged batch, so it is still resident
+    backward_tile(a, c, b, maxnc, last_b0, last_cnt, last_lists, s, gr);
 }
 
 }  // namespace
 
-int32_t fused_lds_entries() { return kFusedEntries; }
+int32_t fused_lds_entries() { return kBatch; }
 
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s) {
     const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);

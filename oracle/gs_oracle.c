@@ -323,9 +323,11 @@ static int composite_pixel(double px, double py, const int32_t* list, int n, con
         const double v = o * G;
         const double alpha = v < p->alpha_max ? v : p->alpha_max;
         if (n_eval) (*n_eval)++;
-        /* float32 error model: q carries ~8 ulp of its absolute-term sum, exp adds a few ulp */
+        /* float32 error model: q carries ~8 ulp of its absolute-term sum; the exponential, and
+         * a logarithm of alpha_min / o where the alpha_min test is taken in log space, add up
+         * to a few ulp of the exponent (16 ulp of alpha budgeted) */
         const double qabs = fabs(A) * dx * dx + 2.0 * fabs(B * dx * dy) + fabs(Cc) * dy * dy;
-        const double rel_a = 0.5 * 8.0 * EPS32 * qabs + 4.0 * EPS32;
+        const double rel_a = 0.5 * 8.0 * EPS32 * qabs + 16.0 * EPS32;
         if (fabs(v - p->alpha_min) <= 4.0 * rel_a * p->alpha_min + 1e-12) *flag = 1;
         if (fabs(v - p->alpha_max) <= 4.0 * rel_a * p->alpha_max + 1e-12) *flag_clamp = 1;
         if (touch) touch[j] = (int8_t)(v >= p->alpha_min * (1.0 - 4.0 * rel_a) - 1e-12);

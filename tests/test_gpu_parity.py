@@ -141,10 +141,10 @@ def test_counters_match_oracle(env):
     ev, bl, box = [int(x) for x in r.counters.cpu().numpy()]
     assert bl <= box <= ev
     ref = oracle.iteration(sc, st, backward=False)[0]["fwd"]
-    # the GPU walks every pixel of a tile until the whole tile stops; blends are exact up to
-    # flagged decisions
+    # blends are exact up to flagged decisions; the GPU culls pairs outside each wavefront's
+    # quarter tile, so it evaluates fewer pairs than the oracle's plain per-pixel walk
     assert abs(bl - ref["n_blended"]) <= 50, (bl, ref["n_blended"])
-    assert ev >= ref["n_evaluated"] * 0.99
+    assert ev <= ref["n_evaluated"]
 
 
 def test_empty_and_fully_culled_scenes(env):
