@@ -124,12 +124,15 @@ struct BinWs {
     uint32_t *tkey_alt, *tval_alt;
     int32_t *hist, *partials;
     int32_t *kept, *cap_offsets;
+    uint32_t *order_keys, *order_vals, *order_keys_alt;  // [tiles_total] tile-order sort
 };
 
 BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t inst_cap, size_t* bytes) {
     Carver c(ws);
     const int64_t nv = (int64_t)n * V;
-    const int32_t sort_n = (int32_t)(nv > inst_cap ? nv : inst_cap);
+    int64_t sort_n64 = nv > inst_cap ? nv : inst_cap;
+    if (tiles_total > sort_n64) sort_n64 = tiles_total;
+    const int32_t sort_n = (int32_t)sort_n64;
     BinWs w;
     w.dkey = c.take<uint32_t>(nv);
     w.dval = c.take<uint32_t>(nv);
@@ -148,6 +151,9 @@ BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t ins
     w.partials = c.take<int32_t>(part / sizeof(int32_t));
     w.kept = c.take<int32_t>(tiles_total);
     w.cap_offsets = c.take<int32_t>(tiles_total);
+    w.order_keys = c.take<uint32_t>(tiles_total);
+    w.order_vals = c.take<uint32_t>(tiles_total);
+    w.order_keys_alt = c.take<uint32_t>(tiles_total);
     *bytes = c.used;
     return w;
 }
@@ -181,6 +187,7 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     ra->conic_opacity = reinterpret_cast<const float4*>(proj->conic_opacity);
     ra->color = proj->color;
     ra->vis_count = proj->vis_count;
+    ra->tile_order = bins->tile_order;
     ra->counters = nullptr;
     return GS_OK;
 }
@@ -356,6 +363,9 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
         if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);
     }
+    if (e == hipSuccess && bins->tile_order)
+        e = launch_tile_order(bins->ranges, tiles_total, w.order_keys, w.order_vals, w.order_keys_alt, bins->tile_order,
+                              w.hist, w.partials, s);
     if (e == hipSuccess && p->tile_cap > 0) {
         e = launch_cap_count(bins->ranges, tiles_total, p->tile_cap, w.kept, s);
         if (e == hipSuccess) e = launch_scan_rows(w.kept, w.cap_offsets, bins->num_capped, tiles_total, 1, w.partials, s);

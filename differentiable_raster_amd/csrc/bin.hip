@@ -75,6 +75,16 @@ __global__ __launch_bounds__(kBlock) void ranges_kernel(const uint32_t* keys, in
     if (j == M - 1 || keys[j + 1] != k) ranges[2 * (size_t)k + 1] = j + 1;
 }
 
+// Heavy-first schedule: key = clz(n + 1) = 31 - floor(log2(n + 1)) in [0, 31] for a tile with n
+// entries; a stable sort on this 5-bit key (ties in tile order) puts the longest lists first.
+__global__ __launch_bounds__(kBlock) void tile_order_keys_kernel(const int32_t* ranges, int32_t n_tiles_total,
+                                                                 uint32_t* keys, uint32_t* vals) {
+    const int32_t t = blockIdx.x * kBlock + threadIdx.x;
+    if (t >= n_tiles_total) return;
+    keys[t] = (uint32_t)__clz(ranges[2 * t + 1] - ranges[2 * t] + 1);
+    vals[t] = (uint32_t)t;
+}
+
 __global__ __launch_bounds__(kBlock) void cap_count_kernel(const int32_t* ranges, int32_t n_tiles_total, int32_t K,
                                                            int32_t* kept) {
     const int32_t t = blockIdx.x * kBlock + threadIdx.x;
@@ -223,6 +233,16 @@ hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, 
     if (M <= 0) return hipSuccess;
     hipLaunchKernelGGL(ranges_kernel, dim3(blocks_for(M)), dim3(kBlock), 0, s, tile_keys, M, ranges);
     return hipGetLastError();
+}
+
+hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, uint32_t* keys, uint32_t* vals,
+                             uint32_t* keys_alt, int32_t* order, int32_t* hist, int32_t* partials, hipStream_t s) {
+    if (n_tiles_total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(tile_order_keys_kernel, dim3(blocks_for(n_tiles_total)), dim3(kBlock), 0, s, ranges,
+                       n_tiles_total, keys, vals);
+    // one 5-bit pass: the result lands in the alternate buffers (keys_alt, order)
+    return launch_radix_sort(keys, vals, keys_alt, reinterpret_cast<uint32_t*>(order), n_tiles_total, 5, hist,
+                             partials, s);
 }
 
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s) {

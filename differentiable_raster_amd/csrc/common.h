@@ -109,6 +109,9 @@ hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ush
                        int32_t* vals, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
 hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s);
+// Heavy-first permutation of the tiles (stable radix pass on a 5-bit length bucket).
+hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, uint32_t* keys, uint32_t* vals,
+                             uint32_t* keys_alt, int32_t* order, int32_t* hist, int32_t* partials, hipStream_t s);
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s);
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
                              int32_t capacity, int32_t tiles_per_view, int32_t n_tiles_total, int32_t K,
@@ -125,7 +128,8 @@ struct RasterArgs {
     const float4* conic_opacity;
     const float* color;
     const int32_t* vis_count;
-    int64_t* counters;       // optional
+    const int32_t* tile_order;  // optional: workgroup -> global tile (heavy tiles first)
+    int64_t* counters;          // optional
 };
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s);
 hipError_t launch_loss_l1(int64_t n, const float* image, const float* target, float scale, float* dl, float* loss_sum,

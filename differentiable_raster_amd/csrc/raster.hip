@@ -57,7 +57,7 @@ __device__ __forceinline__ int block_bit(int w, int r) {
 
 __device__ __forceinline__ TileCtx tile_ctx(const RasterArgs& a) {
     TileCtx c;
-    c.g = blockIdx.x;
+    c.g = a.tile_order ? a.tile_order[blockIdx.x] : (int)blockIdx.x;
     const int tpv = a.tiles_x * a.tiles_y;
     c.v = c.g / tpv;
     const int t = c.g - c.v * tpv;
@@ -89,7 +89,11 @@ struct Batch {
     int32_t slot[kBatch];
     uint16_t mask[kBatch];  // 4x4 blocks of the tile the entry's alpha_min box touches
     uint8_t list[kBlocks4][kBatch];
-    float acc[9][kBatch];
+};
+
+// Per-entry gradient accumulators of the backward (LDS).
+struct Acc {
+    float v[9][kBatch];
 };
 
 // Stage list position j of the tile into batch index k (one thread per entry).
@@ -175,7 +179,7 @@ __device__ __forceinline__ bool eval_pair(const TileCtx& c, const Batch& b, int 
     e.p2 = fmaf(q.x * e.dx, e.dx, fmaf(bdx, e.dy, cdy * e.dy));
     if (!(e.p2 >= q.w)) return false;
     const float o = b.oc[k].x;
-    e.G = exp2f(e.p2);
+    e.G = __builtin_amdgcn_exp2f(e.p2);  // p2 >= log2(alpha_min) > -126: no denormal range
     e.v = o * e.G;
     e.alpha = fminf(amax, e.v);
     e.oma = e.v <= amax ? fmaf(-o, e.G, 1.0f) : 1.0f - amax;
@@ -263,8 +267,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Back-to-front over this block's list of the staged batch (positions j = jbase + k).
-__device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, Batch& b, Lists l, int32_t jbase,
-                                         int row_nc, Bwd& s) {
+__device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Acc& acc, Lists l,
+                                         int32_t jbase, int row_nc, Bwd& s) {
     const float amax = a.p.alpha_max;
     const float bg0 = a.p.bg[0], bg1 = a.p.bg[1], bg2 = a.p.bg[2];
     const uint8_t* lst = b.list[c.list_id];
@@ -280,8 +284,9 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         if (active && jbase + k < s.nc && eval_pair(c, b, k, amax, e)) {
             contrib = true;
             const float4 oc = b.oc[k];
-            const float Tj = s.T / e.oma;
-            const float bgterm = s.Tfin / e.oma;
+            const float inv = __builtin_amdgcn_rcpf(e.oma);  // 1 - alpha >= 1 - alpha_max > 0
+            const float Tj = s.T * inv;
+            const float bgterm = s.Tfin * inv;
             float dLda = s.g0 * (Tj * (oc.y - s.B0) - bgterm * bg0);
             dLda = fmaf(s.g1, Tj * (oc.z - s.B1) - bgterm * bg1, dLda);
             dLda = fmaf(s.g2, Tj * (oc.w - s.B2) - bgterm * bg2, dLda);
@@ -312,7 +317,7 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
             for (int t = 0; t < 9; t++) d[t] = row_total(d[t]);
             if ((c.lane & 15) == 15 && ((cm >> (16 * c.row)) & 0xFFFFull) != 0ull) {
 #pragma unroll
-                for (int t = 0; t < 9; t++) atomicAdd(&b.acc[t][k], d[t]);
+                for (int t = 0; t < 9; t++) atomicAdd(&acc.v[t][k], d[t]);
             }
         }
     }
@@ -320,7 +325,7 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
 
 // After a backward batch: one thread per entry adds its accumulated gradient to the outputs
 // (one float atomic per nonzero component) and clears the accumulators.
-__device__ __forceinline__ void flush_batch(const TileCtx& c, Batch& b, int cnt, Grads gr) {
+__device__ __forceinline__ void flush_batch(const TileCtx& c, const Batch& b, Acc& acc, int cnt, Grads gr) {
     __syncthreads();
     const int k = threadIdx.x;
     if (k < cnt) {
@@ -328,9 +333,9 @@ __device__ __forceinline__ void flush_batch(const TileCtx& c, Batch& b, int cnt,
         bool any = false;
 #pragma unroll
         for (int t = 0; t < 9; t++) {
-            d[t] = b.acc[t][k];
+            d[t] = acc.v[t][k];
             any |= d[t] != 0.0f;
-            b.acc[t][k] = 0.0f;
+            acc.v[t][k] = 0.0f;
         }
         if (any) {
             const size_t idx = c.vbase + b.slot[k];
@@ -375,9 +380,9 @@ __device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
     }
 }
 
-__device__ __forceinline__ void zero_acc(Batch& b) {
+__device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
-    for (int t = 0; t < 9; t++) b.acc[t][threadIdx.x] = 0.0f;
+    for (int t = 0; t < 9; t++) acc.v[t][threadIdx.x] = 0.0f;
 }
 
 // Forward over the whole tile list.  On return *last_b0 is the list position of the last staged
@@ -404,7 +409,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
 // Backward over list positions [0, maxnc); the batch starting at `resident_b0` (with
 // `resident_cnt` entries and this lane's lists `resident`) is already staged.  The gradient
 // accumulators must be zero on entry.
-__device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, int32_t maxnc,
+__device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Acc& acc, int32_t maxnc,
                                               int32_t resident_b0, int resident_cnt, Lists resident, Bwd& s,
                                               Grads gr) {
     const int row_nc = row_max(s.nc);
@@ -419,8 +424,8 @@ __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx
             __syncthreads();
             l = build_lists(c, b, cnt_b);
         }
-        bwd_walk(a, c, b, l, b0, row_nc, s);
-        flush_batch(c, b, cnt_b, gr);
+        bwd_walk(a, c, b, acc, l, b0, row_nc, s);
+        flush_batch(c, b, acc, cnt_b, gr);
         resident_b0 = -1;
     }
 }
@@ -483,6 +488,7 @@ __global__ __launch_bounds__(256) void zero_grads_kernel(const int32_t* vis_coun
 __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const float* t_final, const int32_t* n_contrib,
                                                             const float* dl, Grads gr) {
     __shared__ Batch b;
+    __shared__ Acc acc;
     __shared__ int s_red[kWaves];
     const TileCtx c = tile_ctx(a);
     const size_t plane = (size_t)a.width * a.height;
@@ -501,15 +507,16 @@ __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const 
     }
     s.Tfin = s.T;
     s.B0 = s.B1 = s.B2 = 0.0f;
-    zero_acc(b);
+    zero_acc(acc);
     const int maxnc = block_max(s.nc, s_red);
-    backward_tile(a, c, b, maxnc, -1, 0, Lists{0, 0}, s, gr);
+    backward_tile(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s, gr);
 }
 
 template <bool COUNT>
 __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int mode, const float* tgt, float scale,
                                                               float* image, float* loss_sum, Grads gr) {
     __shared__ Batch b;
+    __shared__ Acc acc;
     __shared__ int s_red[kWaves];
     const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
@@ -517,7 +524,7 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
     int32_t last_b0;
     int last_cnt;
     Lists last_lists;
-    zero_acc(b);
+    zero_acc(acc);
     forward_tile<COUNT>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
     if (COUNT) add_counters(a.counters, cnt);
     // loss gradient in registers
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
     }
     const int maxnc = block_max(s.nc, s_red);
     // every pixel's last blended entry lies in the last staged batch, so it is still resident
-    backward_tile(a, c, b, maxnc, last_b0, last_cnt, last_lists, s, gr);
+    backward_tile(a, c, b, acc, maxnc, last_b0, last_cnt, last_lists, s, gr);
 }
 
 }  // namespace

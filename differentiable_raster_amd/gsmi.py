@@ -56,7 +56,7 @@ class gs_projected(ctypes.Structure):
 class gs_bins(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int64), ("tile_keys", ctypes.c_void_p), ("vals", ctypes.c_void_p),
                 ("ranges", ctypes.c_void_p), ("vals_capped", ctypes.c_void_p), ("ranges_capped", ctypes.c_void_p),
-                ("num_capped", ctypes.c_void_p)]
+                ("num_capped", ctypes.c_void_p), ("tile_order", ctypes.c_void_p)]
 
 
 class gs_bin_info(ctypes.Structure):

@@ -59,6 +59,7 @@ class Renderer:
         self.ranges = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
         self.ranges_capped = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
         self.num_capped = torch.zeros(1, dtype=i32, device=dev)
+        self.tile_order = torch.zeros(V * self.tpv, dtype=i32, device=dev)
         self.inst_capacity = -1
         self._alloc_bins(instance_capacity if instance_capacity is not None else 0)
         plane = self.H * self.W
@@ -87,7 +88,8 @@ class Renderer:
         self.vals = torch.empty(c, dtype=torch.int32, device=dev)
         self.vals_capped = torch.empty(c, dtype=torch.int32, device=dev)
         self.bins = gsmi.gs_bins(c, self.tile_keys.data_ptr(), self.vals.data_ptr(), self.ranges.data_ptr(),
-                                 self.vals_capped.data_ptr(), self.ranges_capped.data_ptr(), self.num_capped.data_ptr())
+                                 self.vals_capped.data_ptr(), self.ranges_capped.data_ptr(), self.num_capped.data_ptr(),
+                                 self.tile_order.data_ptr())
         self.ws_bin = torch.empty(gsmi.gs_bin_workspace_size(self.capacity, self.V, self.W, self.H, c),
                                   dtype=torch.uint8, device=dev)
         self.inst_capacity = c

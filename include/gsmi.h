@@ -110,6 +110,10 @@ typedef struct {
     int32_t* vals_capped;       /* [capacity]  only written when tile_cap > 0 */
     int32_t* ranges_capped;     /* [V * tiles_per_view][2]  only written when tile_cap > 0 */
     int32_t* num_capped;        /* [1] instances kept by the cap, all views (tile_cap > 0) */
+    int32_t* tile_order;        /* [V * tiles_per_view] optional (may be NULL): a permutation of
+                                   the global tiles, longest lists first, written by gs_bin_tiles
+                                   and used by the raster calls to schedule heavy tiles early;
+                                   the order changes no result */
 } gs_bins;
 
 /* Host-side counts that gs_bin_tiles reports. */

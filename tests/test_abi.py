@@ -121,7 +121,7 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     c = cams(gs)
     p = params(gs)
     proj = projected(gs)
-    bins = gs.gs_bins(1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    bins = gs.gs_bins(1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     info = gs.gs_bin_info()
     req = ctypes.c_int64()
     ws = gs.gs_bin_workspace_size(100, 1, 64, 48, 1000)
@@ -132,7 +132,7 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(p), ctypes.byref(bins), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws - 1, None) == 2
     capped = params(gs, tile_cap=64)
-    nocap = gs.gs_bins(1000, FAKE, FAKE, FAKE, None, None, None)
+    nocap = gs.gs_bins(1000, FAKE, FAKE, FAKE, None, None, None, None)
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(capped), ctypes.byref(nocap), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws, None) == 1
     neg = params(gs, tile_cap=-1)

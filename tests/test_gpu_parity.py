@@ -218,3 +218,17 @@ def test_scene_100k_720p_external_gradient(env):
     sc = scenes.make_scene(2)
     run_view_checks(env, sc, sc.settings(), mode="fused")
     run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
+
+
+def test_tile_order_is_a_heavy_first_permutation(env):
+    oracle, pipeline, torch = env
+    sc = scenes.random_scene(5000, 200, 120, seed=55, views=2, log_scale_mean=-3.0)
+    r = pipeline.Renderer(sc, sc.settings())
+    r.project(); r.bin()
+    torch.cuda.synchronize()
+    order = r.tile_order.cpu().numpy()
+    assert np.array_equal(np.sort(order), np.arange(order.size))
+    rng = r.ranges.view(-1, 2).cpu().numpy()
+    n = (rng[:, 1] - rng[:, 0])[order]
+    bucket = np.floor(np.log2(n + 1.0))
+    assert (np.diff(bucket) <= 0).all()
