@@ -94,9 +94,11 @@ __global__ __launch_bounds__(kBlock) void cap_count_kernel(const int32_t* ranges
 }
 
 // Cap score o / sqrt(A C - B^2), one IEEE rounding per operation, compared as its bit pattern.
+// sqrtf (not __fsqrt_rn, which lowers to the 1-ulp v_sqrt_f32 alone) gets the correctly rounded
+// lowering: v_sqrt_f32 followed by an FMA-residual correction of +-1 ulp.
 __device__ __forceinline__ uint32_t cap_score_bits(float4 co) {
     const float det = __fsub_rn(__fmul_rn(co.x, co.z), __fmul_rn(co.y, co.y));
-    return __float_as_uint(__fdiv_rn(co.w, __fsqrt_rn(det)));
+    return __float_as_uint(__fdiv_rn(co.w, sqrtf(det)));
 }
 
 __device__ __forceinline__ int block_excl_scan(int x, int* s_wave, int* total) {
