@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--cap", type=int, default=0, help="per-tile cap K (0 = off)")
     ap.add_argument("--cpu-views", type=int, default=4, help="views of the workload the CPU oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (3x), the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -103,6 +106,15 @@ def main():
     vis = [info.vis_count[v] for v in range(r.V)]
     M = int(info.num_instances)
     log(f"[bench] visible {vis}, instances {M}, evaluated pairs {E_eval}, box pairs {E_box}, blends {B}")
+
+    if args.copy_calibration:
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copies: 3 x {src.numel() * 4} bytes read and written")
+        del src, dst
 
     def stage_times(mode):
         ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
