@@ -184,7 +184,8 @@ def main():
             "gaussians": scene.n, "width": r.W, "height": r.H, "views": r.V, "tile_cap": args.cap,
         },
         "roofline": {
-            "kernel": "raster_fused (gs_raster_fused call: gradient zeroing + fused kernel)",
+            "kernel": "raster_fused (gs_raster_fused call: partial-record clear, fused kernel, per-Gaussian "
+                      "reduction)",
             "bound": "alu",
             "achieved": achieved,
             "peak": ALU_PEAK_TFLOPS,
@@ -194,16 +195,19 @@ def main():
             "algorithmic_flops": flops,
             "launch_ms": raster_fused_ms,
             "hbm_frac_algorithmic": None,
+            "algorithmic_bytes": None,
         },
         "counts": {"visible": vis, "instances": M, "evaluated_pairs": E_eval, "box_pairs": E_box, "blends": B},
         "stages_ms": {"fused": stages_fused, "separate": stages_sep},
         "separate_path": {"ms_per_step": ms_sep, "blends_per_s": B / (ms_sep * 1e-3), "raster_ms": raster_sep_ms},
         "cpu_baseline": None,
     }
-    # the fused kernel's algorithmic HBM bytes: records of every list entry it stages (40 B per
-    # entry incl. the slot id), the target image (12 B/px) and one float atomic per gradient
-    # component and entry (9 x 4 B read-modify-write).
-    alg_bytes = 40 * M + 12 * r.V * r.W * r.H + 72 * M
+    # algorithmic HBM bytes of the call, per instance: its record and slot id (40 B) and the inputs
+    # of its emission index (12 B) read once, its 9-float partial record cleared, written and read
+    # back by the reduction (3 x 36 B); per visible Gaussian the 9 gradient floats written (36 B);
+    # per pixel the target image (12 B).
+    alg_bytes = (40 + 12 + 3 * 36) * M + 36 * sum(vis) + 12 * r.V * r.W * r.H
+    out["roofline"]["algorithmic_bytes"] = alg_bytes
     out["roofline"]["hbm_frac_algorithmic"] = alg_bytes / (raster_fused_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
     if not args.no_cpu_baseline:
         views = list(range(min(args.cpu_views, r.V)))

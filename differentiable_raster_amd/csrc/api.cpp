@@ -174,6 +174,7 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     const int32_t* ranges = use_capped ? bins->ranges_capped : bins->ranges;
     const int32_t* vals = use_capped ? bins->vals_capped : bins->vals;
     if (!ranges || !vals) return fail(GS_ERR_INVALID_ARGUMENT, "bins ranges/vals are null");
+    if (bins->count < 0) return fail(GS_ERR_INVALID_ARGUMENT, "bins hold no lists (the last gs_bin_tiles failed)");
     ra->V = V;
     ra->width = cams[0].width;
     ra->height = cams[0].height;
@@ -188,7 +189,25 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     ra->color = proj->color;
     ra->vis_count = proj->vis_count;
     ra->tile_order = bins->tile_order;
+    ra->tile_rect = reinterpret_cast<const ushort4*>(proj->tile_rect);
+    ra->slot_offset = bins->slot_offset;
+    ra->n_tiles = proj->n_tiles;
+    ra->partials = nullptr;
+    ra->num_instances = bins->count;
     ra->counters = nullptr;
+    return GS_OK;
+}
+
+// The backward's partial-record workspace and the bins/projection fields it needs.
+gs_status check_partials(const gs_projected* proj, const gs_bins* bins, void* ws, size_t ws_bytes, RasterArgs* ra) {
+    if (!proj->tile_rect || !proj->n_tiles || !bins->slot_offset)
+        return fail(GS_ERR_INVALID_ARGUMENT, "tile_rect / n_tiles / slot_offset are null");
+    if (bins->count < 0 || bins->count > bins->capacity)
+        return fail(GS_ERR_INVALID_ARGUMENT, "bins->count %lld outside [0, capacity]", (long long)bins->count);
+    const size_t need = sizeof(float) * 9 * (size_t)bins->count;
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(GS_ERR_CAPACITY, "raster workspace %zu < %zu bytes", ws_bytes, need);
+    ra->partials = static_cast<float*>(ws);
     return GS_OK;
 }
 
@@ -273,6 +292,11 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     return hip_check(launch_project(a, static_cast<hipStream_t>(stream)), "gs_project launch");
 }
 
+size_t gs_raster_workspace_size(int64_t instance_capacity) {
+    if (instance_capacity < 0) return 0;
+    return align256(sizeof(float) * 9 * (size_t)instance_capacity);
+}
+
 size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height, int64_t instance_capacity) {
     if (n < 0 || V < 1 || width <= 0 || height <= 0 || instance_capacity < 0) return 0;
     size_t bytes = 0;
@@ -289,13 +313,14 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
     if ((st = check_projected(proj, true)) != GS_OK) return st;
     if (!proj->depth || !proj->tile_rect || !proj->n_tiles)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected depth/rect/n_tiles are null");
-    if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges)
+    if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges || !bins->slot_offset)
         return fail(GS_ERR_INVALID_ARGUMENT, "bins outputs are null");
     if (p->tile_cap > 0 && (!bins->vals_capped || !bins->ranges_capped || !bins->num_capped))
         return fail(GS_ERR_INVALID_ARGUMENT, "capped outputs are null while tile_cap > 0");
     if (!info) return fail(GS_ERR_INVALID_ARGUMENT, "info is null");
     if (bins->capacity < 0 || bins->capacity >= (int64_t(1) << 31))
         return fail(GS_ERR_INVALID_ARGUMENT, "bins capacity outside [0, 2^31)");
+    bins->count = -1;  // until the lists are complete
     const int tiles_x = tiles_along(cams[0].width), tiles_y = tiles_along(cams[0].height);
     const int32_t tpv = tiles_x * tiles_y;
     const int32_t tiles_total = tpv * V;
@@ -359,7 +384,7 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         uint32_t* v1 = odd ? reinterpret_cast<uint32_t*>(bins->vals) : w.tval_alt;
         if (e == hipSuccess)
             e = launch_emit(packed, w.offsets, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity, nvis,
-                            tiles_x, tpv, (int32_t)M, k0, reinterpret_cast<int32_t*>(v0), s);
+                            tiles_x, tpv, (int32_t)M, k0, reinterpret_cast<int32_t*>(v0), bins->slot_offset, s);
         if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
         if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);
     }
@@ -374,6 +399,7 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
                                   proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets, bins->vals_capped,
                                   bins->ranges_capped, w.tkey_alt, s);
     }
+    if (e == hipSuccess) bins->count = M;
     return hip_check(e, "gs_bin_tiles launch");
 }
 
@@ -402,7 +428,8 @@ gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float*
 
 gs_status gs_raster_bwd(const gs_camera* cams, const gs_projected* proj, const gs_bins* bins, int32_t V,
                         const gs_render_params* p, int32_t use_capped, const float* image, const float* t_final,
-                        const int32_t* n_contrib, const float* dl_dimage, gs_grads2d* grads, void* stream) {
+                        const int32_t* n_contrib, const float* dl_dimage, gs_grads2d* grads, void* ws,
+                        size_t ws_bytes, void* stream) {
     g_last_error.clear();
     RasterArgs ra;
     gs_status st = check_raster(cams, proj, bins, V, p, use_capped, &ra);
@@ -410,6 +437,7 @@ gs_status gs_raster_bwd(const gs_camera* cams, const gs_projected* proj, const g
     if (!t_final || !n_contrib || !dl_dimage) return fail(GS_ERR_INVALID_ARGUMENT, "backward inputs are null");
     Grads g;
     if ((st = check_grads(grads, &g)) != GS_OK) return st;
+    if ((st = check_partials(proj, bins, ws, ws_bytes, &ra)) != GS_OK) return st;
     return hip_check(launch_raster_bwd(ra, image, t_final, n_contrib, dl_dimage, g, static_cast<hipStream_t>(stream)),
                      "gs_raster_bwd launch");
 }
@@ -417,7 +445,7 @@ gs_status gs_raster_bwd(const gs_camera* cams, const gs_projected* proj, const g
 gs_status gs_raster_fused(const gs_camera* cams, const gs_projected* proj, const gs_bins* bins, int32_t V,
                           const gs_render_params* p, int32_t use_capped, gs_loss_mode mode,
                           const float* target_or_dldc, float loss_scale, float* image_opt, float* loss_sum_opt,
-                          gs_grads2d* grads, gs_counters* counters, void* stream) {
+                          gs_grads2d* grads, gs_counters* counters, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     RasterArgs ra;
     gs_status st = check_raster(cams, proj, bins, V, p, use_capped, &ra);
@@ -426,6 +454,7 @@ gs_status gs_raster_fused(const gs_camera* cams, const gs_projected* proj, const
     if (!target_or_dldc) return fail(GS_ERR_INVALID_ARGUMENT, "target_or_dldc is null");
     Grads g;
     if ((st = check_grads(grads, &g)) != GS_OK) return st;
+    if ((st = check_partials(proj, bins, ws, ws_bytes, &ra)) != GS_OK) return st;
     ra.counters = counters;
     return hip_check(launch_raster_fused(ra, (int)mode, target_or_dldc, loss_scale, image_opt, loss_sum_opt, g,
                                          static_cast<hipStream_t>(stream)),

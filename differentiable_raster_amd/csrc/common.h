@@ -106,7 +106,7 @@ hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, 
                                 int32_t* out, hipStream_t s);
 hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
                        int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                       int32_t* vals, hipStream_t s);
+                       int32_t* vals, int32_t* slot_offset, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
 hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s);
 // Heavy-first permutation of the tiles (stable radix pass on a 5-bit length bucket).
@@ -128,8 +128,13 @@ struct RasterArgs {
     const float4* conic_opacity;
     const float* color;
     const int32_t* vis_count;
-    const int32_t* tile_order;  // optional: workgroup -> global tile (heavy tiles first)
-    int64_t* counters;          // optional
+    const int32_t* tile_order;   // optional: workgroup -> global tile (heavy tiles first)
+    const ushort4* tile_rect;    // backward: instance index of (slot, tile)
+    const int32_t* slot_offset;  // backward: first emission index of each slot
+    const int32_t* n_tiles;      // backward: instances per slot
+    float* partials;             // backward: [instances][9] per-instance gradient records
+    int64_t num_instances;       // backward: records in use
+    int64_t* counters;           // optional
 };
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s);
 hipError_t launch_loss_l1(int64_t n, const float* image, const float* target, float scale, float* dl, float* loss_sum,
@@ -140,7 +145,6 @@ struct Grads {
     float* d_opacity;
     float* d_color;
 };
-hipError_t launch_zero_grads(const int32_t* vis_count, int32_t V, int32_t capacity, Grads g, hipStream_t s);
 hipError_t launch_raster_bwd(const RasterArgs& a, const float* image, const float* t_final, const int32_t* n_contrib,
                              const float* dl, Grads g, hipStream_t s);
 hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,

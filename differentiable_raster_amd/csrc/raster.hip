@@ -22,8 +22,9 @@
 // has stopped.  The backward walks it back to front from n_contrib, recovering T by division by
 // (1 - alpha) and carrying the colour behind.  A row sums each entry's nine gradient components
 // over its 16 lanes with four DPP adds each and adds the sums into per-entry accumulators in LDS
-// (ds_add_f32); after each batch one thread per entry flushes its accumulators with one global
-// float atomic per component, so global atomics are one per (entry, tile, component).  The fused
+// (ds_add_f32); after each batch one thread per entry stores its sums as that (Gaussian, tile)
+// instance's partial record, and a per-Gaussian pass adds up each Gaussian's records: the
+// gradients need no global atomics and every record is written once.  The fused
 // kernel runs both passes on one workgroup: per-pixel C, T and n_contrib stay in registers, dL/dC
 // is formed in registers, and the last staged forward batch (which holds the last blended entry
 // of every pixel of the tile) is reused as the first backward batch.
@@ -41,7 +42,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct TileCtx {
-    int v, g, px, py, lane, w, row, x0, y0;
+    int v, g, px, py, lane, w, row, x0, y0, tx, ty;
     int list_id;   // this lane's 4x4 block, as a list index: w * 4 + row
     bool inside;
     float fpx, fpy;
@@ -62,6 +63,8 @@ __device__ __forceinline__ TileCtx tile_ctx(const RasterArgs& a) {
     c.v = c.g / tpv;
     const int t = c.g - c.v * tpv;
     const int tx = t % a.tiles_x, ty = t / a.tiles_x;
+    c.tx = tx;
+    c.ty = ty;
     c.lane = threadIdx.x & (kWave - 1);
     c.w = threadIdx.x / kWave;
     c.row = c.lane >> 4;
@@ -86,7 +89,7 @@ struct Batch {
     float2 xy[kBatch];      // projected centre
     float4 q[kBatch];       // (a, b, c, thr): p2 = a dx^2 + b dx dy + c dy^2, blend iff p2 >= thr
     float4 oc[kBatch];      // (o, r, g, b)
-    int32_t slot[kBatch];
+    int32_t inst[kBatch];   // emission index of the (slot, tile) instance (backward only)
     uint16_t mask[kBatch];  // 4x4 blocks of the tile the entry's alpha_min box touches
     uint8_t list[kBlocks4][kBatch];
 };
@@ -96,7 +99,10 @@ struct Acc {
     float v[9][kBatch];
 };
 
-// Stage list position j of the tile into batch index k (one thread per entry).
+// Stage list position j of the tile into batch index k (one thread per entry).  INST: also the
+// instance's emission index, slot_offset[slot] + (row-major index of this tile in the slot's
+// rectangle), where the backward stores the instance's gradient record.
+template <bool INST>
 __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Batch& b, int k, int32_t j) {
     const int32_t slot = a.vals[c.start + j];
     const size_t idx = c.vbase + slot;
@@ -106,7 +112,10 @@ __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Bat
     b.xy[k] = xy;
     b.q[k] = make_float4(-0.5f * kLog2e * co.x, -kLog2e * co.y, -0.5f * kLog2e * co.z, __log2f(amin / co.w));
     b.oc[k] = make_float4(co.w, a.color[3 * idx], a.color[3 * idx + 1], a.color[3 * idx + 2]);
-    b.slot[k] = slot;
+    if (INST) {
+        const ushort4 rc = a.tile_rect[idx];
+        b.inst[k] = a.slot_offset[idx] + (c.ty - rc.y) * (rc.z - rc.x + 1) + (c.tx - rc.x);
+    }
     // conservative block mask from the alpha_min box of the conic (Sigma' = conic^-1)
     uint32_t m = 0xFFFFu;
     const float det = co.x * co.z - co.y * co.y;
@@ -323,9 +332,10 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
     }
 }
 
-// After a backward batch: one thread per entry adds its accumulated gradient to the outputs
-// (one float atomic per nonzero component) and clears the accumulators.
-__device__ __forceinline__ void flush_batch(const TileCtx& c, const Batch& b, Acc& acc, int cnt, Grads gr) {
+// After a backward batch: one thread per entry stores its accumulated gradient as the
+// instance's partial record (plain stores: every instance belongs to exactly one tile, and the
+// records start zeroed) and clears the accumulators.
+__device__ __forceinline__ void flush_batch(const RasterArgs& a, const Batch& b, Acc& acc, int cnt) {
     __syncthreads();
     const int k = threadIdx.x;
     if (k < cnt) {
@@ -337,17 +347,11 @@ __device__ __forceinline__ void flush_batch(const TileCtx& c, const Batch& b, Ac
             any |= d[t] != 0.0f;
             acc.v[t][k] = 0.0f;
         }
-        if (any) {
-            const size_t idx = c.vbase + b.slot[k];
-            atomicAdd(&gr.d_mean2d[idx].x, d[0]);
-            atomicAdd(&gr.d_mean2d[idx].y, d[1]);
-            atomicAdd(&gr.d_conic[3 * idx + 0], d[2]);
-            atomicAdd(&gr.d_conic[3 * idx + 1], d[3]);
-            atomicAdd(&gr.d_conic[3 * idx + 2], d[4]);
-            atomicAdd(&gr.d_opacity[idx], d[5]);
-            atomicAdd(&gr.d_color[3 * idx + 0], d[6]);
-            atomicAdd(&gr.d_color[3 * idx + 1], d[7]);
-            atomicAdd(&gr.d_color[3 * idx + 2], d[8]);
+        // the bound only matters for a projection changed after binning (stale emission indices)
+        if (any && (uint64_t)(uint32_t)b.inst[k] < (uint64_t)a.num_instances) {
+            float* rec = a.partials + (size_t)b.inst[k] * 9;
+#pragma unroll
+            for (int t = 0; t < 9; t++) rec[t] = d[t];
         }
     }
 }
@@ -387,7 +391,7 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 
 // Forward over the whole tile list.  On return *last_b0 is the list position of the last staged
 // batch (-1 if none), *last_cnt its entry count and *last_lists this lane's lists in it.
-template <bool COUNT>
+template <bool COUNT, bool INST>
 __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Fwd& f, Counts& cnt,
                                              int32_t* last_b0, int* last_cnt, Lists* last_lists) {
     *last_b0 = -1;
@@ -396,7 +400,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
     for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
         if (__syncthreads_count(f.done) == kBlock) break;
         const int cnt_b = min(kBatch, c.n - b0);
-        if ((int)threadIdx.x < cnt_b) stage(a, c, b, threadIdx.x, b0 + threadIdx.x);
+        if ((int)threadIdx.x < cnt_b) stage<INST>(a, c, b, threadIdx.x, b0 + threadIdx.x);
         __syncthreads();
         const Lists l = build_lists(c, b, cnt_b);
         fwd_walk<COUNT>(a, c, b, l, b0, f, cnt);
@@ -410,8 +414,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
 // `resident_cnt` entries and this lane's lists `resident`) is already staged.  The gradient
 // accumulators must be zero on entry.
 __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Acc& acc, int32_t maxnc,
-                                              int32_t resident_b0, int resident_cnt, Lists resident, Bwd& s,
-                                              Grads gr) {
+                                              int32_t resident_b0, int resident_cnt, Lists resident, Bwd& s) {
     const int row_nc = row_max(s.nc);
     if (maxnc <= 0) return;
     for (int32_t b0 = ((maxnc - 1) / kBatch) * kBatch; b0 >= 0; b0 -= kBatch) {
@@ -420,12 +423,12 @@ __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx
         if (b0 != resident_b0) {
             cnt_b = min(kBatch, maxnc - b0);
             __syncthreads();
-            if ((int)threadIdx.x < cnt_b) stage(a, c, b, threadIdx.x, b0 + threadIdx.x);
+            if ((int)threadIdx.x < cnt_b) stage<true>(a, c, b, threadIdx.x, b0 + threadIdx.x);
             __syncthreads();
             l = build_lists(c, b, cnt_b);
         }
         bwd_walk(a, c, b, acc, l, b0, row_nc, s);
-        flush_batch(c, b, acc, cnt_b, gr);
+        flush_batch(a, b, acc, cnt_b);
         resident_b0 = -1;
     }
 }
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(kBlock) void raster_fwd_kernel(RasterArgs a, float*
     int32_t last_b0;
     int last_cnt;
     Lists last_lists;
-    forward_tile<COUNT>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
+    forward_tile<COUNT, false>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
     if (COUNT) add_counters(a.counters, cnt);
     if (!c.inside) return;
     const size_t plane = (size_t)a.width * a.height;
@@ -467,20 +470,38 @@ __global__ __launch_bounds__(256) void loss_l1_kernel(int64_t n, const float* im
     }
 }
 
-__global__ __launch_bounds__(256) void zero_grads_kernel(const int32_t* vis_count, int32_t V, int32_t capacity, Grads g) {
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+// Per-Gaussian gather of the backward: the gradient of a visible slot is the sum of its
+// instances' partial records, which lie contiguously at [slot_offset, slot_offset + n_tiles).
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis_count, int32_t V, int32_t capacity,
+                                                              const int32_t* slot_offset, const int32_t* n_tiles,
+                                                              const float* partials, int64_t num_instances, Grads g) {
     for (int v = 0; v < V; v++) {
         const int32_t cnt = vis_count[v];
         const size_t base = (size_t)v * capacity;
         for (int32_t s = blockIdx.x * 256 + threadIdx.x; s < cnt; s += gridDim.x * 256) {
             const size_t i = base + s;
-            g.d_mean2d[i] = make_float2(0.0f, 0.0f);
-            g.d_conic[3 * i] = 0.0f;
-            g.d_conic[3 * i + 1] = 0.0f;
-            g.d_conic[3 * i + 2] = 0.0f;
-            g.d_opacity[i] = 0.0f;
-            g.d_color[3 * i] = 0.0f;
-            g.d_color[3 * i + 1] = 0.0f;
-            g.d_color[3 * i + 2] = 0.0f;
+            const int64_t off = slot_offset[i];
+            const float* rec = partials + (size_t)off * 9;
+            // clamped to the records that exist (only a stale projection could reach past them)
+            const int n = (off < 0 || off > num_instances) ? 0 : (int)min((int64_t)n_tiles[i], num_instances - off);
+            float d[9];
+#pragma unroll
+            for (int t = 0; t < 9; t++) d[t] = 0.0f;
+            for (int k = 0; k < n; k++)
+#pragma unroll
+                for (int t = 0; t < 9; t++) d[t] += rec[9 * k + t];
+            g.d_mean2d[i] = make_float2(d[0], d[1]);
+            g.d_conic[3 * i] = d[2];
+            g.d_conic[3 * i + 1] = d[3];
+            g.d_conic[3 * i + 2] = d[4];
+            g.d_opacity[i] = d[5];
+            g.d_color[3 * i] = d[6];
+            g.d_color[3 * i + 1] = d[7];
+            g.d_color[3 * i + 2] = d[8];
         }
     }
 }
@@ -509,7 +530,7 @@ __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const 
     s.B0 = s.B1 = s.B2 = 0.0f;
     zero_acc(acc);
     const int maxnc = block_max(s.nc, s_red);
-    backward_tile(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s, gr);
+    backward_tile(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s);
 }
 
 template <bool COUNT>
@@ -525,7 +546,7 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
     int last_cnt;
     Lists last_lists;
     zero_acc(acc);
-    forward_tile<COUNT>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
+    forward_tile<COUNT, true>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
     if (COUNT) add_counters(a.counters, cnt);
     // loss gradient in registers
     const size_t plane = (size_t)a.width * a.height;
@@ -567,7 +588,7 @@ __global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int 
     }
     const int maxnc = block_max(s.nc, s_red);
     // every pixel's last blended entry lies in the last staged batch, so it is still resident
-    backward_tile(a, c, b, acc, maxnc, last_b0, last_cnt, last_lists, s, gr);
+    backward_tile(a, c, b, acc, maxnc, last_b0, last_cnt, last_lists, s);
 }
 
 }  // namespace
@@ -591,35 +612,43 @@ hipError_t launch_loss_l1(int64_t n, const float* image, const float* target, fl
     return hipGetLastError();
 }
 
-hipError_t launch_zero_grads(const int32_t* vis_count, int32_t V, int32_t capacity, Grads g, hipStream_t s) {
-    int blocks = (capacity + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(zero_grads_kernel, dim3(blocks), dim3(256), 0, s, vis_count, V, capacity, g);
+static unsigned grid_for(int64_t n) {
+    int64_t b = (n + 255) / 256;
+    if (b > 8192) b = 8192;
+    if (b < 1) b = 1;
+    return (unsigned)b;
+}
+
+// Zero the partial records, run a backward kernel, then gather the partials per Gaussian.
+template <typename Launch>
+static hipError_t with_partials(const RasterArgs& a, Grads g, hipStream_t s, Launch launch) {
+    const int64_t n = a.num_instances * 9;
+    if (n > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.partials, n);
+    launch();
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(a.capacity)), dim3(256), 0, s, a.vis_count, a.V,
+                       a.capacity, a.slot_offset, a.n_tiles, a.partials, a.num_instances, g);
     return hipGetLastError();
 }
 
 hipError_t launch_raster_bwd(const RasterArgs& a, const float* /*image*/, const float* t_final, const int32_t* n_contrib,
                              const float* dl, Grads g, hipStream_t s) {
-    hipError_t e = launch_zero_grads(a.vis_count, a.V, a.capacity, g, s);
-    if (e != hipSuccess) return e;
     const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
-    hipLaunchKernelGGL(raster_bwd_kernel, dim3(nblocks), dim3(kBlock), 0, s, a, t_final, n_contrib, dl, g);
-    return hipGetLastError();
+    return with_partials(a, g, s, [&] {
+        hipLaunchKernelGGL(raster_bwd_kernel, dim3(nblocks), dim3(kBlock), 0, s, a, t_final, n_contrib, dl, g);
+    });
 }
 
 hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,
                                float* loss_sum, Grads g, hipStream_t s) {
-    hipError_t e = launch_zero_grads(a.vis_count, a.V, a.capacity, g, s);
-    if (e != hipSuccess) return e;
     const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
-    if (a.counters)
-        hipLaunchKernelGGL(raster_fused_kernel<true>, dim3(nblocks), dim3(kBlock), 0, s, a, mode, target_or_dl, scale,
-                           image, loss_sum, g);
-    else
-        hipLaunchKernelGGL(raster_fused_kernel<false>, dim3(nblocks), dim3(kBlock), 0, s, a, mode, target_or_dl, scale,
-                           image, loss_sum, g);
-    return hipGetLastError();
+    return with_partials(a, g, s, [&] {
+        if (a.counters)
+            hipLaunchKernelGGL(raster_fused_kernel<true>, dim3(nblocks), dim3(kBlock), 0, s, a, mode, target_or_dl,
+                               scale, image, loss_sum, g);
+        else
+            hipLaunchKernelGGL(raster_fused_kernel<false>, dim3(nblocks), dim3(kBlock), 0, s, a, mode, target_or_dl,
+                               scale, image, loss_sum, g);
+    });
 }
 
 }  // namespace gsmi

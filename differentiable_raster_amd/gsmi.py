@@ -54,9 +54,10 @@ class gs_projected(ctypes.Structure):
 
 
 class gs_bins(ctypes.Structure):
-    _fields_ = [("capacity", ctypes.c_int64), ("tile_keys", ctypes.c_void_p), ("vals", ctypes.c_void_p),
-                ("ranges", ctypes.c_void_p), ("vals_capped", ctypes.c_void_p), ("ranges_capped", ctypes.c_void_p),
-                ("num_capped", ctypes.c_void_p), ("tile_order", ctypes.c_void_p)]
+    _fields_ = [("capacity", ctypes.c_int64), ("count", ctypes.c_int64), ("tile_keys", ctypes.c_void_p),
+                ("vals", ctypes.c_void_p), ("ranges", ctypes.c_void_p), ("vals_capped", ctypes.c_void_p),
+                ("ranges_capped", ctypes.c_void_p), ("num_capped", ctypes.c_void_p), ("tile_order", ctypes.c_void_p),
+                ("slot_offset", ctypes.c_void_p)]
 
 
 class gs_bin_info(ctypes.Structure):
@@ -90,11 +91,13 @@ _SIGS = {
                                        ctypes.c_void_p]),
     "gs_raster_bwd": (ctypes.c_int, [_P(gs_camera), _P(gs_projected), _P(gs_bins), ctypes.c_int32,
                                      _P(gs_render_params), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_void_p, _P(gs_grads2d), ctypes.c_void_p]),
+                                     ctypes.c_void_p, ctypes.c_void_p, _P(gs_grads2d), ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]),
     "gs_raster_fused": (ctypes.c_int, [_P(gs_camera), _P(gs_projected), _P(gs_bins), ctypes.c_int32,
                                        _P(gs_render_params), ctypes.c_int32, ctypes.c_int, ctypes.c_void_p,
                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, _P(gs_grads2d),
-                                       ctypes.c_void_p, ctypes.c_void_p]),
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "gs_raster_workspace_size": (ctypes.c_size_t, [ctypes.c_int64]),
     "gs_fused_max_cap": (ctypes.c_int, [_P(ctypes.c_int32)]),
 }
 
@@ -179,6 +182,10 @@ def gs_project_workspace_size(n: int, V: int) -> int:
     return int(load().gs_project_workspace_size(n, V))
 
 
+def gs_raster_workspace_size(instance_capacity: int) -> int:
+    return int(load().gs_raster_workspace_size(instance_capacity))
+
+
 def gs_bin_workspace_size(n: int, V: int, width: int, height: int, instance_capacity: int) -> int:
     return int(load().gs_bin_workspace_size(n, V, width, height, instance_capacity))
 
@@ -218,15 +225,17 @@ def gs_loss_l1_grad(V, width, height, image, target, scale, dl, loss_sum=None, s
 
 
 def gs_raster_bwd(cams, proj, bins, V, params, use_capped, image, t_final, n_contrib, dl, grads: gs_grads2d,
-                  stream=None):
+                  ws, stream=None):
     _check(load().gs_raster_bwd(cams, ctypes.byref(proj), ctypes.byref(bins), V, ctypes.byref(params),
                                 int(use_capped), _ptr(image), _ptr(t_final), _ptr(n_contrib), _ptr(dl),
-                                ctypes.byref(grads), _stream(stream)), "gs_raster_bwd")
+                                ctypes.byref(grads), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "gs_raster_bwd")
 
 
 def gs_raster_fused(cams, proj, bins, V, params, use_capped, mode, target_or_dl, scale, image, loss_sum,
-                    grads: gs_grads2d, counters=None, stream=None):
+                    grads: gs_grads2d, ws, counters=None, stream=None):
     _check(load().gs_raster_fused(cams, ctypes.byref(proj), ctypes.byref(bins), V, ctypes.byref(params),
                                   int(use_capped), int(mode), _ptr(target_or_dl), float(scale), _ptr(image),
-                                  _ptr(loss_sum), ctypes.byref(grads), _ptr(counters), _stream(stream)),
+                                  _ptr(loss_sum), ctypes.byref(grads), _ptr(counters), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)),
            "gs_raster_fused")

@@ -60,6 +60,7 @@ class Renderer:
         self.ranges_capped = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
         self.num_capped = torch.zeros(1, dtype=i32, device=dev)
         self.tile_order = torch.zeros(V * self.tpv, dtype=i32, device=dev)
+        self.slot_offset = torch.zeros(V * cap, dtype=i32, device=dev)
         self.inst_capacity = -1
         self._alloc_bins(instance_capacity if instance_capacity is not None else 0)
         plane = self.H * self.W
@@ -87,9 +88,10 @@ class Renderer:
         self.tile_keys = torch.empty(c, dtype=torch.int32, device=dev)
         self.vals = torch.empty(c, dtype=torch.int32, device=dev)
         self.vals_capped = torch.empty(c, dtype=torch.int32, device=dev)
-        self.bins = gsmi.gs_bins(c, self.tile_keys.data_ptr(), self.vals.data_ptr(), self.ranges.data_ptr(),
+        self.bins = gsmi.gs_bins(c, 0, self.tile_keys.data_ptr(), self.vals.data_ptr(), self.ranges.data_ptr(),
                                  self.vals_capped.data_ptr(), self.ranges_capped.data_ptr(), self.num_capped.data_ptr(),
-                                 self.tile_order.data_ptr())
+                                 self.tile_order.data_ptr(), self.slot_offset.data_ptr())
+        self.ws_raster = torch.empty(gsmi.gs_raster_workspace_size(c), dtype=torch.uint8, device=dev)
         self.ws_bin = torch.empty(gsmi.gs_bin_workspace_size(self.capacity, self.V, self.W, self.H, c),
                                   dtype=torch.uint8, device=dev)
         self.inst_capacity = c
@@ -126,7 +128,7 @@ class Renderer:
 
     def backward(self, dl):
         gsmi.gs_raster_bwd(self.cams, self.proj, self.bins, self.V, self.params, self.use_capped, self.image,
-                           self.t_final, self.n_contrib, dl, self.grads)
+                           self.t_final, self.n_contrib, dl, self.grads, self.ws_raster)
 
     def fused(self, scale: float = 1.0, image: bool = True, loss_sum: bool = False, counters: bool = False):
         if counters:
@@ -139,7 +141,7 @@ class Renderer:
             mode, src = gsmi.GS_LOSS_EXTERNAL, self.dldc_in
         gsmi.gs_raster_fused(self.cams, self.proj, self.bins, self.V, self.params, self.use_capped, mode, src,
                              scale, self.image if image else None, self.loss_sum if loss_sum else None, self.grads,
-                             self.counters if counters else None)
+                             self.ws_raster, self.counters if counters else None)
 
     def iteration(self, mode: str = "fused", scale: float = 1.0, image: bool = False):
         self.project()

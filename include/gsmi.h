@@ -104,6 +104,9 @@ typedef struct {
  * ranges[g] = [start, end) into vals (positions over all views); empty tiles hold (0, 0). */
 typedef struct {
     int64_t capacity;           /* instance capacity of tile_keys / vals / vals_capped */
+    int64_t count;              /* written by gs_bin_tiles (host value): instances of all views on
+                                   success, -1 after a failed call; the raster calls refuse
+                                   bins whose count is negative */
     uint32_t* tile_keys;        /* [capacity] global tile id of each sorted instance */
     int32_t* vals;              /* [capacity] slot of each sorted instance */
     int32_t* ranges;            /* [V * tiles_per_view][2] */
@@ -114,6 +117,11 @@ typedef struct {
                                    the global tiles, longest lists first, written by gs_bin_tiles
                                    and used by the raster calls to schedule heavy tiles early;
                                    the order changes no result */
+    int32_t* slot_offset;       /* [V][proj->capacity] written by gs_bin_tiles: the first index of
+                                   each visible slot's instances in emission order; instance k of
+                                   a slot (its k-th tile, row-major in its rectangle) has index
+                                   slot_offset + k.  The backward calls place per-instance gradient
+                                   partials there. */
 } gs_bins;
 
 /* Host-side counts that gs_bin_tiles reports. */
@@ -125,8 +133,8 @@ typedef struct {
                                               on (the count is then on the device, bins->num_capped) */
 } gs_bin_info;
 
-/* Per-slot 2D gradients, [V][capacity][k], float32, device.  Overwritten by the raster calls
- * (zeroed for slots < vis_count, then accumulated with atomics). */
+/* Per-slot 2D gradients, [V][capacity][k], float32, device.  The backward calls overwrite the
+ * entries of every visible slot (slots >= vis_count are left untouched). */
 typedef struct {
     float* d_mean2d;  /* [V][capacity][2] dL/d mean2d (pixels) */
     float* d_conic;   /* [V][capacity][3] dL/d (A, B, C) */
@@ -167,6 +175,10 @@ size_t gs_project_workspace_size(int32_t n, int32_t V);
 gs_status gs_project(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, int32_t V,
                      const gs_render_params* p, gs_projected* out, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Workspace bytes of gs_raster_bwd / gs_raster_fused for an instance capacity: one float32
+ * partial-gradient record (9 values) per (Gaussian, tile) instance. */
+size_t gs_raster_workspace_size(int64_t instance_capacity);
 
 /* Workspace bytes of gs_bin_tiles for n Gaussians, V views and an instance capacity. */
 size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height, int64_t instance_capacity);
@@ -213,31 +225,35 @@ gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float*
  *   dL/dc_j = alpha_j T_j g,  dL/dalpha_j = sum_ch g_ch (T_j (c_j - Bk) - T_final bg / (1 - alpha_j)),
  * and unless alpha was clamped, dL/do = G dL/dalpha, dL/dmean2d = o G dL/dalpha (A dx + B dy,
  * B dx + C dy) with d = pixel centre - mean2d, dL/d(A,B,C) = o G dL/dalpha (-dx^2/2, -dx dy,
- * -dy^2/2).  Contributions are summed across each wavefront before one float atomic per
- * (entry, wavefront, component).  grads are zeroed for the visible slots, then accumulated.
+ * -dy^2/2).  Within a tile, each entry's contributions are summed over the pixels in LDS and
+ * stored once, without atomics, as a partial record at the instance's emission index (see
+ * gs_bins.slot_offset) in the workspace; a per-Gaussian pass then sums each slot's partials into
+ * grads.  ws: gs_raster_workspace_size(bins->capacity) bytes, 256-byte aligned.
  */
 gs_status gs_raster_bwd(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
                         int32_t V, const gs_render_params* p, int32_t use_capped, const float* image,
                         const float* t_final, const int32_t* n_contrib, const float* dl_dimage,
-                        gs_grads2d* grads, void* stream);
+                        gs_grads2d* grads, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * A10: fused forward + loss gradient + backward in one kernel per tile (ByteSplat, arXiv
  * 2610.02851, English abstract: forward and backward rasterization fused into one kernel that
  * keeps intermediates on chip).  Per-pixel colour, transmittance and n_contrib stay in
- * registers; the tile list's records stay in LDS between the two passes when they fit, else
- * they are re-read in chunks.  mode GS_LOSS_L1: target_or_dldc is the target image and the
+ * registers; records are staged through LDS in batches, and the last forward batch is reused as
+ * the first backward batch.  mode GS_LOSS_L1: target_or_dldc is the target image and the
  * gradient is loss_scale * sign(C - target); GS_LOSS_EXTERNAL: target_or_dldc is dL/dC.
  * image_opt (optional) receives the rendered image; loss_sum_opt (optional, device float)
- * accumulates scale * sum |C - target| (L1 mode only).  Same gradients as A7+A8+A9.
+ * accumulates scale * sum |C - target| (L1 mode only).  Same gradients as A7+A8+A9, gathered the
+ * same way (ws as for gs_raster_bwd).
  */
 gs_status gs_raster_fused(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
                           int32_t V, const gs_render_params* p, int32_t use_capped, gs_loss_mode mode,
                           const float* target_or_dldc, float loss_scale, float* image_opt,
-                          float* loss_sum_opt, gs_grads2d* grads, gs_counters* counters, void* stream);
+                          float* loss_sum_opt, gs_grads2d* grads, gs_counters* counters, void* ws,
+                          size_t ws_bytes, void* stream);
 
-/* Largest per-tile list length the fused kernel keeps resident in LDS for one pass
- * (longer lists are processed in chunks).  *k (host) receives it. */
+/* Entries of a tile list the rasterizers stage in LDS at a time (lists of any length are
+ * processed batch by batch).  *k (host) receives it. */
 gs_status gs_fused_max_cap(int32_t* k);
 
 #ifdef __cplusplus

@@ -121,7 +121,7 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     c = cams(gs)
     p = params(gs)
     proj = projected(gs)
-    bins = gs.gs_bins(1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    bins = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
     info = gs.gs_bin_info()
     req = ctypes.c_int64()
     ws = gs.gs_bin_workspace_size(100, 1, 64, 48, 1000)
@@ -132,25 +132,37 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(p), ctypes.byref(bins), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws - 1, None) == 2
     capped = params(gs, tile_cap=64)
-    nocap = gs.gs_bins(1000, FAKE, FAKE, FAKE, None, None, None, None)
+    nocap = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, None, None, None, None, FAKE)
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(capped), ctypes.byref(nocap), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws, None) == 1
     neg = params(gs, tile_cap=-1)
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(neg), ctypes.byref(bins), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws, None) == 1
+    # a failed gs_bin_tiles marks the bins unusable, and the raster calls refuse them
+    assert bins.count == -1
     grads = gs.gs_grads2d(FAKE, FAKE, FAKE, FAKE)
+    assert lib.gs_raster_fwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None,
+                             None) == 1
+    bins.count = 10
     assert lib.gs_raster_fwd(c, ctypes.byref(proj), None, 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, None) == 1
     assert lib.gs_raster_fwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, None, FAKE, FAKE, None,
                              None) == 1
+    rws = gs.gs_raster_workspace_size(1000)
+    assert rws >= 1000 * 36
     assert lib.gs_raster_bwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, None,
-                             ctypes.byref(grads), None) == 1
+                             ctypes.byref(grads), FAKE, rws, None) == 1
     bad_grads = gs.gs_grads2d(FAKE, None, FAKE, FAKE)
     assert lib.gs_raster_bwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE,
-                             ctypes.byref(bad_grads), None) == 1
+                             ctypes.byref(bad_grads), FAKE, rws, None) == 1
+    # partial-record workspace too small for bins->count instances
+    assert lib.gs_raster_bwd(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE,
+                             ctypes.byref(grads), FAKE, 10 * 36 - 1, None) == 2
     assert lib.gs_raster_fused(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, 7, FAKE,
-                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, None) == 1
+                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, FAKE, rws, None) == 1
     assert lib.gs_raster_fused(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, 0, None,
-                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, None) == 1
+                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, FAKE, rws, None) == 1
+    assert lib.gs_raster_fused(c, ctypes.byref(proj), ctypes.byref(bins), 1, ctypes.byref(p), 0, 0, FAKE,
+                               ctypes.c_float(1.0), None, None, ctypes.byref(grads), None, None, 0, None) == 2
     assert lib.gs_loss_l1_grad(0, 64, 48, FAKE, FAKE, ctypes.c_float(1.0), FAKE, None, None) == 1
     assert lib.gs_loss_l1_grad(1, 64, 48, None, FAKE, ctypes.c_float(1.0), FAKE, None, None) == 1
 
