@@ -64,6 +64,9 @@ def _load():
         _lib = ctypes.CDLL(_LIB)
         _lib.orc_sh_basis.restype = None
         _lib.orc_project.restype = None
+        _lib.orc_project_f64.restype = None
+        _lib.orc_project_backward.restype = None
+        _lib.orc_sh_basis_grad.restype = None
         _lib.orc_raster_forward.restype = None
         _lib.orc_raster_backward.restype = None
         _lib.orc_raster_bruteforce.restype = None
@@ -150,6 +153,78 @@ def project(scene, cam, settings) -> dict:
                     _p(out["opacity"]), _p(out["color"]), _p(out["depth"]), _p(out["rect"]),
                     _p(out["n_tiles"]), _p(out["flag"]))
     return out
+
+
+def sh_basis_grad(degree: int, dirs: np.ndarray) -> np.ndarray:
+    """Cartesian gradients (n, 16, 3) of the basis polynomials of ``sh_basis`` at dirs (n, 3).
+
+    Parity: pinned by central finite differences of ``sh_basis`` (itself pinned against scipy)."""
+    lib = _load()
+    dirs = np.ascontiguousarray(dirs, np.float64)
+    out = np.zeros((dirs.shape[0], 16, 3), np.float64)
+    for i in range(dirs.shape[0]):
+        lib.orc_sh_basis_grad(ctypes.c_int(degree), _p(dirs[i]), _p(out[i]))
+    return out[:, : (degree + 1) ** 2]
+
+
+def scene_params_f64(scene) -> dict:
+    """The scene's float32 parameters, widened exactly to float64 (SoA, as the scene holds them)."""
+    return dict(means=np.ascontiguousarray(scene.means, np.float64),
+                log_scales=np.ascontiguousarray(scene.log_scales, np.float64),
+                quats=np.ascontiguousarray(scene.quats, np.float64),
+                opacity_logits=np.ascontiguousarray(scene.opacity_logits, np.float64),
+                sh=np.ascontiguousarray(scene.sh, np.float64))
+
+
+_PARAM_KEYS = ("means", "log_scales", "quats", "opacity_logits", "sh")
+
+
+def project_f64(params: dict, cam, settings) -> dict:
+    """``project`` on double-precision parameters (``scene_params_f64`` layout), so that the
+    projection can be differentiated numerically.  Same outputs as ``project``."""
+    lib = _load()
+    n = params["means"].shape[1]
+    out = dict(visible=np.zeros(n, np.int8), mean2d=np.zeros((n, 2)), cov2d=np.zeros((n, 3)),
+               conic=np.zeros((n, 3)), opacity=np.zeros(n), color=np.zeros((n, 3)), depth=np.zeros(n),
+               rect=np.zeros((n, 4), np.int32), n_tiles=np.zeros(n, np.int32), flag=np.zeros(n, np.int8))
+    arrs = [np.ascontiguousarray(params[k], np.float64) for k in _PARAM_KEYS]
+    c, pp = _cam(cam), _params(settings)
+    lib.orc_project_f64(ctypes.c_int64(n), *[_p(a) for a in arrs], ctypes.byref(c), ctypes.byref(pp),
+                        _p(out["visible"]), _p(out["mean2d"]), _p(out["cov2d"]), _p(out["conic"]),
+                        _p(out["opacity"]), _p(out["color"]), _p(out["depth"]), _p(out["rect"]),
+                        _p(out["n_tiles"]), _p(out["flag"]))
+    return out
+
+
+def project_backward(params: dict, cam, settings, visible: np.ndarray, g_mean2d, g_conic, g_opacity, g_color,
+                     acc: Optional[dict] = None) -> dict:
+    """Chain rule of the projection for one view (test infrastructure).
+
+    ``params``: ``scene_params_f64`` layout.  ``visible`` (n,) selects the Gaussians; the
+    gradients with respect to the 2D outputs are indexed by Gaussian: g_mean2d (n,2),
+    g_conic (n,3) for (A, B, C), g_opacity (n,), g_color (n,3).  Adds this view's share to
+    ``acc`` (created zeroed when None) and returns it: d_means (3,n), d_log_scales (3,n),
+    d_quats (4,n) with respect to the raw quaternion, d_opacity_logits (n,), d_sh (3(d+1)^2, n)
+    and flag (n,) = a colour channel's pre-clamp value lies within float32 reach of zero.
+
+    Parity: pinned by central finite differences of ``project_f64`` for every parameter, by
+    invariances (an isotropic Gaussian has no quaternion gradient; the quaternion gradient is
+    orthogonal to the quaternion) and by closed forms for the colour and opacity terms."""
+    lib = _load()
+    n = params["means"].shape[1]
+    nk = params["sh"].shape[0]
+    if acc is None:
+        acc = dict(d_means=np.zeros((3, n)), d_log_scales=np.zeros((3, n)), d_quats=np.zeros((4, n)),
+                   d_opacity_logits=np.zeros(n), d_sh=np.zeros((nk, n)), flag=np.zeros(n, np.int8))
+    arrs = [np.ascontiguousarray(params[k], np.float64) for k in _PARAM_KEYS]
+    vis = np.ascontiguousarray(visible, np.int8)
+    g = [np.ascontiguousarray(x, np.float64) for x in (g_mean2d, g_conic, g_opacity, g_color)]
+    assert g[0].shape == (n, 2) and g[1].shape == (n, 3) and g[2].shape == (n,) and g[3].shape == (n, 3)
+    c, pp = _cam(cam), _params(settings)
+    lib.orc_project_backward(ctypes.c_int64(n), *[_p(a) for a in arrs], ctypes.byref(c), ctypes.byref(pp),
+                             _p(vis), *[_p(x) for x in g], _p(acc["d_means"]), _p(acc["d_log_scales"]),
+                             _p(acc["d_quats"]), _p(acc["d_opacity_logits"]), _p(acc["d_sh"]), _p(acc["flag"]))
+    return acc
 
 
 def compact(proj: dict) -> dict:

@@ -23,6 +23,12 @@
  *                       two-Gaussian closed form, brute-force all-Gaussians-per-pixel.
  *   orc_raster_backward pinned: central finite differences of the loss, two-Gaussian and
  *                       single-Gaussian closed-form derivatives.
+ *   orc_sh_basis_grad   pinned: central finite differences of orc_sh_basis.
+ *   orc_project_f64     the same per-Gaussian function as orc_project (double inputs).
+ *   orc_project_backward pinned: central finite differences of orc_project_f64 for every
+ *                       parameter component (posed cameras, fx != fy, SH degree 3);
+ *                       rotation invariance of isotropic Gaussians; quaternion-norm
+ *                       invariance; closed forms of the colour and opacity terms.
  *   The constants themselves (0.2, 0.3, 1/255, 0.99, 1e-4, 60 degree FOV) are readings that
  *   no page fixes: parity unpinned for their values.
  *
@@ -85,6 +91,51 @@ void orc_sh_basis(int degree, const double d[3], double* Y)
     Y[15] = 0.25 * sqrt(35.0 / (2.0 * pi)) * x * (x * x - 3.0 * y * y);
 }
 
+/* Cartesian gradient dY[k][0..2] = dY_k/d(x, y, z) of the basis polynomials above, at d.  The
+ * polynomials are differentiated as functions on R^3; a caller on the sphere projects out the
+ * radial part. */
+void orc_sh_basis_grad(int degree, const double d[3], double* dY)
+{
+    const double x = d[0], y = d[1], z = d[2];
+    const double pi = 3.14159265358979323846;
+    for (int k = 0; k < 48; k++) dY[k] = 0.0;
+    if (degree < 1) return;
+    const double c1 = sqrt(3.0 / (4.0 * pi));
+    dY[3 * 1 + 1] = c1;                                   /* c1 y */
+    dY[3 * 2 + 2] = c1;                                   /* c1 z */
+    dY[3 * 3 + 0] = c1;                                   /* c1 x */
+    if (degree < 2) return;
+    const double c2 = 0.5 * sqrt(15.0 / pi), c3 = 0.25 * sqrt(5.0 / pi), c4 = 0.25 * sqrt(15.0 / pi);
+    dY[3 * 4 + 0] = c2 * y;                               /* c2 x y */
+    dY[3 * 4 + 1] = c2 * x;
+    dY[3 * 5 + 1] = c2 * z;                               /* c2 y z */
+    dY[3 * 5 + 2] = c2 * y;
+    dY[3 * 6 + 2] = 6.0 * c3 * z;                         /* c3 (3 z^2 - 1) */
+    dY[3 * 7 + 0] = c2 * z;                               /* c2 x z */
+    dY[3 * 7 + 2] = c2 * x;
+    dY[3 * 8 + 0] = 2.0 * c4 * x;                         /* c4 (x^2 - y^2) */
+    dY[3 * 8 + 1] = -2.0 * c4 * y;
+    if (degree < 3) return;
+    const double c5 = 0.25 * sqrt(35.0 / (2.0 * pi)), c6 = 0.5 * sqrt(105.0 / pi);
+    const double c7 = 0.25 * sqrt(21.0 / (2.0 * pi)), c8 = 0.25 * sqrt(7.0 / pi);
+    const double c9 = 0.25 * sqrt(105.0 / pi);
+    dY[3 * 9 + 0] = 6.0 * c5 * x * y;                     /* c5 y (3 x^2 - y^2) */
+    dY[3 * 9 + 1] = c5 * (3.0 * x * x - 3.0 * y * y);
+    dY[3 * 10 + 0] = c6 * y * z;                          /* c6 x y z */
+    dY[3 * 10 + 1] = c6 * x * z;
+    dY[3 * 10 + 2] = c6 * x * y;
+    dY[3 * 11 + 1] = c7 * (5.0 * z * z - 1.0);            /* c7 y (5 z^2 - 1) */
+    dY[3 * 11 + 2] = 10.0 * c7 * y * z;
+    dY[3 * 12 + 2] = c8 * (15.0 * z * z - 3.0);           /* c8 z (5 z^2 - 3) */
+    dY[3 * 13 + 0] = c7 * (5.0 * z * z - 1.0);            /* c7 x (5 z^2 - 1) */
+    dY[3 * 13 + 2] = 10.0 * c7 * x * z;
+    dY[3 * 14 + 0] = 2.0 * c9 * x * z;                    /* c9 z (x^2 - y^2) */
+    dY[3 * 14 + 1] = -2.0 * c9 * y * z;
+    dY[3 * 14 + 2] = c9 * (x * x - y * y);
+    dY[3 * 15 + 0] = c5 * (3.0 * x * x - 3.0 * y * y);    /* c5 x (x^2 - 3 y^2) */
+    dY[3 * 15 + 1] = -6.0 * c5 * x * y;
+}
+
 /* Rotation matrix (row-major) of the unit quaternion (w, x, y, z). */
 static void quat_to_matrix(const double q[4], double M[9])
 {
@@ -107,6 +158,150 @@ static double frac_dist(double v)
 }
 
 /*
+ * Projection of one Gaussian into one view, in double precision.
+ *   mu[3], ls[3] (log-scales), q[4] (w,x,y,z, any norm), logit, shc[k*3 + ch] (k < (deg+1)^2).
+ * Outputs (index i of the per-Gaussian arrays): see orc_project.  Returns visibility.
+ */
+static int project_one(const double mu[3], const double ls[3], const double q_in[4], double logit,
+                       const double* shc, const orc_camera* cam, const orc_params* p, int64_t i,
+                       double* mean2d, double* cov2d, double* conic, double* opacity, double* color,
+                       double* depth, int32_t* rect, int32_t* n_tiles, int8_t* flag)
+{
+    const int deg = p->sh_degree;
+    const int nk = (deg + 1) * (deg + 1);
+    flag[i] = 0;
+    n_tiles[i] = 0;
+    rect[4 * i + 0] = rect[4 * i + 1] = rect[4 * i + 2] = rect[4 * i + 3] = 0;
+    mean2d[2 * i] = mean2d[2 * i + 1] = 0.0;
+    cov2d[3 * i] = cov2d[3 * i + 1] = cov2d[3 * i + 2] = 0.0;
+    conic[3 * i] = conic[3 * i + 1] = conic[3 * i + 2] = 0.0;
+    opacity[i] = 0.0;
+    color[3 * i] = color[3 * i + 1] = color[3 * i + 2] = 0.0;
+    depth[i] = 0.0;
+
+    double q[4];
+    int finite = isfinite(logit);
+    for (int k = 0; k < 3; k++) finite = finite && isfinite(mu[k]) && isfinite(ls[k]);
+    for (int k = 0; k < 4; k++) finite = finite && isfinite(q_in[k]);
+    if (!finite) return 0;
+
+    /* 1. activations */
+    const double o = 1.0 / (1.0 + exp(-logit));
+    double s[3];
+    for (int k = 0; k < 3; k++) s[k] = exp(ls[k]);
+    const double qn = sqrt(q_in[0] * q_in[0] + q_in[1] * q_in[1] + q_in[2] * q_in[2] + q_in[3] * q_in[3]);
+    if (!(qn > 0.0)) return 0;
+    for (int k = 0; k < 4; k++) q[k] = q_in[k] / qn;
+
+    /* 2. world -> camera, near cull */
+    double tc[3];
+    for (int r = 0; r < 3; r++)
+        tc[r] = cam->R[3 * r + 0] * mu[0] + cam->R[3 * r + 1] * mu[1] + cam->R[3 * r + 2] * mu[2] + cam->t[r];
+    if (fabs(tc[2] - p->znear) <= 1e-5 * fmax(1.0, fabs(tc[2]))) flag[i] = 1;
+    if (!(tc[2] > p->znear)) return 0;
+
+    /* 3. world covariance Sigma = Rq diag(s^2) Rq^T */
+    double Rq[9], Sig[9];
+    quat_to_matrix(q, Rq);
+    for (int a = 0; a < 3; a++)
+        for (int b = 0; b < 3; b++) {
+            double acc = 0.0;
+            for (int k = 0; k < 3; k++) acc += Rq[3 * a + k] * s[k] * s[k] * Rq[3 * b + k];
+            Sig[3 * a + b] = acc;
+        }
+
+    /* 4. EWA: Sigma2D = J W Sigma W^T J^T, plus the low-pass dilation */
+    const double tz = tc[2];
+    double J[6] = {cam->fx / tz, 0.0, -cam->fx * tc[0] / (tz * tz),
+                   0.0, cam->fy / tz, -cam->fy * tc[1] / (tz * tz)};
+    double T[6]; /* T = J W, 2x3 */
+    for (int r = 0; r < 2; r++)
+        for (int c = 0; c < 3; c++) {
+            double acc = 0.0;
+            for (int k = 0; k < 3; k++) acc += J[3 * r + k] * cam->R[3 * k + c];
+            T[3 * r + c] = acc;
+        }
+    double S2[4]; /* T Sigma T^T, 2x2 */
+    for (int r = 0; r < 2; r++)
+        for (int c = 0; c < 2; c++) {
+            double acc = 0.0;
+            for (int a = 0; a < 3; a++)
+                for (int b = 0; b < 3; b++) acc += T[3 * r + a] * Sig[3 * a + b] * T[3 * c + b];
+            S2[2 * r + c] = acc;
+        }
+    const double a = S2[0] + p->eps2d;
+    const double b = S2[1];
+    const double c = S2[3] + p->eps2d;
+    const double det = a * c - b * b;
+    if (!(det > 0.0) || !isfinite(det)) return 0;
+    const double A = c / det, B = -b / det, C = a / det;
+
+    /* 5. projected centre, pixel (u, v) has its centre at (u + 1/2, v + 1/2) */
+    const double mx = cam->fx * tc[0] / tz + cam->cx;
+    const double my = cam->fy * tc[1] / tz + cam->cy;
+
+    /* 7. opacity-aware box: all pixels with o * exp(-q/2) >= alpha_min */
+    if (fabs(255.0 * o - 1.0) <= 1e-5) flag[i] = 1;
+    if (!(o * (1.0 / p->alpha_min) > 1.0)) return 0;
+    const double Q = 2.0 * log(o / p->alpha_min);
+    const double ex = 1.001 * sqrt(Q * a);
+    const double ey = 1.001 * sqrt(Q * c);
+    const double lo_x = mx - ex - 0.5, hi_x = mx + ex - 0.5;
+    const double lo_y = my - ey - 0.5, hi_y = my + ey - 0.5;
+    if (!(isfinite(lo_x) && isfinite(hi_x) && isfinite(lo_y) && isfinite(hi_y))) return 0;
+    const double mx_margin = 1e-3 + 4e-6 * (fabs(mx) + ex);
+    const double my_margin = 1e-3 + 4e-6 * (fabs(my) + ey);
+    if (frac_dist(lo_x) < mx_margin || frac_dist(hi_x) < mx_margin ||
+        frac_dist(lo_y) < my_margin || frac_dist(hi_y) < my_margin)
+        flag[i] = 1;
+    const double u0 = fmax(0.0, ceil(lo_x));
+    const double u1 = fmin((double)(cam->width - 1), floor(hi_x));
+    const double v0 = fmax(0.0, ceil(lo_y));
+    const double v1 = fmin((double)(cam->height - 1), floor(hi_y));
+    if (!(u0 <= u1) || !(v0 <= v1)) return 0;
+
+    /* 6. colour from spherical harmonics along the viewing direction; DC taken as the
+     *    base colour, lower clamp at zero */
+    double dir[3] = {mu[0] - cam->campos[0], mu[1] - cam->campos[1], mu[2] - cam->campos[2]};
+    const double dn = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
+    if (!(dn > 0.0)) return 0;
+    for (int k = 0; k < 3; k++) dir[k] /= dn;
+    double Y[16];
+    orc_sh_basis(deg, dir, Y);
+    double col[3];
+    int col_ok = 1;
+    for (int ch = 0; ch < 3; ch++) {
+        double v = shc[0 * 3 + ch];
+        for (int k = 1; k < nk; k++) v += shc[k * 3 + ch] * Y[k];
+        if (!isfinite(v)) col_ok = 0;
+        col[ch] = v > 0.0 ? v : 0.0;
+    }
+    if (!col_ok) return 0;
+
+    /* 8. outputs */
+    const int tile = p->tile;
+    const int tx0 = (int)u0 / tile, tx1 = (int)u1 / tile;
+    const int ty0 = (int)v0 / tile, ty1 = (int)v1 / tile;
+    mean2d[2 * i] = mx;
+    mean2d[2 * i + 1] = my;
+    cov2d[3 * i] = a;
+    cov2d[3 * i + 1] = b;
+    cov2d[3 * i + 2] = c;
+    conic[3 * i] = A;
+    conic[3 * i + 1] = B;
+    conic[3 * i + 2] = C;
+    opacity[i] = o;
+    for (int ch = 0; ch < 3; ch++) color[3 * i + ch] = col[ch];
+    depth[i] = tz;
+    rect[4 * i + 0] = tx0;
+    rect[4 * i + 1] = ty0;
+    rect[4 * i + 2] = tx1;
+    rect[4 * i + 3] = ty1;
+    n_tiles[i] = (tx1 - tx0 + 1) * (ty1 - ty0 + 1);
+    return 1;
+}
+
+/*
  * Projection of every Gaussian into one view (no compaction; the caller compacts).
  *
  * Inputs are the float32 parameter arrays in structure-of-arrays layout:
@@ -125,47 +320,75 @@ void orc_project(int64_t n, const float* means, const float* log_scales, const f
                  double* conic, double* opacity, double* color, double* depth, int32_t* rect,
                  int32_t* n_tiles, int8_t* flag)
 {
-    const int deg = p->sh_degree;
-    const int nk = (deg + 1) * (deg + 1);
+    const int nk = (p->sh_degree + 1) * (p->sh_degree + 1);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++) {
-        visible[i] = 0;
-        flag[i] = 0;
-        n_tiles[i] = 0;
-        rect[4 * i + 0] = rect[4 * i + 1] = rect[4 * i + 2] = rect[4 * i + 3] = 0;
-        mean2d[2 * i] = mean2d[2 * i + 1] = 0.0;
-        cov2d[3 * i] = cov2d[3 * i + 1] = cov2d[3 * i + 2] = 0.0;
-        conic[3 * i] = conic[3 * i + 1] = conic[3 * i + 2] = 0.0;
-        opacity[i] = 0.0;
-        color[3 * i] = color[3 * i + 1] = color[3 * i + 2] = 0.0;
-        depth[i] = 0.0;
-
-        double mu[3], ls[3], q[4];
+        double mu[3], ls[3], q[4], shc[48];
         for (int k = 0; k < 3; k++) mu[k] = means[k * n + i];
         for (int k = 0; k < 3; k++) ls[k] = log_scales[k * n + i];
         for (int k = 0; k < 4; k++) q[k] = quats[k * n + i];
-        const double logit = opacity_logits[i];
-        int finite = isfinite(logit);
-        for (int k = 0; k < 3; k++) finite = finite && isfinite(mu[k]) && isfinite(ls[k]);
-        for (int k = 0; k < 4; k++) finite = finite && isfinite(q[k]);
-        if (!finite) continue;
+        for (int k = 0; k < 3 * nk; k++) shc[k] = sh[k * n + i];
+        visible[i] = (int8_t)project_one(mu, ls, q, opacity_logits[i], shc, cam, p, i, mean2d, cov2d, conic,
+                                         opacity, color, depth, rect, n_tiles, flag);
+    }
+}
 
-        /* 1. activations */
-        const double o = 1.0 / (1.0 + exp(-logit));
-        double s[3];
-        for (int k = 0; k < 3; k++) s[k] = exp(ls[k]);
-        const double qn = sqrt(q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3]);
-        if (!(qn > 0.0)) continue;
-        for (int k = 0; k < 4; k++) q[k] /= qn;
+/* The same projection with double-precision parameters (used to differentiate it numerically). */
+void orc_project_f64(int64_t n, const double* means, const double* log_scales, const double* quats,
+                     const double* opacity_logits, const double* sh, const orc_camera* cam,
+                     const orc_params* p, int8_t* visible, double* mean2d, double* cov2d,
+                     double* conic, double* opacity, double* color, double* depth, int32_t* rect,
+                     int32_t* n_tiles, int8_t* flag)
+{
+    const int nk = (p->sh_degree + 1) * (p->sh_degree + 1);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        double mu[3], ls[3], q[4], shc[48];
+        for (int k = 0; k < 3; k++) mu[k] = means[k * n + i];
+        for (int k = 0; k < 3; k++) ls[k] = log_scales[k * n + i];
+        for (int k = 0; k < 4; k++) q[k] = quats[k * n + i];
+        for (int k = 0; k < 3 * nk; k++) shc[k] = sh[k * n + i];
+        visible[i] = (int8_t)project_one(mu, ls, q, opacity_logits[i], shc, cam, p, i, mean2d, cov2d, conic,
+                                         opacity, color, depth, rect, n_tiles, flag);
+    }
+}
 
-        /* 2. world -> camera, near cull */
+/*
+ * Backward of the projection for one view (the chain rule of orc_project, step by step in
+ * reverse).  Given dL/dmean2d (n,2), dL/dconic (n,3: A, B, C), dL/dopacity (n) and dL/dcolour
+ * (n,3) of the Gaussians with visible[i] = 1 (indexed by Gaussian), it ADDS this view's share
+ * of dL/dmeans[3][n], dL/dlog_scales[3][n], dL/dquats[4][n] (with respect to the raw,
+ * unnormalised quaternion), dL/dopacity_logits[n] and dL/dsh[3(deg+1)^2][n]; the caller sums
+ * views by calling once per view.  The conic, box and culling decisions are taken as fixed
+ * (they are piecewise constant).  flag[i] is set when a colour channel's value before the
+ * clamp at zero is so close to zero that float32 evaluation may take the clamp the other way.
+ */
+void orc_project_backward(int64_t n, const double* means, const double* log_scales, const double* quats,
+                          const double* opacity_logits, const double* sh, const orc_camera* cam,
+                          const orc_params* p, const int8_t* visible, const double* g_mean2d,
+                          const double* g_conic, const double* g_opacity, const double* g_color,
+                          double* d_means, double* d_log_scales, double* d_quats, double* d_logits,
+                          double* d_sh, int8_t* flag)
+{
+    const int deg = p->sh_degree;
+    const int nk = (deg + 1) * (deg + 1);
+    const double* W = cam->R;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        if (!visible[i]) continue;
+        double mu[3], s[3], qr[4], q[4];
+        for (int k = 0; k < 3; k++) mu[k] = means[k * n + i];
+        for (int k = 0; k < 3; k++) s[k] = exp(log_scales[k * n + i]);
+        for (int k = 0; k < 4; k++) qr[k] = quats[k * n + i];
+        const double o = 1.0 / (1.0 + exp(-opacity_logits[i]));
+        const double qn = sqrt(qr[0] * qr[0] + qr[1] * qr[1] + qr[2] * qr[2] + qr[3] * qr[3]);
+        for (int k = 0; k < 4; k++) q[k] = qr[k] / qn;
+
+        /* forward quantities */
         double tc[3];
-        for (int r = 0; r < 3; r++)
-            tc[r] = cam->R[3 * r + 0] * mu[0] + cam->R[3 * r + 1] * mu[1] + cam->R[3 * r + 2] * mu[2] + cam->t[r];
-        if (fabs(tc[2] - p->znear) <= 1e-5 * fmax(1.0, fabs(tc[2]))) flag[i] = 1;
-        if (!(tc[2] > p->znear)) continue;
-
-        /* 3. world covariance Sigma = Rq diag(s^2) Rq^T */
+        for (int r = 0; r < 3; r++) tc[r] = W[3 * r] * mu[0] + W[3 * r + 1] * mu[1] + W[3 * r + 2] * mu[2] + cam->t[r];
+        const double tx = tc[0], ty = tc[1], tz = tc[2];
+        const double fx = cam->fx, fy = cam->fy;
         double Rq[9], Sig[9];
         quat_to_matrix(q, Rq);
         for (int a = 0; a < 3; a++)
@@ -174,19 +397,15 @@ void orc_project(int64_t n, const float* means, const float* log_scales, const f
                 for (int k = 0; k < 3; k++) acc += Rq[3 * a + k] * s[k] * s[k] * Rq[3 * b + k];
                 Sig[3 * a + b] = acc;
             }
-
-        /* 4. EWA: Sigma2D = J W Sigma W^T J^T, plus the low-pass dilation */
-        const double tz = tc[2];
-        double J[6] = {cam->fx / tz, 0.0, -cam->fx * tc[0] / (tz * tz),
-                       0.0, cam->fy / tz, -cam->fy * tc[1] / (tz * tz)};
-        double T[6]; /* T = J W, 2x3 */
+        const double J[6] = {fx / tz, 0.0, -fx * tx / (tz * tz), 0.0, fy / tz, -fy * ty / (tz * tz)};
+        double T[6];
         for (int r = 0; r < 2; r++)
             for (int c = 0; c < 3; c++) {
                 double acc = 0.0;
-                for (int k = 0; k < 3; k++) acc += J[3 * r + k] * cam->R[3 * k + c];
+                for (int k = 0; k < 3; k++) acc += J[3 * r + k] * W[3 * k + c];
                 T[3 * r + c] = acc;
             }
-        double S2[4]; /* T Sigma T^T, 2x2 */
+        double S2[4];
         for (int r = 0; r < 2; r++)
             for (int c = 0; c < 2; c++) {
                 double acc = 0.0;
@@ -194,76 +413,116 @@ void orc_project(int64_t n, const float* means, const float* log_scales, const f
                     for (int b = 0; b < 3; b++) acc += T[3 * r + a] * Sig[3 * a + b] * T[3 * c + b];
                 S2[2 * r + c] = acc;
             }
-        const double a = S2[0] + p->eps2d;
-        const double b = S2[1];
-        const double c = S2[3] + p->eps2d;
-        const double det = a * c - b * b;
-        if (!(det > 0.0) || !isfinite(det)) continue;
-        const double A = c / det, B = -b / det, C = a / det;
+        const double a = S2[0] + p->eps2d, b = S2[1], c = S2[3] + p->eps2d;
+        const double det = a * c - b * b, det2 = det * det;
 
-        /* 5. projected centre, pixel (u, v) has its centre at (u + 1/2, v + 1/2) */
-        const double mx = cam->fx * tc[0] / tz + cam->cx;
-        const double my = cam->fy * tc[1] / tz + cam->cy;
+        /* conic (A, B, C) = (c, -b, a) / det  ->  dilated covariance (a, b, c); the dilation
+         * is a constant, so these are also the gradients of Sigma2D's xx, xy, yy entries */
+        const double gA = g_conic[3 * i], gB = g_conic[3 * i + 1], gC = g_conic[3 * i + 2];
+        const double ga = (-c * c * gA + b * c * gB - b * b * gC) / det2;
+        const double gb = (2.0 * b * c * gA - (det + 2.0 * b * b) * gB + 2.0 * a * b * gC) / det2;
+        const double gc = (-b * b * gA + a * b * gB - a * a * gC) / det2;
 
-        /* 7. opacity-aware box: all pixels with o * exp(-q/2) >= alpha_min */
-        if (fabs(255.0 * o - 1.0) <= 1e-5) flag[i] = 1;
-        if (!(o * (1.0 / p->alpha_min) > 1.0)) continue;
-        const double Q = 2.0 * log(o / p->alpha_min);
-        const double ex = 1.001 * sqrt(Q * a);
-        const double ey = 1.001 * sqrt(Q * c);
-        const double lo_x = mx - ex - 0.5, hi_x = mx + ex - 0.5;
-        const double lo_y = my - ey - 0.5, hi_y = my + ey - 0.5;
-        if (!(isfinite(lo_x) && isfinite(hi_x) && isfinite(lo_y) && isfinite(hi_y))) continue;
-        const double mx_margin = 1e-3 + 4e-6 * (fabs(mx) + ex);
-        const double my_margin = 1e-3 + 4e-6 * (fabs(my) + ey);
-        if (frac_dist(lo_x) < mx_margin || frac_dist(hi_x) < mx_margin ||
-            frac_dist(lo_y) < my_margin || frac_dist(hi_y) < my_margin)
-            flag[i] = 1;
-        const double u0 = fmax(0.0, ceil(lo_x));
-        const double u1 = fmin((double)(cam->width - 1), floor(hi_x));
-        const double v0 = fmax(0.0, ceil(lo_y));
-        const double v1 = fmin((double)(cam->height - 1), floor(hi_y));
-        if (!(u0 <= u1) || !(v0 <= v1)) continue;
-
-        /* 6. colour from spherical harmonics along the viewing direction; DC taken as the
-         *    base colour, lower clamp at zero */
-        double dir[3] = {mu[0] - cam->campos[0], mu[1] - cam->campos[1], mu[2] - cam->campos[2]};
-        const double dn = sqrt(dir[0] * dir[0] + dir[1] * dir[1] + dir[2] * dir[2]);
-        if (!(dn > 0.0)) continue;
-        for (int k = 0; k < 3; k++) dir[k] /= dn;
-        double Y[16];
-        orc_sh_basis(deg, dir, Y);
-        double col[3];
-        int col_ok = 1;
-        for (int ch = 0; ch < 3; ch++) {
-            double v = sh[(0 * 3 + ch) * n + i];
-            for (int k = 1; k < nk; k++) v += sh[(k * 3 + ch) * n + i] * Y[k];
-            if (!isfinite(v)) col_ok = 0;
-            col[ch] = v > 0.0 ? v : 0.0;
+        /* Sigma2D = T Sigma T^T with xx = T0 Sig T0^T, xy = T0 Sig T1^T, yy = T1 Sig T1^T (rows
+         * T0, T1 of T): gradients of T and of the nine entries of Sigma */
+        double gT[6], gSig[9];
+        for (int k = 0; k < 3; k++) {
+            double st0 = 0.0, st1 = 0.0; /* (Sig T0^T)_k, (Sig T1^T)_k */
+            for (int m = 0; m < 3; m++) {
+                st0 += Sig[3 * k + m] * T[m];
+                st1 += Sig[3 * k + m] * T[3 + m];
+            }
+            gT[k] = 2.0 * ga * st0 + gb * st1;
+            gT[3 + k] = gb * st0 + 2.0 * gc * st1;
         }
-        if (!col_ok) continue;
+        for (int u = 0; u < 3; u++)
+            for (int v = 0; v < 3; v++)
+                gSig[3 * u + v] = ga * T[u] * T[v] + gb * T[u] * T[3 + v] + gc * T[3 + u] * T[3 + v];
 
-        /* 8. outputs */
-        const int tile = p->tile;
-        const int tx0 = (int)u0 / tile, tx1 = (int)u1 / tile;
-        const int ty0 = (int)v0 / tile, ty1 = (int)v1 / tile;
-        visible[i] = 1;
-        mean2d[2 * i] = mx;
-        mean2d[2 * i + 1] = my;
-        cov2d[3 * i] = a;
-        cov2d[3 * i + 1] = b;
-        cov2d[3 * i + 2] = c;
-        conic[3 * i] = A;
-        conic[3 * i + 1] = B;
-        conic[3 * i + 2] = C;
-        opacity[i] = o;
-        for (int ch = 0; ch < 3; ch++) color[3 * i + ch] = col[ch];
-        depth[i] = tz;
-        rect[4 * i + 0] = tx0;
-        rect[4 * i + 1] = ty0;
-        rect[4 * i + 2] = tx1;
-        rect[4 * i + 3] = ty1;
-        n_tiles[i] = (tx1 - tx0 + 1) * (ty1 - ty0 + 1);
+        /* T = J W  ->  J;  J(t) and the projected centre  ->  camera-space t */
+        double gJ[6];
+        for (int r = 0; r < 2; r++)
+            for (int k = 0; k < 3; k++) {
+                double acc = 0.0;
+                for (int col = 0; col < 3; col++) acc += gT[3 * r + col] * W[3 * k + col];
+                gJ[3 * r + k] = acc;
+            }
+        const double gmx = g_mean2d[2 * i], gmy = g_mean2d[2 * i + 1];
+        double gt[3];
+        gt[0] = gmx * fx / tz + gJ[2] * (-fx / (tz * tz));
+        gt[1] = gmy * fy / tz + gJ[5] * (-fy / (tz * tz));
+        gt[2] = -gmx * fx * tx / (tz * tz) - gmy * fy * ty / (tz * tz) + gJ[0] * (-fx / (tz * tz)) +
+                gJ[2] * (2.0 * fx * tx / (tz * tz * tz)) + gJ[4] * (-fy / (tz * tz)) +
+                gJ[5] * (2.0 * fy * ty / (tz * tz * tz));
+
+        /* t = W mu + t_cam  ->  mu */
+        double gmu[3];
+        for (int k = 0; k < 3; k++) gmu[k] = W[k] * gt[0] + W[3 + k] * gt[1] + W[6 + k] * gt[2];
+
+        /* Sigma = sum_k s_k^2 Rq[:,k] Rq[:,k]^T  ->  scales (then log-scales) and Rq */
+        double gRq[9];
+        for (int k = 0; k < 3; k++) {
+            double gs = 0.0;
+            for (int u = 0; u < 3; u++)
+                for (int v = 0; v < 3; v++) gs += gSig[3 * u + v] * 2.0 * s[k] * Rq[3 * u + k] * Rq[3 * v + k];
+            d_log_scales[k * n + i] += gs * s[k];
+        }
+        for (int u = 0; u < 3; u++)
+            for (int k = 0; k < 3; k++) {
+                double acc = 0.0;
+                for (int v = 0; v < 3; v++) acc += (gSig[3 * u + v] + gSig[3 * v + u]) * Rq[3 * v + k];
+                gRq[3 * u + k] = acc * s[k] * s[k];
+            }
+
+        /* Rq(q) of the unit quaternion (w, x, y, z), entry by entry */
+        const double w = q[0], x = q[1], y = q[2], z = q[3];
+        double gq[4] = {0.0, 0.0, 0.0, 0.0};
+        gq[2] += gRq[0] * (-4.0 * y);
+        gq[3] += gRq[0] * (-4.0 * z);
+        gq[0] += gRq[1] * (-2.0 * z); gq[1] += gRq[1] * (2.0 * y); gq[2] += gRq[1] * (2.0 * x); gq[3] += gRq[1] * (-2.0 * w);
+        gq[0] += gRq[2] * (2.0 * y);  gq[1] += gRq[2] * (2.0 * z); gq[2] += gRq[2] * (2.0 * w); gq[3] += gRq[2] * (2.0 * x);
+        gq[0] += gRq[3] * (2.0 * z);  gq[1] += gRq[3] * (2.0 * y); gq[2] += gRq[3] * (2.0 * x); gq[3] += gRq[3] * (2.0 * w);
+        gq[1] += gRq[4] * (-4.0 * x);
+        gq[3] += gRq[4] * (-4.0 * z);
+        gq[0] += gRq[5] * (-2.0 * x); gq[1] += gRq[5] * (-2.0 * w); gq[2] += gRq[5] * (2.0 * z); gq[3] += gRq[5] * (2.0 * y);
+        gq[0] += gRq[6] * (-2.0 * y); gq[1] += gRq[6] * (2.0 * z); gq[2] += gRq[6] * (-2.0 * w); gq[3] += gRq[6] * (2.0 * x);
+        gq[0] += gRq[7] * (2.0 * x);  gq[1] += gRq[7] * (2.0 * w); gq[2] += gRq[7] * (2.0 * z); gq[3] += gRq[7] * (2.0 * y);
+        gq[1] += gRq[8] * (-4.0 * x);
+        gq[2] += gRq[8] * (-4.0 * y);
+        /* normalisation q = qr / |qr|: remove the radial part, divide by |qr| */
+        const double qdot = gq[0] * q[0] + gq[1] * q[1] + gq[2] * q[2] + gq[3] * q[3];
+        for (int k = 0; k < 4; k++) d_quats[k * n + i] += (gq[k] - q[k] * qdot) / qn;
+
+        /* opacity = sigmoid(logit) */
+        d_logits[i] += g_opacity[i] * o * (1.0 - o);
+
+        /* colour = max(0, k0 + sum_k sh_k Y_k(dir)), dir = unit(mu - campos) */
+        double dv[3] = {mu[0] - cam->campos[0], mu[1] - cam->campos[1], mu[2] - cam->campos[2]};
+        const double dn = sqrt(dv[0] * dv[0] + dv[1] * dv[1] + dv[2] * dv[2]);
+        double dir[3] = {dv[0] / dn, dv[1] / dn, dv[2] / dn};
+        double Y[16], dY[48];
+        orc_sh_basis(deg, dir, Y);
+        orc_sh_basis_grad(deg, dir, dY);
+        double gdir[3] = {0.0, 0.0, 0.0};
+        for (int ch = 0; ch < 3; ch++) {
+            const double* shc = sh + (size_t)ch * n + i; /* row k*3 + ch at shc[k * 3 * n] */
+            double v = shc[0], mag = fabs(shc[0]);
+            for (int k = 1; k < nk; k++) {
+                v += shc[(size_t)k * 3 * n] * Y[k];
+                mag += fabs(shc[(size_t)k * 3 * n] * Y[k]);
+            }
+            if (fabs(v) <= 1e-5 * mag) flag[i] = 1;
+            if (!(v > 0.0)) continue;
+            const double g = g_color[3 * i + ch];
+            d_sh[(size_t)ch * n + i] += g;
+            for (int k = 1; k < nk; k++) {
+                d_sh[(size_t)(k * 3 + ch) * n + i] += g * Y[k];
+                for (int m = 0; m < 3; m++) gdir[m] += g * shc[(size_t)k * 3 * n] * dY[3 * k + m];
+            }
+        }
+        const double gdot = gdir[0] * dir[0] + gdir[1] * dir[1] + gdir[2] * dir[2];
+        for (int m = 0; m < 3; m++) gmu[m] += (gdir[m] - dir[m] * gdot) / dn;
+        for (int k = 0; k < 3; k++) d_means[k * n + i] += gmu[k];
     }
 }
 
