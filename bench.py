@@ -161,6 +161,33 @@ def main():
     log(f"[bench] fused: {ms_fused:.3f} ms/iter (raster call {raster_fused_ms:.3f} ms); "
         f"separate: {ms_sep:.3f} ms/iter (raster calls {raster_sep_ms:.3f} ms)")
 
+    # the projection backward (2D gradients of all views -> parameter gradients), one kernel,
+    # timed on its own and inside a full training iteration
+    r.project_backward()
+    torch.cuda.synchronize()
+    pb_steps = max(5, args.steps // 2)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(pb_steps)]
+    for a, b in ev:
+        a.record()
+        r.project_backward()
+        b.record()
+    torch.cuda.synchronize()
+    pb_ms = sum(a.elapsed_time(b) for a, b in ev) / pb_steps
+    for _ in range(2):
+        r.iteration(mode="fused", project_bwd=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(pb_steps):
+        r.iteration(mode="fused", project_bwd=True)
+    torch.cuda.synchronize()
+    full_ms = (time.perf_counter() - t0) * 1000.0 / pb_steps
+    nk = (scene.sh_degree + 1) ** 2
+    # algorithmic bytes: parameters read once and gradients written once per Gaussian
+    # (4 (10 + 3 nk) B each way), vis_ids (4 B) per visible slot and the 36 B of 2D gradients
+    # per visible slot
+    pb_bytes = 2 * 4 * (10 + 3 * nk) * scene.n + (4 + 36) * sum(vis)
+    log(f"[bench] projection backward: {pb_ms:.3f} ms; full iteration with it: {full_ms:.3f} ms")
+
     flops = FLOPS_PER_BOX_PAIR * E_box + FLOPS_PER_BLEND * B
     achieved = flops / (raster_fused_ms * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -201,6 +228,17 @@ def main():
         "stages_ms": {"fused": stages_fused, "separate": stages_sep},
         "separate_path": {"ms_per_step": ms_sep, "blends_per_s": B / (ms_sep * 1e-3), "raster_ms": raster_sep_ms},
         "cpu_baseline": None,
+        "project_bwd": {
+            "kernel": "project_bwd_kernel (gs_project_bwd)",
+            "ms": pb_ms,
+            "bound": "hbm",
+            "algorithmic_bytes": pb_bytes,
+            "achieved": pb_bytes / (pb_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": pb_bytes / (pb_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "full_iteration_ms": full_ms,
+        },
     }
     # algorithmic HBM bytes of the call, per instance: its record and slot id (40 B) and the inputs
     # of its emission index (12 B) read once, its 9-float partial record cleared, written and read

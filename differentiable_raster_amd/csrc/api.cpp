@@ -292,6 +292,50 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     return hip_check(launch_project(a, static_cast<hipStream_t>(stream)), "gs_project launch");
 }
 
+gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
+                         const gs_projected* proj, const gs_grads2d* grads2d, gs_grads3d* out, void* stream) {
+    g_last_error.clear();
+    if (!g) return fail(GS_ERR_INVALID_ARGUMENT, "gaussians is null");
+    gs_status st = check_cams(cams, V);
+    if (st != GS_OK) return st;
+    if ((st = check_params(p)) != GS_OK) return st;
+    if (g->n < 0 || g->n >= (1 << 28)) return fail(GS_ERR_INVALID_ARGUMENT, "n=%d outside [0, 2^28)", g->n);
+    if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
+        return fail(GS_ERR_INVALID_ARGUMENT, "a parameter array is null");
+    if (!proj || !proj->vis_count || !proj->vis_ids)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected vis_count / vis_ids are null");
+    if (proj->capacity < g->n) return fail(GS_ERR_INVALID_ARGUMENT, "capacity %d < n %d", proj->capacity, g->n);
+    if ((int64_t)proj->capacity * V >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARGUMENT, "capacity * V must stay below 2^31");
+    if (!grads2d || !grads2d->d_mean2d || !grads2d->d_conic || !grads2d->d_opacity || !grads2d->d_color)
+        return fail(GS_ERR_INVALID_ARGUMENT, "2D gradients are null");
+    if (!out || !out->d_means || !out->d_log_scales || !out->d_quats || !out->d_opacity_logits || !out->d_sh)
+        return fail(GS_ERR_INVALID_ARGUMENT, "parameter gradient outputs are null");
+    ProjectBwdArgs a;
+    a.n = g->n;
+    a.V = V;
+    a.capacity = proj->capacity;
+    a.means = g->means;
+    a.log_scales = g->log_scales;
+    a.quats = g->quats;
+    a.logits = g->opacity_logits;
+    a.sh = g->sh;
+    a.cams = to_dev(cams, V);
+    a.p = to_dev(p);
+    a.vis_count = proj->vis_count;
+    a.vis_ids = proj->vis_ids;
+    a.d_mean2d = reinterpret_cast<const float2*>(grads2d->d_mean2d);
+    a.d_conic = grads2d->d_conic;
+    a.d_opacity = grads2d->d_opacity;
+    a.d_color = grads2d->d_color;
+    a.g_means = out->d_means;
+    a.g_log_scales = out->d_log_scales;
+    a.g_quats = out->d_quats;
+    a.g_logits = out->d_opacity_logits;
+    a.g_sh = out->d_sh;
+    return hip_check(launch_project_bwd(a, static_cast<hipStream_t>(stream)), "gs_project_bwd launch");
+}
+
 size_t gs_raster_workspace_size(int64_t instance_capacity) {
     if (instance_capacity < 0) return 0;
     return align256(sizeof(float) * 9 * (size_t)instance_capacity);

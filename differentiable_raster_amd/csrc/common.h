@@ -83,6 +83,23 @@ struct ProjectArgs {
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 size_t project_ws_bytes(int32_t n, int32_t V);
 
+// Backward of the projection: per-slot 2D gradients of V views -> per-Gaussian parameter
+// gradients (summed over views), one thread per Gaussian.
+struct ProjectBwdArgs {
+    int32_t n, V, capacity;
+    const float *means, *log_scales, *quats, *logits, *sh;
+    CamArray cams;
+    ParamsDev p;
+    const int32_t* vis_count;
+    const int32_t* vis_ids;
+    const float2* d_mean2d;
+    const float* d_conic;
+    const float* d_opacity;
+    const float* d_color;
+    float *g_means, *g_log_scales, *g_quats, *g_logits, *g_sh;
+};
+hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
+
 // Exclusive scan of `rows` independent int32 rows of length n (row r at in + r*n):
 // out[r][i] = sum_{k<i} in[r][k]; totals[r] = sum of row r (totals may be null).
 hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, int32_t n, int32_t rows,

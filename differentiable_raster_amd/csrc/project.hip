@@ -11,6 +11,7 @@
 // Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read only for
 // Gaussians that pass every geometric test in a view; later views hit the cache.
 #include "common.h"
+#include "gauss.h"
 
 namespace gsmi {
 namespace {
@@ -41,81 +42,21 @@ __device__ Geo load_geo(const ProjectArgs& a, int i) {
     g.mx = a.means[i];
     g.my = a.means[n + i];
     g.mz = a.means[2 * n + i];
-    const float l0 = a.log_scales[i], l1 = a.log_scales[n + i], l2 = a.log_scales[2 * n + i];
-    float qw = a.quats[i], qx = a.quats[n + i], qy = a.quats[2 * n + i], qz = a.quats[3 * n + i];
-    const float logit = a.logits[i];
-    g.ok = finitef(g.mx) && finitef(g.my) && finitef(g.mz) && finitef(l0) && finitef(l1) && finitef(l2) &&
-           finitef(qw) && finitef(qx) && finitef(qy) && finitef(qz) && finitef(logit);
-    // activations: sigmoid opacity, exponential scales, normalized quaternion
-    g.o = 1.0f / (1.0f + expf(-logit));
-    const float s0 = expf(l0), s1 = expf(l1), s2 = expf(l2);
-    const float qn = sqrtf(qw * qw + qx * qx + qy * qy + qz * qz);
-    g.ok = g.ok && qn > 0.0f;
-    const float inv = 1.0f / qn;
-    qw *= inv;
-    qx *= inv;
-    qy *= inv;
-    qz *= inv;
-    // rotation matrix of (w, x, y, z), columns scaled by s: M = R diag(s); Sigma = M M^T
-    const float r00 = 1.0f - 2.0f * (qy * qy + qz * qz), r01 = 2.0f * (qx * qy - qw * qz), r02 = 2.0f * (qx * qz + qw * qy);
-    const float r10 = 2.0f * (qx * qy + qw * qz), r11 = 1.0f - 2.0f * (qx * qx + qz * qz), r12 = 2.0f * (qy * qz - qw * qx);
-    const float r20 = 2.0f * (qx * qz - qw * qy), r21 = 2.0f * (qy * qz + qw * qx), r22 = 1.0f - 2.0f * (qx * qx + qy * qy);
-    const float m00 = r00 * s0, m01 = r01 * s1, m02 = r02 * s2;
-    const float m10 = r10 * s0, m11 = r11 * s1, m12 = r12 * s2;
-    const float m20 = r20 * s0, m21 = r21 * s1, m22 = r22 * s2;
-    g.S[0] = fmaf(m00, m00, fmaf(m01, m01, m02 * m02));
-    g.S[1] = fmaf(m00, m10, fmaf(m01, m11, m02 * m12));
-    g.S[2] = fmaf(m00, m20, fmaf(m01, m21, m02 * m22));
-    g.S[3] = fmaf(m10, m10, fmaf(m11, m11, m12 * m12));
-    g.S[4] = fmaf(m10, m20, fmaf(m11, m21, m12 * m22));
-    g.S[5] = fmaf(m20, m20, fmaf(m21, m21, m22 * m22));
+    const GaussFrame f = gauss_frame(a.log_scales[i], a.log_scales[n + i], a.log_scales[2 * n + i], a.quats[i],
+                                     a.quats[n + i], a.quats[2 * n + i], a.quats[3 * n + i], a.logits[i],
+                                     finitef(g.mx) && finitef(g.my) && finitef(g.mz));
+    g.ok = f.ok;
+    g.o = f.o;
+#pragma unroll
+    for (int k = 0; k < 6; k++) g.S[k] = f.S[k];
     return g;
 }
 
-// Real orthonormal spherical harmonics (textbook Cartesian forms, no Condon-Shortley phase),
-// summed with the coefficients of Gaussian i; the DC rows are the base colour.
+// Colour before the clamp along unit direction (x, y, z); the DC rows are the base colour.
 __device__ float3 sh_colour(const ProjectArgs& a, int i, float x, float y, float z) {
-    const int n = a.n;
-    const float* sh = a.sh;
-    float3 c;
-    c.x = sh[0 * n + i];
-    c.y = sh[1 * n + i];
-    c.z = sh[2 * n + i];
-    const int deg = a.p.sh_degree;
-    if (deg < 1) return c;
     float Y[15];
-    Y[0] = 0.4886025119029199f * y;  // sqrt(3/(4 pi)) (y, z, x)
-    Y[1] = 0.4886025119029199f * z;
-    Y[2] = 0.4886025119029199f * x;
-    int nk = 3;
-    if (deg >= 2) {
-        Y[3] = 1.0925484305920792f * x * y;                // 1/2 sqrt(15/pi) xy
-        Y[4] = 1.0925484305920792f * y * z;                // 1/2 sqrt(15/pi) yz
-        Y[5] = 0.31539156525252005f * (3.0f * z * z - 1.0f);  // 1/4 sqrt(5/pi) (3z^2 - 1)
-        Y[6] = 1.0925484305920792f * x * z;                // 1/2 sqrt(15/pi) xz
-        Y[7] = 0.5462742152960396f * (x * x - y * y);      // 1/4 sqrt(15/pi) (x^2 - y^2)
-        nk = 8;
-    }
-    if (deg >= 3) {
-        Y[8] = 0.5900435899266435f * y * (3.0f * x * x - y * y);   // 1/4 sqrt(35/(2pi))
-        Y[9] = 2.890611442640554f * x * y * z;                     // 1/2 sqrt(105/pi)
-        Y[10] = 0.4570457994644658f * y * (5.0f * z * z - 1.0f);   // 1/4 sqrt(21/(2pi))
-        Y[11] = 0.3731763325901154f * z * (5.0f * z * z - 3.0f);   // 1/4 sqrt(7/pi)
-        Y[12] = 0.4570457994644658f * x * (5.0f * z * z - 1.0f);   // 1/4 sqrt(21/(2pi))
-        Y[13] = 1.445305721320277f * z * (x * x - y * y);          // 1/4 sqrt(105/pi)
-        Y[14] = 0.5900435899266435f * x * (x * x - 3.0f * y * y);  // 1/4 sqrt(35/(2pi))
-        nk = 15;
-    }
-#pragma unroll
-    for (int k = 0; k < 15; k++) {
-        if (k < nk) {
-            const int row = (k + 1) * 3;
-            c.x = fmaf(sh[(row + 0) * n + i], Y[k], c.x);
-            c.y = fmaf(sh[(row + 1) * n + i], Y[k], c.y);
-            c.z = fmaf(sh[(row + 2) * n + i], Y[k], c.z);
-        }
-    }
-    return c;
+    const int nY = sh_basis(a.p.sh_degree, x, y, z, Y);
+    return sh_eval(a.sh + i, a.n, nY, Y);
 }
 
 // All per-view tests and, when visible, the record.  Returns visibility.
@@ -164,13 +105,8 @@ __device__ bool project_view(const ProjectArgs& a, const Geo& g, const CamDev& c
     const float fv0 = fmaxf(0.0f, ceilf(loy)), fv1 = fminf((float)(c.height - 1), floorf(hiy));
     if (!(fu0 <= fu1) || !(fv0 <= fv1)) return false;
     // colour along the viewing direction
-    float dx = g.mx - c.campos[0], dy = g.my - c.campos[1], dz = g.mz - c.campos[2];
-    const float dn = sqrtf(dx * dx + dy * dy + dz * dz);
-    if (!(dn > 0.0f)) return false;
-    const float idn = 1.0f / dn;
-    dx *= idn;
-    dy *= idn;
-    dz *= idn;
+    float dx, dy, dz, idn;
+    if (!view_dir(g.mx, g.my, g.mz, c.campos, &dx, &dy, &dz, &idn)) return false;
     const float3 col = sh_colour(a, i, dx, dy, dz);
     if (!(finitef(col.x) && finitef(col.y) && finitef(col.z))) return false;
     r.xy = make_float2(mx, my);

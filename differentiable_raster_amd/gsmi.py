@@ -70,6 +70,11 @@ class gs_grads2d(ctypes.Structure):
                 ("d_color", ctypes.c_void_p)]
 
 
+class gs_grads3d(ctypes.Structure):
+    _fields_ = [("d_means", ctypes.c_void_p), ("d_log_scales", ctypes.c_void_p), ("d_quats", ctypes.c_void_p),
+                ("d_opacity_logits", ctypes.c_void_p), ("d_sh", ctypes.c_void_p)]
+
+
 _P = ctypes.POINTER
 _SIGS = {
     "gs_version": (ctypes.c_char_p, []),
@@ -98,6 +103,8 @@ _SIGS = {
                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, _P(gs_grads2d),
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "gs_raster_workspace_size": (ctypes.c_size_t, [ctypes.c_int64]),
+    "gs_project_bwd": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
+                                      _P(gs_projected), _P(gs_grads2d), _P(gs_grads3d), ctypes.c_void_p]),
     "gs_fused_max_cap": (ctypes.c_int, [_P(ctypes.c_int32)]),
 }
 
@@ -199,6 +206,12 @@ def gs_fused_max_cap() -> int:
 def gs_project(g: gs_gaussians, cams, V: int, params: gs_render_params, out: gs_projected, ws, stream=None):
     _check(load().gs_project(ctypes.byref(g), cams, V, ctypes.byref(params), ctypes.byref(out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "gs_project")
+
+
+def gs_project_bwd(g: gs_gaussians, cams, V: int, params: gs_render_params, proj: gs_projected,
+                   grads2d: gs_grads2d, out: gs_grads3d, stream=None):
+    _check(load().gs_project_bwd(ctypes.byref(g), cams, V, ctypes.byref(params), ctypes.byref(proj),
+                                 ctypes.byref(grads2d), ctypes.byref(out), _stream(stream)), "gs_project_bwd")
 
 
 def gs_bin_tiles(cams, proj: gs_projected, V: int, params: gs_render_params, bins: gs_bins, ws, stream=None):

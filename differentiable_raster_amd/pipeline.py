@@ -143,7 +143,21 @@ class Renderer:
                              scale, self.image if image else None, self.loss_sum if loss_sum else None, self.grads,
                              self.ws_raster, self.counters if counters else None)
 
-    def iteration(self, mode: str = "fused", scale: float = 1.0, image: bool = False):
+    def project_backward(self):
+        """Chain the per-slot 2D gradients of all views to the parameters (gs_project_bwd)."""
+        if not hasattr(self, "g3"):
+            dev, f32, n = self.device, torch.float32, max(1, self.n)
+            nk = self.sh.shape[0]
+            self.d_means3 = torch.empty(3 * n, dtype=f32, device=dev)
+            self.d_log_scales3 = torch.empty(3 * n, dtype=f32, device=dev)
+            self.d_quats3 = torch.empty(4 * n, dtype=f32, device=dev)
+            self.d_logits3 = torch.empty(n, dtype=f32, device=dev)
+            self.d_sh3 = torch.empty(nk * n, dtype=f32, device=dev)
+            self.g3 = gsmi.gs_grads3d(self.d_means3.data_ptr(), self.d_log_scales3.data_ptr(),
+                                      self.d_quats3.data_ptr(), self.d_logits3.data_ptr(), self.d_sh3.data_ptr())
+        gsmi.gs_project_bwd(self.g, self.cams, self.V, self.params, self.proj, self.grads, self.g3)
+
+    def iteration(self, mode: str = "fused", scale: float = 1.0, image: bool = False, project_bwd: bool = False):
         self.project()
         self.bin()
         if mode == "fused":
@@ -151,6 +165,8 @@ class Renderer:
         else:
             self.forward()
             self.backward(self.loss_grad(scale))
+        if project_bwd:
+            self.project_backward()
 
     # -- host copies for checks ----------------------------------------------------------
     def projected_host(self, v: int) -> dict:
@@ -192,6 +208,14 @@ class Renderer:
         V, H, W = self.V, self.H, self.W
         return (self.image.view(V, 3, H, W).cpu().numpy(), self.t_final.view(V, H, W).cpu().numpy(),
                 self.n_contrib.view(V, H, W).cpu().numpy())
+
+    def grads3d_host(self) -> dict:
+        n, nk = self.n, self.sh.shape[0]
+        return dict(d_means=self.d_means3[:3 * n].view(3, n).cpu().numpy(),
+                    d_log_scales=self.d_log_scales3[:3 * n].view(3, n).cpu().numpy(),
+                    d_quats=self.d_quats3[:4 * n].view(4, n).cpu().numpy(),
+                    d_opacity_logits=self.d_logits3[:n].cpu().numpy(),
+                    d_sh=self.d_sh3[:nk * n].view(nk, n).cpu().numpy())
 
     def grads_host(self, v: int) -> dict:
         cnt = int(self.vis_count[v].item())

@@ -142,6 +142,15 @@ typedef struct {
     float* d_color;   /* [V][capacity][3] dL/d colour (post-clamp RGB) */
 } gs_grads2d;
 
+/* Per-Gaussian parameter gradients, float32, device, in the layout of gs_gaussians. */
+typedef struct {
+    float* d_means;          /* [3][n] */
+    float* d_log_scales;     /* [3][n] */
+    float* d_quats;          /* [4][n] with respect to the raw (unnormalized) quaternion */
+    float* d_opacity_logits; /* [n] */
+    float* d_sh;             /* [3*(d+1)^2][n], row k*3 + channel */
+} gs_grads3d;
+
 typedef enum { GS_LOSS_L1 = 0, GS_LOSS_EXTERNAL = 1 } gs_loss_mode;
 
 /* Optional per-call diagnostics: device int64 [3], accumulated (the caller zeroes them); pass
@@ -251,6 +260,27 @@ gs_status gs_raster_fused(const gs_camera* cams /*host [V]*/, const gs_projected
                           const float* target_or_dldc, float loss_scale, float* image_opt,
                           float* loss_sum_opt, gs_grads2d* grads, gs_counters* counters, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * Backward of A1 (the step that follows the rasterizer backward in training, which ByteSplat,
+ * arXiv 2610.02851, English abstract, names as the workload; no page writes it out): the chain
+ * rule of gs_project from the per-slot gradients `grads2d` of V views (dL/d mean2d, conic (A, B,
+ * C), activated opacity and clamped colour, as gs_raster_bwd / gs_raster_fused write them) to
+ * the parameters, summed over the views in which each Gaussian is visible:
+ *   conic -> dilated 2D covariance -> J W and the world covariance R diag(s^2) R^T -> log-scales
+ *   and the normalized quaternion -> raw quaternion; J(t) and the projected centre -> camera
+ *   point t = W mu + t_cam -> mean; colour = max(0, DC + sum_k sh_k Y_k(dir)) -> SH rows (only
+ *   for channels above zero) and, through dir = unit(mu - campos), the mean;
+ *   opacity = sigmoid(logit) -> logit.
+ * The culling and box decisions are piecewise constant and carry no gradient.  `proj` must be
+ * the output of gs_project for the same parameters, cameras and params (its vis_count and vis_ids
+ * are read: the slots of a view hold ascending Gaussian indices).  Every entry of `out` is
+ * overwritten (zero for Gaussians that no view sees).  One thread per Gaussian; no workspace.
+ * Errors: GS_ERR_INVALID_ARGUMENT for null pointers or sizes as for gs_project.
+ */
+gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, int32_t V,
+                         const gs_render_params* p, const gs_projected* proj, const gs_grads2d* grads2d,
+                         gs_grads3d* out, void* stream);
 
 /* Entries of a tile list the rasterizers stage in LDS at a time (lists of any length are
  * processed batch by batch).  *k (host) receives it. */

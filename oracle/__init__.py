@@ -66,6 +66,7 @@ def _load():
         _lib.orc_project.restype = None
         _lib.orc_project_f64.restype = None
         _lib.orc_project_backward.restype = None
+        _lib.orc_project_backward_errbound.restype = None
         _lib.orc_sh_basis_grad.restype = None
         _lib.orc_raster_forward.restype = None
         _lib.orc_raster_backward.restype = None
@@ -197,7 +198,7 @@ def project_f64(params: dict, cam, settings) -> dict:
 
 
 def project_backward(params: dict, cam, settings, visible: np.ndarray, g_mean2d, g_conic, g_opacity, g_color,
-                     acc: Optional[dict] = None) -> dict:
+                     acc: Optional[dict] = None, error_bound: bool = False) -> dict:
     """Chain rule of the projection for one view (test infrastructure).
 
     ``params``: ``scene_params_f64`` layout.  ``visible`` (n,) selects the Gaussians; the
@@ -209,7 +210,12 @@ def project_backward(params: dict, cam, settings, visible: np.ndarray, g_mean2d,
 
     Parity: pinned by central finite differences of ``project_f64`` for every parameter, by
     invariances (an isotropic Gaussian has no quaternion gradient; the quaternion gradient is
-    orthogonal to the quaternion) and by closed forms for the colour and opacity terms."""
+    orthogonal to the quaternion) and by closed forms for the colour and opacity terms.
+
+    error_bound: also add e_means, e_log_scales, e_quats, e_opacity_logits, e_sh: a first-order
+    running bound on the error of evaluating the same chain in float32 (a tolerance model for
+    comparisons, from the rounding of every operation; pinned against float32 evaluations of the
+    chain in the tests)."""
     lib = _load()
     n = params["means"].shape[1]
     nk = params["sh"].shape[0]
@@ -224,6 +230,13 @@ def project_backward(params: dict, cam, settings, visible: np.ndarray, g_mean2d,
     lib.orc_project_backward(ctypes.c_int64(n), *[_p(a) for a in arrs], ctypes.byref(c), ctypes.byref(pp),
                              _p(vis), *[_p(x) for x in g], _p(acc["d_means"]), _p(acc["d_log_scales"]),
                              _p(acc["d_quats"]), _p(acc["d_opacity_logits"]), _p(acc["d_sh"]), _p(acc["flag"]))
+    if error_bound:
+        for k in ("d_means", "d_log_scales", "d_quats", "d_opacity_logits", "d_sh"):
+            acc.setdefault("e" + k[1:], np.zeros_like(acc[k]))
+        lib.orc_project_backward_errbound(ctypes.c_int64(n), *[_p(a) for a in arrs], ctypes.byref(c),
+                                          ctypes.byref(pp), _p(vis), *[_p(x) for x in g], _p(acc["e_means"]),
+                                          _p(acc["e_log_scales"]), _p(acc["e_quats"]), _p(acc["e_opacity_logits"]),
+                                          _p(acc["e_sh"]))
     return acc
 
 

@@ -526,6 +526,232 @@ void orc_project_backward(int64_t n, const double* means, const double* log_scal
     }
 }
 
+/*
+ * Rounding-error model of the projection backward (a tolerance model, not part of the
+ * definition).  Each quantity carries a first-order bound e on the error that evaluating the
+ * same formulas in float32 (one rounding per operation, exp within a few ulp, inputs exact)
+ * can make: e(a +- b) = e(a) + e(b) + u|a +- b|, e(ab) = |a| e(b) + |b| e(a) + u|ab|,
+ * e(a / b) = e(a)/|b| + |a| e(b)/b^2 + u|a/b|, e(sqrt a) = e(a)/(2 sqrt a) + u sqrt a, with
+ * u = 2^-24 (Higham, Accuracy and Stability of Numerical Algorithms, running error analysis).
+ * It follows orc_project_backward step by step and ADDS, per view, the bound of that view's
+ * contribution to each output plus the rounding of adding it to the running sum.
+ */
+typedef struct {
+    double v, e;
+} ve;
+
+static ve ve_in(double v) { ve r = {v, 0.0}; return r; }
+static ve ve_add(ve a, ve b) { ve r = {a.v + b.v, 0.0}; r.e = a.e + b.e + EPS32 * fabs(r.v); return r; }
+static ve ve_sub(ve a, ve b) { ve r = {a.v - b.v, 0.0}; r.e = a.e + b.e + EPS32 * fabs(r.v); return r; }
+static ve ve_mul(ve a, ve b)
+{
+    ve r = {a.v * b.v, 0.0};
+    r.e = fabs(a.v) * b.e + fabs(b.v) * a.e + EPS32 * fabs(r.v);
+    return r;
+}
+static ve ve_div(ve a, ve b)
+{
+    ve r = {a.v / b.v, 0.0};
+    r.e = a.e / fabs(b.v) + fabs(a.v) * b.e / (b.v * b.v) + EPS32 * fabs(r.v);
+    return r;
+}
+static ve ve_sqrt(ve a) { ve r = {sqrt(a.v), 0.0}; r.e = a.e / (2.0 * r.v) + EPS32 * r.v; return r; }
+static ve ve_exp(ve a) { ve r = {exp(a.v), 0.0}; r.e = r.v * (a.e + 4.0 * EPS32); return r; }
+static ve ve_k(double k, ve a) { ve r = {k * a.v, fabs(k) * a.e}; return r; } /* k a power of two */
+static ve ve_neg(ve a) { ve r = {-a.v, a.e}; return r; }
+static ve ve_dot3(const ve* a, const ve* b)
+{
+    return ve_add(ve_add(ve_mul(a[0], b[0]), ve_mul(a[1], b[1])), ve_mul(a[2], b[2]));
+}
+
+void orc_project_backward_errbound(int64_t n, const double* means, const double* log_scales, const double* quats,
+                                   const double* opacity_logits, const double* sh, const orc_camera* cam,
+                                   const orc_params* p, const int8_t* visible, const double* g_mean2d,
+                                   const double* g_conic, const double* g_opacity, const double* g_color,
+                                   double* e_means, double* e_log_scales, double* e_quats, double* e_logits,
+                                   double* e_sh)
+{
+    const int deg = p->sh_degree;
+    const int nk = (deg + 1) * (deg + 1);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        if (!visible[i]) continue;
+        ve mu[3], s[3], q[4], W[9], tvec[3];
+        for (int k = 0; k < 3; k++) mu[k] = ve_in(means[k * n + i]);
+        for (int k = 0; k < 3; k++) s[k] = ve_exp(ve_in(log_scales[k * n + i]));
+        for (int k = 0; k < 9; k++) W[k] = ve_in(cam->R[k]);
+        for (int k = 0; k < 3; k++) tvec[k] = ve_in(cam->t[k]);
+        const ve one = ve_in(1.0);
+        const ve o = ve_div(one, ve_add(one, ve_exp(ve_in(-opacity_logits[i]))));
+        ve qr[4];
+        for (int k = 0; k < 4; k++) qr[k] = ve_in(quats[k * n + i]);
+        ve qq = ve_mul(qr[0], qr[0]);
+        for (int k = 1; k < 4; k++) qq = ve_add(qq, ve_mul(qr[k], qr[k]));
+        const ve qn = ve_sqrt(qq);
+        for (int k = 0; k < 4; k++) q[k] = ve_div(qr[k], qn);
+
+        /* forward quantities */
+        ve tc[3];
+        for (int r = 0; r < 3; r++) tc[r] = ve_add(ve_dot3(&W[3 * r], mu), tvec[r]);
+        const ve fx = ve_in(cam->fx), fy = ve_in(cam->fy);
+        const ve w = q[0], x = q[1], y = q[2], z = q[3];
+        ve Rq[9];
+        Rq[0] = ve_sub(one, ve_k(2.0, ve_add(ve_mul(y, y), ve_mul(z, z))));
+        Rq[1] = ve_k(2.0, ve_sub(ve_mul(x, y), ve_mul(w, z)));
+        Rq[2] = ve_k(2.0, ve_add(ve_mul(x, z), ve_mul(w, y)));
+        Rq[3] = ve_k(2.0, ve_add(ve_mul(x, y), ve_mul(w, z)));
+        Rq[4] = ve_sub(one, ve_k(2.0, ve_add(ve_mul(x, x), ve_mul(z, z))));
+        Rq[5] = ve_k(2.0, ve_sub(ve_mul(y, z), ve_mul(w, x)));
+        Rq[6] = ve_k(2.0, ve_sub(ve_mul(x, z), ve_mul(w, y)));
+        Rq[7] = ve_k(2.0, ve_add(ve_mul(y, z), ve_mul(w, x)));
+        Rq[8] = ve_sub(one, ve_k(2.0, ve_add(ve_mul(x, x), ve_mul(y, y))));
+        ve M[9], Sig[9];
+        for (int a = 0; a < 3; a++)
+            for (int k = 0; k < 3; k++) M[3 * a + k] = ve_mul(Rq[3 * a + k], s[k]);
+        for (int a = 0; a < 3; a++)
+            for (int b = 0; b < 3; b++) {
+                const ve ra[3] = {M[3 * a], M[3 * a + 1], M[3 * a + 2]};
+                const ve rb[3] = {M[3 * b], M[3 * b + 1], M[3 * b + 2]};
+                Sig[3 * a + b] = ve_dot3(ra, rb);
+            }
+        const ve iz = ve_div(one, tc[2]);
+        const ve iz2 = ve_mul(iz, iz), iz3 = ve_mul(iz2, iz);
+        ve J[6] = {ve_mul(fx, iz), ve_in(0.0), ve_neg(ve_mul(ve_mul(fx, tc[0]), iz2)),
+                   ve_in(0.0), ve_mul(fy, iz), ve_neg(ve_mul(ve_mul(fy, tc[1]), iz2))};
+        ve T[6];
+        for (int r = 0; r < 2; r++)
+            for (int c = 0; c < 3; c++) {
+                const ve col[3] = {W[c], W[3 + c], W[6 + c]};
+                T[3 * r + c] = ve_dot3(&J[3 * r], col);
+            }
+        ve U[3], Vv[3];
+        for (int k = 0; k < 3; k++) {
+            U[k] = ve_dot3(&Sig[3 * k], &T[0]);
+            Vv[k] = ve_dot3(&Sig[3 * k], &T[3]);
+        }
+        const ve eps = ve_in(p->eps2d);
+        const ve a = ve_add(ve_dot3(&T[0], U), eps);
+        const ve b = ve_dot3(&T[3], U);
+        const ve c = ve_add(ve_dot3(&T[3], Vv), eps);
+        const ve det = ve_sub(ve_mul(a, c), ve_mul(b, b));
+        const ve idet = ve_div(one, det);
+        const ve idet2 = ve_mul(idet, idet);
+
+        const ve gA = ve_in(g_conic[3 * i]), gB = ve_in(g_conic[3 * i + 1]), gC = ve_in(g_conic[3 * i + 2]);
+        const ve ga = ve_mul(ve_add(ve_sub(ve_mul(ve_mul(b, c), gB), ve_mul(ve_mul(c, c), gA)),
+                                    ve_neg(ve_mul(ve_mul(b, b), gC))), idet2);
+        const ve gb = ve_mul(ve_add(ve_sub(ve_k(2.0, ve_mul(ve_mul(b, c), gA)),
+                                           ve_mul(ve_add(det, ve_k(2.0, ve_mul(b, b))), gB)),
+                                    ve_k(2.0, ve_mul(ve_mul(a, b), gC))), idet2);
+        const ve gc = ve_mul(ve_sub(ve_sub(ve_mul(ve_mul(a, b), gB), ve_mul(ve_mul(b, b), gA)),
+                                    ve_mul(ve_mul(a, a), gC)), idet2);
+
+        ve gT[6], Gs[9];
+        for (int k = 0; k < 3; k++) {
+            gT[k] = ve_add(ve_k(2.0, ve_mul(ga, U[k])), ve_mul(gb, Vv[k]));
+            gT[3 + k] = ve_add(ve_mul(gb, U[k]), ve_k(2.0, ve_mul(gc, Vv[k])));
+        }
+        for (int u = 0; u < 3; u++)
+            for (int v = 0; v < 3; v++) {
+                const ve t1 = ve_k(2.0, ve_mul(ga, ve_mul(T[u], T[v])));
+                const ve t2 = ve_mul(gb, ve_add(ve_mul(T[u], T[3 + v]), ve_mul(T[3 + u], T[v])));
+                const ve t3 = ve_k(2.0, ve_mul(gc, ve_mul(T[3 + u], T[3 + v])));
+                Gs[3 * u + v] = ve_add(ve_add(t1, t2), t3);
+            }
+        ve gJ[6];
+        for (int r = 0; r < 2; r++)
+            for (int k = 0; k < 3; k++) gJ[3 * r + k] = ve_dot3(&gT[3 * r], &W[3 * k]);
+        const ve gmx = ve_in(g_mean2d[2 * i]), gmy = ve_in(g_mean2d[2 * i + 1]);
+        ve gt[3];
+        gt[0] = ve_sub(ve_mul(ve_mul(gmx, fx), iz), ve_mul(ve_mul(gJ[2], fx), iz2));
+        gt[1] = ve_sub(ve_mul(ve_mul(gmy, fy), iz), ve_mul(ve_mul(gJ[5], fy), iz2));
+        {
+            const ve t1 = ve_mul(ve_mul(ve_mul(gmx, fx), tc[0]), iz2);
+            const ve t2 = ve_mul(ve_mul(ve_mul(gmy, fy), tc[1]), iz2);
+            const ve t3 = ve_mul(ve_mul(gJ[0], fx), iz2);
+            const ve t4 = ve_k(2.0, ve_mul(ve_mul(ve_mul(gJ[2], fx), tc[0]), iz3));
+            const ve t5 = ve_mul(ve_mul(gJ[4], fy), iz2);
+            const ve t6 = ve_k(2.0, ve_mul(ve_mul(ve_mul(gJ[5], fy), tc[1]), iz3));
+            gt[2] = ve_add(ve_sub(ve_add(ve_sub(ve_neg(ve_add(t1, t2)), t3), t4), t5), t6);
+        }
+        ve gmu[3];
+        for (int k = 0; k < 3; k++) {
+            const ve col[3] = {W[k], W[3 + k], W[6 + k]};
+            gmu[k] = ve_dot3(col, gt);
+        }
+
+        ve gR[9];
+        for (int k = 0; k < 3; k++) {
+            const ve r[3] = {Rq[k], Rq[3 + k], Rq[6 + k]};
+            ve wv[3];
+            for (int u = 0; u < 3; u++) wv[u] = ve_dot3(&Gs[3 * u], r);
+            const ve sk2 = ve_mul(s[k], s[k]);
+            const ve gls = ve_mul(sk2, ve_dot3(r, wv));
+            e_log_scales[k * n + i] += gls.e + EPS32 * fabs(gls.v);
+            for (int u = 0; u < 3; u++) gR[3 * u + k] = ve_mul(sk2, wv[u]);
+        }
+        /* quaternion: each component is a sum of 6-8 terms 2 q_a gR_b (factors 2 and 4 exact) */
+        ve gq[4];
+        gq[0] = ve_k(2.0, ve_add(ve_add(ve_add(ve_sub(ve_mul(y, gR[2]), ve_mul(z, gR[1])), ve_mul(z, gR[3])),
+                                        ve_sub(ve_mul(x, gR[7]), ve_mul(x, gR[5]))), ve_neg(ve_mul(y, gR[6]))));
+        gq[1] = ve_k(2.0, ve_add(ve_add(ve_add(ve_mul(y, gR[1]), ve_mul(z, gR[2])), ve_add(ve_mul(y, gR[3]), ve_mul(z, gR[6]))),
+                                 ve_sub(ve_sub(ve_mul(w, gR[7]), ve_mul(w, gR[5])),
+                                        ve_k(2.0, ve_add(ve_mul(x, gR[4]), ve_mul(x, gR[8]))))));
+        gq[2] = ve_k(2.0, ve_add(ve_add(ve_add(ve_mul(x, gR[1]), ve_mul(w, gR[2])), ve_add(ve_mul(x, gR[3]), ve_mul(z, gR[5]))),
+                                 ve_sub(ve_sub(ve_mul(z, gR[7]), ve_mul(w, gR[6])),
+                                        ve_k(2.0, ve_add(ve_mul(y, gR[0]), ve_mul(y, gR[8]))))));
+        gq[3] = ve_k(2.0, ve_add(ve_add(ve_add(ve_mul(x, gR[2]), ve_mul(w, gR[3])), ve_add(ve_mul(y, gR[5]), ve_mul(x, gR[6]))),
+                                 ve_sub(ve_sub(ve_mul(y, gR[7]), ve_mul(w, gR[1])),
+                                        ve_k(2.0, ve_add(ve_mul(z, gR[0]), ve_mul(z, gR[4]))))));
+        ve qd = ve_mul(gq[0], q[0]);
+        for (int k = 1; k < 4; k++) qd = ve_add(qd, ve_mul(gq[k], q[k]));
+        for (int k = 0; k < 4; k++) {
+            const ve d = ve_div(ve_sub(gq[k], ve_mul(q[k], qd)), qn);
+            e_quats[k * n + i] += d.e + EPS32 * fabs(d.v);
+        }
+        const ve glog = ve_mul(ve_mul(ve_in(g_opacity[i]), o), ve_sub(one, o));
+        e_logits[i] += glog.e + EPS32 * fabs(glog.v);
+
+        /* colour */
+        const ve cp[3] = {ve_in(cam->campos[0]), ve_in(cam->campos[1]), ve_in(cam->campos[2])};
+        ve dv[3];
+        for (int k = 0; k < 3; k++) dv[k] = ve_sub(mu[k], cp[k]);
+        const ve dn = ve_sqrt(ve_dot3(dv, dv));
+        const ve idn = ve_div(one, dn);
+        ve dir[3];
+        for (int k = 0; k < 3; k++) dir[k] = ve_mul(dv[k], idn);
+        double dirv[3] = {dir[0].v, dir[1].v, dir[2].v};
+        double Y[16], dY[48];
+        orc_sh_basis(deg, dirv, Y);
+        orc_sh_basis_grad(deg, dirv, dY);
+        /* basis values: polynomials of degree <= 3 in dir; bound their error by the direction's
+         * error times the basis gradient plus a few roundings of the value */
+        const double edir = fmax(dir[0].e, fmax(dir[1].e, dir[2].e));
+        ve gdir[3] = {ve_in(0.0), ve_in(0.0), ve_in(0.0)};
+        for (int ch = 0; ch < 3; ch++) {
+            const double* shc = sh + (size_t)ch * n + i;
+            double v = shc[0];
+            for (int k = 1; k < nk; k++) v += shc[(size_t)k * 3 * n] * Y[k];
+            if (!(v > 0.0)) continue;
+            const ve g = ve_in(g_color[3 * i + ch]); /* the DC row's contribution g is exact */
+            for (int k = 1; k < nk; k++) {
+                const double gy = fabs(dY[3 * k]) + fabs(dY[3 * k + 1]) + fabs(dY[3 * k + 2]);
+                const ve Yk = {Y[k], gy * edir + 8.0 * EPS32 * (fabs(Y[k]) + gy)};
+                const ve t = ve_mul(g, Yk);
+                e_sh[(size_t)(k * 3 + ch) * n + i] += t.e + EPS32 * fabs(t.v);
+                const ve e = ve_mul(g, ve_in(shc[(size_t)k * 3 * n]));
+                for (int m = 0; m < 3; m++) {
+                    const ve dYm = {dY[3 * k + m], 8.0 * EPS32 * (fabs(dY[3 * k + m]) + gy) + 6.0 * gy * edir};
+                    gdir[m] = ve_add(gdir[m], ve_mul(e, dYm));
+                }
+            }
+        }
+        const ve gdot = ve_dot3(gdir, dir);
+        for (int m = 0; m < 3; m++) gmu[m] = ve_add(gmu[m], ve_mul(ve_sub(gdir[m], ve_mul(dir[m], gdot)), idn));
+        for (int k = 0; k < 3; k++) e_means[k * n + i] += gmu[k].e + EPS32 * fabs(gmu[k].v);
+    }
+}
+
 /* ------------------------------------------------------------------------------------- */
 /* Rasterization                                                                          */
 /* ------------------------------------------------------------------------------------- */

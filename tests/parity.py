@@ -209,3 +209,67 @@ def compare_backward(oracle, cam, settings, rec, ranges, vals, dldc, grads_g, fw
         total_bad += bad
     assert total_bad == 0
     return b
+
+
+def slot_to_gaussian(n, vis_ids, arr, k):
+    """Scatter a per-slot array (slots, k) into a per-Gaussian float64 array (n, k) (zeros elsewhere)."""
+    out = np.zeros((n, k))
+    out[vis_ids] = np.asarray(arr, np.float64).reshape(-1, k)[: vis_ids.size]
+    return out
+
+
+def compare_project_backward(oracle, scene, settings, views, grads2d_g, grads3d_g, sample=None):
+    """Projection backward, stage-isolated: the oracle chains the GPU's own per-slot 2D gradients
+    of every view (and the GPU's visible sets) to the parameters in double precision.
+
+    views: list of (camera, vis_ids) per view; grads2d_g: per view the dict of grads_host();
+    grads3d_g: dict of grads3d_host(); sample: optional Gaussian indices (the oracle then runs on
+    that subset only, with the GPU's outputs gathered at them).
+    Contract per component: within 1e-3 relative + 1e-6 absolute plus twice the oracle's
+    first-order bound on the error of a float32 evaluation of the same chain (large only where
+    the chain's terms cancel: scale and rotation gradients of Gaussians elongated along the
+    view direction); and at most 1e-4 of the components of each kind may need that bound term.
+    Colour and mean gradients of Gaussians whose colour sits within float32 reach of the clamp at
+    zero in some view are skipped."""
+    params = oracle.scene_params_f64(scene)
+    n_all = scene.n
+    idx = np.arange(n_all) if sample is None else np.asarray(sample)
+    if sample is not None:
+        params = {k: np.ascontiguousarray(v[..., idx]) for k, v in params.items()}
+    n = idx.size
+    acc = None
+    for (cam, vis_ids), g2 in zip(views, grads2d_g):
+        def per_gauss(key, k):
+            full = slot_to_gaussian(n_all, vis_ids, g2[key], k)
+            return full[idx]
+        vis_full = np.zeros(n_all, np.int8)
+        vis_full[vis_ids] = 1
+        acc = oracle.project_backward(params, cam, settings, vis_full[idx], per_gauss("d_mean2d", 2),
+                                      per_gauss("d_conic", 3), per_gauss("d_opacity", 1)[:, 0],
+                                      per_gauss("d_color", 3), acc=acc, error_bound=True)
+    flag = acc["flag"]
+    bad_total = 0
+    for key in ("d_means", "d_log_scales", "d_quats", "d_opacity_logits", "d_sh"):
+        go = acc[key]
+        eb = acc["e" + key[1:]]
+        gg = np.asarray(grads3d_g[key], np.float64)[..., idx]
+        use = np.ones(n, bool) if key not in ("d_means", "d_sh") else (flag == 0)
+        go_u, gg_u, eb_u = go[..., use], gg[..., use], eb[..., use]
+        err = np.abs(gg_u - go_u)
+        base = GRAD_RTOL * np.abs(go_u) + GRAD_ATOL
+        strict = err <= base
+        ok = err <= base + 2.0 * eb_u
+        n_bound = int((ok & ~strict).sum())
+        rel = err / (np.abs(go_u) + 1e-30)
+        q = np.quantile(rel, [0.5, 0.99]) if rel.size else [0, 0]
+        bad = report(key, ok, f"({int((~use).sum())} Gaussians skipped at the colour clamp; {n_bound} within "
+                              f"tolerance only through the float32 error bound; relative error median "
+                              f"{q[0]:.2g} p99 {q[1]:.2g})")
+        if bad:
+            for loc in np.argwhere(~ok)[:5]:
+                loc = tuple(loc)
+                print(f"    {key}{loc}: gpu {gg_u[loc]:.9g} oracle {go_u[loc]:.9g} bound {eb_u[loc]:.3g}", flush=True)
+        bad_total += bad
+        assert n_bound <= max(1, 1e-4 * ok.size), (key, n_bound)
+    assert bad_total == 0
+    return acc

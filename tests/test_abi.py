@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ["gs_project", "gs_bin_tiles", "gs_raster_fwd", "gs_raster_bwd", "gs_raster_fused",
                  "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
+                 "gs_project_bwd", "gs_raster_workspace_size",
                  "gs_version", "gs_status_string", "gs_last_error"]:
         assert must in names, must
 
@@ -80,6 +81,33 @@ def projected(gs, capacity=100, null=()):
     for f in null:
         fields[f] = None
     return gs.gs_projected(capacity, *[fields[f] for f, _ in gs.gs_projected._fields_ if f != "capacity"])
+
+
+def test_project_bwd_rejects_bad_arguments(gs):
+    lib = gs.load()
+    g = gs.gs_gaussians(100, FAKE, FAKE, FAKE, FAKE, FAKE)
+    c = cams(gs)
+    p = params(gs)
+    pr = projected(gs)
+    g2 = gs.gs_grads2d(FAKE, FAKE, FAKE, FAKE)
+    g3 = gs.gs_grads3d(FAKE, FAKE, FAKE, FAKE, FAKE)
+    call = lambda g_, V, p_, pr_, a, b: lib.gs_project_bwd(g_, c, V, p_, pr_, a, b, None)
+    assert call(None, 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2), ctypes.byref(g3)) == 1
+    assert call(ctypes.byref(g), 0, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2), ctypes.byref(g3)) == 1
+    assert call(ctypes.byref(g), 1, ctypes.byref(params(gs, sh_degree=5)), ctypes.byref(pr), ctypes.byref(g2),
+                ctypes.byref(g3)) == 1
+    assert call(ctypes.byref(g), 1, ctypes.byref(p), None, ctypes.byref(g2), ctypes.byref(g3)) == 1
+    small = projected(gs, capacity=50)
+    assert call(ctypes.byref(g), 1, ctypes.byref(p), ctypes.byref(small), ctypes.byref(g2), ctypes.byref(g3)) == 1
+    assert call(ctypes.byref(g), 1, ctypes.byref(p), ctypes.byref(pr), None, ctypes.byref(g3)) == 1
+    assert call(ctypes.byref(g), 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(gs.gs_grads2d(FAKE, FAKE, None, FAKE)),
+                ctypes.byref(g3)) == 1
+    assert call(ctypes.byref(g), 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2), None) == 1
+    assert call(ctypes.byref(g), 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2),
+                ctypes.byref(gs.gs_grads3d(FAKE, FAKE, FAKE, FAKE, None))) == 1
+    assert b"null" in lib.gs_last_error()
+    g_null = gs.gs_gaussians(100, FAKE, FAKE, None, FAKE, FAKE)
+    assert call(ctypes.byref(g_null), 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2), ctypes.byref(g3)) == 1
 
 
 def test_project_rejects_bad_arguments(gs):

@@ -5,7 +5,10 @@
 * the same scene with per-tile caps K in {256, 512, 1024}: capped lists bit-exact, compositing
   parity, and the PSNR of the capped render against the uncapped oracle render (reported).
 * 40M Gaussians @3840x2160 x4 views: projection on a seeded sample of Gaussians, binning for every
-  visible slot of every view, rasterization on seeded 6x6-tile regions.
+  visible slot of every view, rasterization on seeded 6x6-tile regions, projection backward on
+  the sampled Gaussians.
+* The projection backward (2D gradients of all views -> parameter gradients) follows the fused
+  call in the 1M tests and is compared for every Gaussian.
 """
 import numpy as np
 import pytest
@@ -69,9 +72,14 @@ def test_1m_1080p_4views(env, scene_1m, mode):
     else:
         r.forward()
         r.backward(r.loss_grad(1.0))
+    r.project_backward()
     torch.cuda.synchronize()
     for v in range(r.V):
         full_view_check(env, r, scene_1m, st, mode, v, check_projection=(mode == "fused"))
+    # projection backward of all 1M Gaussians over the 4 views
+    vws = [(scene_1m.cameras[v], r.projected_host(v)["vis_ids"]) for v in range(r.V)]
+    parity.compare_project_backward(oracle, scene_1m, st, vws, [r.grads_host(v) for v in range(r.V)],
+                                    r.grads3d_host())
 
 
 def psnr(a, b):
@@ -120,6 +128,7 @@ def test_40m_4k_4views_sampled(env):
     r.project()
     r.bin()
     r.fused(scale=1.0, image=True)
+    r.project_backward()
     torch.cuda.synchronize()
     print(f"[parity] 40M: visible {[r.info.vis_count[v] for v in range(r.V)]}, instances {r.info.num_instances}",
           flush=True)
@@ -154,3 +163,7 @@ def test_40m_4k_4views_sampled(env):
             dldc, extra = oracle.loss_grad_l1(f["image"], sc.target[v], 1.0, f["err_C"])
             parity.compare_backward(oracle, cam, st, rec, b["ranges"], b["vals"], dldc, r.grads_host(v), f,
                                     region=region, extra_skip=extra, slots_rect=gpu["rect"])
+    # projection backward on the sampled Gaussians (the GPU's 2D gradients of all four views)
+    vws = [(sc.cameras[v], r.projected_host(v)["vis_ids"]) for v in range(r.V)]
+    parity.compare_project_backward(oracle, sc, st, vws, [r.grads_host(v) for v in range(r.V)], r.grads3d_host(),
+                                    sample=sample)

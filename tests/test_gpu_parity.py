@@ -217,7 +217,10 @@ def test_outputs_are_deterministic(env):
     # repeated runs may differ in the last bits only
     for g0, g1 in zip(out[0][4], out[1][4]):
         for k in g0:
-            assert np.allclose(g0[k], g1[k], rtol=1e-5, atol=1e-7), k
+            diff = float(np.abs(g0[k].astype(np.float64) - g1[k]).max())
+            scale = float(np.abs(g0[k]).max())
+            print(f"[determinism] {k}: max run-to-run difference {diff:.3g} (max |g| {scale:.3g})", flush=True)
+            assert diff <= 1e-5 * scale + 1e-7, k
 
 
 def test_scene_100k_720p_external_gradient(env):
@@ -238,3 +241,53 @@ def test_tile_order_is_a_heavy_first_permutation(env):
     n = (rng[:, 1] - rng[:, 0])[order]
     bucket = np.floor(np.log2(n + 1.0))
     assert (np.diff(bucket) <= 0).all()
+
+
+def _project_bwd_check(env, sc, st, r):
+    oracle, pipeline, torch = env
+    torch.cuda.synchronize()
+    vws = [(sc.cameras[v], r.projected_host(v)["vis_ids"]) for v in range(r.V)]
+    return parity.compare_project_backward(oracle, sc, st, vws, [r.grads_host(v) for v in range(r.V)],
+                                           r.grads3d_host())
+
+
+@pytest.mark.parametrize("deg,views,seed", [(0, 1, 31), (1, 2, 32), (3, 3, 33)])
+def test_project_backward_after_fused_raster(env, deg, views, seed):
+    """The projection backward chained after the fused rasterizer, compared with the oracle's chain
+    rule on the GPU's own 2D gradients."""
+    oracle, pipeline, torch = env
+    sc = scenes.random_scene(6000 + 37, 200, 136, seed=seed, views=views, sh_degree=deg, log_scale_mean=-3.0)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.iteration(mode="fused", project_bwd=True)
+    _project_bwd_check(env, sc, st, r)
+
+
+def test_project_backward_random_gradients_and_culled_view(env):
+    """Seeded random 2D gradients on every visible slot (not only the ones the rasterizer
+    reaches), a ragged Gaussian count, one view that sees nothing, and Gaussians no view sees
+    (their parameter gradients must be exactly zero)."""
+    oracle, pipeline, torch = env
+    n = 2 * 256 + 77
+    sc = scenes.random_scene(n, 96, 80, seed=44, views=2, sh_degree=3, log_scale_mean=-2.5)
+    # a third camera looking away from every Gaussian
+    sc.cameras.append(scenes.look_at_camera(96, 80, (0.0, 0.0, 0.0), (0.0, 0.0, -5.0), (0.0, 1.0, 0.0)))
+    # far outside the first two frusta and behind the third camera: seen by no view
+    sc.means[:, :20] = np.array([[50.0], [0.0], [3.0]], np.float32)
+    sc.target = np.zeros((3, 3, 80, 96), np.float32)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.project()
+    torch.cuda.synchronize()
+    assert int(r.vis_count[2].item()) == 0
+    rng = np.random.default_rng(8)
+    for t, k in ((r.d_mean2d, 2), (r.d_conic, 3), (r.d_opacity, 1), (r.d_color, 3)):
+        vals = rng.standard_normal(t.numel()).astype(np.float32)
+        if t is r.d_conic:
+            vals *= np.float32(0.05)
+        t.copy_(torch.from_numpy(vals).to(t.device))
+    r.project_backward()
+    g3 = r.grads3d_host()
+    for key, arr in g3.items():
+        assert np.all(arr[..., :20] == 0.0), key
+    _project_bwd_check(env, sc, st, r)
