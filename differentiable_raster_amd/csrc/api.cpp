@@ -170,6 +170,7 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     if (st != GS_OK) return st;
     if ((st = check_params(p)) != GS_OK) return st;
     if ((st = check_projected(proj, true)) != GS_OK) return st;
+    if (!proj->raster_rec) return fail(GS_ERR_INVALID_ARGUMENT, "projected raster_rec is null");
     if (!bins) return fail(GS_ERR_INVALID_ARGUMENT, "bins is null");
     const int32_t* ranges = use_capped ? bins->ranges_capped : bins->ranges;
     const int32_t* vals = use_capped ? bins->vals_capped : bins->vals;
@@ -184,13 +185,10 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     ra->p = to_dev(p);
     ra->ranges = ranges;
     ra->vals = vals;
-    ra->mean2d = reinterpret_cast<const float2*>(proj->mean2d);
-    ra->conic_opacity = reinterpret_cast<const float4*>(proj->conic_opacity);
-    ra->color = proj->color;
+    ra->rec = reinterpret_cast<const float4*>(proj->raster_rec);
     ra->vis_count = proj->vis_count;
     ra->tile_order = bins->tile_order;
-    ra->tile_rect = reinterpret_cast<const ushort4*>(proj->tile_rect);
-    ra->slot_offset = bins->slot_offset;
+    ra->inst_base = proj->inst_base;
     ra->n_tiles = proj->n_tiles;
     ra->partials = nullptr;
     ra->num_instances = bins->count;
@@ -200,8 +198,8 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
 
 // The backward's partial-record workspace and the bins/projection fields it needs.
 gs_status check_partials(const gs_projected* proj, const gs_bins* bins, void* ws, size_t ws_bytes, RasterArgs* ra) {
-    if (!proj->tile_rect || !proj->n_tiles || !bins->slot_offset)
-        return fail(GS_ERR_INVALID_ARGUMENT, "tile_rect / n_tiles / slot_offset are null");
+    if (!proj->n_tiles || !proj->inst_base)
+        return fail(GS_ERR_INVALID_ARGUMENT, "n_tiles / inst_base are null");
     if (bins->count < 0 || bins->count > bins->capacity)
         return fail(GS_ERR_INVALID_ARGUMENT, "bins->count %lld outside [0, capacity]", (long long)bins->count);
     const size_t need = sizeof(float) * 9 * (size_t)bins->count;
@@ -257,8 +255,10 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
         return fail(GS_ERR_INVALID_ARGUMENT, "a parameter array is null");
     if ((st = check_projected(out, true)) != GS_OK) return st;
-    if (!out->vis_ids || !out->depth || !out->tile_rect || !out->n_tiles)
+    if (!out->vis_ids || !out->depth || !out->tile_rect || !out->n_tiles || !out->inst_base || !out->raster_rec)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected outputs are null");
+    if (reinterpret_cast<uintptr_t>(out->raster_rec) % 64 != 0)
+        return fail(GS_ERR_INVALID_ARGUMENT, "raster_rec is not 64-byte aligned");
     if (out->capacity < g->n) return fail(GS_ERR_INVALID_ARGUMENT, "capacity %d < n %d", out->capacity, g->n);
     if ((int64_t)out->capacity * V >= (int64_t(1) << 31))
         return fail(GS_ERR_INVALID_ARGUMENT, "capacity * V must stay below 2^31");
@@ -284,11 +284,14 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     a.depth = out->depth;
     a.tile_rect = reinterpret_cast<ushort4*>(out->tile_rect);
     a.n_tiles = out->n_tiles;
+    a.inst_base = out->inst_base;
+    a.raster_rec = reinterpret_cast<float4*>(out->raster_rec);
     const int32_t nb = (g->n + 255) / 256 > 0 ? (g->n + 255) / 256 : 1;
     Carver c(ws);
-    a.block_counts = c.take<int32_t>((size_t)nb * V);
-    a.block_offsets = c.take<int32_t>((size_t)nb * V);
-    a.scan_partials = c.take<int32_t>(scan_partials_bytes(nb, V) / sizeof(int32_t));
+    a.block_counts = c.take<int32_t>((size_t)nb * 2 * V);
+    a.block_offsets = c.take<int32_t>((size_t)nb * 2 * V);
+    a.row_totals = c.take<int32_t>((size_t)2 * V);
+    a.scan_partials = c.take<int32_t>(scan_partials_bytes(nb, 2 * V) / sizeof(int32_t));
     return hip_check(launch_project(a, static_cast<hipStream_t>(stream)), "gs_project launch");
 }
 
@@ -357,7 +360,7 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
     if ((st = check_projected(proj, true)) != GS_OK) return st;
     if (!proj->depth || !proj->tile_rect || !proj->n_tiles)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected depth/rect/n_tiles are null");
-    if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges || !bins->slot_offset)
+    if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges)
         return fail(GS_ERR_INVALID_ARGUMENT, "bins outputs are null");
     if (p->tile_cap > 0 && (!bins->vals_capped || !bins->ranges_capped || !bins->num_capped))
         return fail(GS_ERR_INVALID_ARGUMENT, "capped outputs are null while tile_cap > 0");
@@ -428,7 +431,7 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         uint32_t* v1 = odd ? reinterpret_cast<uint32_t*>(bins->vals) : w.tval_alt;
         if (e == hipSuccess)
             e = launch_emit(packed, w.offsets, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity, nvis,
-                            tiles_x, tpv, (int32_t)M, k0, reinterpret_cast<int32_t*>(v0), bins->slot_offset, s);
+                            tiles_x, tpv, (int32_t)M, k0, reinterpret_cast<int32_t*>(v0), s);
         if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
         if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);
     }

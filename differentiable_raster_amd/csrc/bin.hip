@@ -1,9 +1,5 @@
 // A2-A6: tile binning of the visible slots of all views.
 //
-// Emission order (depth order of the slots, then each slot's tiles row-major in its rectangle)
-// also names every (slot, tile) instance: the emission index slot_offset[slot] + k.  The
-// backward uses it to give each instance its own gradient record.
-//
 // The (view, tile, depth, slot) order is produced by an LSD radix sort whose depth digits run
 // first, over one entry per visible slot (key = float32 bits of camera-space z, value =
 // view << 28 | slot, input in (view, slot) order); each slot then emits its tile instances in
@@ -48,14 +44,13 @@ __global__ __launch_bounds__(kBlock) void gather_ntiles_kernel(const uint32_t* p
 __global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* offsets, const ushort4* rect,
                                                       int32_t capacity, int32_t total, int32_t tiles_x,
                                                       int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                                                      int32_t* vals, int32_t* slot_offset) {
+                                                      int32_t* vals) {
     const int32_t r = blockIdx.x * kBlock + threadIdx.x;
     if (r >= total) return;
     const uint32_t p = packed[r];
     const uint32_t v = p >> kSlotBits, slot = p & kSlotMask;
     const ushort4 rc = rect[(size_t)v * capacity + slot];
     int32_t o = offsets[r];
-    slot_offset[(size_t)v * capacity + slot] = o;
     const uint32_t vbase = v * (uint32_t)tiles_per_view;
     for (int ty = rc.y; ty <= rc.w; ty++)
         for (int tx = rc.x; tx <= rc.z; tx++) {
@@ -223,10 +218,10 @@ hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, 
 
 hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
                        int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                       int32_t* vals, int32_t* slot_offset, hipStream_t s) {
+                       int32_t* vals, hipStream_t s) {
     if (total <= 0) return hipSuccess;
     hipLaunchKernelGGL(emit_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, packed, offsets, rect, capacity,
-                       total, tiles_x, tiles_per_view, M, tile_keys, vals, slot_offset);
+                       total, tiles_x, tiles_per_view, M, tile_keys, vals);
     return hipGetLastError();
 }
 

@@ -74,11 +74,13 @@ struct ProjectArgs {
     float* depth;
     ushort4* tile_rect;
     int32_t* n_tiles;
+    int32_t* inst_base;
+    float4* raster_rec;      // [V][capacity][4]
     // workspace
-    int32_t* block_counts;   // [V][nb]
-    int32_t* block_offsets;  // [V][nb]
+    int32_t* block_counts;   // [2V][nb]: visible slots per block (rows 0..V-1), then instances per block
+    int32_t* block_offsets;  // [2V][nb]: exclusive scans of the rows of block_counts
+    int32_t* row_totals;     // [2V]: visible slots per view, then instances per view
     int32_t* scan_partials;  // scan workspace
-    int64_t* inst_accum;     // [V]
 };
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 size_t project_ws_bytes(int32_t n, int32_t V);
@@ -123,7 +125,7 @@ hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, 
                                 int32_t* out, hipStream_t s);
 hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
                        int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                       int32_t* vals, int32_t* slot_offset, hipStream_t s);
+                       int32_t* vals, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
 hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s);
 // Heavy-first permutation of the tiles (stable radix pass on a 5-bit length bucket).
@@ -141,13 +143,10 @@ struct RasterArgs {
     ParamsDev p;
     const int32_t* ranges;   // [V*T][2]
     const int32_t* vals;
-    const float2* mean2d;
-    const float4* conic_opacity;
-    const float* color;
+    const float4* rec;           // [V][capacity][4] packed records (x y A B | C o r g | b rect rect base | ...)
     const int32_t* vis_count;
     const int32_t* tile_order;   // optional: workgroup -> global tile (heavy tiles first)
-    const ushort4* tile_rect;    // backward: instance index of (slot, tile)
-    const int32_t* slot_offset;  // backward: first emission index of each slot
+    const int32_t* inst_base;    // backward: first instance index of each slot
     const int32_t* n_tiles;      // backward: instances per slot
     float* partials;             // backward: [instances][9] per-instance gradient records
     int64_t num_instances;       // backward: records in use

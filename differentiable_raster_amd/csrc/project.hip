@@ -7,7 +7,9 @@
 //   an exclusive scan of the block counts gives each block its first slot per view;
 //   pass 2 recomputes the same decisions (same code, same rounding) and writes the records of
 //          visible Gaussians at slot = block offset + rank within the block, so slots follow
-//          ascending Gaussian index.
+//          ascending Gaussian index, together with each slot's instance base (the same scan
+//          over the blocks' tile-instance counts, plus a wave scan inside the block) and the
+//          packed 64-byte record the rasterizers stage with one line per list entry.
 // Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read only for
 // Gaussians that pass every geometric test in a view; later views hit the cache.
 #include "common.h"
@@ -122,7 +124,7 @@ __device__ bool project_view(const ProjectArgs& a, const Geo& g, const CamDev& c
 
 __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
     __shared__ int s_cnt[kBlock / kWave];
-    __shared__ unsigned long long s_inst[kBlock / kWave];
+    __shared__ int s_inst[kBlock / kWave];
     const int i = blockIdx.x * kBlock + threadIdx.x;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     Geo g;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
         r.ntiles = 0;
         const bool vis = (i < a.n) && project_view(a, g, a.cams.c[v], i, r);
         const unsigned long long m = __ballot(vis);
-        unsigned long long nt = vis ? (unsigned long long)r.ntiles : 0ull;
+        int nt = vis ? r.ntiles : 0;
         for (int o = kWave / 2; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
         if (lane == 0) {
             s_cnt[w] = __popcll(m);
@@ -142,14 +144,14 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            int c = 0;
-            unsigned long long t = 0;
+            int c = 0, t = 0;
             for (int k = 0; k < kBlock / kWave; k++) {
                 c += s_cnt[k];
                 t += s_inst[k];
             }
             a.block_counts[v * nb + blockIdx.x] = c;
-            if (t) atomicAdd((unsigned long long*)&a.inst_count[v], t);
+            a.block_counts[(a.V + v) * nb + blockIdx.x] = t;
+            if (t) atomicAdd((unsigned long long*)&a.inst_count[v], (unsigned long long)t);
         }
         __syncthreads();
     }
@@ -157,23 +159,40 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
 
 __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     __shared__ int s_cnt[kBlock / kWave];
+    __shared__ int s_inst[kBlock / kWave];
     const int i = blockIdx.x * kBlock + threadIdx.x;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    if (blockIdx.x == 0 && threadIdx.x < a.V) a.vis_count[threadIdx.x] = a.row_totals[threadIdx.x];
     Geo g;
     g.ok = false;
     if (i < a.n) g = load_geo(a, i);
     const int nb = gridDim.x;
+    int view_inst = 0;  // instances of the earlier views
     for (int v = 0; v < a.V; v++) {
         Rec r;
+        r.ntiles = 0;
         const bool vis = (i < a.n) && project_view(a, g, a.cams.c[v], i, r);
         const unsigned long long m = __ballot(vis);
+        // inclusive scan of the tile counts over the wave
+        const int nt = vis ? r.ntiles : 0;
+        int inc = nt;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
         if (lane == 0) s_cnt[w] = __popcll(m);
+        if (lane == kWave - 1) s_inst[w] = inc;
         __syncthreads();
         int off = a.block_offsets[v * nb + blockIdx.x];
-        for (int k = 0; k < w; k++) off += s_cnt[k];
+        int ioff = view_inst + a.block_offsets[(a.V + v) * nb + blockIdx.x];
+        for (int k = 0; k < w; k++) {
+            off += s_cnt[k];
+            ioff += s_inst[k];
+        }
         __syncthreads();
         if (vis) {
             const int slot = off + __popcll(m & ((1ull << lane) - 1ull));
+            const int base = ioff + inc - nt;
             const size_t idx = (size_t)v * a.capacity + slot;
             a.vis_ids[idx] = i;
             a.mean2d[idx] = r.xy;
@@ -184,7 +203,15 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
             a.depth[idx] = r.depth;
             a.tile_rect[idx] = r.rect;
             a.n_tiles[idx] = r.ntiles;
+            a.inst_base[idx] = base;
+            float4* rec = a.raster_rec + 4 * idx;
+            rec[0] = make_float4(r.xy.x, r.xy.y, r.co.x, r.co.y);
+            rec[1] = make_float4(r.co.z, r.co.w, r.rgb.x, r.rgb.y);
+            rec[2] = make_float4(r.rgb.z, __int_as_float((int)r.rect.x | ((int)r.rect.y << 16)),
+                                 __int_as_float((int)r.rect.z | ((int)r.rect.w << 16)), __int_as_float(base));
+            rec[3] = make_float4(r.depth, __int_as_float(r.ntiles), 0.0f, 0.0f);
         }
+        view_inst += a.row_totals[a.V + v];
     }
 }
 
@@ -201,7 +228,8 @@ static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t project_ws_bytes(int32_t n, int32_t V) {
     const int32_t nb = project_blocks(n > 0 ? n : 1);
-    return 2 * align256(sizeof(int32_t) * (size_t)nb * V) + align256(scan_partials_bytes(nb, V));
+    return 2 * align256(sizeof(int32_t) * (size_t)nb * 2 * V) + align256(sizeof(int32_t) * 2 * V) +
+           align256(scan_partials_bytes(nb, 2 * V));
 }
 
 hipError_t launch_project(const ProjectArgs& a0, hipStream_t s) {
@@ -209,7 +237,7 @@ hipError_t launch_project(const ProjectArgs& a0, hipStream_t s) {
     const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
     hipLaunchKernelGGL(zero_i64_kernel, dim3(1), dim3(64), 0, s, a.inst_count, a.V);
     hipLaunchKernelGGL(project_count_kernel, dim3(nb), dim3(kBlock), 0, s, a);
-    hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.vis_count, nb, a.V, a.scan_partials, s);
+    hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nb, 2 * a.V, a.scan_partials, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(project_write_kernel, dim3(nb), dim3(kBlock), 0, s, a);
     return hipGetLastError();

@@ -11,7 +11,8 @@
 //  * the per-Gaussian frame (activations, rotation, world covariance) and the colour before its
 //    clamp come from the same device functions as the forward projection, so the colour clamp
 //    takes the forward's decision;
-//  * per view: conic -> dilated 2D covariance (the dilation is constant) -> T = J W and the
+//  * per view: conic -> dilated 2D covariance (the dilation is constant; the derivative of the
+//    inverse, -M G M, in terms of the conic M) -> T = J W and the
 //    world covariance -> J(t) and the projected centre -> camera-space t -> mean; the world
 //    covariance gradient is accumulated over views as a symmetric 3x3 and turned into scale and
 //    rotation gradients once; colour -> SH coefficients and, through the viewing direction,
@@ -130,12 +131,16 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
         const float cc = fmaf(T1[0], Vv[0], fmaf(T1[1], Vv[1], T1[2] * Vv[2])) + a.p.eps2d;
         const float det = ca * cc - cb * cb;
         const float idet = 1.0f / det;
-        const float idet2 = idet * idet;
+        // the conic as the forward stores it: M = [[A, B], [B, C]] = Sigma'^-1
+        const float A = cc * idet, B = -cb * idet, C = ca * idet;
 
-        // conic (A, B, C) = (cc, -cb, ca) / det  ->  (ca, cb, cc)
-        const float ga = (-cc * cc * gA + cb * cc * gB - cb * cb * gC) * idet2;
-        const float gb = (2.0f * cb * cc * gA - (det + 2.0f * cb * cb) * gB + 2.0f * ca * cb * gC) * idet2;
-        const float gcc = (-cb * cb * gA + ca * cb * gB - ca * ca * gC) * idet2;
+        // M = Sigma'^-1  ->  dL/dSigma' = -M G M with G = [[gA, gB/2], [gB/2, gC]]; the
+        // off-diagonal entry appears twice in Sigma', so its gradient is twice the matrix entry.
+        // (Written with the conic rather than 1/det^2, whose square can leave float32 range for
+        // Gaussians just beyond the near plane and far off axis.)
+        const float ga = -(A * A * gA + A * B * gB + B * B * gC);
+        const float gb = -(2.0f * A * B * gA + (A * C + B * B) * gB + 2.0f * B * C * gC);
+        const float gcc = -(B * B * gA + B * C * gB + C * C * gC);
 
         // Sigma2D = T Sigma T^T: gradients of the rows of T and (symmetrized) of Sigma
         float gT0[3], gT1[3];

@@ -23,8 +23,9 @@
 // (1 - alpha) and carrying the colour behind.  A row sums each entry's nine gradient components
 // over its 16 lanes with four DPP adds each and adds the sums into per-entry accumulators in LDS
 // (ds_add_f32); after each batch one thread per entry stores its sums as that (Gaussian, tile)
-// instance's partial record, and a per-Gaussian pass adds up each Gaussian's records: the
-// gradients need no global atomics and every record is written once.  The fused
+// instance's partial record (instances numbered slot by slot, so a Gaussian's records are
+// contiguous), and a per-Gaussian pass adds up each Gaussian's records: the gradients need no
+// global atomics and every record is written once.  The fused
 // kernel runs both passes on one workgroup: per-pixel C, T and n_contrib stay in registers, dL/dC
 // is formed in registers, and the last staged forward batch (which holds the last blended entry
 // of every pixel of the tile) is reused as the first backward batch.
@@ -89,7 +90,7 @@ struct Batch {
     float2 xy[kBatch];      // projected centre
     float4 q[kBatch];       // (a, b, c, thr): p2 = a dx^2 + b dx dy + c dy^2, blend iff p2 >= thr
     float4 oc[kBatch];      // (o, r, g, b)
-    int32_t inst[kBatch];   // emission index of the (slot, tile) instance (backward only)
+    int32_t inst[kBatch];   // index of the (slot, tile) instance (backward only)
     uint16_t mask[kBatch];  // 4x4 blocks of the tile the entry's alpha_min box touches
     uint8_t list[kBlocks4][kBatch];
 };
@@ -99,22 +100,25 @@ struct Acc {
     float v[9][kBatch];
 };
 
-// Stage list position j of the tile into batch index k (one thread per entry).  INST: also the
-// instance's emission index, slot_offset[slot] + (row-major index of this tile in the slot's
-// rectangle), where the backward stores the instance's gradient record.
+// Stage list position j of the tile into batch index k (one thread per entry): three 16-byte
+// loads from the slot's packed 64-byte record.  INST: also the instance's index, inst_base +
+// (row-major index of this tile in the slot's rectangle), where the backward stores the
+// instance's gradient record.
 template <bool INST>
 __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Batch& b, int k, int32_t j) {
     const int32_t slot = a.vals[c.start + j];
-    const size_t idx = c.vbase + slot;
-    const float2 xy = a.mean2d[idx];
-    const float4 co = a.conic_opacity[idx];
+    const float4* r = a.rec + 4 * (c.vbase + slot);
+    const float4 r0 = r[0], r1 = r[1], r2 = r[2];  // (x, y, A, B), (C, o, r, g), (b, rect, rect, base)
+    const float2 xy = make_float2(r0.x, r0.y);
+    const float4 co = make_float4(r0.z, r0.w, r1.x, r1.y);
     const float amin = a.p.alpha_min;
     b.xy[k] = xy;
     b.q[k] = make_float4(-0.5f * kLog2e * co.x, -kLog2e * co.y, -0.5f * kLog2e * co.z, __log2f(amin / co.w));
-    b.oc[k] = make_float4(co.w, a.color[3 * idx], a.color[3 * idx + 1], a.color[3 * idx + 2]);
+    b.oc[k] = make_float4(co.w, r1.z, r1.w, r2.x);
     if (INST) {
-        const ushort4 rc = a.tile_rect[idx];
-        b.inst[k] = a.slot_offset[idx] + (c.ty - rc.y) * (rc.z - rc.x + 1) + (c.tx - rc.x);
+        const int lo = __float_as_int(r2.y), hi = __float_as_int(r2.z);
+        const int tx0 = lo & 0xFFFF, ty0 = lo >> 16, tx1 = hi & 0xFFFF;
+        b.inst[k] = __float_as_int(r2.w) + (c.ty - ty0) * (tx1 - tx0 + 1) + (c.tx - tx0);
     }
     // conservative block mask from the alpha_min box of the conic (Sigma' = conic^-1)
     uint32_t m = 0xFFFFu;
@@ -347,7 +351,7 @@ __device__ __forceinline__ void flush_batch(const RasterArgs& a, const Batch& b,
             any |= d[t] != 0.0f;
             acc.v[t][k] = 0.0f;
         }
-        // the bound only matters for a projection changed after binning (stale emission indices)
+        // the bound only matters for bins and records of different calls (stale instance indices)
         if (any && (uint64_t)(uint32_t)b.inst[k] < (uint64_t)a.num_instances) {
             float* rec = a.partials + (size_t)b.inst[k] * 9;
 #pragma unroll
@@ -475,16 +479,16 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
 }
 
 // Per-Gaussian gather of the backward: the gradient of a visible slot is the sum of its
-// instances' partial records, which lie contiguously at [slot_offset, slot_offset + n_tiles).
+// instances' partial records, which lie contiguously at [inst_base, inst_base + n_tiles).
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis_count, int32_t V, int32_t capacity,
-                                                              const int32_t* slot_offset, const int32_t* n_tiles,
+                                                              const int32_t* inst_base, const int32_t* n_tiles,
                                                               const float* partials, int64_t num_instances, Grads g) {
     for (int v = 0; v < V; v++) {
         const int32_t cnt = vis_count[v];
         const size_t base = (size_t)v * capacity;
         for (int32_t s = blockIdx.x * 256 + threadIdx.x; s < cnt; s += gridDim.x * 256) {
             const size_t i = base + s;
-            const int64_t off = slot_offset[i];
+            const int64_t off = inst_base[i];
             const float* rec = partials + (size_t)off * 9;
             // clamped to the records that exist (only a stale projection could reach past them)
             const int n = (off < 0 || off > num_instances) ? 0 : (int)min((int64_t)n_tiles[i], num_instances - off);
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const 
 }
 
 template <bool COUNT>
-__global__ __launch_bounds__(kBlock) void raster_fused_kernel(RasterArgs a, int mode, const float* tgt, float scale,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void raster_fused_kernel(RasterArgs a, int mode, const float* tgt, float scale,
                                                               float* image, float* loss_sum, Grads gr) {
     __shared__ Batch b;
     __shared__ Acc acc;
@@ -626,7 +630,7 @@ static hipError_t with_partials(const RasterArgs& a, Grads g, hipStream_t s, Lau
     if (n > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.partials, n);
     launch();
     hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(a.capacity)), dim3(256), 0, s, a.vis_count, a.V,
-                       a.capacity, a.slot_offset, a.n_tiles, a.partials, a.num_instances, g);
+                       a.capacity, a.inst_base, a.n_tiles, a.partials, a.num_instances, g);
     return hipGetLastError();
 }
 

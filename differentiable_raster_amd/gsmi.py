@@ -50,14 +50,13 @@ class gs_projected(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int32), ("vis_count", ctypes.c_void_p), ("inst_count", ctypes.c_void_p),
                 ("vis_ids", ctypes.c_void_p), ("mean2d", ctypes.c_void_p), ("conic_opacity", ctypes.c_void_p),
                 ("color", ctypes.c_void_p), ("depth", ctypes.c_void_p), ("tile_rect", ctypes.c_void_p),
-                ("n_tiles", ctypes.c_void_p)]
+                ("n_tiles", ctypes.c_void_p), ("inst_base", ctypes.c_void_p), ("raster_rec", ctypes.c_void_p)]
 
 
 class gs_bins(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int64), ("count", ctypes.c_int64), ("tile_keys", ctypes.c_void_p),
                 ("vals", ctypes.c_void_p), ("ranges", ctypes.c_void_p), ("vals_capped", ctypes.c_void_p),
-                ("ranges_capped", ctypes.c_void_p), ("num_capped", ctypes.c_void_p), ("tile_order", ctypes.c_void_p),
-                ("slot_offset", ctypes.c_void_p)]
+                ("ranges_capped", ctypes.c_void_p), ("num_capped", ctypes.c_void_p), ("tile_order", ctypes.c_void_p)]
 
 
 class gs_bin_info(ctypes.Structure):

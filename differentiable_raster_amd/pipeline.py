@@ -51,16 +51,17 @@ class Renderer:
         self.depth = torch.empty(V * cap, dtype=f32, device=dev)
         self.tile_rect = torch.empty(V * cap * 4, dtype=torch.int16, device=dev)
         self.n_tiles = torch.empty(V * cap, dtype=i32, device=dev)
+        self.inst_base = torch.empty(V * cap, dtype=i32, device=dev)
+        self.raster_rec = torch.empty(V * cap * 16, dtype=f32, device=dev)  # torch allocations are 256-B aligned
         self.proj = gsmi.gs_projected(cap, self.vis_count.data_ptr(), self.inst_count.data_ptr(),
                                       self.vis_ids.data_ptr(), self.mean2d.data_ptr(), self.conic_opacity.data_ptr(),
                                       self.color.data_ptr(), self.depth.data_ptr(), self.tile_rect.data_ptr(),
-                                      self.n_tiles.data_ptr())
+                                      self.n_tiles.data_ptr(), self.inst_base.data_ptr(), self.raster_rec.data_ptr())
         self.ws_proj = torch.empty(gsmi.gs_project_workspace_size(self.n, V), dtype=torch.uint8, device=dev)
         self.ranges = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
         self.ranges_capped = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
         self.num_capped = torch.zeros(1, dtype=i32, device=dev)
         self.tile_order = torch.zeros(V * self.tpv, dtype=i32, device=dev)
-        self.slot_offset = torch.zeros(V * cap, dtype=i32, device=dev)
         self.inst_capacity = -1
         self._alloc_bins(instance_capacity if instance_capacity is not None else 0)
         plane = self.H * self.W
@@ -90,7 +91,7 @@ class Renderer:
         self.vals_capped = torch.empty(c, dtype=torch.int32, device=dev)
         self.bins = gsmi.gs_bins(c, 0, self.tile_keys.data_ptr(), self.vals.data_ptr(), self.ranges.data_ptr(),
                                  self.vals_capped.data_ptr(), self.ranges_capped.data_ptr(), self.num_capped.data_ptr(),
-                                 self.tile_order.data_ptr(), self.slot_offset.data_ptr())
+                                 self.tile_order.data_ptr())
         self.ws_raster = torch.empty(gsmi.gs_raster_workspace_size(c), dtype=torch.uint8, device=dev)
         self.ws_bin = torch.empty(gsmi.gs_bin_workspace_size(self.capacity, self.V, self.W, self.H, c),
                                   dtype=torch.uint8, device=dev)
@@ -183,6 +184,8 @@ class Renderer:
             depth=self.depth[sl].cpu().numpy(),
             rect=self.tile_rect.view(-1, 4)[sl].cpu().numpy().astype(np.int32) & 0xFFFF,
             n_tiles=self.n_tiles[sl].cpu().numpy(),
+            inst_base=self.inst_base[sl].cpu().numpy(),
+            raster_rec=self.raster_rec.view(-1, 16)[sl].cpu().numpy(),
         )
 
     def bins_host(self, v: int, capped: bool = False) -> dict:

@@ -98,6 +98,14 @@ typedef struct {
     float* depth;             /* [V][capacity]    camera-space z */
     uint16_t* tile_rect;      /* [V][capacity][4] (tx0, ty0, tx1, ty1), inclusive */
     int32_t* n_tiles;         /* [V][capacity]    tiles in the rectangle */
+    int32_t* inst_base;       /* [V][capacity]    first index of the slot's (Gaussian, tile) instances
+                                 when the instances of all views are numbered view by view, slot by
+                                 slot, and within a slot row-major over its tile rectangle: the sum
+                                 of n_tiles over every earlier (view, slot) */
+    float* raster_rec;        /* [V][capacity][16] the record the rasterizers read, packed into one
+                                 64-byte line per slot (256-byte aligned array): x, y, A, B, C, o,
+                                 r, g, b, then as 32-bit patterns tx0 | ty0 << 16, tx1 | ty1 << 16,
+                                 inst_base, then depth, n_tiles (32-bit pattern), 0, 0 */
 } gs_projected;
 
 /* Tile bins of all views of one call.  Global tile id = v * tiles_per_view + ty * tiles_x + tx.
@@ -117,11 +125,6 @@ typedef struct {
                                    the global tiles, longest lists first, written by gs_bin_tiles
                                    and used by the raster calls to schedule heavy tiles early;
                                    the order changes no result */
-    int32_t* slot_offset;       /* [V][proj->capacity] written by gs_bin_tiles: the first index of
-                                   each visible slot's instances in emission order; instance k of
-                                   a slot (its k-th tile, row-major in its rectangle) has index
-                                   slot_offset + k.  The backward calls place per-instance gradient
-                                   partials there. */
 } gs_bins;
 
 /* Host-side counts that gs_bin_tiles reports. */
@@ -176,7 +179,8 @@ size_t gs_project_workspace_size(int32_t n, int32_t V);
  * to the image, and its tile rectangle.  Gaussians with any non-finite input or derived value,
  * det <= 0, o <= alpha_min or an empty box are culled (per-view frustum culling as in GS-Scale,
  * arXiv 2509.15645, English abstract).  Visible Gaussians are compacted into slots in ascending
- * index order.  Parameters are read once for all V views.
+ * index order.  Besides the per-field arrays, every visible slot gets its instance base and the
+ * packed 64-byte rasterizer record.  Parameters are read once for all V views.
  * Errors: GS_ERR_INVALID_ARGUMENT for null pointers, n < 0, V outside 1..GS_MAX_VIEWS,
  * capacity < n, sh_degree outside 0..3, non-positive image sizes or differing image sizes
  * between views; GS_ERR_CAPACITY if ws_bytes is too small.
@@ -235,9 +239,9 @@ gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float*
  * and unless alpha was clamped, dL/do = G dL/dalpha, dL/dmean2d = o G dL/dalpha (A dx + B dy,
  * B dx + C dy) with d = pixel centre - mean2d, dL/d(A,B,C) = o G dL/dalpha (-dx^2/2, -dx dy,
  * -dy^2/2).  Within a tile, each entry's contributions are summed over the pixels in LDS and
- * stored once, without atomics, as a partial record at the instance's emission index (see
- * gs_bins.slot_offset) in the workspace; a per-Gaussian pass then sums each slot's partials into
- * grads.  ws: gs_raster_workspace_size(bins->capacity) bytes, 256-byte aligned.
+ * stored once, without atomics, as a partial record at the instance's index (see
+ * gs_projected.inst_base) in the workspace; a per-Gaussian pass then sums each slot's partials
+ * into grads.  ws: gs_raster_workspace_size(bins->count) bytes or more, 256-byte aligned.
  */
 gs_status gs_raster_bwd(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
                         int32_t V, const gs_render_params* p, int32_t use_capped, const float* image,

@@ -414,14 +414,17 @@ void orc_project_backward(int64_t n, const double* means, const double* log_scal
                 S2[2 * r + c] = acc;
             }
         const double a = S2[0] + p->eps2d, b = S2[1], c = S2[3] + p->eps2d;
-        const double det = a * c - b * b, det2 = det * det;
+        const double det = a * c - b * b;
+        const double A = c / det, B = -b / det, C = a / det;
 
-        /* conic (A, B, C) = (c, -b, a) / det  ->  dilated covariance (a, b, c); the dilation
-         * is a constant, so these are also the gradients of Sigma2D's xx, xy, yy entries */
+        /* conic M = [[A, B], [B, C]] = S^-1 of the dilated covariance S = [[a, b], [b, c]]:
+         * dL/dS = -M G M with G = [[gA, gB/2], [gB/2, gC]] (the derivative of the inverse); the
+         * off-diagonal b appears twice in S, so its gradient is twice the matrix entry.  The
+         * dilation is a constant, so these are also the gradients of Sigma2D's xx, xy, yy. */
         const double gA = g_conic[3 * i], gB = g_conic[3 * i + 1], gC = g_conic[3 * i + 2];
-        const double ga = (-c * c * gA + b * c * gB - b * b * gC) / det2;
-        const double gb = (2.0 * b * c * gA - (det + 2.0 * b * b) * gB + 2.0 * a * b * gC) / det2;
-        const double gc = (-b * b * gA + a * b * gB - a * a * gC) / det2;
+        const double ga = -(A * A * gA + A * B * gB + B * B * gC);
+        const double gb = -(2.0 * A * B * gA + (A * C + B * B) * gB + 2.0 * B * C * gC);
+        const double gc = -(B * B * gA + B * C * gB + C * C * gC);
 
         /* Sigma2D = T Sigma T^T with xx = T0 Sig T0^T, xy = T0 Sig T1^T, yy = T1 Sig T1^T (rows
          * T0, T1 of T): gradients of T and of the nine entries of Sigma */
@@ -635,16 +638,16 @@ void orc_project_backward_errbound(int64_t n, const double* means, const double*
         const ve c = ve_add(ve_dot3(&T[3], Vv), eps);
         const ve det = ve_sub(ve_mul(a, c), ve_mul(b, b));
         const ve idet = ve_div(one, det);
-        const ve idet2 = ve_mul(idet, idet);
+        const ve A = ve_mul(c, idet), B = ve_neg(ve_mul(b, idet)), C = ve_mul(a, idet);
 
         const ve gA = ve_in(g_conic[3 * i]), gB = ve_in(g_conic[3 * i + 1]), gC = ve_in(g_conic[3 * i + 2]);
-        const ve ga = ve_mul(ve_add(ve_sub(ve_mul(ve_mul(b, c), gB), ve_mul(ve_mul(c, c), gA)),
-                                    ve_neg(ve_mul(ve_mul(b, b), gC))), idet2);
-        const ve gb = ve_mul(ve_add(ve_sub(ve_k(2.0, ve_mul(ve_mul(b, c), gA)),
-                                           ve_mul(ve_add(det, ve_k(2.0, ve_mul(b, b))), gB)),
-                                    ve_k(2.0, ve_mul(ve_mul(a, b), gC))), idet2);
-        const ve gc = ve_mul(ve_sub(ve_sub(ve_mul(ve_mul(a, b), gB), ve_mul(ve_mul(b, b), gA)),
-                                    ve_mul(ve_mul(a, a), gC)), idet2);
+        const ve ga = ve_neg(ve_add(ve_add(ve_mul(ve_mul(A, A), gA), ve_mul(ve_mul(A, B), gB)),
+                                    ve_mul(ve_mul(B, B), gC)));
+        const ve gb = ve_neg(ve_add(ve_add(ve_k(2.0, ve_mul(ve_mul(A, B), gA)),
+                                           ve_mul(ve_add(ve_mul(A, C), ve_mul(B, B)), gB)),
+                                    ve_k(2.0, ve_mul(ve_mul(B, C), gC))));
+        const ve gc = ve_neg(ve_add(ve_add(ve_mul(ve_mul(B, B), gA), ve_mul(ve_mul(B, C), gB)),
+                                    ve_mul(ve_mul(C, C), gC)));
 
         ve gT[6], Gs[9];
         for (int k = 0; k < 3; k++) {

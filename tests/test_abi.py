@@ -131,6 +131,13 @@ def test_project_rejects_bad_arguments(gs):
     assert b"capacity" in lib.gs_last_error()
     nulls = projected(gs, null=("mean2d",))
     assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(nulls), FAKE, ws_ok) == 1
+    for f in ("inst_base", "raster_rec"):
+        nulls = projected(gs, null=(f,))
+        assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(nulls), FAKE, ws_ok) == 1
+    skew = projected(gs)
+    skew.raster_rec = FAKE + 16
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(skew), FAKE, ws_ok) == 1
+    assert b"aligned" in lib.gs_last_error()
     g_null = gs.gs_gaussians(100, FAKE, None, FAKE, FAKE, FAKE)
     assert call(ctypes.byref(g_null), c, 1, ctypes.byref(p), ctypes.byref(out), FAKE, ws_ok) == 1
     g_big = gs.gs_gaussians(1 << 28, FAKE, FAKE, FAKE, FAKE, FAKE)
@@ -149,7 +156,7 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     c = cams(gs)
     p = params(gs)
     proj = projected(gs)
-    bins = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    bins = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     info = gs.gs_bin_info()
     req = ctypes.c_int64()
     ws = gs.gs_bin_workspace_size(100, 1, 64, 48, 1000)
@@ -160,7 +167,7 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(p), ctypes.byref(bins), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws - 1, None) == 2
     capped = params(gs, tile_cap=64)
-    nocap = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, None, None, None, None, FAKE)
+    nocap = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, None, None, None, None)
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(capped), ctypes.byref(nocap), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws, None) == 1
     neg = params(gs, tile_cap=-1)

@@ -291,3 +291,29 @@ def test_project_backward_random_gradients_and_culled_view(env):
     for key, arr in g3.items():
         assert np.all(arr[..., :20] == 0.0), key
     _project_bwd_check(env, sc, st, r)
+
+
+def test_packed_records_and_instance_bases(env):
+    """Each visible slot's 64-byte rasterizer record holds exactly the per-field values of the
+    projection, and the instance bases number the instances view by view, slot by slot."""
+    oracle, pipeline, torch = env
+    sc = scenes.random_scene(3000 + 5, 150, 100, seed=55, views=3, sh_degree=1, log_scale_mean=-3.0)
+    r = pipeline.Renderer(sc, sc.settings())
+    r.project()
+    torch.cuda.synchronize()
+    base = 0
+    for v in range(r.V):
+        g = r.projected_host(v)
+        rec = g["raster_rec"]
+        bits = rec.view(np.int32)
+        co, col = g["conic_opacity"], g["color"]
+        assert np.array_equal(rec[:, 0:2], g["mean2d"]) and np.array_equal(rec[:, 2:6], co)
+        assert np.array_equal(rec[:, 6:9], col) and np.array_equal(rec[:, 12], g["depth"])
+        rc = g["rect"]
+        assert np.array_equal(bits[:, 9], rc[:, 0] | (rc[:, 1] << 16))
+        assert np.array_equal(bits[:, 10], rc[:, 2] | (rc[:, 3] << 16))
+        assert np.array_equal(bits[:, 13], g["n_tiles"]) and np.all(bits[:, 14:16] == 0)
+        want = base + np.concatenate([[0], np.cumsum(g["n_tiles"])[:-1]]).astype(np.int64)
+        assert np.array_equal(g["inst_base"], want) and np.array_equal(bits[:, 11], g["inst_base"])
+        base += int(g["n_tiles"].sum())
+        assert g["inst_count"] == int(g["n_tiles"].sum())

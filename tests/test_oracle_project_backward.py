@@ -231,11 +231,12 @@ def _chain_float32(params, cam, vis, g):
     b = (T[1] * U).sum(0, dtype=f)
     c = (T[1] * Vv).sum(0, dtype=f) + eps
     det = a * c - b * b
-    idet2 = (one / det) ** 2
+    idet = one / det
+    A, B, C = c * idet, -b * idet, a * idet
     gA, gB, gC = [np.asarray(g["conic"][:, k], f) for k in range(3)]
-    ga = (-c * c * gA + b * c * gB - b * b * gC) * idet2
-    gb = (two * b * c * gA - (det + two * b * b) * gB + two * a * b * gC) * idet2
-    gc = (-b * b * gA + a * b * gB - a * a * gC) * idet2
+    ga = -(A * A * gA + A * B * gB + B * B * gC)
+    gb = -(two * A * B * gA + (A * C + B * B) * gB + two * B * C * gC)
+    gc = -(B * B * gA + B * C * gB + C * C * gC)
     gT0 = two * ga * U + gb * Vv
     gT1 = gb * U + two * gc * Vv
     Gs = (two * ga * T[0][:, None] * T[0][None] + gb * (T[0][:, None] * T[1][None] + T[1][:, None] * T[0][None])
