@@ -125,6 +125,7 @@ struct BinWs {
     int32_t *hist, *partials;
     int32_t *kept, *cap_offsets;
     uint32_t *order_keys, *order_vals, *order_keys_alt;  // [tiles_total] tile-order sort
+    BinReadback* readback;                               // counts and depth range read by the host
 };
 
 BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t inst_cap, size_t* bytes) {
@@ -154,6 +155,7 @@ BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t ins
     w.order_keys = c.take<uint32_t>(tiles_total);
     w.order_vals = c.take<uint32_t>(tiles_total);
     w.order_keys_alt = c.take<uint32_t>(tiles_total);
+    w.readback = c.take<BinReadback>(1);
     *bytes = c.used;
     return w;
 }
@@ -376,16 +378,18 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
     if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "bin workspace %zu < %zu bytes", ws_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // the one read-back: visible and instance counts of every view
-    int32_t vis[GS_MAX_VIEWS];
-    int64_t inst[GS_MAX_VIEWS];
-    if ((st = hip_check(hipMemcpyAsync(vis, proj->vis_count, sizeof(int32_t) * V, hipMemcpyDeviceToHost, s),
-                        "count read")) != GS_OK)
+    // the one read-back: visible and instance counts of every view and the visible depth range
+    BinWs w = carve_bin(ws, proj->capacity, V, tiles_total, bins->capacity, &need);
+    BinReadback rb;
+    if ((st = hip_check(launch_bin_counts(proj->vis_count, proj->inst_count, V, proj->depth, proj->capacity,
+                                          w.readback, s),
+                        "count launch")) != GS_OK)
         return st;
-    if ((st = hip_check(hipMemcpyAsync(inst, proj->inst_count, sizeof(int64_t) * V, hipMemcpyDeviceToHost, s),
-                        "count read")) != GS_OK)
+    if ((st = hip_check(hipMemcpyAsync(&rb, w.readback, sizeof(rb), hipMemcpyDeviceToHost, s), "count read")) != GS_OK)
         return st;
     if ((st = hip_check(hipStreamSynchronize(s), "count read sync")) != GS_OK) return st;
+    const int32_t* vis = rb.vis;
+    const int64_t* inst = rb.inst;
     std::memset(info, 0, sizeof(*info));
     int64_t total_vis = 0, M = 0;
     for (int v = 0; v < V; v++) {
@@ -405,7 +409,6 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         return fail(GS_ERR_CAPACITY, "%lld instances exceed the bins capacity %lld", (long long)M,
                     (long long)bins->capacity);
 
-    BinWs w = carve_bin(ws, proj->capacity, V, tiles_total, bins->capacity, &need);
     hipError_t e = launch_fill_i32(bins->ranges, 0, 2 * (int64_t)tiles_total, s);
     if (e == hipSuccess && M > 0) {
         // depth digits, one entry per visible slot
@@ -417,9 +420,13 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         }
         first[V] = acc;
         const int32_t nvis = (int32_t)total_vis;
-        e = launch_depth_keys(proj->depth, proj->vis_count, first, V, proj->capacity, nvis, w.dkey, w.dval, s);
-        if (e == hipSuccess) e = launch_radix_sort(w.dkey, w.dval, w.dkey_alt, w.dval_alt, nvis, 32, w.hist, w.partials, s);
-        uint32_t* packed = (radix_passes(32) % 2 == 0) ? w.dval : w.dval_alt;
+        // keys relative to the smallest visible depth: as many bits as the depth range needs
+        const uint32_t key_min = rb.bits[0], key_span = ~rb.bits[1] - rb.bits[0];
+        const int dbits = key_span == 0 ? 0 : 32 - __builtin_clz(key_span);
+        e = launch_depth_keys(proj->depth, first, V, proj->capacity, nvis, key_min, w.dkey, w.dval, s);
+        if (e == hipSuccess)
+            e = launch_radix_sort(w.dkey, w.dval, w.dkey_alt, w.dval_alt, nvis, dbits, w.hist, w.partials, s);
+        uint32_t* packed = (radix_passes(dbits) % 2 == 0) ? w.dval : w.dval_alt;
         if (e == hipSuccess) e = launch_gather_ntiles(packed, proj->n_tiles, proj->capacity, nvis, w.ntiles_sorted, s);
         if (e == hipSuccess) e = launch_scan_rows(w.ntiles_sorted, w.offsets, nullptr, nvis, 1, w.partials, s);
         // emit so that the tile sort's final pass lands in the output buffers

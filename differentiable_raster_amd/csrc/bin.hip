@@ -21,16 +21,59 @@ struct ViewFirst {
     int32_t first[GS_MAX_VIEWS + 1];
 };
 
+// Depth keys relative to the smallest one: the float32 bits of positive depths order like the
+// depths, and subtracting the minimum keeps that order while shortening the keys (fewer passes).
 __global__ __launch_bounds__(kBlock) void depth_keys_kernel(const float* depth, ViewFirst vf, int32_t V,
-                                                            int32_t capacity, int32_t total, uint32_t* keys,
-                                                            uint32_t* vals) {
+                                                            int32_t capacity, int32_t total, uint32_t key_min,
+                                                            uint32_t* keys, uint32_t* vals) {
     const int32_t e = blockIdx.x * kBlock + threadIdx.x;
     if (e >= total) return;
     int v = 0;
     while (v + 1 < V && e >= vf.first[v + 1]) v++;
     const int32_t slot = e - vf.first[v];
-    keys[e] = __float_as_uint(depth[(size_t)v * capacity + slot]);
+    keys[e] = __float_as_uint(depth[(size_t)v * capacity + slot]) - key_min;
     vals[e] = ((uint32_t)v << kSlotBits) | (uint32_t)slot;
+}
+
+// The values the host reads back before sizing the binning launches, packed for one copy: the
+// per-view counts and the range of the visible depths' float32 bits, as bits[0] = the smallest
+// pattern and bits[1] = the complement of the largest (both minima, so that one fill of
+// 0xFFFFFFFF initializes them).
+__global__ __launch_bounds__(kBlock) void bin_counts_kernel(const int32_t* vis_count, const int64_t* inst_count,
+                                                            int32_t V, const float* depth, int32_t capacity,
+                                                            BinReadback* out) {
+    __shared__ uint32_t s_lo[kBlock / 64], s_hi[kBlock / 64];
+    if (blockIdx.x == 0 && threadIdx.x < V) {
+        out->vis[threadIdx.x] = vis_count[threadIdx.x];
+        out->inst[threadIdx.x] = inst_count[threadIdx.x];
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int v = 0; v < V; v++) {
+        const int32_t cnt = min(vis_count[v], capacity);
+        const float* d = depth + (size_t)v * capacity;
+        for (int32_t i = blockIdx.x * kBlock + threadIdx.x; i < cnt; i += gridDim.x * kBlock) {
+            const uint32_t b = __float_as_uint(d[i]);
+            lo = min(lo, b);
+            hi = max(hi, b);
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        s_lo[threadIdx.x / 64] = lo;
+        s_hi[threadIdx.x / 64] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < kBlock / 64; k++) {
+            lo = min(lo, s_lo[k]);
+            hi = max(hi, s_hi[k]);
+        }
+        if (lo != 0xFFFFFFFFu) atomicMin(&out->bits[0], lo);
+        if (hi != 0u) atomicMin(&out->bits[1], ~hi);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void gather_ntiles_kernel(const uint32_t* packed, const int32_t* n_tiles,
@@ -198,13 +241,21 @@ __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* range
 
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
 
-hipError_t launch_depth_keys(const float* depth, const int32_t* /*vis_count*/, const int64_t* view_first, int32_t V,
-                             int32_t capacity, int32_t total, uint32_t* keys, uint32_t* vals, hipStream_t s) {
+hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int32_t V, int32_t capacity,
+                             int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, hipStream_t s) {
     if (total <= 0) return hipSuccess;
     ViewFirst vf;
     for (int v = 0; v <= GS_MAX_VIEWS; v++) vf.first[v] = v <= V ? (int32_t)view_first[v] : total;
     hipLaunchKernelGGL(depth_keys_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, depth, vf, V, capacity, total,
-                       keys, vals);
+                       key_min, keys, vals);
+    return hipGetLastError();
+}
+
+hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count, int32_t V, const float* depth,
+                             int32_t capacity, BinReadback* out, hipStream_t s) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kBlock), 0, s, reinterpret_cast<int32_t*>(out->bits), -1, 2);
+    hipLaunchKernelGGL(bin_counts_kernel, dim3(1024), dim3(kBlock), 0, s, vis_count, inst_count, V, depth, capacity,
+                       out);
     return hipGetLastError();
 }
 

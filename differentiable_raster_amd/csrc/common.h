@@ -118,9 +118,15 @@ size_t radix_hist_bytes(int32_t n);
 size_t radix_partials_bytes(int32_t n);
 
 // Binning helpers.
-hipError_t launch_depth_keys(const float* depth, const int32_t* vis_count, const int64_t* view_first,
-                             int32_t V, int32_t capacity, int32_t total, uint32_t* keys, uint32_t* vals,
-                             hipStream_t s);
+struct BinReadback {
+    int64_t inst[GS_MAX_VIEWS];
+    int32_t vis[GS_MAX_VIEWS];
+    uint32_t bits[2];  // smallest float32 bit pattern of the visible depths, complement of the largest
+};
+hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count, int32_t V, const float* depth,
+                             int32_t capacity, BinReadback* out, hipStream_t s);
+hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int32_t V, int32_t capacity,
+                             int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, hipStream_t s);
 hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity, int32_t total,
                                 int32_t* out, hipStream_t s);
 hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
