@@ -10,8 +10,9 @@
 //          ascending Gaussian index, together with each slot's instance base (the same scan
 //          over the blocks' tile-instance counts, plus a wave scan inside the block) and the
 //          packed 64-byte record the rasterizers stage with one line per list entry.
-// Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read only for
-// Gaussians that pass every geometric test in a view; later views hit the cache.
+// Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read once per Gaussian:
+// the counting pass only checks that they are bounded (which makes every colour finite), and the
+// writing pass keeps them in registers for all views.
 #include "common.h"
 #include "gauss.h"
 
@@ -54,15 +55,19 @@ __device__ Geo load_geo(const ProjectArgs& a, int i) {
     return g;
 }
 
-// Colour before the clamp along unit direction (x, y, z); the DC rows are the base colour.
-__device__ float3 sh_colour(const ProjectArgs& a, int i, float x, float y, float z) {
-    float Y[15];
-    const int nY = sh_basis(a.p.sh_degree, x, y, z, Y);
-    return sh_eval(a.sh + i, a.n, nY, Y);
+// True when every SH coefficient of Gaussian i is finite and at most 1e30 in magnitude.  Every
+// real SH basis value of degree <= 3 on the unit sphere is below 1 in magnitude, so the colour
+// sum of at most 48 such terms then stays below 5e31 at every step of its evaluation: it is
+// finite, and the colour cannot cull the Gaussian in any view.
+__device__ __forceinline__ bool sh_bounded(const ProjectArgs& a, int i, int nk3) {
+    bool ok = true;
+    for (int k = 0; k < nk3; k++) ok = ok && fabsf(a.sh[(size_t)k * a.n + i]) <= 1e30f;
+    return ok;
 }
 
-// All per-view tests and, when visible, the record.  Returns visibility.
-__device__ bool project_view(const ProjectArgs& a, const Geo& g, const CamDev& c, int i, Rec& r) {
+// All per-view tests except the colour's finiteness, and the record without the colour.  Also
+// returns the unit viewing direction.  Returns visibility so far.
+__device__ bool project_geom(const ProjectArgs& a, const Geo& g, const CamDev& c, Rec& r, float3& dir) {
     if (!g.ok) return false;
     const ParamsDev& p = a.p;
     const float tx = fmaf(c.R[0], g.mx, fmaf(c.R[1], g.my, fmaf(c.R[2], g.mz, c.t[0])));
@@ -106,14 +111,11 @@ __device__ bool project_view(const ProjectArgs& a, const Geo& g, const CamDev& c
     const float fu0 = fmaxf(0.0f, ceilf(lox)), fu1 = fminf((float)(c.width - 1), floorf(hix));
     const float fv0 = fmaxf(0.0f, ceilf(loy)), fv1 = fminf((float)(c.height - 1), floorf(hiy));
     if (!(fu0 <= fu1) || !(fv0 <= fv1)) return false;
-    // colour along the viewing direction
-    float dx, dy, dz, idn;
-    if (!view_dir(g.mx, g.my, g.mz, c.campos, &dx, &dy, &dz, &idn)) return false;
-    const float3 col = sh_colour(a, i, dx, dy, dz);
-    if (!(finitef(col.x) && finitef(col.y) && finitef(col.z))) return false;
+    // viewing direction (the colour is evaluated by the caller)
+    float idn;
+    if (!view_dir(g.mx, g.my, g.mz, c.campos, &dir.x, &dir.y, &dir.z, &idn)) return false;
     r.xy = make_float2(mx, my);
     r.co = make_float4(cc * idet, -cb * idet, ca * idet, g.o);
-    r.rgb = make_float3(fmaxf(0.0f, col.x), fmaxf(0.0f, col.y), fmaxf(0.0f, col.z));
     r.depth = tz;
     const int u0i = (int)fu0, u1i = (int)fu1, v0i = (int)fv0, v1i = (int)fv1;
     r.rect = make_ushort4((unsigned short)(u0i / kTile), (unsigned short)(v0i / kTile),
@@ -122,19 +124,39 @@ __device__ bool project_view(const ProjectArgs& a, const Geo& g, const CamDev& c
     return true;
 }
 
+// Whether the colour of Gaussian i along dir is finite (the rare case of unbounded
+// coefficients; kept out of line so that it does not hold registers in the counting loop).
+template <int DEG>
+__device__ __noinline__ bool colour_finite(const ProjectArgs& a, int i, float3 dir) {
+    constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
+    float Y[15];
+    sh_basis(DEG, dir.x, dir.y, dir.z, Y);
+    const float3 col = sh_eval(a.sh + i, a.n, NY, Y);
+    return finitef(col.x) && finitef(col.y) && finitef(col.z);
+}
+
+template <int DEG>
 __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
+    constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
     __shared__ int s_cnt[kBlock / kWave];
     __shared__ int s_inst[kBlock / kWave];
     const int i = blockIdx.x * kBlock + threadIdx.x;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     Geo g;
     g.ok = false;
-    if (i < a.n) g = load_geo(a, i);
+    bool bounded = true;
+    if (i < a.n) {
+        g = load_geo(a, i);
+        if (g.ok) bounded = sh_bounded(a, i, 3 * (NY + 1));
+    }
     const int nb = gridDim.x;
     for (int v = 0; v < a.V; v++) {
         Rec r;
         r.ntiles = 0;
-        const bool vis = (i < a.n) && project_view(a, g, a.cams.c[v], i, r);
+        float3 dir;
+        bool vis = (i < a.n) && project_geom(a, g, a.cams.c[v], r, dir);
+        // some coefficient is huge or not finite: the colour itself decides
+        if (vis && !bounded) vis = colour_finite<DEG>(a, i, dir);
         const unsigned long long m = __ballot(vis);
         int nt = vis ? r.ntiles : 0;
         for (int o = kWave / 2; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
@@ -157,7 +179,10 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
     }
 }
 
+template <int DEG>
 __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
+    constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
+    constexpr int NC = 3 * (NY + 1);
     __shared__ int s_cnt[kBlock / kWave];
     __shared__ int s_inst[kBlock / kWave];
     const int i = blockIdx.x * kBlock + threadIdx.x;
@@ -165,13 +190,38 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     if (blockIdx.x == 0 && threadIdx.x < a.V) a.vis_count[threadIdx.x] = a.row_totals[threadIdx.x];
     Geo g;
     g.ok = false;
-    if (i < a.n) g = load_geo(a, i);
+    // the Gaussian's SH coefficients, read once for all views (row k*3 + channel)
+    float coef[NC];
+#pragma unroll
+    for (int k = 0; k < NC; k++) coef[k] = 0.0f;
+    if (i < a.n) {
+        g = load_geo(a, i);
+        if (g.ok) {
+#pragma unroll
+            for (int k = 0; k < NC; k++) coef[k] = a.sh[(size_t)k * a.n + i];
+        }
+    }
     const int nb = gridDim.x;
     int view_inst = 0;  // instances of the earlier views
     for (int v = 0; v < a.V; v++) {
         Rec r;
         r.ntiles = 0;
-        const bool vis = (i < a.n) && project_view(a, g, a.cams.c[v], i, r);
+        float3 dir;
+        bool vis = (i < a.n) && project_geom(a, g, a.cams.c[v], r, dir);
+        if (vis) {
+            // colour along the viewing direction: DC + sum_k sh_k Y_k, in the order of sh_eval
+            float Y[15];
+            sh_basis(DEG, dir.x, dir.y, dir.z, Y);
+            float3 col = make_float3(coef[0], coef[1], coef[2]);
+#pragma unroll
+            for (int k = 0; k < NY; k++) {
+                col.x = fmaf(coef[3 * (k + 1) + 0], Y[k], col.x);
+                col.y = fmaf(coef[3 * (k + 1) + 1], Y[k], col.y);
+                col.z = fmaf(coef[3 * (k + 1) + 2], Y[k], col.z);
+            }
+            vis = finitef(col.x) && finitef(col.y) && finitef(col.z);
+            r.rgb = make_float3(fmaxf(0.0f, col.x), fmaxf(0.0f, col.y), fmaxf(0.0f, col.z));
+        }
         const unsigned long long m = __ballot(vis);
         // inclusive scan of the tile counts over the wave
         const int nt = vis ? r.ntiles : 0;
@@ -236,10 +286,20 @@ hipError_t launch_project(const ProjectArgs& a0, hipStream_t s) {
     ProjectArgs a = a0;
     const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
     hipLaunchKernelGGL(zero_i64_kernel, dim3(1), dim3(64), 0, s, a.inst_count, a.V);
-    hipLaunchKernelGGL(project_count_kernel, dim3(nb), dim3(kBlock), 0, s, a);
+    switch (a.p.sh_degree) {
+        case 0: hipLaunchKernelGGL(project_count_kernel<0>, dim3(nb), dim3(kBlock), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(project_count_kernel<1>, dim3(nb), dim3(kBlock), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(project_count_kernel<2>, dim3(nb), dim3(kBlock), 0, s, a); break;
+        default: hipLaunchKernelGGL(project_count_kernel<3>, dim3(nb), dim3(kBlock), 0, s, a); break;
+    }
     hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nb, 2 * a.V, a.scan_partials, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(project_write_kernel, dim3(nb), dim3(kBlock), 0, s, a);
+    switch (a.p.sh_degree) {
+        case 0: hipLaunchKernelGGL(project_write_kernel<0>, dim3(nb), dim3(kBlock), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(project_write_kernel<1>, dim3(nb), dim3(kBlock), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(project_write_kernel<2>, dim3(nb), dim3(kBlock), 0, s, a); break;
+        default: hipLaunchKernelGGL(project_write_kernel<3>, dim3(nb), dim3(kBlock), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

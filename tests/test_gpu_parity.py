@@ -317,3 +317,39 @@ def test_packed_records_and_instance_bases(env):
         assert np.array_equal(g["inst_base"], want) and np.array_equal(bits[:, 11], g["inst_base"])
         base += int(g["n_tiles"].sum())
         assert g["inst_count"] == int(g["n_tiles"].sum())
+
+
+def test_degenerate_parameters_are_culled_like_the_oracle(env):
+    """Non-finite parameters (mean, scale, quaternion, opacity, SH coefficient) and a zero
+    quaternion cull the Gaussian in every view; a huge but finite SH coefficient (past the bound
+    under which the projection skips evaluating the colour's finiteness) keeps it visible with
+    the colour the oracle computes."""
+    oracle, pipeline, torch = env
+    cam = pinhole(64, 48, f=50.0, cx=32.0, cy=24.0)
+    n = 12
+    rng = np.random.default_rng(3)
+    means = np.column_stack([rng.uniform(-0.3, 0.3, n), rng.uniform(-0.2, 0.2, n), rng.uniform(2.0, 3.0, n)])
+    ls = np.full((n, 3), -2.5)
+    quats = np.tile([1.0, 0.0, 0.0, 0.0], (n, 1))
+    logits = np.full(n, 1.0)
+    rest = rng.standard_normal((n, 45)) * 0.1
+    means[0, 0] = np.nan
+    ls[1, 2] = np.inf
+    quats[2] = 0.0
+    quats[3, 1] = -np.inf
+    logits[4] = np.nan
+    rest[5, 7] = np.inf
+    rest[6, 20] = np.nan
+    rest[7, 3] = 1e31   # unbounded but finite: the colour decides, and it is finite
+    rest[8, 44] = -2e32
+    sc = scene_from(means, ls, quats, logits, rng.uniform(0.2, 0.8, (n, 3)), [cam], sh_rest=rest, sh_degree=3)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.iteration(mode="fused", image=True)
+    torch.cuda.synchronize()
+    gpu = r.projected_host(0)
+    o = oracle.project(sc, cam, st)
+    assert set(gpu["vis_ids"].tolist()) == set(np.nonzero(o["visible"])[0].tolist())
+    assert not set(range(7)) & set(gpu["vis_ids"].tolist())
+    assert {7, 8} <= set(gpu["vis_ids"].tolist())
+    parity.compare_projection(oracle, sc, cam, st, gpu)
