@@ -97,7 +97,9 @@ struct Batch {
 
 // Per-entry gradient accumulators of the backward (LDS).
 struct Acc {
-    float v[9][kBatch];
+    // row stride kBatch + 1: the accumulators of one entry's nine components fall in different
+    // LDS banks, so the four lanes of a row that add them do not conflict
+    float v[9][kBatch + 1];
 };
 
 // Stage list position j of the tile into batch index k (one thread per entry): three 16-byte
@@ -279,58 +281,114 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Back-to-front over this block's list of the staged batch (positions j = jbase + k).
+// Reduce-scatter of nine per-lane values over each 16-lane row.  Afterwards every lane of bank
+// (4-lane group) q of a row holds full row sums: w0 = component {0, 1, 5, 6}[q], w1 =
+// component {2, 3, 7, 8}[q], w2 = component 4.  Each level halves the values a lane carries: a
+// DPP add whose bank mask writes only part of the row lets the two halves (then the two quads of
+// a half) keep different components.  One asm block, so that every DPP source was written at
+// least two instructions earlier (the VALU-write to DPP-read hazard); the leading s_nop covers
+// the inputs.
+__device__ __forceinline__ void row_reduce_scatter(const float d[9], float& w0, float& w1, float& w2) {
+    float r0, r1, r2, r3, r4, t0, t1, t2;
+    asm volatile(
+        "s_nop 1\n"
+        // halves: row_ror:8 pairs lane i with lane i + 8 (mod 16); lanes 0-7 keep 0-3, lanes 8-15 keep 5-8
+        "v_add_f32_dpp %0, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+        "v_add_f32_dpp %1, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+        "v_add_f32_dpp %2, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+        "v_add_f32_dpp %3, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n"
+        "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+        "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+        "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+        "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n"
+        "v_add_f32_dpp %4, %15, %15 row_ror:8 row_mask:0xf bank_mask:0xf\n"
+        // quads of a half: row_half_mirror pairs lane i with lane 7 - i of its half
+        "v_add_f32_dpp %5, %0, %0 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+        "v_add_f32_dpp %5, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+        "v_add_f32_dpp %6, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+        "v_add_f32_dpp %6, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+        "v_add_f32_dpp %7, %4, %4 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+        // within the quad
+        "v_add_f32_dpp %8, %5, %5 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+        "v_add_f32_dpp %9, %6, %6 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+        "v_add_f32_dpp %10, %7, %7 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+        "s_nop 0\n"
+        "v_add_f32_dpp %8, %8, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+        "v_add_f32_dpp %9, %9, %9 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+        "v_add_f32_dpp %10, %10, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(w0),
+          "=&v"(w1), "=&v"(w2)
+        : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]), "v"(d[8]));
+}
+
+// Back-to-front over this block's list of the staged batch (positions j = jbase + k).  Every
+// lane evaluates the step without branches; the results are kept where the pair contributes.
 __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Acc& acc, Lists l,
                                          int32_t jbase, int row_nc, Bwd& s) {
     const float amax = a.p.alpha_max;
     const float bg0 = a.p.bg[0], bg1 = a.p.bg[1], bg2 = a.p.bg[2];
     const uint8_t* lst = b.list[c.list_id];
+    const int quad = (c.lane >> 2) & 3;
+    const bool quad_lead = (c.lane & 3) == 0;
+    // accumulator rows of the components this lane's quad adds after the reduce-scatter
+    float* const acc_w0 = acc.v[quad < 2 ? quad : quad + 3];
+    float* const acc_w1 = acc.v[quad < 2 ? quad + 2 : quad + 5];
     for (int i = l.max_len - 1; i >= 0; i--) {
         const int k = i < l.len ? (int)lst[i] : 0;
         const bool active = i < l.len && jbase + k < row_nc;  // uniform over the row
         if (__ballot(active) == 0ull) continue;
+        const float2 xy = b.xy[k];
+        const float4 q = b.q[k];
+        const float4 oc = b.oc[k];
+        // the pair evaluation of eval_pair, for every lane
+        const float dx = c.fpx - xy.x;
+        const float dy = c.fpy - xy.y;
+        const float bdx = q.y * dx;
+        const float cdy = q.z * dy;
+        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, cdy * dy));
+        const bool contrib = active && jbase + k < s.nc && p2 >= q.w;
+        const float o = oc.x;
+        const float G = __builtin_amdgcn_exp2f(p2);
+        const float v = o * G;
+        const bool unclamped = v <= amax;
+        const float alpha = fminf(amax, v);
+        const float oma = unclamped ? fmaf(-o, G, 1.0f) : 1.0f - amax;
+        const float inv = __builtin_amdgcn_rcpf(oma);  // 1 - alpha >= 1 - alpha_max > 0 where it counts
+        const float Tj = s.T * inv;
+        const float bgterm = s.Tfin * inv;
+        float dLda = s.g0 * (Tj * (oc.y - s.B0) - bgterm * bg0);
+        dLda = fmaf(s.g1, Tj * (oc.z - s.B1) - bgterm * bg1, dLda);
+        dLda = fmaf(s.g2, Tj * (oc.w - s.B2) - bgterm * bg2, dLda);
+        const float wgt = alpha * Tj;
+        // dalpha/dG = o; dG/dq = -G/2; conic (A, B, C) = (-2 a, -b, -2 c) ln 2
+        const float gh = unclamped ? v * dLda : 0.0f;
+        const float ghl = -kLn2 * gh;
         float d[9];
+        d[0] = ghl * fmaf(2.0f * q.x, dx, q.y * dy);  // gh (A dx + B dy)
+        d[1] = ghl * fmaf(q.y, dx, 2.0f * q.z * dy);  // gh (B dx + C dy)
+        d[2] = -0.5f * gh * dx * dx;
+        d[3] = -gh * dx * dy;
+        d[4] = -0.5f * gh * dy * dy;
+        d[5] = unclamped ? G * dLda : 0.0f;
+        d[6] = wgt * s.g0;
+        d[7] = wgt * s.g1;
+        d[8] = wgt * s.g2;
 #pragma unroll
-        for (int t = 0; t < 9; t++) d[t] = 0.0f;
-        bool contrib = false;
-        Pair e;
-        if (active && jbase + k < s.nc && eval_pair(c, b, k, amax, e)) {
-            contrib = true;
-            const float4 oc = b.oc[k];
-            const float inv = __builtin_amdgcn_rcpf(e.oma);  // 1 - alpha >= 1 - alpha_max > 0
-            const float Tj = s.T * inv;
-            const float bgterm = s.Tfin * inv;
-            float dLda = s.g0 * (Tj * (oc.y - s.B0) - bgterm * bg0);
-            dLda = fmaf(s.g1, Tj * (oc.z - s.B1) - bgterm * bg1, dLda);
-            dLda = fmaf(s.g2, Tj * (oc.w - s.B2) - bgterm * bg2, dLda);
-            const float wgt = e.alpha * Tj;
-            d[6] = wgt * s.g0;
-            d[7] = wgt * s.g1;
-            d[8] = wgt * s.g2;
-            s.B0 = fmaf(e.alpha, oc.y, e.oma * s.B0);
-            s.B1 = fmaf(e.alpha, oc.z, e.oma * s.B1);
-            s.B2 = fmaf(e.alpha, oc.w, e.oma * s.B2);
-            if (e.v <= amax) {
-                // dalpha/dG = o; dG/dq = -G/2; conic (A, B, C) = (-2 a, -b, -2 c) ln 2
-                const float gh = e.v * dLda;
-                const float4 q = b.q[k];
-                const float ghl = -kLn2 * gh;
-                d[0] = ghl * fmaf(2.0f * q.x, e.dx, q.y * e.dy);  // gh (A dx + B dy)
-                d[1] = ghl * fmaf(q.y, e.dx, 2.0f * q.z * e.dy);  // gh (B dx + C dy)
-                d[2] = -0.5f * gh * e.dx * e.dx;
-                d[3] = -gh * e.dx * e.dy;
-                d[4] = -0.5f * gh * e.dy * e.dy;
-                d[5] = e.G * dLda;
-            }
+        for (int t = 0; t < 9; t++) d[t] = contrib ? d[t] : 0.0f;
+        if (contrib) {
+            s.B0 = fmaf(alpha, oc.y, oma * s.B0);
+            s.B1 = fmaf(alpha, oc.z, oma * s.B1);
+            s.B2 = fmaf(alpha, oc.w, oma * s.B2);
             s.T = Tj;
         }
         const unsigned long long cm = __ballot(contrib);
         if (cm != 0ull) {
-#pragma unroll
-            for (int t = 0; t < 9; t++) d[t] = row_total(d[t]);
-            if ((c.lane & 15) == 15 && ((cm >> (16 * c.row)) & 0xFFFFull) != 0ull) {
-#pragma unroll
-                for (int t = 0; t < 9; t++) atomicAdd(&acc.v[t][k], d[t]);
+            float w0, w1, w2;
+            row_reduce_scatter(d, w0, w1, w2);
+            if (quad_lead && ((cm >> (16 * c.row)) & 0xFFFFull) != 0ull) {
+                atomicAdd(&acc_w0[k], w0);
+                atomicAdd(&acc_w1[k], w1);
+                if (quad == 0) atomicAdd(&acc.v[4][k], w2);
             }
         }
     }
