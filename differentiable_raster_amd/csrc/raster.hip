@@ -220,6 +220,9 @@ __device__ __forceinline__ bool in_alpha_box(float dx, float dy, float4 co, floa
     return fabsf(dx) <= ex && fabsf(dy) <= ey;
 }
 
+// Front-to-back over this block's list of the staged batch (positions j = jbase + k).  Every
+// lane evaluates the step without branches (the pair evaluation of eval_pair, written out) and
+// keeps the result where it blends.
 template <bool COUNT>
 __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Lists l, int32_t jbase,
                                          Fwd& f, Counts& cnt) {
@@ -228,30 +231,39 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
     for (int i = 0; i < l.max_len; i++) {
         const bool work = !f.done && i < l.len;
         if (__ballot(work) == 0ull) break;
-        if (!work) continue;
-        const int k = lst[i];
-        Pair e;
-        const bool hit = eval_pair(c, b, k, amax, e);
-        if (COUNT) {
-            cnt.eval++;
-            const float4 q = b.q[k];
-            const float4 co = make_float4(-2.0f * kLn2 * q.x, -kLn2 * q.y, -2.0f * kLn2 * q.z, b.oc[k].x);
-            cnt.box += in_alpha_box(e.dx, e.dy, co, a.p.alpha_min) ? 1 : 0;
-        }
-        if (!hit) continue;
-        const float Tn = f.T * e.oma;
-        if (Tn < tmin) {
-            f.done = true;
-            continue;
-        }
-        const float wgt = e.alpha * f.T;
+        const int k = lst[i];  // past this lane's list: a stale index (< kBatch), unused
+        const float2 xy = b.xy[k];
+        const float4 q = b.q[k];
         const float4 oc = b.oc[k];
-        f.C0 = fmaf(wgt, oc.y, f.C0);
-        f.C1 = fmaf(wgt, oc.z, f.C1);
-        f.C2 = fmaf(wgt, oc.w, f.C2);
-        f.T = Tn;
-        f.last = jbase + k + 1;
-        if (COUNT) cnt.blend++;
+        const float dx = c.fpx - xy.x;
+        const float dy = c.fpy - xy.y;
+        const float bdx = q.y * dx;
+        const float cdy = q.z * dy;
+        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, cdy * dy));
+        const bool hit = work && p2 >= q.w;
+        const float o = oc.x;
+        const float G = __builtin_amdgcn_exp2f(p2);
+        const float v = o * G;
+        const float alpha = fminf(amax, v);
+        const float oma = v <= amax ? fmaf(-o, G, 1.0f) : 1.0f - amax;
+        const float Tn = f.T * oma;
+        const bool stop = hit && Tn < tmin;
+        const bool blend = hit && !(Tn < tmin);
+        const float wgt = alpha * f.T;
+        if (COUNT) {
+            if (work) {
+                cnt.eval++;
+                const float4 co = make_float4(-2.0f * kLn2 * q.x, -kLn2 * q.y, -2.0f * kLn2 * q.z, o);
+                cnt.box += in_alpha_box(dx, dy, co, a.p.alpha_min) ? 1 : 0;
+            }
+            cnt.blend += blend ? 1 : 0;
+        }
+        f.done = f.done || stop;
+        f.C0 = blend ? fmaf(wgt, oc.y, f.C0) : f.C0;
+        f.C1 = blend ? fmaf(wgt, oc.z, f.C1) : f.C1;
+        f.C2 = blend ? fmaf(wgt, oc.w, f.C2) : f.C2;
+        f.T = blend ? Tn : f.T;
+        f.last = blend ? jbase + k + 1 : f.last;
     }
 }
 
@@ -334,7 +346,7 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
     float* const acc_w0 = acc.v[quad < 2 ? quad : quad + 3];
     float* const acc_w1 = acc.v[quad < 2 ? quad + 2 : quad + 5];
     for (int i = l.max_len - 1; i >= 0; i--) {
-        const int k = i < l.len ? (int)lst[i] : 0;
+        const int k = lst[i];  // past this lane's list: a stale index (< kBatch), unused
         const bool active = i < l.len && jbase + k < row_nc;  // uniform over the row
         if (__ballot(active) == 0ull) continue;
         const float2 xy = b.xy[k];
