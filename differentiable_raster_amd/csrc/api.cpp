@@ -385,7 +385,8 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
                                           w.readback, s),
                         "count launch")) != GS_OK)
         return st;
-    if ((st = hip_check(hipMemcpyAsync(&rb, w.readback, sizeof(rb), hipMemcpyDeviceToHost, s), "count read")) != GS_OK)
+    if ((st = hip_check(hipMemcpyAsync(&rb, w.readback, offsetof(BinReadback, partial), hipMemcpyDeviceToHost, s),
+                        "count read")) != GS_OK)
         return st;
     if ((st = hip_check(hipStreamSynchronize(s), "count read sync")) != GS_OK) return st;
     const int32_t* vis = rb.vis;

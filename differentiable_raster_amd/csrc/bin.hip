@@ -36,17 +36,13 @@ __global__ __launch_bounds__(kBlock) void depth_keys_kernel(const float* depth, 
 }
 
 // The values the host reads back before sizing the binning launches, packed for one copy: the
-// per-view counts and the range of the visible depths' float32 bits, as bits[0] = the smallest
-// pattern and bits[1] = the complement of the largest (both minima, so that one fill of
-// 0xFFFFFFFF initializes them).
-__global__ __launch_bounds__(kBlock) void bin_counts_kernel(const int32_t* vis_count, const int64_t* inst_count,
-                                                            int32_t V, const float* depth, int32_t capacity,
-                                                            BinReadback* out) {
+// per-view counts and the range of the visible depths' float32 bits (bits[0] = the smallest
+// pattern, bits[1] = the complement of the largest).  Two steps without atomics (many blocks
+// adding into one word serialize across the chip): each block reduces a strided share of the
+// visible depths into partial[block], then one block reduces the partials.
+__global__ __launch_bounds__(kBlock) void depth_range_kernel(const int32_t* vis_count, int32_t V, const float* depth,
+                                                             int32_t capacity, uint2* partial) {
     __shared__ uint32_t s_lo[kBlock / 64], s_hi[kBlock / 64];
-    if (blockIdx.x == 0 && threadIdx.x < V) {
-        out->vis[threadIdx.x] = vis_count[threadIdx.x];
-        out->inst[threadIdx.x] = inst_count[threadIdx.x];
-    }
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for (int v = 0; v < V; v++) {
         const int32_t cnt = min(vis_count[v], capacity);
@@ -71,8 +67,39 @@ __global__ __launch_bounds__(kBlock) void bin_counts_kernel(const int32_t* vis_c
             lo = min(lo, s_lo[k]);
             hi = max(hi, s_hi[k]);
         }
-        if (lo != 0xFFFFFFFFu) atomicMin(&out->bits[0], lo);
-        if (hi != 0u) atomicMin(&out->bits[1], ~hi);
+        partial[blockIdx.x] = make_uint2(lo, ~hi);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void bin_counts_kernel(const int32_t* vis_count, const int64_t* inst_count,
+                                                            int32_t V, const uint2* partial, int32_t nparts,
+                                                            BinReadback* out) {
+    __shared__ uint32_t s_lo[kBlock / 64], s_nhi[kBlock / 64];
+    if (threadIdx.x < V) {
+        out->vis[threadIdx.x] = vis_count[threadIdx.x];
+        out->inst[threadIdx.x] = inst_count[threadIdx.x];
+    }
+    uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;
+    for (int k = threadIdx.x; k < nparts; k += kBlock) {
+        lo = min(lo, partial[k].x);
+        nhi = min(nhi, partial[k].y);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+        nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        s_lo[threadIdx.x / 64] = lo;
+        s_nhi[threadIdx.x / 64] = nhi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < kBlock / 64; k++) {
+            lo = min(lo, s_lo[k]);
+            nhi = min(nhi, s_nhi[k]);
+        }
+        out->bits[0] = lo;
+        out->bits[1] = nhi;
     }
 }
 
@@ -253,9 +280,10 @@ hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int3
 
 hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count, int32_t V, const float* depth,
                              int32_t capacity, BinReadback* out, hipStream_t s) {
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kBlock), 0, s, reinterpret_cast<int32_t*>(out->bits), -1, 2);
-    hipLaunchKernelGGL(bin_counts_kernel, dim3(1024), dim3(kBlock), 0, s, vis_count, inst_count, V, depth, capacity,
-                       out);
+    hipLaunchKernelGGL(depth_range_kernel, dim3(kDepthRangeBlocks), dim3(kBlock), 0, s, vis_count, V, depth, capacity,
+                       out->partial);
+    hipLaunchKernelGGL(bin_counts_kernel, dim3(1), dim3(kBlock), 0, s, vis_count, inst_count, V, out->partial,
+                       kDepthRangeBlocks, out);
     return hipGetLastError();
 }
 

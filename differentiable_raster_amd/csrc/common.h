@@ -118,10 +118,12 @@ size_t radix_hist_bytes(int32_t n);
 size_t radix_partials_bytes(int32_t n);
 
 // Binning helpers.
+constexpr int kDepthRangeBlocks = 512;
 struct BinReadback {
     int64_t inst[GS_MAX_VIEWS];
     int32_t vis[GS_MAX_VIEWS];
     uint32_t bits[2];  // smallest float32 bit pattern of the visible depths, complement of the largest
+    uint2 partial[kDepthRangeBlocks];  // per-block partial depth ranges (device only; not read back)
 };
 hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count, int32_t V, const float* depth,
                              int32_t capacity, BinReadback* out, hipStream_t s);

@@ -59,9 +59,13 @@ __device__ Geo load_geo(const ProjectArgs& a, int i) {
 // real SH basis value of degree <= 3 on the unit sphere is below 1 in magnitude, so the colour
 // sum of at most 48 such terms then stays below 5e31 at every step of its evaluation: it is
 // finite, and the colour cannot cull the Gaussian in any view.
-__device__ __forceinline__ bool sh_bounded(const ProjectArgs& a, int i, int nk3) {
+template <int NK3>
+__device__ __forceinline__ bool sh_bounded(const ProjectArgs& a, int i) {
+    // bitwise and, unrolled: the loads are issued together (a short-circuit chain would
+    // serialize them); a NaN compares false
     bool ok = true;
-    for (int k = 0; k < nk3; k++) ok = ok && fabsf(a.sh[(size_t)k * a.n + i]) <= 1e30f;
+#pragma unroll 16
+    for (int k = 0; k < NK3; k++) ok &= fabsf(a.sh[(size_t)k * a.n + i]) <= 1e30f;
     return ok;
 }
 
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
     bool bounded = true;
     if (i < a.n) {
         g = load_geo(a, i);
-        if (g.ok) bounded = sh_bounded(a, i, 3 * (NY + 1));
+        if (g.ok) bounded = sh_bounded<3 * (NY + 1)>(a, i);
     }
     const int nb = gridDim.x;
     for (int v = 0; v < a.V; v++) {
@@ -173,7 +177,6 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
             }
             a.block_counts[v * nb + blockIdx.x] = c;
             a.block_counts[(a.V + v) * nb + blockIdx.x] = t;
-            if (t) atomicAdd((unsigned long long*)&a.inst_count[v], (unsigned long long)t);
         }
         __syncthreads();
     }
@@ -265,9 +268,23 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     }
 }
 
-__global__ void zero_i64_kernel(int64_t* p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
+// inst_count[v] = the 64-bit sum of row V + v of the block counts (one block per view; 64 bits,
+// so that a total past 2^31 is reported as such and refused by the binning call).
+__global__ __launch_bounds__(kBlock) void inst_total_kernel(const int32_t* block_counts, int32_t V, int32_t nb,
+                                                            int64_t* inst_count) {
+    __shared__ long long s_part[kBlock / kWave];
+    const int v = blockIdx.x;
+    const int32_t* row = block_counts + (size_t)(V + v) * nb;
+    long long t = 0;
+    for (int32_t b = threadIdx.x; b < nb; b += kBlock) t += row[b];
+    for (int o = kWave / 2; o > 0; o >>= 1) t += __shfl_xor(t, o);
+    if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        long long sum = 0;
+        for (int k = 0; k < kBlock / kWave; k++) sum += s_part[k];
+        inst_count[v] = sum;
+    }
 }
 
 }  // namespace
@@ -285,13 +302,13 @@ size_t project_ws_bytes(int32_t n, int32_t V) {
 hipError_t launch_project(const ProjectArgs& a0, hipStream_t s) {
     ProjectArgs a = a0;
     const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
-    hipLaunchKernelGGL(zero_i64_kernel, dim3(1), dim3(64), 0, s, a.inst_count, a.V);
     switch (a.p.sh_degree) {
         case 0: hipLaunchKernelGGL(project_count_kernel<0>, dim3(nb), dim3(kBlock), 0, s, a); break;
         case 1: hipLaunchKernelGGL(project_count_kernel<1>, dim3(nb), dim3(kBlock), 0, s, a); break;
         case 2: hipLaunchKernelGGL(project_count_kernel<2>, dim3(nb), dim3(kBlock), 0, s, a); break;
         default: hipLaunchKernelGGL(project_count_kernel<3>, dim3(nb), dim3(kBlock), 0, s, a); break;
     }
+    hipLaunchKernelGGL(inst_total_kernel, dim3(a.V), dim3(kBlock), 0, s, a.block_counts, a.V, nb, a.inst_count);
     hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nb, 2 * a.V, a.scan_partials, s);
     if (e != hipSuccess) return e;
     switch (a.p.sh_degree) {
