@@ -371,22 +371,24 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         float dLda = s.g0 * (Tj * (oc.y - s.B0) - bgterm * bg0);
         dLda = fmaf(s.g1, Tj * (oc.z - s.B1) - bgterm * bg1, dLda);
         dLda = fmaf(s.g2, Tj * (oc.w - s.B2) - bgterm * bg2, dLda);
-        const float wgt = alpha * Tj;
-        // dalpha/dG = o; dG/dq = -G/2; conic (A, B, C) = (-2 a, -b, -2 c) ln 2
-        const float gh = unclamped ? v * dLda : 0.0f;
-        const float ghl = -kLn2 * gh;
+        // zero where the pair does not contribute (selects, so no garbage of other lanes leaks)
+        const float wgt = contrib ? alpha * Tj : 0.0f;
+        const bool geo = contrib && unclamped;
+        const float gh = geo ? v * dLda : 0.0f;  // o G dL/dalpha
+        // per-pixel sums whose entry-constant factors are applied once per entry when the batch
+        // is flushed: dL/dmean2d = -ln2 (2 a, b; b, 2 c) (gh dx, gh dy) in the log2-scaled conic,
+        // dL/d(A, B, C) = (-1/2, -1, -1/2) (gh dx dx, gh dx dy, gh dy dy)
+        const float gx = gh * dx, gy = gh * dy;
         float d[9];
-        d[0] = ghl * fmaf(2.0f * q.x, dx, q.y * dy);  // gh (A dx + B dy)
-        d[1] = ghl * fmaf(q.y, dx, 2.0f * q.z * dy);  // gh (B dx + C dy)
-        d[2] = -0.5f * gh * dx * dx;
-        d[3] = -gh * dx * dy;
-        d[4] = -0.5f * gh * dy * dy;
-        d[5] = unclamped ? G * dLda : 0.0f;
+        d[0] = gx;
+        d[1] = gy;
+        d[2] = gx * dx;
+        d[3] = gx * dy;
+        d[4] = gy * dy;
+        d[5] = geo ? G * dLda : 0.0f;
         d[6] = wgt * s.g0;
         d[7] = wgt * s.g1;
         d[8] = wgt * s.g2;
-#pragma unroll
-        for (int t = 0; t < 9; t++) d[t] = contrib ? d[t] : 0.0f;
         if (contrib) {
             s.B0 = fmaf(alpha, oc.y, oma * s.B0);
             s.B1 = fmaf(alpha, oc.z, oma * s.B1);
@@ -421,6 +423,14 @@ __device__ __forceinline__ void flush_batch(const RasterArgs& a, const Batch& b,
             any |= d[t] != 0.0f;
             acc.v[t][k] = 0.0f;
         }
+        // the entry-constant factors of the mean and conic gradients (see bwd_walk)
+        const float4 q = b.q[k];
+        const float sx = d[0], sy = d[1];
+        d[0] = -kLn2 * fmaf(2.0f * q.x, sx, q.y * sy);
+        d[1] = -kLn2 * fmaf(q.y, sx, 2.0f * q.z * sy);
+        d[2] *= -0.5f;
+        d[3] = -d[3];
+        d[4] *= -0.5f;
         // the bound only matters for bins and records of different calls (stale instance indices)
         if (any && (uint64_t)(uint32_t)b.inst[k] < (uint64_t)a.num_instances) {
             float* rec = a.partials + (size_t)b.inst[k] * 9;
