@@ -111,24 +111,59 @@ __global__ __launch_bounds__(kBlock) void gather_ntiles_kernel(const uint32_t* p
     out[r] = n_tiles[(size_t)(p >> kSlotBits) * capacity + (p & kSlotMask)];
 }
 
+// One thread per slot in depth order writes the slot's instances (its tiles row-major) from its
+// offset on.  Rectangles of more than kSmallRect tiles are written by the whole wavefront, 64
+// instances per step, so that a few large splats do not serialize on one lane.
+constexpr int kSmallRect = 8;
+
 __global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* offsets, const ushort4* rect,
                                                       int32_t capacity, int32_t total, int32_t tiles_x,
                                                       int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
                                                       int32_t* vals) {
     const int32_t r = blockIdx.x * kBlock + threadIdx.x;
-    if (r >= total) return;
-    const uint32_t p = packed[r];
-    const uint32_t v = p >> kSlotBits, slot = p & kSlotMask;
-    const ushort4 rc = rect[(size_t)v * capacity + slot];
-    int32_t o = offsets[r];
-    const uint32_t vbase = v * (uint32_t)tiles_per_view;
-    for (int ty = rc.y; ty <= rc.w; ty++)
-        for (int tx = rc.x; tx <= rc.z; tx++) {
-            if (o >= M) return;  // never past the instance count sized on the host
-            tile_keys[o] = vbase + (uint32_t)(ty * tiles_x + tx);
-            vals[o] = (int32_t)slot;
-            o++;
+    const int lane = threadIdx.x & 63;
+    const bool live = r < total;
+    uint32_t slot = 0, vbase = 0;
+    ushort4 rc = make_ushort4(0, 0, 0, 0);
+    int32_t o = 0;
+    int nt = 0;
+    if (live) {
+        const uint32_t p = packed[r];
+        const uint32_t v = p >> kSlotBits;
+        slot = p & kSlotMask;
+        rc = rect[(size_t)v * capacity + slot];
+        o = offsets[r];
+        vbase = v * (uint32_t)tiles_per_view;
+        nt = (rc.z - rc.x + 1) * (rc.w - rc.y + 1);
+    }
+    const bool big = nt > kSmallRect;
+    if (live && !big) {
+        for (int ty = rc.y; ty <= rc.w; ty++)
+            for (int tx = rc.x; tx <= rc.z; tx++) {
+                if (o >= M) return;  // never past the instance count sized on the host
+                tile_keys[o] = vbase + (uint32_t)(ty * tiles_x + tx);
+                vals[o] = (int32_t)slot;
+                o++;
+            }
+    }
+    unsigned long long bm = __ballot(big);
+    while (bm != 0ull) {
+        const int src = __ffsll((long long)bm) - 1;
+        bm &= bm - 1ull;
+        const int32_t o0 = __shfl(o, src);
+        const int n0 = __shfl(nt, src);
+        const int x0 = __shfl((int)rc.x, src), y0 = __shfl((int)rc.y, src);
+        const int w0 = __shfl((int)rc.z, src) - x0 + 1;
+        const uint32_t vb = (uint32_t)__shfl((int)vbase, src);
+        const int32_t sl = __shfl((int)slot, src);
+        for (int k = lane; k < n0; k += 64) {
+            const int dy = k / w0, dx = k - dy * w0;
+            if (o0 + k < M) {
+                tile_keys[o0 + k] = vb + (uint32_t)((y0 + dy) * tiles_x + x0 + dx);
+                vals[o0 + k] = sl;
+            }
         }
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
