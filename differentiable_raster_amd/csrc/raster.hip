@@ -270,6 +270,7 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
 struct Bwd {
     float T, Tfin;
     float g0, g1, g2;
+    float gbg;  // sum over channels of dL/dC * background
     float B0, B1, B2;
     int32_t nc;
 };
@@ -335,10 +336,11 @@ __device__ __forceinline__ void row_reduce_scatter(const float d[9], float& w0, 
 
 // Back-to-front over this block's list of the staged batch (positions j = jbase + k).  Every
 // lane evaluates the step without branches; the results are kept where the pair contributes.
+// BG: the background is not black (its term in dL/dalpha is needed).
+template <bool BG>
 __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Acc& acc, Lists l,
                                          int32_t jbase, int row_nc, Bwd& s) {
     const float amax = a.p.alpha_max;
-    const float bg0 = a.p.bg[0], bg1 = a.p.bg[1], bg2 = a.p.bg[2];
     const uint8_t* lst = b.list[c.list_id];
     const int quad = (c.lane >> 2) & 3;
     const bool quad_lead = (c.lane & 3) == 0;
@@ -367,32 +369,32 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float oma = unclamped ? fmaf(-o, G, 1.0f) : 1.0f - amax;
         const float inv = __builtin_amdgcn_rcpf(oma);  // 1 - alpha >= 1 - alpha_max > 0 where it counts
         const float Tj = s.T * inv;
-        const float bgterm = s.Tfin * inv;
-        float dLda = s.g0 * (Tj * (oc.y - s.B0) - bgterm * bg0);
-        dLda = fmaf(s.g1, Tj * (oc.z - s.B1) - bgterm * bg1, dLda);
-        dLda = fmaf(s.g2, Tj * (oc.w - s.B2) - bgterm * bg2, dLda);
+        // dL/dalpha = T_j sum_ch g_ch (c_ch - B_ch) - T_final / (1 - alpha) sum_ch g_ch bg_ch
+        const float e0 = oc.y - s.B0, e1 = oc.z - s.B1, e2 = oc.w - s.B2;
+        float dLda = Tj * fmaf(s.g0, e0, fmaf(s.g1, e1, s.g2 * e2));
+        if (BG) dLda = fmaf(-s.Tfin * inv, s.gbg, dLda);
         // zero where the pair does not contribute (selects, so no garbage of other lanes leaks)
         const float wgt = contrib ? alpha * Tj : 0.0f;
-        const bool geo = contrib && unclamped;
-        const float gh = geo ? v * dLda : 0.0f;  // o G dL/dalpha
+        const float gG = (contrib && unclamped) ? G * dLda : 0.0f;  // dL/do; times o: dL/dq factor
         // per-pixel sums whose entry-constant factors are applied once per entry when the batch
-        // is flushed: dL/dmean2d = -ln2 (2 a, b; b, 2 c) (gh dx, gh dy) in the log2-scaled conic,
-        // dL/d(A, B, C) = (-1/2, -1, -1/2) (gh dx dx, gh dx dy, gh dy dy)
-        const float gx = gh * dx, gy = gh * dy;
+        // is flushed: dL/dmean2d = -ln2 o (2 a, b; b, 2 c) (gG dx, gG dy) in the log2-scaled
+        // conic, dL/d(A, B, C) = o (-1/2, -1, -1/2) (gG dx dx, gG dx dy, gG dy dy)
+        const float gx = gG * dx, gy = gG * dy;
         float d[9];
         d[0] = gx;
         d[1] = gy;
         d[2] = gx * dx;
         d[3] = gx * dy;
         d[4] = gy * dy;
-        d[5] = geo ? G * dLda : 0.0f;
+        d[5] = gG;
         d[6] = wgt * s.g0;
         d[7] = wgt * s.g1;
         d[8] = wgt * s.g2;
         if (contrib) {
-            s.B0 = fmaf(alpha, oc.y, oma * s.B0);
-            s.B1 = fmaf(alpha, oc.z, oma * s.B1);
-            s.B2 = fmaf(alpha, oc.w, oma * s.B2);
+            // colour behind the next entry: alpha c + (1 - alpha) B = B + alpha (c - B)
+            s.B0 = fmaf(alpha, e0, s.B0);
+            s.B1 = fmaf(alpha, e1, s.B1);
+            s.B2 = fmaf(alpha, e2, s.B2);
             s.T = Tj;
         }
         const unsigned long long cm = __ballot(contrib);
@@ -425,12 +427,13 @@ __device__ __forceinline__ void flush_batch(const RasterArgs& a, const Batch& b,
         }
         // the entry-constant factors of the mean and conic gradients (see bwd_walk)
         const float4 q = b.q[k];
+        const float o = b.oc[k].x;
         const float sx = d[0], sy = d[1];
-        d[0] = -kLn2 * fmaf(2.0f * q.x, sx, q.y * sy);
-        d[1] = -kLn2 * fmaf(q.y, sx, 2.0f * q.z * sy);
-        d[2] *= -0.5f;
-        d[3] = -d[3];
-        d[4] *= -0.5f;
+        d[0] = -kLn2 * o * fmaf(2.0f * q.x, sx, q.y * sy);
+        d[1] = -kLn2 * o * fmaf(q.y, sx, 2.0f * q.z * sy);
+        d[2] *= -0.5f * o;
+        d[3] *= -o;
+        d[4] *= -0.5f * o;
         // the bound only matters for bins and records of different calls (stale instance indices)
         if (any && (uint64_t)(uint32_t)b.inst[k] < (uint64_t)a.num_instances) {
             float* rec = a.partials + (size_t)b.inst[k] * 9;
@@ -497,6 +500,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
 // Backward over list positions [0, maxnc); the batch starting at `resident_b0` (with
 // `resident_cnt` entries and this lane's lists `resident`) is already staged.  The gradient
 // accumulators must be zero on entry.
+template <bool BG>
 __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Acc& acc, int32_t maxnc,
                                               int32_t resident_b0, int resident_cnt, Lists resident, Bwd& s) {
     const int row_nc = row_max(s.nc);
@@ -511,7 +515,7 @@ __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx
             __syncthreads();
             l = build_lists(c, b, cnt_b);
         }
-        bwd_walk(a, c, b, acc, l, b0, row_nc, s);
+        bwd_walk<BG>(a, c, b, acc, l, b0, row_nc, s);
         flush_batch(a, b, acc, cnt_b);
         resident_b0 = -1;
     }
@@ -590,6 +594,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis
     }
 }
 
+template <bool BG>
 __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const float* t_final, const int32_t* n_contrib,
                                                             const float* dl, Grads gr) {
     __shared__ Batch b;
@@ -611,13 +616,14 @@ __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const 
         s.g0 = s.g1 = s.g2 = 0.0f;
     }
     s.Tfin = s.T;
+    s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
     s.B0 = s.B1 = s.B2 = 0.0f;
     zero_acc(acc);
     const int maxnc = block_max(s.nc, s_red);
-    backward_tile(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s);
+    backward_tile<BG>(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s);
 }
 
-template <bool COUNT>
+template <bool COUNT, bool BG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void raster_fused_kernel(RasterArgs a, int mode, const float* tgt, float scale,
                                                               float* image, float* loss_sum, Grads gr) {
     __shared__ Batch b;
@@ -672,7 +678,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     }
     const int maxnc = block_max(s.nc, s_red);
     // every pixel's last blended entry lies in the last staged batch, so it is still resident
-    backward_tile(a, c, b, acc, maxnc, last_b0, last_cnt, last_lists, s);
+    s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
+    backward_tile<BG>(a, c, b, acc, maxnc, last_b0, last_cnt, last_lists, s);
 }
 
 }  // namespace
@@ -717,21 +724,33 @@ static hipError_t with_partials(const RasterArgs& a, Grads g, hipStream_t s, Lau
 hipError_t launch_raster_bwd(const RasterArgs& a, const float* /*image*/, const float* t_final, const int32_t* n_contrib,
                              const float* dl, Grads g, hipStream_t s) {
     const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
+    const bool bg = a.p.bg[0] != 0.0f || a.p.bg[1] != 0.0f || a.p.bg[2] != 0.0f;
     return with_partials(a, g, s, [&] {
-        hipLaunchKernelGGL(raster_bwd_kernel, dim3(nblocks), dim3(kBlock), 0, s, a, t_final, n_contrib, dl, g);
+        if (bg)
+            hipLaunchKernelGGL(raster_bwd_kernel<true>, dim3(nblocks), dim3(kBlock), 0, s, a, t_final, n_contrib, dl, g);
+        else
+            hipLaunchKernelGGL(raster_bwd_kernel<false>, dim3(nblocks), dim3(kBlock), 0, s, a, t_final, n_contrib, dl,
+                               g);
     });
 }
 
 hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,
                                float* loss_sum, Grads g, hipStream_t s) {
     const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
+    const bool bg = a.p.bg[0] != 0.0f || a.p.bg[1] != 0.0f || a.p.bg[2] != 0.0f;
     return with_partials(a, g, s, [&] {
-        if (a.counters)
-            hipLaunchKernelGGL(raster_fused_kernel<true>, dim3(nblocks), dim3(kBlock), 0, s, a, mode, target_or_dl,
-                               scale, image, loss_sum, g);
+        if (a.counters && bg)
+            hipLaunchKernelGGL((raster_fused_kernel<true, true>), dim3(nblocks), dim3(kBlock), 0, s, a, mode,
+                               target_or_dl, scale, image, loss_sum, g);
+        else if (a.counters)
+            hipLaunchKernelGGL((raster_fused_kernel<true, false>), dim3(nblocks), dim3(kBlock), 0, s, a, mode,
+                               target_or_dl, scale, image, loss_sum, g);
+        else if (bg)
+            hipLaunchKernelGGL((raster_fused_kernel<false, true>), dim3(nblocks), dim3(kBlock), 0, s, a, mode,
+                               target_or_dl, scale, image, loss_sum, g);
         else
-            hipLaunchKernelGGL(raster_fused_kernel<false>, dim3(nblocks), dim3(kBlock), 0, s, a, mode, target_or_dl,
-                               scale, image, loss_sum, g);
+            hipLaunchKernelGGL((raster_fused_kernel<false, false>), dim3(nblocks), dim3(kBlock), 0, s, a, mode,
+                               target_or_dl, scale, image, loss_sum, g);
     });
 }
 
