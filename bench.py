@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gaussian-pixel blends/s (fwd+bwd) and ms/iter, 1M Gaussians @1080p, 1 GPU"
 # Algorithmic float32 operations (FMA = 2) of the fused rasterizer, per unit:
-FLOPS_PER_BOX_PAIR = 16   # evaluate one (pixel, Gaussian) pair inside the Gaussian's alpha box
+FLOPS_PER_ALPHA_PAIR = 16  # evaluate one (pixel, Gaussian) pair whose alpha reaches alpha_min
 FLOPS_PER_BLEND = 81      # blend it in the forward (11) and back-propagate it (70)
 # Non-packed float32 vector peak of MI355X: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz.
 ALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
@@ -102,10 +102,11 @@ def main():
     info = r.bin()
     r.forward(counters=True)
     torch.cuda.synchronize()
-    E_eval, B, E_box = [int(x) for x in r.counters.cpu().tolist()]
+    E_eval, B, E_alpha = [int(x) for x in r.counters.cpu().tolist()]
     vis = [info.vis_count[v] for v in range(r.V)]
     M = int(info.num_instances)
-    log(f"[bench] visible {vis}, instances {M}, evaluated pairs {E_eval}, box pairs {E_box}, blends {B}")
+    log(f"[bench] visible {vis}, instances {M}, evaluated pairs {E_eval}, pairs past the alpha test {E_alpha}, "
+        f"blends {B}")
 
     if args.copy_calibration:
         src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
@@ -188,7 +189,7 @@ def main():
     pb_bytes = 2 * 4 * (10 + 3 * nk) * scene.n + (4 + 36) * sum(vis)
     log(f"[bench] projection backward: {pb_ms:.3f} ms; full iteration with it: {full_ms:.3f} ms")
 
-    flops = FLOPS_PER_BOX_PAIR * E_box + FLOPS_PER_BLEND * B
+    flops = FLOPS_PER_ALPHA_PAIR * E_alpha + FLOPS_PER_BLEND * B
     achieved = flops / (raster_fused_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     out = {
@@ -224,7 +225,7 @@ def main():
             "hbm_frac_algorithmic": None,
             "algorithmic_bytes": None,
         },
-        "counts": {"visible": vis, "instances": M, "evaluated_pairs": E_eval, "box_pairs": E_box, "blends": B},
+        "counts": {"visible": vis, "instances": M, "evaluated_pairs": E_eval, "alpha_pairs": E_alpha, "blends": B},
         "stages_ms": {"fused": stages_fused, "separate": stages_sep},
         "separate_path": {"ms_per_step": ms_sep, "blends_per_s": B / (ms_sep * 1e-3), "raster_ms": raster_sep_ms},
         "cpu_baseline": None,

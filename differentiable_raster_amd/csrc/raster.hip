@@ -122,29 +122,43 @@ __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Bat
         const int tx0 = lo & 0xFFFF, ty0 = lo >> 16, tx1 = hi & 0xFFFF;
         b.inst[k] = __float_as_int(r2.w) + (c.ty - ty0) * (tx1 - tx0 + 1) + (c.tx - tx0);
     }
-    // conservative block mask from the alpha_min box of the conic (Sigma' = conic^-1)
+    // conservative block mask: the 4x4 blocks that the ellipse {q <= Q}, Q = 2 ln(o / alpha_min),
+    // reaches.  Per block column the ellipse's vertical extent over the column's x-range is
+    // found from its lower (convex) and upper (concave) arcs: at the range ends, or at the
+    // ellipse's lowest / highest point when that lies inside.  The ellipse is taken 2 % larger in
+    // Q (1 % in every radius) and every range 0.05 px wider, far beyond float32 rounding; an
+    // ill-conditioned conic marks every block.
     uint32_t m = 0xFFFFu;
-    const float det = co.x * co.z - co.y * co.y;
+    const float A = co.x, B = co.y, C = co.z;
+    const float det = A * C - B * B;
     if (co.w <= amin) {
         m = 0u;  // never reaches alpha_min (the projection culls these already)
-    } else if (det > 0.0f && co.x * co.z <= 1e4f * det && isfinite(det)) {
-        const float Q = 2.0f * __logf(co.w / amin);
-        const float ex = 1.01f * sqrtf(Q * co.z / det) + 0.05f;
-        const float ey = 1.01f * sqrtf(Q * co.x / det) + 0.05f;
-        if (isfinite(ex) && isfinite(ey)) {
-            const float lx = xy.x - ex, hx = xy.x + ex, ly = xy.y - ey, hy = xy.y + ey;
-            uint32_t mx = 0u, my = 0u;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float cx0 = (float)(c.x0 + 4 * i) + 0.5f, cx1 = cx0 + 3.0f;
-                const float cy0 = (float)(c.y0 + 4 * i) + 0.5f, cy1 = cy0 + 3.0f;
-                mx |= (lx <= cx1 && hx >= cx0) ? (1u << i) : 0u;
-                my |= (ly <= cy1 && hy >= cy0) ? (1u << i) : 0u;
-            }
+    } else if (det > 0.0f && A * C <= 1e4f * det && isfinite(det)) {
+        const float Q = 2.04f * __logf(co.w / amin);
+        const float ex = sqrtf(Q * C / det), ey = sqrtf(Q * A / det);
+        const float xs = B * ey / A;  // dx of the lowest point (dy = -ey); the highest is at -xs
+        const float QC = Q * C, invC = 1.0f / C;
+        if (isfinite(ex) && isfinite(ey) && isfinite(xs)) {
             m = 0u;
 #pragma unroll
-            for (int jy = 0; jy < 4; jy++)
-                if ((my >> jy) & 1u) m |= mx << (4 * jy);
+            for (int i = 0; i < 4; i++) {
+                const float u0 = fmaxf((float)(c.x0 + 4 * i) + 0.45f - xy.x, -ex);
+                const float u1 = fminf((float)(c.x0 + 4 * i) + 3.55f - xy.x, ex);
+                if (!(u0 <= u1)) continue;
+                const float r0 = sqrtf(fmaxf(0.0f, fmaf(-det * u0, u0, QC)));
+                const float r1 = sqrtf(fmaxf(0.0f, fmaf(-det * u1, u1, QC)));
+                float ylo = fminf(-fmaf(B, u0, r0), -fmaf(B, u1, r1)) * invC;
+                float yhi = fmaxf(fmaf(-B, u0, r0), fmaf(-B, u1, r1)) * invC;
+                if (u0 <= xs && xs <= u1) ylo = -ey;
+                if (u0 <= -xs && -xs <= u1) yhi = ey;
+                ylo += xy.y - 0.05f;
+                yhi += xy.y + 0.05f;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float cy0 = (float)(c.y0 + 4 * j) + 0.5f, cy1 = cy0 + 3.0f;
+                    m |= (ylo <= cy1 && yhi >= cy0) ? (1u << (4 * j + i)) : 0u;
+                }
+            }
         }
     }
     b.mask[k] = (uint16_t)m;
@@ -208,17 +222,8 @@ struct Fwd {
 };
 
 struct Counts {
-    int64_t eval, blend, box;
+    int64_t eval, blend, hit;
 };
-
-// Diagnostic only: is the pixel inside the exact bounding box of {o exp(-q/2) >= alpha_min}?
-__device__ __forceinline__ bool in_alpha_box(float dx, float dy, float4 co, float amin) {
-    if (!(co.w > amin)) return false;
-    const float det = co.x * co.z - co.y * co.y;
-    const float Q = 2.0f * logf(co.w / amin);
-    const float ex = 1.001f * sqrtf(Q * co.z / det), ey = 1.001f * sqrtf(Q * co.x / det);
-    return fabsf(dx) <= ex && fabsf(dy) <= ey;
-}
 
 // Front-to-back over this block's list of the staged batch (positions j = jbase + k).  Every
 // lane evaluates the step without branches (the pair evaluation of eval_pair, written out) and
@@ -251,11 +256,8 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         const bool blend = hit && !(Tn < tmin);
         const float wgt = alpha * f.T;
         if (COUNT) {
-            if (work) {
-                cnt.eval++;
-                const float4 co = make_float4(-2.0f * kLn2 * q.x, -kLn2 * q.y, -2.0f * kLn2 * q.z, o);
-                cnt.box += in_alpha_box(dx, dy, co, a.p.alpha_min) ? 1 : 0;
-            }
+            cnt.eval += work ? 1 : 0;
+            cnt.hit += hit ? 1 : 0;
             cnt.blend += blend ? 1 : 0;
         }
         f.done = f.done || stop;
@@ -462,12 +464,12 @@ __device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
     for (int o = kWave / 2; o > 0; o >>= 1) {
         c.eval += __shfl_xor(c.eval, o);
         c.blend += __shfl_xor(c.blend, o);
-        c.box += __shfl_xor(c.box, o);
+        c.hit += __shfl_xor(c.hit, o);
     }
     if ((threadIdx.x & (kWave - 1)) == 0) {
         atomicAdd((unsigned long long*)&counters[0], (unsigned long long)c.eval);
         atomicAdd((unsigned long long*)&counters[1], (unsigned long long)c.blend);
-        atomicAdd((unsigned long long*)&counters[2], (unsigned long long)c.box);
+        atomicAdd((unsigned long long*)&counters[2], (unsigned long long)c.hit);
     }
 }
 

@@ -158,8 +158,9 @@ typedef enum { GS_LOSS_L1 = 0, GS_LOSS_EXTERNAL = 1 } gs_loss_mode;
 
 /* Optional per-call diagnostics: device int64 [3], accumulated (the caller zeroes them); pass
  * NULL to skip (counting selects a slower kernel variant).  [0] (pixel, list entry) pairs the
- * forward evaluated; [1] pairs blended; [2] evaluated pairs whose pixel lies inside the
- * entry's exact alpha_min bounding box (the pairs a per-Gaussian box test cannot skip). */
+ * forward evaluated; [1] pairs blended; [2] evaluated pairs whose alpha reaches alpha_min (the
+ * blended pairs plus, per pixel, at most the one at which it stops: every correct method must
+ * evaluate these, whatever it culls). */
 typedef int64_t gs_counters;
 
 const char* gs_version(void);

@@ -138,8 +138,9 @@ def test_counters_match_oracle(env):
     r = pipeline.Renderer(sc, st)
     r.project(); r.bin(); r.forward(counters=True)
     torch.cuda.synchronize()
-    ev, bl, box = [int(x) for x in r.counters.cpu().numpy()]
-    assert bl <= box <= ev
+    ev, bl, hit = [int(x) for x in r.counters.cpu().numpy()]
+    # pairs past the alpha test: the blends plus at most one stopping pair per pixel
+    assert bl <= hit <= min(ev, bl + 128 * 128)
     ref = oracle.iteration(sc, st, backward=False)[0]["fwd"]
     # blends are exact up to flagged decisions; the GPU culls pairs outside each wavefront's
     # quarter tile, so it evaluates fewer pairs than the oracle's plain per-pixel walk
