@@ -181,7 +181,7 @@ __device__ __forceinline__ Lists build_lists(const TileCtx& c, Batch& b, int cnt
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; r++) {
             const bool hit = (m >> block_bit(c.w, r)) & 1u;
-            const unsigned long long bal = __ballot(hit);
+            const unsigned long long bal = __builtin_amdgcn_ballot_w64(hit);
             if (hit) b.list[c.w * kRowsPerWave + r][len[r] + __popcll(bal & lt)] = (uint8_t)k;
             len[r] += __popcll(bal);
         }
@@ -189,7 +189,8 @@ __device__ __forceinline__ Lists build_lists(const TileCtx& c, Batch& b, int cnt
     __syncthreads();
     Lists l;
     l.len = c.row == 0 ? len[0] : c.row == 1 ? len[1] : c.row == 2 ? len[2] : len[3];
-    l.max_len = max(max(len[0], len[1]), max(len[2], len[3]));
+    // wave-uniform; readfirstlane lets the compiler keep the walks' loop counters in SGPRs
+    l.max_len = __builtin_amdgcn_readfirstlane(max(max(len[0], len[1]), max(len[2], len[3])));
     return l;
 }
 
@@ -218,7 +219,7 @@ __device__ __forceinline__ bool eval_pair(const TileCtx& c, const Batch& b, int 
 struct Fwd {
     float T, C0, C1, C2;
     int32_t last;
-    bool done;
+    float done;  // 1 once the pixel has stopped (a float, so that its test is one compare)
 };
 
 struct Counts {
@@ -234,9 +235,10 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
     const float amax = a.p.alpha_max, tmin = a.p.t_min;
     const uint8_t* lst = b.list[c.list_id];
     for (int i = 0; i < l.max_len; i++) {
-        const bool work = !f.done && i < l.len;
-        if (__ballot(work) == 0ull) break;
-        const int k = lst[i];  // past this lane's list: a stale index (< kBatch), unused
+        const bool work = (f.done == 0.0f) & (i < l.len);
+        // ballots of single compares cost no vector instruction
+        if ((__builtin_amdgcn_ballot_w64(f.done == 0.0f) & __builtin_amdgcn_ballot_w64(i < l.len)) == 0ull) break;
+        const int k = lst[i];  // past this lane's list: an earlier staged entry, unused
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
         const float4 oc = b.oc[k];
@@ -245,25 +247,29 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float bdx = q.y * dx;
         const float cdy = q.z * dy;
         const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, cdy * dy));
-        const bool hit = work && p2 >= q.w;
+        const bool hit = work & (p2 >= q.w);
         const float o = oc.x;
         const float G = __builtin_amdgcn_exp2f(p2);
         const float v = o * G;
-        const float alpha = fminf(amax, v);
-        const float oma = v <= amax ? fmaf(-o, G, 1.0f) : 1.0f - amax;
+        const bool unclamped = v <= amax;
+        const float alpha = unclamped ? v : amax;  // min(alpha_max, v): v is never NaN here
+        const float oma = unclamped ? fmaf(-o, G, 1.0f) : 1.0f - amax;
         const float Tn = f.T * oma;
-        const bool stop = hit && Tn < tmin;
-        const bool blend = hit && !(Tn < tmin);
-        const float wgt = alpha * f.T;
+        const bool below = Tn < tmin;
+        const bool stop = hit & below;
+        const bool blend = hit & !below;
+        // zero where the pair does not blend: every lane's staged colour is finite (the lists
+        // start zeroed, so even an index past a list names a staged entry), and 0 * c adds 0
+        const float wgt = blend ? alpha * f.T : 0.0f;
         if (COUNT) {
             cnt.eval += work ? 1 : 0;
             cnt.hit += hit ? 1 : 0;
             cnt.blend += blend ? 1 : 0;
         }
-        f.done = f.done || stop;
-        f.C0 = blend ? fmaf(wgt, oc.y, f.C0) : f.C0;
-        f.C1 = blend ? fmaf(wgt, oc.z, f.C1) : f.C1;
-        f.C2 = blend ? fmaf(wgt, oc.w, f.C2) : f.C2;
+        f.done = stop ? 1.0f : f.done;
+        f.C0 = fmaf(wgt, oc.y, f.C0);
+        f.C1 = fmaf(wgt, oc.z, f.C1);
+        f.C2 = fmaf(wgt, oc.w, f.C2);
         f.T = blend ? Tn : f.T;
         f.last = blend ? jbase + k + 1 : f.last;
     }
@@ -336,6 +342,14 @@ __device__ __forceinline__ void row_reduce_scatter(const float d[9], float& w0, 
         : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]), "v"(d[8]));
 }
 
+// The lanes of every 16-lane row that has a lane in the wave mask m.
+__device__ __forceinline__ unsigned long long rows_with(unsigned long long m) {
+    unsigned long long r = 0ull;
+#pragma unroll
+    for (int q = 0; q < 4; q++) r |= ((m >> (16 * q)) & 0xFFFFull) ? (0xFFFFull << (16 * q)) : 0ull;
+    return r;
+}
+
 // Back-to-front over this block's list of the staged batch (positions j = jbase + k).  Every
 // lane evaluates the step without branches; the results are kept where the pair contributes.
 // BG: the background is not black (its term in dL/dalpha is needed).
@@ -345,14 +359,16 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
     const float amax = a.p.alpha_max;
     const uint8_t* lst = b.list[c.list_id];
     const int quad = (c.lane >> 2) & 3;
-    const bool quad_lead = (c.lane & 3) == 0;
-    // accumulator rows of the components this lane's quad adds after the reduce-scatter
+    // accumulator row of the component this lane's quad adds as w0 after the reduce-scatter;
+    // its w1 component is two rows further
     float* const acc_w0 = acc.v[quad < 2 ? quad : quad + 3];
-    float* const acc_w1 = acc.v[quad < 2 ? quad + 2 : quad + 5];
     for (int i = l.max_len - 1; i >= 0; i--) {
         const int k = lst[i];  // past this lane's list: a stale index (< kBatch), unused
-        const bool active = i < l.len && jbase + k < row_nc;  // uniform over the row
-        if (__ballot(active) == 0ull) continue;
+        const int jk = jbase + k;
+        const bool active = (i < l.len) & (jk < row_nc);  // uniform over the row
+        // ballots of single compares cost no vector instruction
+        const unsigned long long am = __builtin_amdgcn_ballot_w64(i < l.len) & __builtin_amdgcn_ballot_w64(jk < row_nc);
+        if (am == 0ull) continue;
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
         const float4 oc = b.oc[k];
@@ -362,12 +378,15 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float bdx = q.y * dx;
         const float cdy = q.z * dy;
         const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, cdy * dy));
-        const bool contrib = active && jbase + k < s.nc && p2 >= q.w;
+        // bitwise: no short-circuit branch around the threshold's LDS read
+        const bool contrib = active & (jk < s.nc) & (p2 >= q.w);
+        const unsigned long long cm =
+            am & __builtin_amdgcn_ballot_w64(jk < s.nc) & __builtin_amdgcn_ballot_w64(p2 >= q.w);
         const float o = oc.x;
         const float G = __builtin_amdgcn_exp2f(p2);
         const float v = o * G;
         const bool unclamped = v <= amax;
-        const float alpha = fminf(amax, v);
+        const float alpha = unclamped ? v : amax;  // min(alpha_max, v): v is never NaN here
         const float oma = unclamped ? fmaf(-o, G, 1.0f) : 1.0f - amax;
         const float inv = __builtin_amdgcn_rcpf(oma);  // 1 - alpha >= 1 - alpha_max > 0 where it counts
         const float Tj = s.T * inv;
@@ -399,15 +418,17 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
             s.B2 = fmaf(alpha, e2, s.B2);
             s.T = Tj;
         }
-        const unsigned long long cm = __ballot(contrib);
         if (cm != 0ull) {
             float w0, w1, w2;
             row_reduce_scatter(d, w0, w1, w2);
-            if (quad_lead && ((cm >> (16 * c.row)) & 0xFFFFull) != 0ull) {
+            // the lanes that add: each quad's first lane, in rows with a contributing lane (the
+            // lane mask is formed with scalar instructions and used directly as the exec mask)
+            const unsigned long long rm = rows_with(cm);
+            if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x1111111111111111ull)) {
                 atomicAdd(&acc_w0[k], w0);
-                atomicAdd(&acc_w1[k], w1);
-                if (quad == 0) atomicAdd(&acc.v[4][k], w2);
+                atomicAdd(&acc_w0[k + 2 * (kBatch + 1)], w1);
             }
+            if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x0001000100010001ull)) atomicAdd(&acc.v[4][k], w2);
         }
     }
 }
@@ -473,6 +494,13 @@ __device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
     }
 }
 
+// Zero the block lists once per workgroup, so that an index read past a list's end always names
+// an entry that some batch staged (finite values).  Needs a barrier before the lists are read.
+__device__ __forceinline__ void zero_lists(Batch& b) {
+    static_assert(sizeof(b.list) == kBlock * sizeof(uint4), "one 16-byte store per thread");
+    reinterpret_cast<uint4*>(&b.list[0][0])[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 __device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
     for (int t = 0; t < 9; t++) acc.v[t][threadIdx.x] = 0.0f;
@@ -487,7 +515,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
     *last_cnt = 0;
     last_lists->len = last_lists->max_len = 0;
     for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
-        if (__syncthreads_count(f.done) == kBlock) break;
+        if (__syncthreads_count(f.done != 0.0f) == kBlock) break;
         const int cnt_b = min(kBatch, c.n - b0);
         if ((int)threadIdx.x < cnt_b) stage<INST>(a, c, b, threadIdx.x, b0 + threadIdx.x);
         __syncthreads();
@@ -528,11 +556,12 @@ __global__ __launch_bounds__(kBlock) void raster_fwd_kernel(RasterArgs a, float*
                                                             int32_t* n_contrib) {
     __shared__ Batch b;
     const TileCtx c = tile_ctx(a);
-    Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
+    Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, c.inside ? 0.0f : 1.0f};
     Counts cnt{0, 0, 0};
     int32_t last_b0;
     int last_cnt;
     Lists last_lists;
+    zero_lists(b);
     forward_tile<COUNT, false>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
     if (COUNT) add_counters(a.counters, cnt);
     if (!c.inside) return;
@@ -621,6 +650,7 @@ __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const 
     s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
     s.B0 = s.B1 = s.B2 = 0.0f;
     zero_acc(acc);
+    zero_lists(b);
     const int maxnc = block_max(s.nc, s_red);
     backward_tile<BG>(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s);
 }
@@ -632,12 +662,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     __shared__ Acc acc;
     __shared__ int s_red[kWaves];
     const TileCtx c = tile_ctx(a);
-    Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, !c.inside};
+    Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, c.inside ? 0.0f : 1.0f};
     Counts cnt{0, 0, 0};
     int32_t last_b0;
     int last_cnt;
     Lists last_lists;
     zero_acc(acc);
+    zero_lists(b);
     forward_tile<COUNT, true>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
     if (COUNT) add_counters(a.counters, cnt);
     // loss gradient in registers
