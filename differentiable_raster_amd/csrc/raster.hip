@@ -20,12 +20,17 @@
 //
 // The forward walks each block's list front to back; a workgroup stops staging once every pixel
 // has stopped.  The backward walks it back to front from n_contrib, recovering T by division by
-// (1 - alpha) and carrying the colour behind.  A row sums each entry's nine gradient components
-// over its 16 lanes with four DPP adds each and adds the sums into per-entry accumulators in LDS
-// (ds_add_f32); after each batch one thread per entry stores its sums as that (Gaussian, tile)
-// instance's partial record (instances numbered slot by slot, so a Gaussian's records are
-// contiguous), and a per-Gaussian pass adds up each Gaussian's records: the gradients need no
-// global atomics and every record is written once.  The fused
+// (1 - alpha) and carrying the colour behind.  It takes a staged batch in sub-batches of at most
+// 128 entries whose (entry, block) pairs fit a 256-slot log in LDS: every pair gets its own slot
+// (the pairs of earlier entries of the sub-batch plus the rank of the block among the entry's
+// mask bits).  A row sums
+// each entry's nine gradient components over its 16 lanes with DPP adds and stores the sums in
+// the pair's slot with plain LDS stores; after the walk, two threads per entry add up the
+// entry's slots in a fixed order and store the sums as that (Gaussian, tile) instance's partial
+// record (instances numbered slot by slot, so a Gaussian's records are contiguous), and a
+// per-Gaussian pass adds up each Gaussian's records.  The gradients need no atomics at all (LDS
+// float atomic adds execute one lane at a time), every record is written once, and the sums are
+// the same from run to run.  The fused
 // kernel runs both passes on one workgroup: per-pixel C, T and n_contrib stay in registers, dL/dC
 // is formed in registers, and the last staged forward batch (which holds the last blended entry
 // of every pixel of the tile) is reused as the first backward batch.
@@ -91,15 +96,18 @@ struct Batch {
     float4 q[kBatch];       // (a, b, c, thr): p2 = a dx^2 + b dx dy + c dy^2, blend iff p2 >= thr
     float4 oc[kBatch];      // (o, r, g, b)
     int32_t inst[kBatch];   // index of the (slot, tile) instance (backward only)
-    uint16_t mask[kBatch];  // 4x4 blocks of the tile the entry's alpha_min box touches
+    // [0]: the 4x4 blocks the entry's alpha_min ellipse reaches; [1] (backward): the number of
+    // (entry, block) pairs of the batch's earlier entries, its slot position in the log
+    uint16_t meta[kBatch][2];
     uint8_t list[kBlocks4][kBatch];
 };
 
-// Per-entry gradient accumulators of the backward (LDS).
-struct Acc {
-    // row stride kBatch + 1: the accumulators of one entry's nine components fall in different
-    // LDS banks, so the four lanes of a row that add them do not conflict
-    float v[9][kBatch + 1];
+// The backward's log: one slot of nine gradient sums per (entry, block) pair of a sub-batch.
+constexpr int kSlots = 256;
+constexpr int kSub = 2 * kWave;  // entries per sub-batch at most
+struct Log {
+    // row stride kSlots + 1: the nine components of a slot fall in different LDS banks
+    float v[9][kSlots + 1];
 };
 
 // Stage list position j of the tile into batch index k (one thread per entry): three 16-byte
@@ -161,7 +169,7 @@ __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Bat
             }
         }
     }
-    b.mask[k] = (uint16_t)m;
+    b.meta[k][0] = (uint16_t)m;
 }
 
 struct Lists {
@@ -177,7 +185,7 @@ __device__ __forceinline__ Lists build_lists(const TileCtx& c, Batch& b, int cnt
     const unsigned long long lt = (1ull << c.lane) - 1ull;
     for (int base = 0; base < cnt; base += kWave) {
         const int k = base + c.lane;
-        const uint32_t m = k < cnt ? (uint32_t)b.mask[k] : 0u;
+        const uint32_t m = k < cnt ? (uint32_t)b.meta[k][0] : 0u;
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; r++) {
             const bool hit = (m >> block_bit(c.w, r)) & 1u;
@@ -234,11 +242,13 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
                                          Fwd& f, Counts& cnt) {
     const float amax = a.p.alpha_max, tmin = a.p.t_min;
     const uint8_t* lst = b.list[c.list_id];
+    int k_next = lst[0];  // list entries are read one step ahead
     for (int i = 0; i < l.max_len; i++) {
         const bool work = (f.done == 0.0f) & (i < l.len);
         // ballots of single compares cost no vector instruction
         if ((__builtin_amdgcn_ballot_w64(f.done == 0.0f) & __builtin_amdgcn_ballot_w64(i < l.len)) == 0ull) break;
-        const int k = lst[i];  // past this lane's list: an earlier staged entry, unused
+        const int k = k_next;  // past this lane's list: an earlier staged entry, unused
+        k_next = lst[min(i + 1, kBatch - 1)];
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
         const float4 oc = b.oc[k];
@@ -354,16 +364,20 @@ __device__ __forceinline__ unsigned long long rows_with(unsigned long long m) {
 // lane evaluates the step without branches; the results are kept where the pair contributes.
 // BG: the background is not black (its term in dL/dalpha is needed).
 template <bool BG>
-__device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Acc& acc, Lists l,
-                                         int32_t jbase, int row_nc, Bwd& s) {
+__device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Log& log, Lists l,
+                                         int32_t jbase, int first, int row_nc, Bwd& s) {
     const float amax = a.p.alpha_max;
     const uint8_t* lst = b.list[c.list_id];
     const int quad = (c.lane >> 2) & 3;
-    // accumulator row of the component this lane's quad adds as w0 after the reduce-scatter;
-    // its w1 component is two rows further
-    float* const acc_w0 = acc.v[quad < 2 ? quad : quad + 3];
+    // log row of the component this lane's quad stores as w0 after the reduce-scatter; its w1
+    // component is two rows further
+    float* const log_w0 = log.v[quad < 2 ? quad : quad + 3];
+    // this row's block bit and the bits below it (its rank among an entry's blocks)
+    const uint32_t below = (1u << block_bit(c.w, c.row)) - 1u;
+    int k_next = lst[max(l.max_len - 1, 0)];  // list entries are read one step ahead
     for (int i = l.max_len - 1; i >= 0; i--) {
-        const int k = lst[i];  // past this lane's list: a stale index (< kBatch), unused
+        const int k = k_next;  // past this lane's list: an earlier staged entry, unused
+        k_next = lst[max(i - 1, 0)];
         const int jk = jbase + k;
         const bool active = (i < l.len) & (jk < row_nc);  // uniform over the row
         // ballots of single compares cost no vector instruction
@@ -372,6 +386,7 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
         const float4 oc = b.oc[k];
+        const uint32_t meta = *reinterpret_cast<const uint32_t*>(b.meta[k]);
         // the pair evaluation of eval_pair, for every lane
         const float dx = c.fpx - xy.x;
         const float dy = c.fpy - xy.y;
@@ -421,48 +436,121 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         if (cm != 0ull) {
             float w0, w1, w2;
             row_reduce_scatter(d, w0, w1, w2);
-            // the lanes that add: each quad's first lane, in rows with a contributing lane (the
-            // lane mask is formed with scalar instructions and used directly as the exec mask)
+            // the pair's slot: the entry's pairs position relative to the sub-batch's first entry,
+            // plus this block's rank among the entry's blocks
+            const int slot = (int)(meta >> 16) - first + __builtin_popcount(meta & below);
+            // the lanes that store: each quad's first lane, in rows with a contributing lane (the
+            // lane mask is formed with scalar instructions and used directly as the exec mask);
+            // the slots of other pairs stay zero
             const unsigned long long rm = rows_with(cm);
             if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x1111111111111111ull)) {
-                atomicAdd(&acc_w0[k], w0);
-                atomicAdd(&acc_w0[k + 2 * (kBatch + 1)], w1);
+                log_w0[slot] = w0;
+                log_w0[slot + 2 * (kSlots + 1)] = w1;
             }
-            if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x0001000100010001ull)) atomicAdd(&acc.v[4][k], w2);
+            if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x0001000100010001ull)) log.v[4][slot] = w2;
         }
     }
 }
 
-// After a backward batch: one thread per entry stores its accumulated gradient as the
-// instance's partial record (plain stores: every instance belongs to exactly one tile, and the
-// records start zeroed) and clears the accumulators.
-__device__ __forceinline__ void flush_batch(const RasterArgs& a, const Batch& b, Acc& acc, int cnt) {
-    __syncthreads();
+// Exclusive prefix over the staged batch of the entries' block counts (their (entry, block)
+// pairs), stored in meta[k][1].  Contains workgroup barriers; the staged masks must be visible.
+__device__ __forceinline__ void pair_prefix(const TileCtx& c, Batch& b, int cnt, int* s_wave) {
     const int k = threadIdx.x;
-    if (k < cnt) {
-        float d[9];
-        bool any = false;
+    const int pc = k < cnt ? __builtin_popcount((uint32_t)b.meta[k][0]) : 0;
+    int incl = pc;
 #pragma unroll
-        for (int t = 0; t < 9; t++) {
-            d[t] = acc.v[t][k];
-            any |= d[t] != 0.0f;
-            acc.v[t][k] = 0.0f;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (c.lane >= o) incl += y;
+    }
+    if (c.lane == kWave - 1) s_wave[c.w] = incl;
+    __syncthreads();
+    int off = 0;
+#pragma unroll
+    for (int q = 0; q < kWaves; q++) off += q < c.w ? s_wave[q] : 0;
+    if (k < cnt) b.meta[k][1] = (uint16_t)(off + incl - pc);
+    __syncthreads();
+}
+
+// The backward's sub-batch ending at batch index hi: the longest run of entries [lo, hi), at
+// most kSub, whose (entry, block) pairs fit the log.  Every wavefront computes the same lo.
+__device__ __forceinline__ int sub_batch(const TileCtx& c, const Batch& b, int hi) {
+    const int last = hi - 1;
+    const int end = (int)b.meta[last][1] + __builtin_popcount((uint32_t)b.meta[last][0]);  // pairs before hi
+    const int e0 = hi - 1 - c.lane, e1 = e0 - kWave;
+    const bool f0 = e0 >= 0 && end - (int)b.meta[max(e0, 0)][1] <= kSlots;
+    const bool f1 = e1 >= 0 && end - (int)b.meta[max(e1, 0)][1] <= kSlots;
+    // the entries that fit form a run down from hi: the prefix is non-decreasing
+    return hi - __popcll(__builtin_amdgcn_ballot_w64(f0)) - __popcll(__builtin_amdgcn_ballot_w64(f1));
+}
+
+// Each wavefront compacts sub-batch entries [lo, hi) (at most kSub) into the lists of its four
+// 4x4 blocks, in entry order.  Ends with a workgroup barrier: the previous sub-batch's gather
+// must be done before the walk stores into the log again.
+__device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int lo, int hi) {
+    int len[kRowsPerWave] = {0, 0, 0, 0};
+    const unsigned long long lt = (1ull << c.lane) - 1ull;
+#pragma unroll
+    for (int half = 0; half < kSub / kWave; half++) {
+        const int k = lo + half * kWave + c.lane;
+        const uint32_t m = k < hi ? (uint32_t)b.meta[k][0] : 0u;
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; r++) {
+            const bool hit = (m >> block_bit(c.w, r)) & 1u;
+            const unsigned long long bal = __builtin_amdgcn_ballot_w64(hit);
+            if (hit) b.list[c.w * kRowsPerWave + r][len[r] + __popcll(bal & lt)] = (uint8_t)k;
+            len[r] += __popcll(bal);
         }
+    }
+    __syncthreads();
+    Lists l;
+    l.len = c.row == 0 ? len[0] : c.row == 1 ? len[1] : c.row == 2 ? len[2] : len[3];
+    l.max_len = __builtin_amdgcn_readfirstlane(max(max(len[0], len[1]), max(len[2], len[3])));
+    return l;
+}
+
+// After a sub-batch's walk (and a barrier): two threads per entry of [lo, hi) add up the entry's
+// slots in slot order, clear them for the next sub-batch, apply the entry-constant factors and
+// store the sums as the instance's partial record (plain stores: every instance belongs to
+// exactly one tile, and the records start zeroed, so all-zero sums are not stored).  Thread part
+// 0 takes components 0-4 (mean and conic), part 1 takes 5-8 (opacity and colour).  `first` is the
+// slot position of entry lo.
+__device__ __forceinline__ void gather_sub_batch(const RasterArgs& a, const Batch& b, Log& log, int lo, int hi,
+                                                 int first) {
+    const int k = lo + (int)(threadIdx.x >> 1), part = threadIdx.x & 1;
+    if (k >= hi) return;
+    const int c0 = part == 0 ? 0 : 5;
+    const int nc = part == 0 ? 5 : 4;
+    const uint32_t meta = *reinterpret_cast<const uint32_t*>(b.meta[k]);
+    const int s0 = (int)(meta >> 16) - first, s1 = s0 + __builtin_popcount(meta & 0xFFFFu);
+    float d[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sl = s0; sl < s1; sl++) {
+#pragma unroll
+        for (int t = 0; t < 5; t++) {
+            if (t < nc) {
+                d[t] += log.v[c0 + t][sl];
+                log.v[c0 + t][sl] = 0.0f;
+            }
+        }
+    }
+    const bool any = d[0] != 0.0f || d[1] != 0.0f || d[2] != 0.0f || d[3] != 0.0f || d[4] != 0.0f;
+    // the bound only matters for bins and records of different calls (stale instance indices)
+    if (!any || (uint64_t)(uint32_t)b.inst[k] >= (uint64_t)a.num_instances) return;
+    float* rec = a.partials + (size_t)b.inst[k] * 9 + c0;
+    if (part == 0) {
         // the entry-constant factors of the mean and conic gradients (see bwd_walk)
         const float4 q = b.q[k];
         const float o = b.oc[k].x;
-        const float sx = d[0], sy = d[1];
-        d[0] = -kLn2 * o * fmaf(2.0f * q.x, sx, q.y * sy);
-        d[1] = -kLn2 * o * fmaf(q.y, sx, 2.0f * q.z * sy);
-        d[2] *= -0.5f * o;
-        d[3] *= -o;
-        d[4] *= -0.5f * o;
-        // the bound only matters for bins and records of different calls (stale instance indices)
-        if (any && (uint64_t)(uint32_t)b.inst[k] < (uint64_t)a.num_instances) {
-            float* rec = a.partials + (size_t)b.inst[k] * 9;
-#pragma unroll
-            for (int t = 0; t < 9; t++) rec[t] = d[t];
-        }
+        rec[0] = -kLn2 * o * fmaf(2.0f * q.x, d[0], q.y * d[1]);
+        rec[1] = -kLn2 * o * fmaf(q.y, d[0], 2.0f * q.z * d[1]);
+        rec[2] = d[2] * (-0.5f * o);
+        rec[3] = d[3] * -o;
+        rec[4] = d[4] * (-0.5f * o);
+    } else {
+        rec[0] = d[0];
+        rec[1] = d[1];
+        rec[2] = d[2];
+        rec[3] = d[3];
     }
 }
 
@@ -501,19 +589,19 @@ __device__ __forceinline__ void zero_lists(Batch& b) {
     reinterpret_cast<uint4*>(&b.list[0][0])[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-__device__ __forceinline__ void zero_acc(Acc& acc) {
+__device__ __forceinline__ void zero_log(Log& log) {
+    static_assert(kSlots == kBlock, "one slot per thread");
 #pragma unroll
-    for (int t = 0; t < 9; t++) acc.v[t][threadIdx.x] = 0.0f;
+    for (int t = 0; t < 9; t++) log.v[t][threadIdx.x] = 0.0f;
 }
 
 // Forward over the whole tile list.  On return *last_b0 is the list position of the last staged
-// batch (-1 if none), *last_cnt its entry count and *last_lists this lane's lists in it.
+// batch (-1 if none) and *last_cnt its entry count.
 template <bool COUNT, bool INST>
 __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Fwd& f, Counts& cnt,
-                                             int32_t* last_b0, int* last_cnt, Lists* last_lists) {
+                                             int32_t* last_b0, int* last_cnt) {
     *last_b0 = -1;
     *last_cnt = 0;
-    last_lists->len = last_lists->max_len = 0;
     for (int32_t b0 = 0; b0 < c.n; b0 += kBatch) {
         if (__syncthreads_count(f.done != 0.0f) == kBlock) break;
         const int cnt_b = min(kBatch, c.n - b0);
@@ -523,30 +611,36 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
         fwd_walk<COUNT>(a, c, b, l, b0, f, cnt);
         *last_b0 = b0;
         *last_cnt = cnt_b;
-        *last_lists = l;
     }
 }
 
 // Backward over list positions [0, maxnc); the batch starting at `resident_b0` (with
-// `resident_cnt` entries and this lane's lists `resident`) is already staged.  The gradient
-// accumulators must be zero on entry.
+// `resident_cnt` entries) is already staged.  The log must be zero on entry; it is zero again on
+// return.
 template <bool BG>
-__device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Acc& acc, int32_t maxnc,
-                                              int32_t resident_b0, int resident_cnt, Lists resident, Bwd& s) {
+__device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Log& log, int* s_wave,
+                                              int32_t maxnc, int32_t resident_b0, int resident_cnt, Bwd& s) {
     const int row_nc = row_max(s.nc);
     if (maxnc <= 0) return;
     for (int32_t b0 = ((maxnc - 1) / kBatch) * kBatch; b0 >= 0; b0 -= kBatch) {
-        Lists l = resident;
-        int cnt_b = resident_cnt;
+        // entries past maxnc contribute nowhere
+        int cnt_b = min(resident_cnt, maxnc - b0);
+        __syncthreads();  // the previous batch's gather is done with the staged records
         if (b0 != resident_b0) {
             cnt_b = min(kBatch, maxnc - b0);
-            __syncthreads();
             if ((int)threadIdx.x < cnt_b) stage<true>(a, c, b, threadIdx.x, b0 + threadIdx.x);
             __syncthreads();
-            l = build_lists(c, b, cnt_b);
         }
-        bwd_walk<BG>(a, c, b, acc, l, b0, row_nc, s);
-        flush_batch(a, b, acc, cnt_b);
+        pair_prefix(c, b, cnt_b, s_wave);
+        for (int hi = cnt_b; hi > 0;) {
+            const int lo = sub_batch(c, b, hi);
+            const int first = __builtin_amdgcn_readfirstlane((int)b.meta[lo][1]);
+            const Lists l = build_sub_lists(c, b, lo, hi);
+            bwd_walk<BG>(a, c, b, log, l, b0, first, row_nc, s);
+            __syncthreads();
+            gather_sub_batch(a, b, log, lo, hi, first);
+            hi = lo;
+        }
         resident_b0 = -1;
     }
 }
@@ -560,9 +654,8 @@ __global__ __launch_bounds__(kBlock) void raster_fwd_kernel(RasterArgs a, float*
     Counts cnt{0, 0, 0};
     int32_t last_b0;
     int last_cnt;
-    Lists last_lists;
     zero_lists(b);
-    forward_tile<COUNT, false>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
+    forward_tile<COUNT, false>(a, c, b, f, cnt, &last_b0, &last_cnt);
     if (COUNT) add_counters(a.counters, cnt);
     if (!c.inside) return;
     const size_t plane = (size_t)a.width * a.height;
@@ -626,10 +719,10 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis
 }
 
 template <bool BG>
-__global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const float* t_final, const int32_t* n_contrib,
-                                                            const float* dl, Grads gr) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void raster_bwd_kernel(
+    RasterArgs a, const float* t_final, const int32_t* n_contrib, const float* dl, Grads gr) {
     __shared__ Batch b;
-    __shared__ Acc acc;
+    __shared__ Log log;
     __shared__ int s_red[kWaves];
     const TileCtx c = tile_ctx(a);
     const size_t plane = (size_t)a.width * a.height;
@@ -649,27 +742,26 @@ __global__ __launch_bounds__(kBlock) void raster_bwd_kernel(RasterArgs a, const 
     s.Tfin = s.T;
     s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
     s.B0 = s.B1 = s.B2 = 0.0f;
-    zero_acc(acc);
+    zero_log(log);
     zero_lists(b);
     const int maxnc = block_max(s.nc, s_red);
-    backward_tile<BG>(a, c, b, acc, maxnc, -1, 0, Lists{0, 0}, s);
+    backward_tile<BG>(a, c, b, log, s_red, maxnc, -1, 0, s);
 }
 
 template <bool COUNT, bool BG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void raster_fused_kernel(RasterArgs a, int mode, const float* tgt, float scale,
                                                               float* image, float* loss_sum, Grads gr) {
     __shared__ Batch b;
-    __shared__ Acc acc;
+    __shared__ Log log;
     __shared__ int s_red[kWaves];
     const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, c.inside ? 0.0f : 1.0f};
     Counts cnt{0, 0, 0};
     int32_t last_b0;
     int last_cnt;
-    Lists last_lists;
-    zero_acc(acc);
+    zero_log(log);
     zero_lists(b);
-    forward_tile<COUNT, true>(a, c, b, f, cnt, &last_b0, &last_cnt, &last_lists);
+    forward_tile<COUNT, true>(a, c, b, f, cnt, &last_b0, &last_cnt);
     if (COUNT) add_counters(a.counters, cnt);
     // loss gradient in registers
     const size_t plane = (size_t)a.width * a.height;
@@ -712,7 +804,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     const int maxnc = block_max(s.nc, s_red);
     // every pixel's last blended entry lies in the last staged batch, so it is still resident
     s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
-    backward_tile<BG>(a, c, b, acc, maxnc, last_b0, last_cnt, last_lists, s);
+    backward_tile<BG>(a, c, b, log, s_red, maxnc, last_b0, last_cnt, s);
 }
 
 }  // namespace

@@ -242,7 +242,7 @@ gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float*
  * -dy^2/2).  Within a tile, each entry's contributions are summed over the pixels in LDS and
  * stored once, without atomics, as a partial record at the instance's index (see
  * gs_projected.inst_base) in the workspace; a per-Gaussian pass then sums each slot's partials
- * into grads.  ws: gs_raster_workspace_size(bins->count) bytes or more, 256-byte aligned.
+ * into grads.  Every sum is taken in a fixed order, so repeated calls give identical bits.  ws: gs_raster_workspace_size(bins->count) bytes or more, 256-byte aligned.
  */
 gs_status gs_raster_bwd(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
                         int32_t V, const gs_render_params* p, int32_t use_capped, const float* image,
