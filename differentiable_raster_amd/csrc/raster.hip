@@ -99,7 +99,10 @@ struct Batch {
     // [0]: the 4x4 blocks the entry's alpha_min ellipse reaches; [1] (backward): the number of
     // (entry, block) pairs of the batch's earlier entries, its slot position in the log
     uint16_t meta[kBatch][2];
-    uint8_t list[kBlocks4][kBatch];
+    union {
+        uint8_t list[kBlocks4][kBatch];  // forward: batch indices
+        uint16_t list16[kBlocks4][kBatch / 2];  // backward sub-batch: batch index | log slot << 8
+    };
 };
 
 // The backward's log: one slot of nine gradient sums per (entry, block) pair of a sub-batch.
@@ -142,10 +145,13 @@ __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Bat
     if (co.w <= amin) {
         m = 0u;  // never reaches alpha_min (the projection culls these already)
     } else if (det > 0.0f && A * C <= 1e4f * det && isfinite(det)) {
-        const float Q = 2.04f * __logf(co.w / amin);
-        const float ex = sqrtf(Q * C / det), ey = sqrtf(Q * A / det);
-        const float xs = B * ey / A;  // dx of the lowest point (dy = -ey); the highest is at -xs
-        const float QC = Q * C, invC = 1.0f / C;
+        // hardware reciprocals and square roots (about 1 ulp): far inside the margins
+        const float Q = 2.04f * __logf(co.w * __builtin_amdgcn_rcpf(amin));
+        const float rdet = __builtin_amdgcn_rcpf(det);
+        const float ex = __builtin_amdgcn_sqrtf(Q * C * rdet), ey = __builtin_amdgcn_sqrtf(Q * A * rdet);
+        // dx of the lowest point (dy = -ey); the highest is at -xs
+        const float xs = B * ey * __builtin_amdgcn_rcpf(A);
+        const float QC = Q * C, invC = __builtin_amdgcn_rcpf(C);
         if (isfinite(ex) && isfinite(ey) && isfinite(xs)) {
             m = 0u;
 #pragma unroll
@@ -153,8 +159,8 @@ __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Bat
                 const float u0 = fmaxf((float)(c.x0 + 4 * i) + 0.45f - xy.x, -ex);
                 const float u1 = fminf((float)(c.x0 + 4 * i) + 3.55f - xy.x, ex);
                 if (!(u0 <= u1)) continue;
-                const float r0 = sqrtf(fmaxf(0.0f, fmaf(-det * u0, u0, QC)));
-                const float r1 = sqrtf(fmaxf(0.0f, fmaf(-det * u1, u1, QC)));
+                const float r0 = __builtin_amdgcn_sqrtf(fmaxf(0.0f, fmaf(-det * u0, u0, QC)));
+                const float r1 = __builtin_amdgcn_sqrtf(fmaxf(0.0f, fmaf(-det * u1, u1, QC)));
                 float ylo = fminf(-fmaf(B, u0, r0), -fmaf(B, u1, r1)) * invC;
                 float yhi = fmaxf(fmaf(-B, u0, r0), fmaf(-B, u1, r1)) * invC;
                 if (u0 <= xs && xs <= u1) ylo = -ey;
@@ -365,19 +371,18 @@ __device__ __forceinline__ unsigned long long rows_with(unsigned long long m) {
 // BG: the background is not black (its term in dL/dalpha is needed).
 template <bool BG>
 __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Log& log, Lists l,
-                                         int32_t jbase, int first, int row_nc, Bwd& s) {
+                                         int32_t jbase, int row_nc, Bwd& s) {
     const float amax = a.p.alpha_max;
-    const uint8_t* lst = b.list[c.list_id];
+    const uint16_t* lst = b.list16[c.list_id];
     const int quad = (c.lane >> 2) & 3;
     // log row of the component this lane's quad stores as w0 after the reduce-scatter; its w1
     // component is two rows further
     float* const log_w0 = log.v[quad < 2 ? quad : quad + 3];
-    // this row's block bit and the bits below it (its rank among an entry's blocks)
-    const uint32_t below = (1u << block_bit(c.w, c.row)) - 1u;
-    int k_next = lst[max(l.max_len - 1, 0)];  // list entries are read one step ahead
+    uint32_t e_next = lst[max(l.max_len - 1, 0)];  // list entries are read one step ahead
     for (int i = l.max_len - 1; i >= 0; i--) {
-        const int k = k_next;  // past this lane's list: an earlier staged entry, unused
-        k_next = lst[max(i - 1, 0)];
+        // past this lane's list: an earlier entry (a staged index), unused
+        const int k = e_next & 0xFFu, slot = e_next >> 8;
+        e_next = lst[max(i - 1, 0)];
         const int jk = jbase + k;
         const bool active = (i < l.len) & (jk < row_nc);  // uniform over the row
         // ballots of single compares cost no vector instruction
@@ -386,7 +391,6 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
         const float4 oc = b.oc[k];
-        const uint32_t meta = *reinterpret_cast<const uint32_t*>(b.meta[k]);
         // the pair evaluation of eval_pair, for every lane
         const float dx = c.fpx - xy.x;
         const float dy = c.fpy - xy.y;
@@ -436,9 +440,6 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         if (cm != 0ull) {
             float w0, w1, w2;
             row_reduce_scatter(d, w0, w1, w2);
-            // the pair's slot: the entry's pairs position relative to the sub-batch's first entry,
-            // plus this block's rank among the entry's blocks
-            const int slot = (int)(meta >> 16) - first + __builtin_popcount(meta & below);
             // the lanes that store: each quad's first lane, in rows with a contributing lane (the
             // lane mask is formed with scalar instructions and used directly as the exec mask);
             // the slots of other pairs stay zero
@@ -485,20 +486,25 @@ __device__ __forceinline__ int sub_batch(const TileCtx& c, const Batch& b, int h
 }
 
 // Each wavefront compacts sub-batch entries [lo, hi) (at most kSub) into the lists of its four
-// 4x4 blocks, in entry order.  Ends with a workgroup barrier: the previous sub-batch's gather
-// must be done before the walk stores into the log again.
-__device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int lo, int hi) {
+// 4x4 blocks, in entry order, each list entry holding the batch index and the (entry, block)
+// pair's log slot: the pairs of the sub-batch's entries before it (`first` is the pair position
+// of entry lo) plus the block's rank among the entry's blocks.  Ends with a workgroup barrier:
+// the previous sub-batch's gather must be done before the walk stores into the log again.
+__device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int lo, int hi, int first) {
     int len[kRowsPerWave] = {0, 0, 0, 0};
     const unsigned long long lt = (1ull << c.lane) - 1ull;
 #pragma unroll
     for (int half = 0; half < kSub / kWave; half++) {
         const int k = lo + half * kWave + c.lane;
-        const uint32_t m = k < hi ? (uint32_t)b.meta[k][0] : 0u;
+        const uint32_t meta = k < hi ? *reinterpret_cast<const uint32_t*>(b.meta[k]) : 0u;
+        const int pos = (int)(meta >> 16) - first;
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; r++) {
-            const bool hit = (m >> block_bit(c.w, r)) & 1u;
+            const int bit = block_bit(c.w, r);
+            const bool hit = (meta >> bit) & 1u;
             const unsigned long long bal = __builtin_amdgcn_ballot_w64(hit);
-            if (hit) b.list[c.w * kRowsPerWave + r][len[r] + __popcll(bal & lt)] = (uint8_t)k;
+            const int slot = pos + __builtin_popcount(meta & ((1u << bit) - 1u));
+            if (hit) b.list16[c.w * kRowsPerWave + r][len[r] + __popcll(bal & lt)] = (uint16_t)(k | (slot << 8));
             len[r] += __popcll(bal);
         }
     }
@@ -635,8 +641,8 @@ __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx
         for (int hi = cnt_b; hi > 0;) {
             const int lo = sub_batch(c, b, hi);
             const int first = __builtin_amdgcn_readfirstlane((int)b.meta[lo][1]);
-            const Lists l = build_sub_lists(c, b, lo, hi);
-            bwd_walk<BG>(a, c, b, log, l, b0, first, row_nc, s);
+            const Lists l = build_sub_lists(c, b, lo, hi, first);
+            bwd_walk<BG>(a, c, b, log, l, b0, row_nc, s);
             __syncthreads();
             gather_sub_batch(a, b, log, lo, hi, first);
             hi = lo;
