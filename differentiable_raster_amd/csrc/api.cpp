@@ -194,6 +194,7 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     ra->n_tiles = proj->n_tiles;
     ra->partials = nullptr;
     ra->num_instances = bins->count;
+    ra->capped = use_capped ? 1 : 0;
     ra->counters = nullptr;
     return GS_OK;
 }

@@ -158,6 +158,7 @@ struct RasterArgs {
     const int32_t* n_tiles;      // backward: instances per slot
     float* partials;             // backward: [instances][9] per-instance gradient records
     int64_t num_instances;       // backward: records in use
+    int32_t capped;              // the lists are the top-K capped ones (some instances are in none)
     int64_t* counters;           // optional
 };
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s);

@@ -518,9 +518,8 @@ __device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int
 // After a sub-batch's walk (and a barrier): two threads per entry of [lo, hi) add up the entry's
 // slots in slot order, clear them for the next sub-batch, apply the entry-constant factors and
 // store the sums as the instance's partial record (plain stores: every instance belongs to
-// exactly one tile, and the records start zeroed, so all-zero sums are not stored).  Thread part
-// 0 takes components 0-4 (mean and conic), part 1 takes 5-8 (opacity and colour).  `first` is the
-// slot position of entry lo.
+// exactly one tile).  Thread part 0 takes components 0-4 (mean and conic), part 1 takes 5-8
+// (opacity and colour).  `first` is the slot position of entry lo.
 __device__ __forceinline__ void gather_sub_batch(const RasterArgs& a, const Batch& b, Log& log, int lo, int hi,
                                                  int first) {
     const int k = lo + (int)(threadIdx.x >> 1), part = threadIdx.x & 1;
@@ -539,9 +538,8 @@ __device__ __forceinline__ void gather_sub_batch(const RasterArgs& a, const Batc
             }
         }
     }
-    const bool any = d[0] != 0.0f || d[1] != 0.0f || d[2] != 0.0f || d[3] != 0.0f || d[4] != 0.0f;
     // the bound only matters for bins and records of different calls (stale instance indices)
-    if (!any || (uint64_t)(uint32_t)b.inst[k] >= (uint64_t)a.num_instances) return;
+    if ((uint64_t)(uint32_t)b.inst[k] >= (uint64_t)a.num_instances) return;
     float* rec = a.partials + (size_t)b.inst[k] * 9 + c0;
     if (part == 0) {
         // the entry-constant factors of the mean and conic gradients (see bwd_walk)
@@ -627,6 +625,19 @@ template <bool BG>
 __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Log& log, int* s_wave,
                                               int32_t maxnc, int32_t resident_b0, int resident_cnt, Bwd& s) {
     const int row_nc = row_max(s.nc);
+    // the instances of list positions [maxnc, n) get zero records: the walk never reaches them
+    for (int32_t j = maxnc + (int32_t)threadIdx.x; j < c.n; j += kBlock) {
+        const int32_t slot = a.vals[c.start + j];
+        const float4 r2 = a.rec[4 * (c.vbase + slot) + 2];
+        const int lo = __float_as_int(r2.y), hi = __float_as_int(r2.z);
+        const int tx0 = lo & 0xFFFF, ty0 = lo >> 16, tx1 = hi & 0xFFFF;
+        const int inst = __float_as_int(r2.w) + (c.ty - ty0) * (tx1 - tx0 + 1) + (c.tx - tx0);
+        if ((uint64_t)(uint32_t)inst < (uint64_t)a.num_instances) {
+            float* rec = a.partials + (size_t)inst * 9;
+#pragma unroll
+            for (int t = 0; t < 9; t++) rec[t] = 0.0f;
+        }
+    }
     if (maxnc <= 0) return;
     for (int32_t b0 = ((maxnc - 1) / kBatch) * kBatch; b0 >= 0; b0 -= kBatch) {
         // entries past maxnc contribute nowhere
@@ -841,11 +852,13 @@ static unsigned grid_for(int64_t n) {
     return (unsigned)b;
 }
 
-// Zero the partial records, run a backward kernel, then gather the partials per Gaussian.
+// Run a backward kernel, then gather the partial records per Gaussian.  The backward stores the
+// record of every instance in its lists; with capped lists the instances the cap dropped are in
+// none, so the records are zeroed first.
 template <typename Launch>
 static hipError_t with_partials(const RasterArgs& a, Grads g, hipStream_t s, Launch launch) {
     const int64_t n = a.num_instances * 9;
-    if (n > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.partials, n);
+    if (a.capped && n > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.partials, n);
     launch();
     hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(a.capacity)), dim3(256), 0, s, a.vis_count, a.V,
                        a.capacity, a.inst_base, a.n_tiles, a.partials, a.num_instances, g);
