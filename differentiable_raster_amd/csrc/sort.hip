@@ -26,6 +26,15 @@ constexpr int kMaxBits = 9;
 constexpr int kRadix = 1 << kMaxBits;
 constexpr int kWaves = kBlock / kWave;
 constexpr int kPer = kRadix / kBlock;  // digits per thread
+constexpr int kXcds = 8;                // MI355X: workgroups are dealt round-robin to 8 XCDs
+
+// Tile of workgroup `bid`: the workgroups that land on one XCD take a contiguous run of tiles, so
+// the neighbouring parts of each digit's output run are written through the same L2.  A
+// bijection of [0, nb) for any nb; upsweep and downsweep use the same one.
+__device__ __forceinline__ int32_t tile_of(int32_t bid, int32_t nb) {
+    const int32_t q = nb / kXcds, r = nb % kXcds, x = bid % kXcds, i = bid / kXcds;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
 
 __global__ __launch_bounds__(kBlock) void radix_upsweep_kernel(const uint32_t* keys, int32_t n, int shift, uint32_t mask,
                                                                int32_t nblocks, int32_t* hist) {
@@ -34,7 +43,8 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep_kernel(const uint32_t* k
 #pragma unroll
     for (int k = 0; k < kPer; k++) s_hist[k * kBlock + threadIdx.x] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kChunk;
+    const int32_t tile = tile_of(blockIdx.x, nblocks);
+    const int64_t base = (int64_t)tile * kChunk;
 #pragma unroll
     for (int r = 0; r < kItems; r++) {
         const int64_t e = base + r * kBlock + threadIdx.x;
@@ -44,7 +54,7 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep_kernel(const uint32_t* k
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         const int d = k * kBlock + threadIdx.x;
-        if (d < radix) hist[(size_t)d * nblocks + blockIdx.x] = s_hist[d];
+        if (d < radix) hist[(size_t)d * nblocks + tile] = s_hist[d];
     }
 }
 
@@ -97,6 +107,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const uint32_t mask = (1u << bits) - 1u;
     const int radix = 1 << bits;
+    const int32_t tile = tile_of(blockIdx.x, nblocks);
     // digit starts: exclusive scan of the totals (kPer consecutive digits per thread)
     {
         int v[kPer];
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
 #pragma unroll
         for (int k = 0; k < kPer; k++) {
             const int d = threadIdx.x * kPer + k;
-            s_base[d] = run + (d < radix ? rowpref[(size_t)d * nblocks + blockIdx.x] : 0);
+            s_base[d] = run + (d < radix ? rowpref[(size_t)d * nblocks + tile] : 0);
             run += v[k];
         }
     }
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
         for (int q = 0; q < kWaves; q++) s_whist[q][k * kBlock + threadIdx.x] = 0;
     __syncthreads();
     // rank within the wavefront's 1024 elements: rounds of 64 in input order
-    const int64_t wbase = (int64_t)blockIdx.x * kChunk + w * kWaveChunk;
+    const int64_t wbase = (int64_t)tile * kChunk + w * kWaveChunk;
     const unsigned long long lt = (1ull << lane) - 1ull;
     int* whist = s_whist[w];
     uint32_t key[kItems], val[kItems];
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
         }
     }
     __syncthreads();
-    const int valid_n = (int)min((int64_t)kChunk, (int64_t)n - (int64_t)blockIdx.x * kChunk);
+    const int valid_n = (int)min((int64_t)kChunk, (int64_t)n - (int64_t)tile * kChunk);
 #pragma unroll
     for (int r = 0; r < kItems; r++) {
         if (wbase + r * kWave + lane < n) {
