@@ -523,4 +523,51 @@ gs_status gs_fused_max_cap(int32_t* k) {
     return GS_OK;
 }
 
+size_t gs_grad_encode_workspace_size(int32_t capacity, int32_t V) {
+    if (capacity < 0 || V < 1 || V > GS_MAX_VIEWS) return 0;
+    return encode_workspace_bytes(capacity, V);
+}
+
+gs_status gs_grad_encode(int32_t V, int32_t capacity, const int32_t* vis_count, const int32_t* vis_ids,
+                         const gs_grads2d* grads, int32_t* keys, float* records, int32_t* view_offset, void* ws,
+                         size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (V < 1 || V > GS_MAX_VIEWS) return fail(GS_ERR_INVALID_ARGUMENT, "V=%d outside 1..%d", V, GS_MAX_VIEWS);
+    if (capacity < 0) return fail(GS_ERR_INVALID_ARGUMENT, "capacity < 0");
+    if ((int64_t)capacity * V >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARGUMENT, "V * capacity records exceed 2^31 - 1");
+    if (!vis_count || !vis_ids || !keys || !records || !view_offset)
+        return fail(GS_ERR_INVALID_ARGUMENT, "encode buffers are null");
+    if (!grads || !grads->d_mean2d || !grads->d_conic || !grads->d_opacity || !grads->d_color)
+        return fail(GS_ERR_INVALID_ARGUMENT, "grads are null");
+    const size_t need = encode_workspace_bytes(capacity, V);
+    if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "encode workspace %zu < %zu bytes", ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(GS_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
+    if (capacity == 0) {
+        // no slots: the offsets are all zero (a fill kernel, so that the call can be captured)
+        return hip_check(launch_fill_i32(view_offset, 0, V + 1, static_cast<hipStream_t>(stream)), "gs_grad_encode");
+    }
+    GradsIn g{grads->d_mean2d, grads->d_conic, grads->d_opacity, grads->d_color};
+    return hip_check(launch_grad_encode(V, capacity, vis_count, vis_ids, g, keys, records, view_offset, ws,
+                                        static_cast<hipStream_t>(stream)),
+                     "gs_grad_encode launch");
+}
+
+gs_status gs_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const int32_t* view_offset,
+                         const int32_t* keys, const float* records, gs_grads2d* owner, void* stream) {
+    g_last_error.clear();
+    if (V < 1 || V > GS_MAX_VIEWS) return fail(GS_ERR_INVALID_ARGUMENT, "V=%d outside 1..%d", V, GS_MAX_VIEWS);
+    if (n_owner < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_owner < 0");
+    if (max_records < 0 || max_records >= (int64_t(1) << 31))
+        return fail(GS_ERR_INVALID_ARGUMENT, "max_records outside [0, 2^31)");
+    if (!view_offset || !keys || !records) return fail(GS_ERR_INVALID_ARGUMENT, "decode buffers are null");
+    if (!owner || !owner->d_mean2d || !owner->d_conic || !owner->d_opacity || !owner->d_color)
+        return fail(GS_ERR_INVALID_ARGUMENT, "owner arrays are null");
+    if (max_records == 0 || n_owner == 0) return GS_OK;
+    GradsOut o{owner->d_mean2d, owner->d_conic, owner->d_opacity, owner->d_color};
+    return hip_check(launch_grad_decode(V, n_owner, max_records, view_offset, keys, records, o,
+                                        static_cast<hipStream_t>(stream)),
+                     "gs_grad_decode launch");
+}
+
 }  // extern "C"

@@ -174,6 +174,27 @@ hipError_t launch_raster_bwd(const RasterArgs& a, const float* image, const floa
                              const float* dl, Grads g, hipStream_t s);
 hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,
                                float* loss_sum, Grads g, hipStream_t s);
+
+// F2: sparse 2D gradient records.  Slot-indexed inputs ([V][capacity]) and owner outputs
+// ([V][n_owner]) in the layout of gs_grads2d.
+struct GradsIn {
+    const float* d_mean2d;  // [..][2]
+    const float* d_conic;   // [..][3]
+    const float* d_opacity;
+    const float* d_color;   // [..][3]
+};
+struct GradsOut {
+    float* d_mean2d;
+    float* d_conic;
+    float* d_opacity;
+    float* d_color;
+};
+size_t encode_workspace_bytes(int32_t capacity, int32_t V);
+hipError_t launch_grad_encode(int32_t V, int32_t capacity, const int32_t* vis_count, const int32_t* vis_ids,
+                              GradsIn g, int32_t* keys, float* records, int32_t* view_offset, void* ws,
+                              hipStream_t s);
+hipError_t launch_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const int32_t* view_offset,
+                              const int32_t* keys, const float* records, GradsOut o, hipStream_t s);
 int32_t fused_lds_entries();
 
 }  // namespace gsmi

@@ -105,6 +105,12 @@ _SIGS = {
     "gs_project_bwd": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
                                       _P(gs_projected), _P(gs_grads2d), _P(gs_grads3d), ctypes.c_void_p]),
     "gs_fused_max_cap": (ctypes.c_int, [_P(ctypes.c_int32)]),
+    "gs_grad_encode_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "gs_grad_encode": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                      _P(gs_grads2d), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "gs_grad_decode": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, _P(gs_grads2d), ctypes.c_void_p]),
 }
 
 _lib = None
@@ -251,3 +257,18 @@ def gs_raster_fused(cams, proj, bins, V, params, use_capped, mode, target_or_dl,
                                   _ptr(loss_sum), ctypes.byref(grads), _ptr(counters), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)),
            "gs_raster_fused")
+
+
+def gs_grad_encode_workspace_size(capacity: int, V: int) -> int:
+    return int(load().gs_grad_encode_workspace_size(capacity, V))
+
+
+def gs_grad_encode(V, capacity, vis_count, vis_ids, grads: gs_grads2d, keys, records, view_offset, ws, stream=None):
+    _check(load().gs_grad_encode(V, capacity, _ptr(vis_count), _ptr(vis_ids), ctypes.byref(grads), _ptr(keys),
+                                 _ptr(records), _ptr(view_offset), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "gs_grad_encode")
+
+
+def gs_grad_decode(V, n_owner, max_records, view_offset, keys, records, owner: gs_grads2d, stream=None):
+    _check(load().gs_grad_decode(V, n_owner, int(max_records), _ptr(view_offset), _ptr(keys), _ptr(records),
+                                 ctypes.byref(owner), _stream(stream)), "gs_grad_decode")

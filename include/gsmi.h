@@ -242,7 +242,8 @@ gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float*
  * -dy^2/2).  Within a tile, each entry's contributions are summed over the pixels in LDS and
  * stored once, without atomics, as a partial record at the instance's index (see
  * gs_projected.inst_base) in the workspace; a per-Gaussian pass then sums each slot's partials
- * into grads.  Every sum is taken in a fixed order, so repeated calls give identical bits.  ws: gs_raster_workspace_size(bins->count) bytes or more, 256-byte aligned.
+ * into grads.  Every sum is taken in a fixed order, so repeated calls give identical bits.
+ * ws: gs_raster_workspace_size(bins->count) bytes or more, 256-byte aligned.
  */
 gs_status gs_raster_bwd(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,
                         int32_t V, const gs_render_params* p, int32_t use_capped, const float* image,
@@ -290,6 +291,40 @@ gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams /*host [V]
 /* Entries of a tile list the rasterizers stage in LDS at a time (lists of any length are
  * processed batch by batch).  *k (host) receives it. */
 gs_status gs_fused_max_cap(int32_t* k);
+
+/*
+ * F2: sparse exchange of the per-view 2D gradient records (ByteSplat, English abstract: zero
+ * partial gradients are left out of the exchange between GPUs; an encoder kernel compacts the
+ * remaining records and a decoder kernel adds the received records directly into the arrays of
+ * the Gaussians' owner).  On one GPU the pair is the encoder and decoder of that exchange.
+ *
+ * gs_grad_encode: a record is the nine 2D gradient components of one (view v, visible slot
+ * s < vis_count[v]) of grads (d_mean2d x, y, d_conic A, B, C, d_opacity, d_color r, g, b, at
+ * index v*capacity + s, the layout the backward calls write).  Every record with a component
+ * other than zero (a NaN counts as non-zero, -0 as zero) is written as keys[k] =
+ * vis_ids[v*capacity + s] (its Gaussian) and records[k*9 .. k*9+8] = the nine components in that
+ * order, k increasing with (view, slot).  view_offset (device int32 [V+1]) receives the first
+ * record of each view and, at [V], the number of records.  keys and records must hold
+ * V*capacity records (all visible slots kept); view_offset must not overlap them.  ws:
+ * gs_grad_encode_workspace_size(capacity, V) bytes or more, 256-byte aligned.  capacity and
+ * vis_count/vis_ids are those of the gs_projected the gradients belong to.
+ */
+size_t gs_grad_encode_workspace_size(int32_t capacity, int32_t V);
+gs_status gs_grad_encode(int32_t V, int32_t capacity, const int32_t* vis_count, const int32_t* vis_ids,
+                         const gs_grads2d* grads, int32_t* keys, float* records, int32_t* view_offset, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * gs_grad_decode: adds every record k of an encoded stream into the owner arrays: for the view
+ * v with view_offset[v] <= k < view_offset[v+1], owner entry v*n_owner + keys[k] of each
+ * gs_grads2d array (owner->d_mean2d [V][n_owner][2], ...) is incremented by the record's
+ * components; keys outside [0, n_owner) are skipped.  Within one stream every (view, Gaussian)
+ * appears at most once, so a decode touches each entry at most once; decoding several streams in
+ * sequence accumulates them.  max_records (host) bounds view_offset[V] (V*capacity of the
+ * encode) and sizes the launch.
+ */
+gs_status gs_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const int32_t* view_offset,
+                         const int32_t* keys, const float* records, gs_grads2d* owner, void* stream);
 
 #ifdef __cplusplus
 }

@@ -450,3 +450,48 @@ def iteration(scene, settings, loss_scale: float = 1.0, views=None, backward: bo
                                          pixel_skip=(fwd["flag"] | unsure) if unsure is not None else fwd["flag"])
         out.append(res)
     return out
+
+
+def grad_records(vis_count, d_mean2d, d_conic, d_opacity, d_color) -> list:
+    """The nine-component 2D gradient record of every visible slot, per view:
+    (mean2d x, y, conic A, B, C, opacity, colour r, g, b).  Inputs are [V][capacity][...]."""
+    out = []
+    for v, n in enumerate(vis_count):
+        n = int(n)
+        out.append(np.concatenate([np.asarray(d_mean2d[v][:n]).reshape(n, 2), np.asarray(d_conic[v][:n]).reshape(n, 3),
+                                   np.asarray(d_opacity[v][:n]).reshape(n, 1), np.asarray(d_color[v][:n]).reshape(n, 3)],
+                                  axis=1))
+    return out
+
+
+def grad_encode(vis_count, vis_ids, records_per_view: list) -> dict:
+    """Sparse encoding of partial gradients (ByteSplat, English abstract: zero partial gradients
+    are left out of the exchange, and an encoder compacts the remaining records).  Per view in
+    slot order, a record is kept when any component differs from zero (NaN != 0 holds, so a NaN is
+    kept; -0 == 0, so -0 is dropped); it carries the slot's Gaussian index.  Returns keys,
+    records (K, 9) and view_offset (V + 1).
+    Parity: pinned by the round trip to the dense scatter and by counts from an explicit loop."""
+    keys, recs, off = [], [], [0]
+    for v, R in enumerate(records_per_view):
+        R = np.asarray(R)
+        keep = np.any(R != 0, axis=1)
+        keys.append(np.asarray(vis_ids[v][:R.shape[0]])[keep])
+        recs.append(R[keep])
+        off.append(off[-1] + int(keep.sum()))
+    return dict(keys=np.concatenate(keys) if keys else np.zeros(0, np.int32),
+                records=np.concatenate(recs) if recs else np.zeros((0, 9)), view_offset=np.array(off, np.int64))
+
+
+def grad_decode(view_offset, keys, records, owner: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """Aggregation on the owner (ByteSplat, English abstract: the decoder adds the received
+    gradients directly into the owner's arrays): owner[v, keys[k]] += records[k] for every record
+    k of view v, keys outside [0, n_owner) skipped, in `dtype` arithmetic.  owner is [V][n_owner][9].
+    Parity: pinned by the round trip to the dense scatter and by stream accumulation."""
+    out = np.array(owner, dtype=dtype, copy=True)
+    n_owner = out.shape[1]
+    for v in range(out.shape[0]):
+        for k in range(int(view_offset[v]), int(view_offset[v + 1])):
+            g = int(keys[k])
+            if 0 <= g < n_owner:
+                out[v, g] = (out[v, g] + np.asarray(records[k], dtype=dtype)).astype(dtype)
+    return out

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ["gs_project", "gs_bin_tiles", "gs_raster_fwd", "gs_raster_bwd", "gs_raster_fused",
                  "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
-                 "gs_project_bwd", "gs_raster_workspace_size",
+                 "gs_project_bwd", "gs_raster_workspace_size", "gs_grad_encode", "gs_grad_decode",
+                 "gs_grad_encode_workspace_size",
                  "gs_version", "gs_status_string", "gs_last_error"]:
         assert must in names, must
 
@@ -108,6 +109,30 @@ def test_project_bwd_rejects_bad_arguments(gs):
     assert b"null" in lib.gs_last_error()
     g_null = gs.gs_gaussians(100, FAKE, FAKE, None, FAKE, FAKE)
     assert call(ctypes.byref(g_null), 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2), ctypes.byref(g3)) == 1
+
+
+def test_grad_codec_rejects_bad_arguments(gs):
+    lib = gs.load()
+    g2 = gs.gs_grads2d(FAKE, FAKE, FAKE, FAKE)
+    need = lib.gs_grad_encode_workspace_size(1000, 2)
+    assert need > 0 and lib.gs_grad_encode_workspace_size(1000, 0) == 0
+    enc = lambda V, cap, a, b, c, gr, ws, wsb: lib.gs_grad_encode(V, cap, a, FAKE, gr, b, c, FAKE, ws, wsb, None)
+    assert enc(0, 1000, FAKE, FAKE, FAKE, ctypes.byref(g2), FAKE, need) == 1
+    assert enc(2, -1, FAKE, FAKE, FAKE, ctypes.byref(g2), FAKE, need) == 1
+    assert enc(2, 1000, None, FAKE, FAKE, ctypes.byref(g2), FAKE, need) == 1
+    assert enc(2, 1000, FAKE, None, FAKE, ctypes.byref(g2), FAKE, need) == 1
+    assert enc(2, 1000, FAKE, FAKE, FAKE, ctypes.byref(gs.gs_grads2d(FAKE, None, FAKE, FAKE)), FAKE, need) == 1
+    assert enc(2, 1000, FAKE, FAKE, FAKE, None, FAKE, need) == 1
+    assert enc(2, 1000, FAKE, FAKE, FAKE, ctypes.byref(g2), FAKE, need - 1) == 2
+    assert enc(2, 1000, FAKE, FAKE, FAKE, ctypes.byref(g2), FAKE + 16, need) == 1  # not 256-byte aligned
+    assert enc(16, 1 << 27, FAKE, FAKE, FAKE, ctypes.byref(g2), FAKE, need) == 1  # records past 2^31
+    dec = lambda V, n, m, o: lib.gs_grad_decode(V, n, m, FAKE, FAKE, FAKE, o, None)
+    assert dec(0, 10, 10, ctypes.byref(g2)) == 1
+    assert dec(1, -1, 10, ctypes.byref(g2)) == 1
+    assert dec(1, 10, -1, ctypes.byref(g2)) == 1
+    assert dec(1, 10, 10, None) == 1
+    assert dec(1, 10, 10, ctypes.byref(gs.gs_grads2d(FAKE, FAKE, FAKE, None))) == 1
+    assert lib.gs_grad_decode(1, 10, 10, None, FAKE, FAKE, ctypes.byref(g2), None) == 1
 
 
 def test_project_rejects_bad_arguments(gs):
