@@ -220,6 +220,28 @@ def main():
     log(f"[bench] sparse gradients: {kept} of {n_rec} records non-zero ({100.0 * (1 - kept / max(1, n_rec)):.1f} % "
         f"dropped); encode {enc_ms:.3f} ms, decode {dec_ms:.3f} ms")
 
+    # composition of pixel-level partial renders: two partials (colour on black + transmittance)
+    # of every view, composed over the background
+    P_cmp = 2
+    r.forward()
+    parts_c = [r.image, r.image.clone()]
+    parts_t = [r.t_final, r.t_final.clone()]
+    out_img = torch.empty_like(r.image)
+    out_t = torch.empty_like(r.t_final)
+    bg = settings.bg
+    gsmi.gs_compose(r.V, r.W, r.H, parts_c, parts_t, bg, out_img, out_t)
+    torch.cuda.synchronize()
+    ev_c = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(sp_steps)]
+    for a, b in ev_c:
+        a.record()
+        gsmi.gs_compose(r.V, r.W, r.H, parts_c, parts_t, bg, out_img, out_t)
+        b.record()
+    torch.cuda.synchronize()
+    cmp_ms = sum(a.elapsed_time(b) for a, b in ev_c) / sp_steps
+    # algorithmic bytes: 16 B (colour + transmittance) read per partial and pixel, 16 B written
+    cmp_bytes = (16 * P_cmp + 16) * r.V * r.W * r.H
+    log(f"[bench] composition of {P_cmp} partial renders: {cmp_ms:.3f} ms")
+
     flops = FLOPS_PER_ALPHA_PAIR * E_alpha + FLOPS_PER_BLEND * B
     achieved = flops / (raster_fused_ms * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -268,6 +290,11 @@ def main():
                        "frac": enc_bytes / (enc_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
             "decode": {"ms": dec_ms, "algorithmic_bytes": dec_bytes, "achieved": dec_bytes / (dec_ms * 1e-3) / 1e9,
                        "frac": dec_bytes / (dec_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+        },
+        "compose": {
+            "kernel": "compose_kernel (gs_compose)", "partials": P_cmp, "ms": cmp_ms, "bound": "hbm",
+            "algorithmic_bytes": cmp_bytes, "achieved": cmp_bytes / (cmp_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": cmp_bytes / (cmp_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         },
         "project_bwd": {
             "kernel": "project_bwd_kernel (gs_project_bwd)",

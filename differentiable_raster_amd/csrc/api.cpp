@@ -2,6 +2,7 @@
 // workspace carving, the single count read-back of gs_bin_tiles, and launch orchestration.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -568,6 +569,28 @@ gs_status gs_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const 
     return hip_check(launch_grad_decode(V, n_owner, max_records, view_offset, keys, records, o,
                                         static_cast<hipStream_t>(stream)),
                      "gs_grad_decode launch");
+}
+
+gs_status gs_compose(int32_t P, int32_t V, int32_t width, int32_t height, const float* const* colors,
+                     const float* const* t_finals, const float* bg, float* image, float* t_out, void* stream) {
+    g_last_error.clear();
+    if (P < 1 || P > GS_MAX_PARTIALS) return fail(GS_ERR_INVALID_ARGUMENT, "P=%d outside 1..%d", P, GS_MAX_PARTIALS);
+    if (V < 1 || V > GS_MAX_VIEWS) return fail(GS_ERR_INVALID_ARGUMENT, "V=%d outside 1..%d", V, GS_MAX_VIEWS);
+    if (width <= 0 || height <= 0) return fail(GS_ERR_INVALID_ARGUMENT, "image size %dx%d", width, height);
+    if (!colors || !t_finals || !bg || !image) return fail(GS_ERR_INVALID_ARGUMENT, "compose buffers are null");
+    ComposeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int k = 0; k < P; k++) {
+        if (!colors[k] || !t_finals[k]) return fail(GS_ERR_INVALID_ARGUMENT, "partial %d is null", k);
+        a.c[k] = colors[k];
+        a.t[k] = t_finals[k];
+    }
+    for (int c = 0; c < 3; c++) {
+        if (!std::isfinite(bg[c])) return fail(GS_ERR_INVALID_ARGUMENT, "bg is not finite");
+        a.bg[c] = bg[c];
+    }
+    return hip_check(launch_compose(P, V, (int64_t)width * height, a, image, t_out, static_cast<hipStream_t>(stream)),
+                     "gs_compose launch");
 }
 
 }  // extern "C"

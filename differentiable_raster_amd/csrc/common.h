@@ -195,6 +195,16 @@ hipError_t launch_grad_encode(int32_t V, int32_t capacity, const int32_t* vis_co
                               hipStream_t s);
 hipError_t launch_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const int32_t* view_offset,
                               const int32_t* keys, const float* records, GradsOut o, hipStream_t s);
+
+// F3: composition of P <= kMaxPartials partial renders (C [V][3][H][W], T [V][H][W]), front to back.
+constexpr int kMaxPartials = 16;
+struct ComposeArgs {
+    const float* c[kMaxPartials];
+    const float* t[kMaxPartials];
+    float bg[3];
+};
+hipError_t launch_compose(int32_t P, int32_t V, int64_t plane, const ComposeArgs& a, float* image, float* t_out,
+                          hipStream_t s);
 int32_t fused_lds_entries();
 
 }  // namespace gsmi

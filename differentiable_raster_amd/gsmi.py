@@ -111,6 +111,9 @@ _SIGS = {
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "gs_grad_decode": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, _P(gs_grads2d), ctypes.c_void_p]),
+    "gs_compose": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  _P(ctypes.c_void_p), _P(ctypes.c_void_p), _P(ctypes.c_float), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -272,3 +275,13 @@ def gs_grad_encode(V, capacity, vis_count, vis_ids, grads: gs_grads2d, keys, rec
 def gs_grad_decode(V, n_owner, max_records, view_offset, keys, records, owner: gs_grads2d, stream=None):
     _check(load().gs_grad_decode(V, n_owner, int(max_records), _ptr(view_offset), _ptr(keys), _ptr(records),
                                  ctypes.byref(owner), _stream(stream)), "gs_grad_decode")
+
+
+def gs_compose(V, width, height, colors, t_finals, bg, image, t_out=None, stream=None):
+    """colors / t_finals: sequences of device tensors, front to back."""
+    P = len(colors)
+    c_arr = (ctypes.c_void_p * P)(*[_ptr(c) for c in colors])
+    t_arr = (ctypes.c_void_p * P)(*[_ptr(t) for t in t_finals])
+    bg_arr = (ctypes.c_float * 3)(*[float(x) for x in bg])
+    _check(load().gs_compose(P, V, width, height, c_arr, t_arr, bg_arr, _ptr(image), _ptr(t_out), _stream(stream)),
+           "gs_compose")

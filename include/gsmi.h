@@ -326,6 +326,27 @@ gs_status gs_grad_encode(int32_t V, int32_t capacity, const int32_t* vis_count, 
 gs_status gs_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const int32_t* view_offset,
                          const int32_t* keys, const float* records, gs_grads2d* owner, void* stream);
 
+#define GS_MAX_PARTIALS 16
+
+/*
+ * F3: global composition of pixel-level partial renders (Splaxel, English abstract: each GPU
+ * renders its local subset of the Gaussians and only partial pixel values are exchanged and
+ * composed into the image).  A partial render of a subset of the Gaussians is gs_raster_fwd's
+ * image and t_final for that subset drawn on a black background (bg = 0): its premultiplied
+ * colour C and its final transmittance T.  Given P partials in front-to-back order, writes
+ *   image = C_1 + T_1 (C_2 + T_2 (... + T_{P-1} C_P)) + (T_1 T_2 ... T_P) bg,
+ *   t_out = T_1 T_2 ... T_P   (t_out may be NULL),
+ * per view and pixel.  For subsets whose Gaussians are depth-separated in every view (all of
+ * subset i in front of all of subset i+1 along every pixel's ray: per-pixel, every Gaussian of
+ * subset i sorts before every Gaussian of subset i+1) and with t_min = 0 (no early stop), this
+ * equals rendering the union up to float32 rounding.
+ * colors (host [P]): device [V][3][H][W] each; t_finals (host [P]): device [V][H][W] each;
+ * bg (host [3]); 1 <= P <= GS_MAX_PARTIALS.  image may alias colors[0] and t_out t_finals[0]
+ * (each pixel is read before it is written by the same thread).
+ */
+gs_status gs_compose(int32_t P, int32_t V, int32_t width, int32_t height, const float* const* colors,
+                     const float* const* t_finals, const float* bg, float* image, float* t_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -495,3 +495,20 @@ def grad_decode(view_offset, keys, records, owner: np.ndarray, dtype=np.float64)
             if 0 <= g < n_owner:
                 out[v, g] = (out[v, g] + np.asarray(records[k], dtype=dtype)).astype(dtype)
     return out
+
+
+def compose(colors: list, t_finals: list, bg) -> tuple:
+    """Global composition of pixel-level partial renders (Splaxel, English abstract: each GPU
+    renders its local subset and partial pixel values are composed into the image).  Partials
+    are (premultiplied colour C [V][3][H][W] drawn on black, final transmittance T [V][H][W]) in
+    front-to-back order; front to back, C += T_acc C_i and T_acc *= T_i, and the background is
+    added once: image = C + T_acc bg.  Float64.  Returns (image, T_acc).
+    Parity: pinned by the exactness of composing depth-separated subsets against compositing
+    their union (t_min = 0), identity of a transparent partial, and associativity."""
+    C = np.zeros(np.shape(colors[0]), np.float64)
+    T = np.ones(np.shape(t_finals[0]), np.float64)
+    for c, t in zip(colors, t_finals):
+        C = C + T[:, None] * np.asarray(c, np.float64)
+        T = T * np.asarray(t, np.float64)
+    bgv = np.asarray(bg, np.float64).reshape(1, 3, 1, 1)
+    return C + T[:, None] * bgv, T

@@ -51,3 +51,28 @@ def pinhole(width, height, f=None, cx=None, cy=None, R=None, t=None, fy=None):
 
 def logit(o):
     return float(np.log(o / (1.0 - o)))
+
+
+def subset(scene, idx, name=None):
+    """The scene restricted to the Gaussians idx (same cameras, target and dL/dpixel)."""
+    idx = np.asarray(idx)
+    return scenes.Scene(
+        name=name or f"{scene.name}-subset", means=np.ascontiguousarray(scene.means[:, idx]),
+        log_scales=np.ascontiguousarray(scene.log_scales[:, idx]), quats=np.ascontiguousarray(scene.quats[:, idx]),
+        opacity_logits=np.ascontiguousarray(scene.opacity_logits[idx]), sh=np.ascontiguousarray(scene.sh[:, idx]),
+        sh_degree=scene.sh_degree, cameras=scene.cameras, loss=scene.loss, target=scene.target, dldc=scene.dldc)
+
+
+def depth_layered_scene(n_per_layer, width, height, seed, layers=((2.0, 3.0), (5.0, 7.0)), views=1):
+    """A scene whose Gaussians come in depth layers (layer i entirely in front of layer i + 1 for
+    the identity-posed and slightly moved test cameras); returns (scene, index arrays per layer)."""
+    parts = [scenes.random_scene(n_per_layer, width, height, seed + 17 * i, views=views, z_range=z,
+                                 log_scale_mean=-3.0) for i, z in enumerate(layers)]
+    first = parts[0]
+    cat = lambda f: np.ascontiguousarray(np.concatenate([getattr(p, f) for p in parts], axis=-1))
+    sc = scenes.Scene(name=f"layers-{len(layers)}x{n_per_layer}-{width}x{height}-s{seed}", means=cat("means"),
+                      log_scales=cat("log_scales"), quats=cat("quats"), opacity_logits=cat("opacity_logits"),
+                      sh=cat("sh"), sh_degree=first.sh_degree, cameras=first.cameras, loss=first.loss,
+                      target=first.target, dldc=first.dldc)
+    idx = [np.arange(i * n_per_layer, (i + 1) * n_per_layer) for i in range(len(layers))]
+    return sc, idx

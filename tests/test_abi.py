@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     for must in ["gs_project", "gs_bin_tiles", "gs_raster_fwd", "gs_raster_bwd", "gs_raster_fused",
                  "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
                  "gs_project_bwd", "gs_raster_workspace_size", "gs_grad_encode", "gs_grad_decode",
-                 "gs_grad_encode_workspace_size",
+                 "gs_grad_encode_workspace_size", "gs_compose",
                  "gs_version", "gs_status_string", "gs_last_error"]:
         assert must in names, must
 
@@ -133,6 +133,22 @@ def test_grad_codec_rejects_bad_arguments(gs):
     assert dec(1, 10, 10, None) == 1
     assert dec(1, 10, 10, ctypes.byref(gs.gs_grads2d(FAKE, FAKE, FAKE, None))) == 1
     assert lib.gs_grad_decode(1, 10, 10, None, FAKE, FAKE, ctypes.byref(g2), None) == 1
+
+
+def test_compose_rejects_bad_arguments(gs):
+    lib = gs.load()
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    bg = (ctypes.c_float * 3)(0.0, 0.0, 0.0)
+    call = lambda P, V, W, H, c, t, b, img: lib.gs_compose(P, V, W, H, c, t, b, img, None, None)
+    assert call(0, 1, 8, 8, arr(FAKE), arr(FAKE), bg, FAKE) == 1
+    assert call(17, 1, 8, 8, arr(*[FAKE] * 17), arr(*[FAKE] * 17), bg, FAKE) == 1
+    assert call(1, 0, 8, 8, arr(FAKE), arr(FAKE), bg, FAKE) == 1
+    assert call(1, 1, 0, 8, arr(FAKE), arr(FAKE), bg, FAKE) == 1
+    assert call(2, 1, 8, 8, arr(FAKE, None), arr(FAKE, FAKE), bg, FAKE) == 1
+    assert call(1, 1, 8, 8, None, arr(FAKE), bg, FAKE) == 1
+    assert call(1, 1, 8, 8, arr(FAKE), arr(FAKE), None, FAKE) == 1
+    assert call(1, 1, 8, 8, arr(FAKE), arr(FAKE), bg, None) == 1
+    assert call(1, 1, 8, 8, arr(FAKE), arr(FAKE), (ctypes.c_float * 3)(float("nan"), 0.0, 0.0), FAKE) == 1
 
 
 def test_project_rejects_bad_arguments(gs):
