@@ -242,6 +242,41 @@ def main():
     cmp_bytes = (16 * P_cmp + 16) * r.V * r.W * r.H
     log(f"[bench] composition of {P_cmp} partial renders: {cmp_ms:.3f} ms")
 
+    # Adam over all parameters with this iteration's parameter gradients: the dense step and the
+    # deferred step (Gaussians whose gradient row is zero are left for a later replay)
+    from differentiable_raster_amd import adam as adam_mod
+    r.project_backward()
+    torch.cuda.synchronize()
+    nk = (scene.sh_degree + 1) ** 2
+    rows = [3, 3, 4, 1, 3 * nk]
+    lrs = [1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3]
+    grads3 = [r.d_means3, r.d_log_scales3, r.d_quats3, r.d_logits3, r.d_sh3]
+    zero_rows = int(sum((g.view(k, scene.n) != 0).any(0).logical_not().int() for g, k in zip(grads3, rows))
+                    .eq(len(rows)).sum().item())
+    adam_ms = {}
+    for kind in ("dense", "deferred"):
+        params = [t.clone() for t in (r.means, r.log_scales, r.quats, r.logits, r.sh)]
+        st = adam_mod.AdamState(scene.n, list(zip(params, grads3, rows, lrs)), deferred=kind == "deferred")
+        st.step()
+        torch.cuda.synchronize()
+        ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(sp_steps)]
+        for a, b in ev_a:
+            a.record()
+            st.step()
+            b.record()
+        torch.cuda.synchronize()
+        adam_ms[kind] = sum(a.elapsed_time(b) for a, b in ev_a) / sp_steps
+        del st, params
+    comps = sum(rows)
+    # algorithmic bytes: per component of an updated Gaussian the parameter and both moments read
+    # and written and the gradient read (28 B); the deferred step reads the whole gradient row of a
+    # skipped Gaussian (4 B per component) and the step counter of every Gaussian (+4 B written
+    # for the updated ones)
+    dense_bytes = 28 * comps * scene.n
+    lazy_bytes = 28 * comps * (scene.n - zero_rows) + 4 * comps * zero_rows + 4 * scene.n + 4 * (scene.n - zero_rows)
+    log(f"[bench] Adam: dense {adam_ms['dense']:.3f} ms, deferred {adam_ms['deferred']:.3f} ms "
+        f"({zero_rows} of {scene.n} Gaussians without gradient)")
+
     flops = FLOPS_PER_ALPHA_PAIR * E_alpha + FLOPS_PER_BLEND * B
     achieved = flops / (raster_fused_ms * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -295,6 +330,16 @@ def main():
             "kernel": "compose_kernel (gs_compose)", "partials": P_cmp, "ms": cmp_ms, "bound": "hbm",
             "algorithmic_bytes": cmp_bytes, "achieved": cmp_bytes / (cmp_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": cmp_bytes / (cmp_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        },
+        "adam": {
+            "kernel": "adam_step_kernel (gs_adam_step)", "gaussians": scene.n, "components": comps,
+            "gaussians_without_gradient": zero_rows, "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "dense": {"ms": adam_ms["dense"], "algorithmic_bytes": dense_bytes,
+                      "achieved": dense_bytes / (adam_ms["dense"] * 1e-3) / 1e9,
+                      "frac": dense_bytes / (adam_ms["dense"] * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+            "deferred": {"ms": adam_ms["deferred"], "algorithmic_bytes": lazy_bytes,
+                         "achieved": lazy_bytes / (adam_ms["deferred"] * 1e-3) / 1e9,
+                         "frac": lazy_bytes / (adam_ms["deferred"] * 1e-3) / (HBM_PEAK_GBS * 1e9)},
         },
         "project_bwd": {
             "kernel": "project_bwd_kernel (gs_project_bwd)",

@@ -593,4 +593,53 @@ gs_status gs_compose(int32_t P, int32_t V, int32_t width, int32_t height, const 
                      "gs_compose launch");
 }
 
+namespace {
+
+gs_status adam_args(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp, int32_t t,
+                    AdamArgs* a) {
+    if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
+    if (!groups || n_groups < 1 || n_groups > GS_MAX_ADAM_GROUPS)
+        return fail(GS_ERR_INVALID_ARGUMENT, "n_groups=%d outside 1..%d", n_groups, GS_MAX_ADAM_GROUPS);
+    if (!hp) return fail(GS_ERR_INVALID_ARGUMENT, "hp is null");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !(hp->eps > 0.0f))
+        return fail(GS_ERR_INVALID_ARGUMENT, "Adam needs 0 <= beta1, beta2 < 1 and eps > 0");
+    if (t < 1) return fail(GS_ERR_INVALID_ARGUMENT, "step t=%d < 1", t);
+    std::memset(a, 0, sizeof(*a));
+    for (int k = 0; k < n_groups; k++) {
+        const gs_adam_group& G = groups[k];
+        if (!G.param || !G.grad || !G.m || !G.v) return fail(GS_ERR_INVALID_ARGUMENT, "group %d has a null array", k);
+        if (G.rows < 1) return fail(GS_ERR_INVALID_ARGUMENT, "group %d: rows=%d", k, G.rows);
+        if (!std::isfinite(G.lr)) return fail(GS_ERR_INVALID_ARGUMENT, "group %d: lr is not finite", k);
+        if ((int64_t)G.rows * n >= (int64_t(1) << 40)) return fail(GS_ERR_INVALID_ARGUMENT, "group %d too large", k);
+        a->groups[k] = AdamGroup{G.param, G.grad, G.m, G.v, G.rows, G.lr};
+    }
+    a->n_groups = n_groups;
+    a->h = AdamHyper{hp->beta1, hp->beta2, hp->eps};
+    return GS_OK;
+}
+
+}  // namespace
+
+gs_status gs_adam_step(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
+                       int32_t t, int32_t* last_step, const int32_t* active, int32_t n_active, void* stream) {
+    g_last_error.clear();
+    AdamArgs a;
+    gs_status st = adam_args(n, groups, n_groups, hp, t, &a);
+    if (st != GS_OK) return st;
+    if (last_step && active && n_active < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_active < 0");
+    return hip_check(launch_adam_step(a, n, t, last_step, last_step ? active : nullptr, n_active,
+                                      static_cast<hipStream_t>(stream)),
+                     "gs_adam_step launch");
+}
+
+gs_status gs_adam_flush(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
+                        int32_t t, int32_t* last_step, void* stream) {
+    g_last_error.clear();
+    AdamArgs a;
+    gs_status st = adam_args(n, groups, n_groups, hp, t, &a);
+    if (st != GS_OK) return st;
+    if (!last_step) return fail(GS_ERR_INVALID_ARGUMENT, "last_step is null");
+    return hip_check(launch_adam_flush(a, n, t, last_step, static_cast<hipStream_t>(stream)), "gs_adam_flush launch");
+}
+
 }  // extern "C"

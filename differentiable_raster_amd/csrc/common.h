@@ -205,6 +205,28 @@ struct ComposeArgs {
 };
 hipError_t launch_compose(int32_t P, int32_t V, int64_t plane, const ComposeArgs& a, float* image, float* t_out,
                           hipStream_t s);
+
+// F4: Adam over parameter groups ([rows][n] float32 each), dense or deferred.
+constexpr int kMaxAdamGroups = 8;
+struct AdamGroup {
+    float* param;
+    const float* grad;
+    float* m;
+    float* v;
+    int32_t rows;
+    float lr;
+};
+struct AdamHyper {
+    float beta1, beta2, eps;
+};
+struct AdamArgs {
+    AdamGroup groups[kMaxAdamGroups];
+    int32_t n_groups;
+    AdamHyper h;
+};
+hipError_t launch_adam_step(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, const int32_t* active,
+                            int64_t n_active, hipStream_t s);
+hipError_t launch_adam_flush(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, hipStream_t s);
 int32_t fused_lds_entries();
 
 }  // namespace gsmi

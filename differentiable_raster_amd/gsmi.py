@@ -74,6 +74,15 @@ class gs_grads3d(ctypes.Structure):
                 ("d_opacity_logits", ctypes.c_void_p), ("d_sh", ctypes.c_void_p)]
 
 
+class gs_adam_group(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("rows", ctypes.c_int32), ("lr", ctypes.c_float)]
+
+
+class gs_adam_params(ctypes.Structure):
+    _fields_ = [("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
 _P = ctypes.POINTER
 _SIGS = {
     "gs_version": (ctypes.c_char_p, []),
@@ -114,6 +123,11 @@ _SIGS = {
     "gs_compose": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   _P(ctypes.c_void_p), _P(ctypes.c_void_p), _P(ctypes.c_float), ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]),
+    "gs_adam_step": (ctypes.c_int, [ctypes.c_int32, _P(gs_adam_group), ctypes.c_int32, _P(gs_adam_params),
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_void_p]),
+    "gs_adam_flush": (ctypes.c_int, [ctypes.c_int32, _P(gs_adam_group), ctypes.c_int32, _P(gs_adam_params),
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -285,3 +299,14 @@ def gs_compose(V, width, height, colors, t_finals, bg, image, t_out=None, stream
     bg_arr = (ctypes.c_float * 3)(*[float(x) for x in bg])
     _check(load().gs_compose(P, V, width, height, c_arr, t_arr, bg_arr, _ptr(image), _ptr(t_out), _stream(stream)),
            "gs_compose")
+
+
+def gs_adam_step(n, groups, hp: gs_adam_params, t, last_step=None, active=None, n_active=0, stream=None):
+    """groups: a ctypes array of gs_adam_group."""
+    _check(load().gs_adam_step(n, groups, len(groups), ctypes.byref(hp), int(t), _ptr(last_step), _ptr(active),
+                               int(n_active), _stream(stream)), "gs_adam_step")
+
+
+def gs_adam_flush(n, groups, hp: gs_adam_params, t, last_step, stream=None):
+    _check(load().gs_adam_flush(n, groups, len(groups), ctypes.byref(hp), int(t), _ptr(last_step), _stream(stream)),
+           "gs_adam_flush")

@@ -347,6 +347,48 @@ gs_status gs_grad_decode(int32_t V, int32_t n_owner, int64_t max_records, const 
 gs_status gs_compose(int32_t P, int32_t V, int32_t width, int32_t height, const float* const* colors,
                      const float* const* t_finals, const float* bg, float* image, float* t_out, void* stream);
 
+#define GS_MAX_ADAM_GROUPS 8
+
+/* One parameter group of gs_adam_step / gs_adam_flush: rows x n float32 arrays (row r of
+ * Gaussian i at r*n + i, the layout of gs_gaussians / gs_grads3d), device pointers. */
+typedef struct {
+    float* param;       /* [rows][n] parameters, updated in place */
+    const float* grad;  /* [rows][n] gradients of this step */
+    float* m;           /* [rows][n] first moments (start at 0) */
+    float* v;           /* [rows][n] second moments (start at 0) */
+    int32_t rows;
+    float lr;           /* learning rate of the group */
+} gs_adam_group;
+
+typedef struct {
+    float beta1, beta2, eps; /* [0.9, 0.999, 1e-15..1e-8] */
+} gs_adam_params;
+
+/*
+ * F4: one Adam step t >= 1 (textbook Adam per component: m = b1 m + (1 - b1) g,
+ * v = b2 v + (1 - b2) g^2, p -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps), in float32),
+ * dense or deferred (GS-Scale, English abstract: a deferred optimizer update avoids the memory
+ * accesses of Gaussians with zero gradients).
+ *  - last_step == NULL: dense; every Gaussian takes step t (active is ignored).
+ *  - last_step != NULL (device int32 [n], 0 before the first step): deferred.  The candidates are
+ *    all n Gaussians when active == NULL, and a candidate whose gradient is zero in every row of
+ *    every group is left untouched; with active (device int32 [n_active]) the candidates are the
+ *    listed Gaussians, each updated even if its gradient is zero, and the caller guarantees that
+ *    every unlisted Gaussian has a zero gradient at step t.  An updated Gaussian first replays
+ *    steps last_step+1 .. t-1 with a zero gradient, then takes step t; last_step becomes t.
+ *    Gaussians with last_step >= t are left alone.
+ * The replay performs the dense step's float32 operations in the same order, so after
+ * gs_adam_flush(t) the parameters and moments equal those of t dense steps bit for bit.
+ * groups (host [n_groups], 1 <= n_groups <= GS_MAX_ADAM_GROUPS), hp (host).
+ */
+gs_status gs_adam_step(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
+                       int32_t t, int32_t* last_step, const int32_t* active, int32_t n_active, void* stream);
+
+/* F4: bring every Gaussian of a deferred state to step t (replay of its steps after last_step
+ * with a zero gradient; last_step becomes t).  Same arguments as gs_adam_step. */
+gs_status gs_adam_flush(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
+                        int32_t t, int32_t* last_step, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

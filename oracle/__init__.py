@@ -512,3 +512,24 @@ def compose(colors: list, t_finals: list, bg) -> tuple:
         T = T * np.asarray(t, np.float64)
     bgv = np.asarray(bg, np.float64).reshape(1, 3, 1, 1)
     return C + T[:, None] * bgv, T
+
+
+def adam(params: list, grads_per_step: list, lrs: list, beta1: float, beta2: float, eps: float) -> tuple:
+    """Textbook Adam (the optimizer whose deferred update GS-Scale's English abstract describes as
+    skipping the memory accesses of Gaussians with zero gradients; the deferred form must equal
+    this one): for t = 1, 2, ..., per component, m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2,
+    p -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).  Float64.  params: list of arrays
+    (one per group); grads_per_step: list over steps of lists of arrays.  Returns (params, m, v).
+    Parity: pinned against torch.optim.Adam (float64, CPU), the first-step closed form
+    p - lr g / (|g| + eps) and the zero-gradient decay of the moments."""
+    p = [np.array(x, np.float64, copy=True) for x in params]
+    m = [np.zeros_like(x) for x in p]
+    v = [np.zeros_like(x) for x in p]
+    for t, grads in enumerate(grads_per_step, start=1):
+        bc1, bc2 = 1.0 - beta1 ** t, 1.0 - beta2 ** t
+        for k, g in enumerate(grads):
+            g = np.asarray(g, np.float64)
+            m[k] = beta1 * m[k] + (1.0 - beta1) * g
+            v[k] = beta2 * v[k] + (1.0 - beta2) * g * g
+            p[k] = p[k] - lrs[k] * ((m[k] / bc1) / (np.sqrt(v[k] / bc2) + eps))
+    return p, m, v

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     for must in ["gs_project", "gs_bin_tiles", "gs_raster_fwd", "gs_raster_bwd", "gs_raster_fused",
                  "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
                  "gs_project_bwd", "gs_raster_workspace_size", "gs_grad_encode", "gs_grad_decode",
-                 "gs_grad_encode_workspace_size", "gs_compose",
+                 "gs_grad_encode_workspace_size", "gs_compose", "gs_adam_step", "gs_adam_flush",
                  "gs_version", "gs_status_string", "gs_last_error"]:
         assert must in names, must
 
@@ -149,6 +149,27 @@ def test_compose_rejects_bad_arguments(gs):
     assert call(1, 1, 8, 8, arr(FAKE), arr(FAKE), None, FAKE) == 1
     assert call(1, 1, 8, 8, arr(FAKE), arr(FAKE), bg, None) == 1
     assert call(1, 1, 8, 8, arr(FAKE), arr(FAKE), (ctypes.c_float * 3)(float("nan"), 0.0, 0.0), FAKE) == 1
+
+
+def test_adam_rejects_bad_arguments(gs):
+    lib = gs.load()
+    grp = lambda **k: gs.gs_adam_group(**{**dict(param=FAKE, grad=FAKE, m=FAKE, v=FAKE, rows=3, lr=0.01), **k})
+    groups = (gs.gs_adam_group * 2)(grp(), grp(rows=48))
+    hp = gs.gs_adam_params(0.9, 0.999, 1e-15)
+    step = lambda n, g, ng, h, t, last=FAKE, act=None, na=0: lib.gs_adam_step(n, g, ng, h, t, last, act, na, None)
+    assert step(-1, groups, 2, ctypes.byref(hp), 1) == 1
+    assert step(10, None, 2, ctypes.byref(hp), 1) == 1
+    assert step(10, groups, 0, ctypes.byref(hp), 1) == 1
+    assert step(10, groups, 9, ctypes.byref(hp), 1) == 1
+    assert step(10, groups, 2, None, 1) == 1
+    assert step(10, groups, 2, ctypes.byref(gs.gs_adam_params(1.0, 0.999, 1e-15)), 1) == 1
+    assert step(10, groups, 2, ctypes.byref(gs.gs_adam_params(0.9, 0.999, 0.0)), 1) == 1
+    assert step(10, groups, 2, ctypes.byref(hp), 0) == 1
+    assert step(10, (gs.gs_adam_group * 1)(grp(m=None)), 1, ctypes.byref(hp), 1) == 1
+    assert step(10, (gs.gs_adam_group * 1)(grp(rows=0)), 1, ctypes.byref(hp), 1) == 1
+    assert step(10, (gs.gs_adam_group * 1)(grp(lr=float("inf"))), 1, ctypes.byref(hp), 1) == 1
+    assert step(10, groups, 2, ctypes.byref(hp), 1, FAKE, FAKE, -1) == 1
+    assert lib.gs_adam_flush(10, groups, 2, ctypes.byref(hp), 1, None, None) == 1
 
 
 def test_project_rejects_bad_arguments(gs):
