@@ -704,33 +704,73 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
 }
 
 // Per-Gaussian gather of the backward: the gradient of a visible slot is the sum of its
-// instances' partial records, which lie contiguously at [inst_base, inst_base + n_tiles).
+// instances' partial records, which lie contiguously at [inst_base, inst_base + n_tiles).  A lane
+// adds up the records of its own slot in instance order; a slot with more than kHeavy records
+// (a large splat) is added up by the whole wavefront instead (each lane a strided share, then a
+// fixed-order wavefront reduction), so that one large splat does not hold up 63 lanes.  Every sum
+// is taken in a fixed order.
+constexpr int kHeavy = 16;
+
+__device__ __forceinline__ void store_grad(const Grads& g, size_t i, const float d[9]) {
+    g.d_mean2d[i] = make_float2(d[0], d[1]);
+    g.d_conic[3 * i] = d[2];
+    g.d_conic[3 * i + 1] = d[3];
+    g.d_conic[3 * i + 2] = d[4];
+    g.d_opacity[i] = d[5];
+    g.d_color[3 * i] = d[6];
+    g.d_color[3 * i + 1] = d[7];
+    g.d_color[3 * i + 2] = d[8];
+}
+
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis_count, int32_t V, int32_t capacity,
                                                               const int32_t* inst_base, const int32_t* n_tiles,
                                                               const float* partials, int64_t num_instances, Grads g) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t wave = (int32_t)(blockIdx.x * (256 / kWave) + threadIdx.x / kWave);
+    const int32_t waves = (int32_t)(gridDim.x * (256 / kWave));
     for (int v = 0; v < V; v++) {
         const int32_t cnt = vis_count[v];
         const size_t base = (size_t)v * capacity;
-        for (int32_t s = blockIdx.x * 256 + threadIdx.x; s < cnt; s += gridDim.x * 256) {
+        // wavefront-uniform loop over groups of 64 consecutive slots
+        for (int32_t s0 = wave * kWave; s0 < cnt; s0 += waves * kWave) {
+            const int32_t s = s0 + lane;
             const size_t i = base + s;
-            const int64_t off = inst_base[i];
-            const float* rec = partials + (size_t)off * 9;
-            // clamped to the records that exist (only a stale projection could reach past them)
-            const int n = (off < 0 || off > num_instances) ? 0 : (int)min((int64_t)n_tiles[i], num_instances - off);
-            float d[9];
+            int64_t off = 0;
+            int n = 0;
+            if (s < cnt) {
+                off = inst_base[i];
+                // clamped to the records that exist (only a stale projection could reach past them)
+                n = (off < 0 || off > num_instances) ? 0 : (int)min((int64_t)n_tiles[i], num_instances - off);
+            }
+            const bool heavy = n > kHeavy;
+            if (s < cnt && !heavy) {
+                const float* rec = partials + (size_t)off * 9;
+                float d[9];
 #pragma unroll
-            for (int t = 0; t < 9; t++) d[t] = 0.0f;
-            for (int k = 0; k < n; k++)
+                for (int t = 0; t < 9; t++) d[t] = 0.0f;
+                for (int k = 0; k < n; k++)
 #pragma unroll
-                for (int t = 0; t < 9; t++) d[t] += rec[9 * k + t];
-            g.d_mean2d[i] = make_float2(d[0], d[1]);
-            g.d_conic[3 * i] = d[2];
-            g.d_conic[3 * i + 1] = d[3];
-            g.d_conic[3 * i + 2] = d[4];
-            g.d_opacity[i] = d[5];
-            g.d_color[3 * i] = d[6];
-            g.d_color[3 * i + 1] = d[7];
-            g.d_color[3 * i + 2] = d[8];
+                    for (int t = 0; t < 9; t++) d[t] += rec[9 * k + t];
+                store_grad(g, i, d);
+            }
+            unsigned long long hm = __builtin_amdgcn_ballot_w64(heavy);
+            while (hm != 0ull) {
+                const int src = __ffsll((long long)hm) - 1;
+                hm &= hm - 1ull;
+                const int64_t off0 = __shfl((long long)off, src);
+                const int n0 = __shfl(n, src);
+                const float* rec = partials + (size_t)off0 * 9;
+                float d[9];
+#pragma unroll
+                for (int t = 0; t < 9; t++) d[t] = 0.0f;
+                for (int k = lane; k < n0; k += kWave)
+#pragma unroll
+                    for (int t = 0; t < 9; t++) d[t] += rec[9 * k + t];
+#pragma unroll
+                for (int t = 0; t < 9; t++)
+                    for (int o = kWave / 2; o > 0; o >>= 1) d[t] += __shfl_xor(d[t], o);
+                if (lane == src) store_grad(g, i, d);
+            }
         }
     }
 }
