@@ -121,12 +121,12 @@ gs_status check_projected(const gs_projected* pr, bool records) {
 // Workspace layout of gs_bin_tiles.
 struct BinWs {
     uint32_t *dkey, *dval, *dkey_alt, *dval_alt;
-    int32_t *ntiles_sorted, *offsets;
+    int32_t* emit_offsets;  // [emit_chunks(n * V)] instance offsets of the emission chunks
     uint32_t *tkey_alt, *tval_alt;
     int32_t *hist, *partials;
     int32_t *kept, *cap_offsets;
-    uint32_t *order_keys, *order_vals, *order_keys_alt;  // [tiles_total] tile-order sort
-    BinReadback* readback;                               // counts and depth range read by the host
+    int32_t* order_hist;    // tile-order bucket counts per chunk
+    BinReadback* readback;  // counts and depth range read by the host
 };
 
 BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t inst_cap, size_t* bytes) {
@@ -140,22 +140,17 @@ BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t ins
     w.dval = c.take<uint32_t>(nv);
     w.dkey_alt = c.take<uint32_t>(nv);
     w.dval_alt = c.take<uint32_t>(nv);
-    w.ntiles_sorted = c.take<int32_t>(nv);
-    w.offsets = c.take<int32_t>(nv);
+    w.emit_offsets = c.take<int32_t>(emit_chunks((int32_t)nv) + 1);
     w.tkey_alt = c.take<uint32_t>(inst_cap);
     w.tval_alt = c.take<uint32_t>(inst_cap);
     w.hist = c.take<int32_t>(radix_hist_bytes(sort_n) / sizeof(int32_t));
     size_t part = radix_partials_bytes(sort_n);
-    const size_t p2 = scan_partials_bytes((int32_t)(nv > 0 ? nv : 1), 1);
     const size_t p3 = scan_partials_bytes(tiles_total, 1);
-    if (p2 > part) part = p2;
     if (p3 > part) part = p3;
     w.partials = c.take<int32_t>(part / sizeof(int32_t));
     w.kept = c.take<int32_t>(tiles_total);
     w.cap_offsets = c.take<int32_t>(tiles_total);
-    w.order_keys = c.take<uint32_t>(tiles_total);
-    w.order_vals = c.take<uint32_t>(tiles_total);
-    w.order_keys_alt = c.take<uint32_t>(tiles_total);
+    w.order_hist = c.take<int32_t>(tile_order_hist_ints(tiles_total) + 1);
     w.readback = c.take<BinReadback>(1);
     *bytes = c.used;
     return w;
@@ -430,8 +425,6 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         if (e == hipSuccess)
             e = launch_radix_sort(w.dkey, w.dval, w.dkey_alt, w.dval_alt, nvis, dbits, w.hist, w.partials, s);
         uint32_t* packed = (radix_passes(dbits) % 2 == 0) ? w.dval : w.dval_alt;
-        if (e == hipSuccess) e = launch_gather_ntiles(packed, proj->n_tiles, proj->capacity, nvis, w.ntiles_sorted, s);
-        if (e == hipSuccess) e = launch_scan_rows(w.ntiles_sorted, w.offsets, nullptr, nvis, 1, w.partials, s);
         // emit so that the tile sort's final pass lands in the output buffers
         const int tbits = bits_for(tiles_total);
         const bool odd = radix_passes(tbits) % 2 == 1;
@@ -440,14 +433,13 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         uint32_t* k1 = odd ? bins->tile_keys : w.tkey_alt;
         uint32_t* v1 = odd ? reinterpret_cast<uint32_t*>(bins->vals) : w.tval_alt;
         if (e == hipSuccess)
-            e = launch_emit(packed, w.offsets, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity, nvis,
-                            tiles_x, tpv, (int32_t)M, k0, reinterpret_cast<int32_t*>(v0), s);
+            e = launch_emit(packed, proj->n_tiles, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity,
+                            nvis, tiles_x, tpv, (int32_t)M, w.emit_offsets, k0, reinterpret_cast<int32_t*>(v0), s);
         if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
         if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);
     }
     if (e == hipSuccess && bins->tile_order)
-        e = launch_tile_order(bins->ranges, tiles_total, w.order_keys, w.order_vals, w.order_keys_alt, bins->tile_order,
-                              w.hist, w.partials, s);
+        e = launch_tile_order(bins->ranges, tiles_total, w.order_hist, bins->tile_order, s);
     if (e == hipSuccess && p->tile_cap > 0) {
         e = launch_cap_count(bins->ranges, tiles_total, p->tile_cap, w.kept, s);
         if (e == hipSuccess) e = launch_scan_rows(w.kept, w.cap_offsets, bins->num_capped, tiles_total, 1, w.partials, s);

@@ -103,64 +103,158 @@ __global__ __launch_bounds__(kBlock) void bin_counts_kernel(const int32_t* vis_c
     }
 }
 
-__global__ __launch_bounds__(kBlock) void gather_ntiles_kernel(const uint32_t* packed, const int32_t* n_tiles,
-                                                               int32_t capacity, int32_t total, int32_t* out) {
-    const int32_t r = blockIdx.x * kBlock + threadIdx.x;
-    if (r >= total) return;
-    const uint32_t p = packed[r];
-    out[r] = n_tiles[(size_t)(p >> kSlotBits) * capacity + (p & kSlotMask)];
+// Emission.  The slots in depth order are cut into chunks of kEmitChunk; within a chunk each
+// wavefront owns kEmitRounds x 64 consecutive slots, one per lane and round.  emit_count_kernel
+// sums each chunk's tile counts (n_tiles, the area of the slot's tile rectangle); after an
+// exclusive scan of those sums (one workgroup), emit_kernel adds the earlier wavefronts' totals
+// and an in-wave scan per round to the chunk's offset, and writes each slot's instances (its
+// tiles row-major) from there.
+constexpr int kEmitRounds = 4;
+constexpr int kEmitWaveSlots = kWave * kEmitRounds;
+constexpr int kEmitChunk = kBlock * kEmitRounds;
+constexpr int kEmitWaves = kBlock / kWave;
+
+struct EmitSlot {
+    uint32_t slot, vbase;
+    ushort4 rc;
+    int nt;
+};
+
+// GUARD: the chunk may reach past the last slot; such slots count no instance.  Chunks that lie
+// wholly inside take the unguarded form, whose loads the compiler can issue for all rounds at once.
+template <bool GUARD>
+__device__ __forceinline__ EmitSlot load_emit_slot(const uint32_t* packed, const ushort4* rect, int32_t capacity,
+                                                   int32_t total, int32_t tiles_per_view, int64_t e) {
+    EmitSlot q;
+    q.slot = 0;
+    q.vbase = 0;
+    q.rc = make_ushort4(0, 0, 0, 0);
+    q.nt = 0;
+    if (!GUARD || e < total) {
+        const uint32_t p = packed[e];
+        const uint32_t v = p >> kSlotBits;
+        q.slot = p & kSlotMask;
+        q.rc = rect[(size_t)v * capacity + q.slot];
+        q.vbase = v * (uint32_t)tiles_per_view;
+        q.nt = (q.rc.z - q.rc.x + 1) * (q.rc.w - q.rc.y + 1);
+    }
+    return q;
 }
 
-// One thread per slot in depth order writes the slot's instances (its tiles row-major) from its
-// offset on.  Rectangles of more than kSmallRect tiles are written by the whole wavefront, 64
-// instances per step, so that a few large splats do not serialize on one lane.
+// The slots of this lane in the wavefront's rounds.
+__device__ __forceinline__ void load_emit_rounds(const uint32_t* packed, const ushort4* rect, int32_t capacity,
+                                                 int32_t total, int32_t tiles_per_view, int64_t wbase, int lane,
+                                                 EmitSlot q[kEmitRounds]) {
+    if ((int64_t)(blockIdx.x + 1) * kEmitChunk <= total) {
+#pragma unroll
+        for (int r = 0; r < kEmitRounds; r++)
+            q[r] = load_emit_slot<false>(packed, rect, capacity, total, tiles_per_view, wbase + r * kWave + lane);
+    } else {
+#pragma unroll
+        for (int r = 0; r < kEmitRounds; r++)
+            q[r] = load_emit_slot<true>(packed, rect, capacity, total, tiles_per_view, wbase + r * kWave + lane);
+    }
+}
+
+__device__ __forceinline__ int wave_total(int x) {
+    for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Instance count of the slot at depth-order position e (0 past the last slot when GUARD).
+template <bool GUARD>
+__device__ __forceinline__ int slot_tiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity,
+                                          int32_t total, int64_t e) {
+    if (GUARD && e >= total) return 0;
+    const uint32_t p = packed[e];
+    return n_tiles[(size_t)(p >> kSlotBits) * capacity + (p & kSlotMask)];
+}
+
+__global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* packed, const int32_t* n_tiles,
+                                                            int32_t capacity, int32_t total, int32_t* chunk_counts) {
+    __shared__ int s_wave[kEmitWaves];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int64_t wbase = (int64_t)blockIdx.x * kEmitChunk + w * kEmitWaveSlots;
+    int sum = 0;
+    if ((int64_t)(blockIdx.x + 1) * kEmitChunk <= total) {
+#pragma unroll
+        for (int r = 0; r < kEmitRounds; r++)
+            sum += slot_tiles<false>(packed, n_tiles, capacity, total, wbase + r * kWave + lane);
+    } else {
+#pragma unroll
+        for (int r = 0; r < kEmitRounds; r++)
+            sum += slot_tiles<true>(packed, n_tiles, capacity, total, wbase + r * kWave + lane);
+    }
+    sum = wave_total(sum);
+    if (lane == 0) s_wave[w] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int q = 0; q < kEmitWaves; q++) t += s_wave[q];
+        chunk_counts[blockIdx.x] = t;
+    }
+}
+
+// Rectangles of more than kSmallRect tiles are written by the whole wavefront, 64 instances per
+// step, so that a few large splats do not serialize on one lane.
 constexpr int kSmallRect = 8;
 
-__global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* offsets, const ushort4* rect,
-                                                      int32_t capacity, int32_t total, int32_t tiles_x,
-                                                      int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                                                      int32_t* vals) {
-    const int32_t r = blockIdx.x * kBlock + threadIdx.x;
-    const int lane = threadIdx.x & 63;
-    const bool live = r < total;
-    uint32_t slot = 0, vbase = 0;
-    ushort4 rc = make_ushort4(0, 0, 0, 0);
-    int32_t o = 0;
-    int nt = 0;
-    if (live) {
-        const uint32_t p = packed[r];
-        const uint32_t v = p >> kSlotBits;
-        slot = p & kSlotMask;
-        rc = rect[(size_t)v * capacity + slot];
-        o = offsets[r];
-        vbase = v * (uint32_t)tiles_per_view;
-        nt = (rc.z - rc.x + 1) * (rc.w - rc.y + 1);
-    }
-    const bool big = nt > kSmallRect;
-    if (live && !big) {
-        for (int ty = rc.y; ty <= rc.w; ty++)
-            for (int tx = rc.x; tx <= rc.z; tx++) {
-                if (o >= M) return;  // never past the instance count sized on the host
-                tile_keys[o] = vbase + (uint32_t)(ty * tiles_x + tx);
-                vals[o] = (int32_t)slot;
-                o++;
-            }
-    }
-    unsigned long long bm = __ballot(big);
-    while (bm != 0ull) {
-        const int src = __ffsll((long long)bm) - 1;
-        bm &= bm - 1ull;
-        const int32_t o0 = __shfl(o, src);
-        const int n0 = __shfl(nt, src);
-        const int x0 = __shfl((int)rc.x, src), y0 = __shfl((int)rc.y, src);
-        const int w0 = __shfl((int)rc.z, src) - x0 + 1;
-        const uint32_t vb = (uint32_t)__shfl((int)vbase, src);
-        const int32_t sl = __shfl((int)slot, src);
-        for (int k = lane; k < n0; k += 64) {
-            const int dy = k / w0, dx = k - dy * w0;
-            if (o0 + k < M) {
-                tile_keys[o0 + k] = vb + (uint32_t)((y0 + dy) * tiles_x + x0 + dx);
-                vals[o0 + k] = sl;
+__global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* chunk_offsets,
+                                                      const ushort4* rect, int32_t capacity, int32_t total,
+                                                      int32_t tiles_x, int32_t tiles_per_view, int32_t M,
+                                                      uint32_t* tile_keys, int32_t* vals) {
+    __shared__ int s_wave[kEmitWaves];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int64_t wbase = (int64_t)blockIdx.x * kEmitChunk + w * kEmitWaveSlots;
+    EmitSlot q[kEmitRounds];
+    load_emit_rounds(packed, rect, capacity, total, tiles_per_view, wbase, lane, q);
+    int sum = 0;
+#pragma unroll
+    for (int r = 0; r < kEmitRounds; r++) sum += q[r].nt;
+    sum = wave_total(sum);
+    if (lane == 0) s_wave[w] = sum;
+    __syncthreads();
+    int32_t off = chunk_offsets[blockIdx.x];
+    for (int k = 0; k < w; k++) off += s_wave[k];
+#pragma unroll
+    for (int r = 0; r < kEmitRounds; r++) {
+        // inclusive scan of the round's counts over the wavefront
+        int inc = q[r].nt;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(inc, d);
+            if (lane >= d) inc += y;
+        }
+        const int32_t o = off + inc - q[r].nt;
+        off += __shfl(inc, kWave - 1);
+        const EmitSlot& e = q[r];
+        const bool big = e.nt > kSmallRect;
+        if (!big) {
+            int32_t oo = o;
+            for (int ty = e.rc.y; ty <= e.rc.w && e.nt > 0; ty++)
+                for (int tx = e.rc.x; tx <= e.rc.z; tx++) {
+                    if (oo < M) {  // never past the instance count sized on the host
+                        tile_keys[oo] = e.vbase + (uint32_t)(ty * tiles_x + tx);
+                        vals[oo] = (int32_t)e.slot;
+                    }
+                    oo++;
+                }
+        }
+        unsigned long long bm = __ballot(big);
+        while (bm != 0ull) {
+            const int src = __ffsll((long long)bm) - 1;
+            bm &= bm - 1ull;
+            const int32_t o0 = __shfl(o, src);
+            const int n0 = __shfl(e.nt, src);
+            const int x0 = __shfl((int)e.rc.x, src), y0 = __shfl((int)e.rc.y, src);
+            const int w0 = __shfl((int)e.rc.z, src) - x0 + 1;
+            const uint32_t vb = (uint32_t)__shfl((int)e.vbase, src);
+            const int32_t sl = __shfl((int)e.slot, src);
+            for (int k = lane; k < n0; k += kWave) {
+                const int dy = k / w0, dx = k - dy * w0;
+                if (o0 + k < M) {
+                    tile_keys[o0 + k] = vb + (uint32_t)((y0 + dy) * tiles_x + x0 + dx);
+                    vals[o0 + k] = sl;
+                }
             }
         }
     }
@@ -180,14 +274,130 @@ __global__ __launch_bounds__(kBlock) void ranges_kernel(const uint32_t* keys, in
     if (j == M - 1 || keys[j + 1] != k) ranges[2 * (size_t)k + 1] = j + 1;
 }
 
-// Heavy-first schedule: key = clz(n + 1) = 31 - floor(log2(n + 1)) in [0, 31] for a tile with n
-// entries; a stable sort on this 5-bit key (ties in tile order) puts the longest lists first.
-__global__ __launch_bounds__(kBlock) void tile_order_keys_kernel(const int32_t* ranges, int32_t n_tiles_total,
-                                                                 uint32_t* keys, uint32_t* vals) {
-    const int32_t t = blockIdx.x * kBlock + threadIdx.x;
-    if (t >= n_tiles_total) return;
-    keys[t] = (uint32_t)__clz(ranges[2 * t + 1] - ranges[2 * t] + 1);
-    vals[t] = (uint32_t)t;
+// Heavy-first schedule: a stable counting sort of the tiles on the bucket key clz(n + 1) =
+// 31 - floor(log2(n + 1)) in [0, 31] of a tile with n entries (ties in tile order), so the
+// longest lists come first.  The tiles are cut into chunks of kOrderChunk; within a chunk each
+// wavefront owns kOrderRounds x 64 consecutive tiles.  order_hist_kernel writes each chunk's
+// bucket counts (bucket-major); order_scatter_kernel turns all chunks' counts into the first
+// position of each bucket for its chunk, ranks its tiles stably and writes them there.
+constexpr int kOrderBuckets = 32;
+constexpr int kOrderBits = 5;
+constexpr int kOrderRounds = 8;
+constexpr int kOrderWaveTiles = kWave * kOrderRounds;
+constexpr int kOrderChunk = kBlock * kOrderRounds;
+constexpr int kOrderWaves = kBlock / kWave;
+
+__device__ __forceinline__ uint32_t order_key(const int32_t* ranges, int64_t t) {
+    return (uint32_t)__clz(ranges[2 * t + 1] - ranges[2 * t] + 1);
+}
+
+// Per round: the lanes of the wavefront whose valid tile has the same bucket as this lane's.
+__device__ __forceinline__ unsigned long long same_bucket(bool valid, uint32_t d) {
+    unsigned long long same = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+    for (int b = 0; b < kOrderBits; b++) {
+        const bool bit = (d >> b) & 1u;
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(bit);
+        same &= bit ? m : ~m;
+    }
+    return same;
+}
+
+__global__ __launch_bounds__(kBlock) void order_hist_kernel(const int32_t* ranges, int32_t n_tiles_total,
+                                                            int32_t nchunks, int32_t* hist) {
+    __shared__ int s_hist[kOrderBuckets];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    if (threadIdx.x < kOrderBuckets) s_hist[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t wbase = (int64_t)blockIdx.x * kOrderChunk + w * kOrderWaveTiles;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int r = 0; r < kOrderRounds; r++) {
+        const int64_t t = wbase + r * kWave + lane;
+        const bool valid = t < n_tiles_total;
+        const uint32_t d = valid ? order_key(ranges, t) : 0u;
+        const unsigned long long same = same_bucket(valid, d);
+        // one LDS add per bucket present in the round
+        if (valid && (same & lt) == 0ull) atomicAdd(&s_hist[d], __popcll(same));
+    }
+    __syncthreads();
+    if (threadIdx.x < kOrderBuckets) hist[(size_t)threadIdx.x * nchunks + blockIdx.x] = s_hist[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kBlock) void order_scatter_kernel(const int32_t* ranges, int32_t n_tiles_total,
+                                                               int32_t nchunks, const int32_t* hist, int32_t* order) {
+    constexpr int kParts = kBlock / kOrderBuckets;
+    __shared__ int s_tot[kParts][kOrderBuckets], s_pre[kParts][kOrderBuckets];
+    __shared__ int s_base[kOrderBuckets];
+    __shared__ int s_whist[kOrderWaves][kOrderBuckets];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    // every bucket's total over all chunks and its count in the chunks before this one
+    {
+        const int d = threadIdx.x % kOrderBuckets, part = threadIdx.x / kOrderBuckets;
+        int tot = 0, pre = 0;
+        for (int32_t c = part; c < nchunks; c += kParts) {
+            const int x = hist[(size_t)d * nchunks + c];
+            tot += x;
+            pre += c < (int32_t)blockIdx.x ? x : 0;
+        }
+        s_tot[part][d] = tot;
+        s_pre[part][d] = pre;
+        for (int i = threadIdx.x; i < kOrderWaves * kOrderBuckets; i += kBlock)
+            s_whist[i / kOrderBuckets][i % kOrderBuckets] = 0;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        // exclusive scan of the bucket totals (32 lanes of the first wavefront)
+        const int d = lane;
+        int tot = 0, pre = 0;
+        if (d < kOrderBuckets)
+            for (int q = 0; q < kParts; q++) {
+                tot += s_tot[q][d];
+                pre += s_pre[q][d];
+            }
+        int inc = tot;
+        for (int o = 1; o < kOrderBuckets; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
+        if (d < kOrderBuckets) s_base[d] = inc - tot + pre;
+    }
+    __syncthreads();
+    // stable rank within the wavefront's tiles: rounds of 64 in tile order; the wavefront's LDS
+    // operations are performed in order, so every lane reads the count before the leader of its
+    // bucket adds this round's
+    const int64_t wbase = (int64_t)blockIdx.x * kOrderChunk + w * kOrderWaveTiles;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int* whist = s_whist[w];
+    uint32_t key[kOrderRounds];
+    int rank[kOrderRounds];
+#pragma unroll
+    for (int r = 0; r < kOrderRounds; r++) {
+        const int64_t t = wbase + r * kWave + lane;
+        const bool valid = t < n_tiles_total;
+        const uint32_t d = valid ? order_key(ranges, t) : 0u;
+        const unsigned long long same = same_bucket(valid, d);
+        const int before = __popcll(same & lt);
+        const int seen = whist[d];
+        key[r] = d;
+        rank[r] = seen + before;
+        if (valid && before == 0) whist[d] = seen + __popcll(same);
+    }
+    __syncthreads();
+    // each wavefront's first position within its bucket in this chunk
+    if (threadIdx.x < kOrderBuckets) {
+        int run = 0;
+        for (int q = 0; q < kOrderWaves; q++) {
+            const int c = s_whist[q][threadIdx.x];
+            s_whist[q][threadIdx.x] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kOrderRounds; r++) {
+        const int64_t t = wbase + r * kWave + lane;
+        if (t < n_tiles_total) order[s_base[key[r]] + whist[key[r]] + rank[r]] = (int32_t)t;
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void cap_count_kernel(const int32_t* ranges, int32_t n_tiles_total, int32_t K,
@@ -322,20 +532,19 @@ hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count
     return hipGetLastError();
 }
 
-hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity, int32_t total,
-                                int32_t* out, hipStream_t s) {
-    if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_ntiles_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, packed, n_tiles, capacity,
-                       total, out);
-    return hipGetLastError();
-}
+int32_t emit_chunks(int32_t total) { return total > 0 ? (total + kEmitChunk - 1) / kEmitChunk : 0; }
 
-hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
-                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                       int32_t* vals, hipStream_t s) {
-    if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(emit_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, packed, offsets, rect, capacity,
-                       total, tiles_x, tiles_per_view, M, tile_keys, vals);
+hipError_t launch_emit(const uint32_t* packed, const int32_t* n_tiles, const ushort4* rect, int32_t capacity,
+                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets,
+                       uint32_t* tile_keys, int32_t* vals, hipStream_t s) {
+    const int32_t nc = emit_chunks(total);
+    if (nc == 0) return hipSuccess;
+    hipLaunchKernelGGL(emit_count_kernel, dim3(nc), dim3(kBlock), 0, s, packed, n_tiles, capacity, total,
+                       chunk_offsets);
+    const hipError_t e = launch_scan_small(chunk_offsets, nc, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(emit_kernel, dim3(nc), dim3(kBlock), 0, s, packed, chunk_offsets, rect, capacity, total, tiles_x,
+                       tiles_per_view, M, tile_keys, vals);
     return hipGetLastError();
 }
 
@@ -351,14 +560,19 @@ hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, 
     return hipGetLastError();
 }
 
-hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, uint32_t* keys, uint32_t* vals,
-                             uint32_t* keys_alt, int32_t* order, int32_t* hist, int32_t* partials, hipStream_t s) {
-    if (n_tiles_total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(tile_order_keys_kernel, dim3(blocks_for(n_tiles_total)), dim3(kBlock), 0, s, ranges,
-                       n_tiles_total, keys, vals);
-    // one 5-bit pass: the result lands in the alternate buffers (keys_alt, order)
-    return launch_radix_sort(keys, vals, keys_alt, reinterpret_cast<uint32_t*>(order), n_tiles_total, 5, hist,
-                             partials, s);
+int32_t tile_order_chunks(int32_t n_tiles_total) {
+    return n_tiles_total > 0 ? (n_tiles_total + kOrderChunk - 1) / kOrderChunk : 0;
+}
+
+size_t tile_order_hist_ints(int32_t n_tiles_total) { return (size_t)kOrderBuckets * tile_order_chunks(n_tiles_total); }
+
+hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, int32_t* hist, int32_t* order,
+                             hipStream_t s) {
+    const int32_t nc = tile_order_chunks(n_tiles_total);
+    if (nc == 0) return hipSuccess;
+    hipLaunchKernelGGL(order_hist_kernel, dim3(nc), dim3(kBlock), 0, s, ranges, n_tiles_total, nc, hist);
+    hipLaunchKernelGGL(order_scatter_kernel, dim3(nc), dim3(kBlock), 0, s, ranges, n_tiles_total, nc, hist, order);
+    return hipGetLastError();
 }
 
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s) {

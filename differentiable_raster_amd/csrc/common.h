@@ -104,6 +104,8 @@ hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
 
 // Exclusive scan of `rows` independent int32 rows of length n (row r at in + r*n):
 // out[r][i] = sum_{k<i} in[r][k]; totals[r] = sum of row r (totals may be null).
+// In-place exclusive scan of n int32 values by one workgroup (n up to a few hundred thousand).
+hipError_t launch_scan_small(int32_t* a, int32_t n, hipStream_t s);
 hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, int32_t n, int32_t rows,
                             int32_t* partials, hipStream_t s);
 size_t scan_partials_bytes(int32_t n, int32_t rows);
@@ -129,16 +131,18 @@ hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count
                              int32_t capacity, BinReadback* out, hipStream_t s);
 hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int32_t V, int32_t capacity,
                              int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, hipStream_t s);
-hipError_t launch_gather_ntiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity, int32_t total,
-                                int32_t* out, hipStream_t s);
-hipError_t launch_emit(const uint32_t* packed, const int32_t* offsets, const ushort4* rect, int32_t capacity,
-                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, uint32_t* tile_keys,
-                       int32_t* vals, hipStream_t s);
+// Instances of the depth-sorted slots: chunk_offsets holds emit_chunks(total) ints of workspace.
+int32_t emit_chunks(int32_t total);
+hipError_t launch_emit(const uint32_t* packed, const int32_t* n_tiles, const ushort4* rect, int32_t capacity,
+                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets,
+                       uint32_t* tile_keys, int32_t* vals, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
 hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s);
-// Heavy-first permutation of the tiles (stable radix pass on a 5-bit length bucket).
-hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, uint32_t* keys, uint32_t* vals,
-                             uint32_t* keys_alt, int32_t* order, int32_t* hist, int32_t* partials, hipStream_t s);
+// Heavy-first permutation of the tiles (stable counting sort on a 5-bit length bucket); hist
+// holds tile_order_hist_ints(n_tiles_total) ints of workspace.
+size_t tile_order_hist_ints(int32_t n_tiles_total);
+hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, int32_t* hist, int32_t* order,
+                             hipStream_t s);
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s);
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
                              int32_t capacity, int32_t tiles_per_view, int32_t n_tiles_total, int32_t K,

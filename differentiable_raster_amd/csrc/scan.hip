@@ -101,4 +101,10 @@ hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, in
     return hipGetLastError();
 }
 
+hipError_t launch_scan_small(int32_t* a, int32_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(kBlock), 0, s, a, n, nullptr);
+    return hipGetLastError();
+}
+
 }  // namespace gsmi

@@ -1,6 +1,7 @@
 // Stable LSD radix sort of (uint32 key, uint32 value) pairs, up to 9 bits per pass.
 //
-// Per pass, over tiles of 4096 elements (each of the four wavefronts owns 1024 consecutive ones):
+// Per pass, over tiles of 3072 elements (each of the four wavefronts owns 768 consecutive ones; a
+// tile's 36.5 KB of LDS lets four workgroups share a CU):
 //   upsweep   - each block histograms the digit of its tile in LDS and writes the counts
 //               digit-major, hist[d * nblocks + b];
 //   row scan  - one block per digit scans that digit's row over the blocks (the digit's first
@@ -19,7 +20,7 @@ namespace gsmi {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kItems = 16;
+constexpr int kItems = 12;
 constexpr int kChunk = kBlock * kItems;
 constexpr int kWaveChunk = kWave * kItems;  // elements owned by one wavefront
 constexpr int kMaxBits = 9;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
     for (int k = 0; k < kPer; k++)
         for (int q = 0; q < kWaves; q++) s_whist[q][k * kBlock + threadIdx.x] = 0;
     __syncthreads();
-    // rank within the wavefront's 1024 elements: rounds of 64 in input order
+    // rank within the wavefront's elements: rounds of 64 in input order
     const int64_t wbase = (int64_t)tile * kChunk + w * kWaveChunk;
     const unsigned long long lt = (1ull << lane) - 1ull;
     int* whist = s_whist[w];
