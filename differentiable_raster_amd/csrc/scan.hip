@@ -84,6 +84,33 @@ __global__ __launch_bounds__(kBlock) void scan_apply_kernel(const int32_t* in, i
     }
 }
 
+// One workgroup scans a[0, n) in place (exclusive): each thread takes kSmallItems consecutive
+// values per step, so up to kBlock * kSmallItems values take one step and two barriers.
+constexpr int kSmallItems = 16;
+
+__global__ __launch_bounds__(kBlock) void scan_small_kernel(int32_t* a, int32_t n) {
+    __shared__ int s_wave[kBlock / kWave];
+    int carry = 0;
+    for (int32_t b0 = 0; b0 < n; b0 += kBlock * kSmallItems) {
+        const int32_t first = b0 + threadIdx.x * kSmallItems;
+        int v[kSmallItems];
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kSmallItems; k++) {
+            v[k] = first + k < n ? a[first + k] : 0;
+            sum += v[k];
+        }
+        int tot;
+        int run = carry + block_exclusive_scan(sum, s_wave, &tot);
+#pragma unroll
+        for (int k = 0; k < kSmallItems; k++) {
+            if (first + k < n) a[first + k] = run;
+            run += v[k];
+        }
+        carry += tot;
+    }
+}
+
 }  // namespace
 
 static int32_t scan_blocks(int32_t n) { return (n + kChunk - 1) / kChunk; }
@@ -103,7 +130,7 @@ hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, in
 
 hipError_t launch_scan_small(int32_t* a, int32_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(kBlock), 0, s, a, n, nullptr);
+    hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(kBlock), 0, s, a, n);
     return hipGetLastError();
 }
 
