@@ -243,6 +243,44 @@ size_t gs_project_workspace_size(int32_t n, int32_t V) {
     return project_ws_bytes(n, V);
 }
 
+// Pinned host copy of the count summary and the event gs_project records after copying it.
+// `filled`: the buffer holds the counts of the last gs_project that named it, for V views and
+// this capacity (set when the copy is enqueued; the event says when it has landed).
+struct gs_readback {
+    gsmi::CountSummary* host = nullptr;
+    hipEvent_t done = nullptr;
+    bool filled = false;
+    int32_t V = 0, capacity = 0;
+};
+
+gs_status gs_readback_create(gs_readback** out) {
+    g_last_error.clear();
+    if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "out is null");
+    *out = nullptr;
+    gs_readback* r = new gs_readback();
+    void* h = nullptr;
+    if (hipHostMalloc(&h, sizeof(gsmi::CountSummary), hipHostMallocDefault) != hipSuccess) {
+        delete r;
+        return fail(GS_ERR_HIP, "hipHostMalloc of the count buffer failed");
+    }
+    r->host = static_cast<gsmi::CountSummary*>(h);
+    if (hipEventCreateWithFlags(&r->done, hipEventDisableTiming) != hipSuccess) {
+        (void)hipHostFree(h);
+        delete r;
+        return fail(GS_ERR_HIP, "hipEventCreateWithFlags failed");
+    }
+    *out = r;
+    return GS_OK;
+}
+
+void gs_readback_destroy(gs_readback* r) {
+    if (!r) return;
+    if (r->filled) (void)hipEventSynchronize(r->done);
+    (void)hipEventDestroy(r->done);
+    (void)hipHostFree(r->host);
+    delete r;
+}
+
 gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
                      gs_projected* out, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
@@ -291,7 +329,24 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     a.block_offsets = c.take<int32_t>((size_t)nb * 2 * V);
     a.row_totals = c.take<int32_t>((size_t)2 * V);
     a.scan_partials = c.take<int32_t>(scan_partials_bytes(nb, 2 * V) / sizeof(int32_t));
-    return hip_check(launch_project(a, static_cast<hipStream_t>(stream)), "gs_project launch");
+    gs_readback* rb = out->readback;
+    a.block_depth = rb ? c.take<uint2>((size_t)nb) : nullptr;
+    a.summary = rb ? c.take<CountSummary>(1) : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rb) rb->filled = false;
+    gs_status st2 = hip_check(launch_project_count(a, s), "gs_project launch");
+    if (st2 != GS_OK) return st2;
+    if (rb) {
+        // the counts are final here: copy them out while the writing pass runs
+        if ((st2 = hip_check(hipMemcpyAsync(rb->host, a.summary, sizeof(CountSummary), hipMemcpyDeviceToHost, s),
+                             "count copy")) != GS_OK)
+            return st2;
+        if ((st2 = hip_check(hipEventRecord(rb->done, s), "count event")) != GS_OK) return st2;
+        rb->filled = true;
+        rb->V = V;
+        rb->capacity = out->capacity;
+    }
+    return hip_check(launch_project_write(a, s), "gs_project launch");
 }
 
 gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
@@ -378,14 +433,27 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
     // the one read-back: visible and instance counts of every view and the visible depth range
     BinWs w = carve_bin(ws, proj->capacity, V, tiles_total, bins->capacity, &need);
     BinReadback rb;
-    if ((st = hip_check(launch_bin_counts(proj->vis_count, proj->inst_count, V, proj->depth, proj->capacity,
-                                          w.readback, s),
-                        "count launch")) != GS_OK)
-        return st;
-    if ((st = hip_check(hipMemcpyAsync(&rb, w.readback, offsetof(BinReadback, partial), hipMemcpyDeviceToHost, s),
-                        "count read")) != GS_OK)
-        return st;
-    if ((st = hip_check(hipStreamSynchronize(s), "count read sync")) != GS_OK) return st;
+    gs_readback* early = proj->readback;
+    if (early && early->filled && early->V == V && early->capacity == proj->capacity) {
+        // copied by gs_project before its writing pass: wait for that copy only
+        if ((st = hip_check(hipEventSynchronize(early->done), "count copy wait")) != GS_OK) return st;
+        for (int v = 0; v < V; v++) {
+            rb.vis[v] = early->host->vis[v];
+            rb.inst[v] = early->host->inst[v];
+        }
+        rb.bits[0] = early->host->bits[0];
+        rb.bits[1] = early->host->bits[1];
+    } else {
+        if ((st = hip_check(launch_bin_counts(proj->vis_count, proj->inst_count, V, proj->depth, proj->capacity,
+                                              w.readback, s),
+                            "count launch")) != GS_OK)
+            return st;
+        if ((st = hip_check(hipMemcpyAsync(&rb, w.readback, offsetof(BinReadback, partial), hipMemcpyDeviceToHost,
+                                           s),
+                            "count read")) != GS_OK)
+            return st;
+        if ((st = hip_check(hipStreamSynchronize(s), "count read sync")) != GS_OK) return st;
+    }
     const int32_t* vis = rb.vis;
     const int64_t* inst = rb.inst;
     std::memset(info, 0, sizeof(*info));

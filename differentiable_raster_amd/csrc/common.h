@@ -60,6 +60,15 @@ __device__ __forceinline__ float one_minus_alpha(float o, float G, float v, floa
 // ---------------------------------------------------------------------------------------
 // Launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------------------
+// The counts the binning sizes its launches from, in the order they are copied to the host:
+// instances and visible slots per view, and the smallest float32 bit pattern of the visible
+// depths of all views with the complement of the largest.
+struct CountSummary {
+    int64_t inst[GS_MAX_VIEWS];
+    int32_t vis[GS_MAX_VIEWS];
+    uint32_t bits[2];
+};
+
 struct ProjectArgs {
     int32_t n, V, capacity;
     const float *means, *log_scales, *quats, *logits, *sh;
@@ -81,8 +90,15 @@ struct ProjectArgs {
     int32_t* block_offsets;  // [2V][nb]: exclusive scans of the rows of block_counts
     int32_t* row_totals;     // [2V]: visible slots per view, then instances per view
     int32_t* scan_partials;  // scan workspace
+    uint2* block_depth;      // [nb] (smallest, complement of largest) visible depth bits per block;
+                             // NULL: not computed
+    CountSummary* summary;   // device copy of the counts (written when block_depth is set)
 };
-hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
+// The counting pass, the block scans and (with block_depth) the count summary: afterwards
+// vis/inst counts are final and the summary may be copied out while the writing pass runs.
+hipError_t launch_project_count(const ProjectArgs& a, hipStream_t s);
+// The writing pass (records of the visible slots).
+hipError_t launch_project_write(const ProjectArgs& a, hipStream_t s);
 size_t project_ws_bytes(int32_t n, int32_t V);
 
 // Backward of the projection: per-slot 2D gradients of V views -> per-Gaussian parameter

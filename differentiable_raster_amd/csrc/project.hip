@@ -154,6 +154,9 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
         if (g.ok) bounded = sh_bounded<3 * (NY + 1)>(a, i);
     }
     const int nb = gridDim.x;
+    // visible depth range of this thread over all views, as float32 bit patterns (depths are
+    // above znear > 0, so the patterns order like the values)
+    uint32_t dlo = 0xFFFFFFFFu, dhi = 0u;
     for (int v = 0; v < a.V; v++) {
         Rec r;
         r.ntiles = 0;
@@ -161,6 +164,10 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
         bool vis = (i < a.n) && project_geom(a, g, a.cams.c[v], r, dir);
         // some coefficient is huge or not finite: the colour itself decides
         if (vis && !bounded) vis = colour_finite<DEG>(a, i, dir);
+        if (vis) {
+            dlo = min(dlo, __float_as_uint(r.depth));
+            dhi = max(dhi, __float_as_uint(r.depth));
+        }
         const unsigned long long m = __ballot(vis);
         int nt = vis ? r.ntiles : 0;
         for (int o = kWave / 2; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
@@ -179,6 +186,26 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
             a.block_counts[(a.V + v) * nb + blockIdx.x] = t;
         }
         __syncthreads();
+    }
+    if (a.block_depth) {
+        uint32_t nhi = ~dhi;
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            dlo = min(dlo, (uint32_t)__shfl_xor((int)dlo, o));
+            nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o));
+        }
+        // the count buffers of the view loop are free again after its last barrier
+        if (lane == 0) {
+            s_cnt[w] = (int)dlo;
+            s_inst[w] = (int)nhi;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int k = 1; k < kBlock / kWave; k++) {
+                dlo = min(dlo, (uint32_t)s_cnt[k]);
+                nhi = min(nhi, (uint32_t)s_inst[k]);
+            }
+            a.block_depth[blockIdx.x] = make_uint2(dlo, nhi);
+        }
     }
 }
 
@@ -287,6 +314,40 @@ __global__ __launch_bounds__(kBlock) void inst_total_kernel(const int32_t* block
     }
 }
 
+// The count summary (one block): visible slots per view from the block scans, instances per
+// view from inst_total_kernel, and the visible depth range from the per-block ranges.
+__global__ __launch_bounds__(kBlock) void count_summary_kernel(const int32_t* row_totals, const int64_t* inst_count,
+                                                               int32_t V, const uint2* block_depth, int32_t nb,
+                                                               CountSummary* out) {
+    __shared__ uint32_t s_lo[kBlock / kWave], s_nhi[kBlock / kWave];
+    if ((int)threadIdx.x < V) {
+        out->vis[threadIdx.x] = row_totals[threadIdx.x];
+        out->inst[threadIdx.x] = inst_count[threadIdx.x];
+    }
+    uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;
+    for (int32_t k = threadIdx.x; k < nb; k += kBlock) {
+        lo = min(lo, block_depth[k].x);
+        nhi = min(nhi, block_depth[k].y);
+    }
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+        nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o));
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        s_lo[threadIdx.x / kWave] = lo;
+        s_nhi[threadIdx.x / kWave] = nhi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < kBlock / kWave; k++) {
+            lo = min(lo, s_lo[k]);
+            nhi = min(nhi, s_nhi[k]);
+        }
+        out->bits[0] = lo;
+        out->bits[1] = nhi;
+    }
+}
+
 }  // namespace
 
 static int32_t project_blocks(int32_t n) { return (n + kBlock - 1) / kBlock; }
@@ -296,10 +357,11 @@ static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 size_t project_ws_bytes(int32_t n, int32_t V) {
     const int32_t nb = project_blocks(n > 0 ? n : 1);
     return 2 * align256(sizeof(int32_t) * (size_t)nb * 2 * V) + align256(sizeof(int32_t) * 2 * V) +
-           align256(scan_partials_bytes(nb, 2 * V));
+           align256(scan_partials_bytes(nb, 2 * V)) + align256(sizeof(uint2) * (size_t)nb) +
+           align256(sizeof(CountSummary));
 }
 
-hipError_t launch_project(const ProjectArgs& a0, hipStream_t s) {
+hipError_t launch_project_count(const ProjectArgs& a0, hipStream_t s) {
     ProjectArgs a = a0;
     const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
     switch (a.p.sh_degree) {
@@ -311,6 +373,15 @@ hipError_t launch_project(const ProjectArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(inst_total_kernel, dim3(a.V), dim3(kBlock), 0, s, a.block_counts, a.V, nb, a.inst_count);
     hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nb, 2 * a.V, a.scan_partials, s);
     if (e != hipSuccess) return e;
+    if (a.block_depth)
+        hipLaunchKernelGGL(count_summary_kernel, dim3(1), dim3(kBlock), 0, s, a.row_totals, a.inst_count, a.V,
+                           a.block_depth, nb, a.summary);
+    return hipGetLastError();
+}
+
+hipError_t launch_project_write(const ProjectArgs& a0, hipStream_t s) {
+    ProjectArgs a = a0;
+    const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
     switch (a.p.sh_degree) {
         case 0: hipLaunchKernelGGL(project_write_kernel<0>, dim3(nb), dim3(kBlock), 0, s, a); break;
         case 1: hipLaunchKernelGGL(project_write_kernel<1>, dim3(nb), dim3(kBlock), 0, s, a); break;

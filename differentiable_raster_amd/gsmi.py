@@ -50,7 +50,8 @@ class gs_projected(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int32), ("vis_count", ctypes.c_void_p), ("inst_count", ctypes.c_void_p),
                 ("vis_ids", ctypes.c_void_p), ("mean2d", ctypes.c_void_p), ("conic_opacity", ctypes.c_void_p),
                 ("color", ctypes.c_void_p), ("depth", ctypes.c_void_p), ("tile_rect", ctypes.c_void_p),
-                ("n_tiles", ctypes.c_void_p), ("inst_base", ctypes.c_void_p), ("raster_rec", ctypes.c_void_p)]
+                ("n_tiles", ctypes.c_void_p), ("inst_base", ctypes.c_void_p), ("raster_rec", ctypes.c_void_p),
+                ("readback", ctypes.c_void_p)]
 
 
 class gs_bins(ctypes.Structure):
@@ -88,6 +89,8 @@ _SIGS = {
     "gs_version": (ctypes.c_char_p, []),
     "gs_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gs_last_error": (ctypes.c_char_p, []),
+    "gs_readback_create": (ctypes.c_int, [_P(ctypes.c_void_p)]),
+    "gs_readback_destroy": (None, [ctypes.c_void_p]),
     "gs_project_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "gs_project": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
                                   _P(gs_projected), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -205,6 +208,17 @@ def make_params(s) -> gs_render_params:
 # ---------------------------------------------------------------------------------------
 def gs_version() -> str:
     return load().gs_version().decode()
+
+
+def gs_readback_create() -> int:
+    """A pinned host count buffer for gs_projected.readback (an opaque handle)."""
+    h = ctypes.c_void_p()
+    _check(load().gs_readback_create(ctypes.byref(h)), "gs_readback_create")
+    return int(h.value)
+
+
+def gs_readback_destroy(handle) -> None:
+    load().gs_readback_destroy(handle)
 
 
 def gs_project_workspace_size(n: int, V: int) -> int:

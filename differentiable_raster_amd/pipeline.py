@@ -17,7 +17,7 @@ from . import gsmi
 
 class Renderer:
     def __init__(self, scene, settings, device: str = "cuda", instance_capacity: int | None = None,
-                 headroom: float = 1.25):
+                 headroom: float = 1.25, early_counts: bool = True):
         self.scene = scene
         self.settings = settings
         self.device = torch.device(device)
@@ -56,7 +56,11 @@ class Renderer:
         self.proj = gsmi.gs_projected(cap, self.vis_count.data_ptr(), self.inst_count.data_ptr(),
                                       self.vis_ids.data_ptr(), self.mean2d.data_ptr(), self.conic_opacity.data_ptr(),
                                       self.color.data_ptr(), self.depth.data_ptr(), self.tile_rect.data_ptr(),
-                                      self.n_tiles.data_ptr(), self.inst_base.data_ptr(), self.raster_rec.data_ptr())
+                                      self.n_tiles.data_ptr(), self.inst_base.data_ptr(), self.raster_rec.data_ptr(),
+                                      None)
+        # pinned count buffer: the projection copies the counts out before its writing pass
+        self.readback = gsmi.gs_readback_create() if early_counts else None
+        self.proj.readback = self.readback
         self.ws_proj = torch.empty(gsmi.gs_project_workspace_size(self.n, V), dtype=torch.uint8, device=dev)
         self.ranges = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
         self.ranges_capped = torch.zeros(V * self.tpv * 2, dtype=i32, device=dev)
@@ -80,6 +84,15 @@ class Renderer:
         self.target = up(scene.target.reshape(-1)) if scene.target is not None else None
         self.dldc_in = up(scene.dldc.reshape(-1)) if scene.dldc is not None else None
         self.info = None
+
+    def __del__(self):
+        rb = getattr(self, "readback", None)
+        if rb:
+            self.readback = None
+            try:
+                gsmi.gs_readback_destroy(rb)
+            except Exception:  # interpreter shutdown: the library may be gone already
+                pass
 
     def _alloc_bins(self, capacity: int):
         if capacity <= self.inst_capacity:

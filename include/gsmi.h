@@ -84,6 +84,10 @@ typedef struct {
     const float* sh;             /* [3*(d+1)^2][n], row k*3 + channel; row 0..2 = DC = base colour */
 } gs_gaussians;
 
+/* Opaque host-side buffer for the per-view counts: pinned host memory and an event (see
+ * gs_readback_create).  Owned by the caller through create/destroy. */
+typedef struct gs_readback gs_readback;
+
 /* Per-view projected records, indexed by visible slot.  All arrays are [V][capacity][...]
  * with capacity >= n; slot s of view v lives at index v*capacity + s.  Visible Gaussians of
  * a view take slots 0..vis_count[v]-1 in ascending Gaussian index. */
@@ -106,6 +110,11 @@ typedef struct {
                                  64-byte line per slot (256-byte aligned array): x, y, A, B, C, o,
                                  r, g, b, then as 32-bit patterns tx0 | ty0 << 16, tx1 | ty1 << 16,
                                  inst_base, then depth, n_tiles (32-bit pattern), 0, 0 */
+    gs_readback* readback;    /* optional (may be NULL): when set, gs_project copies the per-view
+                                 visible and instance counts and the visible depth range into it
+                                 as soon as they are known (before the records are written), and
+                                 gs_bin_tiles takes them from there instead of reading the device;
+                                 it holds the counts of the last gs_project call that named it */
 } gs_projected;
 
 /* Tile bins of all views of one call.  Global tile id = v * tiles_per_view + ty * tiles_x + tx.
@@ -167,6 +176,19 @@ const char* gs_version(void);
 const char* gs_status_string(gs_status s);
 const char* gs_last_error(void);
 
+/*
+ * Host-side count buffer for gs_projected.readback: page-locked host memory for the counts of
+ * up to GS_MAX_VIEWS views and an event that gs_project records after its copy.  With it, the
+ * one device-to-host read of an iteration overlaps the projection's record-writing pass, and
+ * gs_bin_tiles waits for that copy only, not for the stream; the GPU keeps working while the
+ * host sizes the binning launches.  *out is set on success.  A buffer serves one projection at
+ * a time: calls that name the same buffer must not overlap.  Errors: GS_ERR_INVALID_ARGUMENT
+ * for out == NULL; GS_ERR_HIP if the pinned allocation or the event cannot be created.
+ */
+gs_status gs_readback_create(gs_readback** out);
+/* Releases a buffer from gs_readback_create (NULL is ignored).  Waits for a pending copy. */
+void gs_readback_destroy(gs_readback* r);
+
 /* Workspace bytes of gs_project for n Gaussians and V views. */
 size_t gs_project_workspace_size(int32_t n, int32_t V);
 
@@ -207,7 +229,9 @@ size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height
  * score = o / sqrt(A C - B^2) (opacity times the square root of the dilated covariance's
  * determinant, evaluated in float32 with one rounding per operation), ties broken by
  * depth then slot, kept in depth order (ByteSplat's pruning under per-tile on-chip limits).
- * Reads the per-view counts back to the host once (info, host), then sizes its launches.
+ * Reads the per-view counts back to the host once (info, host), then sizes its launches: from
+ * proj->readback when the last gs_project filled it (waiting on that copy's event only), else
+ * by its own copy from the device (synchronizing the stream).
  * Errors: GS_ERR_INVALID_ARGUMENT as for gs_project; GS_ERR_CAPACITY (with *required, host,
  * set to the instances needed) when bins->capacity is too small, in which case the bins are
  * left undefined; GS_ERR_CAPACITY if the workspace is too small.

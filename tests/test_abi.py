@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
                  "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
                  "gs_project_bwd", "gs_raster_workspace_size", "gs_grad_encode", "gs_grad_decode",
                  "gs_grad_encode_workspace_size", "gs_compose", "gs_adam_step", "gs_adam_flush",
-                 "gs_version", "gs_status_string", "gs_last_error"]:
+                 "gs_version", "gs_status_string", "gs_last_error", "gs_readback_create", "gs_readback_destroy"]:
         assert must in names, must
 
 
@@ -79,6 +79,7 @@ def params(gs, **kw):
 
 def projected(gs, capacity=100, null=()):
     fields = {f: FAKE for f, _ in gs.gs_projected._fields_ if f != "capacity"}
+    fields["readback"] = None  # a host object: a fake address would be dereferenced
     for f in null:
         fields[f] = None
     return gs.gs_projected(capacity, *[fields[f] for f, _ in gs.gs_projected._fields_ if f != "capacity"])
@@ -274,3 +275,8 @@ def test_product_path_imports_no_oracle():
     for f in os.listdir(os.path.join(ROOT, "differentiable_raster_amd", "csrc")):
         src = open(os.path.join(ROOT, "differentiable_raster_amd", "csrc", f)).read()
         assert "oracle" not in src.lower(), f
+
+
+def test_readback_create_rejects_null(gs):
+    assert gs.load().gs_readback_create(None) == 1
+    gs.load().gs_readback_destroy(None)  # ignored
