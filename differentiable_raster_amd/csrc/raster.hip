@@ -295,7 +295,10 @@ struct Bwd {
     float T, Tfin;
     float g0, g1, g2;
     float gbg;  // sum over channels of dL/dC * background
-    float B0, B1, B2;
+    // sum over channels of dL/dC times the colour behind the current entry: the backward needs
+    // the colour behind only in that combination, and it obeys the same update
+    // (B <- B + alpha (c - B) per channel gives GB <- GB + alpha (sum_ch g_ch c_ch - GB))
+    float GB;
     int32_t nc;
 };
 
@@ -410,8 +413,8 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float inv = __builtin_amdgcn_rcpf(oma);  // 1 - alpha >= 1 - alpha_max > 0 where it counts
         const float Tj = s.T * inv;
         // dL/dalpha = T_j sum_ch g_ch (c_ch - B_ch) - T_final / (1 - alpha) sum_ch g_ch bg_ch
-        const float e0 = oc.y - s.B0, e1 = oc.z - s.B1, e2 = oc.w - s.B2;
-        float dLda = Tj * fmaf(s.g0, e0, fmaf(s.g1, e1, s.g2 * e2));
+        const float ge = fmaf(s.g0, oc.y, fmaf(s.g1, oc.z, s.g2 * oc.w)) - s.GB;
+        float dLda = Tj * ge;
         if (BG) dLda = fmaf(-s.Tfin * inv, s.gbg, dLda);
         // zero where the pair does not contribute (selects, so no garbage of other lanes leaks)
         const float wgt = contrib ? alpha * Tj : 0.0f;
@@ -432,9 +435,7 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         d[8] = wgt * s.g2;
         if (contrib) {
             // colour behind the next entry: alpha c + (1 - alpha) B = B + alpha (c - B)
-            s.B0 = fmaf(alpha, e0, s.B0);
-            s.B1 = fmaf(alpha, e1, s.B1);
-            s.B2 = fmaf(alpha, e2, s.B2);
+            s.GB = fmaf(alpha, ge, s.GB);
             s.T = Tj;
         }
         if (cm != 0ull) {
@@ -448,7 +449,8 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
                 log_w0[slot] = w0;
                 log_w0[slot + 2 * (kSlots + 1)] = w1;
             }
-            if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x0001000100010001ull)) log.v[4][slot] = w2;
+            // the first lane of a row is in quad 0, whose log_w0 is row 0: row 4 is 4 rows further
+            if (__builtin_amdgcn_inverse_ballot_w64(rm & 0x0001000100010001ull)) log_w0[slot + 4 * (kSlots + 1)] = w2;
         }
     }
 }
@@ -798,7 +800,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     }
     s.Tfin = s.T;
     s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
-    s.B0 = s.B1 = s.B2 = 0.0f;
+    s.GB = 0.0f;
     zero_log(log);
     zero_lists(b);
     const int maxnc = block_max(s.nc, s_red);
@@ -827,7 +829,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     s.T = f.T;
     s.Tfin = f.T;
     s.nc = c.inside ? f.last : 0;
-    s.B0 = s.B1 = s.B2 = 0.0f;
+    s.GB = 0.0f;
     s.g0 = s.g1 = s.g2 = 0.0f;
     float lsum = 0.0f;
     if (c.inside) {
