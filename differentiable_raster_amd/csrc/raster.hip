@@ -374,7 +374,7 @@ __device__ __forceinline__ unsigned long long rows_with(unsigned long long m) {
 // BG: the background is not black (its term in dL/dalpha is needed).
 template <bool BG>
 __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Log& log, Lists l,
-                                         int32_t jbase, int row_nc, Bwd& s) {
+                                         int32_t jbase, Bwd& s) {
     const float amax = a.p.alpha_max;
     const uint16_t* lst = b.list16[c.list_id];
     const int quad = (c.lane >> 2) & 3;
@@ -387,9 +387,10 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const int k = e_next & 0xFFu, slot = e_next >> 8;
         e_next = lst[max(i - 1, 0)];
         const int jk = jbase + k;
-        const bool active = (i < l.len) & (jk < row_nc);  // uniform over the row
+        // uniform over the row (the lists hold no entry past the row's largest n_contrib)
+        const bool active = i < l.len;
         // ballots of single compares cost no vector instruction
-        const unsigned long long am = __builtin_amdgcn_ballot_w64(i < l.len) & __builtin_amdgcn_ballot_w64(jk < row_nc);
+        const unsigned long long am = __builtin_amdgcn_ballot_w64(active);
         if (am == 0ull) continue;
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
@@ -492,8 +493,13 @@ __device__ __forceinline__ int sub_batch(const TileCtx& c, const Batch& b, int h
 // pair's log slot: the pairs of the sub-batch's entries before it (`first` is the pair position
 // of entry lo) plus the block's rank among the entry's blocks.  Ends with a workgroup barrier:
 // the previous sub-batch's gather must be done before the walk stores into the log again.
-__device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int lo, int hi, int first) {
+// Entries at batch index >= row_lim (this lane's row: the row's largest n_contrib minus the
+// batch start) lie past every pixel of the row and stay out of its list.
+__device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int lo, int hi, int first, int row_lim) {
     int len[kRowsPerWave] = {0, 0, 0, 0};
+    int lim[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; r++) lim[r] = __builtin_amdgcn_readlane(row_lim, 16 * r);
     const unsigned long long lt = (1ull << c.lane) - 1ull;
 #pragma unroll
     for (int half = 0; half < kSub / kWave; half++) {
@@ -503,7 +509,7 @@ __device__ __forceinline__ Lists build_sub_lists(const TileCtx& c, Batch& b, int
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; r++) {
             const int bit = block_bit(c.w, r);
-            const bool hit = (meta >> bit) & 1u;
+            const bool hit = ((meta >> bit) & 1u) && k < lim[r];
             const unsigned long long bal = __builtin_amdgcn_ballot_w64(hit);
             const int slot = pos + __builtin_popcount(meta & ((1u << bit) - 1u));
             if (hit) b.list16[c.w * kRowsPerWave + r][len[r] + __popcll(bal & lt)] = (uint16_t)(k | (slot << 8));
@@ -654,8 +660,8 @@ __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx
         for (int hi = cnt_b; hi > 0;) {
             const int lo = sub_batch(c, b, hi);
             const int first = __builtin_amdgcn_readfirstlane((int)b.meta[lo][1]);
-            const Lists l = build_sub_lists(c, b, lo, hi, first);
-            bwd_walk<BG>(a, c, b, log, l, b0, row_nc, s);
+            const Lists l = build_sub_lists(c, b, lo, hi, first, row_nc - b0);
+            bwd_walk<BG>(a, c, b, log, l, b0, s);
             __syncthreads();
             gather_sub_batch(a, b, log, lo, hi, first);
             hi = lo;
