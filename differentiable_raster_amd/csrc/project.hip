@@ -140,7 +140,8 @@ __device__ __noinline__ bool colour_finite(const ProjectArgs& a, int i, float3 d
 }
 
 template <int DEG>
-__global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
+// at most 80 registers: 6 waves per SIMD to hide the latency of the coefficient reads (95 otherwise)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void project_count_kernel(ProjectArgs a) {
     constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
     __shared__ int s_cnt[kBlock / kWave];
     __shared__ int s_inst[kBlock / kWave];

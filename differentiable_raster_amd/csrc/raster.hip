@@ -14,9 +14,10 @@
 // pairs are pairs with alpha < alpha_min, and forward and backward cull the same pairs (they run
 // this same code on the same records).
 //
-// Pair evaluation works in base-2 logarithm units: the staged conic is pre-scaled so that the
-// exponent p2 = -q/2 * log2(e) comes out of two FMAs, and the alpha_min test is p2 >= log2(
-// alpha_min / o), taken before the exponential, so skipped pairs never pay for exp2.
+// Pair evaluation works in base-2 logarithm units: the staged conic is pre-scaled and the
+// entry's log2(o) staged beside it, so that p2 = log2(o) - q/2 * log2(e) comes out of three FMAs
+// and exp2(p2) is o * exp(-q/2) itself.  The alpha_min test is p2 >= log2(alpha_min), one
+// compare with a constant, and 1 - alpha is one subtraction after the clamp.
 //
 // The forward walks each block's list front to back; a workgroup stops staging once every pixel
 // has stopped.  The backward walks it back to front from n_contrib, recovering T by division by
@@ -93,8 +94,8 @@ __device__ __forceinline__ TileCtx tile_ctx(const RasterArgs& a) {
 // per-entry gradient accumulators of the backward.
 struct Batch {
     float2 xy[kBatch];      // projected centre
-    float4 q[kBatch];       // (a, b, c, thr): p2 = a dx^2 + b dx dy + c dy^2, blend iff p2 >= thr
-    float4 oc[kBatch];      // (o, r, g, b)
+    float4 q[kBatch];       // (a, b, c, l): p2 = a dx^2 + b dx dy + c dy^2 + l = log2(o exp(-q/2))
+    float4 oc[kBatch];      // (r, g, b, o): the walks read the colour as the first 12 bytes
     int32_t inst[kBatch];   // index of the (slot, tile) instance (backward only)
     // [0]: the 4x4 blocks the entry's alpha_min ellipse reaches; [1] (backward): the number of
     // (entry, block) pairs of the batch's earlier entries, its slot position in the log
@@ -126,8 +127,8 @@ __device__ __forceinline__ void stage(const RasterArgs& a, const TileCtx& c, Bat
     const float4 co = make_float4(r0.z, r0.w, r1.x, r1.y);
     const float amin = a.p.alpha_min;
     b.xy[k] = xy;
-    b.q[k] = make_float4(-0.5f * kLog2e * co.x, -kLog2e * co.y, -0.5f * kLog2e * co.z, __log2f(amin / co.w));
-    b.oc[k] = make_float4(co.w, r1.z, r1.w, r2.x);
+    b.q[k] = make_float4(-0.5f * kLog2e * co.x, -kLog2e * co.y, -0.5f * kLog2e * co.z, __log2f(co.w));
+    b.oc[k] = make_float4(r1.z, r1.w, r2.x, co.w);
     if (INST) {
         const int lo = __float_as_int(r2.y), hi = __float_as_int(r2.z);
         const int tx0 = lo & 0xFFFF, ty0 = lo >> 16, tx1 = hi & 0xFFFF;
@@ -208,28 +209,6 @@ __device__ __forceinline__ Lists build_lists(const TileCtx& c, Batch& b, int cnt
     return l;
 }
 
-struct Pair {
-    float dx, dy, p2, G, v, alpha, oma;
-};
-
-// The shared pair evaluation.  Returns false when alpha < alpha_min (exp2 not evaluated).
-__device__ __forceinline__ bool eval_pair(const TileCtx& c, const Batch& b, int k, float amax, Pair& e) {
-    const float2 xy = b.xy[k];
-    const float4 q = b.q[k];
-    e.dx = c.fpx - xy.x;
-    e.dy = c.fpy - xy.y;
-    const float bdx = q.y * e.dx;
-    const float cdy = q.z * e.dy;
-    e.p2 = fmaf(q.x * e.dx, e.dx, fmaf(bdx, e.dy, cdy * e.dy));
-    if (!(e.p2 >= q.w)) return false;
-    const float o = b.oc[k].x;
-    e.G = __builtin_amdgcn_exp2f(e.p2);  // p2 >= log2(alpha_min) > -126: no denormal range
-    e.v = o * e.G;
-    e.alpha = fminf(amax, e.v);
-    e.oma = e.v <= amax ? fmaf(-o, e.G, 1.0f) : 1.0f - amax;
-    return true;
-}
-
 struct Fwd {
     float T, C0, C1, C2;
     int32_t last;
@@ -241,12 +220,12 @@ struct Counts {
 };
 
 // Front-to-back over this block's list of the staged batch (positions j = jbase + k).  Every
-// lane evaluates the step without branches (the pair evaluation of eval_pair, written out) and
-// keeps the result where it blends.
+// lane evaluates the step without branches and keeps the result where it blends.
 template <bool COUNT>
 __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Lists l, int32_t jbase,
                                          Fwd& f, Counts& cnt) {
     const float amax = a.p.alpha_max, tmin = a.p.t_min;
+    const float l2amin = __log2f(a.p.alpha_min);
     const uint8_t* lst = b.list[c.list_id];
     int k_next = lst[0];  // list entries are read one step ahead
     for (int i = 0; i < l.max_len; i++) {
@@ -262,14 +241,11 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float dy = c.fpy - xy.y;
         const float bdx = q.y * dx;
         const float cdy = q.z * dy;
-        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, cdy * dy));
-        const bool hit = work & (p2 >= q.w);
-        const float o = oc.x;
-        const float G = __builtin_amdgcn_exp2f(p2);
-        const float v = o * G;
-        const bool unclamped = v <= amax;
-        const float alpha = unclamped ? v : amax;  // min(alpha_max, v): v is never NaN here
-        const float oma = unclamped ? fmaf(-o, G, 1.0f) : 1.0f - amax;
+        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, fmaf(cdy, dy, q.w)));
+        const bool hit = work & (p2 >= l2amin);
+        const float v = __builtin_amdgcn_exp2f(p2);              // o exp(-q/2) >= 0
+        const float alpha = __builtin_amdgcn_fmed3f(v, 0.0f, amax);  // min(alpha_max, v)
+        const float oma = 1.0f - alpha;
         const float Tn = f.T * oma;
         const bool below = Tn < tmin;
         const bool stop = hit & below;
@@ -283,9 +259,9 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
             cnt.blend += blend ? 1 : 0;
         }
         f.done = stop ? 1.0f : f.done;
-        f.C0 = fmaf(wgt, oc.y, f.C0);
-        f.C1 = fmaf(wgt, oc.z, f.C1);
-        f.C2 = fmaf(wgt, oc.w, f.C2);
+        f.C0 = fmaf(wgt, oc.x, f.C0);
+        f.C1 = fmaf(wgt, oc.y, f.C1);
+        f.C2 = fmaf(wgt, oc.z, f.C2);
         f.T = blend ? Tn : f.T;
         f.last = blend ? jbase + k + 1 : f.last;
     }
@@ -376,6 +352,7 @@ template <bool BG>
 __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, const Batch& b, Log& log, Lists l,
                                          int32_t jbase, Bwd& s) {
     const float amax = a.p.alpha_max;
+    const float l2amin = __log2f(a.p.alpha_min);
     const uint16_t* lst = b.list16[c.list_id];
     const int quad = (c.lane >> 2) & 3;
     // log row of the component this lane's quad stores as w0 after the reduce-scatter; its w1
@@ -395,42 +372,40 @@ __device__ __forceinline__ void bwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float2 xy = b.xy[k];
         const float4 q = b.q[k];
         const float4 oc = b.oc[k];
-        // the pair evaluation of eval_pair, for every lane
+        // the forward's pair evaluation, for every lane
         const float dx = c.fpx - xy.x;
         const float dy = c.fpy - xy.y;
         const float bdx = q.y * dx;
         const float cdy = q.z * dy;
-        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, cdy * dy));
-        // bitwise: no short-circuit branch around the threshold's LDS read
-        const bool contrib = active & (jk < s.nc) & (p2 >= q.w);
+        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, fmaf(cdy, dy, q.w)));
+        const bool contrib = active & (jk < s.nc) & (p2 >= l2amin);
         const unsigned long long cm =
-            am & __builtin_amdgcn_ballot_w64(jk < s.nc) & __builtin_amdgcn_ballot_w64(p2 >= q.w);
-        const float o = oc.x;
-        const float G = __builtin_amdgcn_exp2f(p2);
-        const float v = o * G;
+            am & __builtin_amdgcn_ballot_w64(jk < s.nc) & __builtin_amdgcn_ballot_w64(p2 >= l2amin);
+        const float v = __builtin_amdgcn_exp2f(p2);              // o G, G = exp(-q/2)
         const bool unclamped = v <= amax;
-        const float alpha = unclamped ? v : amax;  // min(alpha_max, v): v is never NaN here
-        const float oma = unclamped ? fmaf(-o, G, 1.0f) : 1.0f - amax;
+        const float alpha = __builtin_amdgcn_fmed3f(v, 0.0f, amax);  // min(alpha_max, v)
+        const float oma = 1.0f - alpha;
         const float inv = __builtin_amdgcn_rcpf(oma);  // 1 - alpha >= 1 - alpha_max > 0 where it counts
         const float Tj = s.T * inv;
         // dL/dalpha = T_j sum_ch g_ch (c_ch - B_ch) - T_final / (1 - alpha) sum_ch g_ch bg_ch
-        const float ge = fmaf(s.g0, oc.y, fmaf(s.g1, oc.z, s.g2 * oc.w)) - s.GB;
+        const float ge = fmaf(s.g0, oc.x, fmaf(s.g1, oc.y, s.g2 * oc.z)) - s.GB;
         float dLda = Tj * ge;
         if (BG) dLda = fmaf(-s.Tfin * inv, s.gbg, dLda);
         // zero where the pair does not contribute (selects, so no garbage of other lanes leaks)
         const float wgt = contrib ? alpha * Tj : 0.0f;
-        const float gG = (contrib && unclamped) ? G * dLda : 0.0f;  // dL/do; times o: dL/dq factor
+        // o G dL/dalpha: dL/do times o, and the factor of the mean and conic gradients
+        const float gv = (contrib && unclamped) ? v * dLda : 0.0f;
         // per-pixel sums whose entry-constant factors are applied once per entry when the batch
-        // is flushed: dL/dmean2d = -ln2 o (2 a, b; b, 2 c) (gG dx, gG dy) in the log2-scaled
-        // conic, dL/d(A, B, C) = o (-1/2, -1, -1/2) (gG dx dx, gG dx dy, gG dy dy)
-        const float gx = gG * dx, gy = gG * dy;
+        // is flushed: dL/dmean2d = -ln2 (2 a, b; b, 2 c) (gv dx, gv dy) in the log2-scaled
+        // conic, dL/d(A, B, C) = (-1/2, -1, -1/2) (gv dx dx, gv dx dy, gv dy dy), dL/do = gv / o
+        const float gx = gv * dx, gy = gv * dy;
         float d[9];
         d[0] = gx;
         d[1] = gy;
         d[2] = gx * dx;
         d[3] = gx * dy;
         d[4] = gy * dy;
-        d[5] = gG;
+        d[5] = gv;
         d[6] = wgt * s.g0;
         d[7] = wgt * s.g1;
         d[8] = wgt * s.g2;
@@ -552,14 +527,14 @@ __device__ __forceinline__ void gather_sub_batch(const RasterArgs& a, const Batc
     if (part == 0) {
         // the entry-constant factors of the mean and conic gradients (see bwd_walk)
         const float4 q = b.q[k];
-        const float o = b.oc[k].x;
-        rec[0] = -kLn2 * o * fmaf(2.0f * q.x, d[0], q.y * d[1]);
-        rec[1] = -kLn2 * o * fmaf(q.y, d[0], 2.0f * q.z * d[1]);
-        rec[2] = d[2] * (-0.5f * o);
-        rec[3] = d[3] * -o;
-        rec[4] = d[4] * (-0.5f * o);
+        rec[0] = -kLn2 * fmaf(2.0f * q.x, d[0], q.y * d[1]);
+        rec[1] = -kLn2 * fmaf(q.y, d[0], 2.0f * q.z * d[1]);
+        rec[2] = d[2] * -0.5f;
+        rec[3] = -d[3];
+        rec[4] = d[4] * -0.5f;
     } else {
-        rec[0] = d[0];
+        const float o = b.oc[k].w;  // above alpha_min > 0 for every entry that reaches a pixel
+        rec[0] = d[0] != 0.0f ? d[0] / o : 0.0f;
         rec[1] = d[1];
         rec[2] = d[2];
         rec[3] = d[3];
