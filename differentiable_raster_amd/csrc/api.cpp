@@ -127,6 +127,8 @@ struct BinWs {
     int32_t *kept, *cap_offsets;
     int32_t* order_hist;    // tile-order bucket counts per chunk
     BinReadback* readback;  // counts and depth range read by the host
+    int4* huge_rects;       // [2 * huge_rect_cap(inst_cap)] rectangles written by a workgroup each
+    int32_t* huge_count;    // [1]
 };
 
 BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t inst_cap, size_t* bytes) {
@@ -152,6 +154,8 @@ BinWs carve_bin(void* ws, int32_t n, int32_t V, int32_t tiles_total, int64_t ins
     w.cap_offsets = c.take<int32_t>(tiles_total);
     w.order_hist = c.take<int32_t>(tile_order_hist_ints(tiles_total) + 1);
     w.readback = c.take<BinReadback>(1);
+    w.huge_rects = c.take<int4>(2 * (size_t)huge_rect_cap(inst_cap));
+    w.huge_count = c.take<int32_t>(1);
     *bytes = c.used;
     return w;
 }
@@ -189,6 +193,9 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     ra->inst_base = proj->inst_base;
     ra->n_tiles = proj->n_tiles;
     ra->partials = nullptr;
+    ra->huge_slots = nullptr;
+    ra->huge_count = nullptr;
+    ra->huge_cap = 0;
     ra->num_instances = bins->count;
     ra->capped = use_capped ? 1 : 0;
     ra->counters = nullptr;
@@ -201,10 +208,13 @@ gs_status check_partials(const gs_projected* proj, const gs_bins* bins, void* ws
         return fail(GS_ERR_INVALID_ARGUMENT, "n_tiles / inst_base are null");
     if (bins->count < 0 || bins->count > bins->capacity)
         return fail(GS_ERR_INVALID_ARGUMENT, "bins->count %lld outside [0, capacity]", (long long)bins->count);
-    const size_t need = sizeof(float) * 9 * (size_t)bins->count;
-    if (need > 0 && (!ws || ws_bytes < need))
-        return fail(GS_ERR_CAPACITY, "raster workspace %zu < %zu bytes", ws_bytes, need);
-    ra->partials = static_cast<float*>(ws);
+    const size_t need = raster_ws_bytes(bins->count);
+    if (!ws || ws_bytes < need) return fail(GS_ERR_CAPACITY, "raster workspace %zu < %zu bytes", ws_bytes, need);
+    Carver c(ws);
+    ra->partials = c.take<float>(9 * (size_t)bins->count);
+    ra->huge_count = c.take<int32_t>(1);
+    ra->huge_slots = c.take<int4>((size_t)huge_slot_cap(bins->count));
+    ra->huge_cap = huge_slot_cap(bins->count);
     return GS_OK;
 }
 
@@ -395,7 +405,7 @@ gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V
 
 size_t gs_raster_workspace_size(int64_t instance_capacity) {
     if (instance_capacity < 0) return 0;
-    return align256(sizeof(float) * 9 * (size_t)instance_capacity);
+    return raster_ws_bytes(instance_capacity);
 }
 
 size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height, int64_t instance_capacity) {
@@ -502,7 +512,8 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         uint32_t* v1 = odd ? reinterpret_cast<uint32_t*>(bins->vals) : w.tval_alt;
         if (e == hipSuccess)
             e = launch_emit(packed, proj->n_tiles, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity,
-                            nvis, tiles_x, tpv, (int32_t)M, w.emit_offsets, k0, reinterpret_cast<int32_t*>(v0), s);
+                            nvis, tiles_x, tpv, (int32_t)M, w.emit_offsets, w.huge_rects, w.huge_count,
+                            huge_rect_cap(bins->capacity), k0, reinterpret_cast<int32_t*>(v0), s);
         if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
         if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);
     }

@@ -171,8 +171,10 @@ __device__ __forceinline__ int slot_tiles(const uint32_t* packed, const int32_t*
 }
 
 __global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* packed, const int32_t* n_tiles,
-                                                            int32_t capacity, int32_t total, int32_t* chunk_counts) {
+                                                            int32_t capacity, int32_t total, int32_t* chunk_counts,
+                                                            int32_t* huge_count) {
     __shared__ int s_wave[kEmitWaves];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *huge_count = 0;  // the emission appends after this kernel
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int64_t wbase = (int64_t)blockIdx.x * kEmitChunk + w * kEmitWaveSlots;
     int sum = 0;
@@ -196,12 +198,17 @@ __global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* pack
 }
 
 // Rectangles of more than kSmallRect tiles are written by the whole wavefront, 64 instances per
-// step, so that a few large splats do not serialize on one lane.
+// step, so that a few large splats do not serialize on one lane.  Rectangles of more than
+// kHugeRect tiles go to a list instead and emit_huge_kernel writes each with a workgroup: near
+// the camera such splats are many, and the depth order puts them all in the first chunks, where
+// one wavefront would write them one after another.  Every instance's position is fixed by the
+// scan, so the list order changes nothing.
 constexpr int kSmallRect = 8;
 
 __global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* chunk_offsets,
                                                       const ushort4* rect, int32_t capacity, int32_t total,
                                                       int32_t tiles_x, int32_t tiles_per_view, int32_t M,
+                                                      int4* huge_list, int32_t* huge_count, int32_t huge_cap,
                                                       uint32_t* tile_keys, int32_t* vals) {
     __shared__ int s_wave[kEmitWaves];
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -249,12 +256,44 @@ __global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, co
             const int w0 = __shfl((int)e.rc.z, src) - x0 + 1;
             const uint32_t vb = (uint32_t)__shfl((int)e.vbase, src);
             const int32_t sl = __shfl((int)e.slot, src);
+            if (n0 > kHugeRect) {
+                int h = 0;
+                if (lane == 0) h = atomicAdd(huge_count, 1);
+                h = __shfl(h, 0);
+                if (h < huge_cap) {
+                    if (lane == 0) {
+                        huge_list[2 * h] = make_int4(o0, n0, x0 | (y0 << 16), w0);
+                        huge_list[2 * h + 1] = make_int4((int)vb, sl, 0, 0);
+                    }
+                    continue;
+                }
+                // a full list (never, with the list sized for M instances): written here
+            }
             for (int k = lane; k < n0; k += kWave) {
                 const int dy = k / w0, dx = k - dy * w0;
                 if (o0 + k < M) {
                     tile_keys[o0 + k] = vb + (uint32_t)((y0 + dy) * tiles_x + x0 + dx);
                     vals[o0 + k] = sl;
                 }
+            }
+        }
+    }
+}
+
+// One workgroup per listed rectangle (grid-stride over the list).
+__global__ __launch_bounds__(kBlock) void emit_huge_kernel(const int4* huge_list, const int32_t* huge_count,
+                                                           int32_t huge_cap, int32_t tiles_x, int32_t M,
+                                                           uint32_t* tile_keys, int32_t* vals) {
+    const int32_t cnt = min(*huge_count, huge_cap);
+    for (int32_t h = blockIdx.x; h < cnt; h += gridDim.x) {
+        const int4 a = huge_list[2 * h], b = huge_list[2 * h + 1];
+        const int32_t o0 = a.x, n0 = a.y, x0 = a.z & 0xFFFF, y0 = a.z >> 16, w0 = a.w;
+        const uint32_t vb = (uint32_t)b.x;
+        for (int k = threadIdx.x; k < n0; k += kBlock) {
+            const int dy = k / w0, dx = k - dy * w0;
+            if (o0 + k < M) {
+                tile_keys[o0 + k] = vb + (uint32_t)((y0 + dy) * tiles_x + x0 + dx);
+                vals[o0 + k] = b.y;
             }
         }
     }
@@ -536,15 +575,20 @@ int32_t emit_chunks(int32_t total) { return total > 0 ? (total + kEmitChunk - 1)
 
 hipError_t launch_emit(const uint32_t* packed, const int32_t* n_tiles, const ushort4* rect, int32_t capacity,
                        int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets,
-                       uint32_t* tile_keys, int32_t* vals, hipStream_t s) {
+                       int4* huge_list, int32_t* huge_count, int32_t huge_cap, uint32_t* tile_keys, int32_t* vals,
+                       hipStream_t s) {
     const int32_t nc = emit_chunks(total);
     if (nc == 0) return hipSuccess;
     hipLaunchKernelGGL(emit_count_kernel, dim3(nc), dim3(kBlock), 0, s, packed, n_tiles, capacity, total,
-                       chunk_offsets);
+                       chunk_offsets, huge_count);
     const hipError_t e = launch_scan_small(chunk_offsets, nc, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(emit_kernel, dim3(nc), dim3(kBlock), 0, s, packed, chunk_offsets, rect, capacity, total, tiles_x,
-                       tiles_per_view, M, tile_keys, vals);
+                       tiles_per_view, M, huge_list, huge_count, huge_cap, tile_keys, vals);
+    // at most one listed rectangle per kHugeRect instances
+    const int32_t grid = huge_cap < 1024 ? huge_cap : 1024;
+    hipLaunchKernelGGL(emit_huge_kernel, dim3(grid), dim3(kBlock), 0, s, huge_list, huge_count, huge_cap, tiles_x, M,
+                       tile_keys, vals);
     return hipGetLastError();
 }
 

@@ -149,9 +149,14 @@ hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int3
                              int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, hipStream_t s);
 // Instances of the depth-sorted slots: chunk_offsets holds emit_chunks(total) ints of workspace.
 int32_t emit_chunks(int32_t total);
+// Rectangles of more than kHugeRect tiles are listed (huge_list, two int4 per entry, at most
+// huge_rect_cap(M) entries; huge_count one int) and written by a workgroup each.
+constexpr int kHugeRect = 256;
+inline int32_t huge_rect_cap(int64_t instances) { return (int32_t)(instances / kHugeRect + 1); }
 hipError_t launch_emit(const uint32_t* packed, const int32_t* n_tiles, const ushort4* rect, int32_t capacity,
                        int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets,
-                       uint32_t* tile_keys, int32_t* vals, hipStream_t s);
+                       int4* huge_list, int32_t* huge_count, int32_t huge_cap, uint32_t* tile_keys, int32_t* vals,
+                       hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
 hipError_t launch_ranges(const uint32_t* tile_keys, int32_t M, int32_t* ranges, hipStream_t s);
 // Heavy-first permutation of the tiles (stable counting sort on a 5-bit length bucket); hist
@@ -180,7 +185,17 @@ struct RasterArgs {
     int64_t num_instances;       // backward: records in use
     int32_t capped;              // the lists are the top-K capped ones (some instances are in none)
     int64_t* counters;           // optional
+    // backward: slots with more than kHugeSlot records, listed (int4 (slot index, first record,
+    // records, 0)) for a workgroup each; the raster kernel clears the count
+    int4* huge_slots;
+    int32_t* huge_count;
+    int32_t huge_cap;
 };
+constexpr int kHugeSlot = 256;
+inline int32_t huge_slot_cap(int64_t instances) { return (int32_t)(instances / kHugeSlot + 1); }
+// Bytes of the backward's workspace for an instance count: partial records, then the huge-slot
+// list and its count.
+size_t raster_ws_bytes(int64_t instances);
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s);
 hipError_t launch_loss_l1(int64_t n, const float* image, const float* target, float scale, float* dl, float* loss_sum,
                           hipStream_t s);

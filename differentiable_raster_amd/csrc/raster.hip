@@ -690,8 +690,10 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
 // instances' partial records, which lie contiguously at [inst_base, inst_base + n_tiles).  A lane
 // adds up the records of its own slot in instance order; a slot with more than kHeavy records
 // (a large splat) is added up by the whole wavefront instead (each lane a strided share, then a
-// fixed-order wavefront reduction), so that one large splat does not hold up 63 lanes.  Every sum
-// is taken in a fixed order.
+// fixed-order wavefront reduction), so that one large splat does not hold up 63 lanes.  A slot
+// with more than kHugeSlot records is listed and added up by a workgroup of its own
+// (reduce_huge_kernel): in a large scene such splats are many and neighbours in index order, and
+// one wavefront would add them up one after another.  Every sum is taken in a fixed order.
 constexpr int kHeavy = 16;
 
 __device__ __forceinline__ void store_grad(const Grads& g, size_t i, const float d[9]) {
@@ -707,7 +709,9 @@ __device__ __forceinline__ void store_grad(const Grads& g, size_t i, const float
 
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis_count, int32_t V, int32_t capacity,
                                                               const int32_t* inst_base, const int32_t* n_tiles,
-                                                              const float* partials, int64_t num_instances, Grads g) {
+                                                              const float* partials, int64_t num_instances,
+                                                              int4* huge_slots, int32_t* huge_count, int32_t huge_cap,
+                                                              Grads g) {
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t wave = (int32_t)(blockIdx.x * (256 / kWave) + threadIdx.x / kWave);
     const int32_t waves = (int32_t)(gridDim.x * (256 / kWave));
@@ -725,8 +729,17 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis
                 // clamped to the records that exist (only a stale projection could reach past them)
                 n = (off < 0 || off > num_instances) ? 0 : (int)min((int64_t)n_tiles[i], num_instances - off);
             }
-            const bool heavy = n > kHeavy;
-            if (s < cnt && !heavy) {
+            bool heavy = n > kHeavy, listed = false;
+            if (n > kHugeSlot) {
+                const int h = atomicAdd(huge_count, 1);
+                if (h < huge_cap) {
+                    huge_slots[h] = make_int4((int)i, (int)off, n, 0);  // added up by reduce_huge_kernel
+                    listed = true;
+                    heavy = false;
+                }
+                // a full list (never, with the list sized for the instances): summed here
+            }
+            if (s < cnt && !heavy && !listed) {
                 const float* rec = partials + (size_t)off * 9;
                 float d[9];
 #pragma unroll
@@ -758,12 +771,47 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const int32_t* vis
     }
 }
 
+// A listed slot's records summed by one workgroup: each thread a strided share in record order,
+// then a fixed pairwise tree over the threads.
+__global__ __launch_bounds__(256) void reduce_huge_kernel(const int4* huge_slots, const int32_t* huge_count,
+                                                          int32_t huge_cap, const float* partials, Grads g) {
+    __shared__ float s_sum[9][256];
+    const int32_t cnt = min(*huge_count, huge_cap);
+    for (int32_t h = blockIdx.x; h < cnt; h += gridDim.x) {
+        const int4 e = huge_slots[h];
+        const float* rec = partials + (size_t)e.y * 9;
+        float d[9];
+#pragma unroll
+        for (int t = 0; t < 9; t++) d[t] = 0.0f;
+        for (int k = threadIdx.x; k < e.z; k += 256)
+#pragma unroll
+            for (int t = 0; t < 9; t++) d[t] += rec[9 * k + t];
+#pragma unroll
+        for (int t = 0; t < 9; t++) s_sum[t][threadIdx.x] = d[t];
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if ((int)threadIdx.x < o) {
+#pragma unroll
+                for (int t = 0; t < 9; t++) s_sum[t][threadIdx.x] += s_sum[t][threadIdx.x + o];
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+#pragma unroll
+            for (int t = 0; t < 9; t++) d[t] = s_sum[t][0];
+            store_grad(g, (size_t)e.x, d);
+        }
+        __syncthreads();
+    }
+}
+
 template <bool BG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void raster_bwd_kernel(
     RasterArgs a, const float* t_final, const int32_t* n_contrib, const float* dl, Grads gr) {
     __shared__ Batch b;
     __shared__ Log log;
     __shared__ int s_red[kWaves];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.huge_count = 0;  // the gather appends after this kernel
     const TileCtx c = tile_ctx(a);
     const size_t plane = (size_t)a.width * a.height;
     const size_t p = (size_t)c.py * a.width + c.px;
@@ -794,6 +842,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     __shared__ Batch b;
     __shared__ Log log;
     __shared__ int s_red[kWaves];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.huge_count = 0;  // the gather appends after this kernel
     const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, c.inside ? 0.0f : 1.0f};
     Counts cnt{0, 0, 0};
@@ -851,6 +900,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
 
 int32_t fused_lds_entries() { return kBatch; }
 
+// The carving order of the backward's workspace (256-byte aligned pieces): partial records,
+// huge-slot count, huge-slot list.
+size_t raster_ws_bytes(int64_t instances) {
+    const auto a256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+    return a256(sizeof(float) * 9 * (size_t)instances) + a256(sizeof(int32_t)) +
+           a256(sizeof(int4) * (size_t)huge_slot_cap(instances));
+}
+
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s) {
     const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
     if (a.counters)
@@ -884,7 +941,11 @@ static hipError_t with_partials(const RasterArgs& a, Grads g, hipStream_t s, Lau
     if (a.capped && n > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.partials, n);
     launch();
     hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid_for(a.capacity)), dim3(256), 0, s, a.vis_count, a.V,
-                       a.capacity, a.inst_base, a.n_tiles, a.partials, a.num_instances, g);
+                       a.capacity, a.inst_base, a.n_tiles, a.partials, a.num_instances, a.huge_slots, a.huge_count,
+                       a.huge_cap, g);
+    const int32_t grid = a.huge_cap < 1024 ? a.huge_cap : 1024;
+    hipLaunchKernelGGL(reduce_huge_kernel, dim3(grid), dim3(256), 0, s, a.huge_slots, a.huge_count, a.huge_cap,
+                       a.partials, g);
     return hipGetLastError();
 }
 

@@ -213,7 +213,9 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, 
                      void* stream);
 
 /* Workspace bytes of gs_raster_bwd / gs_raster_fused for an instance capacity: one float32
- * partial-gradient record (9 values) per (Gaussian, tile) instance. */
+ * partial-gradient record (9 values) per (Gaussian, tile) instance, then a short list of the
+ * slots with more than 256 instances (16 bytes per 256 instances), whose records one workgroup
+ * each adds up. */
 size_t gs_raster_workspace_size(int64_t instance_capacity);
 
 /* Workspace bytes of gs_bin_tiles for n Gaussians, V views and an instance capacity. */

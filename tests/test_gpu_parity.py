@@ -188,6 +188,27 @@ def test_gaussian_covering_every_tile_and_image_edges(env):
     run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
 
 
+def test_many_large_splats_neighbours_in_index_and_depth(env):
+    """Splats of more than 256 tiles, next to each other in index and depth order, among small
+    ones: their instances are written and their records added up by a workgroup each."""
+    rng = np.random.default_rng(91)
+    cams = [pinhole(400, 320, f=200.0, cx=200.0, cy=160.0), pinhole(400, 320, f=260.0, cx=190.0, cy=170.0)]
+    nb, ns = 12, 3000
+    means = np.concatenate([np.c_[rng.uniform(-1, 1, nb), rng.uniform(-1, 1, nb), rng.uniform(7.5, 8.5, nb)],
+                            np.c_[rng.uniform(-1.6, 1.6, ns), rng.uniform(-1.3, 1.3, ns), rng.uniform(2.5, 6, ns)]])
+    log_scales = np.concatenate([np.full((nb, 3), 0.8), rng.normal(-3.3, 0.4, (ns, 3))])
+    q = rng.normal(size=(nb + ns, 4))
+    logits = np.concatenate([np.full(nb, -1.0), rng.normal(0, 1, ns)])
+    colors = rng.uniform(0, 1, (nb + ns, 3))
+    sc = scene_from(means, log_scales, q / np.linalg.norm(q, axis=1, keepdims=True), logits, colors, cams,
+                    target=rng.uniform(0, 1, (2, 3, 320, 400)))
+    r = run_view_checks(env, sc, sc.settings(), mode="fused")
+    big = [int((r.projected_host(v)["n_tiles"] > 256).sum()) for v in range(2)]
+    print(f"[large] slots with more than 256 tiles per view: {big}", flush=True)
+    assert min(big) >= 8
+    run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
+
+
 def test_capacity_error_then_retry(env):
     oracle, pipeline, torch = env
     from differentiable_raster_amd import gsmi
