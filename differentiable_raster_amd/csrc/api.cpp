@@ -340,8 +340,11 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     a.row_totals = c.take<int32_t>((size_t)2 * V);
     a.scan_partials = c.take<int32_t>(scan_partials_bytes(nb, 2 * V) / sizeof(int32_t));
     gs_readback* rb = out->readback;
-    a.block_depth = rb ? c.take<uint2>((size_t)nb) : nullptr;
-    a.summary = rb ? c.take<CountSummary>(1) : nullptr;
+    uint2* block_depth = c.take<uint2>((size_t)nb);
+    CountSummary* summary = c.take<CountSummary>(1);
+    a.block_depth = rb ? block_depth : nullptr;
+    a.summary = rb ? summary : nullptr;
+    a.seen = c.take<uint8_t>((size_t)nb * 256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (rb) rb->filled = false;
     gs_status st2 = hip_check(launch_project_count(a, s), "gs_project launch");

@@ -93,6 +93,7 @@ struct ProjectArgs {
     uint2* block_depth;      // [nb] (smallest, complement of largest) visible depth bits per block;
                              // NULL: not computed
     CountSummary* summary;   // device copy of the counts (written when block_depth is set)
+    uint8_t* seen;           // [nb * 256] 1 where some view sees the Gaussian (counting pass)
 };
 // The counting pass, the block scans and (with block_depth) the count summary: afterwards
 // vis/inst counts are final and the summary may be copied out while the writing pass runs.

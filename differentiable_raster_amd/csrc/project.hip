@@ -5,14 +5,17 @@
 //   pass 1 counts the visible Gaussians of each 256-Gaussian block and view, and adds the
 //          block's tile-instance count into the view's total;
 //   an exclusive scan of the block counts gives each block its first slot per view;
-//   pass 2 recomputes the same decisions (same code, same rounding) and writes the records of
-//          visible Gaussians at slot = block offset + rank within the block, so slots follow
-//          ascending Gaussian index, together with each slot's instance base (the same scan
-//          over the blocks' tile-instance counts, plus a wave scan inside the block) and the
-//          packed 64-byte record the rasterizers stage with one line per list entry.
-// Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read once per Gaussian:
-// the counting pass only checks that they are bounded (which makes every colour finite), and the
-// writing pass keeps them in registers for all views.
+//   pass 2 recomputes the same decisions (same code, same rounding) for the Gaussians that
+//          pass 1 found in some view and writes the records of visible Gaussians at
+//          slot = block offset + rank within the block, so slots follow ascending Gaussian
+//          index, together with each slot's instance base (the same scan over the blocks'
+//          tile-instance counts, plus a wave scan inside the block) and the packed 64-byte
+//          record the rasterizers stage with one line per list entry.
+// Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read only for Gaussians
+// that some view sees (in a large scene most are outside every view): the counting pass checks
+// at the first such view that they are bounded (which makes every colour finite) and flags the
+// Gaussian, and the writing pass keeps a flagged Gaussian's coefficients in registers for all
+// views.
 #include "common.h"
 #include "gauss.h"
 
@@ -149,11 +152,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     Geo g;
     g.ok = false;
-    bool bounded = true;
-    if (i < a.n) {
-        g = load_geo(a, i);
-        if (g.ok) bounded = sh_bounded<3 * (NY + 1)>(a, i);
-    }
+    if (i < a.n) g = load_geo(a, i);
+    // the coefficients are checked at the first view that sees the Gaussian: most Gaussians of a
+    // large scene are outside every view and their 192 bytes are never read
+    bool bounded = true, checked = false, seen = false;
     const int nb = gridDim.x;
     // visible depth range of this thread over all views, as float32 bit patterns (depths are
     // above znear > 0, so the patterns order like the values)
@@ -163,8 +165,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         r.ntiles = 0;
         float3 dir;
         bool vis = (i < a.n) && project_geom(a, g, a.cams.c[v], r, dir);
+        if (vis && !checked) {
+            bounded = sh_bounded<3 * (NY + 1)>(a, i);
+            checked = true;
+        }
         // some coefficient is huge or not finite: the colour itself decides
         if (vis && !bounded) vis = colour_finite<DEG>(a, i, dir);
+        seen |= vis;
         if (vis) {
             dlo = min(dlo, __float_as_uint(r.depth));
             dhi = max(dhi, __float_as_uint(r.depth));
@@ -188,6 +195,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         }
         __syncthreads();
     }
+    if (i < a.n) a.seen[i] = seen ? 1 : 0;
     if (a.block_depth) {
         uint32_t nhi = ~dhi;
         for (int o = kWave / 2; o > 0; o >>= 1) {
@@ -221,11 +229,13 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     if (blockIdx.x == 0 && threadIdx.x < a.V) a.vis_count[threadIdx.x] = a.row_totals[threadIdx.x];
     Geo g;
     g.ok = false;
-    // the Gaussian's SH coefficients, read once for all views (row k*3 + channel)
+    // the Gaussian's SH coefficients (row k*3 + channel), read once for all views, and only for
+    // Gaussians that the counting pass found in some view: those outside every view (most of a
+    // large scene) cost neither coefficient reads nor projection here
     float coef[NC];
 #pragma unroll
     for (int k = 0; k < NC; k++) coef[k] = 0.0f;
-    if (i < a.n) {
+    if (i < a.n && a.seen[i]) {
         g = load_geo(a, i);
         if (g.ok) {
 #pragma unroll
@@ -359,7 +369,7 @@ size_t project_ws_bytes(int32_t n, int32_t V) {
     const int32_t nb = project_blocks(n > 0 ? n : 1);
     return 2 * align256(sizeof(int32_t) * (size_t)nb * 2 * V) + align256(sizeof(int32_t) * 2 * V) +
            align256(scan_partials_bytes(nb, 2 * V)) + align256(sizeof(uint2) * (size_t)nb) +
-           align256(sizeof(CountSummary));
+           align256(sizeof(CountSummary)) + align256((size_t)nb * kBlock);
 }
 
 hipError_t launch_project_count(const ProjectArgs& a0, hipStream_t s) {
