@@ -308,37 +308,60 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
 
 // inst_count[v] = the 64-bit sum of row V + v of the block counts (one block per view; 64 bits,
 // so that a total past 2^31 is reported as such and refused by the binning call).
-__global__ __launch_bounds__(kBlock) void inst_total_kernel(const int32_t* block_counts, int32_t V, int32_t nb,
-                                                            int64_t* inst_count) {
-    __shared__ long long s_part[kBlock / kWave];
+// 1024 threads, four independent loads per step: a large scene has ~10^5 blocks per row, and a
+// loop of dependent loads over them would take hundreds of microseconds.
+constexpr int kSumBlock = 1024;
+
+__global__ __launch_bounds__(kSumBlock) void inst_total_kernel(const int32_t* block_counts, int32_t V, int32_t nb,
+                                                               int64_t* inst_count) {
+    __shared__ long long s_part[kSumBlock / kWave];
     const int v = blockIdx.x;
     const int32_t* row = block_counts + (size_t)(V + v) * nb;
     long long t = 0;
-    for (int32_t b = threadIdx.x; b < nb; b += kBlock) t += row[b];
+    for (int32_t b0 = 0; b0 < nb; b0 += 4 * kSumBlock) {
+        int x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int32_t b = b0 + u * kSumBlock + (int)threadIdx.x;
+            x[u] = b < nb ? row[b] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) t += x[u];
+    }
     for (int o = kWave / 2; o > 0; o >>= 1) t += __shfl_xor(t, o);
     if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = t;
     __syncthreads();
     if (threadIdx.x == 0) {
         long long sum = 0;
-        for (int k = 0; k < kBlock / kWave; k++) sum += s_part[k];
+        for (int k = 0; k < kSumBlock / kWave; k++) sum += s_part[k];
         inst_count[v] = sum;
     }
 }
 
 // The count summary (one block): visible slots per view from the block scans, instances per
 // view from inst_total_kernel, and the visible depth range from the per-block ranges.
-__global__ __launch_bounds__(kBlock) void count_summary_kernel(const int32_t* row_totals, const int64_t* inst_count,
-                                                               int32_t V, const uint2* block_depth, int32_t nb,
-                                                               CountSummary* out) {
-    __shared__ uint32_t s_lo[kBlock / kWave], s_nhi[kBlock / kWave];
+__global__ __launch_bounds__(kSumBlock) void count_summary_kernel(const int32_t* row_totals,
+                                                                  const int64_t* inst_count, int32_t V,
+                                                                  const uint2* block_depth, int32_t nb,
+                                                                  CountSummary* out) {
+    __shared__ uint32_t s_lo[kSumBlock / kWave], s_nhi[kSumBlock / kWave];
     if ((int)threadIdx.x < V) {
         out->vis[threadIdx.x] = row_totals[threadIdx.x];
         out->inst[threadIdx.x] = inst_count[threadIdx.x];
     }
     uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;
-    for (int32_t k = threadIdx.x; k < nb; k += kBlock) {
-        lo = min(lo, block_depth[k].x);
-        nhi = min(nhi, block_depth[k].y);
+    for (int32_t k0 = 0; k0 < nb; k0 += 4 * kSumBlock) {
+        uint2 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int32_t k = k0 + u * kSumBlock + (int)threadIdx.x;
+            x[u] = k < nb ? block_depth[k] : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            lo = min(lo, x[u].x);
+            nhi = min(nhi, x[u].y);
+        }
     }
     for (int o = kWave / 2; o > 0; o >>= 1) {
         lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
@@ -350,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void count_summary_kernel(const int32_t* ro
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int k = 1; k < kBlock / kWave; k++) {
+        for (int k = 1; k < kSumBlock / kWave; k++) {
             lo = min(lo, s_lo[k]);
             nhi = min(nhi, s_nhi[k]);
         }
@@ -381,11 +404,11 @@ hipError_t launch_project_count(const ProjectArgs& a0, hipStream_t s) {
         case 2: hipLaunchKernelGGL(project_count_kernel<2>, dim3(nb), dim3(kBlock), 0, s, a); break;
         default: hipLaunchKernelGGL(project_count_kernel<3>, dim3(nb), dim3(kBlock), 0, s, a); break;
     }
-    hipLaunchKernelGGL(inst_total_kernel, dim3(a.V), dim3(kBlock), 0, s, a.block_counts, a.V, nb, a.inst_count);
+    hipLaunchKernelGGL(inst_total_kernel, dim3(a.V), dim3(kSumBlock), 0, s, a.block_counts, a.V, nb, a.inst_count);
     hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nb, 2 * a.V, a.scan_partials, s);
     if (e != hipSuccess) return e;
     if (a.block_depth)
-        hipLaunchKernelGGL(count_summary_kernel, dim3(1), dim3(kBlock), 0, s, a.row_totals, a.inst_count, a.V,
+        hipLaunchKernelGGL(count_summary_kernel, dim3(1), dim3(kSumBlock), 0, s, a.row_totals, a.inst_count, a.V,
                            a.block_depth, nb, a.summary);
     return hipGetLastError();
 }
