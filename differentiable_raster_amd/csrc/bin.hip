@@ -514,15 +514,20 @@ __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* range
             if ((b & pmask) == prefix) atomicAdd(&s_hist[(b >> shift) & 255u], 1);
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            int cum = 0;
-            int d = 255;
-            for (; d > 0; d--) {
-                if (cum + s_hist[d] >= remaining) break;
-                cum += s_hist[d];
+        // the digit d holding the remaining-th best entry: above(d) < remaining <= above(d) +
+        // hist[d], with above(d) the entries of larger digits (d = 0 when no larger digit holds
+        // it); thread t takes digit 255 - t, so an exclusive prefix over the threads is above(d)
+        {
+            static_assert(kBlock == 256, "one digit per thread");
+            const int d = 255 - (int)threadIdx.x;
+            const int h = s_hist[d];
+            int all;
+            const int above = block_excl_scan(h, s_wave, &all);
+            const bool sel = d > 0 ? (above < remaining && above + h >= remaining) : above < remaining;
+            if (sel) {
+                s_sel[0] = (uint32_t)d;
+                s_sel[1] = (uint32_t)(remaining - above);
             }
-            s_sel[0] = (uint32_t)d;
-            s_sel[1] = (uint32_t)(remaining - cum);
         }
         __syncthreads();
         prefix |= s_sel[0] << shift;
