@@ -227,6 +227,12 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     const int i = blockIdx.x * kBlock + threadIdx.x;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     if (blockIdx.x == 0 && threadIdx.x < a.V) a.vis_count[threadIdx.x] = a.row_totals[threadIdx.x];
+    // a block whose Gaussians no view sees (most blocks of a large scene) writes nothing
+    {
+        bool any = false;
+        for (int v = 0; v < a.V; v++) any |= a.block_counts[v * gridDim.x + blockIdx.x] > 0;
+        if (!any) return;
+    }
     Geo g;
     g.ok = false;
     // the Gaussian's SH coefficients (row k*3 + channel), read once for all views, and only for
