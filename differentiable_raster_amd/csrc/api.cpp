@@ -488,7 +488,8 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         return fail(GS_ERR_CAPACITY, "%lld instances exceed the bins capacity %lld", (long long)M,
                     (long long)bins->capacity);
 
-    hipError_t e = launch_fill_i32(bins->ranges, 0, 2 * (int64_t)tiles_total, s);
+    // the tile ranges start cleared: by the depth-key kernel when there are instances
+    hipError_t e = M > 0 ? hipSuccess : launch_fill_i32(bins->ranges, 0, 2 * (int64_t)tiles_total, s);
     if (e == hipSuccess && M > 0) {
         // depth digits, one entry per visible slot
         int64_t first[GS_MAX_VIEWS + 1];
@@ -502,7 +503,8 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         // keys relative to the smallest visible depth: as many bits as the depth range needs
         const uint32_t key_min = rb.bits[0], key_span = ~rb.bits[1] - rb.bits[0];
         const int dbits = key_span == 0 ? 0 : 32 - __builtin_clz(key_span);
-        e = launch_depth_keys(proj->depth, first, V, proj->capacity, nvis, key_min, w.dkey, w.dval, s);
+        e = launch_depth_keys(proj->depth, first, V, proj->capacity, nvis, key_min, w.dkey, w.dval, bins->ranges,
+                              2 * tiles_total, s);
         if (e == hipSuccess)
             e = launch_radix_sort(w.dkey, w.dval, w.dkey_alt, w.dval_alt, nvis, dbits, w.hist, w.partials, s);
         uint32_t* packed = (radix_passes(dbits) % 2 == 0) ? w.dval : w.dval_alt;

@@ -23,10 +23,13 @@ struct ViewFirst {
 
 // Depth keys relative to the smallest one: the float32 bits of positive depths order like the
 // depths, and subtracting the minimum keeps that order while shortening the keys (fewer passes).
+// Also clears zero[0, n_zero) (the tile ranges), which saves a launch.
 __global__ __launch_bounds__(kBlock) void depth_keys_kernel(const float* depth, ViewFirst vf, int32_t V,
                                                             int32_t capacity, int32_t total, uint32_t key_min,
-                                                            uint32_t* keys, uint32_t* vals) {
+                                                            uint32_t* keys, uint32_t* vals, int32_t* zero,
+                                                            int32_t n_zero) {
     const int32_t e = blockIdx.x * kBlock + threadIdx.x;
+    if (e < n_zero) zero[e] = 0;
     if (e >= total) return;
     int v = 0;
     while (v + 1 < V && e >= vf.first[v + 1]) v++;
@@ -558,12 +561,13 @@ __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* range
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
 
 hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int32_t V, int32_t capacity,
-                             int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, hipStream_t s) {
-    if (total <= 0) return hipSuccess;
+                             int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, int32_t* zero,
+                             int32_t n_zero, hipStream_t s) {
+    if (total <= 0 && n_zero <= 0) return hipSuccess;
     ViewFirst vf;
     for (int v = 0; v <= GS_MAX_VIEWS; v++) vf.first[v] = v <= V ? (int32_t)view_first[v] : total;
-    hipLaunchKernelGGL(depth_keys_kernel, dim3(blocks_for(total)), dim3(kBlock), 0, s, depth, vf, V, capacity, total,
-                       key_min, keys, vals);
+    hipLaunchKernelGGL(depth_keys_kernel, dim3(blocks_for(total > n_zero ? total : n_zero)), dim3(kBlock), 0, s, depth,
+                       vf, V, capacity, total, key_min, keys, vals, zero, n_zero);
     return hipGetLastError();
 }
 

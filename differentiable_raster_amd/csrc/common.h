@@ -146,8 +146,10 @@ struct BinReadback {
 };
 hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count, int32_t V, const float* depth,
                              int32_t capacity, BinReadback* out, hipStream_t s);
+// Also clears zero[0, n_zero).
 hipError_t launch_depth_keys(const float* depth, const int64_t* view_first, int32_t V, int32_t capacity,
-                             int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, hipStream_t s);
+                             int32_t total, uint32_t key_min, uint32_t* keys, uint32_t* vals, int32_t* zero,
+                             int32_t n_zero, hipStream_t s);
 // Instances of the depth-sorted slots: chunk_offsets holds emit_chunks(total) ints of workspace.
 int32_t emit_chunks(int32_t total);
 // Rectangles of more than kHugeRect tiles are listed (huge_list, two int4 per entry, at most
