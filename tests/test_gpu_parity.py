@@ -340,6 +340,43 @@ def test_packed_records_and_instance_bases(env):
         assert g["inst_count"] == int(g["n_tiles"].sum())
 
 
+def test_coefficients_first_checked_at_a_later_view(env):
+    """Gaussians that only the second of two views sees, with non-finite, huge-but-finite and
+    ordinary SH coefficients: the projection reads and checks the coefficients at the first view
+    that sees a Gaussian, so the second view's visible set and records must still equal the
+    oracle's, and a Gaussian outside both views must stay out."""
+    oracle, pipeline, torch = env
+    cam0 = pinhole(64, 48, f=50.0, cx=32.0, cy=24.0)
+    # the second camera looks at the same points from 10 units to the side
+    cam1 = pinhole(64, 48, f=50.0, cx=32.0, cy=24.0, R=np.eye(3), t=[-10.0, 0.0, 0.0])
+    n = 10
+    rng = np.random.default_rng(5)
+    means = np.column_stack([rng.uniform(9.7, 10.3, n), rng.uniform(-0.2, 0.2, n), rng.uniform(2.0, 3.0, n)])
+    means[9] = [40.0, 0.0, 2.5]  # outside both views
+    ls = np.full((n, 3), -2.5)
+    quats = np.tile([1.0, 0.0, 0.0, 0.0], (n, 1))
+    logits = np.full(n, 1.0)
+    rest = rng.standard_normal((n, 45)) * 0.1
+    rest[1, 7] = np.inf
+    rest[2, 20] = np.nan
+    rest[3, 3] = 1e31
+    rest[4, 44] = -2e32
+    rest[9, 5] = np.nan
+    sc = scene_from(means, ls, quats, logits, rng.uniform(0.2, 0.8, (n, 3)), [cam0, cam1], sh_rest=rest,
+                    sh_degree=3)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.iteration(mode="fused", image=True)
+    torch.cuda.synchronize()
+    assert r.projected_host(0)["vis_count"] == 0
+    gpu = r.projected_host(1)
+    o = oracle.project(sc, cam1, st)
+    assert set(gpu["vis_ids"].tolist()) == set(np.nonzero(o["visible"])[0].tolist())
+    assert not {1, 2, 9} & set(gpu["vis_ids"].tolist())
+    assert {0, 3, 4, 5} <= set(gpu["vis_ids"].tolist())
+    parity.compare_projection(oracle, sc, cam1, st, gpu)
+
+
 def test_degenerate_parameters_are_culled_like_the_oracle(env):
     """Non-finite parameters (mean, scale, quaternion, opacity, SH coefficient) and a zero
     quaternion cull the Gaussian in every view; a huge but finite SH coefficient (past the bound
