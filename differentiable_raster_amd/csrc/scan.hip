@@ -1,4 +1,5 @@
-// Device-wide exclusive prefix sums of int32 rows (reduce, scan the block sums, apply).
+// Device-wide exclusive prefix sums of int32 rows (reduce, scan the block sums, apply; rows of at
+// most 16384 values are scanned by one workgroup each in a single launch).
 // Each block owns kChunk = 2048 consecutive elements (8 per thread, thread-contiguous), so
 // every pass reads the input with 128-bit loads where the row length allows.
 #include "common.h"
@@ -111,6 +112,37 @@ __global__ __launch_bounds__(kBlock) void scan_small_kernel(int32_t* a, int32_t 
     }
 }
 
+// Short rows: one workgroup per row scans it in steps of kBlock * kSmallItems values (one
+// launch instead of three) and writes the row total.
+constexpr int32_t kShortRow = 4 * kBlock * kSmallItems;
+
+__global__ __launch_bounds__(kBlock) void scan_rows_short_kernel(const int32_t* in, int32_t* out, int32_t* totals,
+                                                                 int32_t n) {
+    __shared__ int s_wave[kBlock / kWave];
+    const int32_t* r = in + (size_t)blockIdx.x * n;
+    int32_t* o = out + (size_t)blockIdx.x * n;
+    int carry = 0;
+    for (int32_t b0 = 0; b0 < n; b0 += kBlock * kSmallItems) {
+        const int32_t first = b0 + threadIdx.x * kSmallItems;
+        int v[kSmallItems];
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kSmallItems; k++) {
+            v[k] = first + k < n ? r[first + k] : 0;
+            sum += v[k];
+        }
+        int tot;
+        int run = carry + block_exclusive_scan(sum, s_wave, &tot);
+#pragma unroll
+        for (int k = 0; k < kSmallItems; k++) {
+            if (first + k < n) o[first + k] = run;
+            run += v[k];
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0 && totals) totals[blockIdx.x] = carry;
+}
+
 }  // namespace
 
 static int32_t scan_blocks(int32_t n) { return (n + kChunk - 1) / kChunk; }
@@ -121,6 +153,10 @@ size_t scan_partials_bytes(int32_t n, int32_t rows) {
 
 hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, int32_t n, int32_t rows,
                             int32_t* partials, hipStream_t s) {
+    if (n <= kShortRow) {
+        hipLaunchKernelGGL(scan_rows_short_kernel, dim3(rows), dim3(kBlock), 0, s, in, out, totals, n);
+        return hipGetLastError();
+    }
     const int32_t nb = scan_blocks(n > 0 ? n : 1);
     hipLaunchKernelGGL(scan_reduce_kernel, dim3(nb, rows), dim3(kBlock), 0, s, in, n, nb, partials);
     hipLaunchKernelGGL(scan_partials_kernel, dim3(rows), dim3(kBlock), 0, s, partials, nb, totals);
