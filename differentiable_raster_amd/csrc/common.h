@@ -15,6 +15,8 @@ namespace gsmi {
 constexpr int kTile = GS_TILE;            // 16x16 pixels per tile
 constexpr int kTileThreads = kTile * kTile;  // one thread per pixel, 4 wavefronts of 64
 constexpr int kWave = 64;
+// guard band of the per-view frustum cull, as a fraction of the image size beyond each edge
+constexpr float kGuard = 0.15f;
 
 // Camera as the kernels read it (kernel-argument struct, by value).
 struct CamDev {

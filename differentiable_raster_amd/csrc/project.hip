@@ -107,6 +107,12 @@ __device__ bool project_geom(const ProjectArgs& a, const Geo& g, const CamDev& c
     const float idet = 1.0f / det;
     const float mx = fmaf(c.fx * tx, iz, c.cx);
     const float my = fmaf(c.fy * ty, iz, c.cy);
+    // per-view frustum cull with a guard band: the projected centre must lie inside the image
+    // widened by 15 % of its size on every side.  Beyond it lie the near-plane splats far off
+    // axis, whose 2D covariance reaches 1e12 px^2: at image pixels their quadratic form cancels
+    // terms of 1e8 and more, which float32 (records or arithmetic) cannot resolve.
+    const float gx = kGuard * (float)c.width, gy = kGuard * (float)c.height;
+    if (!(mx >= -gx && mx <= (float)c.width + gx && my >= -gy && my <= (float)c.height + gy)) return false;
     // opacity-aware box: o exp(-q/2) >= alpha_min  <=>  q <= 2 ln(o / alpha_min)
     if (!(g.o > p.alpha_min)) return false;
     const float Q = 2.0f * logf(g.o / p.alpha_min);

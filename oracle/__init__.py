@@ -71,6 +71,7 @@ def _load():
         _lib.orc_raster_forward.restype = None
         _lib.orc_raster_backward.restype = None
         _lib.orc_raster_bruteforce.restype = None
+        _lib.orc_pair_alpha.restype = None
         _lib.orc_num_threads.restype = ctypes.c_int
     return _lib
 
@@ -343,63 +344,110 @@ def raster_forward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray
 
     Per pixel: alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop before a
     blend that takes T below t_min; C += alpha T c; T *= 1 - alpha; finally C += T bg.
-    Returns image (3,H,W), T_final (H,W), n_contrib (H,W), flag (H,W), err_C (H,W),
-    evaluated and blended pair counts.
+    Returns image (3,H,W), T_final (H,W), n_contrib (H,W), the evaluated / blended / clamped
+    pair counts, and the float32 error model used by comparisons: err_C (3,H,W) absolute and
+    err_T (H,W) relative bounds; n_dec (H,W) = flagged alpha_min / t_min decisions of the pixel
+    (within float32 reach of their threshold), -1 when more than three; flag = n_dec != 0;
+    unresolved = n_dec < 0; alt = the pixel under every combination of its flagged decisions
+    taken the other way: dict(pix (k,) = y W + x, C (k,3), T (k,), nc (k,)).
     Parity: pinned by the single-Gaussian profile, telescoping identities, a two-Gaussian
-    closed form and brute-force all-Gaussians-per-pixel compositing."""
+    closed form and brute-force all-Gaussians-per-pixel compositing; the error model by
+    float32 evaluations of the same compositing."""
     lib = _load()
     image = np.zeros((3, height, width))
     T = np.zeros((height, width))
     nc = np.zeros((height, width), np.int32)
     flag = np.zeros((height, width), np.int8)
-    err = np.zeros((height, width))
+    err = np.zeros((3, height, width))
     err_T = np.zeros((height, width))
     counters = np.zeros(3, np.int64)
     ranges = np.ascontiguousarray(ranges, np.int32)
     vals = np.ascontiguousarray(vals, np.int32)
     pp = _params(settings)
     m, c, o, col = _rec(records)
-    lib.orc_raster_forward(ctypes.c_int32(width), ctypes.c_int32(height), _p(ranges), _p(vals), _p(m), _p(c), _p(o),
-                           _p(col), ctypes.byref(pp), _p(image), _p(T), _p(nc), _p(flag), _p(err), _p(err_T),
-                           _p(counters))
-    return dict(image=image, T_final=T, n_contrib=nc, flag=flag.astype(bool), err_C=err, err_T=err_T,
-                n_evaluated=int(counters[0]), n_blended=int(counters[1]), n_clamped=int(counters[2]))
+    cap = 4096 + (width * height) // 64
+    while True:
+        alt_n = np.zeros(1, np.int64)
+        alt_pix = np.zeros(cap, np.int64)
+        alt_C = np.zeros((cap, 3))
+        alt_T = np.zeros(cap)
+        alt_nc = np.zeros(cap, np.int32)
+        lib.orc_raster_forward(ctypes.c_int32(width), ctypes.c_int32(height), _p(ranges), _p(vals), _p(m), _p(c),
+                               _p(o), _p(col), ctypes.byref(pp), _p(image), _p(T), _p(nc), _p(flag), _p(err),
+                               _p(err_T), ctypes.c_int64(cap), _p(alt_n), _p(alt_pix), _p(alt_C), _p(alt_T),
+                               _p(alt_nc), _p(counters))
+        if int(alt_n[0]) <= cap:
+            break
+        cap = int(alt_n[0])
+    k = int(alt_n[0])
+    order = np.argsort(alt_pix[:k], kind="stable")
+    alt = dict(pix=alt_pix[:k][order], C=alt_C[:k][order], T=alt_T[:k][order], nc=alt_nc[:k][order])
+    return dict(image=image, T_final=T, n_contrib=nc, n_dec=flag, flag=flag != 0, unresolved=flag < 0, err_C=err,
+                err_T=err_T, alt=alt, n_evaluated=int(counters[0]), n_blended=int(counters[1]),
+                n_clamped=int(counters[2]))
 
 
 def loss_grad_l1(image: np.ndarray, target: np.ndarray, scale: float, err_C: Optional[np.ndarray] = None):
     """dL/dC of L = scale * sum |C - target|: scale * sign(C - target), sign(0) = 0.
-    Also returns the pixels whose sign float32 evaluation could decide differently."""
+    Also returns dg (3,H,W): 2 |scale| for the components whose sign float32 evaluation could
+    take differently (|C - target| within the colour's error bound err_C), 0 elsewhere: the
+    most that such a component of dL/dC can differ by."""
     diff = image - target.astype(np.float64)
     g = np.sign(diff) * scale
-    unsure = None
+    dg = None
     if err_C is not None:
-        unsure = (np.abs(diff) <= 4.0 * err_C[None] + 1e-12).any(axis=0)
-    return g, unsure
+        dg = np.where(np.abs(diff) <= err_C, 2.0 * abs(scale), 0.0)
+    return g, dg
 
 
 def raster_backward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray, records: dict, settings,
-                    dldc: np.ndarray, pixel_skip: Optional[np.ndarray] = None) -> dict:
+                    dldc: np.ndarray, dg: Optional[np.ndarray] = None) -> dict:
     """Gradients of L with respect to the per-slot 2D records (means2D in pixels, conic
     (A, B, C), activated opacity, post-clamp colour), by reverse traversal of each pixel's
-    blended entries.  Returns d_mean2d (S,2), d_conic (S,3), d_opacity (S,), d_color (S,3),
-    mag (S,9) = summed absolute contributions, slot_flag (S,).
-    Parity: pinned by central finite differences of the loss and closed-form derivatives."""
+    blended entries.  Returns d_mean2d (S,2), d_conic (S,3), d_opacity (S,), d_color (S,3) and,
+    per slot and component (mean x, y, conic A, B, C, opacity, colour r, g, b): mag (S,9) =
+    summed magnitudes of the contributions' parts; err (S,9) = summed float32 error bounds of
+    the contributions; widen (S,9) = the most that taking flagged decisions the other way (and
+    the dL/dC uncertainty dg, optional (3,H,W)) changes the slot's gradient; slot_flag (S,) =
+    slots of unresolved pixels; stats = (pixels with flagged decisions, unresolved pixels,
+    alternative walks).
+    Parity: pinned by central finite differences of the loss and closed-form derivatives; the
+    error bounds by float32 evaluations of the same backward."""
     lib = _load()
     S = records["opacity"].shape[0]
     out = dict(d_mean2d=np.zeros((S, 2)), d_conic=np.zeros((S, 3)), d_opacity=np.zeros(S), d_color=np.zeros((S, 3)),
-               mag=np.zeros((S, 9)), slot_flag=np.zeros(S, np.int8))
+               mag=np.zeros((S, 9)), err=np.zeros((S, 9)), widen=np.zeros((S, 9)), slot_flag=np.zeros(S, np.int8))
+    stats = np.zeros(3, np.int64)
     ranges = np.ascontiguousarray(ranges, np.int32)
     vals = np.ascontiguousarray(vals, np.int32)
     dldc = np.ascontiguousarray(dldc, np.float64)
-    skip = None if pixel_skip is None else np.ascontiguousarray(pixel_skip, np.int8)
+    dgc = None if dg is None else np.ascontiguousarray(dg, np.float64)
     pp = _params(settings)
     m, c, o, col = _rec(records)
     lib.orc_raster_backward(ctypes.c_int32(width), ctypes.c_int32(height), _p(ranges), _p(vals), _p(m), _p(c), _p(o),
-                            _p(col), ctypes.byref(pp), _p(dldc), None if skip is None else _p(skip),
+                            _p(col), ctypes.byref(pp), _p(dldc), None if dgc is None else _p(dgc),
                             _p(out["d_mean2d"]), _p(out["d_conic"]), _p(out["d_opacity"]), _p(out["d_color"]),
-                            _p(out["mag"]), _p(out["slot_flag"]))
+                            _p(out["mag"]), _p(out["err"]), _p(out["widen"]), _p(out["slot_flag"]), _p(stats))
     out["slot_flag"] = out["slot_flag"].astype(bool)
+    out["stats"] = dict(flagged_pixels=int(stats[0]), unresolved_pixels=int(stats[1]), alternative_walks=int(stats[2]))
     return out
+
+
+def pair_alpha(px, py, mean2d, conic, opacity):
+    """v = o exp(-q/2) and the float32 error bound rel (relative) of the compositing's error
+    model for n arbitrary (pixel centre, record) pairs: px, py (n,), mean2d (n,2), conic (n,3),
+    opacity (n,).  Returns (v, rel)."""
+    lib = _load()
+    px = np.ascontiguousarray(px, np.float64)
+    py = np.ascontiguousarray(py, np.float64)
+    m = np.ascontiguousarray(mean2d, np.float64)
+    c = np.ascontiguousarray(conic, np.float64)
+    o = np.ascontiguousarray(opacity, np.float64)
+    n = px.size
+    v = np.zeros(n)
+    rel = np.zeros(n)
+    lib.orc_pair_alpha(ctypes.c_int64(n), _p(px), _p(py), _p(m), _p(c), _p(o), _p(v), _p(rel))
+    return v, rel
 
 
 def raster_bruteforce(width: int, height: int, order: np.ndarray, records: dict, settings) -> dict:
@@ -442,12 +490,11 @@ def iteration(scene, settings, loss_scale: float = 1.0, views=None, backward: bo
         res = dict(view=v, proj=proj, rec=rec, bins=bins, fwd=fwd)
         if backward:
             if scene.loss == "l1":
-                g, unsure = loss_grad_l1(fwd["image"], scene.target[v], loss_scale, fwd["err_C"])
+                g, dg = loss_grad_l1(fwd["image"], scene.target[v], loss_scale, fwd["err_C"])
             else:
-                g, unsure = scene.dldc[v].astype(np.float64), None
+                g, dg = scene.dldc[v].astype(np.float64), None
             res["dldc"] = g
-            res["bwd"] = raster_backward(cam.width, cam.height, ranges, vals, rec, settings, g,
-                                         pixel_skip=(fwd["flag"] | unsure) if unsure is not None else fwd["flag"])
+            res["bwd"] = raster_backward(cam.width, cam.height, ranges, vals, rec, settings, g, dg=dg)
         out.append(res)
     return out
 

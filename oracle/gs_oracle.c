@@ -59,6 +59,10 @@ typedef struct {
     int32_t tile;     /* tile side in pixels */
 } orc_params;
 
+/* Guard band of the frustum cull: the projected centre may lie this fraction of the image size
+ * beyond each image edge. */
+#define GUARD 0.15
+
 /* Unit roundoff of IEEE binary32, used only by the decision-margin model. */
 #define EPS32 5.9604644775390625e-08
 
@@ -239,6 +243,17 @@ static int project_one(const double mu[3], const double ls[3], const double q_in
     /* 5. projected centre, pixel (u, v) has its centre at (u + 1/2, v + 1/2) */
     const double mx = cam->fx * tc[0] / tz + cam->cx;
     const double my = cam->fy * tc[1] / tz + cam->cy;
+
+    /* 5b. per-view frustum cull with a guard band: the projected centre must lie inside the
+     *     image widened by 15 % of its size on every side (1.3 times its half extents) */
+    {
+        const double gx = GUARD * cam->width, gy = GUARD * cam->height;
+        const double mgx = 1e-3 + 4e-6 * fabs(mx), mgy = 1e-3 + 4e-6 * fabs(my);
+        if (fabs(mx + gx) < mgx || fabs(mx - cam->width - gx) < mgx || fabs(my + gy) < mgy ||
+            fabs(my - cam->height - gy) < mgy)
+            flag[i] = 1;
+        if (!(mx >= -gx && mx <= cam->width + gx && my >= -gy && my <= cam->height + gy)) return 0;
+    }
 
     /* 7. opacity-aware box: all pixels with o * exp(-q/2) >= alpha_min */
     if (fabs(255.0 * o - 1.0) <= 1e-5) flag[i] = 1;
@@ -755,6 +770,7 @@ void orc_project_backward_errbound(int64_t n, const double* means, const double*
     }
 }
 
+
 /* ------------------------------------------------------------------------------------- */
 /* Rasterization                                                                          */
 /* ------------------------------------------------------------------------------------- */
@@ -767,245 +783,522 @@ typedef struct {
     const double* color;   /* [slots][3] */
 } orc_records;
 
+/*
+ * Float32 error model of the compositing: a tolerance model for comparisons, not part of
+ * the definition.  u = 2^-24 is the rounding of one correctly rounded float32 operation; a
+ * hardware exponential, logarithm or reciprocal is taken as faithful (within one ulp: 2u).
+ *
+ * pair_alpha_error bounds the relative error of v = o exp(-q/2), evaluated in float32 from the
+ * float32 records, for either of two evaluation orders:
+ *   (a) the definition's: q = A dx^2 + 2B dx dy + C dy^2 term by term, exp(-q/2), times o.
+ *       Each term carries four roundings (dx twice, two products) and the two additions one
+ *       rounding of at most qabs = |A| dx^2 + 2|B dx dy| + |C| dy^2 each, so |dq| <= 6u qabs
+ *       and rel(v) <= 3u qabs + 2u (exp) + u (times o).
+ *   (b) base 2: p = a dx^2 + b dx dy + c dy^2 + log2 o with a = -log2(e) A / 2 (and b, c)
+ *       rounded from a rounded constant, the terms and log2 o added by three fused
+ *       multiply-adds, then v = exp2(p).  Each term carries five roundings (the constant, the
+ *       scaled coefficient, dx twice, one product), each fused add one rounding of at most
+ *       log2(e) qabs / 2 + |log2 o|, log2 o one ulp; so |dp| <= 8u log2(e) qabs / 2 +
+ *       5u |log2 o| and rel(v) <= ln(2) |dp| + 2u = 4u qabs + 5u |ln o| + 2u.
+ * The bound u (4 qabs + 5 |ln o| + 3) covers both.  A threshold compared in base-2 logarithm
+ * units carries its own logarithm's ulp: 2u |ln alpha_min| more for the alpha_min test.
+ *
+ * Transmittance: 1 - alpha has relative error alpha rel(v) / (1 - alpha) + u, the product one
+ * rounding more; so the relative error of T grows by alpha rel / (1 - alpha) + 2u per blend.
+ * Colour (per channel): alpha T c has relative error rel + err(T) + 2u, and the running sum one
+ * rounding of |C|; the background adds T bg with err(T) + u and one rounding.
+ *
+ * A decision whose fp64 margin is within these bounds is "flagged": float32 code may take it
+ * the other way.  Flagged decisions are resolved, not skipped: the comparisons evaluate the
+ * pixel under every combination of its flagged decisions taken the other way (up to
+ * KMAX_DEC of them; a pixel with more is "unresolved" and left out).
+ */
+#define KMAX_DEC 3
+
+static double pair_alpha_error(double qabs, double o)
+{
+    return EPS32 * (4.0 * qabs + 5.0 * fabs(log(o)) + 3.0);
+}
+
+/* A decision of a pixel's walk that float32 evaluation could take the other way. */
+enum {
+    DEC_AMIN = 1,  /* alpha against alpha_min at entry j: blended or skipped */
+    DEC_TMIN = 2,  /* T (1 - alpha) against t_min at entry j: blended or stopped */
+    DEC_CLAMP = 3  /* o G against alpha_max at entry j: geometry gradient or none */
+};
+typedef struct {
+    int32_t j, kind;
+} orc_decision;
+
 /* One blended entry of a pixel's walk, kept for the backward pass. */
 typedef struct {
-    int32_t j;        /* position in the tile list */
+    int32_t j;     /* position in the tile list */
     int32_t slot;
-    double alpha;     /* alpha used for blending */
-    double T;         /* transmittance in front of this entry */
-    double G;         /* exp(-q/2) */
-    double dx, dy;    /* pixel centre minus projected centre */
-    int clamped;      /* 1 if o*G exceeded alpha_max */
+    double alpha;  /* alpha used for blending */
+    double T;      /* transmittance in front of this entry */
+    double v;      /* o exp(-q/2), before the clamp */
+    double rel;    /* float32 error bound of v, relative */
+    double dx, dy; /* pixel centre minus projected centre */
+    int clamped;   /* no geometry gradient: o G above alpha_max */
 } orc_blend;
 
-/*
- * Front-to-back compositing of one pixel over its tile list.
- * Writes C[3], returns n_contrib; *T_out = final transmittance.  When log != NULL, the
- * blended entries are appended to log (capacity n).  *flag is set when a decision (alpha
- * against alpha_min, the transmittance cut-off, alpha against alpha_max) lies within the
- * error that float32 evaluation of the same formulas can make, so that float32 code may
- * decide it differently.  Counters: evaluated pairs; n_blend[0] blended pairs and n_blend[1]
- * blended pairs with a clamped alpha.  touch[j] (optional,
- * per list position) marks the evaluated entries whose alpha reaches alpha_min within that
- * error: the entries whose gradient at this pixel a flipped decision can change.
- */
-static int composite_pixel(double px, double py, const int32_t* list, int n, const orc_records* r,
-                           const orc_params* p, double C[3], double* T_out, orc_blend* log,
-                           int* n_log, int* flag, int* flag_clamp, int64_t* n_eval, int64_t* n_blend,
-                           double* err_C, int8_t* touch, double* err_T)
+/* One walk of a pixel over its list: inputs (forced decisions, optional log and touch
+ * buffers) and outputs. */
+typedef struct {
+    const orc_decision* force; /* decisions taken the other way */
+    int n_force;
+    orc_blend* log;            /* optional, capacity n: the blended entries */
+    int8_t* touch;             /* optional, per list position: v reaches alpha_min within the bound */
+    double C[3], T;
+    double eC[3];              /* float32 error bound of C, absolute, per channel */
+    double eT;                 /* float32 error bound of T, relative */
+    int n_contrib, n_log;
+    orc_decision fwd[KMAX_DEC + 1]; /* flagged alpha_min / t_min decisions (first KMAX_DEC + 1) */
+    orc_decision clamp[KMAX_DEC + 1];
+    int n_fwd, n_clamp_flag;   /* counts (may exceed the stored) */
+    int64_t n_eval, n_blend, n_clamped;
+} orc_walk;
+
+static void walk_init(orc_walk* w, const orc_decision* force, int n_force, orc_blend* log, int8_t* touch)
 {
-    double T = 1.0;
-    double errT = 0.0;   /* relative error model of T in float32 */
-    double eC = 0.0;     /* absolute error model of C (any channel) in float32 */
-    int n_contrib = 0;
-    C[0] = C[1] = C[2] = 0.0;
-    if (n_log) *n_log = 0;
+    memset(w, 0, sizeof(*w));
+    w->force = force;
+    w->n_force = n_force;
+    w->log = log;
+    w->touch = touch;
+}
+
+static int is_forced(const orc_walk* w, int32_t j, int32_t kind)
+{
+    for (int k = 0; k < w->n_force; k++)
+        if (w->force[k].j == j && w->force[k].kind == kind) return 1;
+    return 0;
+}
+
+static void note_decision(orc_walk* w, int32_t j, int32_t kind)
+{
+    orc_decision d = {j, kind};
+    if (kind == DEC_CLAMP) {
+        if (w->n_clamp_flag <= KMAX_DEC) w->clamp[w->n_clamp_flag] = d;
+        w->n_clamp_flag++;
+    } else {
+        if (w->n_fwd <= KMAX_DEC) w->fwd[w->n_fwd] = d;
+        w->n_fwd++;
+    }
+}
+
+/*
+ * Front-to-back compositing of one pixel (centre (px, py)) over its tile list:
+ *   alpha = min(alpha_max, o exp(-q/2)), q = A dx^2 + 2B dx dy + C dy^2, d = centre - mean2d;
+ *   entries with alpha < alpha_min are skipped; the walk stops before the blend that would
+ *   take T below t_min (that entry is not blended); C += alpha T c; T *= 1 - alpha;
+ *   finally C += T bg.
+ * Decisions listed in w->force are taken the other way.
+ */
+static void composite_walk(double px, double py, const int32_t* list, int n, const orc_records* r,
+                           const orc_params* p, orc_walk* w)
+{
+    const double u = EPS32;
+    const double thr = 2.0 * u * fabs(log(p->alpha_min));
+    double T = 1.0, errT = 0.0;
     for (int j = 0; j < n; j++) {
         const int s = list[j];
         const double dx = px - r->mean2d[2 * s];
         const double dy = py - r->mean2d[2 * s + 1];
         const double A = r->conic[3 * s], B = r->conic[3 * s + 1], Cc = r->conic[3 * s + 2];
         const double q = A * dx * dx + 2.0 * B * dx * dy + Cc * dy * dy;
-        const double G = exp(-0.5 * q);
-        const double o = r->opacity[s];
-        const double v = o * G;
-        const double alpha = v < p->alpha_max ? v : p->alpha_max;
-        if (n_eval) (*n_eval)++;
-        /* float32 error model: q carries ~8 ulp of its absolute-term sum; the exponential, and
-         * a logarithm of alpha_min / o where the alpha_min test is taken in log space, add up
-         * to a few ulp of the exponent (16 ulp of alpha budgeted) */
         const double qabs = fabs(A) * dx * dx + 2.0 * fabs(B * dx * dy) + fabs(Cc) * dy * dy;
-        const double rel_a = 0.5 * 8.0 * EPS32 * qabs + 16.0 * EPS32;
-        if (fabs(v - p->alpha_min) <= 4.0 * rel_a * p->alpha_min + 1e-12) *flag = 1;
-        if (fabs(v - p->alpha_max) <= 4.0 * rel_a * p->alpha_max + 1e-12) *flag_clamp = 1;
-        if (touch) touch[j] = (int8_t)(v >= p->alpha_min * (1.0 - 4.0 * rel_a) - 1e-12);
-        if (alpha < p->alpha_min) continue;
+        const double o = r->opacity[s];
+        const double v = o * exp(-0.5 * q);
+        const double rel = pair_alpha_error(qabs, o);
+        w->n_eval++;
+        int pass = v >= p->alpha_min;
+        if (fabs(v - p->alpha_min) <= (rel + thr) * p->alpha_min) note_decision(w, j, DEC_AMIN);
+        if (w->touch) w->touch[j] = (int8_t)(v >= p->alpha_min * (1.0 - rel - thr));
+        if (is_forced(w, j, DEC_AMIN)) pass = !pass;
+        if (!pass) continue;
+        const double alpha = v < p->alpha_max ? v : p->alpha_max;
+        int clamped = !(v <= p->alpha_max);
+        if (fabs(v - p->alpha_max) <= rel * p->alpha_max) note_decision(w, j, DEC_CLAMP);
+        if (is_forced(w, j, DEC_CLAMP)) clamped = !clamped;
         const double Tn = T * (1.0 - alpha);
-        const double rel_1ma = (alpha * rel_a + EPS32) / (1.0 - alpha);
-        const double errTn = errT + rel_1ma + EPS32;
-        if (fabs(Tn - p->t_min) <= 4.0 * errTn * p->t_min + 1e-15) *flag = 1;
-        if (Tn < p->t_min) break;
-        for (int ch = 0; ch < 3; ch++) C[ch] += alpha * T * r->color[3 * s + ch];
-        {
-            double cmax = fmax(fabs(r->color[3 * s]), fmax(fabs(r->color[3 * s + 1]), fabs(r->color[3 * s + 2])));
-            eC += alpha * T * cmax * (rel_a + errT + 3.0 * EPS32) + fabs(C[0] + C[1] + C[2]) * EPS32;
+        const double errTn = errT + alpha * rel / (1.0 - alpha) + 2.0 * u;
+        int stop = Tn < p->t_min;
+        if (fabs(Tn - p->t_min) <= errTn * Tn) note_decision(w, j, DEC_TMIN);
+        if (is_forced(w, j, DEC_TMIN)) stop = !stop;
+        if (stop) break;
+        for (int ch = 0; ch < 3; ch++) {
+            const double c = r->color[3 * s + ch];
+            w->C[ch] += alpha * T * c;
+            w->eC[ch] += alpha * T * fabs(c) * (rel + errT + 2.0 * u) + u * fabs(w->C[ch]);
         }
-        if (log) {
-            orc_blend* e = &log[*n_log];
+        if (w->log) {
+            orc_blend* e = &w->log[w->n_log];
             e->j = j;
             e->slot = s;
             e->alpha = alpha;
             e->T = T;
-            e->G = G;
+            e->v = v;
+            e->rel = rel;
             e->dx = dx;
             e->dy = dy;
-            e->clamped = !(v <= p->alpha_max);
-            (*n_log)++;
+            e->clamped = clamped;
+            w->n_log++;
         }
-        if (n_blend) {
-            (*n_blend)++;
-            if (!(v <= p->alpha_max)) n_blend[1]++;
-        }
+        w->n_blend++;
+        w->n_clamped += clamped;
         T = Tn;
         errT = errTn;
-        n_contrib = j + 1;
+        w->n_contrib = j + 1;
     }
-    for (int ch = 0; ch < 3; ch++) C[ch] += T * p->bg[ch];
-    eC += T * fmax(fabs(p->bg[0]), fmax(fabs(p->bg[1]), fabs(p->bg[2]))) * (errT + EPS32);
-    if (err_C) *err_C = eC;
-    if (err_T) *err_T = errT;
-    *T_out = T;
-    return n_contrib;
+    for (int ch = 0; ch < 3; ch++) {
+        w->C[ch] += T * p->bg[ch];
+        w->eC[ch] += T * fabs(p->bg[ch]) * (errT + u) + u * fabs(w->C[ch]);
+    }
+    w->T = T;
+    w->eT = errT;
+}
+
+/* Bit k of mask selects decision k of the pixel's flagged list d[0..k). */
+static int subset(const orc_decision* d, int k, int mask, orc_decision* out)
+{
+    int m = 0;
+    for (int i = 0; i < k; i++)
+        if (mask & (1 << i)) out[m++] = d[i];
+    return m;
 }
 
 /*
  * Forward rasterization of one view.
  * ranges[tile][2] = [start, end) into vals; vals[] = slot of each list entry; tiles are
  * row-major with tiles_x = ceil(W / tile).  Outputs: image[3][H][W], T_final[H][W],
- * n_contrib[H][W], flag[H][W] (decision within float32 reach), err_C[H][W] (float32 error
- * model of the colour, absolute), err_T[H][W] (float32 error model of T_final, relative), counters[3] = {evaluated pairs, blended pairs, blended pairs whose
- * alpha was clamped}.
+ * n_contrib[H][W]; flag[H][W] = the number of flagged alpha_min / t_min decisions of the pixel
+ * (-1: more than KMAX_DEC, unresolved); err_C[3][H][W] (float32 error bound of the colour,
+ * absolute); err_T[H][W] (of T_final, relative); counters[3] = {evaluated pairs, blended pairs,
+ * blended pairs whose alpha was clamped}.  Alternatives: for every pixel with 1..KMAX_DEC
+ * flagged decisions and every non-empty combination of them taken the other way, one entry
+ * (alt_pix = y W + x, alt_C[3], alt_T, alt_nc); *alt_n = their number (entries past alt_cap are
+ * counted, not written).
  */
-void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals,
-                        const double* mean2d, const double* conic, const double* opacity,
-                        const double* color, const orc_params* p, double* image, double* T_final,
-                        int32_t* n_contrib, int8_t* flag, double* err_C, double* err_T, int64_t* counters)
+void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals, const double* mean2d,
+                        const double* conic, const double* opacity, const double* color, const orc_params* p,
+                        double* image, double* T_final, int32_t* n_contrib, int8_t* flag, double* err_C,
+                        double* err_T, int64_t alt_cap, int64_t* alt_n, int64_t* alt_pix, double* alt_C,
+                        double* alt_T, int32_t* alt_nc, int64_t* counters)
 {
     const int tile = p->tile;
     const int tx_n = (W + tile - 1) / tile, ty_n = (H + tile - 1) / tile;
     const orc_records r = {mean2d, conic, opacity, color};
-    int64_t tot_eval = 0, tot_blend = 0, tot_clamp = 0;
+    const int64_t plane = (int64_t)W * H;
+    int64_t tot_eval = 0, tot_blend = 0, tot_clamp = 0, n_alt = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : tot_eval, tot_blend, tot_clamp)
     for (int t = 0; t < tx_n * ty_n; t++) {
         const int tx = t % tx_n, ty = t / tx_n;
         const int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
         for (int y = ty * tile; y < (ty + 1) * tile && y < H; y++)
             for (int x = tx * tile; x < (tx + 1) * tile && x < W; x++) {
-                double C[3], T, eC, eT;
-                int f = 0, fc = 0;
-                int64_t ne = 0, nb[2] = {0, 0};
-                const int nc = composite_pixel(x + 0.5, y + 0.5, vals + start, end - start, &r, p, C, &T,
-                                               NULL, NULL, &f, &fc, &ne, nb, &eC, NULL, &eT);
+                orc_walk w;
+                walk_init(&w, NULL, 0, NULL, NULL);
+                composite_walk(x + 0.5, y + 0.5, vals + start, end - start, &r, p, &w);
                 const int64_t px = (int64_t)y * W + x;
-                for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = C[ch];
-                T_final[px] = T;
-                n_contrib[px] = nc;
-                flag[px] = (int8_t)(f ? 1 : 0);
-                err_C[px] = eC;
-                err_T[px] = eT;
-                tot_eval += ne;
-                tot_blend += nb[0];
-                tot_clamp += nb[1];
+                for (int ch = 0; ch < 3; ch++) {
+                    image[ch * plane + px] = w.C[ch];
+                    err_C[ch * plane + px] = w.eC[ch];
+                }
+                T_final[px] = w.T;
+                n_contrib[px] = w.n_contrib;
+                err_T[px] = w.eT;
+                flag[px] = (int8_t)(w.n_fwd > KMAX_DEC ? -1 : w.n_fwd);
+                tot_eval += w.n_eval;
+                tot_blend += w.n_blend;
+                tot_clamp += w.n_clamped;
+                if (w.n_fwd == 0 || w.n_fwd > KMAX_DEC) continue;
+                for (int mask = 1; mask < (1 << w.n_fwd); mask++) {
+                    orc_decision f[KMAX_DEC];
+                    const int nf = subset(w.fwd, w.n_fwd, mask, f);
+                    orc_walk a;
+                    walk_init(&a, f, nf, NULL, NULL);
+                    composite_walk(x + 0.5, y + 0.5, vals + start, end - start, &r, p, &a);
+                    int64_t k;
+#pragma omp atomic capture
+                    k = n_alt++;
+                    if (k < alt_cap) {
+                        alt_pix[k] = px;
+                        for (int ch = 0; ch < 3; ch++) alt_C[3 * k + ch] = a.C[ch];
+                        alt_T[k] = a.T;
+                        alt_nc[k] = a.n_contrib;
+                    }
+                }
             }
     }
+    *alt_n = n_alt;
     counters[0] = tot_eval;
     counters[1] = tot_blend;
     counters[2] = tot_clamp;
 }
 
+/* ve helpers for the compositing backward: a faithful reciprocal (one ulp) */
+static ve ve_rcp(ve a)
+{
+    ve r = {1.0 / a.v, 0.0};
+    r.e = a.e / (a.v * a.v) + 2.0 * EPS32 * fabs(r.v);
+    return r;
+}
+
 /*
- * Backward rasterization of one view: gradients of L with respect to the per-slot 2D
- * records, given dL/dC (dldc[3][H][W]).  The forward walk of each pixel is recomputed with
- * its blend log, then the log is traversed from the last blended entry to the first:
- *   dL/dc_j     += alpha_j T_j g
- *   dL/dalpha_j  = sum_ch g_ch (T_j (c_j,ch - Bk_ch) - T_final bg_ch / (1 - alpha_j))
- *   Bk          <- alpha_j c_j + (1 - alpha_j) Bk           (colour behind entry j)
- * and, unless alpha was clamped (o G > alpha_max),
- *   dL/do       += G dL/dalpha
- *   dL/dmean2d  += o G dL/dalpha (A dx + B dy, B dx + C dy)   with d = pixel - mean2d
- *   dL/dconic   += o G dL/dalpha (-dx^2/2, -dx dy, -dy^2/2).
- * Outputs (double, accumulated over the view's pixels): d_mean2d[slots][2],
- * d_conic[slots][3], d_opacity[slots], d_color[slots][3]; mag[slots][9] = sum of the
- * absolute values of the same contributions; slot_flag[slots] = 1 when the slot was
- * evaluated at a pixel whose decisions (including the clamp) lie within float32 reach.
- * Output arrays must be zeroed by the caller.
+ * Gradient contributions of one pixel's blended entries (the walk's log), traversed from the
+ * last blended entry to the first, with dL/dC = g:
+ *   dL/dc_j     = alpha_j T_j g
+ *   dL/dalpha_j = T_j (sum_ch g_ch c_j,ch - GB) - T_final / (1 - alpha_j) sum_ch g_ch bg_ch
+ *   GB         <- GB + alpha_j (sum_ch g_ch c_j,ch - GB)      (sum_ch g_ch x colour behind)
+ * and, unless alpha was clamped, with gv = o G dL/dalpha_j:
+ *   dL/do       = gv / o
+ *   dL/dmean2d  = gv (A dx + B dy, B dx + C dy)
+ *   dL/dconic   = gv (-dx^2 / 2, -dx dy, -dy^2 / 2).
+ * Per entry e of the log and component k (mean x, y, conic A, B, C, opacity, colour r, g, b):
+ * val[9 e + k] = the contribution; err[9 e + k] = a first-order running bound on its float32
+ * evaluation error (Higham's running error analysis, the ve arithmetic above): T_j recovered
+ * from T_final by dividing by 1 - alpha (faithful reciprocals), alpha and v = o G within
+ * pair_alpha_error, dx and dy rounded once, the mean gradient formed as A (gv dx) + B (gv dy)
+ * and the opacity gradient as gv / o; mag[9 e + k] = the sum of the absolute values of the
+ * parts that a float32 sum adds (A gv dx and B gv dy for the means).
  */
-void orc_raster_backward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals,
-                         const double* mean2d, const double* conic, const double* opacity,
-                         const double* color, const orc_params* p, const double* dldc,
-                         const int8_t* pixel_skip, double* d_mean2d, double* d_conic,
-                         double* d_opacity, double* d_color, double* mag, int8_t* slot_flag)
+static void pixel_backward(const orc_walk* w, const orc_records* r, const orc_params* p, const double g[3],
+                           double* val, double* err, double* mag)
+{
+    const double u = EPS32;
+    const int bg = p->bg[0] != 0.0 || p->bg[1] != 0.0 || p->bg[2] != 0.0;
+    const ve one = ve_in(1.0);
+    const ve TN = {w->T, w->T * w->eT};
+    const ve gbg = ve_add(ve_add(ve_mul(ve_in(g[0]), ve_in(p->bg[0])), ve_mul(ve_in(g[1]), ve_in(p->bg[1]))),
+                          ve_mul(ve_in(g[2]), ve_in(p->bg[2])));
+    ve GB = ve_in(0.0);
+    double accT = w->eT; /* relative error bound of T recovered at the current entry */
+    for (int e = w->n_log - 1; e >= 0; e--) {
+        const orc_blend* b = &w->log[e];
+        const int s = b->slot;
+        const double* c = &r->color[3 * s];
+        double* vv = val + 9 * e;
+        double* ee = err + 9 * e;
+        double* mm = mag + 9 * e;
+        const ve alpha = {b->alpha, b->rel * b->alpha};
+        const ve oma = ve_sub(one, alpha);
+        accT += b->alpha * b->rel / (1.0 - b->alpha) + 4.0 * u;
+        const ve Tj = {b->T, b->T * accT};
+        const ve wgt = ve_mul(alpha, Tj);
+        for (int ch = 0; ch < 3; ch++) {
+            const ve dc = ve_mul(wgt, ve_in(g[ch]));
+            vv[6 + ch] = dc.v;
+            ee[6 + ch] = dc.e;
+            mm[6 + ch] = fabs(dc.v);
+        }
+        const ve sgc = ve_add(ve_add(ve_mul(ve_in(g[0]), ve_in(c[0])), ve_mul(ve_in(g[1]), ve_in(c[1]))),
+                              ve_mul(ve_in(g[2]), ve_in(c[2])));
+        const ve ge = ve_sub(sgc, GB);
+        ve dLda = ve_mul(Tj, ge);
+        if (bg) dLda = ve_sub(dLda, ve_mul(ve_mul(TN, ve_rcp(oma)), gbg));
+        GB = ve_add(GB, ve_mul(alpha, ge));
+        if (b->clamped) {
+            for (int k = 0; k < 6; k++) vv[k] = ee[k] = mm[k] = 0.0;
+            continue;
+        }
+        const double o = r->opacity[s];
+        const double A = r->conic[3 * s], B = r->conic[3 * s + 1], Cc = r->conic[3 * s + 2];
+        const ve vG = {b->v, b->rel * b->v};
+        const ve gv = ve_mul(vG, dLda);
+        const ve dx = {b->dx, u * fabs(b->dx)}, dy = {b->dy, u * fabs(b->dy)};
+        const ve gx = ve_mul(gv, dx), gy = ve_mul(gv, dy);
+        vv[0] = A * gx.v + B * gy.v;
+        ee[0] = fabs(A) * gx.e + fabs(B) * gy.e;
+        mm[0] = fabs(A * gx.v) + fabs(B * gy.v);
+        vv[1] = B * gx.v + Cc * gy.v;
+        ee[1] = fabs(B) * gx.e + fabs(Cc) * gy.e;
+        mm[1] = fabs(B * gx.v) + fabs(Cc * gy.v);
+        const ve xx = ve_mul(gx, dx), xy = ve_mul(gx, dy), yy = ve_mul(gy, dy);
+        vv[2] = -0.5 * xx.v;
+        ee[2] = 0.5 * xx.e;
+        mm[2] = 0.5 * fabs(xx.v);
+        vv[3] = -xy.v;
+        ee[3] = xy.e;
+        mm[3] = fabs(xy.v);
+        vv[4] = -0.5 * yy.v;
+        ee[4] = 0.5 * yy.e;
+        mm[4] = 0.5 * fabs(yy.v);
+        vv[5] = gv.v / o;
+        ee[5] = gv.e / o;
+        mm[5] = fabs(gv.v / o);
+    }
+}
+
+static void atomic_add9(double* dst, const double* src)
+{
+    for (int k = 0; k < 9; k++) {
+        if (src[k] == 0.0) continue;
+#pragma omp atomic
+        dst[k] += src[k];
+    }
+}
+
+/* Per list position: the contributions of a walk (zero for entries it does not blend). */
+static void by_position(const orc_walk* w, const double* val, double* out, int n_pos)
+{
+    memset(out, 0, sizeof(double) * 9 * (size_t)n_pos);
+    for (int e = 0; e < w->n_log; e++) memcpy(out + 9 * (size_t)w->log[e].j, val + 9 * e, sizeof(double) * 9);
+}
+
+/*
+ * Backward rasterization of one view: gradients of L with respect to the per-slot 2D records,
+ * given dL/dC (dldc[3][H][W]); each pixel's walk is recomputed with its blend log and
+ * pixel_backward gives the contributions.
+ * Outputs (double, accumulated over the view's pixels; zeroed by the caller): d_mean2d[slots][2],
+ * d_conic[slots][3], d_opacity[slots], d_color[slots][3] in the component order above;
+ * mag[slots][9] = summed magnitudes of the parts; err[slots][9] = summed float32 error bounds of
+ * the contributions; widen[slots][9] = for the pixels with flagged decisions, the most that
+ * taking any combination of them the other way changes the slot's contribution, plus, where
+ * dg[3][H][W] (optional) gives an uncertainty of dL/dC, dg_ch times the contribution of a unit
+ * dL/dC_ch; slot_flag[slots] = 1 for the slots a pixel with more than KMAX_DEC flagged
+ * decisions may blend (unresolved, left out of comparisons).
+ * stats[3] = {pixels with flagged decisions, unresolved pixels, alternative walks}.
+ */
+void orc_raster_backward(int32_t W, int32_t H, const int32_t* ranges, const int32_t* vals, const double* mean2d,
+                         const double* conic, const double* opacity, const double* color, const orc_params* p,
+                         const double* dldc, const double* dg, double* d_mean2d, double* d_conic, double* d_opacity,
+                         double* d_color, double* mag, double* err, double* widen, int8_t* slot_flag,
+                         int64_t* stats)
 {
     const int tile = p->tile;
     const int tx_n = (W + tile - 1) / tile, ty_n = (H + tile - 1) / tile;
     const orc_records r = {mean2d, conic, opacity, color};
-    int max_n = 0;
+    const int64_t plane = (int64_t)W * H;
+    int max_n = 1;
     for (int t = 0; t < tx_n * ty_n; t++)
         if (ranges[2 * t + 1] - ranges[2 * t] > max_n) max_n = ranges[2 * t + 1] - ranges[2 * t];
-#pragma omp parallel
+    int64_t n_flagged = 0, n_unresolved = 0, n_alt = 0;
+#pragma omp parallel reduction(+ : n_flagged, n_unresolved, n_alt)
     {
-        orc_blend* log = (orc_blend*)malloc(sizeof(orc_blend) * (size_t)(max_n > 0 ? max_n : 1));
-        int8_t* touch = (int8_t*)calloc((size_t)(max_n > 0 ? max_n : 1), 1);
+        const size_t n9 = 9 * (size_t)max_n;
+        orc_blend* log = (orc_blend*)malloc(sizeof(orc_blend) * (size_t)max_n);
+        orc_blend* alog = (orc_blend*)malloc(sizeof(orc_blend) * (size_t)max_n);
+        int8_t* touch = (int8_t*)calloc((size_t)max_n, 1);
+        double* bv = (double*)malloc(sizeof(double) * n9);
+        double* be = (double*)malloc(sizeof(double) * n9);
+        double* bm = (double*)malloc(sizeof(double) * n9);
+        double* tv = (double*)malloc(sizeof(double) * n9);
+        double* te = (double*)malloc(sizeof(double) * n9);
+        double* tm = (double*)malloc(sizeof(double) * n9);
+        double* base_j = (double*)malloc(sizeof(double) * n9);
+        double* alt_j = (double*)malloc(sizeof(double) * n9);
+        double* wid = (double*)malloc(sizeof(double) * n9);
 #pragma omp for schedule(dynamic, 1)
         for (int t = 0; t < tx_n * ty_n; t++) {
             const int tx = t % tx_n, ty = t / tx_n;
             const int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
             const int32_t* list = vals + start;
+            const int n = end - start;
             for (int y = ty * tile; y < (ty + 1) * tile && y < H; y++)
                 for (int x = tx * tile; x < (tx + 1) * tile && x < W; x++) {
                     const int64_t px = (int64_t)y * W + x;
-                    double C[3], T_fin;
-                    int f = 0, fc = 0, nl = 0;
-                    int64_t n_evaluated = 0;
-                    composite_pixel(x + 0.5, y + 0.5, list, end - start, &r, p, C, &T_fin, log, &nl, &f, &fc,
-                                    &n_evaluated, NULL, NULL, touch, NULL);
-                    if (f || fc || (pixel_skip && pixel_skip[px])) {
-                        /* the slots this pixel blends, or could blend under float32 decisions */
-                        for (int j = 0; j < (int)n_evaluated; j++)
+                    const double g[3] = {dldc[px], dldc[plane + px], dldc[2 * plane + px]};
+                    orc_walk w;
+                    walk_init(&w, NULL, 0, log, touch);
+                    composite_walk(x + 0.5, y + 0.5, list, n, &r, p, &w);
+                    pixel_backward(&w, &r, p, g, bv, be, bm);
+                    for (int e = 0; e < w.n_log; e++) {
+                        const int s = w.log[e].slot;
+                        const double* vv = bv + 9 * e;
+                        const double cv[9] = {vv[0], vv[1], vv[2], vv[3], vv[4], vv[5], vv[6], vv[7], vv[8]};
+                        double* outs[9] = {&d_mean2d[2 * s], &d_mean2d[2 * s + 1], &d_conic[3 * s],
+                                           &d_conic[3 * s + 1], &d_conic[3 * s + 2], &d_opacity[s],
+                                           &d_color[3 * s], &d_color[3 * s + 1], &d_color[3 * s + 2]};
+                        for (int k = 0; k < 9; k++) {
+                            if (cv[k] == 0.0) continue;
+#pragma omp atomic
+                            *outs[k] += cv[k];
+                        }
+                        atomic_add9(mag + 9 * (size_t)s, bm + 9 * e);
+                        atomic_add9(err + 9 * (size_t)s, be + 9 * e);
+                    }
+                    const int nd = w.n_fwd + w.n_clamp_flag;
+                    const int unsure = dg && (dg[px] > 0.0 || dg[plane + px] > 0.0 || dg[2 * plane + px] > 0.0);
+                    if (nd == 0 && !unsure) continue;
+                    n_flagged += nd > 0;
+                    if (nd > KMAX_DEC) {
+                        /* unresolved: the slots it blends, or could blend under float32 decisions */
+                        n_unresolved++;
+                        for (int j = 0; j < (int)w.n_eval; j++)
                             if (touch[j]) {
 #pragma omp atomic write
                                 slot_flag[list[j]] = 1;
                             }
+                        continue;
                     }
-                    double g[3];
-                    for (int ch = 0; ch < 3; ch++) g[ch] = dldc[(int64_t)ch * W * H + px];
-                    double Bk[3] = {0.0, 0.0, 0.0};
-                    for (int e = nl - 1; e >= 0; e--) {
-                        const orc_blend* b = &log[e];
-                        const int s = b->slot;
-                        const double* c = &color[3 * s];
-                        double dL_dalpha = 0.0;
+                    const int n_pos = n; /* alternatives may reach further down the list */
+                    by_position(&w, bv, base_j, n_pos);
+                    memset(wid, 0, sizeof(double) * 9 * (size_t)n_pos);
+                    orc_decision all[2 * KMAX_DEC];
+                    int na = 0;
+                    for (int k = 0; k < w.n_fwd; k++) all[na++] = w.fwd[k];
+                    for (int k = 0; k < w.n_clamp_flag; k++) all[na++] = w.clamp[k];
+                    for (int mask = 1; mask < (1 << na); mask++) {
+                        orc_decision f[2 * KMAX_DEC];
+                        const int nf = subset(all, na, mask, f);
+                        orc_walk a;
+                        walk_init(&a, f, nf, alog, NULL);
+                        composite_walk(x + 0.5, y + 0.5, list, n, &r, p, &a);
+                        pixel_backward(&a, &r, p, g, tv, te, tm);
+                        by_position(&a, tv, alt_j, n_pos);
+                        for (size_t i = 0; i < 9 * (size_t)n_pos; i++) {
+                            const double d = fabs(alt_j[i] - base_j[i]);
+                            if (d > wid[i]) wid[i] = d;
+                        }
+                        n_alt++;
+                    }
+                    if (unsure) {
                         for (int ch = 0; ch < 3; ch++) {
-                            const double dc = b->alpha * b->T * g[ch];
-#pragma omp atomic
-                            d_color[3 * s + ch] += dc;
-#pragma omp atomic
-                            mag[9 * s + 6 + ch] += fabs(dc);
-                            dL_dalpha += g[ch] * (b->T * (c[ch] - Bk[ch]) - T_fin * p->bg[ch] / (1.0 - b->alpha));
-                        }
-                        for (int ch = 0; ch < 3; ch++) Bk[ch] = b->alpha * c[ch] + (1.0 - b->alpha) * Bk[ch];
-                        if (b->clamped) continue;
-                        const double o = opacity[s];
-                        const double A = conic[3 * s], B = conic[3 * s + 1], Cc = conic[3 * s + 2];
-                        const double gh = o * b->G * dL_dalpha; /* dL/dalpha * dalpha/dG * G */
-                        const double v[6] = {
-                            gh * (A * b->dx + B * b->dy),       /* d mean2d x */
-                            gh * (B * b->dx + Cc * b->dy),      /* d mean2d y */
-                            -0.5 * gh * b->dx * b->dx,          /* d A */
-                            -gh * b->dx * b->dy,                /* d B */
-                            -0.5 * gh * b->dy * b->dy,          /* d C */
-                            b->G * dL_dalpha};                  /* d opacity */
-#pragma omp atomic
-                        d_mean2d[2 * s] += v[0];
-#pragma omp atomic
-                        d_mean2d[2 * s + 1] += v[1];
-#pragma omp atomic
-                        d_conic[3 * s] += v[2];
-#pragma omp atomic
-                        d_conic[3 * s + 1] += v[3];
-#pragma omp atomic
-                        d_conic[3 * s + 2] += v[4];
-#pragma omp atomic
-                        d_opacity[s] += v[5];
-                        for (int k = 0; k < 6; k++) {
-#pragma omp atomic
-                            mag[9 * s + k] += fabs(v[k]);
+                            const double dgc = dg[ch * plane + px];
+                            if (!(dgc > 0.0)) continue;
+                            const double unit[3] = {ch == 0, ch == 1, ch == 2};
+                            pixel_backward(&w, &r, p, unit, tv, te, tm);
+                            by_position(&w, tv, alt_j, n_pos);
+                            for (size_t i = 0; i < 9 * (size_t)n_pos; i++) wid[i] += dgc * fabs(alt_j[i]);
                         }
                     }
+                    for (int j = 0; j < n_pos; j++) atomic_add9(widen + 9 * (size_t)list[j], wid + 9 * (size_t)j);
                 }
         }
         free(log);
+        free(alog);
         free(touch);
+        free(bv);
+        free(be);
+        free(bm);
+        free(tv);
+        free(te);
+        free(tm);
+        free(base_j);
+        free(alt_j);
+        free(wid);
+    }
+    stats[0] = n_flagged;
+    stats[1] = n_unresolved;
+    stats[2] = n_alt;
+}
+
+/*
+ * The float32 error bound of v = o exp(-q/2) for n arbitrary (pixel, record) pairs: the same
+ * function the walks use, exposed so that it can be checked against float32 evaluations.
+ * Outputs v[n] and rel[n].
+ */
+void orc_pair_alpha(int64_t n, const double* px, const double* py, const double* mean2d, const double* conic,
+                    const double* opacity, double* v, double* rel)
+{
+    for (int64_t i = 0; i < n; i++) {
+        const double dx = px[i] - mean2d[2 * i], dy = py[i] - mean2d[2 * i + 1];
+        const double A = conic[3 * i], B = conic[3 * i + 1], Cc = conic[3 * i + 2];
+        const double q = A * dx * dx + 2.0 * B * dx * dy + Cc * dy * dy;
+        const double qabs = fabs(A) * dx * dx + 2.0 * fabs(B * dx * dy) + fabs(Cc) * dy * dy;
+        v[i] = opacity[i] * exp(-0.5 * q);
+        rel[i] = pair_alpha_error(qabs, opacity[i]);
     }
 }
 
@@ -1021,14 +1314,13 @@ void orc_raster_bruteforce(int32_t W, int32_t H, const int32_t* order, int32_t n
 #pragma omp parallel for schedule(dynamic, 4)
     for (int y = 0; y < H; y++)
         for (int x = 0; x < W; x++) {
-            double C[3], T;
-            int f = 0, fc = 0;
-            const int nc = composite_pixel(x + 0.5, y + 0.5, order, n, &r, p, C, &T, NULL, NULL, &f, &fc, NULL,
-                                           NULL, NULL, NULL, NULL);
+            orc_walk w;
+            walk_init(&w, NULL, 0, NULL, NULL);
+            composite_walk(x + 0.5, y + 0.5, order, n, &r, p, &w);
             const int64_t px = (int64_t)y * W + x;
-            for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = C[ch];
-            T_final[px] = T;
-            n_contrib[px] = nc; /* position in the global order, not in a tile list */
+            for (int ch = 0; ch < 3; ch++) image[(int64_t)ch * W * H + px] = w.C[ch];
+            T_final[px] = w.T;
+            n_contrib[px] = w.n_contrib; /* position in the global order, not in a tile list */
         }
 }
 

@@ -51,16 +51,17 @@ def run_view_checks(env, scene, settings, mode="separate", region=None, check_pr
         sep = mode == "separate"
         f = parity.compare_forward(oracle, cam, settings, rec, ranges, vals, img[v], T[v] if sep else None,
                                    nc[v] if sep else None, region=region)
-        if mode == "separate":
-            dldc = dl_host[v].astype(np.float64)
-            extra = None
-        else:
-            if scene.loss == "l1":
-                dldc, extra = oracle.loss_grad_l1(f["image"], scene.target[v], 1.0, f["err_C"])
+        if scene.loss == "l1":
+            if mode == "separate":
+                # the L1 kernel's output against the oracle's L1 gradient of the oracle's image
+                dldc, dg = parity.compare_loss_grad_l1(oracle, f["image"], scene.target[v], 1.0, f["err_C"],
+                                                       dl_host[v])
             else:
-                dldc, extra = scene.dldc[v].astype(np.float64), None
-        parity.compare_backward(oracle, cam, settings, rec, ranges, vals, dldc, r.grads_host(v), f, region=region,
-                                extra_skip=extra, slots_rect=gpu["rect"])
+                dldc, dg = oracle.loss_grad_l1(f["image"], scene.target[v], 1.0, f["err_C"])
+        else:
+            dldc, dg = scene.dldc[v].astype(np.float64), None
+        parity.compare_backward(oracle, cam, settings, rec, ranges, vals, dldc, r.grads_host(v), dg=dg, region=region,
+                                slots_rect=gpu["rect"])
     return r
 
 
