@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -360,6 +361,58 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
         rb->capacity = out->capacity;
     }
     return hip_check(launch_project_write(a, s), "gs_project launch");
+}
+
+// gs_project_noalloc: gs_project with its workspace in a file-scope device array instead of a
+// caller's buffer, for callers that cannot allocate.  The array's name is a host-side stand-in
+// in host code; its device address is looked up once per device, with that device current, on
+// the first call there, and only that address is used afterwards.  Every byte of the projection
+// workspace is written before it is read within one call (the count pass writes the block
+// counts, depth ranges and seen flags of every block it reads back), so the contents a previous
+// call left behind need no clearing.  All calls on one device share the array: calls that
+// overlap in time on one device (different host threads or streams) race.
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+gs_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GS_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GS_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GS_ERR_HIP, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GS_OK;
+}
+}  // namespace
+
+size_t gs_project_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+gs_status gs_project_noalloc(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
+                             gs_projected* out, void* stream) {
+    g_last_error.clear();
+    if (!g) return fail(GS_ERR_INVALID_ARGUMENT, "gaussians is null");
+    gs_status st = check_cams(cams, V);
+    if (st != GS_OK) return st;
+    if (g->n < 0 || g->n >= (1 << 28)) return fail(GS_ERR_INVALID_ARGUMENT, "n=%d outside [0, 2^28)", g->n);
+    const size_t need = project_ws_bytes(g->n, V);
+    if (need > kNoAllocScratchBytes)
+        return fail(GS_ERR_CAPACITY, "gs_project_noalloc: n=%d and V=%d need %zu workspace bytes, above the %zu-byte "
+                                     "static scratch (use gs_project with a workspace)",
+                    g->n, V, need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != GS_OK) return st;
+    return gs_project(g, cams, V, p, out, ws, kNoAllocScratchBytes, stream);
 }
 
 gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,

@@ -94,6 +94,9 @@ _SIGS = {
     "gs_project_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "gs_project": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
                                   _P(gs_projected), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "gs_project_noalloc": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
+                                          _P(gs_projected), ctypes.c_void_p]),
+    "gs_project_noalloc_max_bytes": (ctypes.c_size_t, []),
     "gs_bin_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int64]),
     "gs_bin_tiles": (ctypes.c_int, [_P(gs_camera), _P(gs_projected), ctypes.c_int32, _P(gs_render_params),
@@ -242,6 +245,15 @@ def gs_fused_max_cap() -> int:
 def gs_project(g: gs_gaussians, cams, V: int, params: gs_render_params, out: gs_projected, ws, stream=None):
     _check(load().gs_project(ctypes.byref(g), cams, V, ctypes.byref(params), ctypes.byref(out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "gs_project")
+
+
+def gs_project_noalloc(g: gs_gaussians, cams, V: int, params: gs_render_params, out: gs_projected, stream=None):
+    _check(load().gs_project_noalloc(ctypes.byref(g), cams, V, ctypes.byref(params), ctypes.byref(out),
+                                     _stream(stream)), "gs_project_noalloc")
+
+
+def gs_project_noalloc_max_bytes() -> int:
+    return int(load().gs_project_noalloc_max_bytes())
 
 
 def gs_project_bwd(g: gs_gaussians, cams, V: int, params: gs_render_params, proj: gs_projected,

@@ -212,6 +212,24 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, 
                      const gs_render_params* p, gs_projected* out, void* ws, size_t ws_bytes,
                      void* stream);
 
+/*
+ * gs_project without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * projection's scratch (block counts and their scans, per-block depth ranges, the count summary,
+ * one flag byte per Gaussian: about 1.3 bytes per Gaussian at 4 views) lives in a static device
+ * array of gs_project_noalloc_max_bytes() = 8 MiB that the library holds on every device it runs
+ * on until the process ends.  Calls nothing that allocates.  Same arguments, outputs and errors
+ * as gs_project, plus GS_ERR_CAPACITY when gs_project_workspace_size(n, V) exceeds that size
+ * (about 6.5 million Gaussians at 4 views), and GS_ERR_HIP if the array's device address cannot
+ * be found.  All calls on one device share the array: calls that overlap in time on one device
+ * (from several host threads or streams) race and must be serialised by the caller.
+ */
+gs_status gs_project_noalloc(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, int32_t V,
+                             const gs_render_params* p, gs_projected* out, void* stream);
+
+/* The static scratch of gs_project_noalloc, in bytes. */
+size_t gs_project_noalloc_max_bytes(void);
+
 /* Workspace bytes of gs_raster_bwd / gs_raster_fused for an instance capacity: one float32
  * partial-gradient record (9 values) per (Gaussian, tile) instance, then a short list of the
  * slots with more than 256 instances (16 bytes per 256 instances), whose records one workgroup

@@ -280,3 +280,19 @@ def test_product_path_imports_no_oracle():
 def test_readback_create_rejects_null(gs):
     assert gs.load().gs_readback_create(None) == 1
     gs.load().gs_readback_destroy(None)  # ignored
+
+
+def test_project_noalloc_rejects_inputs_beyond_its_scratch(gs):
+    """gs_project_noalloc refuses, on the host, inputs whose projection workspace exceeds its
+    static 8 MiB scratch (nothing is launched, so the fake pointers are never touched)."""
+    lib = gs.load()
+    assert gs.gs_project_noalloc_max_bytes() == 8 << 20
+    c = cams(gs, V=4)
+    p = params(gs)
+    n_fit = 6_000_000
+    assert gs.gs_project_workspace_size(n_fit, 4) <= 8 << 20 < gs.gs_project_workspace_size(8_000_000, 4)
+    g_big = gs.gs_gaussians(8_000_000, FAKE, FAKE, FAKE, FAKE, FAKE)
+    out = projected(gs, capacity=8_000_000)
+    assert lib.gs_project_noalloc(ctypes.byref(g_big), c, 4, ctypes.byref(p), ctypes.byref(out), None) == 2
+    assert b"static scratch" in lib.gs_last_error()
+    assert lib.gs_project_noalloc(None, c, 4, ctypes.byref(p), ctypes.byref(out), None) == 1
