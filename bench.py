@@ -53,16 +53,48 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(scene, settings, views):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(scene, settings, views, single_views):
+    """The oracle as it stands (float64 C with OpenMP, NumPy binning): one full iteration of the
+    given views on all host threads, then of `single_views` on one thread.  Also returns the
+    oracle's pair counts E_tile (list entries walked up to each pixel's stop) and E_box (those
+    whose exact alpha_min box holds the pixel) of the all-thread views."""
     import oracle
     oracle.build(force=False)
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     res = oracle.iteration(scene, settings, loss_scale=1.0, views=views, backward=True)
     dt = time.perf_counter() - t0
     blends = sum(r["fwd"]["n_blended"] for r in res)
-    return dict(value=blends / dt, unit="blends/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{len(views)} of {len(scene.cameras)} views of the same workload, full iteration "
-                       f"(project, bin, forward, L1 gradient, backward) in float64: {blends} blends in {dt:.2f} s")
+    e_tile = sum(r["fwd"]["n_evaluated"] for r in res)
+    e_box = sum(r["fwd"]["n_box"] for r in res)
+    del res
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    res1 = oracle.iteration(scene, settings, loss_scale=1.0, views=single_views, backward=True)
+    dt1 = time.perf_counter() - t1
+    blends1 = sum(r["fwd"]["n_blended"] for r in res1)
+    del res1
+    oracle.set_num_threads(threads)
+    model = cpu_model()
+    out = dict(value=blends / dt, unit="blends/s", cores=threads, kind="oracle",
+               sample=f"{len(views)} of {len(scene.cameras)} views of the same workload, one full iteration "
+                      f"(project, bin, forward, L1 gradient, backward) in float64 on {threads} threads: {blends} "
+                      f"blends in {dt:.2f} s; CPU {model}",
+               cpu_model=model,
+               single_thread=dict(value=blends1 / dt1, unit="blends/s", cores=1,
+                                  sample=f"{len(single_views)} view(s), the same iteration on one thread: {blends1} "
+                                         f"blends in {dt1:.2f} s"))
+    return out, e_tile, e_box
 
 
 def main():
@@ -72,7 +104,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload 1..5 (3 = 1M Gaussians @1080p)")
     ap.add_argument("--cap", type=int, default=0, help="per-tile cap K (0 = off)")
-    ap.add_argument("--cpu-views", type=int, default=4, help="views of the workload the CPU oracle times")
+    ap.add_argument("--cpu-views", type=int, default=4, help="views of the workload the CPU oracle times on all threads "
+                                                             "(the first of them is also timed on one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (3x), the reference kernel that "
@@ -155,7 +188,24 @@ def main():
         raster_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
         return (t1 - t0) * 1000.0 / steps, raster_ms
 
+    def timed_median(mode, min_iters=20, min_s=1.0):
+        """Per-iteration hipEvent times on the library's stream (torch's current stream): the
+        median of at least min_iters iterations spanning at least min_s seconds of GPU time."""
+        times = []
+        while len(times) < min_iters or sum(times) < min_s * 1e3:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+            for a, b in ev:
+                a.record()
+                r.iteration(mode=mode)
+                b.record()
+            torch.cuda.synchronize()
+            times += [a.elapsed_time(b) for a, b in ev]
+        times.sort()
+        return times[len(times) // 2], len(times), sum(times) / 1e3
+
     ms_fused, raster_fused_ms = run("fused", args.steps, args.warmup)
+    med_fused, n_med, s_med = timed_median("fused")
+    log(f"[bench] fused: median {med_fused:.3f} ms/iter over {n_med} event-timed iterations ({s_med:.2f} s)")
     stages_fused = stage_times("fused")
     ms_sep, raster_sep_ms = run("separate", max(3, args.steps // 4), 1)
     stages_sep = stage_times("separate")
@@ -282,6 +332,16 @@ def main():
     # the committed counter summary was taken on the default workload (1M Gaussians, 1080p, 4
     # views, no cap); other workloads have no counter figure
     traffic = measured_traffic() if (args.workload == 3 and args.cap == 0) else None
+    P = r.V * r.W * r.H
+    M_K = int(info.num_instances_capped) if args.cap > 0 else M
+    N_vis = sum(vis)
+    # the minimum HBM bytes of the fused rasterizer: each (capped) list entry's record and slot
+    # (40 B), the target of every pixel (12 B), the 2D gradient of every visible slot (36 B)
+    alg_bytes = 40 * M_K + 12 * P + 36 * N_vis
+    # this design's own: + per entry its instance index inputs (12 B) and its partial gradient
+    # record written by the rasterizer and read back by the per-Gaussian reduction (2 x 36 B)
+    design_bytes = (40 + 12 + 2 * 36) * M_K + 12 * P + 36 * N_vis
+    hbm_achieved = alg_bytes / (raster_fused_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": B / (ms_fused * 1e-3),
@@ -290,6 +350,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_fused,
+        "ms_per_iter_median": med_fused,
+        "median_iterations": n_med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -311,10 +373,12 @@ def main():
             "traffic": traffic,
             "algorithmic_flops": flops,
             "launch_ms": raster_fused_ms,
-            "hbm_frac_algorithmic": None,
-            "algorithmic_bytes": None,
+            "hbm": {"algorithmic_bytes": alg_bytes, "achieved": hbm_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": hbm_achieved / HBM_PEAK_GBS, "design_bytes": design_bytes,
+                    "target_frac": 0.5, "met": hbm_achieved / HBM_PEAK_GBS >= 0.5},
         },
-        "counts": {"visible": vis, "instances": M, "evaluated_pairs": E_eval, "alpha_pairs": E_alpha, "blends": B},
+        "counts": {"visible": vis, "instances": M, "instances_capped": M_K, "evaluated_pairs": E_eval,
+                   "alpha_pairs": E_alpha, "blends": B, "e_box": None, "e_tile": None},
         "stages_ms": {"fused": stages_fused, "separate": stages_sep},
         "separate_path": {"ms_per_step": ms_sep, "blends_per_s": B / (ms_sep * 1e-3), "raster_ms": raster_sep_ms},
         "cpu_baseline": None,
@@ -355,17 +419,12 @@ def main():
             "full_iteration_ms": full_ms,
         },
     }
-    # algorithmic HBM bytes of the call, per instance: its record and slot id (40 B) and the inputs
-    # of its emission index (12 B) read once, its 9-float partial record written and read back by
-    # the reduction (2 x 36 B); per visible Gaussian the 9 gradient floats written (36 B); per pixel
-    # the target image (12 B).
-    alg_bytes = (40 + 12 + 2 * 36) * M + 36 * sum(vis) + 12 * r.V * r.W * r.H
-    out["roofline"]["algorithmic_bytes"] = alg_bytes
-    out["roofline"]["hbm_frac_algorithmic"] = alg_bytes / (raster_fused_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
     if not args.no_cpu_baseline:
         views = list(range(min(args.cpu_views, r.V)))
-        out["cpu_baseline"] = cpu_baseline(scene, settings, views)
-        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+        out["cpu_baseline"], e_tile, e_box = cpu_baseline(scene, settings, views, views[:1])
+        if len(views) == r.V:
+            out["counts"]["e_tile"], out["counts"]["e_box"] = e_tile, e_box
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}; E_tile {e_tile}, E_box {e_box}")
     print(json.dumps(out), flush=True)
 
 

@@ -334,18 +334,20 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     a.n_tiles = out->n_tiles;
     a.inst_base = out->inst_base;
     a.raster_rec = reinterpret_cast<float4*>(out->raster_rec);
-    const int32_t nb = (g->n + 255) / 256 > 0 ? (g->n + 255) / 256 : 1;
+    const int32_t nw = project_count_waves(g->n);
     Carver c(ws);
-    a.block_counts = c.take<int32_t>((size_t)nb * 2 * V);
-    a.block_offsets = c.take<int32_t>((size_t)nb * 2 * V);
+    a.block_counts = c.take<int32_t>((size_t)nw * 2 * V);
+    a.block_offsets = c.take<int32_t>((size_t)nw * 2 * V);
     a.row_totals = c.take<int32_t>((size_t)2 * V);
-    a.scan_partials = c.take<int32_t>(scan_partials_bytes(nb, 2 * V) / sizeof(int32_t));
+    a.scan_partials = c.take<int32_t>(scan_partials_bytes(nw, 2 * V) / sizeof(int32_t));
     gs_readback* rb = out->readback;
-    uint2* block_depth = c.take<uint2>((size_t)nb);
+    uint2* block_depth = c.take<uint2>((size_t)nw);
     CountSummary* summary = c.take<CountSummary>(1);
     a.block_depth = rb ? block_depth : nullptr;
     a.summary = rb ? summary : nullptr;
-    a.seen = c.take<uint8_t>((size_t)nb * 256);
+    a.seen = c.take<uint8_t>((size_t)nw * 64);
+    a.inst_partials = c.take<int64_t>((size_t)V * project_partials());
+    a.depth_partials = c.take<uint2>((size_t)project_partials());
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (rb) rb->filled = false;
     gs_status st2 = hip_check(launch_project_count(a, s), "gs_project launch");
@@ -372,7 +374,7 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
 // call left behind need no clearing.  All calls on one device share the array: calls that
 // overlap in time on one device (different host threads or streams) race.
 namespace {
-constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;

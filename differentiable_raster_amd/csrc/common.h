@@ -88,14 +88,17 @@ struct ProjectArgs {
     int32_t* inst_base;
     float4* raster_rec;      // [V][capacity][4]
     // workspace
-    int32_t* block_counts;   // [2V][nb]: visible slots per block (rows 0..V-1), then instances per block
-    int32_t* block_offsets;  // [2V][nb]: exclusive scans of the rows of block_counts
+    int32_t* block_counts;   // [2V][nw]: visible slots per wavefront of 64 Gaussians (rows 0..V-1), then
+                             // instances per wavefront
+    int32_t* block_offsets;  // [2V][nw]: exclusive scans of the rows of block_counts
     int32_t* row_totals;     // [2V]: visible slots per view, then instances per view
     int32_t* scan_partials;  // scan workspace
-    uint2* block_depth;      // [nb] (smallest, complement of largest) visible depth bits per block;
+    uint2* block_depth;      // [nw] (smallest, complement of largest) visible depth bits per wavefront;
                              // NULL: not computed
     CountSummary* summary;   // device copy of the counts (written when block_depth is set)
-    uint8_t* seen;           // [nb * 256] 1 where some view sees the Gaussian (counting pass)
+    uint8_t* seen;           // [nw * 64] 1 where some view sees the Gaussian (counting pass)
+    int64_t* inst_partials;  // [V][project_partials()] partial instance sums
+    uint2* depth_partials;   // [project_partials()] partial depth ranges
 };
 // The counting pass, the block scans and (with block_depth) the count summary: afterwards
 // vis/inst counts are final and the summary may be copied out while the writing pass runs.
@@ -103,6 +106,8 @@ hipError_t launch_project_count(const ProjectArgs& a, hipStream_t s);
 // The writing pass (records of the visible slots).
 hipError_t launch_project_write(const ProjectArgs& a, hipStream_t s);
 size_t project_ws_bytes(int32_t n, int32_t V);
+int32_t project_count_waves(int32_t n);
+int32_t project_partials();
 
 // Backward of the projection: per-slot 2D gradients of V views -> per-Gaussian parameter
 // gradients (summed over views), one thread per Gaussian.

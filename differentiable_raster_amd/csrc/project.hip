@@ -2,20 +2,22 @@
 //
 // Two passes over the Gaussians, one thread per Gaussian, all V views per thread so the
 // geometry (44 B per Gaussian) is read once per pass:
-//   pass 1 counts the visible Gaussians of each 256-Gaussian block and view, and adds the
-//          block's tile-instance count into the view's total;
-//   an exclusive scan of the block counts gives each block its first slot per view;
+//   pass 1 counts the visible Gaussians of each wavefront (64 consecutive Gaussians) and view,
+//          and the wavefront's tile instances per view: wave ballots and reductions only, no
+//          workgroup barrier;
+//   an exclusive scan of the wavefront counts gives each wavefront its first slot per view;
 //   pass 2 recomputes the same decisions (same code, same rounding) for the Gaussians that
 //          pass 1 found in some view and writes the records of visible Gaussians at
-//          slot = block offset + rank within the block, so slots follow ascending Gaussian
-//          index, together with each slot's instance base (the same scan over the blocks'
-//          tile-instance counts, plus a wave scan inside the block) and the packed 64-byte
-//          record the rasterizers stage with one line per list entry.
-// Spherical-harmonic coefficients (192 B per Gaussian at degree 3) are read only for Gaussians
-// that some view sees (in a large scene most are outside every view): the counting pass checks
-// at the first such view that they are bounded (which makes every colour finite) and flags the
-// Gaussian, and the writing pass keeps a flagged Gaussian's coefficients in registers for all
-// views.
+//          slot = wavefront offset + rank within the wavefront, so slots follow ascending
+//          Gaussian index, together with each slot's instance base (the same scan over the
+//          wavefronts' tile-instance counts, plus a wave scan) and the packed 64-byte record the
+//          rasterizers stage with one line per list entry.  No barrier either.
+// The mean alone decides the near plane and the frustum guard of every view, so pass 1 reads
+// the other 32 B of geometry only for Gaussians some view keeps.  Spherical-harmonic
+// coefficients (192 B per Gaussian at degree 3) are read only for Gaussians that some view sees
+// (in a large scene most are outside every view): the counting pass checks at the first such
+// view that they are bounded (which makes every colour finite) and flags the Gaussian, and the
+// writing pass keeps a flagged Gaussian's coefficients in registers for all views.
 #include "common.h"
 #include "gauss.h"
 
@@ -23,6 +25,9 @@ namespace gsmi {
 namespace {
 
 constexpr int kBlock = 256;
+
+// Wavefronts of 64 consecutive Gaussians: the unit of the counts and of the slot offsets.
+__host__ __device__ __forceinline__ int32_t project_waves(int32_t n) { return n > 0 ? (n + 63) / 64 : 1; }
 
 struct Geo {
     float mx, my, mz;   // world mean
@@ -42,12 +47,13 @@ struct Rec {
 
 __device__ __forceinline__ bool finitef(float x) { return isfinite(x); }
 
-__device__ Geo load_geo(const ProjectArgs& a, int i) {
+// The rest of a Gaussian's geometry (activations, world covariance) for a mean already read.
+__device__ Geo load_geo_rest(const ProjectArgs& a, int i, float mx, float my, float mz) {
     const int n = a.n;
     Geo g;
-    g.mx = a.means[i];
-    g.my = a.means[n + i];
-    g.mz = a.means[2 * n + i];
+    g.mx = mx;
+    g.my = my;
+    g.mz = mz;
     const GaussFrame f = gauss_frame(a.log_scales[i], a.log_scales[n + i], a.log_scales[2 * n + i], a.quats[i],
                                      a.quats[n + i], a.quats[2 * n + i], a.quats[3 * n + i], a.logits[i],
                                      finitef(g.mx) && finitef(g.my) && finitef(g.mz));
@@ -56,6 +62,52 @@ __device__ Geo load_geo(const ProjectArgs& a, int i) {
 #pragma unroll
     for (int k = 0; k < 6; k++) g.S[k] = f.S[k];
     return g;
+}
+
+__device__ Geo load_geo(const ProjectArgs& a, int i) {
+    return load_geo_rest(a, i, a.means[i], a.means[a.n + i], a.means[2 * a.n + i]);
+}
+
+// The camera-space centre of a mean and its projection, with the decisions taken from the mean
+// alone: the near plane, and the per-view frustum cull with a guard band (the projected centre
+// must lie inside the image widened by 15 % of its size on every side).  Beyond the guard lie
+// the near-plane splats far off axis, whose 2D covariance reaches 1e12 px^2: at image pixels
+// their quadratic form cancels terms of 1e8 and more, which float32 (records or arithmetic)
+// cannot resolve.  The projection and the counting pass's early test both call this, so they
+// decide identically.
+struct Centre {
+    float tx, ty, tz, iz, mx, my;
+};
+
+// A conservative form of view_centre's tests without the division: false only when the
+// centre lies behind the near plane or clearly (by 1e-3 of the compared magnitudes, far above
+// the float32 rounding of either form) outside the guard band, so that view_centre would fail
+// too.  With tz > 0 the guard test  -g <= fx tx / tz + cx <= W + g  reads
+// (-g - cx) tz <= fx tx <= (W + g - cx) tz, and likewise in y.
+__device__ __forceinline__ bool view_centre_maybe(const CamDev& c, float znear, float wx, float wy, float wz) {
+    const float tx = fmaf(c.R[0], wx, fmaf(c.R[1], wy, fmaf(c.R[2], wz, c.t[0])));
+    const float ty = fmaf(c.R[3], wx, fmaf(c.R[4], wy, fmaf(c.R[5], wz, c.t[1])));
+    const float tz = fmaf(c.R[6], wx, fmaf(c.R[7], wy, fmaf(c.R[8], wz, c.t[2])));
+    if (!(tz > znear)) return false;
+    const float gx = kGuard * (float)c.width, gy = kGuard * (float)c.height;
+    const float u = c.fx * tx, v = c.fy * ty;
+    const float ulo = (-gx - c.cx) * tz, uhi = ((float)c.width + gx - c.cx) * tz;
+    const float vlo = (-gy - c.cy) * tz, vhi = ((float)c.height + gy - c.cy) * tz;
+    const float su = 1e-3f * (fabsf(u) + fabsf(ulo) + fabsf(uhi)), sv = 1e-3f * (fabsf(v) + fabsf(vlo) + fabsf(vhi));
+    // a NaN anywhere leaves the comparisons false: kept, and the exact test decides
+    return !(u < ulo - su || u > uhi + su || v < vlo - sv || v > vhi + sv);
+}
+
+__device__ __forceinline__ bool view_centre(const CamDev& c, float znear, float wx, float wy, float wz, Centre& ce) {
+    ce.tx = fmaf(c.R[0], wx, fmaf(c.R[1], wy, fmaf(c.R[2], wz, c.t[0])));
+    ce.ty = fmaf(c.R[3], wx, fmaf(c.R[4], wy, fmaf(c.R[5], wz, c.t[1])));
+    ce.tz = fmaf(c.R[6], wx, fmaf(c.R[7], wy, fmaf(c.R[8], wz, c.t[2])));
+    if (!(ce.tz > znear)) return false;
+    ce.iz = 1.0f / ce.tz;
+    ce.mx = fmaf(c.fx * ce.tx, ce.iz, c.cx);
+    ce.my = fmaf(c.fy * ce.ty, ce.iz, c.cy);
+    const float gx = kGuard * (float)c.width, gy = kGuard * (float)c.height;
+    return ce.mx >= -gx && ce.mx <= (float)c.width + gx && ce.my >= -gy && ce.my <= (float)c.height + gy;
 }
 
 // True when every SH coefficient of Gaussian i is finite and at most 1e30 in magnitude.  Every
@@ -77,12 +129,10 @@ __device__ __forceinline__ bool sh_bounded(const ProjectArgs& a, int i) {
 __device__ bool project_geom(const ProjectArgs& a, const Geo& g, const CamDev& c, Rec& r, float3& dir) {
     if (!g.ok) return false;
     const ParamsDev& p = a.p;
-    const float tx = fmaf(c.R[0], g.mx, fmaf(c.R[1], g.my, fmaf(c.R[2], g.mz, c.t[0])));
-    const float ty = fmaf(c.R[3], g.mx, fmaf(c.R[4], g.my, fmaf(c.R[5], g.mz, c.t[1])));
-    const float tz = fmaf(c.R[6], g.mx, fmaf(c.R[7], g.my, fmaf(c.R[8], g.mz, c.t[2])));
-    if (!(tz > p.znear)) return false;
+    Centre ce;
+    if (!view_centre(c, p.znear, g.mx, g.my, g.mz, ce)) return false;
+    const float tx = ce.tx, ty = ce.ty, tz = ce.tz, iz = ce.iz;
     // EWA: T = J W with J the Jacobian of the perspective map at the centre
-    const float iz = 1.0f / tz;
     const float j00 = c.fx * iz, j02 = -c.fx * tx * iz * iz;
     const float j11 = c.fy * iz, j12 = -c.fy * ty * iz * iz;
     const float t00 = fmaf(j00, c.R[0], j02 * c.R[6]);
@@ -105,14 +155,7 @@ __device__ bool project_geom(const ProjectArgs& a, const Geo& g, const CamDev& c
     const float det = ca * cc - cb * cb;
     if (!(det > 0.0f) || !finitef(det)) return false;
     const float idet = 1.0f / det;
-    const float mx = fmaf(c.fx * tx, iz, c.cx);
-    const float my = fmaf(c.fy * ty, iz, c.cy);
-    // per-view frustum cull with a guard band: the projected centre must lie inside the image
-    // widened by 15 % of its size on every side.  Beyond it lie the near-plane splats far off
-    // axis, whose 2D covariance reaches 1e12 px^2: at image pixels their quadratic form cancels
-    // terms of 1e8 and more, which float32 (records or arithmetic) cannot resolve.
-    const float gx = kGuard * (float)c.width, gy = kGuard * (float)c.height;
-    if (!(mx >= -gx && mx <= (float)c.width + gx && my >= -gy && my <= (float)c.height + gy)) return false;
+    const float mx = ce.mx, my = ce.my;
     // opacity-aware box: o exp(-q/2) >= alpha_min  <=>  q <= 2 ln(o / alpha_min)
     if (!(g.o > p.alpha_min)) return false;
     const float Q = 2.0f * logf(g.o / p.alpha_min);
@@ -148,21 +191,45 @@ __device__ __noinline__ bool colour_finite(const ProjectArgs& a, int i, float3 d
     return finitef(col.x) && finitef(col.y) && finitef(col.z);
 }
 
+__device__ __forceinline__ int wave_sum_i(int x) {
+    for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 template <int DEG>
-// at most 80 registers: 6 waves per SIMD to hide the latency of the coefficient reads (95 otherwise)
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void project_count_kernel(ProjectArgs a) {
+__global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
     constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
-    __shared__ int s_cnt[kBlock / kWave];
-    __shared__ int s_inst[kBlock / kWave];
     const int i = blockIdx.x * kBlock + threadIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t nw = project_waves(a.n);
+    const int32_t gw = (int32_t)(i / kWave);  // this wavefront's index over all Gaussians
+    if (gw >= nw) return;                     // whole wavefronts past the last Gaussian
+    // the mean alone decides the near plane and the frustum guard of every view; the remaining
+    // 32 bytes of geometry are read only for Gaussians whose centre some view keeps (in a large
+    // scene most Gaussians lie outside every view)
+    uint32_t vmask = 0u;
+    float wx = 0.0f, wy = 0.0f, wz = 0.0f;
+    if (i < a.n) {
+        wx = a.means[i];
+        wy = a.means[a.n + i];
+        wz = a.means[2 * a.n + i];
+        for (int v = 0; v < a.V; v++)
+            if (view_centre_maybe(a.cams.c[v], a.p.znear, wx, wy, wz)) vmask |= 1u << v;
+    }
+    if (__ballot(vmask != 0u) == 0ull) {
+        // no view keeps any centre of this wavefront (most of a large scene): zero counts, no
+        // seen flags, an empty depth range
+        if (lane < 2 * a.V) a.block_counts[(size_t)lane * nw + gw] = 0;
+        if (i < a.n) a.seen[i] = 0;
+        if (a.block_depth && lane == 0) a.block_depth[gw] = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+        return;
+    }
     Geo g;
     g.ok = false;
-    if (i < a.n) g = load_geo(a, i);
+    if (vmask) g = load_geo_rest(a, i, wx, wy, wz);
     // the coefficients are checked at the first view that sees the Gaussian: most Gaussians of a
     // large scene are outside every view and their 192 bytes are never read
     bool bounded = true, checked = false, seen = false;
-    const int nb = gridDim.x;
     // visible depth range of this thread over all views, as float32 bit patterns (depths are
     // above znear > 0, so the patterns order like the values)
     uint32_t dlo = 0xFFFFFFFFu, dhi = 0u;
@@ -170,7 +237,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         Rec r;
         r.ntiles = 0;
         float3 dir;
-        bool vis = (i < a.n) && project_geom(a, g, a.cams.c[v], r, dir);
+        bool vis = ((vmask >> v) & 1u) && project_geom(a, g, a.cams.c[v], r, dir);
         if (vis && !checked) {
             bounded = sh_bounded<3 * (NY + 1)>(a, i);
             checked = true;
@@ -183,23 +250,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
             dhi = max(dhi, __float_as_uint(r.depth));
         }
         const unsigned long long m = __ballot(vis);
-        int nt = vis ? r.ntiles : 0;
-        for (int o = kWave / 2; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
+        const int nt = wave_sum_i(vis ? r.ntiles : 0);
         if (lane == 0) {
-            s_cnt[w] = __popcll(m);
-            s_inst[w] = nt;
+            a.block_counts[(size_t)v * nw + gw] = __popcll(m);
+            a.block_counts[(size_t)(a.V + v) * nw + gw] = nt;
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int c = 0, t = 0;
-            for (int k = 0; k < kBlock / kWave; k++) {
-                c += s_cnt[k];
-                t += s_inst[k];
-            }
-            a.block_counts[v * nb + blockIdx.x] = c;
-            a.block_counts[(a.V + v) * nb + blockIdx.x] = t;
-        }
-        __syncthreads();
     }
     if (i < a.n) a.seen[i] = seen ? 1 : 0;
     if (a.block_depth) {
@@ -208,19 +263,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
             dlo = min(dlo, (uint32_t)__shfl_xor((int)dlo, o));
             nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o));
         }
-        // the count buffers of the view loop are free again after its last barrier
-        if (lane == 0) {
-            s_cnt[w] = (int)dlo;
-            s_inst[w] = (int)nhi;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int k = 1; k < kBlock / kWave; k++) {
-                dlo = min(dlo, (uint32_t)s_cnt[k]);
-                nhi = min(nhi, (uint32_t)s_inst[k]);
-            }
-            a.block_depth[blockIdx.x] = make_uint2(dlo, nhi);
-        }
+        if (lane == 0) a.block_depth[gw] = make_uint2(dlo, nhi);
     }
 }
 
@@ -228,15 +271,16 @@ template <int DEG>
 __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
     constexpr int NC = 3 * (NY + 1);
-    __shared__ int s_cnt[kBlock / kWave];
-    __shared__ int s_inst[kBlock / kWave];
     const int i = blockIdx.x * kBlock + threadIdx.x;
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t nw = project_waves(a.n);
+    const int32_t gw = (int32_t)(i / kWave);
     if (blockIdx.x == 0 && threadIdx.x < a.V) a.vis_count[threadIdx.x] = a.row_totals[threadIdx.x];
-    // a block whose Gaussians no view sees (most blocks of a large scene) writes nothing
+    if (gw >= nw) return;
+    // a wavefront whose Gaussians no view sees (most of a large scene) writes nothing
     {
         bool any = false;
-        for (int v = 0; v < a.V; v++) any |= a.block_counts[v * gridDim.x + blockIdx.x] > 0;
+        for (int v = 0; v < a.V; v++) any |= a.block_counts[(size_t)v * nw + gw] > 0;
         if (!any) return;
     }
     Geo g;
@@ -254,7 +298,6 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
             for (int k = 0; k < NC; k++) coef[k] = a.sh[(size_t)k * a.n + i];
         }
     }
-    const int nb = gridDim.x;
     int view_inst = 0;  // instances of the earlier views
     for (int v = 0; v < a.V; v++) {
         Rec r;
@@ -283,19 +326,9 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
             const int y = __shfl_up(inc, o);
             if (lane >= o) inc += y;
         }
-        if (lane == 0) s_cnt[w] = __popcll(m);
-        if (lane == kWave - 1) s_inst[w] = inc;
-        __syncthreads();
-        int off = a.block_offsets[v * nb + blockIdx.x];
-        int ioff = view_inst + a.block_offsets[(a.V + v) * nb + blockIdx.x];
-        for (int k = 0; k < w; k++) {
-            off += s_cnt[k];
-            ioff += s_inst[k];
-        }
-        __syncthreads();
         if (vis) {
-            const int slot = off + __popcll(m & ((1ull << lane) - 1ull));
-            const int base = ioff + inc - nt;
+            const int slot = a.block_offsets[(size_t)v * nw + gw] + __popcll(m & ((1ull << lane) - 1ull));
+            const int base = view_inst + a.block_offsets[(size_t)(a.V + v) * nw + gw] + inc - nt;
             const size_t idx = (size_t)v * a.capacity + slot;
             a.vis_ids[idx] = i;
             a.mean2d[idx] = r.xy;
@@ -318,76 +351,93 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     }
 }
 
-// inst_count[v] = the 64-bit sum of row V + v of the block counts (one block per view; 64 bits,
-// so that a total past 2^31 is reported as such and refused by the binning call).
-// 1024 threads, four independent loads per step: a large scene has ~10^5 blocks per row, and a
-// loop of dependent loads over them would take hundreds of microseconds.
-constexpr int kSumBlock = 1024;
+// The per-view instance totals in 64 bits (so that a total past 2^31 is reported as such and
+// refused by the binning call) and the visible depth range, in two steps: kParts workgroups per
+// row each reduce a strided share of the wavefront counts (rows V..2V-1) or, in row V, of the
+// wavefront depth ranges, then one workgroup adds the partials up.  Every workgroup keeps many
+// independent loads in flight: a large scene has ~10^6 wavefronts per row.
+constexpr int kParts = 128;
+constexpr int kSumBlock = 256;
 
-__global__ __launch_bounds__(kSumBlock) void inst_total_kernel(const int32_t* block_counts, int32_t V, int32_t nb,
-                                                               int64_t* inst_count) {
-    __shared__ long long s_part[kSumBlock / kWave];
-    const int v = blockIdx.x;
-    const int32_t* row = block_counts + (size_t)(V + v) * nb;
-    long long t = 0;
-    for (int32_t b0 = 0; b0 < nb; b0 += 4 * kSumBlock) {
-        int x[4];
+__global__ __launch_bounds__(kSumBlock) void count_partials_kernel(const int32_t* block_counts, int32_t V, int32_t nw,
+                                                                   const uint2* block_depth, int64_t* inst_partials,
+                                                                   uint2* depth_partials) {
+    __shared__ long long s_sum[kSumBlock / kWave];
+    __shared__ uint32_t s_lo[kSumBlock / kWave], s_nhi[kSumBlock / kWave];
+    const int v = blockIdx.y;
+    const int32_t stride = kParts * kSumBlock;
+    const int32_t first = blockIdx.x * kSumBlock + threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    if (v < V) {
+        const int32_t* row = block_counts + (size_t)(V + v) * nw;
+        long long t = 0;
+        for (int32_t k = first; k < nw; k += 4 * stride) {
+            int x[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int32_t b = b0 + u * kSumBlock + (int)threadIdx.x;
-            x[u] = b < nb ? row[b] : 0;
+            for (int u = 0; u < 4; u++) x[u] = k + u * stride < nw ? row[k + u * stride] : 0;
+#pragma unroll
+            for (int u = 0; u < 4; u++) t += x[u];
         }
+        for (int o = kWave / 2; o > 0; o >>= 1) t += __shfl_xor(t, o);
+        if (lane == 0) s_sum[w] = t;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            long long sum = 0;
+            for (int k = 0; k < kSumBlock / kWave; k++) sum += s_sum[k];
+            inst_partials[(size_t)v * kParts + blockIdx.x] = sum;
+        }
+    } else if (block_depth) {
+        uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;
+        for (int32_t k = first; k < nw; k += 4 * stride) {
+            uint2 x[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) t += x[u];
-    }
-    for (int o = kWave / 2; o > 0; o >>= 1) t += __shfl_xor(t, o);
-    if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = t;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        long long sum = 0;
-        for (int k = 0; k < kSumBlock / kWave; k++) sum += s_part[k];
-        inst_count[v] = sum;
+            for (int u = 0; u < 4; u++)
+                x[u] = k + u * stride < nw ? block_depth[k + u * stride] : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                lo = min(lo, x[u].x);
+                nhi = min(nhi, x[u].y);
+            }
+        }
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+            nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o));
+        }
+        if (lane == 0) {
+            s_lo[w] = lo;
+            s_nhi[w] = nhi;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int k = 1; k < kSumBlock / kWave; k++) {
+                lo = min(lo, s_lo[k]);
+                nhi = min(nhi, s_nhi[k]);
+            }
+            depth_partials[blockIdx.x] = make_uint2(lo, nhi);
+        }
     }
 }
 
-// The count summary (one block): visible slots per view from the block scans, instances per
-// view from inst_total_kernel, and the visible depth range from the per-block ranges.
-__global__ __launch_bounds__(kSumBlock) void count_summary_kernel(const int32_t* row_totals,
-                                                                  const int64_t* inst_count, int32_t V,
-                                                                  const uint2* block_depth, int32_t nb,
-                                                                  CountSummary* out) {
-    __shared__ uint32_t s_lo[kSumBlock / kWave], s_nhi[kSumBlock / kWave];
+// One workgroup: inst_count[v] from the partials; with `out`, the count summary (visible slots
+// per view from the scans, instances per view, the visible depth range).
+__global__ __launch_bounds__(kSumBlock) void count_summary_kernel(const int32_t* row_totals, const int64_t* inst_partials,
+                                                                  const uint2* depth_partials, int32_t V,
+                                                                  int64_t* inst_count, CountSummary* out) {
     if ((int)threadIdx.x < V) {
-        out->vis[threadIdx.x] = row_totals[threadIdx.x];
-        out->inst[threadIdx.x] = inst_count[threadIdx.x];
-    }
-    uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;
-    for (int32_t k0 = 0; k0 < nb; k0 += 4 * kSumBlock) {
-        uint2 x[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int32_t k = k0 + u * kSumBlock + (int)threadIdx.x;
-            x[u] = k < nb ? block_depth[k] : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            lo = min(lo, x[u].x);
-            nhi = min(nhi, x[u].y);
+        const int v = threadIdx.x;
+        long long sum = 0;
+        for (int k = 0; k < kParts; k++) sum += inst_partials[(size_t)v * kParts + k];
+        inst_count[v] = sum;
+        if (out) {
+            out->vis[v] = row_totals[v];
+            out->inst[v] = sum;
         }
     }
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-        nhi = min(nhi, (uint32_t)__shfl_xor((int)nhi, o));
-    }
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-        s_lo[threadIdx.x / kWave] = lo;
-        s_nhi[threadIdx.x / kWave] = nhi;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int k = 1; k < kSumBlock / kWave; k++) {
-            lo = min(lo, s_lo[k]);
-            nhi = min(nhi, s_nhi[k]);
+    if (out && threadIdx.x == kSumBlock - 1) {
+        uint32_t lo = 0xFFFFFFFFu, nhi = 0xFFFFFFFFu;
+        for (int k = 0; k < kParts; k++) {
+            lo = min(lo, depth_partials[k].x);
+            nhi = min(nhi, depth_partials[k].y);
         }
         out->bits[0] = lo;
         out->bits[1] = nhi;
@@ -400,28 +450,36 @@ static int32_t project_blocks(int32_t n) { return (n + kBlock - 1) / kBlock; }
 
 static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// The carving order of the projection's workspace (256-byte aligned pieces): wavefront counts,
+// their scans, row totals, scan partials, wavefront depth ranges, the count summary, the seen
+// flags, the instance partials, the depth partials.
 size_t project_ws_bytes(int32_t n, int32_t V) {
-    const int32_t nb = project_blocks(n > 0 ? n : 1);
-    return 2 * align256(sizeof(int32_t) * (size_t)nb * 2 * V) + align256(sizeof(int32_t) * 2 * V) +
-           align256(scan_partials_bytes(nb, 2 * V)) + align256(sizeof(uint2) * (size_t)nb) +
-           align256(sizeof(CountSummary)) + align256((size_t)nb * kBlock);
+    const int32_t nw = project_waves(n);
+    return 2 * align256(sizeof(int32_t) * (size_t)nw * 2 * V) + align256(sizeof(int32_t) * 2 * V) +
+           align256(scan_partials_bytes(nw, 2 * V)) + align256(sizeof(uint2) * (size_t)nw) +
+           align256(sizeof(CountSummary)) + align256((size_t)nw * kWave) +
+           align256(sizeof(int64_t) * (size_t)V * kParts) + align256(sizeof(uint2) * kParts);
 }
+
+int32_t project_count_waves(int32_t n) { return project_waves(n); }
+int32_t project_partials() { return kParts; }
 
 hipError_t launch_project_count(const ProjectArgs& a0, hipStream_t s) {
     ProjectArgs a = a0;
     const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
+    const int32_t nw = project_waves(a.n);
     switch (a.p.sh_degree) {
         case 0: hipLaunchKernelGGL(project_count_kernel<0>, dim3(nb), dim3(kBlock), 0, s, a); break;
         case 1: hipLaunchKernelGGL(project_count_kernel<1>, dim3(nb), dim3(kBlock), 0, s, a); break;
         case 2: hipLaunchKernelGGL(project_count_kernel<2>, dim3(nb), dim3(kBlock), 0, s, a); break;
         default: hipLaunchKernelGGL(project_count_kernel<3>, dim3(nb), dim3(kBlock), 0, s, a); break;
     }
-    hipLaunchKernelGGL(inst_total_kernel, dim3(a.V), dim3(kSumBlock), 0, s, a.block_counts, a.V, nb, a.inst_count);
-    hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nb, 2 * a.V, a.scan_partials, s);
+    hipLaunchKernelGGL(count_partials_kernel, dim3(kParts, a.V + 1), dim3(kSumBlock), 0, s, a.block_counts, a.V, nw,
+                       a.block_depth, a.inst_partials, a.depth_partials);
+    hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nw, 2 * a.V, a.scan_partials, s);
     if (e != hipSuccess) return e;
-    if (a.block_depth)
-        hipLaunchKernelGGL(count_summary_kernel, dim3(1), dim3(kSumBlock), 0, s, a.row_totals, a.inst_count, a.V,
-                           a.block_depth, nb, a.summary);
+    hipLaunchKernelGGL(count_summary_kernel, dim3(1), dim3(kSumBlock), 0, s, a.row_totals, a.inst_partials,
+                       a.depth_partials, a.V, a.inst_count, a.block_depth ? a.summary : nullptr);
     return hipGetLastError();
 }
 

@@ -215,12 +215,12 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, 
 /*
  * gs_project without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
- * projection's scratch (block counts and their scans, per-block depth ranges, the count summary,
- * one flag byte per Gaussian: about 1.3 bytes per Gaussian at 4 views) lives in a static device
- * array of gs_project_noalloc_max_bytes() = 8 MiB that the library holds on every device it runs
- * on until the process ends.  Calls nothing that allocates.  Same arguments, outputs and errors
+ * projection's scratch (per-wavefront counts and their scans, per-wavefront depth ranges, the
+ * count summary, one flag byte per Gaussian: about 2.1 bytes per Gaussian at 4 views) lives in a
+ * static device array of gs_project_noalloc_max_bytes() = 16 MiB that the library holds on every
+ * device it runs on until the process ends.  Calls nothing that allocates.  Same arguments, outputs and errors
  * as gs_project, plus GS_ERR_CAPACITY when gs_project_workspace_size(n, V) exceeds that size
- * (about 6.5 million Gaussians at 4 views), and GS_ERR_HIP if the array's device address cannot
+ * (about 7.8 million Gaussians at 4 views), and GS_ERR_HIP if the array's device address cannot
  * be found.  All calls on one device share the array: calls that overlap in time on one device
  * (from several host threads or streams) race and must be serialised by the caller.
  */

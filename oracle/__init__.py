@@ -73,12 +73,18 @@ def _load():
         _lib.orc_raster_bruteforce.restype = None
         _lib.orc_pair_alpha.restype = None
         _lib.orc_num_threads.restype = ctypes.c_int
+        _lib.orc_set_num_threads.restype = None
     return _lib
 
 
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP threads of the oracle's parallel loops."""
+    _load().orc_set_num_threads(ctypes.c_int(int(n)))
 
 
 def _p(a: np.ndarray):
@@ -344,8 +350,9 @@ def raster_forward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray
 
     Per pixel: alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop before a
     blend that takes T below t_min; C += alpha T c; T *= 1 - alpha; finally C += T bg.
-    Returns image (3,H,W), T_final (H,W), n_contrib (H,W), the evaluated / blended / clamped
-    pair counts, and the float32 error model used by comparisons: err_C (3,H,W) absolute and
+    Returns image (3,H,W), T_final (H,W), n_contrib (H,W), the pair counts n_evaluated (every
+    list entry up to the pixel's stop: E_tile), n_blended, n_clamped and n_box (of the evaluated,
+    those whose exact alpha_min box holds the pixel: E_box), and the float32 error model used by comparisons: err_C (3,H,W) absolute and
     err_T (H,W) relative bounds; n_dec (H,W) = flagged alpha_min / t_min decisions of the pixel
     (within float32 reach of their threshold), -1 when more than three; flag = n_dec != 0;
     unresolved = n_dec < 0; alt = the pixel under every combination of its flagged decisions
@@ -360,7 +367,7 @@ def raster_forward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray
     flag = np.zeros((height, width), np.int8)
     err = np.zeros((3, height, width))
     err_T = np.zeros((height, width))
-    counters = np.zeros(3, np.int64)
+    counters = np.zeros(4, np.int64)
     ranges = np.ascontiguousarray(ranges, np.int32)
     vals = np.ascontiguousarray(vals, np.int32)
     pp = _params(settings)
@@ -384,7 +391,7 @@ def raster_forward(width: int, height: int, ranges: np.ndarray, vals: np.ndarray
     alt = dict(pix=alt_pix[:k][order], C=alt_C[:k][order], T=alt_T[:k][order], nc=alt_nc[:k][order])
     return dict(image=image, T_final=T, n_contrib=nc, n_dec=flag, flag=flag != 0, unresolved=flag < 0, err_C=err,
                 err_T=err_T, alt=alt, n_evaluated=int(counters[0]), n_blended=int(counters[1]),
-                n_clamped=int(counters[2]))
+                n_clamped=int(counters[2]), n_box=int(counters[3]))
 
 
 def loss_grad_l1(image: np.ndarray, target: np.ndarray, scale: float, err_C: Optional[np.ndarray] = None):

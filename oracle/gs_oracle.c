@@ -857,6 +857,7 @@ typedef struct {
     orc_decision clamp[KMAX_DEC + 1];
     int n_fwd, n_clamp_flag;   /* counts (may exceed the stored) */
     int64_t n_eval, n_blend, n_clamped;
+    int64_t n_box;             /* evaluated entries whose exact alpha_min box holds the pixel */
 } orc_walk;
 
 static void walk_init(orc_walk* w, const orc_decision* force, int n_force, orc_blend* log, int8_t* touch)
@@ -912,6 +913,13 @@ static void composite_walk(double px, double py, const int32_t* list, int n, con
         const double v = o * exp(-0.5 * q);
         const double rel = pair_alpha_error(qabs, o);
         w->n_eval++;
+        {
+            /* the exact box of {o exp(-q/2) >= alpha_min}: half extents sqrt(Q Sxx), sqrt(Q Syy)
+             * with Sxx = C / (AC - B^2), Syy = A / (AC - B^2) the dilated covariance's diagonal */
+            const double dc = A * Cc - B * B;
+            const double Q = 2.0 * log(o / p->alpha_min);
+            if (Q >= 0.0 && dc > 0.0 && dx * dx <= Q * Cc / dc && dy * dy <= Q * A / dc) w->n_box++;
+        }
         int pass = v >= p->alpha_min;
         if (fabs(v - p->alpha_min) <= (rel + thr) * p->alpha_min) note_decision(w, j, DEC_AMIN);
         if (w->touch) w->touch[j] = (int8_t)(v >= p->alpha_min * (1.0 - rel - thr));
@@ -974,8 +982,9 @@ static int subset(const orc_decision* d, int k, int mask, orc_decision* out)
  * row-major with tiles_x = ceil(W / tile).  Outputs: image[3][H][W], T_final[H][W],
  * n_contrib[H][W]; flag[H][W] = the number of flagged alpha_min / t_min decisions of the pixel
  * (-1: more than KMAX_DEC, unresolved); err_C[3][H][W] (float32 error bound of the colour,
- * absolute); err_T[H][W] (of T_final, relative); counters[3] = {evaluated pairs, blended pairs,
- * blended pairs whose alpha was clamped}.  Alternatives: for every pixel with 1..KMAX_DEC
+ * absolute); err_T[H][W] (of T_final, relative); counters[4] = {evaluated pairs (every list entry
+ * up to the pixel's stop: E_tile), blended pairs, blended pairs whose alpha was clamped, evaluated
+ * pairs whose pixel lies in the entry's exact alpha_min box (E_box)}.  Alternatives: for every pixel with 1..KMAX_DEC
  * flagged decisions and every non-empty combination of them taken the other way, one entry
  * (alt_pix = y W + x, alt_C[3], alt_T, alt_nc); *alt_n = their number (entries past alt_cap are
  * counted, not written).
@@ -990,8 +999,8 @@ void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32
     const int tx_n = (W + tile - 1) / tile, ty_n = (H + tile - 1) / tile;
     const orc_records r = {mean2d, conic, opacity, color};
     const int64_t plane = (int64_t)W * H;
-    int64_t tot_eval = 0, tot_blend = 0, tot_clamp = 0, n_alt = 0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(+ : tot_eval, tot_blend, tot_clamp)
+    int64_t tot_eval = 0, tot_blend = 0, tot_clamp = 0, tot_box = 0, n_alt = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : tot_eval, tot_blend, tot_clamp, tot_box)
     for (int t = 0; t < tx_n * ty_n; t++) {
         const int tx = t % tx_n, ty = t / tx_n;
         const int32_t start = ranges[2 * t], end = ranges[2 * t + 1];
@@ -1012,6 +1021,7 @@ void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32
                 tot_eval += w.n_eval;
                 tot_blend += w.n_blend;
                 tot_clamp += w.n_clamped;
+                tot_box += w.n_box;
                 if (w.n_fwd == 0 || w.n_fwd > KMAX_DEC) continue;
                 for (int mask = 1; mask < (1 << w.n_fwd); mask++) {
                     orc_decision f[KMAX_DEC];
@@ -1035,6 +1045,7 @@ void orc_raster_forward(int32_t W, int32_t H, const int32_t* ranges, const int32
     counters[0] = tot_eval;
     counters[1] = tot_blend;
     counters[2] = tot_clamp;
+    counters[3] = tot_box;
 }
 
 /* ve helpers for the compositing backward: a faithful reciprocal (one ulp) */
@@ -1328,4 +1339,11 @@ void orc_raster_bruteforce(int32_t W, int32_t H, const int32_t* order, int32_t n
 int orc_num_threads(void)
 {
     return omp_get_max_threads();
+}
+
+/* Set the threads of the parallel loops above (the CPU baseline is timed at all threads and at
+ * one). */
+void orc_set_num_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
 }

@@ -284,13 +284,13 @@ def test_readback_create_rejects_null(gs):
 
 def test_project_noalloc_rejects_inputs_beyond_its_scratch(gs):
     """gs_project_noalloc refuses, on the host, inputs whose projection workspace exceeds its
-    static 8 MiB scratch (nothing is launched, so the fake pointers are never touched)."""
+    static 16 MiB scratch (nothing is launched, so the fake pointers are never touched)."""
     lib = gs.load()
-    assert gs.gs_project_noalloc_max_bytes() == 8 << 20
+    assert gs.gs_project_noalloc_max_bytes() == 16 << 20
     c = cams(gs, V=4)
     p = params(gs)
     n_fit = 6_000_000
-    assert gs.gs_project_workspace_size(n_fit, 4) <= 8 << 20 < gs.gs_project_workspace_size(8_000_000, 4)
+    assert gs.gs_project_workspace_size(n_fit, 4) <= 16 << 20 < gs.gs_project_workspace_size(8_000_000, 4)
     g_big = gs.gs_gaussians(8_000_000, FAKE, FAKE, FAKE, FAKE, FAKE)
     out = projected(gs, capacity=8_000_000)
     assert lib.gs_project_noalloc(ctypes.byref(g_big), c, 4, ctypes.byref(p), ctypes.byref(out), None) == 2

@@ -169,3 +169,29 @@ def test_anisotropic_profile_with_library_inverse(oracle_mod):
     alpha = np.minimum(widen(0.99), o32 * np.exp(-0.5 * qf))
     alpha = np.where(alpha >= widen(1 / 255), alpha, 0.0)
     np.testing.assert_allclose(r["fwd"]["T_final"], 1 - alpha, rtol=1e-9, atol=1e-11)
+
+
+def test_evaluation_counts(oracle_mod):
+    """E_tile (every list entry a pixel walks up to its stop) and E_box (those whose exact
+    alpha_min box holds the pixel): for one Gaussian, E_tile = the pixels of its tiles and
+    E_box = the pixel centres inside the box sqrt(2 ln(o / alpha_min) Sigma'_xx) x (..yy) around
+    its centre; on a scene, blends <= E_box <= E_tile."""
+    cam = pinhole(64, 64, f=80.0, cx=29.3, cy=35.1)
+    sc = scene_from([[0.1, -0.05, 3.0]], [[-2.3, -2.8, -2.5]], [[0.9, 0.2, -0.3, 0.1]], [logit(0.7)], [[1, 1, 1]],
+                    [cam])
+    st = sc.settings()
+    r = render(oracle_mod, sc, st)
+    rec = r["rec"]
+    (tx0, ty0, tx1, ty1) = rec["rect"][0]
+    assert r["fwd"]["n_evaluated"] == (tx1 - tx0 + 1) * (ty1 - ty0 + 1) * 256
+    A, B, C = rec["conic"][0]
+    det = A * C - B * B
+    Q = 2 * math.log(rec["opacity"][0] / widen(1 / 255))
+    ys, xs = np.mgrid[0:64, 0:64]
+    dx, dy = xs + 0.5 - rec["mean2d"][0, 0], ys + 0.5 - rec["mean2d"][0, 1]
+    in_tiles = (xs // 16 >= tx0) & (xs // 16 <= tx1) & (ys // 16 >= ty0) & (ys // 16 <= ty1)
+    box = (dx * dx <= Q * C / det) & (dy * dy <= Q * A / det) & in_tiles
+    assert r["fwd"]["n_box"] == int(box.sum()) > 0
+    sc2 = scenes.random_scene(2000, 96, 80, seed=4, log_scale_mean=-2.6, opacity_std=1.5)
+    f = render(oracle_mod, sc2, sc2.settings())["fwd"]
+    assert 0 < f["n_blended"] <= f["n_box"] <= f["n_evaluated"]

@@ -47,7 +47,7 @@ def snapshot(r):
 @pytest.mark.parametrize("cases", [[(300_000, 3, 640, 480, 11), (40_000, 2, 320, 200, 12)]])
 def test_noalloc_projection_equals_workspace_projection(env, cases):
     gsmi, pipeline, torch = env
-    assert gsmi.gs_project_noalloc_max_bytes() == 8 << 20
+    assert gsmi.gs_project_noalloc_max_bytes() == 16 << 20
     for n, V, W, H, seed in cases:
         sc = scenes.random_scene(n, W, H, seed=seed, views=V, sh_degree=3)
         need = gsmi.gs_project_workspace_size(n, V)
