@@ -135,7 +135,7 @@ def main():
     info = r.bin()
     r.forward(counters=True)
     torch.cuda.synchronize()
-    E_eval, B, E_alpha = [int(x) for x in r.counters.cpu().tolist()]
+    E_eval, B, E_alpha, _ = [int(x) for x in r.counters.cpu().tolist()]
     vis = [info.vis_count[v] for v in range(r.V)]
     M = int(info.num_instances)
     log(f"[bench] visible {vis}, instances {M}, evaluated pairs {E_eval}, pairs past the alpha test {E_alpha}, "

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgsmi.so")
 SOURCES = ["project.hip", "project_bwd.hip", "scan.hip", "sort.hip", "bin.hip", "raster.hip", "sparse.hip",
-           "compose.hip", "adam.hip", "api.cpp"]
+           "compose.hip", "adam.hip", "check.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "common.h"
 
@@ -647,6 +648,102 @@ gs_status gs_raster_fused(const gs_camera* cams, const gs_projected* proj, const
     return hip_check(launch_raster_fused(ra, (int)mode, target_or_dldc, loss_scale, image_opt, loss_sum_opt, g,
                                          static_cast<hipStream_t>(stream)),
                      "gs_raster_fused launch");
+}
+
+gs_status gs_check_bins(const gs_camera* cams, const gs_projected* proj, int32_t V, const gs_render_params* p,
+                        const gs_bins* bins, int64_t* violations, void* stream) {
+    g_last_error.clear();
+    gs_status st = check_cams(cams, V);
+    if (st != GS_OK) return st;
+    if ((st = check_params(p)) != GS_OK) return st;
+    if ((st = check_projected(proj, false)) != GS_OK) return st;
+    if (!proj->depth || !proj->tile_rect || !proj->n_tiles || !proj->inst_base)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected depth/rect/n_tiles/inst_base are null");
+    if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges)
+        return fail(GS_ERR_INVALID_ARGUMENT, "bins outputs are null");
+    if (p->tile_cap > 0 && (!bins->vals_capped || !bins->ranges_capped || !bins->num_capped))
+        return fail(GS_ERR_INVALID_ARGUMENT, "capped outputs are null while tile_cap > 0");
+    if (bins->count < 0) return fail(GS_ERR_INVALID_ARGUMENT, "bins hold no successful gs_bin_tiles result");
+    if (!violations) return fail(GS_ERR_INVALID_ARGUMENT, "violations is null");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int tiles_x = tiles_along(cams[0].width), tiles_y = tiles_along(cams[0].height);
+    // device counters: violations, then [2V] sums of the full lists, then [2V] of the capped ones
+    const size_t bytes = sizeof(unsigned long long) * GS_CHECK_KINDS + sizeof(long long) * 4 * V;
+    void* dbuf = nullptr;
+    if ((st = hip_check(hipMalloc(&dbuf, bytes), "check buffer")) != GS_OK) return st;
+    struct Free {
+        void* p;
+        ~Free() { (void)hipFree(p); }
+    } guard{dbuf};
+    unsigned long long* viol = static_cast<unsigned long long*>(dbuf);
+    long long* sums = reinterpret_cast<long long*>(viol + GS_CHECK_KINDS);
+    if ((st = hip_check(hipMemsetAsync(dbuf, 0, bytes, s), "check clear")) != GS_OK) return st;
+    CheckArgs a;
+    a.V = V;
+    a.capacity = proj->capacity;
+    a.tpv = tiles_x * tiles_y;
+    a.tiles_x = tiles_x;
+    a.count = bins->count;
+    a.vis_count = proj->vis_count;
+    a.depth = proj->depth;
+    a.rect = reinterpret_cast<const ushort4*>(proj->tile_rect);
+    a.n_tiles = proj->n_tiles;
+    a.inst_base = proj->inst_base;
+    a.tile_keys = bins->tile_keys;
+    a.vals = bins->vals;
+    a.ranges = bins->ranges;
+    a.cap = 0;
+    a.viol = viol;
+    a.sums = sums;
+    if ((st = hip_check(launch_check_bins(a, true, s), "check launch")) != GS_OK) return st;
+    int32_t kept = 0;
+    if (p->tile_cap > 0) {
+        if ((st = hip_check(hipMemcpyAsync(&kept, bins->num_capped, sizeof(kept), hipMemcpyDeviceToHost, s),
+                            "check kept read")) != GS_OK)
+            return st;
+        if ((st = hip_check(hipStreamSynchronize(s), "check sync")) != GS_OK) return st;
+        CheckArgs c = a;
+        c.count = kept;
+        c.tile_keys = nullptr;
+        c.vals = bins->vals_capped;
+        c.ranges = bins->ranges_capped;
+        c.cap = p->tile_cap;
+        c.sums = sums + 2 * V;
+        if ((st = hip_check(launch_check_bins(c, false, s), "check launch")) != GS_OK) return st;
+    }
+    unsigned long long hv[GS_CHECK_KINDS];
+    std::vector<long long> hs(4 * (size_t)V);
+    std::vector<int32_t> vis(V), first(V, 0);
+    if ((st = hip_check(hipMemcpyAsync(hv, viol, sizeof(hv), hipMemcpyDeviceToHost, s), "check read")) != GS_OK ||
+        (st = hip_check(hipMemcpyAsync(hs.data(), sums, sizeof(long long) * 4 * V, hipMemcpyDeviceToHost, s),
+                        "check read")) != GS_OK ||
+        (st = hip_check(hipMemcpyAsync(vis.data(), proj->vis_count, sizeof(int32_t) * V, hipMemcpyDeviceToHost, s),
+                        "check read")) != GS_OK)
+        return st;
+    if ((st = hip_check(hipStreamSynchronize(s), "check sync")) != GS_OK) return st;
+    for (int v = 0; v < V; v++)
+        if (vis[v] > 0 &&
+            (st = hip_check(hipMemcpy(&first[v], proj->inst_base + (size_t)v * proj->capacity, sizeof(int32_t),
+                                      hipMemcpyDeviceToHost),
+                            "check read")) != GS_OK)
+            return st;
+    // host rules: per view, the full lists hold exactly the slots' instances, which the instance
+    // bases number view after view; the capped lists are no longer than the full ones
+    long long before = 0;
+    for (int v = 0; v < V; v++) {
+        if (hs[V + v] != hs[v]) hv[GS_CHECK_COUNT]++;
+        if (vis[v] > 0 && first[v] != before) hv[GS_CHECK_SLOT_RECORD]++;
+        before += hs[v];
+        if (p->tile_cap > 0 && hs[3 * V + v] > hs[V + v]) hv[GS_CHECK_COUNT]++;
+    }
+    static const char* names[GS_CHECK_KINDS] = {"range", "key", "slot", "rect", "order", "count", "cap", "slot record"};
+    std::string found;
+    for (int k = 0; k < GS_CHECK_KINDS; k++) {
+        violations[k] = (int64_t)hv[k];
+        if (hv[k]) found += std::string(found.empty() ? "" : ", ") + names[k] + " x" + std::to_string(hv[k]);
+    }
+    if (!found.empty()) return fail(GS_ERR_INTERNAL, "bins violate: %s", found.c_str());
+    return GS_OK;
 }
 
 gs_status gs_fused_max_cap(int32_t* k) {

@@ -274,4 +274,23 @@ hipError_t launch_adam_step(const AdamArgs& a, int64_t n, int32_t t, int32_t* la
 hipError_t launch_adam_flush(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, hipStream_t s);
 int32_t fused_lds_entries();
 
+// GS_CHECK: device validation of tile lists (gs_check_bins).
+struct CheckArgs {
+    int32_t V, capacity, tpv, tiles_x;
+    int64_t count;              // entries of the lists checked (instances, or the kept ones)
+    const int32_t* vis_count;   // [V]
+    const float* depth;         // [V][capacity]
+    const ushort4* rect;        // [V][capacity]
+    const int32_t* n_tiles;     // [V][capacity]
+    const int32_t* inst_base;   // [V][capacity]
+    const uint32_t* tile_keys;  // sorted tile keys of the full lists; NULL for the capped lists
+    const int32_t* vals;
+    const int32_t* ranges;      // [V * tpv][2]
+    int32_t cap;                // the cap of capped lists, else 0
+    unsigned long long* viol;   // [GS_CHECK_KINDS] violation counts
+    long long* sums;            // [2V]: n_tiles summed over each view's slots, then list lengths per view
+};
+// slots: also the per-slot checks and sums (once per call, with the full lists)
+hipError_t launch_check_bins(const CheckArgs& a, bool slots, hipStream_t s);
+
 }  // namespace gsmi

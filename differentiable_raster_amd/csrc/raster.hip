@@ -216,7 +216,7 @@ struct Fwd {
 };
 
 struct Counts {
-    int64_t eval, blend, hit;
+    int64_t eval, blend, hit, staged;
 };
 
 // Front-to-back over this block's list of the staged batch (positions j = jbase + k).  Every
@@ -561,11 +561,13 @@ __device__ __forceinline__ void add_counters(int64_t* counters, Counts c) {
         c.eval += __shfl_xor(c.eval, o);
         c.blend += __shfl_xor(c.blend, o);
         c.hit += __shfl_xor(c.hit, o);
+        c.staged += __shfl_xor(c.staged, o);
     }
     if ((threadIdx.x & (kWave - 1)) == 0) {
         atomicAdd((unsigned long long*)&counters[0], (unsigned long long)c.eval);
         atomicAdd((unsigned long long*)&counters[1], (unsigned long long)c.blend);
         atomicAdd((unsigned long long*)&counters[2], (unsigned long long)c.hit);
+        if (c.staged) atomicAdd((unsigned long long*)&counters[3], (unsigned long long)c.staged);
     }
 }
 
@@ -593,6 +595,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
         if (__syncthreads_count(f.done != 0.0f) == kBlock) break;
         const int cnt_b = min(kBatch, c.n - b0);
         if ((int)threadIdx.x < cnt_b) stage<INST>(a, c, b, threadIdx.x, b0 + threadIdx.x);
+        if (COUNT && threadIdx.x == 0) cnt.staged += cnt_b;
         __syncthreads();
         const Lists l = build_lists(c, b, cnt_b);
         fwd_walk<COUNT>(a, c, b, l, b0, f, cnt);
@@ -604,7 +607,7 @@ __device__ __forceinline__ void forward_tile(const RasterArgs& a, const TileCtx&
 // Backward over list positions [0, maxnc); the batch starting at `resident_b0` (with
 // `resident_cnt` entries) is already staged.  The log must be zero on entry; it is zero again on
 // return.
-template <bool BG>
+template <bool BG, bool COUNT = false>
 __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx& c, Batch& b, Log& log, int* s_wave,
                                               int32_t maxnc, int32_t resident_b0, int resident_cnt, Bwd& s) {
     const int row_nc = row_max(s.nc);
@@ -629,6 +632,8 @@ __device__ __forceinline__ void backward_tile(const RasterArgs& a, const TileCtx
         if (b0 != resident_b0) {
             cnt_b = min(kBatch, maxnc - b0);
             if ((int)threadIdx.x < cnt_b) stage<true>(a, c, b, threadIdx.x, b0 + threadIdx.x);
+            // the restaged entries (diagnostics of the counting variant)
+            if (COUNT && threadIdx.x == 0) atomicAdd((unsigned long long*)&a.counters[3], (unsigned long long)cnt_b);
             __syncthreads();
         }
         pair_prefix(c, b, cnt_b, s_wave);
@@ -651,7 +656,7 @@ __global__ __launch_bounds__(kBlock) void raster_fwd_kernel(RasterArgs a, float*
     __shared__ Batch b;
     const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, c.inside ? 0.0f : 1.0f};
-    Counts cnt{0, 0, 0};
+    Counts cnt{0, 0, 0, 0};
     int32_t last_b0;
     int last_cnt;
     zero_lists(b);
@@ -845,7 +850,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.huge_count = 0;  // the gather appends after this kernel
     const TileCtx c = tile_ctx(a);
     Fwd f{1.0f, 0.0f, 0.0f, 0.0f, 0, c.inside ? 0.0f : 1.0f};
-    Counts cnt{0, 0, 0};
+    Counts cnt{0, 0, 0, 0};
     int32_t last_b0;
     int last_cnt;
     zero_log(log);
@@ -893,7 +898,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     const int maxnc = block_max(s.nc, s_red);
     // every pixel's last blended entry lies in the last staged batch, so it is still resident
     s.gbg = fmaf(s.g0, a.p.bg[0], fmaf(s.g1, a.p.bg[1], s.g2 * a.p.bg[2]));
-    backward_tile<BG>(a, c, b, log, s_red, maxnc, last_b0, last_cnt, s);
+    backward_tile<BG, COUNT>(a, c, b, log, s_red, maxnc, last_b0, last_cnt, s);
 }
 
 }  // namespace

@@ -120,6 +120,8 @@ _SIGS = {
     "gs_project_bwd": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
                                       _P(gs_projected), _P(gs_grads2d), _P(gs_grads3d), ctypes.c_void_p]),
     "gs_fused_max_cap": (ctypes.c_int, [_P(ctypes.c_int32)]),
+    "gs_check_bins": (ctypes.c_int, [_P(gs_camera), _P(gs_projected), ctypes.c_int32, _P(gs_render_params),
+                                     _P(gs_bins), _P(ctypes.c_int64), ctypes.c_void_p]),
     "gs_grad_encode_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "gs_grad_encode": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                       _P(gs_grads2d), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -234,6 +236,20 @@ def gs_raster_workspace_size(instance_capacity: int) -> int:
 
 def gs_bin_workspace_size(n: int, V: int, width: int, height: int, instance_capacity: int) -> int:
     return int(load().gs_bin_workspace_size(n, V, width, height, instance_capacity))
+
+
+GS_CHECK_KINDS = 8
+GS_CHECK_NAMES = ("range", "key", "slot", "rect", "order", "count", "cap", "slot_record")
+
+
+def gs_check_bins(cams, proj: gs_projected, V: int, params: gs_render_params, bins: gs_bins, stream=None):
+    """GS_CHECK: (status, {kind: violations}) of the device validation of the tile lists."""
+    out = (ctypes.c_int64 * GS_CHECK_KINDS)()
+    st = load().gs_check_bins(cams, ctypes.byref(proj), V, ctypes.byref(params), ctypes.byref(bins), out,
+                              _stream(stream))
+    if st not in (0, 5):  # GS_ERR_INTERNAL reports violations
+        _check(st, "gs_check_bins")
+    return st, dict(zip(GS_CHECK_NAMES, [int(x) for x in out]))
 
 
 def gs_fused_max_cap() -> int:

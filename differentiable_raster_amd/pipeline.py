@@ -80,7 +80,7 @@ class Renderer:
         self.grads = gsmi.gs_grads2d(self.d_mean2d.data_ptr(), self.d_conic.data_ptr(), self.d_opacity.data_ptr(),
                                      self.d_color.data_ptr())
         self.loss_sum = torch.zeros(1, dtype=f32, device=dev)
-        self.counters = torch.zeros(3, dtype=torch.int64, device=dev)
+        self.counters = torch.zeros(4, dtype=torch.int64, device=dev)
         self.target = up(scene.target.reshape(-1)) if scene.target is not None else None
         self.dldc_in = up(scene.dldc.reshape(-1)) if scene.dldc is not None else None
         self.info = None
@@ -123,6 +123,10 @@ class Renderer:
                 raise gsmi.GsError(st, "gs_bin_tiles", gsmi.load().gs_last_error().decode())
         self.info = info
         return info
+
+    def check_bins(self):
+        """GS_CHECK: validate the tile lists on the device; returns (status, {kind: violations})."""
+        return gsmi.gs_check_bins(self.cams, self.proj, self.V, self.params, self.bins)
 
     @property
     def use_capped(self) -> int:

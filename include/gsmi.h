@@ -165,11 +165,12 @@ typedef struct {
 
 typedef enum { GS_LOSS_L1 = 0, GS_LOSS_EXTERNAL = 1 } gs_loss_mode;
 
-/* Optional per-call diagnostics: device int64 [3], accumulated (the caller zeroes them); pass
+/* Optional per-call diagnostics: device int64 [4], accumulated (the caller zeroes them); pass
  * NULL to skip (counting selects a slower kernel variant).  [0] (pixel, list entry) pairs the
  * forward evaluated; [1] pairs blended; [2] evaluated pairs whose alpha reaches alpha_min (the
  * blended pairs plus, per pixel, at most the one at which it stops: every correct method must
- * evaluate these, whatever it culls). */
+ * evaluate these, whatever it culls); [3] list entries staged from the packed records into LDS
+ * (every forward batch, and in gs_raster_fused every batch the backward stages again). */
 typedef int64_t gs_counters;
 
 const char* gs_version(void);
@@ -332,8 +333,48 @@ gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams /*host [V]
                          const gs_render_params* p, const gs_projected* proj, const gs_grads2d* grads2d,
                          gs_grads3d* out, void* stream);
 
-/* Entries of a tile list the rasterizers stage in LDS at a time (lists of any length are
- * processed batch by batch).  *k (host) receives it. */
+/*
+ * GS_CHECK, a debug aid: validates on the device what gs_bin_tiles wrote for `proj`, `V` views
+ * and params `p` (the full lists, and the capped ones too when p->tile_cap > 0), against the
+ * properties the (view, tile, depth, slot) order fixes.  violations (host [GS_CHECK_KINDS]) receives
+ * the count of each kind:
+ *   GS_CHECK_RANGE       a tile range reversed, outside [0, count), non-zero while empty, or not
+ *                        where the partition of [0, count) in global tile order puts it;
+ *   GS_CHECK_KEY         a full-list entry whose sorted tile key is not its range's tile;
+ *   GS_CHECK_SLOT        an entry naming no visible slot of its tile's view;
+ *   GS_CHECK_RECT        an entry whose tile lies outside its slot's tile rectangle;
+ *   GS_CHECK_ORDER       a list that is not strictly increasing in (depth, slot);
+ *   GS_CHECK_COUNT       list lengths that do not add up to each view's instances (the slots'
+ *                        n_tiles; for capped lists, to *num_capped and at most the full lists);
+ *   GS_CHECK_CAP         a capped list longer than the cap;
+ *   GS_CHECK_SLOT_RECORD a slot rectangle off the tile grid, an n_tiles that is not its area, or
+ *                        instance bases that do not follow the slots view by view.
+ * Allocates a small device buffer and synchronizes the stream (never call it where allocation or
+ * waiting is not allowed).  Returns GS_ERR_INTERNAL, naming the kinds found, when any count is
+ * non-zero; GS_ERR_INVALID_ARGUMENT for null pointers or bins without a successful count.
+ */
+#define GS_CHECK_RANGE 0
+#define GS_CHECK_KEY 1
+#define GS_CHECK_SLOT 2
+#define GS_CHECK_RECT 3
+#define GS_CHECK_ORDER 4
+#define GS_CHECK_COUNT 5
+#define GS_CHECK_CAP 6
+#define GS_CHECK_SLOT_RECORD 7
+#define GS_CHECK_KINDS 8
+gs_status gs_check_bins(const gs_camera* cams /*host [V]*/, const gs_projected* proj, int32_t V,
+                        const gs_render_params* p, const gs_bins* bins, int64_t* violations /*host*/,
+                        void* stream);
+
+/*
+ * The largest per-tile cap K (gs_render_params.tile_cap) under which gs_raster_fused keeps every
+ * tile's list on chip from the forward through the backward: a list of at most K entries is
+ * staged from the packed records into LDS once, in one batch, and the backward walks that same
+ * batch (ByteSplat, English abstract: pruning that respects per-tile shared-memory limits).
+ * Longer lists (a larger cap, or none) are still rendered exactly: they stream through LDS in
+ * batches of K entries and the backward stages every batch but the last one again, which
+ * diagnostics counter [3] shows.  *k (host) receives K.
+ */
 gs_status gs_fused_max_cap(int32_t* k);
 
 /*

@@ -296,3 +296,23 @@ def test_project_noalloc_rejects_inputs_beyond_its_scratch(gs):
     assert lib.gs_project_noalloc(ctypes.byref(g_big), c, 4, ctypes.byref(p), ctypes.byref(out), None) == 2
     assert b"static scratch" in lib.gs_last_error()
     assert lib.gs_project_noalloc(None, c, 4, ctypes.byref(p), ctypes.byref(out), None) == 1
+
+
+def test_check_bins_rejects_bad_arguments(gs):
+    """gs_check_bins validates its arguments on the host before touching the device."""
+    lib = gs.load()
+    c = cams(gs)
+    p = params(gs)
+    pr = projected(gs)
+    viol = (ctypes.c_int64 * gs.GS_CHECK_KINDS)()
+    b = gs.gs_bins(100, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert lib.gs_check_bins(None, ctypes.byref(pr), 1, ctypes.byref(p), ctypes.byref(b), viol, None) == 1
+    assert lib.gs_check_bins(c, None, 1, ctypes.byref(p), ctypes.byref(b), viol, None) == 1
+    assert lib.gs_check_bins(c, ctypes.byref(pr), 1, ctypes.byref(p), None, viol, None) == 1
+    assert lib.gs_check_bins(c, ctypes.byref(pr), 1, ctypes.byref(p), ctypes.byref(b), None, None) == 1
+    failed = gs.gs_bins(100, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert lib.gs_check_bins(c, ctypes.byref(pr), 1, ctypes.byref(p), ctypes.byref(failed), viol, None) == 1
+    assert b"successful" in lib.gs_last_error()
+    capped = params(gs, tile_cap=4)
+    nocap = gs.gs_bins(100, 10, FAKE, FAKE, FAKE, None, None, None, None)
+    assert lib.gs_check_bins(c, ctypes.byref(pr), 1, ctypes.byref(capped), ctypes.byref(nocap), viol, None) == 1

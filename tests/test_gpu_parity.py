@@ -79,7 +79,8 @@ def test_tiny_scene(env, mode):
     run_view_checks(env, sc, sc.settings(), mode=mode)
 
 
-@pytest.mark.parametrize("seed,views,size", [(101, 2, (100, 75)), (102, 3, (130, 47)), (103, 1, (16, 16))])
+@pytest.mark.parametrize("seed,views,size", [(101, 2, (100, 75)), (102, 3, (130, 47)), (103, 1, (16, 16)),
+                                             (104, 7, (72, 40)), (105, 16, (48, 32))])
 def test_random_multiview_ragged(env, seed, views, size):
     sc = scenes.random_scene(3000, size[0], size[1], seed=seed, views=views, log_scale_mean=-3.2, sh_degree=2,
                              opacity_std=1.5)
@@ -117,6 +118,42 @@ def test_long_lists_take_the_chunked_fused_path(env):
     run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
 
 
+def test_fused_max_cap_keeps_capped_lists_on_chip(env):
+    """With tile_cap K = gs_fused_max_cap() every capped tile list is staged into LDS exactly once
+    and the backward walks that copy (diagnostics counter [3]: staged entries equal the kept
+    instances, and the fused call stages nothing the forward did not); with a cap of 2K the lists
+    stream in batches and the backward stages earlier batches again.  Both render like the
+    oracle."""
+    oracle, pipeline, torch = env
+    from differentiable_raster_amd import gsmi
+    K = gsmi.gs_fused_max_cap()
+    rng = np.random.default_rng(6)
+    n = 3000
+    cam = pinhole(32, 32, f=40.0, cx=16.0, cy=16.0)
+    means = np.stack([rng.uniform(-0.15, 0.15, n), rng.uniform(-0.15, 0.15, n), rng.uniform(2, 3, n)], 1)
+    sc = scene_from(means, np.full((n, 3), -4.0), rng.standard_normal((n, 4)), rng.normal(-3.0, 1.0, n),
+                    rng.uniform(0, 1, (n, 3)), [cam], target=rng.uniform(0, 1, (1, 3, 32, 32)))
+    for cap in (K, 2 * K):
+        st = sc.settings(tile_cap=cap)
+        r = pipeline.Renderer(sc, st)
+        r.project(); r.bin()
+        r.forward(counters=True)
+        torch.cuda.synchronize()
+        fwd_staged = int(r.counters[3].item())
+        r.fused(scale=1.0, image=True, counters=True)
+        torch.cuda.synchronize()
+        fused_staged = int(r.counters[3].item())
+        kept = int(r.num_capped.item())
+        print(f"[cap contract] K={cap}: kept {kept}, forward staged {fwd_staged}, fused staged {fused_staged}",
+              flush=True)
+        assert kept > 2 * K  # four tiles, each list capped at `cap`
+        if cap <= K:
+            assert fwd_staged == kept and fused_staged == fwd_staged
+        else:
+            assert fused_staged > fwd_staged
+        run_view_checks(env, sc, st, mode="fused", check_projection=False)
+
+
 def test_fused_equals_separate(env):
     oracle, pipeline, torch = env
     sc = scenes.make_scene(1)
@@ -139,7 +176,7 @@ def test_counters_match_oracle(env):
     r = pipeline.Renderer(sc, st)
     r.project(); r.bin(); r.forward(counters=True)
     torch.cuda.synchronize()
-    ev, bl, hit = [int(x) for x in r.counters.cpu().numpy()]
+    ev, bl, hit, _ = [int(x) for x in r.counters.cpu().numpy()]
     # pairs past the alpha test: the blends plus at most one stopping pair per pixel
     assert bl <= hit <= min(ev, bl + 128 * 128)
     ref = oracle.iteration(sc, st, backward=False)[0]["fwd"]
