@@ -43,6 +43,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Debug build: the host code (argument checks, workspace carving, launch set-up) instrumented
+# with AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code is built as usual (the
+# sanitizers have no GPU form on this target).  The library expects the ASan runtime in the
+# process: preload asan_runtime() (LD_PRELOAD) when loading it into an uninstrumented program.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of the compiler hipcc drives."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"no shared ASan runtime found ({path!r})")
+    return path
+
+
+def build_sanitized(out_dir: str) -> str:
+    """Build out_dir/libgsmi_san.so with the host code under ASan and UBSan."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *SANITIZE]
+
+    def comp(src):
+        obj = os.path.join(out_dir, src + ".o")
+        r = subprocess.run([HIPCC, *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    lib = os.path.join(out_dir, "libgsmi_san.so")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libsan", *SANITIZE, *objs,
+                        "-o", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

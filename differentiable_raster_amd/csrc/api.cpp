@@ -244,6 +244,7 @@ const char* gs_status_string(gs_status s) {
         case GS_ERR_UNSUPPORTED: return "unsupported";
         case GS_ERR_HIP: return "HIP runtime error";
         case GS_ERR_INTERNAL: return "internal error";
+        default: break;
     }
     return "unknown status";
 }

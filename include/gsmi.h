@@ -47,9 +47,12 @@ typedef enum {
     GS_OK = 0,
     GS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent cameras, ... */
     GS_ERR_CAPACITY = 2,         /* an output buffer is too small; *required says how large */
-    GS_ERR_UNSUPPORTED = 3,      /* e.g. a tile cap above the fused kernel's on-chip limit */
+    GS_ERR_UNSUPPORTED = 3,      /* a request the library does not serve (e.g. a device index past
+                                    the ones it keeps state for) */
     GS_ERR_HIP = 4,              /* a HIP runtime call failed */
-    GS_ERR_INTERNAL = 5
+    GS_ERR_INTERNAL = 5,         /* a check of the library's own results failed */
+    GS_STATUS_FORCE_INT32 = 0x7FFFFFFF /* not a status: makes every int32 value a valid gs_status
+                                          (callers in C may pass any int) */
 } gs_status;
 
 /* Pinhole camera, OpenCV axes (x right, y down, z forward).  Host struct.
@@ -163,7 +166,12 @@ typedef struct {
     float* d_sh;             /* [3*(d+1)^2][n], row k*3 + channel */
 } gs_grads3d;
 
-typedef enum { GS_LOSS_L1 = 0, GS_LOSS_EXTERNAL = 1 } gs_loss_mode;
+typedef enum {
+    GS_LOSS_L1 = 0,
+    GS_LOSS_EXTERNAL = 1,
+    GS_LOSS_MODE_FORCE_INT32 = 0x7FFFFFFF /* not a mode: any int32 value is a valid gs_loss_mode,
+                                             so that an unknown one is refused, not undefined */
+} gs_loss_mode;
 
 /* Optional per-call diagnostics: device int64 [4], accumulated (the caller zeroes them); pass
  * NULL to skip (counting selects a slower kernel variant).  [0] (pixel, list entry) pairs the

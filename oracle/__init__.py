@@ -25,7 +25,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gs_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# GS_ORACLE_LIB names another build of gs_oracle.c to load (the sanitizer test's).
+_LIB = os.environ.get("GS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 
 def build(force: bool = True) -> str:
@@ -36,6 +37,17 @@ def build(force: bool = True) -> str:
                                "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(out_dir: str) -> str:
+    """out_dir/liboracle_san.so: the oracle under gcc's AddressSanitizer and
+    UndefinedBehaviorSanitizer (load it with gcc's libasan preloaded and GS_ORACLE_LIB set)."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "liboracle_san.so")
+    subprocess.check_call(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=all", "-fopenmp", "-ffp-contract=off", "-std=c11", "-Wall",
+                           "-shared", "-fPIC", _SRC, "-o", lib, "-lm"])
+    return lib
 
 
 class _Camera(ctypes.Structure):
