@@ -13,11 +13,11 @@
 //          wavefronts' tile-instance counts, plus a wave scan) and the packed 64-byte record the
 //          rasterizers stage with one line per list entry.  No barrier either.
 // The mean alone decides the near plane and the frustum guard of every view, so pass 1 reads
-// the other 32 B of geometry only for Gaussians some view keeps.  Spherical-harmonic
-// coefficients (192 B per Gaussian at degree 3) are read only for Gaussians that some view sees
-// (in a large scene most are outside every view): the counting pass checks at the first such
-// view that they are bounded (which makes every colour finite) and flags the Gaussian, and the
-// writing pass keeps a flagged Gaussian's coefficients in registers for all views.
+// the other 32 B of geometry only for Gaussians some view keeps.  Visibility never depends on
+// the colour (a Gaussian whose colour is not finite in a view is kept there, transparent: its
+// record carries opacity 0 and colour 0), so pass 1 reads no spherical-harmonic coefficient at
+// all, and pass 2 reads them (192 B per Gaussian at degree 3) only for Gaussians that some view
+// sees, once for all views.
 #include "common.h"
 #include "gauss.h"
 
@@ -110,20 +110,6 @@ __device__ __forceinline__ bool view_centre(const CamDev& c, float znear, float 
     return ce.mx >= -gx && ce.mx <= (float)c.width + gx && ce.my >= -gy && ce.my <= (float)c.height + gy;
 }
 
-// True when every SH coefficient of Gaussian i is finite and at most 1e30 in magnitude.  Every
-// real SH basis value of degree <= 3 on the unit sphere is below 1 in magnitude, so the colour
-// sum of at most 48 such terms then stays below 5e31 at every step of its evaluation: it is
-// finite, and the colour cannot cull the Gaussian in any view.
-template <int NK3>
-__device__ __forceinline__ bool sh_bounded(const ProjectArgs& a, int i) {
-    // bitwise and, unrolled: the loads are issued together (a short-circuit chain would
-    // serialize them); a NaN compares false
-    bool ok = true;
-#pragma unroll 16
-    for (int k = 0; k < NK3; k++) ok &= fabsf(a.sh[(size_t)k * a.n + i]) <= 1e30f;
-    return ok;
-}
-
 // All per-view tests except the colour's finiteness, and the record without the colour.  Also
 // returns the unit viewing direction.  Returns visibility so far.
 __device__ bool project_geom(const ProjectArgs& a, const Geo& g, const CamDev& c, Rec& r, float3& dir) {
@@ -180,25 +166,12 @@ __device__ bool project_geom(const ProjectArgs& a, const Geo& g, const CamDev& c
     return true;
 }
 
-// Whether the colour of Gaussian i along dir is finite (the rare case of unbounded
-// coefficients; kept out of line so that it does not hold registers in the counting loop).
-template <int DEG>
-__device__ __noinline__ bool colour_finite(const ProjectArgs& a, int i, float3 dir) {
-    constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
-    float Y[15];
-    sh_basis(DEG, dir.x, dir.y, dir.z, Y);
-    const float3 col = sh_eval(a.sh + i, a.n, NY, Y);
-    return finitef(col.x) && finitef(col.y) && finitef(col.z);
-}
-
 __device__ __forceinline__ int wave_sum_i(int x) {
     for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
 }
 
-template <int DEG>
 __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
-    constexpr int NY = DEG == 0 ? 0 : (DEG == 1 ? 3 : (DEG == 2 ? 8 : 15));
     const int i = blockIdx.x * kBlock + threadIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t nw = project_waves(a.n);
@@ -227,9 +200,7 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
     Geo g;
     g.ok = false;
     if (vmask) g = load_geo_rest(a, i, wx, wy, wz);
-    // the coefficients are checked at the first view that sees the Gaussian: most Gaussians of a
-    // large scene are outside every view and their 192 bytes are never read
-    bool bounded = true, checked = false, seen = false;
+    bool seen = false;
     // visible depth range of this thread over all views, as float32 bit patterns (depths are
     // above znear > 0, so the patterns order like the values)
     uint32_t dlo = 0xFFFFFFFFu, dhi = 0u;
@@ -237,13 +208,7 @@ __global__ __launch_bounds__(kBlock) void project_count_kernel(ProjectArgs a) {
         Rec r;
         r.ntiles = 0;
         float3 dir;
-        bool vis = ((vmask >> v) & 1u) && project_geom(a, g, a.cams.c[v], r, dir);
-        if (vis && !checked) {
-            bounded = sh_bounded<3 * (NY + 1)>(a, i);
-            checked = true;
-        }
-        // some coefficient is huge or not finite: the colour itself decides
-        if (vis && !bounded) vis = colour_finite<DEG>(a, i, dir);
+        const bool vis = ((vmask >> v) & 1u) && project_geom(a, g, a.cams.c[v], r, dir);
         seen |= vis;
         if (vis) {
             dlo = min(dlo, __float_as_uint(r.depth));
@@ -315,8 +280,12 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
                 col.y = fmaf(coef[3 * (k + 1) + 1], Y[k], col.y);
                 col.z = fmaf(coef[3 * (k + 1) + 2], Y[k], col.z);
             }
-            vis = finitef(col.x) && finitef(col.y) && finitef(col.z);
             r.rgb = make_float3(fmaxf(0.0f, col.x), fmaxf(0.0f, col.y), fmaxf(0.0f, col.z));
+            if (!(finitef(col.x) && finitef(col.y) && finitef(col.z))) {
+                // no colour: kept in the view, transparent (nothing ever blends it)
+                r.rgb = make_float3(0.0f, 0.0f, 0.0f);
+                r.co.w = 0.0f;
+            }
         }
         const unsigned long long m = __ballot(vis);
         // inclusive scan of the tile counts over the wave
@@ -468,12 +437,7 @@ hipError_t launch_project_count(const ProjectArgs& a0, hipStream_t s) {
     ProjectArgs a = a0;
     const int32_t nb = project_blocks(a.n > 0 ? a.n : 1);
     const int32_t nw = project_waves(a.n);
-    switch (a.p.sh_degree) {
-        case 0: hipLaunchKernelGGL(project_count_kernel<0>, dim3(nb), dim3(kBlock), 0, s, a); break;
-        case 1: hipLaunchKernelGGL(project_count_kernel<1>, dim3(nb), dim3(kBlock), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(project_count_kernel<2>, dim3(nb), dim3(kBlock), 0, s, a); break;
-        default: hipLaunchKernelGGL(project_count_kernel<3>, dim3(nb), dim3(kBlock), 0, s, a); break;
-    }
+    hipLaunchKernelGGL(project_count_kernel, dim3(nb), dim3(kBlock), 0, s, a);
     hipLaunchKernelGGL(count_partials_kernel, dim3(kParts, a.V + 1), dim3(kSumBlock), 0, s, a.block_counts, a.V, nw,
                        a.block_depth, a.inst_partials, a.depth_partials);
     hipError_t e = launch_scan_rows(a.block_counts, a.block_offsets, a.row_totals, nw, 2 * a.V, a.scan_partials, s);

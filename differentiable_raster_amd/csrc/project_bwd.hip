@@ -87,9 +87,26 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
         }
         s_slot[v][threadIdx.x] = (lo < kBlock && s_win[v][lo] == i) ? s_lo[v] + lo : -1;
     }
+    const int64_t nn = n;
+    {
+        // a Gaussian that no view sees gets zero gradients, without reading its parameters (they
+        // may be anything, non-finite included; in a large scene most Gaussians are such)
+        bool seen = false;
+        for (int v = 0; v < a.V; v++) seen |= s_slot[v][threadIdx.x] >= 0;
+        if (!seen) {
+            for (int k = 0; k < 3; k++) {
+                a.g_means[k * nn + i] = 0.0f;
+                a.g_log_scales[k * nn + i] = 0.0f;
+            }
+            for (int k = 0; k < 4; k++) a.g_quats[k * nn + i] = 0.0f;
+            a.g_logits[i] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 3 * NK; k++) a.g_sh[k * nn + i] = 0.0f;
+            return;
+        }
+    }
 
     // 2. per-Gaussian frame, as the forward projection computes it
-    const int64_t nn = n;
     const float mx = a.means[i], my = a.means[nn + i], mz = a.means[2 * nn + i];
     const GaussFrame f = gauss_frame(a.log_scales[i], a.log_scales[nn + i], a.log_scales[2 * nn + i], a.quats[i],
                                      a.quats[nn + i], a.quats[2 * nn + i], a.quats[3 * nn + i], a.logits[i], true);
@@ -195,7 +212,10 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
             view_dir(mx, my, mz, c.campos, &dx, &dy, &dz, &idn);
             float Y[15];
             sh_basis(DEG, dx, dy, dz, Y);
-            if (!(sh_eval_channel(coef, NY, Y) > 0.0f)) continue;
+            // clamped at zero, or not finite (the view then holds the Gaussian transparent and
+            // its 2D gradients are zero; a non-finite coefficient times zero would not be)
+            const float val = sh_eval_channel(coef, NY, Y);
+            if (!(val > 0.0f) || !isfinite(val)) continue;
             const float g = a.d_color[3 * idx + ch];
             gsh[0] += g;
             if (NY > 0) {

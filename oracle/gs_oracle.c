@@ -289,9 +289,16 @@ static int project_one(const double mu[3], const double ls[3], const double q_in
         double v = shc[0 * 3 + ch];
         for (int k = 1; k < nk; k++) v += shc[k * 3 + ch] * Y[k];
         if (!isfinite(v)) col_ok = 0;
+        /* finite here but past float32's range (about 3.4e38): a float32 evaluation overflows */
+        else if (fabs(v) > 1e38) flag[i] = 1;
         col[ch] = v > 0.0 ? v : 0.0;
     }
-    if (!col_ok) return 0;
+    /* no finite colour: the Gaussian stays in the view, transparent (opacity 0, colour 0) */
+    double o_view = o;
+    if (!col_ok) {
+        o_view = 0.0;
+        col[0] = col[1] = col[2] = 0.0;
+    }
 
     /* 8. outputs */
     const int tile = p->tile;
@@ -305,7 +312,7 @@ static int project_one(const double mu[3], const double ls[3], const double q_in
     conic[3 * i] = A;
     conic[3 * i + 1] = B;
     conic[3 * i + 2] = C;
-    opacity[i] = o;
+    opacity[i] = o_view;
     for (int ch = 0; ch < 3; ch++) color[3 * i + ch] = col[ch];
     depth[i] = tz;
     rect[4 * i + 0] = tx0;
@@ -327,7 +334,9 @@ static int project_one(const double mu[3], const double ls[3], const double q_in
  *   conic[i][3] = (A, B, C) with q = A dx^2 + 2 B dx dy + C dy^2, opacity[i], color[i][3],
  *   depth[i] = camera-space z, rect[i][4] = (tx0, ty0, tx1, ty1) inclusive tile rectangle
  *   (int32), n_tiles[i] (int32), flag[i] = 1 when a visibility or box decision lies so close
- *   to its threshold that float32 arithmetic may decide it the other way.
+ *   to its threshold that float32 arithmetic may decide it the other way (or a colour channel is
+ *   finite but past float32's range).  The colour never decides visibility: where it is not
+ *   finite the Gaussian is visible and transparent (opacity[i] = 0, colour 0).
  */
 void orc_project(int64_t n, const float* means, const float* log_scales, const float* quats,
                  const float* opacity_logits, const float* sh, const orc_camera* cam,
@@ -530,7 +539,9 @@ void orc_project_backward(int64_t n, const double* means, const double* log_scal
                 mag += fabs(shc[(size_t)k * 3 * n] * Y[k]);
             }
             if (fabs(v) <= 1e-5 * mag) flag[i] = 1;
-            if (!(v > 0.0)) continue;
+            /* clamped at zero; or not finite, where the view holds the Gaussian transparent and
+             * its 2D gradients are zero */
+            if (!(v > 0.0) || !isfinite(v)) continue;
             const double g = g_color[3 * i + ch];
             d_sh[(size_t)ch * n + i] += g;
             for (int k = 1; k < nk; k++) {

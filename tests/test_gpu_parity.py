@@ -378,11 +378,10 @@ def test_packed_records_and_instance_bases(env):
         assert g["inst_count"] == int(g["n_tiles"].sum())
 
 
-def test_coefficients_first_checked_at_a_later_view(env):
+def test_non_finite_colour_in_the_second_view(env):
     """Gaussians that only the second of two views sees, with non-finite, huge-but-finite and
-    ordinary SH coefficients: the projection reads and checks the coefficients at the first view
-    that sees a Gaussian, so the second view's visible set and records must still equal the
-    oracle's, and a Gaussian outside both views must stay out."""
+    ordinary SH coefficients: the second view's visible set and records equal the oracle's (the
+    non-finite ones kept transparent), and a Gaussian outside both views stays out."""
     oracle, pipeline, torch = env
     cam0 = pinhole(64, 48, f=50.0, cx=32.0, cy=24.0)
     # the second camera looks at the same points from 10 units to the side
@@ -410,16 +409,21 @@ def test_coefficients_first_checked_at_a_later_view(env):
     gpu = r.projected_host(1)
     o = oracle.project(sc, cam1, st)
     assert set(gpu["vis_ids"].tolist()) == set(np.nonzero(o["visible"])[0].tolist())
-    assert not {1, 2, 9} & set(gpu["vis_ids"].tolist())
-    assert {0, 3, 4, 5} <= set(gpu["vis_ids"].tolist())
+    assert 9 not in set(gpu["vis_ids"].tolist())
+    assert {0, 1, 2, 3, 4, 5} <= set(gpu["vis_ids"].tolist())
+    slot = {g: s for s, g in enumerate(gpu["vis_ids"].tolist())}
+    for g in (1, 2):  # transparent: opacity 0, colour 0
+        assert gpu["conic_opacity"][slot[g], 3] == 0.0 and not gpu["color"][slot[g]].any()
+    for g in (0, 3, 4, 5):
+        assert gpu["conic_opacity"][slot[g], 3] > 0.0
     parity.compare_projection(oracle, sc, cam1, st, gpu)
 
 
-def test_degenerate_parameters_are_culled_like_the_oracle(env):
-    """Non-finite parameters (mean, scale, quaternion, opacity, SH coefficient) and a zero
-    quaternion cull the Gaussian in every view; a huge but finite SH coefficient (past the bound
-    under which the projection skips evaluating the colour's finiteness) keeps it visible with
-    the colour the oracle computes."""
+def test_degenerate_parameters_like_the_oracle(env):
+    """Non-finite geometric parameters (mean, scale, quaternion, opacity) and a zero quaternion
+    cull the Gaussian in every view; a non-finite SH coefficient keeps it visible and
+    transparent; a huge but finite one keeps it visible with the colour the oracle computes.
+    The projection backward gives the transparent ones zero gradients and no NaN anywhere."""
     oracle, pipeline, torch = env
     cam = pinhole(64, 48, f=50.0, cx=32.0, cy=24.0)
     n = 12
@@ -446,6 +450,16 @@ def test_degenerate_parameters_are_culled_like_the_oracle(env):
     gpu = r.projected_host(0)
     o = oracle.project(sc, cam, st)
     assert set(gpu["vis_ids"].tolist()) == set(np.nonzero(o["visible"])[0].tolist())
-    assert not set(range(7)) & set(gpu["vis_ids"].tolist())
-    assert {7, 8} <= set(gpu["vis_ids"].tolist())
+    assert not set(range(5)) & set(gpu["vis_ids"].tolist())
+    assert {5, 6, 7, 8} <= set(gpu["vis_ids"].tolist())
+    slot = {g: s for s, g in enumerate(gpu["vis_ids"].tolist())}
+    for g in (5, 6):
+        assert gpu["conic_opacity"][slot[g], 3] == 0.0 and not gpu["color"][slot[g]].any()
     parity.compare_projection(oracle, sc, cam, st, gpu)
+    r.project_backward()
+    torch.cuda.synchronize()
+    g3 = r.grads3d_host()
+    for k, v in g3.items():
+        assert np.isfinite(v).all(), k
+        assert not v[..., 5:7].any(), k
+    _project_bwd_check(env, sc, st, r)

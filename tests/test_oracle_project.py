@@ -175,6 +175,54 @@ def test_culling_rules(oracle_mod):
     assert out["n_tiles"][:5].tolist() == [0] * 5
 
 
+def test_non_finite_colour_keeps_the_gaussian_transparent(oracle_mod):
+    """A Gaussian whose SH colour is not finite (a NaN or an infinite coefficient) keeps its
+    slot, 2D geometry and tiles, with opacity 0 and colour 0: the same geometry as with a finite
+    coefficient, a render identical to the one without it, zero projection-backward gradients for
+    it and unchanged gradients for the others."""
+    cam = pinhole(64, 48, f=50.0, cx=32.0, cy=24.0)
+    st = settings(sh_degree=1)
+    means = [[-0.1, 0.0, 2.5], [0.05, 0.02, 2.0], [0.1, -0.05, 2.2], [0.0, 0.1, 3.0]]
+    ls = [[-2.5, -2.9, -2.2], [-2.7, -2.4, -2.6], [-2.3, -2.8, -2.5], [-2.6, -2.2, -2.9]]
+    quats = [[0.95, 0.1, -0.2, 0.1], [0.9, 0.1, 0.2, 0.3], [0.8, -0.2, 0.1, 0.4], [0.9, 0.3, 0.1, -0.2]]
+    logits = [1.0, 0.5, 2.0, 0.8]
+    dc = [[0.5, 0.4, 0.3], [0.2, 0.6, 0.7], [0.9, 0.1, 0.5], [0.3, 0.3, 0.3]]
+    rest = np.full((4, 9), 0.05)
+    bad = rest.copy()
+    bad[1, 4] = np.nan    # Gaussian 1: NaN coefficient
+    bad[2, 7] = np.inf    # Gaussian 2: infinite coefficient
+    rng = np.random.default_rng(2)
+    target = rng.uniform(0, 1, (1, 3, 48, 64))
+    good = scene_from(means, ls, quats, logits, dc, [cam], sh_rest=rest, sh_degree=1, target=target)
+    sick = scene_from(means, ls, quats, logits, dc, [cam], sh_rest=bad, sh_degree=1, target=target)
+    pg, ps = oracle_mod.project(good, cam, st), oracle_mod.project(sick, cam, st)
+    assert pg["visible"].tolist() == [1, 1, 1, 1] and ps["visible"].tolist() == [1, 1, 1, 1]
+    for k in ("mean2d", "conic", "depth", "rect", "n_tiles"):
+        assert np.array_equal(pg[k], ps[k]), k
+    assert ps["opacity"][1] == 0.0 and ps["opacity"][2] == 0.0 and not ps["color"][1:3].any()
+    assert np.array_equal(pg["opacity"][[0, 3]], ps["opacity"][[0, 3]])
+    # the render equals the render of the two healthy Gaussians alone
+    alone = scene_from([means[0], means[3]], [ls[0], ls[3]], [quats[0], quats[3]], [logits[0], logits[3]],
+                       [dc[0], dc[3]], [cam], sh_rest=rest[[0, 3]], sh_degree=1, target=target)
+    r_sick = oracle_mod.iteration(sick, st)[0]
+    r_alone = oracle_mod.iteration(alone, st)[0]
+    assert np.array_equal(r_sick["fwd"]["image"], r_alone["fwd"]["image"])
+    assert r_sick["bins"]["num_instances"] > r_alone["bins"]["num_instances"]  # its tiles are kept
+    # projection backward of the rasterizer's gradients: zero for the transparent ones
+    b = r_sick["bwd"]
+    vis = ps["visible"].astype(bool)
+    g2 = {k: np.zeros((4,) + b[k].shape[1:]) for k in ("d_mean2d", "d_conic", "d_opacity", "d_color")}
+    for k in g2:
+        g2[k][r_sick["rec"]["vis_ids"]] = b[k]
+    params = oracle_mod.scene_params_f64(sick)
+    acc = oracle_mod.project_backward(params, cam, st, vis, g2["d_mean2d"], g2["d_conic"], g2["d_opacity"],
+                                      g2["d_color"])
+    for k in ("d_means", "d_log_scales", "d_quats", "d_opacity_logits", "d_sh"):
+        assert np.isfinite(acc[k]).all(), k
+        assert not acc[k][..., 1:3].any(), k
+        assert acc[k][..., 0].any(), k
+
+
 def test_box_contains_every_pixel_above_alpha_min(oracle_mod):
     """Brute force: every pixel centre with o exp(-q/2) >= alpha_min lies in a tile of the
     rectangle, and the rectangle lies inside the image's tile grid."""
