@@ -217,6 +217,7 @@ gs_status check_partials(const gs_projected* proj, const gs_bins* bins, void* ws
     ra->huge_count = c.take<int32_t>(1);
     ra->huge_slots = c.take<int4>((size_t)huge_slot_cap(bins->count));
     ra->huge_cap = huge_slot_cap(bins->count);
+    ra->loss_acc = c.take<long long>(1);
     return GS_OK;
 }
 

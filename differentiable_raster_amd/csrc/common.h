@@ -199,6 +199,7 @@ struct RasterArgs {
     // records, 0)) for a workgroup each; the raster kernel clears the count
     int4* huge_slots;
     int32_t* huge_count;
+    long long* loss_acc;         // fused call's loss sum in fixed point (workspace)
     int32_t huge_cap;
 };
 constexpr int kHugeSlot = 256;

@@ -687,6 +687,16 @@ __global__ __launch_bounds__(256) void loss_l1_kernel(int64_t n, const float* im
     }
 }
 
+// The fused call's loss sum: an integer accumulator in units of 2^-20, cleared before the
+// kernel and added to the caller's float afterwards.
+constexpr double kLossFix = 1048576.0;
+
+__global__ void loss_acc_clear_kernel(long long* acc) { *acc = 0; }
+
+__global__ void loss_acc_finish_kernel(const long long* acc, float* loss_sum) {
+    *loss_sum += (float)((double)*acc / kLossFix);
+}
+
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
 }
@@ -892,8 +902,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         }
     }
     if (loss_sum && mode == GS_LOSS_L1) {
+        // in fixed point (2^-20): integer sums do not depend on the order of the workgroups
         lsum = wave_sum(lsum);
-        if (c.lane == 0 && lsum != 0.0f) atomicAdd(loss_sum, lsum);
+        if (c.lane == 0 && lsum != 0.0f)
+            atomicAdd(reinterpret_cast<unsigned long long*>(a.loss_acc),
+                      (unsigned long long)(long long)llrint((double)lsum * kLossFix));
     }
     const int maxnc = block_max(s.nc, s_red);
     // every pixel's last blended entry lies in the last staged batch, so it is still resident
@@ -910,7 +923,7 @@ int32_t fused_lds_entries() { return kBatch; }
 size_t raster_ws_bytes(int64_t instances) {
     const auto a256 = [](size_t b) { return (b + 255) & ~size_t(255); };
     return a256(sizeof(float) * 9 * (size_t)instances) + a256(sizeof(int32_t)) +
-           a256(sizeof(int4) * (size_t)huge_slot_cap(instances));
+           a256(sizeof(int4) * (size_t)huge_slot_cap(instances)) + a256(sizeof(long long));
 }
 
 hipError_t launch_raster_fwd(const RasterArgs& a, float* image, float* t_final, int32_t* n_contrib, hipStream_t s) {
@@ -967,10 +980,9 @@ hipError_t launch_raster_bwd(const RasterArgs& a, const float* /*image*/, const 
     });
 }
 
-hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,
-                               float* loss_sum, Grads g, hipStream_t s) {
-    const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
-    const bool bg = a.p.bg[0] != 0.0f || a.p.bg[1] != 0.0f || a.p.bg[2] != 0.0f;
+static hipError_t launch_raster_fused_kernels(const RasterArgs& a, int mode, const float* target_or_dl, float scale,
+                                              float* image, float* loss_sum, Grads g, hipStream_t s,
+                                              unsigned nblocks, bool bg) {
     return with_partials(a, g, s, [&] {
         if (a.counters && bg)
             hipLaunchKernelGGL((raster_fused_kernel<true, true>), dim3(nblocks), dim3(kBlock), 0, s, a, mode,
@@ -985,6 +997,18 @@ hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* targe
             hipLaunchKernelGGL((raster_fused_kernel<false, false>), dim3(nblocks), dim3(kBlock), 0, s, a, mode,
                                target_or_dl, scale, image, loss_sum, g);
     });
+}
+
+hipError_t launch_raster_fused(const RasterArgs& a, int mode, const float* target_or_dl, float scale, float* image,
+                               float* loss_sum, Grads g, hipStream_t s) {
+    const unsigned nblocks = (unsigned)(a.V * a.tiles_x * a.tiles_y);
+    const bool bg = a.p.bg[0] != 0.0f || a.p.bg[1] != 0.0f || a.p.bg[2] != 0.0f;
+    const bool lsum = loss_sum && mode == GS_LOSS_L1;
+    if (lsum) hipLaunchKernelGGL(loss_acc_clear_kernel, dim3(1), dim3(1), 0, s, a.loss_acc);
+    const hipError_t e = launch_raster_fused_kernels(a, mode, target_or_dl, scale, image, loss_sum, g, s, nblocks, bg);
+    if (e != hipSuccess) return e;
+    if (lsum) hipLaunchKernelGGL(loss_acc_finish_kernel, dim3(1), dim3(1), 0, s, a.loss_acc, loss_sum);
+    return hipGetLastError();
 }
 
 }  // namespace gsmi

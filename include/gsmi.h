@@ -242,7 +242,7 @@ size_t gs_project_noalloc_max_bytes(void);
 /* Workspace bytes of gs_raster_bwd / gs_raster_fused for an instance capacity: one float32
  * partial-gradient record (9 values) per (Gaussian, tile) instance, then a short list of the
  * slots with more than 256 instances (16 bytes per 256 instances), whose records one workgroup
- * each adds up. */
+ * each adds up, then the fused call's fixed-point loss sum (8 bytes). */
 size_t gs_raster_workspace_size(int64_t instance_capacity);
 
 /* Workspace bytes of gs_bin_tiles for n Gaussians, V views and an instance capacity. */
@@ -270,8 +270,11 @@ gs_status gs_bin_tiles(const gs_camera* cams /*host [V]*/, const gs_projected* p
                        int64_t* required /*host*/, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * A7: forward rasterization.  One 256-thread workgroup per 16x16 tile and view; records of the
- * tile list are staged in LDS in batches.  Per pixel, front to back:
+ * A7: forward rasterization (ByteSplat, arXiv 2610.02851, English abstract: forward
+ * rasterization, one of the two passes whose repeated off-chip accesses it names as a
+ * bottleneck; the compositing rule is the plain front-to-back reading below, which no page
+ * writes out).  One 256-thread workgroup per 16x16 tile and view; records of the tile list are
+ * staged in LDS in batches.  Per pixel, front to back:
  * alpha = min(alpha_max, o exp(-q/2)); skip alpha < alpha_min; stop before a blend that would
  * take T below t_min; C += alpha T c; T *= (1 - alpha); at the end C += T bg.
  * n_contrib = 1 + list position of the last blended entry (0 if none).  `use_capped` selects
@@ -282,13 +285,16 @@ gs_status gs_raster_fwd(const gs_camera* cams /*host [V]*/, const gs_projected* 
                         float* t_final, int32_t* n_contrib, gs_counters* counters, void* stream);
 
 /* A8: dL/dC of L = scale * sum |C - target| (L1): scale * sign(C - target), sign(0) = 0.
- * image, target, dl_dimage: [V][3][H][W].  loss_sum (optional, device float, accumulated). */
+ * image, target, dl_dimage: [V][3][H][W].  loss_sum (optional, device float, accumulated with
+ * float atomics: its last bits may differ between calls; gs_raster_fused's loss sum does not). */
 gs_status gs_loss_l1_grad(int32_t V, int32_t width, int32_t height, const float* image, const float* target,
                           float scale, float* dl_dimage, float* loss_sum, void* stream);
 
 /*
- * A9: backward rasterization.  Per pixel, back to front from n_contrib: T is recovered by
- * division by (1 - alpha); with Bk the colour behind entry j,
+ * A9: backward rasterization (ByteSplat, arXiv 2610.02851, English abstract: backward
+ * rasterization, the second of the two passes; the derivative is the chain rule of A7's
+ * compositing, which no page writes out).  Per pixel, back to front from n_contrib: T is
+ * recovered by division by (1 - alpha); with Bk the colour behind entry j,
  *   dL/dc_j = alpha_j T_j g,  dL/dalpha_j = sum_ch g_ch (T_j (c_j - Bk) - T_final bg / (1 - alpha_j)),
  * and unless alpha was clamped, dL/do = G dL/dalpha, dL/dmean2d = o G dL/dalpha (A dx + B dy,
  * B dx + C dy) with d = pixel centre - mean2d, dL/d(A,B,C) = o G dL/dalpha (-dx^2/2, -dx dy,
@@ -311,7 +317,8 @@ gs_status gs_raster_bwd(const gs_camera* cams /*host [V]*/, const gs_projected* 
  * the first backward batch.  mode GS_LOSS_L1: target_or_dldc is the target image and the
  * gradient is loss_scale * sign(C - target); GS_LOSS_EXTERNAL: target_or_dldc is dL/dC.
  * image_opt (optional) receives the rendered image; loss_sum_opt (optional, device float)
- * accumulates scale * sum |C - target| (L1 mode only).  Same gradients as A7+A8+A9, gathered the
+ * accumulates scale * sum |C - target| (L1 mode only), summed in fixed point (units of 2^-20
+ * per wavefront's partial) so that repeated calls give identical bits.  Same gradients as A7+A8+A9, gathered the
  * same way (ws as for gs_raster_bwd).
  */
 gs_status gs_raster_fused(const gs_camera* cams /*host [V]*/, const gs_projected* proj, const gs_bins* bins,

@@ -463,3 +463,23 @@ def test_degenerate_parameters_like_the_oracle(env):
         assert np.isfinite(v).all(), k
         assert not v[..., 5:7].any(), k
     _project_bwd_check(env, sc, st, r)
+
+
+def test_fused_loss_sum_repeats_bit_for_bit(env):
+    """The fused call's optional loss sum is summed in fixed point: repeated calls give the same
+    bits, and the value is the L1 sum of the rendered image against the target."""
+    oracle, pipeline, torch = env
+    sc = scenes.random_scene(20000, 320, 240, seed=77, views=3, log_scale_mean=-3.0)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.project()
+    r.bin()
+    sums = []
+    for _ in range(4):
+        r.fused(scale=0.5, image=True, loss_sum=True)
+        torch.cuda.synchronize()
+        sums.append(r.loss_sum.cpu().numpy().copy())
+    assert all(np.array_equal(sums[0], x) for x in sums[1:]), sums
+    img = r.images_host()[0].astype(np.float64)
+    want = 0.5 * np.abs(img - sc.target.astype(np.float64)).sum()
+    assert abs(float(sums[0][0]) - want) <= 1e-5 * want, (float(sums[0][0]), want)
