@@ -11,7 +11,9 @@ constexpr int kBlock = 256;
 constexpr int kItems = 8;
 constexpr int kChunk = kBlock * kItems;
 
-// Exclusive scan of one value per thread across the block; returns the prefix, *total the sum.
+// Exclusive scan of one value per thread across a block of BLOCK threads; returns the prefix,
+// *total the sum.
+template <int BLOCK = kBlock>
 __device__ __forceinline__ int block_exclusive_scan(int x, int* s_wave, int* total) {
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     int inc = x;
@@ -22,7 +24,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* s_wave, int* tot
     if (lane == kWave - 1) s_wave[w] = inc;
     __syncthreads();
     int off = 0, tot = 0;
-    for (int k = 0; k < kBlock / kWave; k++) {
+    for (int k = 0; k < BLOCK / kWave; k++) {
         if (k < w) off += s_wave[k];
         tot += s_wave[k];
     }
@@ -112,17 +114,19 @@ __global__ __launch_bounds__(kBlock) void scan_small_kernel(int32_t* a, int32_t 
     }
 }
 
-// Short rows: one workgroup per row scans it in steps of kBlock * kSmallItems values (one
-// launch instead of three) and writes the row total.
-constexpr int32_t kShortRow = 4 * kBlock * kSmallItems;
+// Short rows: one workgroup of 1024 threads per row scans it in one step of kShortRow values
+// (one launch instead of three, the row's loads all in flight together) and writes the row
+// total.
+constexpr int kShortBlock = 1024;
+constexpr int32_t kShortRow = kShortBlock * kSmallItems;
 
-__global__ __launch_bounds__(kBlock) void scan_rows_short_kernel(const int32_t* in, int32_t* out, int32_t* totals,
-                                                                 int32_t n) {
-    __shared__ int s_wave[kBlock / kWave];
+__global__ __launch_bounds__(kShortBlock) void scan_rows_short_kernel(const int32_t* in, int32_t* out,
+                                                                      int32_t* totals, int32_t n) {
+    __shared__ int s_wave[kShortBlock / kWave];
     const int32_t* r = in + (size_t)blockIdx.x * n;
     int32_t* o = out + (size_t)blockIdx.x * n;
     int carry = 0;
-    for (int32_t b0 = 0; b0 < n; b0 += kBlock * kSmallItems) {
+    for (int32_t b0 = 0; b0 < n; b0 += kShortBlock * kSmallItems) {
         const int32_t first = b0 + threadIdx.x * kSmallItems;
         int v[kSmallItems];
         int sum = 0;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void scan_rows_short_kernel(const int32_t* 
             sum += v[k];
         }
         int tot;
-        int run = carry + block_exclusive_scan(sum, s_wave, &tot);
+        int run = carry + block_exclusive_scan<kShortBlock>(sum, s_wave, &tot);
 #pragma unroll
         for (int k = 0; k < kSmallItems; k++) {
             if (first + k < n) o[first + k] = run;
@@ -154,7 +158,7 @@ size_t scan_partials_bytes(int32_t n, int32_t rows) {
 hipError_t launch_scan_rows(const int32_t* in, int32_t* out, int32_t* totals, int32_t n, int32_t rows,
                             int32_t* partials, hipStream_t s) {
     if (n <= kShortRow) {
-        hipLaunchKernelGGL(scan_rows_short_kernel, dim3(rows), dim3(kBlock), 0, s, in, out, totals, n);
+        hipLaunchKernelGGL(scan_rows_short_kernel, dim3(rows), dim3(kShortBlock), 0, s, in, out, totals, n);
         return hipGetLastError();
     }
     const int32_t nb = scan_blocks(n > 0 ? n : 1);
