@@ -233,10 +233,15 @@ def main():
     torch.cuda.synchronize()
     full_ms = (time.perf_counter() - t0) * 1000.0 / pb_steps
     nk = (scene.sh_degree + 1) ** 2
-    # algorithmic bytes: parameters read once and gradients written once per Gaussian
-    # (4 (10 + 3 nk) B each way), vis_ids (4 B) per visible slot and the 36 B of 2D gradients
-    # per visible slot
-    pb_bytes = 2 * 4 * (10 + 3 * nk) * scene.n + (4 + 36) * sum(vis)
+    # algorithmic bytes: the parameters of each Gaussian some view sees read once, the gradient
+    # row of every Gaussian written once (zeros for the others), 4 (10 + 3 nk) B each, and the
+    # vis_ids entry (4 B) and 36 B of 2D gradients per visible slot
+    seen = torch.zeros(scene.n, dtype=torch.bool, device=r.vis_ids.device)
+    for v in range(r.V):
+        seen[r.vis_ids[v * r.capacity: v * r.capacity + vis[v]].long()] = True
+    n_seen = int(seen.sum().item())
+    del seen
+    pb_bytes = 4 * (10 + 3 * nk) * (n_seen + scene.n) + (4 + 36) * sum(vis)
     log(f"[bench] projection backward: {pb_ms:.3f} ms; full iteration with it: {full_ms:.3f} ms")
 
     # sparse exchange of this iteration's 2D gradient records: the encoder compacts the non-zero
@@ -412,6 +417,7 @@ def main():
             "ms": pb_ms,
             "bound": "hbm",
             "algorithmic_bytes": pb_bytes,
+            "gaussians_seen": n_seen,
             "achieved": pb_bytes / (pb_ms * 1e-3) / 1e9,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
