@@ -242,7 +242,20 @@ def main():
     n_seen = int(seen.sum().item())
     del seen
     pb_bytes = 4 * (10 + 3 * nk) * (n_seen + scene.n) + (4 + 36) * sum(vis)
-    log(f"[bench] projection backward: {pb_ms:.3f} ms; full iteration with it: {full_ms:.3f} ms")
+    # the seen-only form (gs_project_bwd_seen): rows of the seen Gaussians only, plus one flag byte
+    # per Gaussian
+    r.project_backward(seen_only=True)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(pb_steps)]
+    for a, b in ev:
+        a.record()
+        r.project_backward(seen_only=True)
+        b.record()
+    torch.cuda.synchronize()
+    pbs_ms = sum(a.elapsed_time(b) for a, b in ev) / pb_steps
+    pbs_bytes = 2 * 4 * (10 + 3 * nk) * n_seen + scene.n + (4 + 36) * sum(vis)
+    log(f"[bench] projection backward: {pb_ms:.3f} ms (seen rows only: {pbs_ms:.3f} ms); "
+        f"full iteration with it: {full_ms:.3f} ms")
 
     # sparse exchange of this iteration's 2D gradient records: the encoder compacts the non-zero
     # (view, slot) records, the decoder adds them into per-view owner arrays indexed by Gaussian
@@ -308,16 +321,19 @@ def main():
     grads3 = [r.d_means3, r.d_log_scales3, r.d_quats3, r.d_logits3, r.d_sh3]
     zero_rows = int(sum((g.view(k, scene.n) != 0).any(0).logical_not().int() for g, k in zip(grads3, rows))
                     .eq(len(rows)).sum().item())
+    r.project_backward(seen_only=True)  # the seen flags of this iteration
+    torch.cuda.synchronize()
     adam_ms = {}
-    for kind in ("dense", "deferred"):
+    for kind in ("dense", "deferred", "seen"):
         params = [t.clone() for t in (r.means, r.log_scales, r.quats, r.logits, r.sh)]
-        st = adam_mod.AdamState(scene.n, list(zip(params, grads3, rows, lrs)), deferred=kind == "deferred")
-        st.step()
+        st = adam_mod.AdamState(scene.n, list(zip(params, grads3, rows, lrs)), deferred=kind != "dense")
+        seen_arg = r.seen if kind == "seen" else None
+        st.step(seen=seen_arg)
         torch.cuda.synchronize()
         ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(sp_steps)]
         for a, b in ev_a:
             a.record()
-            st.step()
+            st.step(seen=seen_arg)
             b.record()
         torch.cuda.synchronize()
         adam_ms[kind] = sum(a.elapsed_time(b) for a, b in ev_a) / sp_steps
@@ -329,8 +345,12 @@ def main():
     # for the updated ones)
     dense_bytes = 28 * comps * scene.n
     lazy_bytes = 28 * comps * (scene.n - zero_rows) + 4 * comps * zero_rows + 4 * scene.n + 4 * (scene.n - zero_rows)
+    # with seen flags: one flag byte per Gaussian, and the step counter read and written and the
+    # 28 B per component for each seen one
+    seen_bytes = 28 * comps * n_seen + scene.n + 8 * n_seen
     log(f"[bench] Adam: dense {adam_ms['dense']:.3f} ms, deferred {adam_ms['deferred']:.3f} ms "
-        f"({zero_rows} of {scene.n} Gaussians without gradient)")
+        f"({zero_rows} of {scene.n} Gaussians without gradient), deferred with seen flags "
+        f"{adam_ms['seen']:.3f} ms ({n_seen} seen)")
 
     flops = FLOPS_PER_ALPHA_PAIR * E_alpha + FLOPS_PER_BLEND * B
     achieved = flops / (raster_fused_ms * 1e-3) / 1e12
@@ -411,6 +431,10 @@ def main():
             "deferred": {"ms": adam_ms["deferred"], "algorithmic_bytes": lazy_bytes,
                          "achieved": lazy_bytes / (adam_ms["deferred"] * 1e-3) / 1e9,
                          "frac": lazy_bytes / (adam_ms["deferred"] * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+            "deferred_seen": {"kernel": "adam_step_kernel (gs_adam_step_seen)", "ms": adam_ms["seen"],
+                              "gaussians_seen": n_seen, "algorithmic_bytes": seen_bytes,
+                              "achieved": seen_bytes / (adam_ms["seen"] * 1e-3) / 1e9,
+                              "frac": seen_bytes / (adam_ms["seen"] * 1e-3) / (HBM_PEAK_GBS * 1e9)},
         },
         "project_bwd": {
             "kernel": "project_bwd_kernel (gs_project_bwd)",
@@ -423,6 +447,13 @@ def main():
             "unit": "GB/s",
             "frac": pb_bytes / (pb_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "full_iteration_ms": full_ms,
+            "seen_only": {"kernel": "project_bwd_kernel (gs_project_bwd_seen)", "ms": pbs_ms,
+                          "algorithmic_bytes": pbs_bytes,
+                          "achieved": pbs_bytes / (pbs_ms * 1e-3) / 1e9,
+                          "frac": pbs_bytes / (pbs_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+            # one training step with frustum culling and deferred updates: the fused iteration,
+            # the seen-only projection backward and the seen-flag Adam step
+            "training_step_ms": med_fused + pbs_ms + adam_ms["seen"],
         },
     }
     if not args.no_cpu_baseline:

@@ -24,9 +24,16 @@ class AdamState:
         self.last_step = torch.zeros(max(1, n), dtype=torch.int32, device=dev) if deferred else None
         self.t = 0
 
-    def step(self, active=None):
-        """One step; with a deferred state and `active` (device int32 ids), only those Gaussians."""
+    def step(self, active=None, seen=None):
+        """One step; with a deferred state and `active` (device int32 ids), only those Gaussians, or
+        with `seen` (device uint8 [n] flags, as gs_project_bwd_seen writes them), only the flagged
+        ones."""
         self.t += 1
+        if seen is not None:
+            if self.last_step is None:
+                raise ValueError("seen flags need a deferred state")
+            gsmi.gs_adam_step_seen(self.n, self.groups, self.hp, self.t, self.last_step, seen)
+            return
         gsmi.gs_adam_step(self.n, self.groups, self.hp, self.t, self.last_step, active,
                           0 if active is None else active.numel())
 

@@ -7,7 +7,8 @@
 // then takes the current step.  The replay performs the same float32 operations in the same order
 // as the dense form would have, so the parameters and moments after a flush are bit-identical to
 // the dense ones; only the memory traffic of the skipped Gaussians is saved (their gradient row
-// is read, or not even that when the caller passes the list of Gaussians to update).
+// is read, or not even that when the caller names the Gaussians to update, by a list or by
+// per-Gaussian seen flags).
 //
 // One thread per Gaussian: the rows of a group are read and written one after the other at the
 // Gaussian's column, so a wavefront touches 64 consecutive floats of each row.
@@ -61,10 +62,10 @@ __device__ __forceinline__ bool grad_row_zero(const AdamArgs& a, int64_t n, int6
 }
 
 // mode 0: dense (every Gaussian, step t); 1: deferred over all Gaussians (zero rows skipped);
-// 2: deferred over the listed Gaussians.
+// 2: deferred over the listed Gaussians; 3: deferred over the Gaussians whose seen flag is set.
 __global__ __launch_bounds__(kBlock) void adam_step_kernel(AdamArgs a, int64_t n, int32_t t, int mode,
                                                            int32_t* last_step, const int32_t* active,
-                                                           int64_t n_items) {
+                                                           const uint8_t* seen, int64_t n_items) {
     const float bc1 = bias_correction(a.h.beta1, t), bc2 = bias_correction(a.h.beta2, t);
     for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < n_items; k += (int64_t)gridDim.x * kBlock) {
         int64_t i = k;
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(kBlock) void adam_step_kernel(AdamArgs a, int64_t n
             advance(a, n, i, t, t, true, bc1, bc2);
             continue;
         }
+        if (mode == 3 && seen[i] == 0) continue;  // gradient zero by the caller's contract, not read
         const int32_t last = last_step[i];
         if (last >= t) continue;  // already current
         if (mode == 1 && grad_row_zero(a, n, i)) continue;
@@ -110,7 +112,15 @@ hipError_t launch_adam_step(const AdamArgs& a, int64_t n, int32_t t, int32_t* la
     const int64_t items = mode == 2 ? n_active : n;
     if (items <= 0) return hipSuccess;
     hipLaunchKernelGGL(adam_step_kernel, dim3(blocks_for(items)), dim3(kBlock), 0, s, a, n, t, mode, last_step,
-                       active, items);
+                       active, nullptr, items);
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_step_seen(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, const uint8_t* seen,
+                                 hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(adam_step_kernel, dim3(blocks_for(n)), dim3(kBlock), 0, s, a, n, t, 3, last_step, nullptr,
+                       seen, n);
     return hipGetLastError();
 }
 

@@ -420,9 +420,9 @@ gs_status gs_project_noalloc(const gs_gaussians* g, const gs_camera* cams, int32
     return gs_project(g, cams, V, p, out, ws, kNoAllocScratchBytes, stream);
 }
 
-gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
-                         const gs_projected* proj, const gs_grads2d* grads2d, gs_grads3d* out, void* stream) {
-    g_last_error.clear();
+static gs_status project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
+                             const gs_projected* proj, const gs_grads2d* grads2d, gs_grads3d* out, uint8_t* seen_out,
+                             void* stream, const char* what) {
     if (!g) return fail(GS_ERR_INVALID_ARGUMENT, "gaussians is null");
     gs_status st = check_cams(cams, V);
     if (st != GS_OK) return st;
@@ -461,7 +461,22 @@ gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V
     a.g_quats = out->d_quats;
     a.g_logits = out->d_opacity_logits;
     a.g_sh = out->d_sh;
-    return hip_check(launch_project_bwd(a, static_cast<hipStream_t>(stream)), "gs_project_bwd launch");
+    a.seen_out = seen_out;
+    return hip_check(launch_project_bwd(a, static_cast<hipStream_t>(stream)), what);
+}
+
+gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
+                         const gs_projected* proj, const gs_grads2d* grads2d, gs_grads3d* out, void* stream) {
+    g_last_error.clear();
+    return project_bwd(g, cams, V, p, proj, grads2d, out, nullptr, stream, "gs_project_bwd launch");
+}
+
+gs_status gs_project_bwd_seen(const gs_gaussians* g, const gs_camera* cams, int32_t V, const gs_render_params* p,
+                              const gs_projected* proj, const gs_grads2d* grads2d, gs_grads3d* out, uint8_t* seen,
+                              void* stream) {
+    g_last_error.clear();
+    if (!seen && g && g->n > 0) return fail(GS_ERR_INVALID_ARGUMENT, "seen is null");
+    return project_bwd(g, cams, V, p, proj, grads2d, out, seen, stream, "gs_project_bwd_seen launch");
 }
 
 size_t gs_raster_workspace_size(int64_t instance_capacity) {
@@ -860,6 +875,17 @@ gs_status gs_adam_step(int32_t n, const gs_adam_group* groups, int32_t n_groups,
     return hip_check(launch_adam_step(a, n, t, last_step, last_step ? active : nullptr, n_active,
                                       static_cast<hipStream_t>(stream)),
                      "gs_adam_step launch");
+}
+
+gs_status gs_adam_step_seen(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
+                            int32_t t, int32_t* last_step, const uint8_t* seen, void* stream) {
+    g_last_error.clear();
+    AdamArgs a;
+    gs_status st = adam_args(n, groups, n_groups, hp, t, &a);
+    if (st != GS_OK) return st;
+    if (n > 0 && (!last_step || !seen)) return fail(GS_ERR_INVALID_ARGUMENT, "last_step or seen is null");
+    return hip_check(launch_adam_step_seen(a, n, t, last_step, seen, static_cast<hipStream_t>(stream)),
+                     "gs_adam_step_seen launch");
 }
 
 gs_status gs_adam_flush(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,

@@ -123,6 +123,9 @@ struct ProjectBwdArgs {
     const float* d_opacity;
     const float* d_color;
     float *g_means, *g_log_scales, *g_quats, *g_logits, *g_sh;
+    // null: every gradient row is written (zeros for Gaussians no view sees); otherwise
+    // seen_out[i] = 1 for a Gaussian some view sees, 0 for the others, whose rows are not written
+    uint8_t* seen_out;
 };
 hipError_t launch_project_bwd(const ProjectBwdArgs& a, hipStream_t s);
 
@@ -272,6 +275,10 @@ struct AdamArgs {
 };
 hipError_t launch_adam_step(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, const int32_t* active,
                             int64_t n_active, hipStream_t s);
+// Deferred step whose candidates are the Gaussians with seen[i] != 0 (the others' gradient rows
+// are not read).
+hipError_t launch_adam_step_seen(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, const uint8_t* seen,
+                                 hipStream_t s);
 hipError_t launch_adam_flush(const AdamArgs& a, int64_t n, int32_t t, int32_t* last_step, hipStream_t s);
 int32_t fused_lds_entries();
 

@@ -90,9 +90,14 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
     const int64_t nn = n;
     {
         // a Gaussian that no view sees gets zero gradients, without reading its parameters (they
-        // may be anything, non-finite included; in a large scene most Gaussians are such)
+        // may be anything, non-finite included; in a large scene most Gaussians are such); with
+        // seen flags requested, its rows are not written either
         bool seen = false;
         for (int v = 0; v < a.V; v++) seen |= s_slot[v][threadIdx.x] >= 0;
+        if (a.seen_out) {
+            a.seen_out[i] = seen ? 1 : 0;
+            if (!seen) return;
+        }
         if (!seen) {
             for (int k = 0; k < 3; k++) {
                 a.g_means[k * nn + i] = 0.0f;

@@ -119,6 +119,9 @@ _SIGS = {
     "gs_raster_workspace_size": (ctypes.c_size_t, [ctypes.c_int64]),
     "gs_project_bwd": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
                                       _P(gs_projected), _P(gs_grads2d), _P(gs_grads3d), ctypes.c_void_p]),
+    "gs_project_bwd_seen": (ctypes.c_int, [_P(gs_gaussians), _P(gs_camera), ctypes.c_int32, _P(gs_render_params),
+                                           _P(gs_projected), _P(gs_grads2d), _P(gs_grads3d), ctypes.c_void_p,
+                                           ctypes.c_void_p]),
     "gs_fused_max_cap": (ctypes.c_int, [_P(ctypes.c_int32)]),
     "gs_check_bins": (ctypes.c_int, [_P(gs_camera), _P(gs_projected), ctypes.c_int32, _P(gs_render_params),
                                      _P(gs_bins), _P(ctypes.c_int64), ctypes.c_void_p]),
@@ -134,6 +137,8 @@ _SIGS = {
     "gs_adam_step": (ctypes.c_int, [ctypes.c_int32, _P(gs_adam_group), ctypes.c_int32, _P(gs_adam_params),
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_void_p]),
+    "gs_adam_step_seen": (ctypes.c_int, [ctypes.c_int32, _P(gs_adam_group), ctypes.c_int32, _P(gs_adam_params),
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "gs_adam_flush": (ctypes.c_int, [ctypes.c_int32, _P(gs_adam_group), ctypes.c_int32, _P(gs_adam_params),
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
 }
@@ -278,6 +283,14 @@ def gs_project_bwd(g: gs_gaussians, cams, V: int, params: gs_render_params, proj
                                  ctypes.byref(grads2d), ctypes.byref(out), _stream(stream)), "gs_project_bwd")
 
 
+def gs_project_bwd_seen(g: gs_gaussians, cams, V: int, params: gs_render_params, proj: gs_projected,
+                        grads2d: gs_grads2d, out: gs_grads3d, seen, stream=None):
+    """seen: device uint8 [n], written."""
+    _check(load().gs_project_bwd_seen(ctypes.byref(g), cams, V, ctypes.byref(params), ctypes.byref(proj),
+                                      ctypes.byref(grads2d), ctypes.byref(out), _ptr(seen), _stream(stream)),
+           "gs_project_bwd_seen")
+
+
 def gs_bin_tiles(cams, proj: gs_projected, V: int, params: gs_render_params, bins: gs_bins, ws, stream=None):
     """Returns (status, gs_bin_info, required); raises on any error except GS_ERR_CAPACITY."""
     info = gs_bin_info()
@@ -347,6 +360,12 @@ def gs_adam_step(n, groups, hp: gs_adam_params, t, last_step=None, active=None, 
     """groups: a ctypes array of gs_adam_group."""
     _check(load().gs_adam_step(n, groups, len(groups), ctypes.byref(hp), int(t), _ptr(last_step), _ptr(active),
                                int(n_active), _stream(stream)), "gs_adam_step")
+
+
+def gs_adam_step_seen(n, groups, hp: gs_adam_params, t, last_step, seen, stream=None):
+    """Deferred step over the Gaussians whose seen flag (device uint8 [n]) is set."""
+    _check(load().gs_adam_step_seen(n, groups, len(groups), ctypes.byref(hp), int(t), _ptr(last_step), _ptr(seen),
+                                    _stream(stream)), "gs_adam_step_seen")
 
 
 def gs_adam_flush(n, groups, hp: gs_adam_params, t, last_step, stream=None):

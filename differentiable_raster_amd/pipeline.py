@@ -161,8 +161,10 @@ class Renderer:
                              scale, self.image if image else None, self.loss_sum if loss_sum else None, self.grads,
                              self.ws_raster, self.counters if counters else None)
 
-    def project_backward(self):
-        """Chain the per-slot 2D gradients of all views to the parameters (gs_project_bwd)."""
+    def project_backward(self, seen_only: bool = False):
+        """Chain the per-slot 2D gradients of all views to the parameters (gs_project_bwd); with
+        seen_only, gs_project_bwd_seen: rows of Gaussians no view sees are left as they are and
+        self.seen flags the others."""
         if not hasattr(self, "g3"):
             dev, f32, n = self.device, torch.float32, max(1, self.n)
             nk = self.sh.shape[0]
@@ -173,6 +175,12 @@ class Renderer:
             self.d_sh3 = torch.empty(nk * n, dtype=f32, device=dev)
             self.g3 = gsmi.gs_grads3d(self.d_means3.data_ptr(), self.d_log_scales3.data_ptr(),
                                       self.d_quats3.data_ptr(), self.d_logits3.data_ptr(), self.d_sh3.data_ptr())
+        if seen_only:
+            if not hasattr(self, "seen"):
+                self.seen = torch.empty(max(1, self.n), dtype=torch.uint8, device=self.device)
+            gsmi.gs_project_bwd_seen(self.g, self.cams, self.V, self.params, self.proj, self.grads, self.g3,
+                                     self.seen)
+            return
         gsmi.gs_project_bwd(self.g, self.cams, self.V, self.params, self.proj, self.grads, self.g3)
 
     def iteration(self, mode: str = "fused", scale: float = 1.0, image: bool = False, project_bwd: bool = False):

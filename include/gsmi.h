@@ -349,6 +349,20 @@ gs_status gs_project_bwd(const gs_gaussians* g, const gs_camera* cams /*host [V]
                          gs_grads3d* out, void* stream);
 
 /*
+ * gs_project_bwd for training with frustum culling and deferred updates (GS-Scale, arXiv
+ * 2509.15645, English abstract: frustum culling and a deferred optimizer update keep the
+ * Gaussians outside the views from costing memory traffic): the same gradients for every
+ * Gaussian that some view sees, but the gradient rows of the others are neither read nor written
+ * (they keep whatever they held); seen (device uint8 [n], written) is 1 for a Gaussian that some
+ * view's visible set holds and 0 otherwise, the flags gs_adam_step_seen takes.  The rows written
+ * are bit-identical to gs_project_bwd's.  Errors: those of gs_project_bwd, and
+ * GS_ERR_INVALID_ARGUMENT for a null seen with n > 0.
+ */
+gs_status gs_project_bwd_seen(const gs_gaussians* g, const gs_camera* cams /*host [V]*/, int32_t V,
+                              const gs_render_params* p, const gs_projected* proj, const gs_grads2d* grads2d,
+                              gs_grads3d* out, uint8_t* seen, void* stream);
+
+/*
  * GS_CHECK, a debug aid: validates on the device what gs_bin_tiles wrote for `proj`, `V` views
  * and params `p` (the full lists, and the capped ones too when p->tile_cap > 0), against the
  * properties the (view, tile, depth, slot) order fixes.  violations (host [GS_CHECK_KINDS]) receives
@@ -483,6 +497,19 @@ typedef struct {
  */
 gs_status gs_adam_step(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
                        int32_t t, int32_t* last_step, const int32_t* active, int32_t n_active, void* stream);
+
+/*
+ * F4, deferred, with the Gaussians to update named by flags (GS-Scale, English abstract, as for
+ * gs_adam_step): the candidates are the Gaussians with seen[i] != 0 (device uint8 [n], as
+ * gs_project_bwd_seen writes it), each updated as in gs_adam_step's deferred form even if its
+ * gradient is zero; a Gaussian with seen[i] == 0 is left untouched and its gradient rows are not
+ * read (the caller guarantees its gradient is zero at step t, which holds for a Gaussian no view
+ * sees).  last_step (device int32 [n]) as for gs_adam_step; after gs_adam_flush(t) the parameters
+ * and moments equal those of t dense steps bit for bit.  Errors: those of gs_adam_step, and
+ * GS_ERR_INVALID_ARGUMENT for a null last_step or seen with n > 0.
+ */
+gs_status gs_adam_step_seen(int32_t n, const gs_adam_group* groups, int32_t n_groups, const gs_adam_params* hp,
+                            int32_t t, int32_t* last_step, const uint8_t* seen, void* stream);
 
 /* F4: bring every Gaussian of a deferred state to step t (replay of its steps after last_step
  * with a zero gradient; last_step becomes t).  Same arguments as gs_adam_step. */

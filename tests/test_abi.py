@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ["gs_project", "gs_bin_tiles", "gs_raster_fwd", "gs_raster_bwd", "gs_raster_fused",
                  "gs_fused_max_cap", "gs_loss_l1_grad", "gs_project_workspace_size", "gs_bin_workspace_size",
-                 "gs_project_bwd", "gs_raster_workspace_size", "gs_grad_encode", "gs_grad_decode",
+                 "gs_project_bwd", "gs_project_bwd_seen", "gs_adam_step_seen", "gs_raster_workspace_size", "gs_grad_encode", "gs_grad_decode",
                  "gs_grad_encode_workspace_size", "gs_compose", "gs_adam_step", "gs_adam_flush",
                  "gs_version", "gs_status_string", "gs_last_error", "gs_readback_create", "gs_readback_destroy"]:
         assert must in names, must
@@ -110,6 +110,13 @@ def test_project_bwd_rejects_bad_arguments(gs):
     assert b"null" in lib.gs_last_error()
     g_null = gs.gs_gaussians(100, FAKE, FAKE, None, FAKE, FAKE)
     assert call(ctypes.byref(g_null), 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2), ctypes.byref(g3)) == 1
+    # the seen-flag variant: the same checks, and the flags must be given
+    seen = lambda g_, s: lib.gs_project_bwd_seen(g_, c, 1, ctypes.byref(p), ctypes.byref(pr), ctypes.byref(g2),
+                                                 ctypes.byref(g3), s, None)
+    assert seen(ctypes.byref(g), None) == 1
+    assert b"seen" in lib.gs_last_error()
+    assert seen(ctypes.byref(g_null), FAKE) == 1
+    assert seen(None, FAKE) == 1
 
 
 def test_grad_codec_rejects_bad_arguments(gs):
@@ -171,6 +178,11 @@ def test_adam_rejects_bad_arguments(gs):
     assert step(10, (gs.gs_adam_group * 1)(grp(lr=float("inf"))), 1, ctypes.byref(hp), 1) == 1
     assert step(10, groups, 2, ctypes.byref(hp), 1, FAKE, FAKE, -1) == 1
     assert lib.gs_adam_flush(10, groups, 2, ctypes.byref(hp), 1, None, None) == 1
+    step_seen = lambda n, last, seen, t=1: lib.gs_adam_step_seen(n, groups, 2, ctypes.byref(hp), t, last, seen, None)
+    assert step_seen(10, None, FAKE) == 1
+    assert step_seen(10, FAKE, None) == 1
+    assert step_seen(-1, FAKE, FAKE) == 1
+    assert step_seen(10, FAKE, FAKE, t=0) == 1
 
 
 def test_project_rejects_bad_arguments(gs):

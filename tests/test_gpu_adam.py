@@ -52,6 +52,18 @@ def _run(torch, adam, params, seq, mode):
             # the Gaussians with a gradient, plus some without: listing them too changes nothing
             extra = np.arange(0, params[0].shape[1], 7, dtype=np.int32)
             st.step(torch.from_numpy(np.union1d(ids, extra).astype(np.int32)).cuda())
+        elif mode == "seen":
+            # flags on the Gaussians with a gradient and some without; the gradient rows of the
+            # unflagged ones hold NaN, which the step must not read
+            n = params[0].shape[1]
+            flag = np.zeros(n, np.uint8)
+            flag[ids] = 1
+            flag[::7] = 1
+            for dst, src in zip(g, gs):
+                h = src.copy()
+                h[:, flag == 0] = np.nan
+                dst.copy_(torch.from_numpy(h.reshape(-1)))
+            st.step(seen=torch.from_numpy(flag).cuda())
         else:
             st.step()
     st.flush()
@@ -78,7 +90,7 @@ def test_dense_adam_matches_the_oracle(env, n):
         assert np.abs(v[k] - rv[k]).max() <= 1e-5 * np.abs(rv[k]).max(), k
 
 
-@pytest.mark.parametrize("mode", ["deferred", "active"])
+@pytest.mark.parametrize("mode", ["deferred", "active", "seen"])
 def test_deferred_adam_equals_dense_bit_for_bit(env, mode):
     oracle, torch, adam = env
     n = 3000

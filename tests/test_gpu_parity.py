@@ -352,6 +352,47 @@ def test_project_backward_random_gradients_and_culled_view(env):
     _project_bwd_check(env, sc, st, r)
 
 
+def test_project_backward_seen_only(env):
+    """gs_project_bwd_seen: the seen flags are the union of the oracle's per-view visibility, the
+    rows of seen Gaussians equal gs_project_bwd's bit for bit (which the oracle checks), and the
+    rows of the Gaussians no view sees keep what they held."""
+    oracle, pipeline, torch = env
+    n = 3 * 256 + 45
+    sc = scenes.random_scene(n, 96, 80, seed=45, views=2, sh_degree=3, log_scale_mean=-2.5)
+    sc.means[:, :30] = np.array([[50.0], [0.0], [3.0]], np.float32)  # outside both frusta
+    sc.means[:, 300:340] = np.array([[-40.0], [5.0], [2.0]], np.float32)
+    st = sc.settings()
+    r = pipeline.Renderer(sc, st)
+    r.iteration(mode="fused")
+    torch.cuda.synchronize()
+    print(f"[seen-only F1] n={n}", flush=True)
+    sentinel = np.float32(-7.25)
+    r.project_backward()  # allocates the parameter-gradient outputs
+    for t in (r.d_means3, r.d_log_scales3, r.d_quats3, r.d_logits3, r.d_sh3):
+        t.fill_(float(sentinel))
+    r.project_backward(seen_only=True)
+    torch.cuda.synchronize()
+    seen = r.seen[:n].cpu().numpy()
+    sparse = r.grads3d_host()
+    vis = np.zeros(n, bool)
+    flagged = np.zeros(n, bool)
+    for cam in sc.cameras:
+        po = oracle.project(sc, cam, st)
+        vis |= po["visible"] != 0
+        flagged |= po["flag"] != 0
+    ok = ~flagged
+    assert np.array_equal(seen[ok] != 0, vis[ok])
+    assert not seen[:30].any() and not seen[300:340].any() and seen.any()
+    r.project_backward()  # the dense rows, compared with the oracle
+    dense = r.grads3d_host()
+    for key in dense:
+        s, d = sparse[key][..., seen != 0], dense[key][..., seen != 0]
+        assert np.array_equal(s.view(np.uint32), d.view(np.uint32)), key
+        assert np.all(sparse[key][..., seen == 0] == sentinel), key
+        assert np.all(dense[key][..., seen == 0] == 0.0), key
+    _project_bwd_check(env, sc, st, r)
+
+
 def test_packed_records_and_instance_bases(env):
     """Each visible slot's 64-byte rasterizer record holds exactly the per-field values of the
     projection, and the instance bases number the instances view by view, slot by slot."""
