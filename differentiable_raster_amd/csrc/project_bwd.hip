@@ -6,8 +6,9 @@
 //  * slot lookup: visible Gaussians of a view occupy slots in ascending index order, so the
 //    visible Gaussians of a 256-Gaussian block are one run of vis_ids that starts at the first
 //    slot whose id is >= the block's first index.  One wave per view finds that start with a
-//    64-ary search (four rounds for a million slots), the block loads the 256-entry window into
-//    LDS, and each thread finds its own slot there by binary search;
+//    64-ary search (four rounds for a million slots); unless the slot there names a Gaussian
+//    past the block (then the view sees none of the block's Gaussians), the block loads the
+//    256-entry window into LDS, and each thread finds its own slot there by binary search;
 //  * the per-Gaussian frame (activations, rotation, world covariance) and the colour before its
 //    clamp come from the same device functions as the forward projection, so the colour clamp
 //    takes the forward's decision;
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
     __shared__ int s_lo[GS_MAX_VIEWS];
     __shared__ int s_win[GS_MAX_VIEWS][kBlock];
     __shared__ int s_slot[GS_MAX_VIEWS][kBlock];
+    __shared__ int s_has[GS_MAX_VIEWS];  // 0 when the view sees none of the block's Gaussians
     const int i0 = blockIdx.x * kBlock;
     const int i = i0 + threadIdx.x;
     const int n = a.n;
@@ -67,11 +69,18 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
     // 1. start of this block's run of slots in every view, the windows, then each thread's slot
     for (int v = w; v < a.V; v += kBlock / kWave) {
         const int cnt = min(a.vis_count[v], a.capacity);
-        const int lo = wave_lower_bound(a.vis_ids + (size_t)v * a.capacity, cnt, i0);
-        if ((threadIdx.x & (kWave - 1)) == 0) s_lo[v] = lo;
+        const int32_t* ids = a.vis_ids + (size_t)v * a.capacity;
+        const int lo = wave_lower_bound(ids, cnt, i0);
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            s_lo[v] = lo;
+            // the first slot at or after the block's start names a later Gaussian: none of this
+            // block's Gaussians is in the view (most blocks of a large scene)
+            s_has[v] = (lo < cnt && ids[lo] < i0 + kBlock) ? 1 : 0;
+        }
     }
     __syncthreads();
     for (int v = 0; v < a.V; v++) {
+        if (!s_has[v]) continue;  // no slot of this view in the block (uniform)
         const int cnt = min(a.vis_count[v], a.capacity);
         const int p = s_lo[v] + threadIdx.x;
         s_win[v][threadIdx.x] = p < cnt ? a.vis_ids[(size_t)v * a.capacity + p] : INT_MAX;
@@ -79,6 +88,10 @@ __global__ __launch_bounds__(kBlock) void project_bwd_kernel(ProjectBwdArgs a) {
     __syncthreads();
     if (i >= n) return;
     for (int v = 0; v < a.V; v++) {
+        if (!s_has[v]) {
+            s_slot[v][threadIdx.x] = -1;
+            continue;
+        }
         int lo = 0, hi = kBlock;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
