@@ -13,6 +13,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -150,20 +151,24 @@ def main():
         log(f"[bench] calibration copies: 3 x {src.numel() * 4} bytes read and written")
         del src, dst
 
-    def stage_times(mode):
-        ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for k in ("project", "bin", "raster")}
-        ev["project"][0].record(); r.project(); ev["project"][1].record()
-        ev["bin"][0].record(); r.bin(); ev["bin"][1].record()
-        ev["raster"][0].record()
-        if mode == "fused":
-            r.fused(image=False)
-        else:
-            r.forward()
-            r.backward(r.loss_grad(1.0))
-        ev["raster"][1].record()
-        torch.cuda.synchronize()
-        return {k: a.elapsed_time(b) for k, (a, b) in ev.items()}
+    def stage_times(mode, passes=11):
+        """Per stage, the median over `passes` event-timed iterations of that stage's time."""
+        times = {k: [] for k in ("project", "bin", "raster")}
+        for _ in range(passes):
+            ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in times}
+            ev["project"][0].record(); r.project(); ev["project"][1].record()
+            ev["bin"][0].record(); r.bin(); ev["bin"][1].record()
+            ev["raster"][0].record()
+            if mode == "fused":
+                r.fused(image=False)
+            else:
+                r.forward()
+                r.backward(r.loss_grad(1.0))
+            ev["raster"][1].record()
+            torch.cuda.synchronize()
+            for k, (a, b) in ev.items():
+                times[k].append(a.elapsed_time(b))
+        return {k: statistics.median(v) for k, v in times.items()}
 
     def run(mode, steps, warmup):
         for _ in range(warmup):
