@@ -72,7 +72,11 @@ gs_status check_params(const gs_render_params* p) {
     if (!(p->alpha_min > 0.0f) || !(p->alpha_max <= 1.0f) || !(p->alpha_min < p->alpha_max) || !(p->alpha_max < 1.0f))
         return fail(GS_ERR_INVALID_ARGUMENT, "alpha bounds must satisfy 0 < alpha_min < alpha_max < 1");
     if (!(p->t_min >= 0.0f) || !(p->t_min < 1.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "t_min outside [0, 1)");
-    if (!(p->eps2d >= 0.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "eps2d < 0");
+    if (!(p->eps2d >= 0.0f) || !std::isfinite(p->eps2d)) return fail(GS_ERR_INVALID_ARGUMENT, "eps2d outside [0, inf)");
+    // the depth keys are float32 bit patterns, which order like the values only for positive depths
+    if (!(p->znear >= 0.0f) || !std::isfinite(p->znear)) return fail(GS_ERR_INVALID_ARGUMENT, "znear outside [0, inf)");
+    for (int c = 0; c < 3; c++)
+        if (!std::isfinite(p->bg[c])) return fail(GS_ERR_INVALID_ARGUMENT, "background is not finite");
     return GS_OK;
 }
 

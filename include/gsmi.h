@@ -65,7 +65,10 @@ typedef struct {
     float campos[3];        /* camera centre in world coordinates (SH view direction origin) */
 } gs_camera;
 
-/* Constants the pages leave open.  Host struct.  Typical values in brackets. */
+/* Constants the pages leave open.  Host struct.  Typical values in brackets.  Every call that
+ * takes it returns GS_ERR_INVALID_ARGUMENT unless 0 < alpha_min < alpha_max < 1, 0 <= t_min < 1,
+ * eps2d and znear are finite and >= 0 (depths must stay positive: their float32 bit patterns
+ * are the sort keys), bg is finite, 0 <= sh_degree <= 3 and tile_cap >= 0. */
 typedef struct {
     float znear;      /* [0.2]   Gaussians with camera-space z <= znear are culled */
     float eps2d;      /* [0.3]   low-pass dilation added to the 2D covariance diagonal, px^2 */

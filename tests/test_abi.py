@@ -201,6 +201,13 @@ def test_project_rejects_bad_arguments(gs):
     assert call(ctypes.byref(g), c, 1, ctypes.byref(bad), ctypes.byref(out), FAKE, ws_ok) == 1
     bad = params(gs, alpha_max=1.0)
     assert call(ctypes.byref(g), c, 1, ctypes.byref(bad), ctypes.byref(out), FAKE, ws_ok) == 1
+    # depth keys need positive depths; non-finite constants are refused
+    for kw in (dict(znear=-0.1), dict(znear=float("nan")), dict(znear=float("inf")), dict(eps2d=float("inf")),
+               dict(bg=(0.0, float("nan"), 0.0))):
+        bad = params(gs, **kw)
+        assert call(ctypes.byref(g), c, 1, ctypes.byref(bad), ctypes.byref(out), FAKE, ws_ok) == 1, kw
+    ok = params(gs, znear=0.0)
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(ok), ctypes.byref(out), FAKE, ws_ok - 1) == 2  # past the checks
     small = projected(gs, capacity=50)
     assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(small), FAKE, ws_ok) == 1
     assert b"capacity" in lib.gs_last_error()
