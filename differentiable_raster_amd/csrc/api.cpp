@@ -606,8 +606,8 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         if (e == hipSuccess) e = launch_scan_rows(w.kept, w.cap_offsets, bins->num_capped, tiles_total, 1, w.partials, s);
         if (e == hipSuccess)
             e = launch_cap_select(bins->ranges, bins->vals, reinterpret_cast<const float4*>(proj->conic_opacity),
-                                  proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets, bins->vals_capped,
-                                  bins->ranges_capped, w.tkey_alt, s);
+                                  proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets, bins->tile_order,
+                                  bins->vals_capped, bins->ranges_capped, w.tkey_alt, s);
     }
     if (e == hipSuccess) bins->count = M;
     return hip_check(e, "gs_bin_tiles launch");

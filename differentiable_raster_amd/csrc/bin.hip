@@ -477,44 +477,33 @@ __device__ __forceinline__ int block_excl_scan(int x, int* s_wave, int* total) {
     return off + inc - x;
 }
 
-// One block per global tile.  Tiles with at most K entries copy their list; longer lists keep
-// the K best by (score desc, depth asc, slot asc).  The list is in (depth, slot) order, so the
-// tie-break is list order: a radix select over the score bits (most significant digit first)
-// finds the K-th best bit pattern `thr`; entries above it are kept, and of those equal to it the
-// first `need` in list order.
-__global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* ranges, const int32_t* vals,
-                                                            const float4* conic_opacity, int32_t capacity,
-                                                            int32_t tiles_per_view, int32_t K,
-                                                            const int32_t* cap_offsets, int32_t* vals_capped,
-                                                            int32_t* ranges_capped, uint32_t* scratch_bits) {
-    __shared__ int s_hist[256];
-    __shared__ int s_wave[kBlock / kWave];
-    __shared__ uint32_t s_sel[2];
-    const int32_t g = blockIdx.x;
-    const int32_t start = ranges[2 * g], end = ranges[2 * g + 1];
-    const int32_t n = end - start;
-    const int32_t out0 = cap_offsets[g];
-    const int32_t kept = n < K ? n : K;
-    if (threadIdx.x == 0) {
-        ranges_capped[2 * g] = kept > 0 ? out0 : 0;
-        ranges_capped[2 * g + 1] = kept > 0 ? out0 + kept : 0;
-    }
-    if (n <= K) {
-        for (int32_t j = threadIdx.x; j < n; j += kBlock) vals_capped[out0 + j] = vals[start + j];
-        return;
-    }
-    const size_t vbase = (size_t)(g / tiles_per_view) * capacity;
-    for (int32_t j = threadIdx.x; j < n; j += kBlock)
-        scratch_bits[start + j] = cap_score_bits(conic_opacity[vbase + vals[start + j]]);
-    __syncthreads();
+// Scores of a full tile's list held in LDS up to this many entries (24 KB); longer lists keep
+// them in the global scratch.
+constexpr int kCapLds = 6144;
+
+// The K best of one full tile's n > K entries by (score desc, depth asc, slot asc).  The list is
+// in (depth, slot) order, so the tie-break is list order: a radix select over the score bits
+// (most significant digit first) finds the K-th best bit pattern `thr`; entries above it are
+// kept, and of those equal to it the first `need` in list order.  Each wavefront counts digits
+// into its own histogram (scores of one tile share their leading bits, so one shared histogram
+// would put every lane's increment on the same few words).
+// IN_PLACE (bits in LDS): the compaction first turns each entry's bits into its output position
+// (or ~0u), and the list entries are copied afterwards in one pass, so that no global load or
+// store waits at the compaction's barriers.
+template <bool IN_PLACE>
+__device__ __forceinline__ void cap_select_full(uint32_t* bits, int32_t n, int K, const int32_t* vals_in,
+                                                int32_t* vals_out, int (*s_hist)[256], int* s_wave,
+                                                uint32_t* s_sel) {
+    const int w = threadIdx.x / kWave;
     uint32_t prefix = 0, pmask = 0;
     int remaining = K;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        s_hist[threadIdx.x] = 0;
+#pragma unroll
+        for (int q = 0; q < kBlock / kWave; q++) s_hist[q][threadIdx.x] = 0;
         __syncthreads();
         for (int32_t j = threadIdx.x; j < n; j += kBlock) {
-            const uint32_t b = scratch_bits[start + j];
-            if ((b & pmask) == prefix) atomicAdd(&s_hist[(b >> shift) & 255u], 1);
+            const uint32_t b = bits[j];
+            if ((b & pmask) == prefix) atomicAdd(&s_hist[w][(b >> shift) & 255u], 1);
         }
         __syncthreads();
         // the digit d holding the remaining-th best entry: above(d) < remaining <= above(d) +
@@ -523,7 +512,9 @@ __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* range
         {
             static_assert(kBlock == 256, "one digit per thread");
             const int d = 255 - (int)threadIdx.x;
-            const int h = s_hist[d];
+            int h = 0;
+#pragma unroll
+            for (int q = 0; q < kBlock / kWave; q++) h += s_hist[q][d];
             int all;
             const int above = block_excl_scan(h, s_wave, &all);
             const bool sel = d > 0 ? (above < remaining && above + h >= remaining) : above < remaining;
@@ -543,16 +534,88 @@ __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* range
     int eq_seen = 0, out_seen = 0;
     for (int32_t j0 = 0; j0 < n; j0 += kBlock) {
         const int32_t j = j0 + threadIdx.x;
-        const uint32_t b = j < n ? scratch_bits[start + j] : 0u;
+        const uint32_t b = j < n ? bits[j] : 0u;
         const int is_eq = (j < n && b == thr) ? 1 : 0;
         int eq_tot;
         const int eq_rank = eq_seen + block_excl_scan(is_eq, s_wave, &eq_tot);
         const int keep = (j < n) && (b > thr || (is_eq && eq_rank < need)) ? 1 : 0;
         int keep_tot;
         const int pos = out_seen + block_excl_scan(keep, s_wave, &keep_tot);
-        if (keep) vals_capped[out0 + pos] = vals[start + j];
+        if (IN_PLACE) {
+            if (j < n) bits[j] = keep ? (uint32_t)pos : ~0u;  // this thread's own entry
+        } else if (keep) {
+            vals_out[pos] = vals_in[j];
+        }
         eq_seen += eq_tot;
         out_seen += keep_tot;
+    }
+    if (IN_PLACE) {
+        __syncthreads();
+        for (int32_t j = threadIdx.x; j < n; j += kBlock) {
+            const uint32_t pos = bits[j];
+            if (pos != ~0u) vals_out[pos] = vals_in[j];
+        }
+    }
+}
+
+// The score bits of a list's n entries into bits[0, n).  The records are gathered from scattered
+// slots, so each thread first loads four list entries, then their four records, with all four
+// loads of a kind in flight at once.
+__device__ __forceinline__ void cap_scores(const int32_t* list, int32_t n, const float4* co, uint32_t* bits) {
+    constexpr int kU = 4;
+    for (int32_t j0 = 0; j0 < n; j0 += kU * kBlock) {
+        int32_t slot[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const int32_t j = j0 + u * kBlock + (int32_t)threadIdx.x;
+            slot[u] = j < n ? list[j] : -1;
+        }
+        float4 r[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) r[u] = slot[u] >= 0 ? co[slot[u]] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const int32_t j = j0 + u * kBlock + (int32_t)threadIdx.x;
+            if (j < n) bits[j] = cap_score_bits(r[u]);
+        }
+    }
+}
+
+// One block per global tile, heaviest first when the tile order is given.  Tiles with at most K
+// entries copy their list; longer lists keep the K best (cap_select_full).
+__global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* ranges, const int32_t* vals,
+                                                            const float4* conic_opacity, int32_t capacity,
+                                                            int32_t tiles_per_view, int32_t K,
+                                                            const int32_t* cap_offsets, const int32_t* tile_order,
+                                                            int32_t* vals_capped, int32_t* ranges_capped,
+                                                            uint32_t* scratch_bits) {
+    __shared__ uint32_t s_bits[kCapLds];
+    __shared__ int s_hist[kBlock / kWave][256];
+    __shared__ int s_wave[kBlock / kWave];
+    __shared__ uint32_t s_sel[2];
+    const int32_t g = tile_order ? tile_order[blockIdx.x] : (int32_t)blockIdx.x;
+    const int32_t start = ranges[2 * g], end = ranges[2 * g + 1];
+    const int32_t n = end - start;
+    const int32_t out0 = cap_offsets[g];
+    const int32_t kept = n < K ? n : K;
+    if (threadIdx.x == 0) {
+        ranges_capped[2 * g] = kept > 0 ? out0 : 0;
+        ranges_capped[2 * g + 1] = kept > 0 ? out0 + kept : 0;
+    }
+    if (n <= K) {
+        for (int32_t j = threadIdx.x; j < n; j += kBlock) vals_capped[out0 + j] = vals[start + j];
+        return;
+    }
+    const size_t vbase = (size_t)(g / tiles_per_view) * capacity;
+    if (n <= kCapLds) {
+        cap_scores(vals + start, n, conic_opacity + vbase, s_bits);
+        __syncthreads();
+        cap_select_full<true>(s_bits, n, K, vals + start, vals_capped + out0, s_hist, s_wave, s_sel);
+    } else {
+        uint32_t* bits = scratch_bits + start;
+        cap_scores(vals + start, n, conic_opacity + vbase, bits);
+        __syncthreads();
+        cap_select_full<false>(bits, n, K, vals + start, vals_capped + out0, s_hist, s_wave, s_sel);
     }
 }
 
@@ -636,9 +699,10 @@ hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_
 
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity, int32_t capacity,
                              int32_t tiles_per_view, int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets,
-                             int32_t* vals_capped, int32_t* ranges_capped, uint32_t* scratch_bits, hipStream_t s) {
+                             const int32_t* tile_order, int32_t* vals_capped, int32_t* ranges_capped,
+                             uint32_t* scratch_bits, hipStream_t s) {
     hipLaunchKernelGGL(cap_select_kernel, dim3(n_tiles_total), dim3(kBlock), 0, s, ranges, vals, conic_opacity, capacity,
-                       tiles_per_view, K, cap_offsets, vals_capped, ranges_capped, scratch_bits);
+                       tiles_per_view, K, cap_offsets, tile_order, vals_capped, ranges_capped, scratch_bits);
     return hipGetLastError();
 }
 

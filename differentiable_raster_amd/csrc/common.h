@@ -180,8 +180,8 @@ hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, int32
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s);
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
                              int32_t capacity, int32_t tiles_per_view, int32_t n_tiles_total, int32_t K,
-                             const int32_t* cap_offsets, int32_t* vals_capped, int32_t* ranges_capped,
-                             uint32_t* scratch_bits, hipStream_t s);
+                             const int32_t* cap_offsets, const int32_t* tile_order, int32_t* vals_capped,
+                             int32_t* ranges_capped, uint32_t* scratch_bits, hipStream_t s);
 
 // Rasterizers.
 struct RasterArgs {

@@ -118,6 +118,23 @@ def test_long_lists_take_the_chunked_fused_path(env):
     run_view_checks(env, sc, sc.settings(), mode="separate", check_projection=False)
 
 
+@pytest.mark.parametrize("K", [64, 7000])
+def test_tile_cap_on_lists_longer_than_the_select_keeps_on_chip(env, K):
+    """8000 Gaussians in a one-tile 16x16 image: a list of almost 8000 entries, past the 6144
+    scores the cap's select keeps in LDS (it then works through the global scratch); K = 7000
+    keeps most of it."""
+    oracle, pipeline, torch = env
+    rng = np.random.default_rng(6)
+    n = 8000
+    cam = pinhole(16, 16, f=20.0, cx=8.0, cy=8.0)
+    means = np.stack([rng.uniform(-0.6, 0.6, n), rng.uniform(-0.6, 0.6, n), rng.uniform(2, 3, n)], 1)
+    sc = scene_from(means, np.full((n, 3), -3.5), rng.standard_normal((n, 4)), rng.normal(-3.0, 1.0, n),
+                    rng.uniform(0, 1, (n, 3)), [cam], target=rng.uniform(0, 1, (1, 3, 16, 16)))
+    r = run_view_checks(env, sc, sc.settings(tile_cap=K), mode="fused")
+    lens = np.diff(r.bins_host(0)["ranges"], axis=1)[:, 0]
+    assert lens.max() > 6144, lens.max()
+
+
 def test_fused_max_cap_keeps_capped_lists_on_chip(env):
     """With tile_cap K = gs_fused_max_cap() every capped tile list is staged into LDS exactly once
     and the backward walks that copy (diagnostics counter [3]: staged entries equal the kept
