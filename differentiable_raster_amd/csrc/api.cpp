@@ -605,9 +605,10 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         e = launch_cap_count(bins->ranges, tiles_total, p->tile_cap, w.kept, s);
         if (e == hipSuccess) e = launch_scan_rows(w.kept, w.cap_offsets, bins->num_capped, tiles_total, 1, w.partials, s);
         if (e == hipSuccess)
+            // the depth sort's key buffer (capacity * V words) is free again: the slots' scores
             e = launch_cap_select(bins->ranges, bins->vals, reinterpret_cast<const float4*>(proj->conic_opacity),
-                                  proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets, bins->tile_order,
-                                  bins->vals_capped, bins->ranges_capped, w.tkey_alt, s);
+                                  proj->vis_count, V, proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets,
+                                  bins->tile_order, bins->vals_capped, bins->ranges_capped, w.dkey, w.tkey_alt, s);
     }
     if (e == hipSuccess) bins->count = M;
     return hip_check(e, "gs_bin_tiles launch");

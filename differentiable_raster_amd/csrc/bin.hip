@@ -558,10 +558,22 @@ __device__ __forceinline__ void cap_select_full(uint32_t* bits, int32_t n, int K
     }
 }
 
-// The score bits of a list's n entries into bits[0, n).  The records are gathered from scattered
-// slots, so each thread first loads four list entries, then their four records, with all four
-// loads of a kind in flight at once.
-__device__ __forceinline__ void cap_scores(const int32_t* list, int32_t n, const float4* co, uint32_t* bits) {
+// The score bits of every visible slot (slot_bits[v * capacity + s]), in one coalesced pass: the
+// select then gathers 4 bytes per list entry instead of the slot's 16-byte conic and opacity.
+__global__ __launch_bounds__(kBlock) void cap_slot_scores_kernel(const float4* conic_opacity, const int32_t* vis_count,
+                                                                 int32_t capacity, uint32_t* slot_bits) {
+    const int v = blockIdx.y;
+    const int32_t s = blockIdx.x * kBlock + threadIdx.x;
+    if (s < vis_count[v] && s < capacity) {
+        const size_t i = (size_t)v * capacity + s;
+        slot_bits[i] = cap_score_bits(conic_opacity[i]);
+    }
+}
+
+// The score bits of a list's n entries into bits[0, n), gathered by slot from slot_bits; each
+// thread loads four list entries, then their four scores, with all four loads of a kind in
+// flight at once.
+__device__ __forceinline__ void cap_scores(const int32_t* list, int32_t n, const uint32_t* slot_bits, uint32_t* bits) {
     constexpr int kU = 4;
     for (int32_t j0 = 0; j0 < n; j0 += kU * kBlock) {
         int32_t slot[kU];
@@ -570,13 +582,13 @@ __device__ __forceinline__ void cap_scores(const int32_t* list, int32_t n, const
             const int32_t j = j0 + u * kBlock + (int32_t)threadIdx.x;
             slot[u] = j < n ? list[j] : -1;
         }
-        float4 r[kU];
+        uint32_t r[kU];
 #pragma unroll
-        for (int u = 0; u < kU; u++) r[u] = slot[u] >= 0 ? co[slot[u]] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int u = 0; u < kU; u++) r[u] = slot[u] >= 0 ? slot_bits[slot[u]] : 0u;
 #pragma unroll
         for (int u = 0; u < kU; u++) {
             const int32_t j = j0 + u * kBlock + (int32_t)threadIdx.x;
-            if (j < n) bits[j] = cap_score_bits(r[u]);
+            if (j < n) bits[j] = r[u];
         }
     }
 }
@@ -584,7 +596,7 @@ __device__ __forceinline__ void cap_scores(const int32_t* list, int32_t n, const
 // One block per global tile, heaviest first when the tile order is given.  Tiles with at most K
 // entries copy their list; longer lists keep the K best (cap_select_full).
 __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* ranges, const int32_t* vals,
-                                                            const float4* conic_opacity, int32_t capacity,
+                                                            const uint32_t* slot_bits, int32_t capacity,
                                                             int32_t tiles_per_view, int32_t K,
                                                             const int32_t* cap_offsets, const int32_t* tile_order,
                                                             int32_t* vals_capped, int32_t* ranges_capped,
@@ -608,12 +620,12 @@ __global__ __launch_bounds__(kBlock) void cap_select_kernel(const int32_t* range
     }
     const size_t vbase = (size_t)(g / tiles_per_view) * capacity;
     if (n <= kCapLds) {
-        cap_scores(vals + start, n, conic_opacity + vbase, s_bits);
+        cap_scores(vals + start, n, slot_bits + vbase, s_bits);
         __syncthreads();
         cap_select_full<true>(s_bits, n, K, vals + start, vals_capped + out0, s_hist, s_wave, s_sel);
     } else {
         uint32_t* bits = scratch_bits + start;
-        cap_scores(vals + start, n, conic_opacity + vbase, bits);
+        cap_scores(vals + start, n, slot_bits + vbase, bits);
         __syncthreads();
         cap_select_full<false>(bits, n, K, vals + start, vals_capped + out0, s_hist, s_wave, s_sel);
     }
@@ -697,11 +709,15 @@ hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_
     return hipGetLastError();
 }
 
-hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity, int32_t capacity,
-                             int32_t tiles_per_view, int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets,
-                             const int32_t* tile_order, int32_t* vals_capped, int32_t* ranges_capped,
+hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
+                             const int32_t* vis_count, int32_t V, int32_t capacity, int32_t tiles_per_view,
+                             int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets, const int32_t* tile_order,
+                             int32_t* vals_capped, int32_t* ranges_capped, uint32_t* slot_bits,
                              uint32_t* scratch_bits, hipStream_t s) {
-    hipLaunchKernelGGL(cap_select_kernel, dim3(n_tiles_total), dim3(kBlock), 0, s, ranges, vals, conic_opacity, capacity,
+    if (capacity > 0)
+        hipLaunchKernelGGL(cap_slot_scores_kernel, dim3((unsigned)((capacity + kBlock - 1) / kBlock), (unsigned)V),
+                           dim3(kBlock), 0, s, conic_opacity, vis_count, capacity, slot_bits);
+    hipLaunchKernelGGL(cap_select_kernel, dim3(n_tiles_total), dim3(kBlock), 0, s, ranges, vals, slot_bits, capacity,
                        tiles_per_view, K, cap_offsets, tile_order, vals_capped, ranges_capped, scratch_bits);
     return hipGetLastError();
 }

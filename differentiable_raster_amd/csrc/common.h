@@ -178,10 +178,13 @@ size_t tile_order_hist_ints(int32_t n_tiles_total);
 hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, int32_t* hist, int32_t* order,
                              hipStream_t s);
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s);
+// slot_bits: V * capacity words of workspace (the visible slots' scores); scratch_bits: one word
+// per instance (the scores of lists longer than the select keeps in LDS).
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
-                             int32_t capacity, int32_t tiles_per_view, int32_t n_tiles_total, int32_t K,
-                             const int32_t* cap_offsets, const int32_t* tile_order, int32_t* vals_capped,
-                             int32_t* ranges_capped, uint32_t* scratch_bits, hipStream_t s);
+                             const int32_t* vis_count, int32_t V, int32_t capacity, int32_t tiles_per_view,
+                             int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets, const int32_t* tile_order,
+                             int32_t* vals_capped, int32_t* ranges_capped, uint32_t* slot_bits,
+                             uint32_t* scratch_bits, hipStream_t s);
 
 // Rasterizers.
 struct RasterArgs {
