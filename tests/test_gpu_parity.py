@@ -327,7 +327,7 @@ def _project_bwd_check(env, sc, st, r):
                                            r.grads3d_host())
 
 
-@pytest.mark.parametrize("deg,views,seed", [(0, 1, 31), (1, 2, 32), (3, 3, 33)])
+@pytest.mark.parametrize("deg,views,seed", [(0, 1, 31), (1, 2, 32), (2, 2, 34), (3, 3, 33)])
 def test_project_backward_after_fused_raster(env, deg, views, seed):
     """The projection backward chained after the fused rasterizer, compared with the oracle's chain
     rule on the GPU's own 2D gradients."""
