@@ -1,7 +1,9 @@
 // Device-wide exclusive prefix sums of int32 rows (reduce, scan the block sums, apply; rows of at
 // most 16384 values are scanned by one workgroup each in a single launch).
-// Each block owns kChunk = 2048 consecutive elements (8 per thread, thread-contiguous), so
-// every pass reads the input with 128-bit loads where the row length allows.
+// Each block owns kChunk = 2048 consecutive elements, and each thread scans kItems consecutive
+// ones of them.  Global memory is read and written in the coalesced order (consecutive threads,
+// consecutive elements) and turned into the thread-contiguous order through LDS, whose rows are
+// padded by one word so that neither order puts two lanes of an access on one bank.
 #include "common.h"
 
 namespace gsmi {
@@ -33,16 +35,42 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* s_wave, int* tot
     return off + inc - x;
 }
 
+// Values [b0, b0 + BLOCK * ITEMS) of a row (zero past n) into LDS, thread t's ITEMS consecutive
+// ones at s[t * (ITEMS + 1) + k].  Ends with a barrier.
+template <int BLOCK, int ITEMS>
+__device__ __forceinline__ void stage_in(const int32_t* r, int64_t b0, int64_t n, int* s) {
+#pragma unroll
+    for (int k = 0; k < ITEMS; k++) {
+        const int e = k * BLOCK + (int)threadIdx.x;
+        s[(e / ITEMS) * (ITEMS + 1) + e % ITEMS] = b0 + e < n ? r[b0 + e] : 0;
+    }
+    __syncthreads();
+}
+
+// The reverse of stage_in: s (thread-contiguous, padded) to o[b0, min(n, b0 + BLOCK * ITEMS)).
+// Starts with a barrier.
+template <int BLOCK, int ITEMS>
+__device__ __forceinline__ void stage_out(const int* s, int64_t b0, int64_t n, int32_t* o) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; k++) {
+        const int e = k * BLOCK + (int)threadIdx.x;
+        if (b0 + e < n) o[b0 + e] = s[(e / ITEMS) * (ITEMS + 1) + e % ITEMS];
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void scan_reduce_kernel(const int32_t* in, int32_t n, int32_t nblocks,
                                                              int32_t* partials) {
     __shared__ int s_wave[kBlock / kWave];
     const int row = blockIdx.y;
     const int32_t* r = in + (size_t)row * n;
-    const int64_t base = (int64_t)blockIdx.x * kChunk + threadIdx.x * kItems;
-    int sum = 0;
+    const int64_t b0 = (int64_t)blockIdx.x * kChunk;
+    int sum = 0;  // the block's sum: any order, so the coalesced one
 #pragma unroll
-    for (int k = 0; k < kItems; k++)
-        if (base + k < n) sum += r[base + k];
+    for (int k = 0; k < kItems; k++) {
+        const int64_t e = b0 + k * kBlock + threadIdx.x;
+        if (e < n) sum += r[e];
+    }
     int tot;
     block_exclusive_scan(sum, s_wave, &tot);
     if (threadIdx.x == 0) partials[(size_t)row * nblocks + blockIdx.x] = tot;
@@ -67,24 +95,28 @@ __global__ __launch_bounds__(kBlock) void scan_partials_kernel(int32_t* partials
 __global__ __launch_bounds__(kBlock) void scan_apply_kernel(const int32_t* in, int32_t* out, int32_t n, int32_t nblocks,
                                                             const int32_t* partials) {
     __shared__ int s_wave[kBlock / kWave];
+    __shared__ int s_v[kBlock * (kItems + 1)];
     const int row = blockIdx.y;
     const int32_t* r = in + (size_t)row * n;
     int32_t* o = out + (size_t)row * n;
-    const int64_t base = (int64_t)blockIdx.x * kChunk + threadIdx.x * kItems;
+    const int64_t b0 = (int64_t)blockIdx.x * kChunk;
+    stage_in<kBlock, kItems>(r, b0, n, s_v);
+    int* mine = s_v + threadIdx.x * (kItems + 1);
     int v[kItems];
     int sum = 0;
 #pragma unroll
     for (int k = 0; k < kItems; k++) {
-        v[k] = (base + k < n) ? r[base + k] : 0;
+        v[k] = mine[k];
         sum += v[k];
     }
     int tot;
     int run = block_exclusive_scan(sum, s_wave, &tot) + partials[(size_t)row * nblocks + blockIdx.x];
 #pragma unroll
     for (int k = 0; k < kItems; k++) {
-        if (base + k < n) o[base + k] = run;
+        mine[k] = run;
         run += v[k];
     }
+    stage_out<kBlock, kItems>(s_v, b0, n, o);
 }
 
 // One workgroup scans a[0, n) in place (exclusive): each thread takes kSmallItems consecutive
@@ -123,25 +155,29 @@ constexpr int32_t kShortRow = kShortBlock * kSmallItems;
 __global__ __launch_bounds__(kShortBlock) void scan_rows_short_kernel(const int32_t* in, int32_t* out,
                                                                       int32_t* totals, int32_t n) {
     __shared__ int s_wave[kShortBlock / kWave];
+    __shared__ int s_v[kShortBlock * (kSmallItems + 1)];
     const int32_t* r = in + (size_t)blockIdx.x * n;
     int32_t* o = out + (size_t)blockIdx.x * n;
     int carry = 0;
+    int* mine = s_v + threadIdx.x * (kSmallItems + 1);
     for (int32_t b0 = 0; b0 < n; b0 += kShortBlock * kSmallItems) {
-        const int32_t first = b0 + threadIdx.x * kSmallItems;
+        if (b0 > 0) __syncthreads();  // the previous step's stores have read s_v
+        stage_in<kShortBlock, kSmallItems>(r, b0, n, s_v);
         int v[kSmallItems];
         int sum = 0;
 #pragma unroll
         for (int k = 0; k < kSmallItems; k++) {
-            v[k] = first + k < n ? r[first + k] : 0;
+            v[k] = mine[k];
             sum += v[k];
         }
         int tot;
         int run = carry + block_exclusive_scan<kShortBlock>(sum, s_wave, &tot);
 #pragma unroll
         for (int k = 0; k < kSmallItems; k++) {
-            if (first + k < n) o[first + k] = run;
+            mine[k] = run;
             run += v[k];
         }
+        stage_out<kShortBlock, kSmallItems>(s_v, b0, n, o);
         carry += tot;
     }
     if (threadIdx.x == 0 && totals) totals[blockIdx.x] = carry;
