@@ -64,8 +64,19 @@ __device__ Geo load_geo_rest(const ProjectArgs& a, int i, float mx, float my, fl
     return g;
 }
 
-__device__ Geo load_geo(const ProjectArgs& a, int i) {
-    return load_geo_rest(a, i, a.means[i], a.means[a.n + i], a.means[2 * a.n + i]);
+// The same from the eleven raw values (mean, log-scales, quaternion w x y z, opacity logit).
+__device__ __forceinline__ Geo geo_from(const float raw[11]) {
+    Geo g;
+    g.mx = raw[0];
+    g.my = raw[1];
+    g.mz = raw[2];
+    const GaussFrame f = gauss_frame(raw[3], raw[4], raw[5], raw[6], raw[7], raw[8], raw[9], raw[10],
+                                     finitef(g.mx) && finitef(g.my) && finitef(g.mz));
+    g.ok = f.ok;
+    g.o = f.o;
+#pragma unroll
+    for (int k = 0; k < 6; k++) g.S[k] = f.S[k];
+    return g;
 }
 
 // The camera-space centre of a mean and its projection, with the decisions taken from the mean
@@ -242,12 +253,10 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
     const int32_t gw = (int32_t)(i / kWave);
     if (blockIdx.x == 0 && threadIdx.x < a.V) a.vis_count[threadIdx.x] = a.row_totals[threadIdx.x];
     if (gw >= nw) return;
-    // a wavefront whose Gaussians no view sees (most of a large scene) writes nothing
-    {
-        bool any = false;
-        for (int v = 0; v < a.V; v++) any |= a.block_counts[(size_t)v * nw + gw] > 0;
-        if (!any) return;
-    }
+    // a wavefront whose Gaussians no view sees (most of a large scene) writes nothing: its
+    // per-view counts in one load, one view per lane (V <= 16)
+    const int cnt_raw = a.block_counts[(size_t)min(lane, a.V - 1) * nw + gw];
+    if (__ballot(lane < a.V && cnt_raw > 0) == 0ull) return;
     Geo g;
     g.ok = false;
     // the Gaussian's SH coefficients (row k*3 + channel), read once for all views, and only for
@@ -257,11 +266,23 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
 #pragma unroll
     for (int k = 0; k < NC; k++) coef[k] = 0.0f;
     if (i < a.n && a.seen[i]) {
-        g = load_geo(a, i);
-        if (g.ok) {
+        // A seen Gaussian's geometry is valid (the counting pass ran this same code on it), so
+        // the coefficient loads need not wait for that check.  Geometry loads first, then the
+        // coefficients (an empty asm with a memory clobber between them keeps that order): the
+        // covariance needs only the geometry, whose loads complete first, so it is built while
+        // the coefficients arrive.
+        float raw[11];
 #pragma unroll
-            for (int k = 0; k < NC; k++) coef[k] = a.sh[(size_t)k * a.n + i];
-        }
+        for (int k = 0; k < 3; k++) raw[k] = a.means[(size_t)k * a.n + i];
+#pragma unroll
+        for (int k = 0; k < 3; k++) raw[3 + k] = a.log_scales[(size_t)k * a.n + i];
+#pragma unroll
+        for (int k = 0; k < 4; k++) raw[6 + k] = a.quats[(size_t)k * a.n + i];
+        raw[10] = a.logits[i];
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < NC; k++) coef[k] = a.sh[(size_t)k * a.n + i];
+        g = geo_from(raw);
     }
     int view_inst = 0;  // instances of the earlier views
     for (int v = 0; v < a.V; v++) {
