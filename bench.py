@@ -129,7 +129,9 @@ def main():
     scene = scenes.make_scene(args.workload)
     settings = scene.settings(tile_cap=args.cap)
     log(f"[bench] workload {args.workload} ({scene.name}) generated in {time.perf_counter() - t:.1f} s")
-    r = pipeline.Renderer(scene, settings, device="cuda:0")
+    # lean: the optional per-field projection arrays are not requested (nothing downstream reads
+    # them; the packed records hold the same values)
+    r = pipeline.Renderer(scene, settings, device="cuda:0", lean=True)
 
     # sizing pass and algorithmic counts (outside the timed region)
     r.project()

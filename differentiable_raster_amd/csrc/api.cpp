@@ -115,12 +115,12 @@ ParamsDev to_dev(const gs_render_params* p) {
     return d;
 }
 
-gs_status check_projected(const gs_projected* pr, bool records) {
+// mean2d, conic_opacity and color are optional everywhere: copies of values the packed record
+// holds, written only when given.
+gs_status check_projected(const gs_projected* pr) {
     if (!pr) return fail(GS_ERR_INVALID_ARGUMENT, "projected is null");
     if (pr->capacity < 0) return fail(GS_ERR_INVALID_ARGUMENT, "projected capacity < 0");
     if (!pr->vis_count || !pr->inst_count) return fail(GS_ERR_INVALID_ARGUMENT, "projected counts are null");
-    if (records && (!pr->mean2d || !pr->conic_opacity || !pr->color))
-        return fail(GS_ERR_INVALID_ARGUMENT, "projected records are null");
     return GS_OK;
 }
 
@@ -177,7 +177,7 @@ gs_status check_raster(const gs_camera* cams, const gs_projected* proj, const gs
     gs_status st = check_cams(cams, V);
     if (st != GS_OK) return st;
     if ((st = check_params(p)) != GS_OK) return st;
-    if ((st = check_projected(proj, true)) != GS_OK) return st;
+    if ((st = check_projected(proj)) != GS_OK) return st;
     if (!proj->raster_rec) return fail(GS_ERR_INVALID_ARGUMENT, "projected raster_rec is null");
     if (!bins) return fail(GS_ERR_INVALID_ARGUMENT, "bins is null");
     const int32_t* ranges = use_capped ? bins->ranges_capped : bins->ranges;
@@ -309,7 +309,7 @@ gs_status gs_project(const gs_gaussians* g, const gs_camera* cams, int32_t V, co
     if (g->n < 0 || g->n >= (1 << 28)) return fail(GS_ERR_INVALID_ARGUMENT, "n=%d outside [0, 2^28)", g->n);
     if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
         return fail(GS_ERR_INVALID_ARGUMENT, "a parameter array is null");
-    if ((st = check_projected(out, true)) != GS_OK) return st;
+    if ((st = check_projected(out)) != GS_OK) return st;
     if (!out->vis_ids || !out->depth || !out->tile_rect || !out->n_tiles || !out->inst_base || !out->raster_rec)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected outputs are null");
     if (reinterpret_cast<uintptr_t>(out->raster_rec) % 64 != 0)
@@ -501,9 +501,11 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
     gs_status st = check_cams(cams, V);
     if (st != GS_OK) return st;
     if ((st = check_params(p)) != GS_OK) return st;
-    if ((st = check_projected(proj, true)) != GS_OK) return st;
+    if ((st = check_projected(proj)) != GS_OK) return st;
     if (!proj->depth || !proj->tile_rect || !proj->n_tiles)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected depth/rect/n_tiles are null");
+    if (p->tile_cap > 0 && !proj->conic_opacity && !proj->raster_rec)
+        return fail(GS_ERR_INVALID_ARGUMENT, "tile_cap > 0 needs conic_opacity or raster_rec");
     if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges)
         return fail(GS_ERR_INVALID_ARGUMENT, "bins outputs are null");
     if (p->tile_cap > 0 && (!bins->vals_capped || !bins->ranges_capped || !bins->num_capped))
@@ -607,7 +609,7 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         if (e == hipSuccess)
             // the depth sort's key buffer (capacity * V words) is free again: the slots' scores
             e = launch_cap_select(bins->ranges, bins->vals, reinterpret_cast<const float4*>(proj->conic_opacity),
-                                  proj->vis_count, V, proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets,
+                                  reinterpret_cast<const float4*>(proj->raster_rec), proj->vis_count, V, proj->capacity, tpv, tiles_total, p->tile_cap, w.cap_offsets,
                                   bins->tile_order, bins->vals_capped, bins->ranges_capped, w.dkey, w.tkey_alt, s);
     }
     if (e == hipSuccess) bins->count = M;
@@ -678,7 +680,7 @@ gs_status gs_check_bins(const gs_camera* cams, const gs_projected* proj, int32_t
     gs_status st = check_cams(cams, V);
     if (st != GS_OK) return st;
     if ((st = check_params(p)) != GS_OK) return st;
-    if ((st = check_projected(proj, false)) != GS_OK) return st;
+    if ((st = check_projected(proj)) != GS_OK) return st;
     if (!proj->depth || !proj->tile_rect || !proj->n_tiles || !proj->inst_base)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected depth/rect/n_tiles/inst_base are null");
     if (!bins || !bins->tile_keys || !bins->vals || !bins->ranges)

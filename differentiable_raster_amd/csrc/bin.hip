@@ -560,13 +560,22 @@ __device__ __forceinline__ void cap_select_full(uint32_t* bits, int32_t n, int K
 
 // The score bits of every visible slot (slot_bits[v * capacity + s]), in one coalesced pass: the
 // select then gathers 4 bytes per list entry instead of the slot's 16-byte conic and opacity.
-__global__ __launch_bounds__(kBlock) void cap_slot_scores_kernel(const float4* conic_opacity, const int32_t* vis_count,
-                                                                 int32_t capacity, uint32_t* slot_bits) {
+__global__ __launch_bounds__(kBlock) void cap_slot_scores_kernel(const float4* conic_opacity, const float4* rec,
+                                                                 const int32_t* vis_count, int32_t capacity,
+                                                                 uint32_t* slot_bits) {
     const int v = blockIdx.y;
     const int32_t s = blockIdx.x * kBlock + threadIdx.x;
     if (s < vis_count[v] && s < capacity) {
         const size_t i = (size_t)v * capacity + s;
-        slot_bits[i] = cap_score_bits(conic_opacity[i]);
+        float4 co;
+        if (conic_opacity) {
+            co = conic_opacity[i];
+        } else {
+            // the packed record holds the same values: (x, y, A, B), (C, o, r, g), ...
+            const float4 r0 = rec[4 * i], r1 = rec[4 * i + 1];
+            co = make_float4(r0.z, r0.w, r1.x, r1.y);
+        }
+        slot_bits[i] = cap_score_bits(co);
     }
 }
 
@@ -710,13 +719,13 @@ hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_
 }
 
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
-                             const int32_t* vis_count, int32_t V, int32_t capacity, int32_t tiles_per_view,
+                             const float4* rec, const int32_t* vis_count, int32_t V, int32_t capacity, int32_t tiles_per_view,
                              int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets, const int32_t* tile_order,
                              int32_t* vals_capped, int32_t* ranges_capped, uint32_t* slot_bits,
                              uint32_t* scratch_bits, hipStream_t s) {
     if (capacity > 0)
         hipLaunchKernelGGL(cap_slot_scores_kernel, dim3((unsigned)((capacity + kBlock - 1) / kBlock), (unsigned)V),
-                           dim3(kBlock), 0, s, conic_opacity, vis_count, capacity, slot_bits);
+                           dim3(kBlock), 0, s, conic_opacity, rec, vis_count, capacity, slot_bits);
     hipLaunchKernelGGL(cap_select_kernel, dim3(n_tiles_total), dim3(kBlock), 0, s, ranges, vals, slot_bits, capacity,
                        tiles_per_view, K, cap_offsets, tile_order, vals_capped, ranges_capped, scratch_bits);
     return hipGetLastError();

@@ -79,7 +79,7 @@ struct ProjectArgs {
     int32_t* vis_count;
     int64_t* inst_count;
     int32_t* vis_ids;
-    float2* mean2d;
+    float2* mean2d;          // optional (NULL: not written), as conic_opacity and color
     float4* conic_opacity;
     float* color;
     float* depth;
@@ -179,9 +179,10 @@ hipError_t launch_tile_order(const int32_t* ranges, int32_t n_tiles_total, int32
                              hipStream_t s);
 hipError_t launch_cap_count(const int32_t* ranges, int32_t n_tiles_total, int32_t K, int32_t* kept, hipStream_t s);
 // slot_bits: V * capacity words of workspace (the visible slots' scores); scratch_bits: one word
-// per instance (the scores of lists longer than the select keeps in LDS).
+// per instance (the scores of lists longer than the select keeps in LDS).  The scores come from
+// conic_opacity, or from the packed records rec when conic_opacity is NULL.
 hipError_t launch_cap_select(const int32_t* ranges, const int32_t* vals, const float4* conic_opacity,
-                             const int32_t* vis_count, int32_t V, int32_t capacity, int32_t tiles_per_view,
+                             const float4* rec, const int32_t* vis_count, int32_t V, int32_t capacity, int32_t tiles_per_view,
                              int32_t n_tiles_total, int32_t K, const int32_t* cap_offsets, const int32_t* tile_order,
                              int32_t* vals_capped, int32_t* ranges_capped, uint32_t* slot_bits,
                              uint32_t* scratch_bits, hipStream_t s);

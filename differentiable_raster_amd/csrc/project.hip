@@ -321,11 +321,15 @@ __global__ __launch_bounds__(kBlock) void project_write_kernel(ProjectArgs a) {
             const int base = view_inst + a.block_offsets[(size_t)(a.V + v) * nw + gw] + inc - nt;
             const size_t idx = (size_t)v * a.capacity + slot;
             a.vis_ids[idx] = i;
-            a.mean2d[idx] = r.xy;
-            a.conic_opacity[idx] = r.co;
-            a.color[3 * idx + 0] = r.rgb.x;
-            a.color[3 * idx + 1] = r.rgb.y;
-            a.color[3 * idx + 2] = r.rgb.z;
+            // optional copies of values the packed record also holds (kernel arguments: the
+            // tests are uniform)
+            if (a.mean2d) a.mean2d[idx] = r.xy;
+            if (a.conic_opacity) a.conic_opacity[idx] = r.co;
+            if (a.color) {
+                a.color[3 * idx + 0] = r.rgb.x;
+                a.color[3 * idx + 1] = r.rgb.y;
+                a.color[3 * idx + 2] = r.rgb.z;
+            }
             a.depth[idx] = r.depth;
             a.tile_rect[idx] = r.rect;
             a.n_tiles[idx] = r.ntiles;

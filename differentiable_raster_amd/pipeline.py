@@ -15,9 +15,18 @@ import torch
 from . import gsmi
 
 
+def ptr(t):
+    """Device address of a tensor, or None (a NULL pointer) for an absent optional array."""
+    return t.data_ptr() if t is not None else None
+
+
 class Renderer:
     def __init__(self, scene, settings, device: str = "cuda", instance_capacity: int | None = None,
-                 headroom: float = 1.25, early_counts: bool = True):
+                 headroom: float = 1.25, early_counts: bool = True, lean: bool = False):
+        """lean: request only the optional per-field projection arrays that a later call reads
+        (conic/opacity for the cap's scores when the tiles are capped: read from the packed records
+        instead it would cost the cap more than the store costs the projection); the packed
+        records hold the same values, and projected_host reads the others from there."""
         self.scene = scene
         self.settings = settings
         self.device = torch.device(device)
@@ -45,17 +54,19 @@ class Renderer:
         self.vis_count = torch.zeros(V, dtype=i32, device=dev)
         self.inst_count = torch.zeros(V, dtype=torch.int64, device=dev)
         self.vis_ids = torch.empty(V * cap, dtype=i32, device=dev)
-        self.mean2d = torch.empty(V * cap * 2, dtype=f32, device=dev)
-        self.conic_opacity = torch.empty(V * cap * 4, dtype=f32, device=dev)
-        self.color = torch.empty(V * cap * 3, dtype=f32, device=dev)
+        self.lean = lean
+        opt = lambda want, k: torch.empty(V * cap * k, dtype=f32, device=dev) if want else None
+        self.mean2d = opt(not lean, 2)
+        self.conic_opacity = opt(not lean or settings.tile_cap > 0, 4)
+        self.color = opt(not lean, 3)
         self.depth = torch.empty(V * cap, dtype=f32, device=dev)
         self.tile_rect = torch.empty(V * cap * 4, dtype=torch.int16, device=dev)
         self.n_tiles = torch.empty(V * cap, dtype=i32, device=dev)
         self.inst_base = torch.empty(V * cap, dtype=i32, device=dev)
         self.raster_rec = torch.empty(V * cap * 16, dtype=f32, device=dev)  # torch allocations are 256-B aligned
         self.proj = gsmi.gs_projected(cap, self.vis_count.data_ptr(), self.inst_count.data_ptr(),
-                                      self.vis_ids.data_ptr(), self.mean2d.data_ptr(), self.conic_opacity.data_ptr(),
-                                      self.color.data_ptr(), self.depth.data_ptr(), self.tile_rect.data_ptr(),
+                                      self.vis_ids.data_ptr(), ptr(self.mean2d), ptr(self.conic_opacity),
+                                      ptr(self.color), self.depth.data_ptr(), self.tile_rect.data_ptr(),
                                       self.n_tiles.data_ptr(), self.inst_base.data_ptr(), self.raster_rec.data_ptr(),
                                       None)
         # pinned count buffer: the projection copies the counts out before its writing pass
@@ -199,18 +210,21 @@ class Renderer:
         cnt = int(self.vis_count[v].item())
         cap = self.capacity
         sl = slice(v * cap, v * cap + cnt)
+        rec = self.raster_rec.view(-1, 16)[sl].cpu().numpy()
+        # the per-field arrays where requested, else the same values from the packed records
+        field = lambda t, k, lo: t.view(-1, k)[sl].cpu().numpy() if t is not None else rec[:, lo:lo + k].copy()
         return dict(
             vis_count=cnt,
             inst_count=int(self.inst_count[v].item()),
             vis_ids=self.vis_ids[sl].cpu().numpy(),
-            mean2d=self.mean2d.view(-1, 2)[sl].cpu().numpy(),
-            conic_opacity=self.conic_opacity.view(-1, 4)[sl].cpu().numpy(),
-            color=self.color.view(-1, 3)[sl].cpu().numpy(),
+            mean2d=field(self.mean2d, 2, 0),
+            conic_opacity=field(self.conic_opacity, 4, 2),
+            color=field(self.color, 3, 6),
             depth=self.depth[sl].cpu().numpy(),
             rect=self.tile_rect.view(-1, 4)[sl].cpu().numpy().astype(np.int32) & 0xFFFF,
             n_tiles=self.n_tiles[sl].cpu().numpy(),
             inst_base=self.inst_base[sl].cpu().numpy(),
-            raster_rec=self.raster_rec.view(-1, 16)[sl].cpu().numpy(),
+            raster_rec=rec,
         )
 
     def bins_host(self, v: int, capped: bool = False) -> dict:

@@ -96,15 +96,19 @@ typedef struct gs_readback gs_readback;
 
 /* Per-view projected records, indexed by visible slot.  All arrays are [V][capacity][...]
  * with capacity >= n; slot s of view v lives at index v*capacity + s.  Visible Gaussians of
- * a view take slots 0..vis_count[v]-1 in ascending Gaussian index. */
+ * a view take slots 0..vis_count[v]-1 in ascending Gaussian index.  mean2d, conic_opacity and
+ * color are optional (NULL: not written; the packed record holds the same values): no call
+ * needs them, and gs_bin_tiles with tile_cap > 0 reads the conic and opacity from
+ * conic_opacity when it is given, else from raster_rec. */
 typedef struct {
     int32_t capacity;
     int32_t* vis_count;       /* [V]  number of visible Gaussians per view */
     int64_t* inst_count;      /* [V]  sum of n_tiles per view ((Gaussian, tile) instances) */
     int32_t* vis_ids;         /* [V][capacity]    Gaussian index of each slot */
-    float* mean2d;            /* [V][capacity][2] projected centre, pixels */
-    float* conic_opacity;     /* [V][capacity][4] (A, B, C, o): q = A dx^2 + 2B dx dy + C dy^2 */
-    float* color;             /* [V][capacity][3] RGB after the lower clamp at 0 */
+    float* mean2d;            /* [V][capacity][2] projected centre, pixels (optional) */
+    float* conic_opacity;     /* [V][capacity][4] (A, B, C, o): q = A dx^2 + 2B dx dy + C dy^2
+                                 (optional) */
+    float* color;             /* [V][capacity][3] RGB after the lower clamp at 0 (optional) */
     float* depth;             /* [V][capacity]    camera-space z */
     uint16_t* tile_rect;      /* [V][capacity][4] (tx0, ty0, tx1, ty1), inclusive */
     int32_t* n_tiles;         /* [V][capacity]    tiles in the rectangle */
@@ -214,8 +218,9 @@ size_t gs_project_workspace_size(int32_t n, int32_t V);
  * to the image, and its tile rectangle.  Gaussians with any non-finite input or derived value,
  * det <= 0, o <= alpha_min or an empty box are culled (per-view frustum culling as in GS-Scale,
  * arXiv 2509.15645, English abstract).  Visible Gaussians are compacted into slots in ascending
- * index order.  Besides the per-field arrays, every visible slot gets its instance base and the
- * packed 64-byte rasterizer record.  Parameters are read once for all V views.
+ * index order.  Besides the per-field arrays (mean2d, conic_opacity and color only where given),
+ * every visible slot gets its instance base and the packed 64-byte rasterizer record.
+ * Parameters are read once for all V views.
  * Errors: GS_ERR_INVALID_ARGUMENT for null pointers, n < 0, V outside 1..GS_MAX_VIEWS,
  * capacity < n, sh_degree outside 0..3, non-positive image sizes or differing image sizes
  * between views; GS_ERR_CAPACITY if ws_bytes is too small.
@@ -264,7 +269,8 @@ size_t gs_bin_workspace_size(int32_t n, int32_t V, int32_t width, int32_t height
  * Reads the per-view counts back to the host once (info, host), then sizes its launches: from
  * proj->readback when the last gs_project filled it (waiting on that copy's event only), else
  * by its own copy from the device (synchronizing the stream).
- * Errors: GS_ERR_INVALID_ARGUMENT as for gs_project; GS_ERR_CAPACITY (with *required, host,
+ * Errors: GS_ERR_INVALID_ARGUMENT as for gs_project, and when tile_cap > 0 while both
+ * proj->conic_opacity and proj->raster_rec are NULL; GS_ERR_CAPACITY (with *required, host,
  * set to the instances needed) when bins->capacity is too small, in which case the bins are
  * left undefined; GS_ERR_CAPACITY if the workspace is too small.
  */

@@ -211,9 +211,10 @@ def test_project_rejects_bad_arguments(gs):
     small = projected(gs, capacity=50)
     assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(small), FAKE, ws_ok) == 1
     assert b"capacity" in lib.gs_last_error()
-    nulls = projected(gs, null=("mean2d",))
-    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(nulls), FAKE, ws_ok) == 1
-    for f in ("inst_base", "raster_rec"):
+    # the per-field copies of centre, conic/opacity and colour are optional: past the checks
+    lean = projected(gs, null=("mean2d", "conic_opacity", "color"))
+    assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(lean), FAKE, ws_ok - 1) == 2
+    for f in ("vis_ids", "depth", "tile_rect", "n_tiles", "inst_base", "raster_rec"):
         nulls = projected(gs, null=(f,))
         assert call(ctypes.byref(g), c, 1, ctypes.byref(p), ctypes.byref(nulls), FAKE, ws_ok) == 1
     skew = projected(gs)
@@ -252,6 +253,14 @@ def test_bin_and_raster_reject_bad_arguments(gs):
     nocap = gs.gs_bins(1000, 10, FAKE, FAKE, FAKE, None, None, None, None)
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(capped), ctypes.byref(nocap), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws, None) == 1
+    # the cap's scores need the conic and opacity: from conic_opacity, else from the packed records
+    for nulls, code in ((("conic_opacity",), 2), (("raster_rec",), 2), (("conic_opacity", "raster_rec"), 1)):
+        pr = projected(gs, null=nulls)
+        assert lib.gs_bin_tiles(c, ctypes.byref(pr), 1, ctypes.byref(capped), ctypes.byref(bins), ctypes.byref(info),
+                                ctypes.byref(req), FAKE, ws - 1, None) == code, nulls
+    lean = projected(gs, null=("conic_opacity", "raster_rec"))
+    assert lib.gs_bin_tiles(c, ctypes.byref(lean), 1, ctypes.byref(p), ctypes.byref(bins), ctypes.byref(info),
+                            ctypes.byref(req), FAKE, ws - 1, None) == 2  # uncapped: neither is read
     neg = params(gs, tile_cap=-1)
     assert lib.gs_bin_tiles(c, ctypes.byref(proj), 1, ctypes.byref(neg), ctypes.byref(bins), ctypes.byref(info),
                             ctypes.byref(req), FAKE, ws, None) == 1

@@ -9,6 +9,8 @@
   of 1M Gaussians.
 * The projection backward (2D gradients of all views -> parameter gradients) follows the fused
   call in the 1M tests and is compared for every Gaussian.
+* Like the benchmark, the fused runs leave out the optional per-field projection arrays; the
+  projection is then read back from the packed records.
 """
 import numpy as np
 import pytest
@@ -65,7 +67,9 @@ def full_view_check(env, r, scene, settings, mode, v, capped=False, check_projec
 def test_1m_1080p_4views(env, scene_1m, mode):
     oracle, pipeline, torch = env
     st = scene_1m.settings()
-    r = pipeline.Renderer(scene_1m, st)
+    # the fused run in the benchmark's configuration (no per-field projection arrays: the
+    # projection is read back from the packed records), the separate one with them
+    r = pipeline.Renderer(scene_1m, st, lean=(mode == "fused"))
     r.project()
     r.bin()
     if mode == "fused":
@@ -92,7 +96,7 @@ def psnr(a, b):
 def test_1m_1080p_tile_cap(env, scene_1m, K):
     oracle, pipeline, torch = env
     st = scene_1m.settings(tile_cap=K)
-    r = pipeline.Renderer(scene_1m, st)
+    r = pipeline.Renderer(scene_1m, st, lean=True)
     r.project()
     r.bin()
     r.fused(scale=1.0, image=True)
@@ -139,7 +143,7 @@ def test_40m_4k_4views(env):
     oracle, pipeline, torch = env
     sc = scenes.make_scene(5)
     st = sc.settings()
-    r = pipeline.Renderer(sc, st)
+    r = pipeline.Renderer(sc, st, lean=True)
     r.project()
     r.bin()
     r.fused(scale=1.0, image=True)

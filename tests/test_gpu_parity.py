@@ -19,9 +19,10 @@ def env(oracle_mod):
     return oracle_mod, pipeline, torch
 
 
-def run_view_checks(env, scene, settings, mode="separate", region=None, check_projection=True, views=None):
+def run_view_checks(env, scene, settings, mode="separate", region=None, check_projection=True, views=None,
+                    lean=False):
     oracle, pipeline, torch = env
-    r = pipeline.Renderer(scene, settings)
+    r = pipeline.Renderer(scene, settings, lean=lean)
     r.project()
     r.bin()
     if mode == "separate":
@@ -91,7 +92,8 @@ def test_random_multiview_ragged(env, seed, views, size):
 @pytest.mark.parametrize("K", [1, 7, 64])
 def test_tile_cap(env, K):
     sc = scenes.random_scene(6000, 96, 64, seed=200 + K, views=2, log_scale_mean=-3.0, opacity_std=1.5)
-    run_view_checks(env, sc, sc.settings(tile_cap=K), mode="fused", check_projection=False)
+    # fused in the benchmark's configuration (no centre or colour arrays)
+    run_view_checks(env, sc, sc.settings(tile_cap=K), mode="fused", check_projection=False, lean=True)
     run_view_checks(env, sc, sc.settings(tile_cap=K), mode="separate", check_projection=False)
 
 
@@ -169,6 +171,39 @@ def test_fused_max_cap_keeps_capped_lists_on_chip(env):
         else:
             assert fused_staged > fwd_staged
         run_view_checks(env, sc, st, mode="fused", check_projection=False)
+
+
+@pytest.mark.parametrize("K", [0, 24])
+def test_lean_projection_matches_full(env, K):
+    """Without the optional per-field projection arrays (the benchmark's configuration) the
+    packed records hold the per-field values, and the bins (with a cap, scored from the records),
+    images and 2D gradients are those of the full projection bit for bit."""
+    oracle, pipeline, torch = env
+    sc = scenes.random_scene(6000, 96, 64, seed=900 + K, views=2, log_scale_mean=-3.0, opacity_std=1.5)
+    st = sc.settings(tile_cap=K)
+    full = pipeline.Renderer(sc, st)
+    lean = pipeline.Renderer(sc, st, lean=True)
+    # none of the three arrays, also with a cap (whose scores then come from the records)
+    lean.conic_opacity = None
+    lean.proj.conic_opacity = None
+    assert lean.mean2d is None and lean.color is None
+    for r in (full, lean):
+        r.project(); r.bin(); r.fused(image=True)
+    torch.cuda.synchronize()
+    for v in range(len(sc.cameras)):
+        pf, pl = full.projected_host(v), lean.projected_host(v)
+        assert pf["vis_count"] > 0
+        for k in pf:
+            assert np.array_equal(np.asarray(pf[k]), np.asarray(pl[k])), (v, k)
+        for capped in ([False, True] if K else [False]):
+            bf, bl = full.bins_host(v, capped), lean.bins_host(v, capped)
+            for k in bf:
+                assert np.array_equal(bf[k], bl[k]), (v, capped, k)
+        gf, gl = full.grads_host(v), lean.grads_host(v)
+        for k in gf:
+            assert np.array_equal(gf[k], gl[k]), (v, k)
+    # the fused call writes the image (not T or n_contrib)
+    assert np.array_equal(full.images_host()[0], lean.images_host()[0])
 
 
 def test_fused_equals_separate(env):
