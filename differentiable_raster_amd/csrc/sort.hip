@@ -1,7 +1,9 @@
 // Stable LSD radix sort of (uint32 key, uint32 value) pairs, up to 9 bits per pass.
 //
-// Per pass, over tiles of 3072 elements (each of the four wavefronts owns 768 consecutive ones; a
-// tile's 36.5 KB of LDS lets four workgroups share a CU):
+// Per pass, over tiles of 256 x ITEMS elements, ITEMS = 12 (3072 elements; each of the four
+// wavefronts owns 768 consecutive ones; a tile's 36.5 KB of LDS lets four workgroups share a CU),
+// or 6 for sorts of at most kSmallSortN elements (twice as many tiles, so that a small sort
+// spreads over more CUs; 100 K Gaussians at 720p: bin stage 188 -> 164 us):
 //   upsweep   - each block histograms the digit of its tile in LDS and writes the counts
 //               digit-major, hist[d * nblocks + b];
 //   row scan  - one block per digit scans that digit's row over the blocks (the digit's first
@@ -20,9 +22,9 @@ namespace gsmi {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kItems = 12;
-constexpr int kChunk = kBlock * kItems;
-constexpr int kWaveChunk = kWave * kItems;  // elements owned by one wavefront
+constexpr int kItemsLarge = 12;
+constexpr int kItemsSmall = 6;
+constexpr int32_t kSmallSortN = 1024 * kBlock * kItemsSmall;  // 1.57 M elements
 constexpr int kMaxBits = 9;
 constexpr int kRadix = 1 << kMaxBits;
 constexpr int kWaves = kBlock / kWave;
@@ -37,8 +39,10 @@ __device__ __forceinline__ int32_t tile_of(int32_t bid, int32_t nb) {
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void radix_upsweep_kernel(const uint32_t* keys, int32_t n, int shift, uint32_t mask,
                                                                int32_t nblocks, int32_t* hist) {
+    constexpr int kChunk = kBlock * ITEMS;
     __shared__ int s_hist[kRadix];
     const int radix = (int)mask + 1;
 #pragma unroll
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep_kernel(const uint32_t* k
     const int32_t tile = tile_of(blockIdx.x, nblocks);
     const int64_t base = (int64_t)tile * kChunk;
 #pragma unroll
-    for (int r = 0; r < kItems; r++) {
+    for (int r = 0; r < ITEMS; r++) {
         const int64_t e = base + r * kBlock + threadIdx.x;
         if (e < n) atomicAdd(&s_hist[(keys[e] >> shift) & mask], 1);
     }
@@ -95,10 +99,13 @@ __global__ __launch_bounds__(kBlock) void radix_rowscan_kernel(int32_t* hist, in
     if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t* keys, const uint32_t* vals, uint32_t* okeys,
                                                                  uint32_t* ovals, int32_t n, int shift, int bits,
                                                                  int32_t nblocks, const int32_t* rowpref,
                                                                  const int32_t* totals) {
+    constexpr int kChunk = kBlock * ITEMS;
+    constexpr int kWaveChunk = kWave * ITEMS;  // elements owned by one wavefront
     __shared__ int s_base[kRadix];          // first output position of each digit for this block
     __shared__ int s_local[kRadix];         // first position of each digit in the sorted tile
     __shared__ int s_whist[kWaves][kRadix]; // per-wavefront digit counts, then their prefixes
@@ -136,17 +143,17 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
     const int64_t wbase = (int64_t)tile * kChunk + w * kWaveChunk;
     const unsigned long long lt = (1ull << lane) - 1ull;
     int* whist = s_whist[w];
-    uint32_t key[kItems], val[kItems];
-    int rank[kItems];
+    uint32_t key[ITEMS], val[ITEMS];
+    int rank[ITEMS];
 #pragma unroll
-    for (int r = 0; r < kItems; r++) {
+    for (int r = 0; r < ITEMS; r++) {
         const int64_t e = wbase + r * kWave + lane;
         const bool valid = e < n;
         key[r] = valid ? keys[e] : 0u;
         val[r] = valid ? vals[e] : 0u;
     }
 #pragma unroll
-    for (int r = 0; r < kItems; r++) {
+    for (int r = 0; r < ITEMS; r++) {
         const int64_t e = wbase + r * kWave + lane;
         const bool valid = e < n;
         const uint32_t d = (key[r] >> shift) & mask;
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
     __syncthreads();
     const int valid_n = (int)min((int64_t)kChunk, (int64_t)n - (int64_t)tile * kChunk);
 #pragma unroll
-    for (int r = 0; r < kItems; r++) {
+    for (int r = 0; r < ITEMS; r++) {
         if (wbase + r * kWave + lane < n) {
             const uint32_t d = (key[r] >> shift) & mask;
             const int p = s_local[d] + whist[d] + rank[r];
@@ -212,12 +219,24 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep_kernel(const uint32_t*
 
 }  // namespace
 
-static int32_t radix_blocks(int32_t n) { return (n + kChunk - 1) / kChunk; }
+static bool radix_small(int32_t n) { return n <= kSmallSortN; }
+
+static int32_t radix_blocks(int32_t n) {
+    const int32_t chunk = kBlock * (radix_small(n) ? kItemsSmall : kItemsLarge);
+    return (n + chunk - 1) / chunk;
+}
 
 int radix_passes(int bits) { return bits <= 0 ? 0 : (bits + kMaxBits - 1) / kMaxBits; }
 
-// digit-major histograms, then the per-digit totals
-size_t radix_hist_bytes(int32_t n) { return sizeof(int32_t) * ((size_t)kRadix * radix_blocks(n > 0 ? n : 1) + kRadix); }
+// digit-major histograms, then the per-digit totals, for any sort of at most n elements (the
+// small tiles give sorts up to kSmallSortN more tiles than a slightly larger sort has)
+size_t radix_hist_bytes(int32_t n) {
+    n = n > 0 ? n : 1;
+    int32_t nb = radix_blocks(n);
+    const int32_t nb_small = radix_blocks(n < kSmallSortN ? n : kSmallSortN);
+    if (nb_small > nb) nb = nb_small;
+    return sizeof(int32_t) * ((size_t)kRadix * nb + kRadix);
+}
 
 size_t radix_partials_bytes(int32_t /*n*/) { return 0; }
 
@@ -233,10 +252,19 @@ hipError_t launch_radix_sort(uint32_t* keys, uint32_t* vals, uint32_t* keys_alt,
         const int shift = p * dbits;
         const int b = (bits - shift) < dbits ? (bits - shift) : dbits;
         const uint32_t mask = (1u << b) - 1u;
-        hipLaunchKernelGGL(radix_upsweep_kernel, dim3(nb), dim3(kBlock), 0, s, ki, n, shift, mask, nb, hist);
+        if (radix_small(n))
+            hipLaunchKernelGGL(radix_upsweep_kernel<kItemsSmall>, dim3(nb), dim3(kBlock), 0, s, ki, n, shift, mask, nb,
+                               hist);
+        else
+            hipLaunchKernelGGL(radix_upsweep_kernel<kItemsLarge>, dim3(nb), dim3(kBlock), 0, s, ki, n, shift, mask, nb,
+                               hist);
         hipLaunchKernelGGL(radix_rowscan_kernel, dim3(1 << b), dim3(kBlock), 0, s, hist, nb, totals);
-        hipLaunchKernelGGL(radix_downsweep_kernel, dim3(nb), dim3(kBlock), 0, s, ki, vi, ko, vo, n, shift, b, nb, hist,
-                           totals);
+        if (radix_small(n))
+            hipLaunchKernelGGL(radix_downsweep_kernel<kItemsSmall>, dim3(nb), dim3(kBlock), 0, s, ki, vi, ko, vo, n,
+                               shift, b, nb, hist, totals);
+        else
+            hipLaunchKernelGGL(radix_downsweep_kernel<kItemsLarge>, dim3(nb), dim3(kBlock), 0, s, ki, vi, ko, vo, n,
+                               shift, b, nb, hist, totals);
         uint32_t* t = ki;
         ki = ko;
         ko = t;
