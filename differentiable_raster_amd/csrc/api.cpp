@@ -594,9 +594,10 @@ gs_status gs_bin_tiles(const gs_camera* cams, const gs_projected* proj, int32_t 
         uint32_t* v0 = odd ? w.tval_alt : reinterpret_cast<uint32_t*>(bins->vals);
         uint32_t* k1 = odd ? bins->tile_keys : w.tkey_alt;
         uint32_t* v1 = odd ? reinterpret_cast<uint32_t*>(bins->vals) : w.tval_alt;
+        // the depth keys are spent: their two buffers hold the rectangles in depth order
         if (e == hipSuccess)
-            e = launch_emit(packed, proj->n_tiles, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity,
-                            nvis, tiles_x, tpv, (int32_t)M, w.emit_offsets, w.huge_rects, w.huge_count,
+            e = launch_emit(packed, reinterpret_cast<const ushort4*>(proj->tile_rect), proj->capacity, nvis, tiles_x, tpv,
+                            (int32_t)M, w.emit_offsets, w.dkey, w.dkey_alt, w.huge_rects, w.huge_count,
                             huge_rect_cap(bins->capacity), k0, reinterpret_cast<int32_t*>(v0), s);
         if (e == hipSuccess) e = launch_radix_sort(k0, v0, k1, v1, (int32_t)M, tbits, w.hist, w.partials, s);
         if (e == hipSuccess) e = launch_ranges(bins->tile_keys, (int32_t)M, bins->ranges, s);

@@ -108,10 +108,11 @@ __global__ __launch_bounds__(kBlock) void bin_counts_kernel(const int32_t* vis_c
 
 // Emission.  The slots in depth order are cut into chunks of kEmitChunk; within a chunk each
 // wavefront owns kEmitRounds x 64 consecutive slots, one per lane and round.  emit_count_kernel
-// sums each chunk's tile counts (n_tiles, the area of the slot's tile rectangle); after an
-// exclusive scan of those sums (one workgroup), emit_kernel adds the earlier wavefronts' totals
-// and an in-wave scan per round to the chunk's offset, and writes each slot's instances (its
-// tiles row-major) from there.
+// gathers each slot's tile rectangle (the only random access of the emission), stores it in
+// depth order (two words per slot, coalesced) and sums each chunk's tile counts (the rectangles'
+// areas); after an exclusive scan of those sums (one workgroup), emit_kernel reads the
+// rectangles back in order, adds the earlier wavefronts' totals and an in-wave scan per round to
+// the chunk's offset, and writes each slot's instances (its tiles row-major) from there.
 constexpr int kEmitRounds = 4;
 constexpr int kEmitWaveSlots = kWave * kEmitRounds;
 constexpr int kEmitChunk = kBlock * kEmitRounds;
@@ -125,9 +126,11 @@ struct EmitSlot {
 
 // GUARD: the chunk may reach past the last slot; such slots count no instance.  Chunks that lie
 // wholly inside take the unguarded form, whose loads the compiler can issue for all rounds at once.
+// The rectangle comes from the depth-ordered copy that emit_count_kernel wrote.
 template <bool GUARD>
-__device__ __forceinline__ EmitSlot load_emit_slot(const uint32_t* packed, const ushort4* rect, int32_t capacity,
-                                                   int32_t total, int32_t tiles_per_view, int64_t e) {
+__device__ __forceinline__ EmitSlot load_emit_slot(const uint32_t* packed, const uint32_t* rect_lo,
+                                                   const uint32_t* rect_hi, int32_t total, int32_t tiles_per_view,
+                                                   int64_t e) {
     EmitSlot q;
     q.slot = 0;
     q.vbase = 0;
@@ -135,27 +138,28 @@ __device__ __forceinline__ EmitSlot load_emit_slot(const uint32_t* packed, const
     q.nt = 0;
     if (!GUARD || e < total) {
         const uint32_t p = packed[e];
-        const uint32_t v = p >> kSlotBits;
+        const uint32_t lo = rect_lo[e], hi = rect_hi[e];
         q.slot = p & kSlotMask;
-        q.rc = rect[(size_t)v * capacity + q.slot];
-        q.vbase = v * (uint32_t)tiles_per_view;
+        q.rc = make_ushort4((unsigned short)(lo & 0xFFFFu), (unsigned short)(lo >> 16), (unsigned short)(hi & 0xFFFFu),
+                            (unsigned short)(hi >> 16));
+        q.vbase = (p >> kSlotBits) * (uint32_t)tiles_per_view;
         q.nt = (q.rc.z - q.rc.x + 1) * (q.rc.w - q.rc.y + 1);
     }
     return q;
 }
 
 // The slots of this lane in the wavefront's rounds.
-__device__ __forceinline__ void load_emit_rounds(const uint32_t* packed, const ushort4* rect, int32_t capacity,
-                                                 int32_t total, int32_t tiles_per_view, int64_t wbase, int lane,
-                                                 EmitSlot q[kEmitRounds]) {
+__device__ __forceinline__ void load_emit_rounds(const uint32_t* packed, const uint32_t* rect_lo,
+                                                 const uint32_t* rect_hi, int32_t total, int32_t tiles_per_view,
+                                                 int64_t wbase, int lane, EmitSlot q[kEmitRounds]) {
     if ((int64_t)(blockIdx.x + 1) * kEmitChunk <= total) {
 #pragma unroll
         for (int r = 0; r < kEmitRounds; r++)
-            q[r] = load_emit_slot<false>(packed, rect, capacity, total, tiles_per_view, wbase + r * kWave + lane);
+            q[r] = load_emit_slot<false>(packed, rect_lo, rect_hi, total, tiles_per_view, wbase + r * kWave + lane);
     } else {
 #pragma unroll
         for (int r = 0; r < kEmitRounds; r++)
-            q[r] = load_emit_slot<true>(packed, rect, capacity, total, tiles_per_view, wbase + r * kWave + lane);
+            q[r] = load_emit_slot<true>(packed, rect_lo, rect_hi, total, tiles_per_view, wbase + r * kWave + lane);
     }
 }
 
@@ -164,18 +168,23 @@ __device__ __forceinline__ int wave_total(int x) {
     return x;
 }
 
-// Instance count of the slot at depth-order position e (0 past the last slot when GUARD).
+// Instance count of the slot at depth-order position e (0 past the last slot when GUARD), after
+// storing its tile rectangle at e of the depth-ordered copy.
 template <bool GUARD>
-__device__ __forceinline__ int slot_tiles(const uint32_t* packed, const int32_t* n_tiles, int32_t capacity,
-                                          int32_t total, int64_t e) {
+__device__ __forceinline__ int slot_tiles(const uint32_t* packed, const ushort4* rect, int32_t capacity, int32_t total,
+                                          int64_t e, uint32_t* rect_lo, uint32_t* rect_hi) {
     if (GUARD && e >= total) return 0;
     const uint32_t p = packed[e];
-    return n_tiles[(size_t)(p >> kSlotBits) * capacity + (p & kSlotMask)];
+    const ushort4 rc = rect[(size_t)(p >> kSlotBits) * capacity + (p & kSlotMask)];
+    rect_lo[e] = (uint32_t)rc.x | ((uint32_t)rc.y << 16);
+    rect_hi[e] = (uint32_t)rc.z | ((uint32_t)rc.w << 16);
+    return (rc.z - rc.x + 1) * (rc.w - rc.y + 1);
 }
 
-__global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* packed, const int32_t* n_tiles,
+__global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* packed, const ushort4* rect,
                                                             int32_t capacity, int32_t total, int32_t* chunk_counts,
-                                                            int32_t* huge_count) {
+                                                            int32_t* huge_count, uint32_t* rect_lo,
+                                                            uint32_t* rect_hi) {
     __shared__ int s_wave[kEmitWaves];
     if (blockIdx.x == 0 && threadIdx.x == 0) *huge_count = 0;  // the emission appends after this kernel
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -184,11 +193,11 @@ __global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* pack
     if ((int64_t)(blockIdx.x + 1) * kEmitChunk <= total) {
 #pragma unroll
         for (int r = 0; r < kEmitRounds; r++)
-            sum += slot_tiles<false>(packed, n_tiles, capacity, total, wbase + r * kWave + lane);
+            sum += slot_tiles<false>(packed, rect, capacity, total, wbase + r * kWave + lane, rect_lo, rect_hi);
     } else {
 #pragma unroll
         for (int r = 0; r < kEmitRounds; r++)
-            sum += slot_tiles<true>(packed, n_tiles, capacity, total, wbase + r * kWave + lane);
+            sum += slot_tiles<true>(packed, rect, capacity, total, wbase + r * kWave + lane, rect_lo, rect_hi);
     }
     sum = wave_total(sum);
     if (lane == 0) s_wave[w] = sum;
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void emit_count_kernel(const uint32_t* pack
 constexpr int kSmallRect = 8;
 
 __global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, const int32_t* chunk_offsets,
-                                                      const ushort4* rect, int32_t capacity, int32_t total,
+                                                      const uint32_t* rect_lo, const uint32_t* rect_hi, int32_t total,
                                                       int32_t tiles_x, int32_t tiles_per_view, int32_t M,
                                                       int4* huge_list, int32_t* huge_count, int32_t huge_cap,
                                                       uint32_t* tile_keys, int32_t* vals) {
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(kBlock) void emit_kernel(const uint32_t* packed, co
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int64_t wbase = (int64_t)blockIdx.x * kEmitChunk + w * kEmitWaveSlots;
     EmitSlot q[kEmitRounds];
-    load_emit_rounds(packed, rect, capacity, total, tiles_per_view, wbase, lane, q);
+    load_emit_rounds(packed, rect_lo, rect_hi, total, tiles_per_view, wbase, lane, q);
     int sum = 0;
 #pragma unroll
     for (int r = 0; r < kEmitRounds; r++) sum += q[r].nt;
@@ -666,18 +675,18 @@ hipError_t launch_bin_counts(const int32_t* vis_count, const int64_t* inst_count
 
 int32_t emit_chunks(int32_t total) { return total > 0 ? (total + kEmitChunk - 1) / kEmitChunk : 0; }
 
-hipError_t launch_emit(const uint32_t* packed, const int32_t* n_tiles, const ushort4* rect, int32_t capacity,
-                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets,
+hipError_t launch_emit(const uint32_t* packed, const ushort4* rect, int32_t capacity, int32_t total, int32_t tiles_x,
+                       int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets, uint32_t* rect_lo, uint32_t* rect_hi,
                        int4* huge_list, int32_t* huge_count, int32_t huge_cap, uint32_t* tile_keys, int32_t* vals,
                        hipStream_t s) {
     const int32_t nc = emit_chunks(total);
     if (nc == 0) return hipSuccess;
-    hipLaunchKernelGGL(emit_count_kernel, dim3(nc), dim3(kBlock), 0, s, packed, n_tiles, capacity, total,
-                       chunk_offsets, huge_count);
+    hipLaunchKernelGGL(emit_count_kernel, dim3(nc), dim3(kBlock), 0, s, packed, rect, capacity, total, chunk_offsets,
+                       huge_count, rect_lo, rect_hi);
     const hipError_t e = launch_scan_small(chunk_offsets, nc, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(emit_kernel, dim3(nc), dim3(kBlock), 0, s, packed, chunk_offsets, rect, capacity, total, tiles_x,
-                       tiles_per_view, M, huge_list, huge_count, huge_cap, tile_keys, vals);
+    hipLaunchKernelGGL(emit_kernel, dim3(nc), dim3(kBlock), 0, s, packed, chunk_offsets, rect_lo, rect_hi, total,
+                       tiles_x, tiles_per_view, M, huge_list, huge_count, huge_cap, tile_keys, vals);
     // at most one listed rectangle per kHugeRect instances
     const int32_t grid = huge_cap < 1024 ? huge_cap : 1024;
     hipLaunchKernelGGL(emit_huge_kernel, dim3(grid), dim3(kBlock), 0, s, huge_list, huge_count, huge_cap, tiles_x, M,

@@ -166,8 +166,9 @@ int32_t emit_chunks(int32_t total);
 // huge_rect_cap(M) entries; huge_count one int) and written by a workgroup each.
 constexpr int kHugeRect = 256;
 inline int32_t huge_rect_cap(int64_t instances) { return (int32_t)(instances / kHugeRect + 1); }
-hipError_t launch_emit(const uint32_t* packed, const int32_t* n_tiles, const ushort4* rect, int32_t capacity,
-                       int32_t total, int32_t tiles_x, int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets,
+// rect_lo / rect_hi: total words each of workspace (the rectangles in depth order).
+hipError_t launch_emit(const uint32_t* packed, const ushort4* rect, int32_t capacity, int32_t total, int32_t tiles_x,
+                       int32_t tiles_per_view, int32_t M, int32_t* chunk_offsets, uint32_t* rect_lo, uint32_t* rect_hi,
                        int4* huge_list, int32_t* huge_count, int32_t huge_cap, uint32_t* tile_keys, int32_t* vals,
                        hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
