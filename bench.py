@@ -24,8 +24,11 @@ METRIC = "Gaussian-pixel blends/s (fwd+bwd) and ms/iter, 1M Gaussians @1080p, 1 
 # Algorithmic float32 operations (FMA = 2) of the fused rasterizer, per unit:
 FLOPS_PER_ALPHA_PAIR = 16  # evaluate one (pixel, Gaussian) pair whose alpha reaches alpha_min
 FLOPS_PER_BLEND = 81      # blend it in the forward (11) and back-propagate it (70)
-# Non-packed float32 vector peak of MI355X: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz.
-ALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+# Float32 vector peak of MI355X, the published rate: 256 CUs x 128 FMA lanes per cycle (4 SIMDs,
+# each issuing a wave64 float32 instruction every 2 cycles) x 2 flops x 2.4 GHz = 157.3 TFLOP/s.
+# Non-packed instructions with vector operands come close to it (a dense stream of them issues
+# about every 2.5 cycles); the kernels here use no packed float32 instructions.
+ALU_PEAK_TFLOPS = 256 * 128 * 2 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_raster_fused_1m_1080p.md")
 RASTER_SRC = os.path.join(ROOT, "differentiable_raster_amd", "csrc", "raster.hip")
