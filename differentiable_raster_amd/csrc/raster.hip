@@ -227,43 +227,49 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
     const float amax = a.p.alpha_max, tmin = a.p.t_min;
     const float l2amin = __log2f(a.p.alpha_min);
     const uint8_t* lst = b.list[c.list_id];
-    int k_next = lst[0];  // list entries are read one step ahead
-    for (int i = 0; i < l.max_len; i++) {
-        const bool work = (f.done == 0.0f) & (i < l.len);
+    // two list entries per iteration: both are evaluated (their alpha does not depend on T)
+    // before the two compositing updates, in list order; entries are read one pair ahead
+    int k0 = lst[0], k1 = lst[1];
+    for (int i = 0; i < l.max_len; i += 2) {
         // ballots of single compares cost no vector instruction
         if ((__builtin_amdgcn_ballot_w64(f.done == 0.0f) & __builtin_amdgcn_ballot_w64(i < l.len)) == 0ull) break;
-        const int k = k_next;  // past this lane's list: an earlier staged entry, unused
-        k_next = lst[min(i + 1, kBatch - 1)];
-        const float2 xy = b.xy[k];
-        const float4 q = b.q[k];
-        const float4 oc = b.oc[k];
-        const float dx = c.fpx - xy.x;
-        const float dy = c.fpy - xy.y;
-        const float bdx = q.y * dx;
-        const float cdy = q.z * dy;
-        const float p2 = fmaf(q.x * dx, dx, fmaf(bdx, dy, fmaf(cdy, dy, q.w)));
-        const bool hit = work & (p2 >= l2amin);
-        const float v = __builtin_amdgcn_exp2f(p2);              // o exp(-q/2) >= 0
-        const float alpha = __builtin_amdgcn_fmed3f(v, 0.0f, amax);  // min(alpha_max, v)
-        const float oma = 1.0f - alpha;
-        const float Tn = f.T * oma;
-        const bool below = Tn < tmin;
-        const bool stop = hit & below;
-        const bool blend = hit & !below;
-        // zero where the pair does not blend: every lane's staged colour is finite (the lists
-        // start zeroed, so even an index past a list names a staged entry), and 0 * c adds 0
-        const float wgt = blend ? alpha * f.T : 0.0f;
-        if (COUNT) {
-            cnt.eval += work ? 1 : 0;
-            cnt.hit += hit ? 1 : 0;
-            cnt.blend += blend ? 1 : 0;
+        const int ka = k0, kb = k1;  // past this lane's list: earlier staged entries, unused
+        k0 = lst[min(i + 2, kBatch - 1)];
+        k1 = lst[min(i + 3, kBatch - 1)];
+        const float2 xya = b.xy[ka], xyb = b.xy[kb];
+        const float4 qa = b.q[ka], qb = b.q[kb];
+        const float4 oca = b.oc[ka], ocb = b.oc[kb];
+        const float dxa = c.fpx - xya.x, dya = c.fpy - xya.y;
+        const float dxb = c.fpx - xyb.x, dyb = c.fpy - xyb.y;
+        const float p2a = fmaf(qa.x * dxa, dxa, fmaf(qa.y * dxa, dya, fmaf(qa.z * dya, dya, qa.w)));
+        const float p2b = fmaf(qb.x * dxb, dxb, fmaf(qb.y * dxb, dyb, fmaf(qb.z * dyb, dyb, qb.w)));
+        const float alphaa = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(p2a), 0.0f, amax);
+        const float alphab = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(p2b), 0.0f, amax);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const float p2 = h ? p2b : p2a, alpha = h ? alphab : alphaa;
+            const float4 oc = h ? ocb : oca;
+            const int k = h ? kb : ka;
+            const bool work = (f.done == 0.0f) & (i + h < l.len);
+            const bool hit = work & (p2 >= l2amin);
+            const float oma = 1.0f - alpha;
+            const float Tn = f.T * oma;
+            const bool below = Tn < tmin;
+            const bool stop = hit & below;
+            const bool blend = hit & !below;
+            const float wgt = blend ? alpha * f.T : 0.0f;
+            if (COUNT) {
+                cnt.eval += work ? 1 : 0;
+                cnt.hit += hit ? 1 : 0;
+                cnt.blend += blend ? 1 : 0;
+            }
+            f.done = stop ? 1.0f : f.done;
+            f.C0 = fmaf(wgt, oc.x, f.C0);
+            f.C1 = fmaf(wgt, oc.y, f.C1);
+            f.C2 = fmaf(wgt, oc.z, f.C2);
+            f.T = blend ? Tn : f.T;
+            f.last = blend ? jbase + k + 1 : f.last;
         }
-        f.done = stop ? 1.0f : f.done;
-        f.C0 = fmaf(wgt, oc.x, f.C0);
-        f.C1 = fmaf(wgt, oc.y, f.C1);
-        f.C2 = fmaf(wgt, oc.z, f.C2);
-        f.T = blend ? Tn : f.T;
-        f.last = blend ? jbase + k + 1 : f.last;
     }
 }
 
