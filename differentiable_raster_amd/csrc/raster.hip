@@ -243,6 +243,7 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
         const float dxb = c.fpx - xyb.x, dyb = c.fpy - xyb.y;
         const float p2a = fmaf(qa.x * dxa, dxa, fmaf(qa.y * dxa, dya, fmaf(qa.z * dya, dya, qa.w)));
         const float p2b = fmaf(qb.x * dxb, dxb, fmaf(qb.y * dxb, dyb, fmaf(qb.z * dyb, dyb, qb.w)));
+        // exp2(p2) = o exp(-q/2) >= 0; alpha = min(alpha_max, o exp(-q/2))
         const float alphaa = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(p2a), 0.0f, amax);
         const float alphab = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(p2b), 0.0f, amax);
 #pragma unroll
@@ -257,6 +258,8 @@ __device__ __forceinline__ void fwd_walk(const RasterArgs& a, const TileCtx& c, 
             const bool below = Tn < tmin;
             const bool stop = hit & below;
             const bool blend = hit & !below;
+            // zero where the pair does not blend: every lane's staged colour is finite (the lists
+            // start zeroed, so even an index past a list names a staged entry), and 0 * c adds 0
             const float wgt = blend ? alpha * f.T : 0.0f;
             if (COUNT) {
                 cnt.eval += work ? 1 : 0;
