@@ -104,8 +104,10 @@ def cpu_baseline(scene, settings, views, single_views):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 10 warm-up steps and 100 timed ones (about 0.13 s at 1M Gaussians): with 3 and 20 the mean
+    # still carried about 30 us per step of warm-up against the per-iteration median
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload 1..5 (3 = 1M Gaussians @1080p)")
     ap.add_argument("--cap", type=int, default=0, help="per-tile cap K (0 = off)")
     ap.add_argument("--cpu-views", type=int, default=4, help="views of the workload the CPU oracle times on all threads "
